@@ -1,0 +1,204 @@
+"""CPU oracle for the hybrid-head sparse decode step (LycheeDecode).
+
+TEST INFRASTRUCTURE ONLY. This module is the slow, plain, fp64 statement of what
+the decode step computes. Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import it; the product path (the HIP library and its Python
+binding) never does, and shares no code, headers, tables or helpers with it.
+
+Sources (cited by page title and passage):
+  [LD]  "LycheeDecode: Accelerating Long-Context LLM Inference via Hybrid-Head
+        Sparse Decoding" (summary page of arXiv 2602.04541), method paragraph,
+        steps (1), (3), (4) and (7); reproducibility paragraph (30 % key-token budget).
+  [SK]  "LycheeDecode: Head-Level KV Cache Sharing" (skill page), Step 3
+        "Implement Hybrid Attention Layer" (1/sqrt(head_dim) scaling, softmax, 0.5
+        head-type threshold).
+  [HS]  "HySparse: A Hybrid Sparse Attention Architecture with Oracle Token
+        Selection and KV Cache Sharing", section 3 Methodology (sparse layers reuse
+        the full layer's token selection and KV cache).
+  [TSA] "Token Sparse Attention: Efficient Long-Context Inference" (skill page),
+        Step 3 (the budget is clamped to the sequence length: k = min(k, seq_len)).
+
+Readings taken where the pages are silent (each is listed in the design notes):
+  * Head type and the token set S are per *query* head; under grouped KV heads,
+    query head h reads KV head g = h // (Hq // Hkv).
+  * argsTopK ranks the logits q.k/sqrt(d) (softmax is strictly increasing per row,
+    so the selected set equals that of the probabilities whenever they are untied).
+    Total order: larger value first; equal values -> lower index first; -0.0 equals
+    +0.0; NaN ranks below every number (NaNs among themselves by index).
+  * S is a set; it is stored in ascending index order.
+  * No causal mask at decode: the single query attends to all N cached rows.
+  * A sparse head reads its own layer's K/V at S ([LD] step 4); for HySparse-style
+    stacks the caller passes the full layer's K/V ([HS] section 3).
+
+Parity pins: tests/test_oracle_pins.py checks every function here against closed
+forms, hand-derived examples (tests/golden/), brute-force ranking and invariants.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64",
+    "softmax_attention",
+    "select_topk",
+    "select_topk_f32",
+    "retrieval_head",
+    "sparse_head",
+    "hybrid_layer_f64",
+    "hybrid_layer_bf16",
+    "default_scale",
+]
+
+
+def default_scale(head_dim: int) -> float:
+    """1/sqrt(d_k) ([LD] step 3; [SK] Step 3)."""
+    return 1.0 / math.sqrt(head_dim)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float64.
+
+    A bf16 value is the upper half of an IEEE binary32 word, so shifting the 16 bits
+    into the high half gives the identical float32, which widens exactly to float64.
+    """
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                      scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """One query row against n cached rows, in fp64 ([LD] step 3).
+
+    s_i = (q . K_i) * scale;  w_i = exp(s_i - max s);  O = sum_i w_i V_i / sum_i w_i.
+    Returns (O [d], s [n]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    assert K.ndim == 2 and K.shape[0] >= 1, "softmax over an empty set is undefined"
+    s = (K @ q) * scale
+    m = np.max(s)
+    w = np.exp(s - m)
+    O = (w @ V) / np.sum(w)
+    return O, s
+
+
+def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """argsTopK ([LD] step 3): the k best entries under the total order above,
+    returned as ascending int64 indices."""
+    s = np.asarray(scores)
+    n = s.shape[0]
+    assert 1 <= k <= n, "k must satisfy 1 <= k <= n"
+    s = s.astype(np.float64)                     # exact for float32 inputs
+    isnan = np.isnan(s)
+    v = np.where(isnan, 0.0, s) + 0.0            # -0.0 + 0.0 == +0.0
+    # lexsort: last key is primary -> non-NaN first, then value descending,
+    # then index ascending.
+    order = np.lexsort((np.arange(n), -v, isnan))
+    return np.sort(order[:k]).astype(np.int64)
+
+
+def select_topk_f32(scores_f32: np.ndarray, k: int) -> np.ndarray:
+    """The same selection applied to float32 values exactly as given."""
+    s = np.asarray(scores_f32)
+    assert s.dtype == np.float32
+    return select_topk(s, k)
+
+
+def retrieval_head(q, K, V, k: int, scale: float):
+    """Retrieval head ([LD] step 3): full attention over all n rows, then
+    S_next = argsTopK(scores, k). Returns (O, S_next, scores)."""
+    O, s = softmax_attention(q, K, V, scale)
+    return O, select_topk(s, k), s
+
+
+def sparse_head(q, K, V, S: np.ndarray, scale: float):
+    """Sparse head ([LD] step 4): attention over rows S of its own layer's K/V;
+    S is forwarded unchanged. Returns (O, S)."""
+    S = np.asarray(S, dtype=np.int64)
+    n = K.shape[0]
+    assert S.ndim == 1 and S.size >= 1
+    assert np.all((S >= 0) & (S < n)), "S entries must lie in [0, n)"
+    assert np.unique(S).size == S.size, "S entries must be distinct"
+    O, _ = softmax_attention(q, K[S], V[S], scale)
+    return O, S
+
+
+def hybrid_layer_f64(Q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                     kv_offsets: Sequence[int], retrieval: Sequence[bool],
+                     k_per_seq: Sequence[int], S_in: Optional[Dict[Tuple[int, int], np.ndarray]],
+                     scale: Optional[float] = None, active: Optional[Sequence[bool]] = None,
+                     ):
+    """One layer of the recurrence for every (sequence b, query head h).
+
+    Q: [B][Hq][d]; K, V: [Hkv][T][d] (sequence b owns rows kv_offsets[b]:kv_offsets[b+1]).
+    retrieval[h]: True for a retrieval head (the inference split E[z] > 0.5 of
+    [LD] step 7 is given as this mask). S_in[(b, h)]: the set handed over by the
+    previous layer (required for every active sparse head).
+    active[h]: heads to compute (default all).
+
+    Returns (O [B][Hq][d] with NaN rows for inactive heads,
+             S_out {(b,h): indices}, scores {(b,h): fp64 scores of retrieval rows}).
+    S_out[(b,h)] = argsTopK for retrieval heads ([LD] step 3), S_in[(b,h)] for sparse
+    heads ([LD] step 4).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, Hq, d = Q.shape
+    Hkv = K.shape[0]
+    assert Hq % Hkv == 0
+    G = Hq // Hkv
+    if scale is None:
+        scale = default_scale(d)
+    if active is None:
+        active = [True] * Hq
+    O = np.full((B, Hq, d), np.nan)
+    S_out: Dict[Tuple[int, int], np.ndarray] = {}
+    scores: Dict[Tuple[int, int], np.ndarray] = {}
+    for b in range(B):
+        lo, hi = int(kv_offsets[b]), int(kv_offsets[b + 1])
+        n = hi - lo
+        kb = min(int(k_per_seq[b]), n)           # [TSA] Step 3 clamp
+        for h in range(Hq):
+            if not active[h]:
+                if S_in is not None and (b, h) in S_in:
+                    S_out[(b, h)] = np.asarray(S_in[(b, h)], dtype=np.int64)
+                continue
+            g = h // G
+            Kg, Vg = K[g, lo:hi], V[g, lo:hi]
+            if retrieval[h]:
+                O[b, h], S_out[(b, h)], scores[(b, h)] = retrieval_head(Q[b, h], Kg, Vg, kb, scale)
+            else:
+                assert S_in is not None and (b, h) in S_in, "sparse head needs S from the previous layer"
+                O[b, h], S_out[(b, h)] = sparse_head(Q[b, h], Kg, Vg, S_in[(b, h)], scale)
+    return O, S_out, scores
+
+
+def hybrid_layer_bf16(q_bits, k_bits, v_bits, kv_offsets, retrieval, k_per_seq, S_in,
+                      scale=None, active=None):
+    """hybrid_layer_f64 on raw bf16 bit patterns (uint16), widened exactly."""
+    return hybrid_layer_f64(bf16_bits_to_f64(q_bits), bf16_bits_to_f64(k_bits),
+                            bf16_bits_to_f64(v_bits), kv_offsets, retrieval, k_per_seq,
+                            S_in, scale=scale, active=active)
+
+
+def decode_step_f64(layers: List[Tuple[np.ndarray, np.ndarray, np.ndarray]],
+                    kv_offsets, retrieval_masks: Sequence[Sequence[bool]], k_per_seq,
+                    scale=None):
+    """The whole recurrence over L layers ([LD] steps (1), (3), (4)).
+
+    layers[l] = (Q, K, V) in fp64. Layer 0 must be all retrieval ([LD] step 1).
+    Returns lists of per-layer O and S_out.
+    """
+    assert all(retrieval_masks[0]), "every head of layer 0 is a retrieval head"
+    S = None
+    outs, sets = [], []
+    for l, (Q, K, V) in enumerate(layers):
+        O, S, _ = hybrid_layer_f64(Q, K, V, kv_offsets, retrieval_masks[l], k_per_seq, S, scale)
+        outs.append(O)
+        sets.append(S)
+    return outs, sets

@@ -1,0 +1,300 @@
+"""Pins for the CPU oracle against things other than itself: hand-derived golden
+examples, closed forms, brute-force ranking and invariants of the recurrence on the
+LycheeDecode summary page (method steps (1), (3), (4))."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import lychee_oracle as orc
+from tests.conftest import GOLDEN
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f(x):
+    return float(x)  # "nan", "inf", "-inf" strings parse too
+
+
+# ----------------------------------------------------------------- bf16 widening
+
+def test_bf16_widening_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x7F80, 0xFF80, 0x0000, 0x8000, 0x3E80, 0x4049, 0x0001],
+                    dtype=np.uint16)
+    got = orc.bf16_bits_to_f64(bits)
+    want = [1.0, -2.0, math.inf, -math.inf, 0.0, -0.0, 0.25, 3.140625, 2.0 ** -133]
+    for g, w in zip(got, want):
+        assert g == w and math.copysign(1, g) == math.copysign(1, w)
+    assert np.isnan(orc.bf16_bits_to_f64(np.array([0x7FC0], dtype=np.uint16)))[0]
+
+
+# ------------------------------------------------------------ attention closed forms
+
+def test_two_token_golden():
+    g = _load("two_token_softmax.json")
+    O, s = orc.softmax_attention(np.array(g["q"]), np.array(g["K"]), np.array(g["V"]),
+                                 orc.default_scale(4))
+    np.testing.assert_allclose(O, g["expected_O"], rtol=1e-14, atol=1e-13)
+    np.testing.assert_allclose(s, g["expected_scores"], rtol=1e-14, atol=1e-15)
+
+
+def test_single_row_returns_value_row():
+    rng = np.random.default_rng(0)
+    q, K, V = rng.normal(size=8), rng.normal(size=(1, 8)), rng.normal(size=(1, 8))
+    O, _ = orc.softmax_attention(q, K, V, 0.3)
+    assert np.array_equal(O, V[0])
+
+
+@pytest.mark.parametrize("d", [4, 64, 128])
+def test_identical_keys_give_mean_of_values(d):
+    rng = np.random.default_rng(d)
+    n = 37
+    q = rng.normal(size=d)
+    K = np.tile(rng.normal(size=d), (n, 1))
+    V = rng.normal(size=(n, d))
+    O, _ = orc.softmax_attention(q, K, V, orc.default_scale(d))
+    np.testing.assert_allclose(O, V.mean(axis=0), rtol=1e-12, atol=1e-13)
+
+
+def test_zero_query_gives_mean_of_values():
+    rng = np.random.default_rng(1)
+    K, V = rng.normal(size=(11, 16)), rng.normal(size=(11, 16))
+    O, _ = orc.softmax_attention(np.zeros(16), K, V, 0.25)
+    np.testing.assert_allclose(O, V.mean(axis=0), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("gap", [60.0, 1000.0])
+def test_dominant_logit_selects_its_value_row(gap):
+    # A logit `gap` above all others puts weight exp(-gap) (< 1e-26) elsewhere;
+    # gap = 1000 also checks that the maximum is subtracted before exp.
+    rng = np.random.default_rng(2)
+    d, n, p = 8, 20, 13
+    K = rng.normal(size=(n, d)) * 0.1
+    q = np.zeros(d); q[0] = 1.0
+    K[p, 0] = gap / orc.default_scale(d) + 1.0
+    V = rng.normal(size=(n, d))
+    O, _ = orc.softmax_attention(q, K, V, orc.default_scale(d))
+    np.testing.assert_allclose(O, V[p], rtol=1e-15, atol=1e-15)
+
+
+def test_row_permutation_invariance():
+    rng = np.random.default_rng(3)
+    q, K, V = rng.normal(size=32), rng.normal(size=(50, 32)), rng.normal(size=(50, 32))
+    perm = rng.permutation(50)
+    O1, _ = orc.softmax_attention(q, K, V, 0.2)
+    O2, _ = orc.softmax_attention(q, K[perm], V[perm], 0.2)
+    np.testing.assert_allclose(O1, O2, rtol=1e-13, atol=1e-14)
+
+
+def test_key_shift_along_null_direction_is_invariant():
+    # Adding c to every key with q.c = t shifts every logit by the same t*scale,
+    # which softmax cancels.
+    rng = np.random.default_rng(4)
+    d = 16
+    q, K, V = rng.normal(size=d), rng.normal(size=(25, d)), rng.normal(size=(25, d))
+    c = rng.normal(size=d) * 3
+    O1, _ = orc.softmax_attention(q, K, V, 0.25)
+    O2, _ = orc.softmax_attention(q, K + c, V, 0.25)
+    np.testing.assert_allclose(O1, O2, rtol=1e-12, atol=1e-13)
+
+
+# -------------------------------------------------------------------- top-k
+
+def _brute_force_topk(vals, k):
+    """Rank by counting who beats whom (no sorting), then keep rank < k."""
+    n = len(vals)
+    v = [float(x) for x in vals]
+
+    def beats(j, i):
+        nj, ni = math.isnan(v[j]), math.isnan(v[i])
+        if nj != ni:
+            return ni                      # a number beats NaN
+        if nj and ni:
+            return j < i
+        if v[j] != v[i]:                   # -0.0 == +0.0 here
+            return v[j] > v[i]
+        return j < i
+
+    rank = [sum(beats(j, i) for j in range(n) if j != i) for i in range(n)]
+    return sorted(i for i in range(n) if rank[i] < k)
+
+
+def test_topk_golden_special_values():
+    g = _load("topk_special_values.json")
+    vals = np.array([_f(x) for x in g["values"]], dtype=np.float32)
+    for k, want in g["expected"].items():
+        assert orc.select_topk_f32(vals, int(k)).tolist() == want
+    for case in g["signed_zero_cases"]:
+        vals = np.array(case["values"], dtype=np.float32)
+        assert orc.select_topk_f32(vals, case["k"]).tolist() == case["expected"]
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_topk_matches_brute_force_with_heavy_ties(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 41))
+    pool = np.array([-1.0, -0.0, 0.0, 0.5, 2.0, np.inf, -np.inf, np.nan], dtype=np.float32)
+    if seed % 3 == 0:
+        vals = rng.normal(size=n).astype(np.float32)
+    else:
+        vals = pool[rng.integers(0, len(pool), size=n)]
+    for k in range(1, n + 1):
+        assert orc.select_topk_f32(vals, k).tolist() == _brute_force_topk(vals, k)
+
+
+def test_topk_special_cases():
+    n = 100
+    const = np.full(n, 0.75, dtype=np.float32)
+    assert orc.select_topk_f32(const, 17).tolist() == list(range(17))
+    inc = np.arange(n, dtype=np.float32)
+    assert orc.select_topk_f32(inc, 30).tolist() == list(range(70, 100))
+    dec = inc[::-1].copy()
+    assert orc.select_topk_f32(dec, 30).tolist() == list(range(30))
+    assert orc.select_topk_f32(np.random.default_rng(0).normal(size=n).astype(np.float32), n).tolist() == list(range(n))
+
+
+def test_topk_on_logits_equals_topk_on_probabilities():
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        s = rng.normal(size=500) * 3
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        assert np.unique(p).size == p.size
+        for k in (1, 50, 150, 499):
+            assert np.array_equal(orc.select_topk(s, k), orc.select_topk(p, k))
+
+
+def test_topk_rejects_bad_k():
+    with pytest.raises(AssertionError):
+        orc.select_topk(np.zeros(4), 0)
+    with pytest.raises(AssertionError):
+        orc.select_topk(np.zeros(4), 5)
+
+
+# ------------------------------------------------------- sparse head and layer
+
+def test_sparse_with_all_rows_equals_full():
+    rng = np.random.default_rng(8)
+    n, d = 64, 32
+    q, K, V = rng.normal(size=d), rng.normal(size=(n, d)), rng.normal(size=(n, d))
+    O_full, _ = orc.softmax_attention(q, K, V, 0.2)
+    O_sp, S = orc.sparse_head(q, K, V, np.arange(n), 0.2)
+    np.testing.assert_allclose(O_sp, O_full, rtol=1e-13, atol=1e-14)
+    # S given in any order is the same set
+    O_sp2, _ = orc.sparse_head(q, K, V, rng.permutation(n), 0.2)
+    np.testing.assert_allclose(O_sp2, O_full, rtol=1e-13, atol=1e-14)
+
+
+def test_sparse_single_index_returns_that_row():
+    rng = np.random.default_rng(9)
+    q, K, V = rng.normal(size=16), rng.normal(size=(40, 16)), rng.normal(size=(40, 16))
+    for p in (0, 17, 39):
+        O, S = orc.sparse_head(q, K, V, np.array([p]), 0.25)
+        assert np.array_equal(O, V[p]) and S.tolist() == [p]
+
+
+def test_sparse_ignores_rows_outside_set():
+    rng = np.random.default_rng(10)
+    n, d = 30, 8
+    q, K, V = rng.normal(size=d), rng.normal(size=(n, d)), rng.normal(size=(n, d))
+    S = np.array([2, 5, 11, 29])
+    O1, _ = orc.sparse_head(q, K, V, S, 0.3)
+    K2, V2 = K.copy(), V.copy()
+    mask = np.ones(n, bool); mask[S] = False
+    K2[mask] = 1e3; V2[mask] = -1e3
+    O2, _ = orc.sparse_head(q, K2, V2, S, 0.3)
+    assert np.array_equal(O1, O2)
+
+
+def test_gqa_head_to_kv_mapping():
+    # KV head g holds constant value rows equal to g+1; query head h must read
+    # KV head h // (Hq/Hkv).
+    B, Hq, Hkv, n, d = 1, 8, 2, 10, 4
+    rng = np.random.default_rng(11)
+    Q = rng.normal(size=(B, Hq, d))
+    K = rng.normal(size=(Hkv, n, d))
+    V = np.stack([np.full((n, d), g + 1.0) for g in range(Hkv)])
+    O, S, _ = orc.hybrid_layer_f64(Q, K, V, [0, n], [True] * Hq, [3], None)
+    for h in range(Hq):
+        np.testing.assert_allclose(O[0, h], np.full(d, h // 4 + 1.0), rtol=1e-14)
+
+
+def test_recurrence_golden_three_layers():
+    g = _load("recurrence_3layer.json")
+    N, d, k = g["N"], g["d"], g["k"]
+    layers = []
+    for l in range(3):
+        Q = np.zeros((1, 2, d)); Q[0, :, 0] = math.sqrt(2.0)
+        K = np.zeros((2, N, d)); V = np.zeros((2, N, d))
+        for h in range(2):
+            K[h, :, 0] = g["K_first_coord"][l][h]
+            for i in range(N):
+                V[h, i] = [i + 1 + 10 * h + 100 * l, (i + 1) ** 2]
+        layers.append((Q, K, V))
+    outs, sets = orc.decode_step_f64(layers, [0, N], g["retrieval_masks"], [k])
+    for l in range(3):
+        for h in range(2):
+            assert sets[l][(0, h)].tolist() == g["expected_S"][l][h], (l, h)
+    for e in g["expected_O_sparse"]:
+        np.testing.assert_allclose(outs[e["layer"]][0, e["head"]], e["O"], rtol=1e-14)
+
+
+def test_layer0_must_be_all_retrieval():
+    Q = np.zeros((1, 2, 2)); K = np.zeros((2, 4, 2)); V = np.zeros((2, 4, 2))
+    with pytest.raises(AssertionError):
+        orc.decode_step_f64([(Q, K, V)], [0, 4], [[True, False]], [2])
+
+
+def test_sparse_head_carries_layer0_set_through_all_sparse_layers():
+    rng = np.random.default_rng(12)
+    B, Hq, n, d, L = 1, 3, 40, 8, 5
+    masks = [[True] * Hq] + [[h == 0 for h in range(Hq)] for _ in range(L - 1)]
+    layers = [(rng.normal(size=(B, Hq, d)), rng.normal(size=(Hq, n, d)), rng.normal(size=(Hq, n, d)))
+              for _ in range(L)]
+    outs, sets = orc.decode_step_f64(layers, [0, n], masks, [12])
+    for h in (1, 2):
+        for l in range(1, L):
+            assert np.array_equal(sets[l][(0, h)], sets[0][(0, h)])
+    assert not np.array_equal(sets[L - 1][(0, 0)], sets[0][(0, 0)])
+
+
+def test_batch_permutation_invariance_ragged():
+    rng = np.random.default_rng(13)
+    Hq, Hkv, d = 4, 2, 16
+    lens = [23, 40, 17]
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    T = offs[-1]
+    Q = rng.normal(size=(3, Hq, d))
+    K = rng.normal(size=(Hkv, T, d)); V = rng.normal(size=(Hkv, T, d))
+    ks = [7, 12, 5]
+    ret = [True, False, True, False]
+    S_in = {(b, h): np.sort(rng.choice(lens[b], ks[b], replace=False)) for b in range(3) for h in range(Hq)}
+    O, S, _ = orc.hybrid_layer_f64(Q, K, V, offs, ret, ks, S_in)
+    perm = [2, 0, 1]
+    lens_p = [lens[p] for p in perm]
+    offs_p = np.concatenate([[0], np.cumsum(lens_p)])
+    Kp = np.concatenate([K[:, offs[p]:offs[p + 1]] for p in perm], axis=1)
+    Vp = np.concatenate([V[:, offs[p]:offs[p + 1]] for p in perm], axis=1)
+    S_in_p = {(i, h): S_in[(p, h)] for i, p in enumerate(perm) for h in range(Hq)}
+    Op, Sp, _ = orc.hybrid_layer_f64(Q[perm], Kp, Vp, offs_p, ret, [ks[p] for p in perm], S_in_p)
+    for i, p in enumerate(perm):
+        assert np.array_equal(Op[i], O[p])
+        for h in range(Hq):
+            assert np.array_equal(Sp[(i, h)], S[(p, h)])
+
+
+def test_hybrid_layer_bf16_matches_widened_f64():
+    rng = np.random.default_rng(14)
+    Hq, Hkv, n, d = 4, 2, 33, 8
+    qb = rng.integers(0x3000, 0x4000, size=(1, Hq, d)).astype(np.uint16)
+    kb = rng.integers(0x3000, 0x4000, size=(Hkv, n, d)).astype(np.uint16)
+    vb = rng.integers(0xB000, 0xC000, size=(Hkv, n, d)).astype(np.uint16)
+    O1, S1, _ = orc.hybrid_layer_bf16(qb, kb, vb, [0, n], [True] * Hq, [9], None)
+    O2, S2, _ = orc.hybrid_layer_f64(orc.bf16_bits_to_f64(qb), orc.bf16_bits_to_f64(kb),
+                                     orc.bf16_bits_to_f64(vb), [0, n], [True] * Hq, [9], None)
+    assert np.array_equal(O1, O2)
