@@ -1,0 +1,285 @@
+"""Python binding of liblychee_decode.so (the gfx950 hybrid-head sparse decode step).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels
+behind the C ABI declared in include/lychee_decode.h. PyTorch supplies device
+memory and the current stream. The library must have been built
+(``python -m hybrid_head_sparse_retrieval_amd.build``); importing the functions
+below without it raises ``LycheeDecodeUnavailable`` -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = [
+    "LycheeDecodeError", "LycheeDecodeUnavailable", "library_path", "load_library",
+    "Shape", "workspace_bytes", "topk_workspace_bytes", "Workspace", "TopkWorkspace",
+    "retrieval_decode", "sparse_decode", "hybrid_layer", "topk_select",
+    "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "flag_split_rows", "EXPORTED_SYMBOLS",
+]
+
+LD_OK = 0
+FLAG_SKIP_TOPK = 1
+FLAG_S_CHAINED = 2
+_STATUS = {1: "invalid argument", 2: "unsupported shape", 3: "workspace missing or too small",
+           4: "HIP launch failed"}
+EXPORTED_SYMBOLS = ("ld_status_string", "ld_workspace_size", "ld_topk_workspace_size",
+                    "ld_workspace_init", "ld_retrieval_decode", "ld_sparse_decode",
+                    "ld_hybrid_layer", "ld_topk_select")
+
+
+def flag_split_rows(v: int) -> int:
+    """Rows per attention split = 256 << (v - 1), v in 1..4 (0 = automatic)."""
+    return (int(v) & 0xF) << 8
+
+
+class LycheeDecodeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, 'status %d' % status)}")
+
+
+class LycheeDecodeUnavailable(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblychee_decode.so")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int64),
+        ("kv_indptr", ctypes.c_void_p),
+        ("softmax_scale", ctypes.c_float),
+        ("reserved1", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library():
+    """Load the shared library (once). Raises LycheeDecodeUnavailable if not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise LycheeDecodeUnavailable(
+            f"{path} is missing; build it with `python -m hybrid_head_sparse_retrieval_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, u32, u64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t)
+    sp = ctypes.POINTER(Shape)
+    lib.ld_status_string.restype = ctypes.c_char_p
+    lib.ld_status_string.argtypes = [i32]
+    lib.ld_workspace_size.restype = sz
+    lib.ld_workspace_size.argtypes = [sp, i32]
+    lib.ld_topk_workspace_size.restype = sz
+    lib.ld_topk_workspace_size.argtypes = [i32, i32]
+    lib.ld_workspace_init.restype = i32
+    lib.ld_workspace_init.argtypes = [vp, sz, vp]
+    lib.ld_retrieval_decode.restype = i32
+    lib.ld_retrieval_decode.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.ld_sparse_decode.restype = i32
+    lib.ld_sparse_decode.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, u32, vp, sz, vp]
+    lib.ld_hybrid_layer.restype = i32
+    lib.ld_hybrid_layer.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, vp, vp, u32, vp, sz, vp]
+    lib.ld_topk_select.restype = i32
+    lib.ld_topk_select.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    torch = _torch()
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != LD_OK:
+        raise LycheeDecodeError(status, where)
+
+
+def make_shape(q, k_cache, kv_indptr=None, seq_len=None, scale=None) -> Shape:
+    """ld_shape from tensors: q [B][Hq][d], k_cache [Hkv][T][d]."""
+    B, Hq, d = q.shape
+    Hkv, T, d2 = k_cache.shape
+    if d2 != d:
+        raise ValueError("head_dim of q and k_cache differ")
+    if kv_indptr is None:
+        n = seq_len if seq_len is not None else T // B
+    else:
+        if seq_len is None:
+            raise ValueError("seq_len (max sequence length) is required with kv_indptr")
+        n = seq_len
+    s = Shape()
+    s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim = B, Hq, Hkv, d
+    s.seq_len = int(n)
+    s.total_tokens = int(T)
+    s.kv_indptr = _ptr(kv_indptr)
+    s.softmax_scale = float(scale) if scale is not None else 0.0
+    return s
+
+
+def workspace_bytes(shape: Shape, k_max: int) -> int:
+    n = load_library().ld_workspace_size(ctypes.byref(shape), int(k_max))
+    if n == 0:
+        raise LycheeDecodeError(1, "ld_workspace_size")
+    return int(n)
+
+
+def topk_workspace_bytes(rows: int, n: int) -> int:
+    v = load_library().ld_topk_workspace_size(int(rows), int(n))
+    if v == 0:
+        raise LycheeDecodeError(1, "ld_topk_workspace_size")
+    return int(v)
+
+
+class _WS:
+    def __init__(self, nbytes: int, device):
+        torch = _torch()
+        self.nbytes = int(nbytes)
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        _check(load_library().ld_workspace_init(self.buf.data_ptr(), self.nbytes, _stream()),
+               "ld_workspace_init")
+
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+
+class Workspace(_WS):
+    """Zero-initialised device workspace for the layer entry points."""
+
+    def __init__(self, shape: Shape, k_max: int, device="cuda"):
+        super().__init__(workspace_bytes(shape, k_max), device)
+
+
+class TopkWorkspace(_WS):
+    def __init__(self, rows: int, n: int, device="cuda"):
+        super().__init__(topk_workspace_bytes(rows, n), device)
+
+
+def _req(t, dtype, name):
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _opt(t, dtype, name):
+    return None if t is None else _req(t, dtype, name)
+
+
+def _prep(q, k_cache, v_cache, out, kv_indptr):
+    torch = _torch()
+    _req(q, torch.bfloat16, "q")
+    _req(k_cache, torch.bfloat16, "k_cache")
+    _req(v_cache, torch.bfloat16, "v_cache")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    if out is None:
+        out = torch.empty_like(q)
+    _req(out, torch.bfloat16, "out")
+    _opt(kv_indptr, torch.int64, "kv_indptr")
+    return out
+
+
+def retrieval_decode(q, k_cache, v_cache, head_mask: int, k: int, *, s_out=None, s_indptr=None,
+                     scores_out=None, out=None, workspace: Optional[Workspace] = None,
+                     kv_indptr=None, seq_len=None, scale=None):
+    """Retrieval heads: full attention (+ argsTopK into s_out when given). Returns out."""
+    torch = _torch()
+    out = _prep(q, k_cache, v_cache, out, kv_indptr)
+    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale)
+    _opt(s_out, torch.int32, "s_out"); _opt(s_indptr, torch.int64, "s_indptr")
+    _opt(scores_out, torch.float32, "scores_out")
+    ws = workspace or Workspace(shape, k, q.device)
+    _check(load_library().ld_retrieval_decode(
+        ctypes.byref(shape), int(head_mask), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        int(k), _ptr(s_out), _ptr(s_indptr), _ptr(scores_out), out.data_ptr(), ws.ptr(), ws.nbytes,
+        _stream()), "ld_retrieval_decode")
+    return out
+
+
+def sparse_decode(q, k_cache, v_cache, head_mask: int, k: int, s_in, *, s_indptr=None, out=None,
+                  flags: int = 0, workspace: Optional[Workspace] = None, kv_indptr=None,
+                  seq_len=None, scale=None):
+    """Sparse heads: attention over K[S], V[S]. Returns out."""
+    torch = _torch()
+    out = _prep(q, k_cache, v_cache, out, kv_indptr)
+    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale)
+    _req(s_in, torch.int32, "s_in"); _opt(s_indptr, torch.int64, "s_indptr")
+    ws = workspace or Workspace(shape, k, q.device)
+    _check(load_library().ld_sparse_decode(
+        ctypes.byref(shape), int(head_mask), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        int(k), s_in.data_ptr(), _ptr(s_indptr), out.data_ptr(), int(flags), ws.ptr(), ws.nbytes,
+        _stream()), "ld_sparse_decode")
+    return out
+
+
+def hybrid_layer(q, k_cache, v_cache, retrieval_mask: int, k: int, s, *, s_out=None,
+                 s_indptr=None, scores_out=None, out=None, flags: int = 0,
+                 workspace: Optional[Workspace] = None, kv_indptr=None, seq_len=None,
+                 scale=None):
+    """One layer of the recurrence. `s` is S^{l} (None for an all-retrieval layer);
+    S^{l+1} is written to `s_out` (default: in place into `s`). Returns out."""
+    torch = _torch()
+    out = _prep(q, k_cache, v_cache, out, kv_indptr)
+    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale)
+    _opt(s, torch.int32, "s"); _opt(s_out, torch.int32, "s_out")
+    _opt(s_indptr, torch.int64, "s_indptr"); _opt(scores_out, torch.float32, "scores_out")
+    if s_out is None:
+        s_out = s
+    ws = workspace or Workspace(shape, k, q.device)
+    _check(load_library().ld_hybrid_layer(
+        ctypes.byref(shape), int(retrieval_mask), q.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), int(k), _ptr(s), _ptr(s_out), _ptr(s_indptr), _ptr(scores_out),
+        out.data_ptr(), int(flags), ws.ptr(), ws.nbytes, _stream()), "ld_hybrid_layer")
+    return out
+
+
+def topk_select(scores, k: int, *, idx_out=None, val_out=None,
+                workspace: Optional[TopkWorkspace] = None):
+    """argsTopK of each row of a 2-D fp32 tensor; ascending indices [rows][k] (int32)."""
+    torch = _torch()
+    if scores.dim() != 2:
+        raise ValueError("scores must be 2-D [rows][n]")
+    rows, n = scores.shape
+    row_stride = scores.stride(0) if rows > 1 else n     # a size-1 dim has no meaningful stride
+    if (n > 1 and scores.stride(1) != 1) or row_stride < n:
+        raise ValueError("scores must have unit stride along each row")
+    if not scores.is_cuda or scores.dtype != torch.float32:
+        raise ValueError("scores must be a float32 device tensor")
+    if idx_out is None:
+        idx_out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    _req(idx_out, torch.int32, "idx_out"); _opt(val_out, torch.float32, "val_out")
+    ws = workspace or TopkWorkspace(rows, n, scores.device)
+    _check(load_library().ld_topk_select(
+        scores.data_ptr(), int(rows), int(n), int(row_stride), int(k), idx_out.data_ptr(),
+        _ptr(val_out), ws.ptr(), ws.nbytes, _stream()), "ld_topk_select")
+    return idx_out

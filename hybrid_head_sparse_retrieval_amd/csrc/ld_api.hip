@@ -1,0 +1,322 @@
+// Host side of liblychee_decode.so: argument validation, workspace layout and the
+// launch sequence of one layer (declared in include/lychee_decode.h).
+
+#include <cmath>
+#include <cstring>
+
+#include "lychee_decode.h"
+#include "ld_internal.h"
+
+namespace {
+
+using namespace ld;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct LayerLayout {
+  int slots, P, C, W;
+  int64_t ncap;
+  size_t attn_tickets, sel_tickets, hist1, hist2, cand_count;   // zero between calls
+  size_t sel_info, chunk_cnt, cand_key, cand_idx, logits, part_ml, part_acc, bitmaps;
+  size_t total;
+};
+
+struct SelLayout {
+  size_t tickets, hist1, hist2, cand_count, sel_info, chunk_cnt, cand_key, cand_idx, total;
+};
+
+bool shape_ok(const ld_shape* s, ld_status* why) {
+  *why = LD_ERR_INVALID_ARGUMENT;
+  if (!s) return false;
+  if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->seq_len < 1) return false;
+  if (s->reserved0 != 0 || s->reserved1 != 0 || s->total_tokens < 0) return false;
+  if (s->seq_len > kMaxSeq) { *why = LD_ERR_UNSUPPORTED; return false; }
+  if (s->num_q_heads > 64) { *why = LD_ERR_UNSUPPORTED; return false; }
+  if (s->num_q_heads % s->num_kv_heads != 0) return false;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) { *why = LD_ERR_UNSUPPORTED; return false; }
+  if (s->head_dim != 64 && s->head_dim != 128) { *why = LD_ERR_UNSUPPORTED; return false; }
+  if (!s->kv_indptr && s->total_tokens != 0 &&
+      s->total_tokens < (int64_t)s->batch * s->seq_len)
+    return false;
+  if (!(std::isfinite(s->softmax_scale))) return false;
+  return true;
+}
+
+LayerLayout layer_layout(const ld_shape* s) {
+  LayerLayout L{};
+  const int N = s->seq_len;
+  L.slots = s->batch * s->num_q_heads;
+  L.P = (N + 255) / 256;
+  if (L.P > kMaxSplits) L.P = kMaxSplits;
+  L.C = (N + kSelChunk - 1) / kSelChunk;
+  L.W = (N + 31) / 32;
+  L.ncap = N;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  L.attn_tickets = take((size_t)s->batch * s->num_kv_heads * 4);
+  L.sel_tickets = take((size_t)L.slots * 4);
+  L.hist1 = take((size_t)L.slots * kHist1Bins * 4);
+  L.hist2 = take((size_t)L.slots * kHist2Bins * 4);
+  L.cand_count = take((size_t)L.slots * 4);
+  L.sel_info = take((size_t)L.slots * 16);
+  L.chunk_cnt = take((size_t)L.slots * L.C * 8);
+  L.cand_key = take((size_t)L.slots * L.ncap * 4);
+  L.cand_idx = take((size_t)L.slots * L.ncap * 4);
+  L.logits = take((size_t)L.slots * N * 4);
+  L.part_ml = take((size_t)L.slots * L.P * 8);
+  L.part_acc = take((size_t)L.slots * L.P * s->head_dim * 4);
+  L.bitmaps = take((size_t)L.slots * L.W * 4);
+  L.total = o;
+  return L;
+}
+
+SelLayout sel_layout(int rows, int n) {
+  SelLayout L{};
+  const int C = (n + kSelChunk - 1) / kSelChunk;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  L.tickets = take((size_t)rows * 4);
+  L.hist1 = take((size_t)rows * kHist1Bins * 4);
+  L.hist2 = take((size_t)rows * kHist2Bins * 4);
+  L.cand_count = take((size_t)rows * 4);
+  L.sel_info = take((size_t)rows * 16);
+  L.chunk_cnt = take((size_t)rows * C * 8);
+  L.cand_key = take((size_t)rows * n * 4);
+  L.cand_idx = take((size_t)rows * n * 4);
+  L.total = o;
+  return L;
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+// Rows per attention split: 256 << v. Automatic choice: the smallest split that keeps
+// the launch at or below ~2 workgroups' worth per compute unit times 2 (about 1024
+// workgroups), capped so that no sequence needs more than kMaxSplits splits.
+int choose_split_rows(int N, int64_t groups_total, uint32_t flags) {
+  int v = (int)((flags >> 8) & 0xfu);
+  int ts;
+  if (v >= 1 && v <= 4) {
+    ts = 256 << (v - 1);
+  } else {
+    ts = 256;
+    while (ts < kMaxSplitRows && groups_total * (int64_t)((N + ts - 1) / ts) > 1024) ts <<= 1;
+  }
+  while ((N + ts - 1) / ts > kMaxSplits && ts < kMaxSplitRows) ts <<= 1;
+  return ts;
+}
+
+// Core of the three layer entry points.
+// active: heads computed; retrieval: heads attending to all rows (subset of active).
+ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, const void* q,
+                    const void* kc, const void* vc, int32_t k, const int32_t* s_in,
+                    int32_t* s_out, const int64_t* s_indptr, float* scores_out, void* out,
+                    uint32_t flags, bool want_topk, void* ws, size_t ws_bytes, hipStream_t st) {
+  ld_status why;
+  if (!shape_ok(shape, &why)) return why;
+  const int B = shape->batch, Hq = shape->num_q_heads, Hkv = shape->num_kv_heads;
+  const int D = shape->head_dim, G = Hq / Hkv, N = shape->seq_len;
+  const uint64_t all = (Hq == 64) ? ~0ull : ((1ull << Hq) - 1ull);
+  if ((active & ~all) || (retrieval & ~active)) return LD_ERR_INVALID_ARGUMENT;
+  if (!q || !kc || !vc || !out) return LD_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(out)) return LD_ERR_INVALID_ARGUMENT;
+  if (k < 1 || k > N) return LD_ERR_INVALID_ARGUMENT;
+  const uint64_t sparse = active & ~retrieval;
+  const bool do_topk = want_topk && retrieval != 0;
+  if (sparse && !s_in) return LD_ERR_INVALID_ARGUMENT;
+  if (do_topk && !s_out) return LD_ERR_INVALID_ARGUMENT;
+  if ((s_in && ((uintptr_t)s_in & 3u)) || (s_out && ((uintptr_t)s_out & 3u))) return LD_ERR_INVALID_ARGUMENT;
+  if (scores_out && ((uintptr_t)scores_out & 3u)) return LD_ERR_INVALID_ARGUMENT;
+  const LayerLayout L = layer_layout(shape);
+  if (!ws || ws_bytes < L.total || ((uintptr_t)ws & 15u)) return LD_ERR_WORKSPACE;
+  if (active == 0) return LD_OK;
+
+  int64_t T = shape->total_tokens;
+  if (T == 0) T = (int64_t)B * N;
+  const float scale = shape->softmax_scale > 0.f ? shape->softmax_scale : 1.0f / std::sqrt((float)D);
+
+  // heads lists
+  uint8_t sp_heads[64], ret_heads[64];
+  int nsp = 0, nret = 0;
+  for (int h = 0; h < Hq; ++h) {
+    if (sparse >> h & 1ull) sp_heads[nsp++] = (uint8_t)h;
+    if (retrieval >> h & 1ull) ret_heads[nret++] = (uint8_t)h;
+  }
+  uint32_t* bitmaps = at<uint32_t>(ws, L.bitmaps);
+
+  // 1. membership bitmaps of the sparse heads (unless the caller chains them)
+  if (nsp && !(flags & LD_FLAG_S_CHAINED)) {
+    BitmapParams bp{};
+    bp.s = s_in; bp.s_indptr = s_indptr; bp.k_dense = k;
+    bp.kv_indptr = shape->kv_indptr; bp.seq_len = N;
+    bp.Hq = Hq; bp.nsp = nsp;
+    std::memcpy(bp.heads, sp_heads, sizeof(sp_heads));
+    bp.bitmaps = bitmaps; bp.W = L.W;
+    bp.wblocks = (L.W + kBitmapWordsPerBlock - 1) / kBitmapWordsPerBlock;
+    if (launch_bitmap_build(bp, B * nsp, st) != hipSuccess) return LD_ERR_HIP;
+  }
+  // 2. S^{l+1} = S^{l} for sparse heads when the output buffer is a different one
+  if (nsp && s_out && s_out != s_in) {
+    CopyParams cp{};
+    cp.src = s_in; cp.dst = s_out; cp.s_indptr = s_indptr; cp.k_dense = k;
+    cp.Hq = Hq; cp.nsp = nsp;
+    std::memcpy(cp.heads, sp_heads, sizeof(sp_heads));
+    if (launch_copy_rows(cp, B * nsp, st) != hipSuccess) return LD_ERR_HIP;
+  }
+  // 3. attention (+ fused first selection digit)
+  AttnParams ap{};
+  ap.q = static_cast<const uint16_t*>(q);
+  ap.kc = static_cast<const uint16_t*>(kc);
+  ap.vc = static_cast<const uint16_t*>(vc);
+  ap.out = static_cast<uint16_t*>(out);
+  ap.kv_indptr = shape->kv_indptr;
+  ap.kv_head_stride = T * D;
+  ap.total_tokens = T;
+  ap.B = B; ap.Hq = Hq; ap.Hkv = Hkv; ap.seq_len = N;
+  ap.scale = scale;
+  ap.active = active; ap.retrieval = retrieval;
+  int ng = 0;
+  for (int g = 0; g < Hkv; ++g) {
+    const uint64_t gm = ((G == 64) ? ~0ull : ((1ull << G) - 1ull)) << (g * G);
+    if (active & gm) ap.groups[ng++] = (uint8_t)g;
+  }
+  ap.ngroups = ng;
+  ap.ts = choose_split_rows(N, (int64_t)B * ng, flags);
+  ap.nsplit = (N + ap.ts - 1) / ap.ts;
+  ap.bitmaps = bitmaps; ap.W = L.W;
+  ap.logits = scores_out ? scores_out : (do_topk ? at<float>(ws, L.logits) : nullptr);
+  ap.part_ml = at<float>(ws, L.part_ml);
+  ap.part_acc = at<float>(ws, L.part_acc);
+  ap.P = L.P;
+  ap.tickets = at<uint32_t>(ws, L.attn_tickets);
+  ap.do_topk = do_topk ? 1 : 0;
+  ap.hist1 = at<uint32_t>(ws, L.hist1);
+  ap.sel_info = at<uint32_t>(ws, L.sel_info);
+  ap.k_dense = k;
+  ap.s_indptr = s_indptr;
+  const dim3 grid((unsigned)((int64_t)B * ng * ap.nsplit));
+  if (launch_attention(ap, D, G, grid, st) != hipSuccess) return LD_ERR_HIP;
+
+  // 4. argsTopK of the retrieval rows
+  if (do_topk) {
+    SelParams sp{};
+    sp.mode = 1;
+    sp.nrows = B * nret;
+    sp.C = L.C;
+    sp.logits = ap.logits; sp.Hq = Hq; sp.seq_len = N; sp.kv_indptr = shape->kv_indptr;
+    sp.s_out = s_out; sp.s_indptr = s_indptr; sp.k_dense = k;
+    sp.bitmaps = bitmaps; sp.W = L.W;
+    sp.nret = nret;
+    std::memcpy(sp.heads, ret_heads, sizeof(ret_heads));
+    sp.hist1 = at<uint32_t>(ws, L.hist1);
+    sp.hist2 = at<uint32_t>(ws, L.hist2);
+    sp.tickets = at<uint32_t>(ws, L.sel_tickets);
+    sp.sel_info = at<uint32_t>(ws, L.sel_info);
+    sp.cand_count = at<uint32_t>(ws, L.cand_count);
+    sp.chunk_cnt = at<uint32_t>(ws, L.chunk_cnt);
+    sp.cand_key = at<uint32_t>(ws, L.cand_key);
+    sp.cand_idx = at<int32_t>(ws, L.cand_idx);
+    sp.ncap = L.ncap;
+    if (launch_select(sp, st, false) != hipSuccess) return LD_ERR_HIP;
+  }
+  return LD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ld_status_string(ld_status status) {
+  switch (status) {
+    case LD_OK: return "ok";
+    case LD_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case LD_ERR_UNSUPPORTED: return "unsupported shape";
+    case LD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case LD_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t ld_workspace_size(const ld_shape* shape, int32_t k_max) {
+  ld_status why;
+  if (!shape_ok(shape, &why) || k_max < 1 || k_max > shape->seq_len) return 0;
+  return layer_layout(shape).total;
+}
+
+size_t ld_topk_workspace_size(int32_t rows, int32_t n) {
+  if (rows < 1 || n < 1 || n > kMaxSeq) return 0;
+  return sel_layout(rows, n).total;
+}
+
+ld_status ld_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace || workspace_bytes == 0) return LD_ERR_WORKSPACE;
+  return launch_zero(workspace, workspace_bytes, stream) == hipSuccess ? LD_OK : LD_ERR_HIP;
+}
+
+ld_status ld_retrieval_decode(const ld_shape* shape, uint64_t head_mask, const void* q,
+                              const void* k_cache, const void* v_cache, int32_t k,
+                              int32_t* s_out, const int64_t* s_indptr, float* scores_out,
+                              void* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  return run_layer(shape, head_mask, head_mask, q, k_cache, v_cache, k, nullptr, s_out, s_indptr,
+                   scores_out, out, 0u, s_out != nullptr, workspace, workspace_bytes, stream);
+}
+
+ld_status ld_sparse_decode(const ld_shape* shape, uint64_t head_mask, const void* q,
+                           const void* k_cache, const void* v_cache, int32_t k,
+                           const int32_t* s_in, const int64_t* s_indptr, void* out,
+                           uint32_t flags, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (head_mask && !s_in) return LD_ERR_INVALID_ARGUMENT;
+  return run_layer(shape, head_mask, 0ull, q, k_cache, v_cache, k, s_in, nullptr, s_indptr,
+                   nullptr, out, flags, false, workspace, workspace_bytes, stream);
+}
+
+ld_status ld_hybrid_layer(const ld_shape* shape, uint64_t retrieval_mask, const void* q,
+                          const void* k_cache, const void* v_cache, int32_t k,
+                          const int32_t* s_in, int32_t* s_out, const int64_t* s_indptr,
+                          float* scores_out, void* out, uint32_t flags, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  ld_status why;
+  if (!shape_ok(shape, &why)) return why;
+  const int Hq = shape->num_q_heads;
+  const uint64_t all = (Hq == 64) ? ~0ull : ((1ull << Hq) - 1ull);
+  if (retrieval_mask & ~all) return LD_ERR_INVALID_ARGUMENT;
+  return run_layer(shape, all, retrieval_mask, q, k_cache, v_cache, k, s_in, s_out, s_indptr,
+                   scores_out, out, flags, !(flags & LD_FLAG_SKIP_TOPK), workspace,
+                   workspace_bytes, stream);
+}
+
+ld_status ld_topk_select(const float* scores, int32_t rows, int32_t n, int64_t row_stride,
+                         int32_t k, int32_t* idx_out, float* val_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (!scores || !idx_out || rows < 1 || n < 1 || n > kMaxSeq || k < 1 || k > n ||
+      row_stride < n)
+    return LD_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)scores & 3u) || ((uintptr_t)idx_out & 3u) || (val_out && ((uintptr_t)val_out & 3u)))
+    return LD_ERR_INVALID_ARGUMENT;
+  const SelLayout L = sel_layout(rows, n);
+  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 15u)) return LD_ERR_WORKSPACE;
+  SelParams sp{};
+  sp.mode = 0;
+  sp.nrows = rows;
+  sp.C = (n + kSelChunk - 1) / kSelChunk;
+  sp.scores = scores; sp.row_stride = row_stride; sp.n = n; sp.k = k;
+  sp.idx_out = idx_out; sp.val_out = val_out;
+  sp.hist1 = at<uint32_t>(workspace, L.hist1);
+  sp.hist2 = at<uint32_t>(workspace, L.hist2);
+  sp.tickets = at<uint32_t>(workspace, L.tickets);
+  sp.sel_info = at<uint32_t>(workspace, L.sel_info);
+  sp.cand_count = at<uint32_t>(workspace, L.cand_count);
+  sp.chunk_cnt = at<uint32_t>(workspace, L.chunk_cnt);
+  sp.cand_key = at<uint32_t>(workspace, L.cand_key);
+  sp.cand_idx = at<int32_t>(workspace, L.cand_idx);
+  sp.ncap = n;
+  return launch_select(sp, stream, true) == hipSuccess ? LD_OK : LD_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Internal definitions shared by the gfx950 kernels and the host launcher of
+// liblychee_decode.so. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ld {
+
+// ---------------------------------------------------------------- constants
+
+constexpr int kThreads = 256;          // every kernel runs 4 wave64s per workgroup
+constexpr int kMaxSplitRows = 2048;    // largest attention split (rows per workgroup)
+constexpr int kSelChunk = 512;         // scores per select workgroup (2 per thread)
+constexpr int kHist1Bins = 2048;       // digit 1: key bits 31..21
+constexpr int kHist2Bins = 2048;       // digit 2: key bits 20..10
+constexpr int kHist3Bins = 1024;       // digit 3: key bits 9..0
+constexpr int kMaxSeq = 1 << 21;       // seq_len limit
+constexpr int kMaxSelChunks = kMaxSeq / kSelChunk;   // 4096
+constexpr int kMaxSplits = 1024;       // attention splits per sequence
+constexpr int kBitmapWordsPerBlock = 4096;           // bitmap-build LDS tile (16 KiB)
+
+// ---------------------------------------------------------------- parameters
+
+// Attention over one layer: workgroup = (sequence b, KV group, split of rows).
+struct AttnParams {
+  const uint16_t* q;      // bf16 [B][Hq][D]
+  const uint16_t* kc;     // bf16 [Hkv][T][D]
+  const uint16_t* vc;
+  uint16_t* out;          // bf16 [B][Hq][D]
+  const int64_t* kv_indptr;
+  int64_t kv_head_stride; // T*D elements
+  int64_t total_tokens;   // T
+  int B, Hq, Hkv, seq_len;
+  float scale;            // logit scale
+  uint64_t active;        // heads computed by this launch
+  uint64_t retrieval;     // heads attending to every row (subset of active)
+  int ts;                 // rows per split (multiple of 256)
+  int nsplit;             // splits per sequence at seq_len (grid stride)
+  int ngroups;            // KV groups launched
+  uint8_t groups[64];     // their ids
+  const uint32_t* bitmaps;   // [B*Hq][W] membership bits of sparse heads
+  int W;
+  float* logits;          // [B*Hq][seq_len] scores of retrieval heads, or null
+  float* part_ml;         // [B*Hq][P][2]  (max in log2 units, sum)
+  float* part_acc;        // [B*Hq][P][D]
+  int P;                  // partial stride in splits
+  uint32_t* tickets;      // [B*Hkv], zero between calls
+  // fused first selection digit (only when do_topk)
+  int do_topk;
+  uint32_t* hist1;        // [B*Hq][kHist1Bins], zero between calls
+  uint32_t* sel_info;     // [B*Hq][4]
+  int k_dense;
+  const int64_t* s_indptr;
+};
+
+// argsTopK over rows. Row slots index the per-row workspace arrays.
+struct SelParams {
+  int mode;               // 0: standalone rows, 1: retrieval rows of a layer
+  int nrows;              // rows launched
+  int C;                  // chunk-grid stride (chunks per row at max length)
+  // standalone
+  const float* scores; int64_t row_stride; int n; int k; int32_t* idx_out; float* val_out;
+  // layer rows: row r -> (b = r / nret, h = heads[r % nret])
+  const float* logits; int Hq; int seq_len; const int64_t* kv_indptr;
+  int32_t* s_out; const int64_t* s_indptr; int k_dense;
+  uint32_t* bitmaps; int W;
+  int nret; uint8_t heads[64];
+  // workspace
+  uint32_t* hist1;        // [slots][kHist1Bins]
+  uint32_t* hist2;        // [slots][kHist2Bins]
+  uint32_t* tickets;      // [slots]
+  uint32_t* sel_info;     // [slots][4]: b1, k1, T, i_tie
+  uint32_t* cand_count;   // [slots]
+  uint32_t* chunk_cnt;    // [slots][C][2]: greater-than count, output offset
+  uint32_t* cand_key;     // [slots][ncap]
+  int32_t* cand_idx;      // [slots][ncap]
+  int64_t ncap;
+};
+
+// Build membership bitmaps of sparse heads from S rows.
+struct BitmapParams {
+  const int32_t* s; const int64_t* s_indptr; int k_dense;
+  const int64_t* kv_indptr; int seq_len;
+  int Hq; int nsp; uint8_t heads[64];   // row r -> (b = r / nsp, h = heads[r % nsp])
+  uint32_t* bitmaps; int W;
+  int wblocks;                          // word tiles per row
+};
+
+struct CopyParams {
+  const int32_t* src; int32_t* dst; const int64_t* s_indptr; int k_dense;
+  int Hq; int nsp; uint8_t heads[64];
+};
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_attention(const AttnParams& p, int D, int G, dim3 grid, hipStream_t st);
+hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist);
+hipError_t launch_bitmap_build(const BitmapParams& p, int rows, hipStream_t st);
+hipError_t launch_copy_rows(const CopyParams& p, int rows, hipStream_t st);
+hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t st);
+
+}  // namespace ld

@@ -1,0 +1,162 @@
+/*
+ * lychee_decode.h -- C ABI of the MI355X (gfx950) hybrid-head sparse decode step.
+ *
+ * The method (LycheeDecode; "LycheeDecode: Accelerating Long-Context LLM Inference
+ * via Hybrid-Head Sparse Decoding", summary page of arXiv 2602.04541, method
+ * paragraph): for one decode token, every attention head of every layer is either a
+ * RETRIEVAL head or a SPARSE head (the inference-time split E[z] > 0.5 of method
+ * step 7 is supplied by the caller as a bit mask). Every head of layer 0 is a
+ * retrieval head (step 1).
+ *   - A retrieval head computes full attention softmax(q K^T / sqrt(d_k)) V over its
+ *     whole KV cache and hands S = argsTopK(scores, k), a set of k token indices, to
+ *     the head at the same position in the next layer (step 3).
+ *   - A sparse head attends only to K[S], V[S] of its own layer's cache and forwards
+ *     S unchanged (step 4).
+ * For HySparse-style stacks ("HySparse: A Hybrid Sparse Attention Architecture
+ * with Oracle Token Selection and KV Cache Sharing", section 3) the caller passes the
+ * full layer's K/V pointers to the sparse layers.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or synchronises. Every call is asynchronous on `stream`.
+ *  - bf16 tensors are 16-byte aligned:
+ *      Q   [B][Hq][d]          (one decode token per sequence)
+ *      K,V [Hkv][T][d]         (one layer; sequence b owns token rows
+ *                               [kv_indptr[b], kv_indptr[b+1]) or [b*N, (b+1)*N))
+ *      O   [B][Hq][d]
+ *    Query head h reads KV head h / (Hq/Hkv).
+ *  - S (int32, indices local to the sequence, in [0, N_b)):
+ *      dense: [B][Hq][k];  CSR: row (b,h) = s[s_indptr[b*Hq+h] .. s_indptr[b*Hq+h+1]),
+ *      s_indptr is a device int64 array of B*Hq+1 entries and the row length is that
+ *      row's k. S rows written by this library are ascending. S rows read by it must
+ *      hold distinct in-range entries (any order); entries outside [0, N_b) are
+ *      ignored and duplicates count once.
+ *  - The head-type mask is a uint64 passed by value: bit h set = retrieval head.
+ *  - Top-k order: larger score first; equal scores -> lower index first; -0.0 equals
+ *    +0.0; NaN ranks below every number. Scores are the fp32 logits q.k * scale.
+ *  - Workspace: caller-owned device memory of at least ld_workspace_size() bytes
+ *    (ld_topk_workspace_size() for ld_topk_select), 256-byte aligned. It must be
+ *    zeroed once with ld_workspace_init() before its first use; every completed call
+ *    leaves it zeroed again, except for the S bitmaps that LD_FLAG_S_CHAINED relies
+ *    on. Calls that share a workspace must be ordered (same stream); concurrent
+ *    calls need separate workspaces.
+ *  - Errors: arguments are validated on the host before any launch; a failing check
+ *    returns an error code and launches nothing. Launch failures return LD_ERR_HIP.
+ *    Faults inside kernels surface at the caller's next synchronisation. Per-sequence
+ *    device-side values (kv_indptr, s_indptr) are preconditions: N_b >= 1 and
+ *    1 <= k_{b,h} <= N_b; the kernels clamp k to N_b and never write outside a row.
+ */
+#ifndef LYCHEE_DECODE_H
+#define LYCHEE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ld_status;
+enum {
+  LD_OK = 0,
+  LD_ERR_INVALID_ARGUMENT = 1,  /* null pointer, bad size, misalignment, k out of range */
+  LD_ERR_UNSUPPORTED = 2,       /* head_dim not 64/128, group size not 1/2/4/8, Hq > 64 */
+  LD_ERR_WORKSPACE = 3,         /* workspace missing or smaller than required */
+  LD_ERR_HIP = 4                /* a HIP launch failed */
+};
+
+/* Flags (bitwise OR). */
+enum {
+  /* Skip argsTopK for the retrieval heads (e.g. the last layer of a step); S and the
+     workspace bitmaps are then left unchanged for those heads. */
+  LD_FLAG_SKIP_TOPK = 1u << 0,
+  /* The caller promises that s_in is the s_out written by the previous call on this
+     workspace with the same shape, so the workspace's per-head membership bitmaps
+     already describe s_in and need not be rebuilt. */
+  LD_FLAG_S_CHAINED = 1u << 1
+};
+/* Optional split-size override in bits 8..11: rows per split = 256 << v (v = 1..4;
+   0 = automatic). */
+#define LD_FLAG_SPLIT_ROWS(v) ((uint32_t)(v) << 8)
+
+typedef struct ld_shape {
+  int32_t batch;          /* B >= 1 */
+  int32_t num_q_heads;    /* Hq, 1..64 */
+  int32_t num_kv_heads;   /* Hkv, divides Hq; Hq/Hkv in {1,2,4,8} */
+  int32_t head_dim;       /* d in {64, 128} */
+  int32_t seq_len;        /* N (uniform) or max_b N_b (ragged), 1..2097152 */
+  int32_t reserved0;      /* must be 0 */
+  int64_t total_tokens;   /* T: token rows per KV head in K/V (the head stride, in
+                             rows); 0 selects batch*seq_len. Must cover every
+                             sequence's rows. */
+  const int64_t* kv_indptr; /* device [B+1] token offsets, or NULL for uniform N */
+  float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t reserved1;      /* must be 0 */
+} ld_shape;
+
+/* Human-readable text of a status code (static storage). */
+const char* ld_status_string(ld_status status);
+
+/* Bytes of workspace needed by ld_retrieval_decode / ld_sparse_decode /
+   ld_hybrid_layer for this shape and a dense/CSR row length of at most k_max.
+   Returns 0 for an invalid shape. */
+size_t ld_workspace_size(const ld_shape* shape, int32_t k_max);
+
+/* Bytes of workspace needed by ld_topk_select for `rows` rows of `n` scores. */
+size_t ld_topk_workspace_size(int32_t rows, int32_t n);
+
+/* Zero a workspace (a fill kernel on `stream`; safe to capture in a HIP graph). */
+ld_status ld_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Retrieval heads (method step 3): for every head h with bit h of head_mask set,
+   O[b][h] = softmax(q K^T * scale) V over all N_b rows of its KV head, and, when
+   s_out is non-NULL, S row (b,h) = argsTopK(scores, k) in ascending order (dense
+   [B][Hq][k] or CSR through s_indptr). When scores_out is non-NULL the fp32 logits of
+   the computed heads are written to scores_out [B][Hq][seq_len] (row-major; entries
+   past N_b untouched). Heads outside head_mask are not touched. */
+ld_status ld_retrieval_decode(const ld_shape* shape, uint64_t head_mask,
+                              const void* q, const void* k_cache, const void* v_cache,
+                              int32_t k, int32_t* s_out, const int64_t* s_indptr,
+                              float* scores_out, void* out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Sparse heads (method step 4): for every head h with bit h of head_mask set,
+   O[b][h] = softmax(q K[S]^T * scale) V[S] over the rows of S row (b,h). S is not
+   modified. flags: LD_FLAG_S_CHAINED. */
+ld_status ld_sparse_decode(const ld_shape* shape, uint64_t head_mask,
+                           const void* q, const void* k_cache, const void* v_cache,
+                           int32_t k, const int32_t* s_in, const int64_t* s_indptr,
+                           void* out, uint32_t flags,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One full layer of the recurrence (method steps 3 and 4) for all Hq heads:
+   retrieval heads (bits of retrieval_mask) attend to all rows and write their
+   argsTopK rows into s_out; sparse heads attend to S row (b,h) of s_in and S^{l+1} =
+   S^{l} for them (s_out may alias s_in; otherwise their rows are copied). s_in may be
+   NULL only when every head is a retrieval head (layer 0, method step 1). A KV head
+   whose query heads include a retrieval head streams its whole cache once for all of
+   them; a KV head serving only sparse heads reads the union of their sets once.
+   flags: LD_FLAG_SKIP_TOPK, LD_FLAG_S_CHAINED, LD_FLAG_SPLIT_ROWS(). scores_out as in
+   ld_retrieval_decode (retrieval heads only; may be NULL). */
+ld_status ld_hybrid_layer(const ld_shape* shape, uint64_t retrieval_mask,
+                          const void* q, const void* k_cache, const void* v_cache,
+                          int32_t k, const int32_t* s_in, int32_t* s_out,
+                          const int64_t* s_indptr, float* scores_out, void* out,
+                          uint32_t flags, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Standalone argsTopK (method step 3) on fp32 scores: for each of `rows` rows of `n`
+   values (row r starts at scores + r*row_stride), writes the k selected indices in
+   ascending order to idx_out[r*k .. r*k+k) and, when val_out is non-NULL, their
+   scores to val_out (same positions). Bit-exact: the result depends only on the fp32
+   values and the order stated above. Requires 1 <= k <= n, row_stride >= n. */
+ld_status ld_topk_select(const float* scores, int32_t rows, int32_t n, int64_t row_stride,
+                         int32_t k, int32_t* idx_out, float* val_out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LYCHEE_DECODE_H */

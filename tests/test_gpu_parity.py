@@ -1,0 +1,194 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on the
+same bf16 inputs, layer by layer with teacher forcing (the oracle consumes the S the
+GPU handed to the layer), over shapes that span several splits, ragged tails, MHA and
+grouped KV heads, mixed and sparse-only groups."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import lychee_oracle as orc
+from tests import gpu_helpers as gh
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _ld():
+    import hybrid_head_sparse_retrieval_amd as ld
+    ld.load_library()
+    return ld
+
+
+def run_layers(B, Hq, Hkv, d, lens, masks, seed, k=None, csr=False, chain=True, split=0,
+               check=True, frac=0.3):
+    """Run len(masks) layers on the GPU and check every layer against the oracle."""
+    ld = _ld()
+    dev = "cuda"
+    L = len(masks)
+    lens = list(lens)
+    N = max(lens)
+    ragged = len(set(lens)) > 1 or csr
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(offs[-1])
+    kb = [min(k, n) if k is not None else max(1, int(frac * n)) for n in lens]
+    kv_indptr = torch.as_tensor(offs, device=dev) if ragged else None
+    if csr:
+        rows = [kb[b] for b in range(B) for _ in range(Hq)]
+        s_indptr_h = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+        s_indptr = torch.as_tensor(s_indptr_h, device=dev)
+        S = torch.zeros(int(s_indptr_h[-1]), dtype=torch.int32, device=dev)
+        kmax = max(kb)
+    else:
+        assert len(set(kb)) == 1
+        s_indptr_h, s_indptr = None, None
+        S = torch.zeros((B, Hq, kb[0]), dtype=torch.int32, device=dev)
+        kmax = kb[0]
+    layers = [wl.random_qkv(B, Hq, Hkv, d, T, seed * 100 + l) for l in range(L)]
+    shape = ld.make_shape(layers[0][0].to(dev), layers[0][1].to(dev), kv_indptr, N)
+    ws = ld.Workspace(shape, kmax, dev)
+    scores = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device=dev)
+    results = []
+    for l in range(L):
+        qc, kc, vc = layers[l]
+        q, kk, vv = qc.to(dev), kc.to(dev), vc.to(dev)
+        S_before = S.cpu().numpy().copy()
+        out = torch.empty_like(q)
+        flags = (ld.FLAG_S_CHAINED if (chain and l > 0) else 0) | ld.flag_split_rows(split)
+        ld.hybrid_layer(q, kk, vv, masks[l], kmax, S if l > 0 else None, s_out=S, s_indptr=s_indptr,
+                        scores_out=scores, out=out, flags=flags, workspace=ws,
+                        kv_indptr=kv_indptr, seq_len=N)
+        torch.cuda.synchronize()
+        S_after = S.cpu().numpy()
+        sc = scores.cpu().numpy()
+        results.append((out.clone(), S_after.copy()))
+        if not check:
+            continue
+        ret = [bool(masks[l] >> h & 1) for h in range(Hq)]
+        S_in = None if l == 0 else gh.s_rows_to_dict(S_before, B, Hq, s_indptr_h)
+        O_ref, S_ref, sc_ref = orc.hybrid_layer_bf16(
+            wl.bf16_bits(qc), wl.bf16_bits(kc), wl.bf16_bits(vc), offs, ret, kb, S_in)
+        gh.check_outputs(out, O_ref, [(b, h) for b in range(B) for h in range(Hq)], f"layer {l}")
+        S_dict = gh.s_rows_to_dict(S_after, B, Hq, s_indptr_h)
+        for b in range(B):
+            for h in range(Hq):
+                if ret[h]:
+                    gh.check_selected_row(S_dict[(b, h)], sc[b, h, :lens[b]], sc_ref[(b, h)], kb[b])
+                else:
+                    assert np.array_equal(S_dict[(b, h)], S_in[(b, h)]), "sparse row changed"
+    return results
+
+
+@pytest.mark.parametrize("case", [
+    # B, Hq, Hkv, d, lens, masks (layer 0 all retrieval), seed
+    (1, 8, 2, 128, [5000], [0xFF, 0b00100001, 0, 0b1000], 1),      # GQA 4:1, mixed + sparse-only groups
+    (2, 4, 4, 64, [3000, 3000], [0xF, 0b0010, 0], 2),               # MHA d=64
+    (1, 16, 2, 128, [1100], [0xFFFF, 0x0101, 0], 3),                 # GQA 8:1
+    (1, 8, 4, 64, [2049], [0xFF, 0b01000010, 0], 4),                 # GQA 2:1, tail of 1 row
+    (1, 32, 8, 128, [4096], wl.seeded_masks(5, 3, 32, 2), 5),        # Llama head shape
+])
+def test_layers_match_oracle(case):
+    B, Hq, Hkv, d, lens, masks, seed = case
+    run_layers(B, Hq, Hkv, d, lens, masks, seed)
+
+
+def test_ragged_csr_batch():
+    run_layers(3, 8, 2, 128, [777, 2100, 1500], [0xFF, 0b10000100, 0], 6, csr=True)
+
+
+def test_unchained_equals_chained():
+    a = run_layers(1, 8, 2, 128, [3000], [0xFF, 0b00010000, 0], 7, chain=True, check=False)
+    b = run_layers(1, 8, 2, 128, [3000], [0xFF, 0b00010000, 0], 7, chain=False, check=True)
+    for (oa, sa), (ob, sb) in zip(a, b):
+        assert torch.equal(oa, ob) and np.array_equal(sa, sb)
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 31, 257, 513])
+def test_small_and_tail_lengths(n):
+    k = max(1, (3 * n) // 10)
+    run_layers(1, 4, 2, 128, [n], [0xF, 0b0001, 0], 10 + n, k=k)
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 4])
+def test_split_size_invariance(split):
+    run_layers(1, 8, 2, 128, [6000], [0xFF, 0b00000010, 0], 11, split=split)
+
+
+def test_deterministic_and_batch_permutation():
+    ld = _ld()
+    dev = "cuda"
+    Hq, Hkv, d = 8, 2, 128
+    lens = [900, 2500, 1700]
+    k = 250
+    perm = [2, 0, 1]
+    q, kc, vc = wl.random_qkv(3, Hq, Hkv, d, sum(lens), 12)
+    offs = np.concatenate([[0], np.cumsum(lens)])
+
+    def run(q, kc, vc, lens):
+        offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        kvi = torch.as_tensor(offs, device=dev)
+        qd, kd, vd = q.to(dev), kc.to(dev), vc.to(dev)
+        shape = ld.make_shape(qd, kd, kvi, max(lens))
+        ws = ld.Workspace(shape, k, dev)
+        S = torch.zeros((3, Hq, k), dtype=torch.int32, device=dev)
+        out0 = ld.hybrid_layer(qd, kd, vd, 0xFF, k, None, s_out=S, workspace=ws, kv_indptr=kvi, seq_len=max(lens))
+        out1 = ld.hybrid_layer(qd, kd, vd, 0b00100000, k, S, workspace=ws, kv_indptr=kvi, seq_len=max(lens),
+                               flags=ld.FLAG_S_CHAINED)
+        torch.cuda.synchronize()
+        return out0.cpu(), out1.cpu(), S.cpu()
+
+    r1 = run(q, kc, vc, lens)
+    r2 = run(q, kc, vc, lens)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b), "run-to-run results differ"
+    kp = torch.cat([kc[:, offs[p]:offs[p + 1]] for p in perm], dim=1)
+    vp = torch.cat([vc[:, offs[p]:offs[p + 1]] for p in perm], dim=1)
+    rp = run(q[perm], kp, vp, [lens[p] for p in perm])
+    for a, b in zip(r1, rp):
+        assert torch.equal(a[perm], b), "batch permutation changed results"
+
+
+def test_sparse_full_set_equals_retrieval_and_single_index():
+    ld = _ld()
+    dev = "cuda"
+    Hq, Hkv, d, n = 8, 2, 128, 3333
+    q, kc, vc = [t.to(dev) for t in wl.random_qkv(1, Hq, Hkv, d, n, 13)]
+    shape = ld.make_shape(q, kc)
+    ws = ld.Workspace(shape, n, dev)
+    full = ld.retrieval_decode(q, kc, vc, 0xFF, n, workspace=ws)
+    S = torch.arange(n, dtype=torch.int32, device=dev).repeat(1, Hq, 1).contiguous()
+    sp = ld.sparse_decode(q, kc, vc, 0xFF, n, S, workspace=ws)
+    torch.cuda.synchronize()
+    O_ref, _, _ = orc.hybrid_layer_bf16(wl.bf16_bits(q), wl.bf16_bits(kc), wl.bf16_bits(vc),
+                                        [0, n], [True] * Hq, [n], None)
+    gh.check_outputs(full, O_ref, [(0, h) for h in range(Hq)])
+    gh.check_outputs(sp, O_ref, [(0, h) for h in range(Hq)])
+    # a single index: weight exactly 1, output is that value row bit for bit
+    pos = torch.tensor([0, 17, 3332, 1666, 5, 900, 2048, 1], dtype=torch.int32, device=dev)
+    S1 = pos.view(1, Hq, 1).contiguous()
+    ws1 = ld.Workspace(shape, 1, dev)
+    o1 = ld.sparse_decode(q, kc, vc, 0xFF, 1, S1, workspace=ws1)
+    torch.cuda.synchronize()
+    for h in range(Hq):
+        assert torch.equal(o1[0, h].cpu(), vc[h // 4, int(pos[h])].cpu())
+
+
+def test_retrieval_decode_subset_of_heads_leaves_others():
+    ld = _ld()
+    dev = "cuda"
+    Hq, Hkv, d, n, k = 8, 2, 64, 2000, 600
+    q, kc, vc = [t.to(dev) for t in wl.random_qkv(1, Hq, Hkv, d, n, 14)]
+    shape = ld.make_shape(q, kc)
+    ws = ld.Workspace(shape, k, dev)
+    out = torch.full_like(q, 7.0)
+    S = torch.full((1, Hq, k), -5, dtype=torch.int32, device=dev)
+    mask = 0b01100100
+    ld.retrieval_decode(q, kc, vc, mask, k, s_out=S, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    O_ref, S_ref, _ = orc.hybrid_layer_bf16(wl.bf16_bits(q), wl.bf16_bits(kc), wl.bf16_bits(vc),
+                                            [0, n], [True] * Hq, [k], None)
+    for h in range(Hq):
+        if mask >> h & 1:
+            gh.check_outputs(out, O_ref, [(0, h)])
+            assert np.all(np.diff(S[0, h].cpu().numpy()) > 0)
+        else:
+            assert torch.all(out[0, h] == 7.0) and torch.all(S[0, h] == -5)

@@ -1,0 +1,103 @@
+"""ld_topk_select must equal the oracle's selection bit for bit on identical fp32
+scores (LycheeDecode summary page, method step 3: S = argsTopK(scores, k); ties go
+to the lower index, -0.0 equals +0.0, NaN ranks last)."""
+import numpy as np
+import pytest
+
+from oracle import lychee_oracle as orc
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _ld():
+    import hybrid_head_sparse_retrieval_amd as ld
+    ld.load_library()
+    return ld
+
+
+def _check(rows_np, k, with_vals=True):
+    ld = _ld()
+    x = torch.as_tensor(np.ascontiguousarray(rows_np, dtype=np.float32), device="cuda")
+    val = torch.empty((x.shape[0], k), dtype=torch.float32, device="cuda") if with_vals else None
+    idx = ld.topk_select(x, k, val_out=val)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for r in range(x.shape[0]):
+        want = orc.select_topk_f32(rows_np[r].astype(np.float32), k)
+        assert np.array_equal(got[r], want), f"row {r}: first mismatch at {np.nonzero(got[r] != want)[0][:5]}"
+        if with_vals:
+            v = val.cpu().numpy()[r]
+            assert np.array_equal(v.view(np.uint32), rows_np[r].astype(np.float32)[want].view(np.uint32))
+
+
+def _rng(s):
+    return np.random.default_rng(s)
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (7, 3), (64, 64), (511, 100), (512, 1), (513, 512),
+                                 (5000, 1500), (32768, 9830), (131072, 39321)])
+def test_random_normal(n, k):
+    _check(_rng(n).normal(size=(3, n)).astype(np.float32), k)
+
+
+def test_constant_rows_take_lowest_indices():
+    for n, k in [(10, 4), (20000, 6000), (1025, 1025)]:
+        _check(np.full((2, n), 0.5, dtype=np.float32), k)
+
+
+def test_signed_zeros_infs_nans_and_duplicates():
+    rng = _rng(1)
+    pool = np.array([-1.0, -0.0, 0.0, 0.5, 2.0, np.inf, -np.inf, np.nan], dtype=np.float32)
+    for n in (9, 300, 4097):
+        rows = pool[rng.integers(0, len(pool), size=(4, n))]
+        for k in sorted({1, 2, n // 3, n // 2, n - 1, n} - {0}):
+            _check(rows, k)
+
+
+def test_sorted_and_reverse_sorted():
+    n = 10000
+    inc = np.arange(n, dtype=np.float32)[None, :]
+    _check(inc, 3000)
+    _check(inc[:, ::-1].copy(), 3000)
+
+
+def test_heavy_ties_at_threshold():
+    # many keys equal to the k-th value: the kept ones are the lowest indices
+    rng = _rng(2)
+    n = 50000
+    x = rng.integers(0, 4, size=(2, n)).astype(np.float32)
+    for k in (1, 12345, 25000, 49999):
+        _check(x, k)
+
+
+def test_near_ties_differ_in_last_bit():
+    base = np.float32(0.7)
+    n = 3000
+    bits = (np.int64(base.view(np.uint32)) + np.arange(-5, 5)).astype(np.uint32)
+    x = np.resize(bits.view(np.float32), n)[None, :]
+    _check(x, 1000)
+
+
+def test_many_rows_and_strided_input():
+    ld = _ld()
+    rng = _rng(3)
+    full = rng.normal(size=(33, 1200)).astype(np.float32)
+    x = torch.as_tensor(full, device="cuda")[:, :1000]     # row stride 1200
+    idx = ld.topk_select(x, 250)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for r in range(33):
+        assert np.array_equal(got[r], orc.select_topk_f32(full[r, :1000], 250))
+
+
+def test_repeated_calls_reuse_workspace():
+    ld = _ld()
+    rng = _rng(4)
+    ws = ld.TopkWorkspace(2, 4000, "cuda")
+    for it in range(5):
+        x = rng.normal(size=(2, 4000)).astype(np.float32)
+        idx = ld.topk_select(torch.as_tensor(x, device="cuda"), 1000 + it, workspace=ws)
+        torch.cuda.synchronize()
+        for r in range(2):
+            assert np.array_equal(idx.cpu().numpy()[r], orc.select_topk_f32(x[r], 1000 + it))

@@ -206,3 +206,26 @@ def random_sorted_sets(seed: int, n: int, k: int, rows: int) -> np.ndarray:
     for r in range(rows):
         out[r] = np.sort(rng.choice(n, size=k, replace=False))
     return out
+
+
+def random_qkv(B: int, Hq: int, Hkv: int, d: int, T: int, seed: int, scale_q: float = 1.0):
+    """Unstructured N(0,1) draws in bf16 (CPU tensors): q [B][Hq][d], k, v [Hkv][T][d]."""
+    import torch
+    g = torch.Generator(device="cpu")
+    g.manual_seed(stream_seed("qkv", seed))
+    q = (torch.randn((B, Hq, d), generator=g) * scale_q).to(torch.bfloat16)
+    k = torch.randn((Hkv, T, d), generator=g).to(torch.bfloat16)
+    v = torch.randn((Hkv, T, d), generator=g).to(torch.bfloat16)
+    return q, k, v
+
+
+def seeded_masks(seed: int, layers: int, hq: int, per_layer: int) -> list:
+    """Layer 0 all retrieval, then `per_layer` seeded retrieval heads in each later layer."""
+    rng = np.random.Generator(np.random.PCG64(stream_seed("masks", seed)))
+    out = [(1 << hq) - 1]
+    for _ in range(1, layers):
+        m = 0
+        for h in rng.choice(hq, size=min(per_layer, hq), replace=False):
+            m |= 1 << int(h)
+        out.append(m)
+    return out
