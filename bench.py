@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid-head sparse decode step on one MI355X.
+
+A step is one pass of every layer of the workload (attention of retrieval and sparse
+heads, argsTopK of the retrieval heads, S hand-over) for one decode token, with all
+inputs already resident in HBM. Prints ONE JSON line (rank 0).
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Metric: effective HBM GB/s of the step = algorithmic bytes / step time, where the
+algorithmic bytes of a layer are
+  sum over (b, KV group g): 2*N_b*d*2 if g serves a retrieval head, else
+                            |union of the group's S rows|*2*d*2
+  + Q and O (B*Hq*d*2 each) + S reads of sparse heads and S writes of retrieval
+  heads (k_b*4 each).
+The roofline object is for the attention kernel (the dominant kernel): its
+algorithmic bytes (KV + Q + O) per launch over its average launch duration, timed
+with HIP events on the launch stream in a pass where each layer's attention kernel
+runs alone (LD_FLAG_SKIP_TOPK; the untimed full layer follows to advance S).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b_32k")
+    ap.add_argument("--split", type=int, default=0, help="rows per split = 256<<(v-1), 0 = auto")
+    ap.add_argument("--waves", type=int, default=0, help="attention waves per workgroup: 1 = 4, 2 = 8, 0 = auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--no-kernel-pass", action="store_true")
+    ap.add_argument("--layers-detail", action="store_true", help="print per-layer times to stderr")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def layer_bytes(w, l, S_in, d):
+    """Algorithmic bytes of layer l given S^{l} (dict {(b,h): indices}) -> (attention, total)."""
+    B, Hq, Hkv = w.batch, w.num_q_heads, w.num_kv_heads
+    G = Hq // Hkv
+    mask = w.retrieval_masks[l]
+    kv = 0
+    for b in range(B):
+        n = w.seq_lens[b]
+        for g in range(Hkv):
+            heads = range(g * G, (g + 1) * G)
+            if any(mask >> h & 1 for h in heads):
+                kv += 2 * n * d * 2
+            else:
+                u = np.unique(np.concatenate([S_in[(b, h)] for h in heads]))
+                kv += int(u.size) * 2 * d * 2
+    qo = 2 * B * Hq * d * 2
+    s_io = 0
+    for b in range(B):
+        kb = min(w.k_per_seq[b], w.seq_lens[b])
+        for h in range(Hq):
+            s_io += kb * 4
+    return kv + qo, kv + qo + s_io
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import hybrid_head_sparse_retrieval_amd as ld
+    from hybrid_head_sparse_retrieval_amd.step import DecodeStep
+    import workloads as wl
+
+    ld.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.get_workload(args.workload)
+    L, d = w.layers, w.head_dim
+    log(f"[bench] workload {w.name}: B={w.batch} L={L} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+        f"d={d} N={w.seq_lens if w.batch > 1 else w.seq_lens[0]} k={w.k_per_seq if w.batch > 1 else w.k_per_seq[0]}")
+
+    # ---- inputs resident in HBM
+    t0 = time.time()
+    inputs = []
+    for l in range(L):
+        x = wl.make_layer_inputs(w, l, device=dev)
+        if w.shared_kv_from_layer0 and l > 0:
+            inputs.append((x.q, inputs[0][1], inputs[0][2]))
+        else:
+            inputs.append((x.q, x.k, x.v))
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated in {time.time() - t0:.1f}s "
+        f"({sum(t.numel() * 2 for t in (inputs[0][1], inputs[0][2])) * w.kv_layers() / 1e9:.2f} GB KV)")
+
+    split_flag = ld.flag_split_rows(args.split) | ld.flag_waves(args.waves)
+    step = DecodeStep(w.batch, w.num_q_heads, w.num_kv_heads, d, w.seq_lens, w.k_per_seq,
+                      w.retrieval_masks, csr=w.ragged_csr, device=dev, split_flag=split_flag)
+
+    # ---- accounting pass (untimed): S before every layer -> algorithmic bytes
+    attn_bytes, total_bytes = [], []
+    for l in range(L):
+        S_in = step.s_rows() if l > 0 else None
+        q, kc, vc = inputs[l]
+        step.layer(l, q, kc, vc)
+        a, t = layer_bytes(w, l, S_in, d) if l > 0 else layer_bytes(w, l, None, d)
+        attn_bytes.append(a)
+        total_bytes.append(t)
+    torch.cuda.synchronize()
+    step_bytes = float(sum(total_bytes))
+    log(f"[bench] algorithmic bytes/step {step_bytes / 1e9:.3f} GB")
+
+    # ---- warmup + timed steps
+    for _ in range(args.warmup):
+        step.run(inputs)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step.run(inputs)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
+
+    # ---- per-layer times inside full steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
+    reps = 5
+    per_layer = np.zeros(L)
+    for _ in range(reps):
+        step.run(inputs, events=evs)
+        torch.cuda.synchronize()
+        per_layer += np.array([evs[l].elapsed_time(evs[l + 1]) for l in range(L)]) * 1e3
+    per_layer /= reps
+    if args.layers_detail:
+        for l in range(L):
+            log(f"  layer {l:2d} mask={w.retrieval_masks[l]:#x} {per_layer[l]:8.1f} us "
+                f"{total_bytes[l] / per_layer[l] / 1e3:8.1f} GB/s")
+
+    # ---- attention kernel alone, per layer (HIP events on the launch stream)
+    roof = None
+    if not args.no_kernel_pass:
+        ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        durs = []
+        for rep in range(3):
+            d_rep = []
+            for l in range(L):
+                q, kc, vc = inputs[l]
+                # a GPU-side wait keeps the host's launch latency out of the timed span
+                torch.cuda._sleep(200000)
+                ka.record()
+                step.layer(l, q, kc, vc, extra_flags=ld.FLAG_SKIP_TOPK)
+                kb.record()
+                step.layer(l, q, kc, vc)          # untimed: advances S and the bitmaps
+                torch.cuda.synchronize()
+                d_rep.append(ka.elapsed_time(kb) * 1e3)
+            durs.append(d_rep)
+        durs = np.median(np.array(durs), axis=0)
+        avg_us = float(np.mean(durs))
+        avg_bytes = float(np.mean(attn_bytes))
+        achieved = avg_bytes / (avg_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "k_attention<128,4>" if d == 128 and w.group_size == 4 else "k_attention",
+                "avg_launch_us": round(avg_us, 2), "avg_bytes_per_launch": int(avg_bytes),
+                "launches_timed": L}
+        log(f"[bench] attention kernel: avg {avg_us:.1f} us/launch, {achieved:.0f} GB/s "
+            f"({achieved / HBM_PEAK_GBS * 100:.1f}% of peak)")
+
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    nonzero = [l for l in range(1, L) if w.retrieval_masks[l]]
+    zero = [l for l in range(1, L) if not w.retrieval_masks[l]]
+    result = {
+        "metric": "hybrid-head decode attention effective HBM GB/s (us/layer, us/step alongside)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "us_per_layer": round(ms_step * 1e3 / L, 2),
+        "pct_of_hbm_peak": round(value / HBM_PEAK_GBS * 100, 2),
+        "us_layer0": round(float(per_layer[0]), 2),
+        "us_layers_with_retrieval": round(float(np.mean(per_layer[nonzero])), 2) if nonzero else None,
+        "us_layers_sparse_only": round(float(np.mean(per_layer[zero])), 2) if zero else None,
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "layers": L, "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": d,
+                   "seq_len": w.seq_lens[0] if w.batch == 1 else list(w.seq_lens),
+                   "k": w.k_per_seq[0] if w.batch == 1 else list(w.k_per_seq),
+                   "retrieval_heads_after_layer0": sum(bin(m).count("1") for m in w.retrieval_masks[1:]),
+                   "split_rows": "auto" if args.split == 0 else 256 << (args.split - 1)},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+
+    # ---- CPU oracle baseline on a bounded sample of the same workload
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inputs, total_bytes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, inputs, total_bytes, target_s):
+    """Time the fp64 oracle (as it stands) on the first layers of the step until about
+    target_s seconds of CPU work; report GB/s of algorithmic bytes processed."""
+    from oracle import lychee_oracle as orc
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    offs = w.kv_offsets()
+    S = None
+    spent, done, nbytes = 0.0, 0, 0
+    for l in range(w.layers):
+        q, kc, vc = inputs[l]
+        qb, kb_, vb = wl.bf16_bits(q), wl.bf16_bits(kc), wl.bf16_bits(vc)
+        ret = [bool(w.retrieval_masks[l] >> h & 1) for h in range(w.num_q_heads)]
+        t0 = time.perf_counter()
+        _, S, _ = orc.hybrid_layer_bf16(qb, kb_, vb, offs, ret, w.k_per_seq, S)
+        spent += time.perf_counter() - t0
+        done += 1
+        nbytes += total_bytes[l]
+        log(f"[bench] oracle layer {l}: cumulative {spent:.1f}s")
+        if spent >= target_s:
+            break
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"layers 0..{done - 1} of {w.layers} of one step of {w.name} "
+                      f"({nbytes / 1e9:.2f} GB algorithmic), fp64 NumPy oracle, {spent:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

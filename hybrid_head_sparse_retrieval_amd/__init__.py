@@ -17,7 +17,7 @@ __all__ = [
     "LycheeDecodeError", "LycheeDecodeUnavailable", "library_path", "load_library",
     "Shape", "workspace_bytes", "topk_workspace_bytes", "Workspace", "TopkWorkspace",
     "retrieval_decode", "sparse_decode", "hybrid_layer", "topk_select",
-    "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "flag_split_rows", "EXPORTED_SYMBOLS",
+    "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "flag_split_rows", "flag_waves", "EXPORTED_SYMBOLS",
 ]
 
 LD_OK = 0
@@ -33,6 +33,11 @@ EXPORTED_SYMBOLS = ("ld_status_string", "ld_workspace_size", "ld_topk_workspace_
 def flag_split_rows(v: int) -> int:
     """Rows per attention split = 256 << (v - 1), v in 1..4 (0 = automatic)."""
     return (int(v) & 0xF) << 8
+
+
+def flag_waves(v: int) -> int:
+    """Waves per attention workgroup: 1 = 4 waves, 2 = 8 waves (0 = automatic)."""
+    return (int(v) & 0x3) << 12
 
 
 class LycheeDecodeError(RuntimeError):

@@ -15,15 +15,14 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct LayerLayout {
-  int slots, P, C, W;
-  int64_t ncap;
-  size_t attn_tickets, sel_tickets, hist1, hist2, cand_count;   // zero between calls
-  size_t sel_info, chunk_cnt, cand_key, cand_idx, logits, part_ml, part_acc, bitmaps;
+  int slots, P, W;
+  size_t attn_tickets, hist1;                       // zero between calls
+  size_t sel_info, logits, part_ml, part_acc, bitmaps;
   size_t total;
 };
 
 struct SelLayout {
-  size_t tickets, hist1, hist2, cand_count, sel_info, chunk_cnt, cand_key, cand_idx, total;
+  size_t tickets, hist1, sel_info, total;
 };
 
 bool shape_ok(const ld_shape* s, ld_status* why) {
@@ -50,20 +49,12 @@ LayerLayout layer_layout(const ld_shape* s) {
   L.slots = s->batch * s->num_q_heads;
   L.P = (N + 255) / 256;
   if (L.P > kMaxSplits) L.P = kMaxSplits;
-  L.C = (N + kSelChunk - 1) / kSelChunk;
   L.W = (N + 31) / 32;
-  L.ncap = N;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   L.attn_tickets = take((size_t)s->batch * s->num_kv_heads * 4);
-  L.sel_tickets = take((size_t)L.slots * 4);
   L.hist1 = take((size_t)L.slots * kHist1Bins * 4);
-  L.hist2 = take((size_t)L.slots * kHist2Bins * 4);
-  L.cand_count = take((size_t)L.slots * 4);
   L.sel_info = take((size_t)L.slots * 16);
-  L.chunk_cnt = take((size_t)L.slots * L.C * 8);
-  L.cand_key = take((size_t)L.slots * L.ncap * 4);
-  L.cand_idx = take((size_t)L.slots * L.ncap * 4);
   L.logits = take((size_t)L.slots * N * 4);
   L.part_ml = take((size_t)L.slots * L.P * 8);
   L.part_acc = take((size_t)L.slots * L.P * s->head_dim * 4);
@@ -74,17 +65,12 @@ LayerLayout layer_layout(const ld_shape* s) {
 
 SelLayout sel_layout(int rows, int n) {
   SelLayout L{};
-  const int C = (n + kSelChunk - 1) / kSelChunk;
+  (void)n;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   L.tickets = take((size_t)rows * 4);
   L.hist1 = take((size_t)rows * kHist1Bins * 4);
-  L.hist2 = take((size_t)rows * kHist2Bins * 4);
-  L.cand_count = take((size_t)rows * 4);
   L.sel_info = take((size_t)rows * 16);
-  L.chunk_cnt = take((size_t)rows * C * 8);
-  L.cand_key = take((size_t)rows * n * 4);
-  L.cand_idx = take((size_t)rows * n * 4);
   L.total = o;
   return L;
 }
@@ -94,20 +80,25 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
-// Rows per attention split: 256 << v. Automatic choice: the smallest split that keeps
-// the launch at or below ~2 workgroups' worth per compute unit times 2 (about 1024
-// workgroups), capped so that no sequence needs more than kMaxSplits splits.
-int choose_split_rows(int N, int64_t groups_total, uint32_t flags) {
-  int v = (int)((flags >> 8) & 0xfu);
+// Rows per attention split (256 << (v-1), override v in flag bits 8..11) and waves
+// per workgroup (flag bits 12..13: 1 = 4 waves, 2 = 8 waves). Automatic choice: 8
+// waves and the smallest split of at least 512 rows that keeps the launch at or below
+// 512 workgroups (two per compute unit over the launch), capped so that no sequence
+// needs more than kMaxSplits splits.
+void choose_split(int N, int64_t groups_total, uint32_t flags, int* ts_out, int* waves_out) {
+  const int wv = (int)((flags >> 12) & 0x3u);
+  const int waves = (wv == 1) ? 4 : 8;
+  const int v = (int)((flags >> 8) & 0xfu);
   int ts;
   if (v >= 1 && v <= 4) {
     ts = 256 << (v - 1);
   } else {
-    ts = 256;
-    while (ts < kMaxSplitRows && groups_total * (int64_t)((N + ts - 1) / ts) > 1024) ts <<= 1;
+    ts = waves == 8 ? 512 : 256;
+    while (ts < kMaxSplitRows && groups_total * (int64_t)((N + ts - 1) / ts) > 512) ts <<= 1;
   }
   while ((N + ts - 1) / ts > kMaxSplits && ts < kMaxSplitRows) ts <<= 1;
-  return ts;
+  *ts_out = ts;
+  *waves_out = waves;
 }
 
 // Core of the three layer entry points.
@@ -185,7 +176,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     if (active & gm) ap.groups[ng++] = (uint8_t)g;
   }
   ap.ngroups = ng;
-  ap.ts = choose_split_rows(N, (int64_t)B * ng, flags);
+  choose_split(N, (int64_t)B * ng, flags, &ap.ts, &ap.waves);
   ap.nsplit = (N + ap.ts - 1) / ap.ts;
   ap.bitmaps = bitmaps; ap.W = L.W;
   ap.logits = scores_out ? scores_out : (do_topk ? at<float>(ws, L.logits) : nullptr);
@@ -206,21 +197,15 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     SelParams sp{};
     sp.mode = 1;
     sp.nrows = B * nret;
-    sp.C = L.C;
+    sp.C = 0;
     sp.logits = ap.logits; sp.Hq = Hq; sp.seq_len = N; sp.kv_indptr = shape->kv_indptr;
     sp.s_out = s_out; sp.s_indptr = s_indptr; sp.k_dense = k;
     sp.bitmaps = bitmaps; sp.W = L.W;
     sp.nret = nret;
     std::memcpy(sp.heads, ret_heads, sizeof(ret_heads));
     sp.hist1 = at<uint32_t>(ws, L.hist1);
-    sp.hist2 = at<uint32_t>(ws, L.hist2);
-    sp.tickets = at<uint32_t>(ws, L.sel_tickets);
+    sp.tickets = nullptr;
     sp.sel_info = at<uint32_t>(ws, L.sel_info);
-    sp.cand_count = at<uint32_t>(ws, L.cand_count);
-    sp.chunk_cnt = at<uint32_t>(ws, L.chunk_cnt);
-    sp.cand_key = at<uint32_t>(ws, L.cand_key);
-    sp.cand_idx = at<int32_t>(ws, L.cand_idx);
-    sp.ncap = L.ncap;
     if (launch_select(sp, st, false) != hipSuccess) return LD_ERR_HIP;
   }
   return LD_OK;
@@ -308,14 +293,8 @@ ld_status ld_topk_select(const float* scores, int32_t rows, int32_t n, int64_t r
   sp.scores = scores; sp.row_stride = row_stride; sp.n = n; sp.k = k;
   sp.idx_out = idx_out; sp.val_out = val_out;
   sp.hist1 = at<uint32_t>(workspace, L.hist1);
-  sp.hist2 = at<uint32_t>(workspace, L.hist2);
   sp.tickets = at<uint32_t>(workspace, L.tickets);
   sp.sel_info = at<uint32_t>(workspace, L.sel_info);
-  sp.cand_count = at<uint32_t>(workspace, L.cand_count);
-  sp.chunk_cnt = at<uint32_t>(workspace, L.chunk_cnt);
-  sp.cand_key = at<uint32_t>(workspace, L.cand_key);
-  sp.cand_idx = at<int32_t>(workspace, L.cand_idx);
-  sp.ncap = n;
   return launch_select(sp, stream, true) == hipSuccess ? LD_OK : LD_ERR_HIP;
 }
 

@@ -10,16 +10,21 @@
 //     outside their S (membership bitmaps),
 //   * a group of sparse heads only reads the rows in the union of its heads' S and
 //     each head accumulates its own rows.
-// Each wave keeps an online softmax state per row slot (no block barriers while
-// streaming); the states are merged at the end of the tile and written as split
-// partials. The last workgroup of a (b, g) (integer ticket, agent-scope
-// acquire/release) merges the partials into O, and, when selection is requested,
+//
+// Per wave, rows are consumed in 16-row tiles:
+//   q.K   on the matrix cores: v_mfma_f32_16x16x32_bf16 with the K tile as the A
+//         operand (16 rows x 32 dims, loaded straight from HBM in operand layout) and
+//         the group's queries as the B operand (heads padded to 16 columns). bf16
+//         products are exact, accumulation is fp32.
+//   softmax in the MFMA output layout (lane = head column, 4 rows); the running max
+//         of each head is wave-uniform; the probabilities go through LDS.
+//   P.V   on the vector ALU in fp32 (8 lanes per V row, 16 dims per lane).
+// The next chunk's K and V are loaded while the current one is computed. Each
+// workgroup writes one partial (max in log2 units, sum, unnormalised output) per
+// head; the last workgroup of a (b, g) (integer ticket, device-coherent stores and
+// loads, no cache-wide fences) merges them into O and, when selection is requested,
 // turns the fused first-digit histogram of each retrieval head into the first
 // selection digit for the argsTopK kernels.
-//
-// Lane layout: 8 lanes per K/V row (16 bf16 each at d=128, 8 at d=64), 8 rows per
-// wave step, 4 waves -> 32 rows per workgroup step. q.K uses v_dot2c_f32_bf16 on
-// packed bf16 (exact products, fp32 accumulate); P.V converts V to fp32 and uses FMA.
 
 #include "ld_device.h"
 
@@ -28,40 +33,82 @@ namespace ld {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kTile = 16;        // rows per MFMA tile
+constexpr int kTPC = 1;          // tiles per chunk per wave
+constexpr int kChunkRows = kTile * kTPC;
 
-template <int D, int G, bool HIST>
-struct AttnSmem {
-  uint8_t hm[kMaxSplitRows];        // per-row membership mask of the group's heads
-  uint16_t list[kMaxSplitRows];     // rows to visit (gather mode)
-  int wcnt[4];
-  int misc[4];
-  union {
-    uint32_t hist[HIST ? G : 1][kHist1Bins];
-    struct {
-      float acc[4][G][D];
-      float m[4][G];
-      float l[4][G];
-    } red;
-    struct {
-      float w[G][kMaxSplits];   // split weights
-      float inv_l[G];
-    } cmb;
-  } u;
-  uint32_t res[2];
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// 128-bit device-coherent (sc1) access through a buffer resource over `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+constexpr int kSc1 = 16;   // cache-policy bit of sc1 for buffer instructions
+__device__ __forceinline__ float4 ld_dev4_b(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kSc1);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+__device__ __forceinline__ void st_dev4_b(__amdgpu_buffer_rsrc_t r, int byte_off, float4 x) {
+  u32x4_t v = {__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, kSc1);
+}
+
+// Workgroup of NW waves. After the in-wave reduction each wave keeps RP row parts.
+template <int NW>
+struct WaveCfg {
+  static constexpr int NT = 64 * NW;
+  static constexpr int RP = 16 / NW;        // row parts per wave written to LDS (4 or 2)
 };
 
-template <int D, int G, bool HIST>
-__global__ __launch_bounds__(kThreads) void k_attention(const AttnParams p) {
-  constexpr int LPR = 8;             // lanes per row
-  constexpr int EPL = D / LPR;       // bf16 elements per lane
-  constexpr int DWL = EPL / 2;       // dwords per lane
-  constexpr int NV = DWL / 4;        // 16-byte loads per lane per row
-  constexpr int U = 4;               // wave steps per chunk
-  using Smem = AttnSmem<D, G, HIST>;
+template <int D, int G, int NW>
+struct AttnSmem {
+  static constexpr int RP = WaveCfg<NW>::RP;
+  static constexpr int COLS = G * (D / 4);  // float4 output columns
+  static constexpr int TPCOL = (64 * NW) / COLS >= 4 ? 4 : ((64 * NW) / COLS >= 2 ? 2 : 1);
+  uint8_t hmp[kMaxSplitRows];        // membership mask (bit j = head g*G+j) per visit position
+  uint16_t list[kMaxSplitRows];      // token row (within the tile) of each visit position
+  int wcnt[NW];
+  int misc[4];
+  uint32_t res[2];
+  float pl[NW][kChunkRows][G];       // per wave: probabilities of the chunk's rows
+  union {
+    uint32_t hist[G][kHist1Bins];
+    struct {
+      float acc[NW][RP][G * D];      // [wave][row part][head*D + dim]
+      float m[NW][G];
+      float l[NW][G];
+    } red;
+    struct {
+      float w[G][kMaxSplits];        // split maxima, then split weights
+      float lp[G][kMaxSplits];       // split sums
+      float inv_l[G];
+      float4 part[TPCOL > 1 ? TPCOL - 1 : 1][COLS];   // partial column sums of the merge
+    } cmb;
+  } u;
+};
+
+template <int D, int G, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams p) {
+  constexpr int NT = 64 * NW;
+  constexpr int KCH = D / 32;        // MFMA k-steps per row
+  constexpr int EPL = D / 8;         // dims per lane in the P.V layout
+  constexpr int NV = D / 64;         // 16-byte V loads per lane per row
+  constexpr int RSC = 2 * kTPC;      // P.V row steps (8 rows) per chunk
+  using Smem = AttnSmem<D, G, NW>;
+  constexpr int RP = Smem::RP;
   __shared__ Smem sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rg = lane >> 3, li = lane & 7;
+  const int mr = lane & 15, mk = lane >> 4;   // MFMA roles: row/column, k-group
+  const int rg = lane >> 3, li = lane & 7;    // P.V roles: row in step, dim slice
+  const bool do_hist = p.do_topk != 0;
 
   int bid = blockIdx.x;
   const int split = bid % p.nsplit;
@@ -99,309 +146,391 @@ __global__ __launch_bounds__(kThreads) void k_attention(const AttnParams p) {
   ret &= act;
   const uint32_t spm = act & ~ret;
   const bool dense = ret != 0;
+  const int hq0 = b * p.Hq + g * G;           // first query-head slot of the group
 
-  // ---- membership of each row of the tile
-  if (spm) {
-    for (int r = tid; r < nrows; r += kThreads) {
-      uint32_t m = ret;
-      const int row = r0 + r;
+  // ---- query operand (B): column mr = head, k-group mk; zero for padding columns
+  uint4 qb[KCH];
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        if (spm >> j & 1) {
-          const uint32_t w = p.bitmaps[(size_t)(b * p.Hq + g * G + j) * p.W + (row >> 5)];
-          m |= ((w >> (row & 31)) & 1u) << j;
+  for (int kk = 0; kk < KCH; ++kk) {
+    if (mr < G)
+      qb[kk] = *reinterpret_cast<const uint4*>(p.q + (size_t)(hq0 + mr) * D + kk * 32 + mk * 8);
+    else
+      qb[kk] = make_uint4(0, 0, 0, 0);
+  }
+
+  // ---- per-wave streaming state (tiles wave, wave+4, ...; kTPC tiles per chunk)
+  const uint16_t* kbase = p.kc + (size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D;
+  const uint16_t* vbase = p.vc + (size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D;
+  int nlist = nrows;
+  auto chunks_of = [&](int n) {
+    const int ntiles = (n + kTile - 1) / kTile;
+    const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
+    return (my_tiles + kTPC - 1) / kTPC;
+  };
+
+  const bool head_lane = mr < G;
+  const bool ret_lane = head_lane && ((ret >> mr) & 1u);
+  float* lg = (p.logits && ret_lane) ? p.logits + (size_t)(hq0 + mr) * p.seq_len + r0 : nullptr;
+  const float scale = p.scale;
+
+  float m_lane = -LD_INF, l_lane = 0.f;     // running max / sum of head mr (lanes mr < G)
+  float acc[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
+
+  uint4 kr[3][kTPC][KCH], vr[3][RSC][NV];
+
+  auto row_of = [&](int pos) -> int { return dense ? pos : (int)sm.list[pos]; };
+  auto load_chunk = [&](int c, uint4 (&kd)[kTPC][KCH], uint4 (&vd)[RSC][NV]) {
+#pragma unroll
+    for (int t = 0; t < kTPC; ++t) {
+      const int tb = (wave + NW * (c * kTPC + t)) * kTile;
+      const int pa = tb + mr;                 // A-operand row of this lane
+      const bool va = pa < nlist;
+      const uint16_t* kp = kbase + (size_t)(va ? row_of(pa) : 0) * D + mk * 8;
+#pragma unroll
+      for (int kk = 0; kk < KCH; ++kk)
+        kd[t][kk] = va ? *reinterpret_cast<const uint4*>(kp + kk * 32) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int pv = tb + h2 * 8 + rg;      // P.V row of this lane
+        const bool vv = pv < nlist;
+        const uint16_t* vp = vbase + (size_t)(vv ? row_of(pv) : 0) * D + li * 8;
+#pragma unroll
+        for (int c2 = 0; c2 < NV; ++c2)
+          vd[t * 2 + h2][c2] = vv ? *reinterpret_cast<const uint4*>(vp + c2 * 64) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  if (dense) {
+    const int nc0 = chunks_of(nrows);
+    if (nc0 > 0) load_chunk(0, kr[0], vr[0]);
+    if (nc0 > 1) load_chunk(1, kr[1], vr[1]);
+  }
+
+  // ---- membership of each row of the tile, and the visit list
+  if (do_hist) {
+    for (int i = tid; i < G * kHist1Bins; i += NT) (&sm.u.hist[0][0])[i] = 0;
+  }
+  if (spm) {
+    constexpr int IT = kMaxSplitRows / NT;
+    uint32_t mrow[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int r = it * NT + tid;
+      uint32_t m = ret;
+      if (r < nrows) {
+        const int row = r0 + r;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          if (spm >> j & 1) {
+            const uint32_t w = p.bitmaps[(size_t)(hq0 + j) * p.W + (row >> 5)];
+            m |= ((w >> (row & 31)) & 1u) << j;
+          }
         }
       }
-      sm.hm[r] = (uint8_t)m;
+      mrow[it] = m;
     }
-  }
-  if (HIST) {
-    for (int i = tid; i < G * kHist1Bins; i += kThreads) (&sm.u.hist[0][0])[i] = 0;
+    if (dense) {
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int r = it * NT + tid;
+        if (r < nrows) sm.hmp[r] = (uint8_t)mrow[it];
+      }
+    } else {
+      int total = 0;
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        if (it * NT >= nrows) break;
+        const int r = it * NT + tid;
+        const bool f = r < nrows && mrow[it] != 0;
+        const uint64_t bal = __ballot(f);
+        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) sm.wcnt[wave] = __popcll(bal);
+        __syncthreads();
+        int woff = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          woff += (w < wave) ? sm.wcnt[w] : 0;
+          tot += sm.wcnt[w];
+        }
+        if (f) {
+          sm.list[total + woff + pre] = (uint16_t)r;
+          sm.hmp[total + woff + pre] = (uint8_t)mrow[it];
+        }
+        total += tot;
+        __syncthreads();
+      }
+      nlist = total;
+    }
   }
   __syncthreads();
 
-  int nlist = nrows;
+  int nchunks = chunks_of(nlist);
   if (!dense) {
-    int total = 0;
-    for (int base = 0; base < nrows; base += kThreads) {
-      const int r = base + tid;
-      const bool f = r < nrows && sm.hm[r] != 0;
-      const uint64_t bal = __ballot(f);
-      const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-      if (lane == 0) sm.wcnt[wave] = __popcll(bal);
-      __syncthreads();
-      int woff = 0, tot = 0;
+    if (nchunks > 0) load_chunk(0, kr[0], vr[0]);
+    if (nchunks > 1) load_chunk(1, kr[1], vr[1]);
+  }
+
+  auto compute_chunk = [&](int c, const uint4 (&kd)[kTPC][KCH], const uint4 (&vd)[RSC][NV]) {
+    // q . K on the matrix cores
+    f32x4_t dacc[kTPC];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        woff += (w < wave) ? sm.wcnt[w] : 0;
-        tot += sm.wcnt[w];
-      }
-      if (f) sm.list[total + woff + pre] = (uint16_t)r;
-      total += tot;
-      __syncthreads();
+    for (int t = 0; t < kTPC; ++t) {
+      dacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KCH; ++kk) dacc[t] = mfma_bf16(kd[t][kk], qb[kk], dacc[t]);
     }
-    nlist = total;
-  }
-
-  // ---- query registers: packed bf16 pairs of this lane's slice, per head
-  uint32_t qv[G][DWL];
+    // scores of head mr for rows tb + 4*mk + r
+    float tl[kTPC][4];
+    float cm = -LD_INF;
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const uint4* qp = reinterpret_cast<const uint4*>(p.q + (size_t)(b * p.Hq + g * G + j) * D + li * EPL);
+    for (int t = 0; t < kTPC; ++t) {
+      const int tb = (wave + NW * (c * kTPC + t)) * kTile;
+      const int pos0 = tb + 4 * mk;
+      uint32_t hm4 = 0;
+      if (spm) hm4 = *reinterpret_cast<const uint32_t*>(&sm.hmp[pos0]);
 #pragma unroll
-    for (int c = 0; c < NV; ++c) {
-      const uint4 x = qp[c];
-      qv[j][4 * c + 0] = x.x; qv[j][4 * c + 1] = x.y; qv[j][4 * c + 2] = x.z; qv[j][4 * c + 3] = x.w;
-    }
-  }
-
-  float m_[G], l_[G], acc[G][EPL];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    m_[j] = -LD_INF;
-    l_[j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
-  }
-
-  const uint16_t* kbase = p.kc + (size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D + li * EPL;
-  const uint16_t* vbase = p.vc + (size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D + li * EPL;
-  float* lg_base[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j)
-    lg_base[j] = p.logits ? p.logits + (size_t)(b * p.Hq + g * G + j) * p.seq_len + r0 : nullptr;
-
-  const int nsteps = (nlist + 7) >> 3;
-  for (int st0 = wave; st0 < nsteps; st0 += 4 * U) {
-    uint4 kr[U][NV], vr[U][NV];
-    int rowv[U];
-    bool valid[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int pos = (st0 + 4 * u) * 8 + rg;
-      valid[u] = pos < nlist;
-      const int row = valid[u] ? (dense ? pos : (int)sm.list[pos]) : 0;
-      rowv[u] = row;
-      const uint4* kp = reinterpret_cast<const uint4*>(kbase + (size_t)row * D);
-      const uint4* vp = reinterpret_cast<const uint4*>(vbase + (size_t)row * D);
-#pragma unroll
-      for (int c = 0; c < NV; ++c) {
-        if (valid[u]) {
-          kr[u][c] = kp[c];
-          vr[u][c] = vp[c];
-        } else {
-          kr[u][c] = make_uint4(0, 0, 0, 0);
-          vr[u][c] = make_uint4(0, 0, 0, 0);
+      for (int r = 0; r < 4; ++r) {
+        const int pos = pos0 + r;
+        const uint32_t hm = spm ? ((hm4 >> (8 * r)) & 0xffu) : ret;
+        const bool mem = head_lane && pos < nlist && ((hm >> mr) & 1u);
+        const float s = dacc[t][r] * scale;
+        if (ret_lane && pos < nlist) {
+          if (lg) lg[pos] = s;                           // stream mode: pos is the row
+          if (do_hist) atomicAdd(&sm.u.hist[mr][score_key(s) >> 21], 1u);
         }
+        tl[t][r] = mem ? s * kLog2e : -LD_INF;
+        cm = fmaxf(cm, tl[t][r]);
       }
     }
-    // q . k for every head and row slot
-    float t[U][G];
+    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    const float mn = fmaxf(m_lane, cm);
+    const float mu = (mn == -LD_INF) ? 0.f : mn;
+    const float alpha = exp2_fast(m_lane - mu);       // 0 when m_lane was -inf
+    const bool grew = mn > m_lane;
+    m_lane = mn;
+    float ps = 0.f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t hm = valid[u] ? (spm ? (uint32_t)sm.hm[rowv[u]] : ret) : 0u;
-      const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[u][0]);
+    for (int t = 0; t < kTPC; ++t)
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float d = 0.f;
-#pragma unroll
-        for (int c = 0; c < DWL; ++c) d = dot2_bf16(qv[j][c], kw[c], d);
-        d = sum8(d);
-        const float s = d * p.scale;
-        const bool mem = (hm >> j) & 1u;
-        if ((ret >> j & 1u) && mem && li == 0) {
-          if (lg_base[j]) lg_base[j][rowv[u]] = s;
-          if (HIST) atomicAdd(&sm.u.hist[j][score_key(s) >> 21], 1u);
-        }
-        t[u][j] = mem ? s * kLog2e : -LD_INF;
+      for (int r = 0; r < 4; ++r) {
+        const float pr = exp2_fast(tl[t][r] - mu);
+        ps += pr;
+        if (head_lane) sm.pl[wave][t * kTile + 4 * mk + r][mr] = pr;
       }
-    }
-    // online softmax update (rescale only when some running max grows)
-    float pr[U][G];
+    l_lane = l_lane * (grew ? alpha : 1.f) + ps;
+    // rescale the output accumulators of heads whose running max grew (wave-uniform)
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      float mc = t[0][j];
+      const int gj = __builtin_amdgcn_readlane(__float_as_int(grew ? alpha : 1.f), j);
+      const float aj = __int_as_float(gj);
+      if (aj != 1.f) {
 #pragma unroll
-      for (int u = 1; u < U; ++u) mc = fmaxf(mc, t[u][j]);
-      const float mn = fmaxf(m_[j], mc);
-      if (__any(mn > m_[j])) {
-        const float mu = (mn == -LD_INF) ? 0.f : mn;
-        const float alpha = exp2_fast(m_[j] - mu);
-        l_[j] *= alpha;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[j][e] *= alpha;
-        m_[j] = mn;
-      }
-      const float mu = (m_[j] == -LD_INF) ? 0.f : m_[j];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        pr[u][j] = exp2_fast(t[u][j] - mu);
-        l_[j] += pr[u][j];
+        for (int e = 0; e < EPL; ++e) acc[j][e] *= aj;
       }
     }
     // P . V
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vr[u][0]);
+    for (int rs = 0; rs < RSC; ++rs) {
+      const int tr = (rs >> 1) * kTile + (rs & 1) * 8 + rg;
+      float pj[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) pj[j] = sm.pl[wave][tr][j];
       float vf[EPL];
 #pragma unroll
-      for (int c = 0; c < DWL; ++c) {
-        vf[2 * c] = bf_lo(vw[c]);
-        vf[2 * c + 1] = bf_hi(vw[c]);
+      for (int c2 = 0; c2 < NV; ++c2) {
+        const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vd[rs][c2]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          vf[c2 * 8 + 2 * q] = bf_lo(vw[q]);
+          vf[c2 * 8 + 2 * q + 1] = bf_hi(vw[q]);
+        }
       }
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
+      for (int j = 0; j < G; ++j)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(pr[u][j], vf[e], acc[j][e]);
+        for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(pj[j], vf[e], acc[j][e]);
+    }
+  };
+
+  // ---- main loop: two chunks in flight while one is computed
+  for (int c = 0; c < nchunks; c += 3) {
+    if (c + 2 < nchunks) load_chunk(c + 2, kr[2], vr[2]);
+    compute_chunk(c, kr[0], vr[0]);
+    if (c + 1 < nchunks) {
+      if (c + 3 < nchunks) load_chunk(c + 3, kr[0], vr[0]);
+      compute_chunk(c + 1, kr[1], vr[1]);
+      if (c + 2 < nchunks) {
+        if (c + 4 < nchunks) load_chunk(c + 4, kr[1], vr[1]);
+        compute_chunk(c + 2, kr[2], vr[2]);
       }
     }
   }
 
   // ---- flush the fused selection histogram
-  if (HIST) {
+  if (do_hist) {
     __syncthreads();
-    for (int i = tid; i < G * kHist1Bins; i += kThreads) {
+    for (int i = tid; i < G * kHist1Bins; i += NT) {
       const int j = i / kHist1Bins, bin = i % kHist1Bins;
-      const uint32_t c = sm.u.hist[j][bin];
-      if (c) atomicAdd(p.hist1 + (size_t)(b * p.Hq + g * G + j) * kHist1Bins + bin, c);
+      const uint32_t cnt = sm.u.hist[j][bin];
+      if (cnt) atomicAdd(p.hist1 + (size_t)(hq0 + j) * kHist1Bins + bin, cnt);
     }
-    __syncthreads();
   }
+  __syncthreads();   // the LDS union is reused below
 
-  // ---- merge the 8 row slots of each wave (lanes li, li+8, ..., li+56)
+  // ---- wave totals: sum of head mr over the 4 k-groups; outputs over row pairs
+  l_lane += __shfl_xor(l_lane, 16, 64);
+  l_lane += __shfl_xor(l_lane, 32, 64);
 #pragma unroll
-  for (int off = 8; off < 64; off <<= 1) {
+  for (int j = 0; j < G; ++j)
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float mo = shfl_xor_f(m_[j], off);
-      const float lo = shfl_xor_f(l_[j], off);
-      const float mn = fmaxf(m_[j], mo);
-      const float mu = (mn == -LD_INF) ? 0.f : mn;
-      const float a = exp2_fast(m_[j] - mu), c = exp2_fast(mo - mu);
-      l_[j] = l_[j] * a + lo * c;
+    for (int e = 0; e < EPL; ++e) acc[j][e] += __shfl_xor(acc[j][e], 8, 64);
+  if (RP == 2) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[j][e] = acc[j][e] * a + shfl_xor_f(acc[j][e], off) * c;
-      m_[j] = mn;
-    }
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[j][e] += __shfl_xor(acc[j][e], 16, 64);
   }
-  if (rg == 0) {
+  constexpr int RSTEP = 8 / RP;               // row slots folded into one part
+  if ((rg % RSTEP) == 0) {
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
+    for (int j = 0; j < G; ++j)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm.u.red.acc[wave][j][li * EPL + e] = acc[j][e];
-      if (li == 0) {
-        sm.u.red.m[wave][j] = m_[j];
-        sm.u.red.l[wave][j] = l_[j];
+      for (int e = 0; e < EPL; ++e) {
+        const int d = (e < 8) ? (li * 8 + e) : (64 + li * 8 + (e - 8));
+        sm.u.red.acc[wave][rg / RSTEP][j * D + d] = acc[j][e];
       }
-    }
+  }
+  if (lane < G) {
+    sm.u.red.m[wave][lane] = m_lane;
+    sm.u.red.l[wave][lane] = l_lane;
   }
   __syncthreads();
-  // ---- merge the 4 waves and write this split's partials
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int j = i / D, d = i % D;
+
+  // ---- merge the 4 waves and write this split's partials (4 dims per thread)
+  for (int i = tid; i < G * (D / 4); i += NT) {
+    const int j = i / (D / 4), d0 = (i % (D / 4)) * 4;
     if (!(act >> j & 1u)) continue;
-    float mw[4], M = -LD_INF;
+    float M = -LD_INF;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) { mw[w] = sm.u.red.m[w][j]; M = fmaxf(M, mw[w]); }
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.u.red.m[w][j]);
     const float mu = (M == -LD_INF) ? 0.f : M;
-    float a = 0.f, L = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float sc = exp2_fast(mw[w] - mu);
-      a += sm.u.red.acc[w][j][d] * sc;
+    for (int w = 0; w < NW; ++w) {
+      const float sc = exp2_fast(sm.u.red.m[w][j] - mu);
       L += sm.u.red.l[w][j] * sc;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int x2 = 0; x2 < RP; ++x2) {
+        x.x += sm.u.red.acc[w][x2][j * D + d0 + 0];
+        x.y += sm.u.red.acc[w][x2][j * D + d0 + 1];
+        x.z += sm.u.red.acc[w][x2][j * D + d0 + 2];
+        x.w += sm.u.red.acc[w][x2][j * D + d0 + 3];
+      }
+      a.x += x.x * sc; a.y += x.y * sc; a.z += x.z * sc; a.w += x.w * sc;
     }
-    const size_t slot = (size_t)(b * p.Hq + g * G + j) * p.P + split;
-    p.part_acc[slot * D + d] = a;
-    if (d == 0) {
-      p.part_ml[slot * 2 + 0] = M;
-      p.part_ml[slot * 2 + 1] = L;
+    const size_t pslot = (size_t)(hq0 + j) * p.P + split;
+    st_dev4_b(rsrc(p.part_acc + (size_t)(hq0 + j) * p.P * D), (split * D + d0) * 4, a);
+    if (d0 == 0) {
+      st_dev(p.part_ml + pslot * 2 + 0, M);
+      st_dev(p.part_ml + pslot * 2 + 1, L);
     }
   }
 
   // ---- ticket: the last split of (b, g) merges all partials
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(p.tickets + b * p.Hkv + g, 1u, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    sm.misc[0] = (old == (uint32_t)(nsplit_b - 1));
-  }
-  __syncthreads();
-  if (!sm.misc[0]) return;
-  __threadfence();
+  if (!arrive_last(p.tickets + b * p.Hkv + g, (uint32_t)nsplit_b, &sm.misc[0])) return;
   if (tid == 0) p.tickets[b * p.Hkv + g] = 0u;
 
-  // split weights w_p = exp2(m_p - M) / L per head, kept in LDS
-  constexpr int kMaxW = sizeof(sm.u.cmb.w[0]) / sizeof(float);
   const int np = nsplit_b;
-  for (int j = 0; j < G; ++j) {
-    if (!(act >> j & 1u)) continue;
-    const size_t base = (size_t)(b * p.Hq + g * G + j) * p.P;
-    float M = -LD_INF;
-    for (int s = tid; s < np; s += kThreads) M = fmaxf(M, p.part_ml[(base + s) * 2]);
-    // block max
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    if (lane == 0) sm.wcnt[wave] = __float_as_int(M);
-    __syncthreads();
-    M = fmaxf(fmaxf(__int_as_float(sm.wcnt[0]), __int_as_float(sm.wcnt[1])),
-              fmaxf(__int_as_float(sm.wcnt[2]), __int_as_float(sm.wcnt[3])));
-    __syncthreads();
-    const float mu = (M == -LD_INF) ? 0.f : M;
-    float L = 0.f;
-    for (int s = tid; s < np; s += kThreads) {
-      const float w = exp2_fast(p.part_ml[(base + s) * 2] - mu);
-      if (s < kMaxW) sm.u.cmb.w[j][s] = w;
-      L += p.part_ml[(base + s) * 2 + 1] * w;
-    }
-    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
-    if (lane == 0) sm.wcnt[wave] = __float_as_int(L);
-    __syncthreads();
-    if (tid == 0)
-      sm.u.cmb.inv_l[j] = 1.f / (__int_as_float(sm.wcnt[0]) + __int_as_float(sm.wcnt[1]) +
-                                 __int_as_float(sm.wcnt[2]) + __int_as_float(sm.wcnt[3]));
-    __syncthreads();
-  }
-  // O[d] = sum_p acc_p[d] * w_p / L ; 4-float columns, threads split over (head, column)
   {
-    constexpr int COLS = D / 4;
-    for (int i = tid; i < G * COLS; i += kThreads) {
-      const int j = i / COLS, c = i % COLS;
-      if (!(act >> j & 1u)) continue;
-      const size_t base = (size_t)(b * p.Hq + g * G + j) * p.P;
-      const float4* ap = reinterpret_cast<const float4*>(p.part_acc + base * D) + c;
-      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-      int s = 0;
-      for (; s + 8 <= np; s += 8) {
-        float4 x[8];
+    constexpr int COLS = Smem::COLS;
+    constexpr int TPCOL = Smem::TPCOL;    // threads per column, each over a share of splits
+    constexpr int PF = 16;                // partial columns fetched per round
+    const int col = tid % COLS, part = tid / COLS;
+    const int j = col / (D / 4), d0 = (col % (D / 4)) * 4;
+    const bool live = part < TPCOL && (act >> j & 1u);
+    const int s_lo = (np * part) / TPCOL;
+    const int s_hi = (np * (part + 1)) / TPCOL;
+    const __amdgpu_buffer_rsrc_t rr = rsrc(p.part_acc + (size_t)(hq0 + j) * p.P * D);
+    float4 x[PF];
+    if (live) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) x[q] = ap[(size_t)(s + q) * COLS];
+      for (int q = 0; q < PF; ++q)
+        if (s_lo + q < s_hi) x[q] = ld_dev4_b(rr, ((s_lo + q) * D + d0) * 4);
+    }
+    // maxima and sums of every (head, split) in one round
+    for (int i = tid; i < G * np; i += NT) {
+      const int jj = i / np, ss = i % np;
+      if (act >> jj & 1u) {
+        const size_t ms = ((size_t)(hq0 + jj) * p.P + ss) * 2;
+        sm.u.cmb.w[jj][ss] = ld_dev(p.part_ml + ms);
+        sm.u.cmb.lp[jj][ss] = ld_dev(p.part_ml + ms + 1);
+      }
+    }
+    __syncthreads();
+    for (int jj = wave; jj < G; jj += NW) {
+      if (!(act >> jj & 1u)) continue;
+      float M = -LD_INF;
+      for (int ss = lane; ss < np; ss += 64) M = fmaxf(M, sm.u.cmb.w[jj][ss]);
+      for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+      const float mu = (M == -LD_INF) ? 0.f : M;
+      float L = 0.f;
+      for (int ss = lane; ss < np; ss += 64) {
+        const float w = exp2_fast(sm.u.cmb.w[jj][ss] - mu);
+        sm.u.cmb.w[jj][ss] = w;
+        L += sm.u.cmb.lp[jj][ss] * w;
+      }
+      for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+      if (lane == 0) sm.u.cmb.inv_l[jj] = 1.f / L;
+    }
+    __syncthreads();
+    // O[d] = sum_p acc_p[d] * w_p / L over columns of 4 dims
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (live) {
+      for (int s0 = s_lo; s0 < s_hi; s0 += PF) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float w = (s + q < kMaxW) ? sm.u.cmb.w[j][s + q] : 0.f;
-          o.x = fmaf(x[q].x, w, o.x); o.y = fmaf(x[q].y, w, o.y);
-          o.z = fmaf(x[q].z, w, o.z); o.w = fmaf(x[q].w, w, o.w);
+        for (int q = 0; q < PF; ++q) {
+          if (s0 + q < s_hi) {
+            const float w = sm.u.cmb.w[j][s0 + q];
+            o.x = fmaf(x[q].x, w, o.x); o.y = fmaf(x[q].y, w, o.y);
+            o.z = fmaf(x[q].z, w, o.z); o.w = fmaf(x[q].w, w, o.w);
+          }
+        }
+        if (s0 + PF < s_hi) {
+#pragma unroll
+          for (int q = 0; q < PF; ++q)
+            if (s0 + PF + q < s_hi) x[q] = ld_dev4_b(rr, ((s0 + PF + q) * D + d0) * 4);
         }
       }
-      for (; s < np; ++s) {
-        const float4 x = ap[(size_t)s * COLS];
-        const float w = (s < kMaxW) ? sm.u.cmb.w[j][s] : 0.f;
-        o.x = fmaf(x.x, w, o.x); o.y = fmaf(x.y, w, o.y);
-        o.z = fmaf(x.z, w, o.z); o.w = fmaf(x.w, w, o.w);
+    }
+    if (TPCOL > 1 && live && part > 0) sm.u.cmb.part[part - 1][col] = o;
+    __syncthreads();
+    if (live && part == 0) {
+#pragma unroll
+      for (int q = 1; q < TPCOL; ++q) {
+        const float4 y = sm.u.cmb.part[q - 1][col];
+        o.x += y.x; o.y += y.y; o.z += y.z; o.w += y.w;
       }
       const float il = sm.u.cmb.inv_l[j];
       ushort4 r;
       r.x = f32_to_bf16(o.x * il); r.y = f32_to_bf16(o.y * il);
       r.z = f32_to_bf16(o.z * il); r.w = f32_to_bf16(o.w * il);
-      reinterpret_cast<ushort4*>(p.out + (size_t)(b * p.Hq + g * G + j) * D)[c] = r;
+      *reinterpret_cast<ushort4*>(p.out + (size_t)(hq0 + j) * D + d0) = r;
     }
   }
 
   // ---- first selection digit for each retrieval head (fused histogram complete)
-  if (HIST && p.do_topk) {
+  if (do_hist) {
     for (int j = 0; j < G; ++j) {
       if (!(ret >> j & 1u)) continue;
-      const int slot = b * p.Hq + g * G + j;
+      const int slot = hq0 + j;
       uint32_t* hist = p.hist1 + (size_t)slot * kHist1Bins;
       int kk = p.k_dense;
       if (p.s_indptr) kk = (int)(p.s_indptr[slot + 1] - p.s_indptr[slot]);
@@ -409,15 +538,15 @@ __global__ __launch_bounds__(kThreads) void k_attention(const AttnParams p) {
       if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
       __syncthreads();
       if (kk >= 1) {
-        find_bin_from_top<kHist1Bins / kThreads>([&](int i) { return hist[i]; }, (uint32_t)kk,
-                                                 sm.wcnt, sm.res);
+        find_bin_from_top<kHist1Bins, NT>([&](int i) { return ld_dev(hist + i); }, (uint32_t)kk,
+                                          sm.wcnt, sm.res);
       }
       __syncthreads();
       if (tid == 0) {
         p.sel_info[slot * 4 + 0] = sm.res[0];
         p.sel_info[slot * 4 + 1] = (uint32_t)kk - sm.res[1];   // still needed from bin b1
       }
-      for (int i = tid; i < kHist1Bins; i += kThreads) hist[i] = 0u;
+      for (int i = tid; i < kHist1Bins; i += NT) hist[i] = 0u;
       __syncthreads();
     }
   }
@@ -425,10 +554,10 @@ __global__ __launch_bounds__(kThreads) void k_attention(const AttnParams p) {
 
 template <int D, int G>
 hipError_t launch_dg(const AttnParams& p, dim3 grid, hipStream_t st) {
-  if (p.do_topk)
-    hipLaunchKernelGGL((k_attention<D, G, true>), grid, dim3(kThreads), 0, st, p);
+  if (p.waves == 8)
+    hipLaunchKernelGGL((k_attention<D, G, 8>), grid, dim3(512), 0, st, p);
   else
-    hipLaunchKernelGGL((k_attention<D, G, false>), grid, dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((k_attention<D, G, 4>), grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

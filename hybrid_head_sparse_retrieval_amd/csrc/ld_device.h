@@ -41,6 +41,36 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Device-coherent accesses for data handed between workgroups of one launch: stores
+// write through to the device coherence point and loads read from it (sc1), so no
+// L2 writeback/invalidate fence is needed around the hand-off.
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float4 ld_dev4(const float* p) {
+  return make_float4(ld_dev(p), ld_dev(p + 1), ld_dev(p + 2), ld_dev(p + 3));
+}
+
+// Count this workgroup in `ticket` once all of its device-coherent stores have
+// completed; true in every thread of the workgroup that arrives last (of `target`).
+// Every thread must call it.
+__device__ __forceinline__ bool arrive_last(uint32_t* ticket, uint32_t target, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's stores are acknowledged
+  __syncthreads();                 // ... and every other wave's
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = (old == target - 1u);
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
 // DPP lane moves inside a row of 16 lanes.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -76,19 +106,20 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
   return off + x - v;
 }
 
-// Find the digit bin that holds the k-th largest key. `cnt(i)` gives the count of
-// bin i (i < NB, NB = 256*PER). On return (in every thread): bin and the number of
-// keys in bins above it. Requires 1 <= k <= total count.
-template <int PER, typename F>
+// Find the digit bin that holds the k-th largest key, with all NT threads of the
+// workgroup. `cnt(i)` gives the count of bin i (i < NB). On return (in every thread):
+// res[0] = bin, res[1] = number of keys in bins above it. Requires 1 <= k <= total.
+// `tmp` is __shared__ int[NT/64].
+template <int NB, int NT, typename F>
 __device__ __forceinline__ void find_bin_from_top(F cnt, uint32_t k, int* tmp, uint32_t* res) {
+  constexpr int PER = NB / NT;
+  constexpr int NWV = NT / 64;
   const int t = threadIdx.x;
   uint32_t c[PER];
   uint32_t s = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) { c[i] = cnt(t * PER + i); s += c[i]; }
-  // suffix sum over threads with a higher index = exclusive scan in reversed order
-  // (workgroup totals stay below 2^31 since n <= 2^22)
-  int total;
+  // keys in the bins of higher threads: exclusive suffix sum (totals stay below 2^31)
   const int lane = t & 63, wave = t >> 6;
   int x = (int)s;
 #pragma unroll
@@ -98,13 +129,11 @@ __device__ __forceinline__ void find_bin_from_top(F cnt, uint32_t k, int* tmp, u
   }
   if (lane == 0) tmp[wave] = x;
   __syncthreads();
-  int w[4] = {tmp[0], tmp[1], tmp[2], tmp[3]};
-  __syncthreads();
   int above_waves = 0;
-  for (int i = wave + 1; i < 4; ++i) above_waves += w[i];
-  total = w[0] + w[1] + w[2] + w[3];
-  (void)total;
-  uint32_t run = (uint32_t)(above_waves + x - (int)s);   // keys in bins of higher threads
+#pragma unroll
+  for (int i = 0; i < NWV; ++i) above_waves += (i > wave) ? tmp[i] : 0;
+  __syncthreads();
+  uint32_t run = (uint32_t)(above_waves + x - (int)s);
   if (run < k && run + s >= k) {
 #pragma unroll
     for (int i = PER - 1; i >= 0; --i) {

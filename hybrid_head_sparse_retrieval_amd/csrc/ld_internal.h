@@ -36,6 +36,7 @@ struct AttnParams {
   uint64_t active;        // heads computed by this launch
   uint64_t retrieval;     // heads attending to every row (subset of active)
   int ts;                 // rows per split (multiple of 256)
+  int waves;              // waves per workgroup (4 or 8)
   int nsplit;             // splits per sequence at seq_len (grid stride)
   int ngroups;            // KV groups launched
   uint8_t groups[64];     // their ids
@@ -67,15 +68,9 @@ struct SelParams {
   uint32_t* bitmaps; int W;
   int nret; uint8_t heads[64];
   // workspace
-  uint32_t* hist1;        // [slots][kHist1Bins]
-  uint32_t* hist2;        // [slots][kHist2Bins]
-  uint32_t* tickets;      // [slots]
-  uint32_t* sel_info;     // [slots][4]: b1, k1, T, i_tie
-  uint32_t* cand_count;   // [slots]
-  uint32_t* chunk_cnt;    // [slots][C][2]: greater-than count, output offset
-  uint32_t* cand_key;     // [slots][ncap]
-  int32_t* cand_idx;      // [slots][ncap]
-  int64_t ncap;
+  uint32_t* hist1;        // [slots][kHist1Bins], zero between calls
+  uint32_t* tickets;      // [slots], zero between calls
+  uint32_t* sel_info;     // [slots][4]: b1, k1
 };
 
 // Build membership bitmaps of sparse heads from S rows.

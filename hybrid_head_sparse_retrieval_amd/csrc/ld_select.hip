@@ -3,19 +3,18 @@
 // workspace fill).
 //
 // Selection is an exact three-digit radix select on order-preserving 32-bit keys
-// (digit 1 = bits 31..21, digit 2 = bits 20..10, digit 3 = bits 9..0) spread over
-// many workgroups, one per 512-score chunk of a row:
+// (digit 1 = bits 31..21, digit 2 = bits 20..10, digit 3 = bits 9..0):
 //   1. digit-1 histogram of the row (fused into the attention kernel for retrieval
-//      heads, or k_sel_hist for standalone rows); the last workgroup of the row picks
-//      the bin b1 holding the k-th largest key;
-//   2. k_sel_cand: every chunk counts its keys above bin b1 and appends the keys of
-//      bin b1 (the candidates) to a per-row list, plus a digit-2 histogram of them;
-//      the last chunk workgroup of the row resolves digits 2 and 3 on the candidates,
-//      giving the exact threshold key T, and the highest index i_tie among the keys
-//      equal to T that are kept (ties go to lower indices), then the output offset of
-//      every chunk;
-//   3. k_sel_write: every chunk writes its selected indices (key > T, or key == T and
-//      index <= i_tie) in ascending order at its offset, and its membership bitmap.
+//      heads, or k_sel_hist over 512-score chunks for standalone rows); the last
+//      workgroup of the row picks the bin b1 holding the k-th largest key;
+//   2. k_topk_row, one 1024-thread workgroup per row: the keys of bin b1 (the
+//      candidates) go to LDS with their digit-2 histogram, digits 2 and 3 give the
+//      exact threshold key T, and the highest index i_tie among the keys equal to T
+//      that are kept (ties go to lower indices); then every thread writes its
+//      selected indices (key > T, or key == T and index <= i_tie) at its offset from
+//      one workgroup scan, in ascending order, plus one membership bitmap word.
+// Each wave owns 4096 consecutive scores of a 32768-score segment, so a row of up to
+// 32K scores stays in registers between the passes; longer rows are re-read per pass.
 // Only integer atomics are used, so the result is deterministic.
 
 #include "ld_device.h"
@@ -68,20 +67,6 @@ __device__ __forceinline__ RowView row_view(const SelParams& p, int r) {
   return v;
 }
 
-// Arrive at the row's ticket; returns true in every thread of the last workgroup.
-__device__ __forceinline__ bool arrive_last(uint32_t* ticket, uint32_t target, int* flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (old == target - 1u);
-  }
-  __syncthreads();
-  const bool last = *flag != 0;
-  if (last) __threadfence();
-  return last;
-}
-
 // ------------------------------------------------------------- digit-1 histogram
 
 __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
@@ -108,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
   if (!arrive_last(p.tickets + v.slot, nch, &flag)) return;
   if (tid == 0) { res[0] = 0; res[1] = 0; p.tickets[v.slot] = 0; }
   __syncthreads();
-  find_bin_from_top<kHist1Bins / kThreads>([&](int i) { return gh[i]; }, (uint32_t)v.k, tmp, res);
+  find_bin_from_top<kHist1Bins, kThreads>([&](int i) { return ld_dev(gh + i); }, (uint32_t)v.k, tmp, res);
   if (tid == 0) {
     p.sel_info[v.slot * 4 + 0] = res[0];
     p.sel_info[v.slot * 4 + 1] = (uint32_t)v.k - res[1];
@@ -116,188 +101,236 @@ __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
   for (int i = tid; i < kHist1Bins; i += kThreads) gh[i] = 0u;
 }
 
-// ------------------------------------------------- candidates + exact threshold
+// ------------------------------------------------- one workgroup per row
 
-constexpr int kResolveLds = kMaxSelChunks;   // 4096 words, reused by every phase
+constexpr int kRowThreads = 512;
+constexpr int kRowWaves = kRowThreads / 64;
+constexpr int kRounds = 16;                     // 256-score rounds per wave per segment
+constexpr int kWaveSpan = kRounds * 256;        // 4096 scores per wave per segment
+constexpr int kSeg = kRowWaves * kWaveSpan;     // 32768 scores per segment
+constexpr int kCandCap = 8192;                  // candidates kept in LDS
 
-__global__ __launch_bounds__(kThreads) void k_sel_cand(const SelParams p) {
-  __shared__ uint32_t buf[kResolveLds];
-  __shared__ int tmp[4];
-  __shared__ uint32_t res[2];
-  __shared__ int flag;
-  __shared__ uint32_t base_s;
-  const int r = blockIdx.x / p.C, c = blockIdx.x % p.C;
-  const RowView v = row_view(p, r);
-  if (c * kSelChunk >= v.n || v.k < 1) return;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int slot = v.slot;
-  const uint32_t b1 = p.sel_info[slot * 4 + 0];
-
-  uint32_t key[2];
-  bool gt[2], cand[2];
+// Keys of this lane's scores of segment sg: round r holds indices
+// sg*kSeg + wave*kWaveSpan + r*256 + lane*4 + e (coalesced 1 KB per wave load);
+// positions past the end of the row get key 0 and are masked by index.
+__device__ __forceinline__ void load_keys(const float* __restrict__ sc, int n, int wbase, int lane,
+                                          uint32_t (&key)[kRounds][4]) {
+  // wave-uniform test, so that the fast path issues all loads before any wait
+  const bool whole = wbase + kWaveSpan <= n && (reinterpret_cast<uintptr_t>(sc + wbase) & 15u) == 0;
+  if (whole) {
+    float4 x[kRounds];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int i = c * kSelChunk + h * kThreads + tid;
-    const bool valid = i < v.n;
-    key[h] = valid ? score_key(v.sc[i]) : 0u;
-    gt[h] = valid && (key[h] >> 21) > b1;
-    cand[h] = valid && (key[h] >> 21) == b1;
-  }
-  int ngt_total;
-  block_excl_scan((int)gt[0] + (int)gt[1], tmp, ngt_total);
-  int ncand_total;
-  const int cpos = block_excl_scan((int)cand[0] + (int)cand[1], tmp, ncand_total);
-  if (tid == 0) {
-    base_s = ncand_total ? atomicAdd(p.cand_count + slot, (uint32_t)ncand_total) : 0u;
-    p.chunk_cnt[((size_t)slot * p.C + c) * 2 + 0] = (uint32_t)ngt_total;
-  }
-  __syncthreads();
-  {
-    int q = (int)base_s + cpos;
-    uint32_t* ck = p.cand_key + (size_t)slot * p.ncap;
-    int32_t* ci = p.cand_idx + (size_t)slot * p.ncap;
-    uint32_t* h2 = p.hist2 + (size_t)slot * kHist2Bins;
+    for (int r = 0; r < kRounds; ++r) x[r] = *reinterpret_cast<const float4*>(sc + wbase + r * 256 + lane * 4);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (cand[h] && q < p.ncap) {
-        ck[q] = key[h];
-        ci[q] = c * kSelChunk + h * kThreads + tid;
-        atomicAdd(h2 + ((key[h] >> 10) & 0x7ffu), 1u);
-        ++q;
+    for (int r = 0; r < kRounds; ++r) {
+      key[r][0] = score_key(x[r].x); key[r][1] = score_key(x[r].y);
+      key[r][2] = score_key(x[r].z); key[r][3] = score_key(x[r].w);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = wbase + r * 256 + lane * 4 + e;
+        key[r][e] = (i < n) ? score_key(sc[i]) : 0u;
       }
-    }
-  }
-  (void)lane;
-  const uint32_t nch = (uint32_t)((v.n + kSelChunk - 1) / kSelChunk);
-  if (!arrive_last(p.tickets + slot, nch, &flag)) return;
-
-  // ---------------- last chunk workgroup of the row: resolve the threshold
-  const int M = (int)min((int64_t)p.cand_count[slot], p.ncap);
-  const uint32_t k1 = p.sel_info[slot * 4 + 1];
-  const uint32_t* ck = p.cand_key + (size_t)slot * p.ncap;
-  const int32_t* ci = p.cand_idx + (size_t)slot * p.ncap;
-  uint32_t* h2 = p.hist2 + (size_t)slot * kHist2Bins;
-  if (tid == 0) { res[0] = 0; res[1] = 0; p.tickets[slot] = 0; }
-  __syncthreads();
-  find_bin_from_top<kHist2Bins / kThreads>([&](int i) { return h2[i]; }, k1, tmp, res);
-  const uint32_t b2 = res[0];
-  const uint32_t k2 = k1 - res[1];
-  for (int i = tid; i < kHist2Bins; i += kThreads) h2[i] = 0u;
-  // digit 3 over candidates in bin (b1, b2)
-  for (int i = tid; i < kHist3Bins; i += kThreads) buf[i] = 0;
-  __syncthreads();
-  for (int q = tid; q < M; q += kThreads) {
-    const uint32_t kk = ck[q];
-    if (((kk >> 10) & 0x7ffu) == b2) atomicAdd(&buf[kk & 0x3ffu], 1u);
-  }
-  __syncthreads();
-  if (tid == 0) { res[0] = 0; res[1] = 0; }
-  __syncthreads();
-  find_bin_from_top<kHist3Bins / kThreads>([&](int i) { return buf[i]; }, k2, tmp, res);
-  const uint32_t b3 = res[0];
-  const uint32_t e_take = k2 - res[1];          // keys equal to T that are kept
-  const uint32_t nties = buf[b3];
-  const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
-  __syncthreads();
-  // highest kept tie index: the e_take-th smallest index among keys == T
-  uint32_t i_tie = 0x7fffffffu;
-  if (e_take < nties) {
-    // indices are < 2^22: digit A = bits 21..11, digit B = bits 10..0
-    for (int i = tid; i < 2048; i += kThreads) buf[i] = 0;
-    __syncthreads();
-    for (int q = tid; q < M; q += kThreads)
-      if (ck[q] == T) atomicAdd(&buf[(uint32_t)ci[q] >> 11], 1u);
-    __syncthreads();
-    if (tid == 0) { res[0] = 0; res[1] = 0; }
-    __syncthreads();
-    // smallest-index side: search the reversed histogram from its top
-    find_bin_from_top<2048 / kThreads>([&](int i) { return buf[2047 - i]; }, e_take, tmp, res);
-    const uint32_t binA = 2047u - res[0];
-    const uint32_t eB = e_take - res[1];
-    __syncthreads();
-    for (int i = tid; i < 2048; i += kThreads) buf[i] = 0;
-    __syncthreads();
-    for (int q = tid; q < M; q += kThreads)
-      if (ck[q] == T && ((uint32_t)ci[q] >> 11) == binA) atomicAdd(&buf[(uint32_t)ci[q] & 0x7ffu], 1u);
-    __syncthreads();
-    if (tid == 0) { res[0] = 0; res[1] = 0; }
-    __syncthreads();
-    find_bin_from_top<2048 / kThreads>([&](int i) { return buf[2047 - i]; }, eB, tmp, res);
-    i_tie = (binA << 11) | (2047u - res[0]);
-    __syncthreads();
-  }
-  // selected candidates per chunk, then the chunk output offsets
-  const int nchi = (int)nch;
-  for (int i = tid; i < nchi; i += kThreads) buf[i] = 0;
-  __syncthreads();
-  for (int q = tid; q < M; q += kThreads) {
-    const uint32_t kk = ck[q];
-    const uint32_t ix = (uint32_t)ci[q];
-    if (kk > T || (kk == T && ix <= i_tie)) atomicAdd(&buf[ix / kSelChunk], 1u);
-  }
-  __syncthreads();
-  {
-    const int per = (nchi + kThreads - 1) / kThreads;
-    const int c0 = tid * per;
-    int local = 0;
-    for (int i = 0; i < per; ++i) {
-      const int cc = c0 + i;
-      if (cc < nchi) local += (int)(p.chunk_cnt[((size_t)slot * p.C + cc) * 2 + 0] + buf[cc]);
-    }
-    int total;
-    int run = block_excl_scan(local, tmp, total);
-    for (int i = 0; i < per; ++i) {
-      const int cc = c0 + i;
-      if (cc < nchi) {
-        const int cnt = (int)(p.chunk_cnt[((size_t)slot * p.C + cc) * 2 + 0] + buf[cc]);
-        p.chunk_cnt[((size_t)slot * p.C + cc) * 2 + 1] = (uint32_t)run;
-        run += cnt;
-      }
-    }
-  }
-  if (tid == 0) {
-    p.sel_info[slot * 4 + 2] = T;
-    p.sel_info[slot * 4 + 3] = i_tie;
-    p.cand_count[slot] = 0u;
   }
 }
 
-// ------------------------------------------------------------- ordered write
+// Candidate histograms (keys of digit-1 bin b1) by `mode`:
+//   0: digit 2 == b2            -> histogram of digit 3
+//   1: key == T                 -> histogram of index bits 20..11
+//   2: key == T, index bin binA -> histogram of index bits 10..0
+__device__ __forceinline__ void cand_hist_one(int mode, uint32_t kv, uint32_t ix, uint32_t b2, uint32_t T,
+                                              uint32_t binA, uint32_t* hist) {
+  if (mode == 0) {
+    if (((kv >> 10) & 0x7ffu) == b2) atomicAdd(&hist[kv & 0x3ffu], 1u);
+  } else if (mode == 1) {
+    if (kv == T) atomicAdd(&hist[ix >> 11], 1u);
+  } else {
+    if (kv == T && (ix >> 11) == binA) atomicAdd(&hist[ix & 0x7ffu], 1u);
+  }
+}
 
-__global__ __launch_bounds__(kThreads) void k_sel_write(const SelParams p) {
-  __shared__ int tmp[4];
-  const int r = blockIdx.x / p.C, c = blockIdx.x % p.C;
-  const RowView v = row_view(p, r);
-  if (c * kSelChunk >= v.n || v.k < 1) return;
+__global__ __launch_bounds__(kRowThreads) void k_topk_row(const SelParams p) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t ckey[kCandCap];
+  __shared__ uint32_t cidx[kCandCap];
+  __shared__ int tmp[kRowWaves];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t ncand_s;
+  const RowView v = row_view(p, blockIdx.x);
+  const int n = v.n, kk = v.k;
+  if (n < 1 || kk < 1) return;
+  const float* __restrict__ sc = v.sc;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
   const int slot = v.slot;
-  const uint32_t T = p.sel_info[slot * 4 + 2];
-  const uint32_t i_tie = p.sel_info[slot * 4 + 3];
-  int run = (int)p.chunk_cnt[((size_t)slot * p.C + c) * 2 + 1];
+  const uint32_t b1 = p.sel_info[slot * 4 + 0];
+  const uint32_t k1 = p.sel_info[slot * 4 + 1];
+  const int nseg = (n + kSeg - 1) / kSeg;
+
+  uint32_t key[kRounds][4];
+
+  // ---- pass 1: candidates of bin b1 and their digit-2 histogram
+  for (int i = tid; i < 2048; i += kRowThreads) hist[i] = 0;
+  if (tid == 0) ncand_s = 0;
+  __syncthreads();
+  for (int sg = 0; sg < nseg; ++sg) {
+    const int wbase = sg * kSeg + wave * kWaveSpan;
+    load_keys(sc, n, wbase, lane, key);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int i = c * kSelChunk + h * kThreads + tid;
-    const bool valid = i < v.n;
-    float s = 0.f;
-    bool f = false;
-    if (valid) {
-      s = v.sc[i];
-      const uint32_t kk = score_key(s);
-      f = kk > T || (kk == T && (uint32_t)i <= i_tie);
+    for (int r = 0; r < kRounds; ++r) {
+      bool c[4];
+      uint64_t bal[4];
+      uint32_t cnt = 0, before = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ix = wbase + r * 256 + lane * 4 + e;
+        c[e] = ix < n && (key[r][e] >> 21) == b1;
+        bal[e] = __ballot(c[e]);
+        cnt += (uint32_t)__popcll(bal[e]);
+        before += (uint32_t)__popcll(bal[e] & lt_mask);
+      }
+      if (cnt) {                               // one LDS atomic per wave and round
+        uint32_t wb = 0;
+        if (lane == 0) wb = atomicAdd(&ncand_s, cnt);
+        wb = __shfl(wb, 0, 64) + before;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (c[e]) {
+            if (wb < (uint32_t)kCandCap) {
+              ckey[wb] = key[r][e];
+              cidx[wb] = (uint32_t)(wbase + r * 256 + lane * 4 + e);
+            }
+            ++wb;
+            atomicAdd(&hist[(key[r][e] >> 10) & 0x7ffu], 1u);
+          }
+        }
+      }
     }
-    int total;
-    const int pos = block_excl_scan((int)f, tmp, total);
-    if (f && run + pos < v.k) {
-      v.out[run + pos] = i;
-      if (v.vout) v.vout[run + pos] = s;
+  }
+  if (tid == 0) { res[0] = 0; res[1] = 0; }
+  __syncthreads();
+  const uint32_t ncand = ncand_s;
+  const bool in_lds = ncand <= (uint32_t)kCandCap;
+  find_bin_from_top<2048, kRowThreads>([&](int i) { return hist[i]; }, k1, tmp, res);
+  const uint32_t b2 = res[0];
+  const uint32_t k2 = k1 - res[1];
+
+  auto cand_hist = [&](int mode, uint32_t T, uint32_t binA) {
+    for (int i = tid; i < 2048; i += kRowThreads) hist[i] = 0;
+    if (tid == 0) { res[0] = 0; res[1] = 0; }
+    __syncthreads();
+    if (in_lds) {
+      for (int q = tid; q < (int)ncand; q += kRowThreads)
+        cand_hist_one(mode, ckey[q], cidx[q], b2, T, binA, hist);
+    } else {
+      // a one-segment row is still in registers; longer rows are re-read
+      for (int sg = 0; sg < nseg; ++sg) {
+        const int wbase = sg * kSeg + wave * kWaveSpan;
+        if (nseg > 1) load_keys(sc, n, wbase, lane, key);
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int ix = wbase + r * 256 + lane * 4 + e;
+            if (ix < n && (key[r][e] >> 21) == b1) cand_hist_one(mode, key[r][e], (uint32_t)ix, b2, T, binA, hist);
+          }
+      }
     }
-    run += total;
-    if (v.bm) {
-      const uint64_t bal = __ballot(f);
-      const int w0 = (c * kSelChunk + h * kThreads + wave * 64) >> 5;
-      if (lane == 0 && w0 < p.W) v.bm[w0] = (uint32_t)bal;
-      if (lane == 32 && w0 + 1 < p.W) v.bm[w0 + 1] = (uint32_t)(bal >> 32);
+    __syncthreads();
+  };
+
+  // ---- digit 3
+  __syncthreads();
+  cand_hist(0, 0u, 0u);
+  find_bin_from_top<1024, kRowThreads>([&](int i) { return hist[i]; }, k2, tmp, res);
+  const uint32_t b3 = res[0];
+  const uint32_t e_take = k2 - res[1];          // keys equal to T that are kept
+  const uint32_t nties = hist[b3];
+  const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
+  __syncthreads();
+
+  // ---- highest kept tie index: the e_take-th smallest index among keys == T
+  uint32_t i_tie = 0x7fffffffu;
+  if (e_take < nties) {
+    // indices are < 2^21: digit A = bits 20..11 (1024 bins), digit B = bits 10..0
+    cand_hist(1, T, 0u);
+    find_bin_from_top<1024, kRowThreads>([&](int i) { return hist[1023 - i]; }, e_take, tmp, res);
+    const uint32_t binA = 1023u - res[0];
+    const uint32_t eB = e_take - res[1];
+    __syncthreads();
+    cand_hist(2, T, binA);
+    find_bin_from_top<2048, kRowThreads>([&](int i) { return hist[2047 - i]; }, eB, tmp, res);
+    i_tie = (binA << 11) | (2047u - res[0]);
+    __syncthreads();
+  }
+
+  // ---- pass 3: ascending write of the selected indices and the bitmap words
+  int run = 0;
+  for (int sg = 0; sg < nseg; ++sg) {
+    const int wbase = sg * kSeg + wave * kWaveSpan;
+    if (nseg > 1) load_keys(sc, n, wbase, lane, key);
+    uint32_t fl[kRounds];                       // 4 selection bits per round
+    uint32_t wtot = 0;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      fl[r] = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t ix = (uint32_t)(wbase + r * 256 + lane * 4 + e);
+        const bool f = (int)ix < n && (key[r][e] > T || (key[r][e] == T && ix <= i_tie));
+        fl[r] |= (uint32_t)f << e;
+      }
+      wtot += (uint32_t)__popc(fl[r]);
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wtot += __shfl_xor(wtot, o, 64);
+    // wave blocks are contiguous in index order: exclusive scan of the wave totals
+    if (lane == 0) tmp[wave] = (int)wtot;
+    __syncthreads();
+    int woff = 0, stot = 0;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+      woff += (w < wave) ? tmp[w] : 0;
+      stot += tmp[w];
+    }
+    __syncthreads();
+    int pos = run + woff;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      // lanes before this one, then this lane's elements in order
+      int before = 0, rtot = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint64_t b = __ballot((fl[r] >> e) & 1u);
+        before += __popcll(b & lt_mask);
+        rtot += __popcll(b);
+      }
+      int j = pos + before;
+      const int i0 = wbase + r * 256 + lane * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((fl[r] >> e) & 1u) {
+          if (j < kk) {
+            v.out[j] = i0 + e;
+            if (v.vout) v.vout[j] = sc[i0 + e];
+          }
+          ++j;
+        }
+      }
+      pos += rtot;
+      if (v.bm) {                               // 8 lanes x 4 bits = one 32-bit word
+        uint32_t w = fl[r] << ((lane & 7) * 4);
+        w |= __shfl_xor(w, 1, 64);
+        w |= __shfl_xor(w, 2, 64);
+        w |= __shfl_xor(w, 4, 64);
+        const int wi = i0 >> 5;
+        if ((lane & 7) == 0 && i0 < n && wi < p.W) v.bm[wi] = w;
+      }
+    }
+    run += stot;
   }
 }
 
@@ -365,10 +398,9 @@ __global__ __launch_bounds__(kThreads) void k_zero(uint4* p16, size_t n16, uint8
 }  // namespace
 
 hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist) {
-  const dim3 grid((unsigned)p.nrows * (unsigned)p.C);
-  if (with_hist) hipLaunchKernelGGL(k_sel_hist, grid, dim3(kThreads), 0, st, p);
-  hipLaunchKernelGGL(k_sel_cand, grid, dim3(kThreads), 0, st, p);
-  hipLaunchKernelGGL(k_sel_write, grid, dim3(kThreads), 0, st, p);
+  if (with_hist)
+    hipLaunchKernelGGL(k_sel_hist, dim3((unsigned)p.nrows * (unsigned)p.C), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(k_topk_row, dim3((unsigned)p.nrows), dim3(kRowThreads), 0, st, p);
   return hipGetLastError();
 }
 

@@ -77,9 +77,12 @@ enum {
      already describe s_in and need not be rebuilt. */
   LD_FLAG_S_CHAINED = 1u << 1
 };
-/* Optional split-size override in bits 8..11: rows per split = 256 << v (v = 1..4;
-   0 = automatic). */
+/* Optional launch-shape overrides (0 = automatic): rows per attention split =
+   256 << (v - 1) for v = 1..4 in bits 8..11, and waves per attention workgroup in
+   bits 12..13 (1 = 4 waves, 2 = 8 waves). Results do not depend on them beyond fp32
+   rounding. */
 #define LD_FLAG_SPLIT_ROWS(v) ((uint32_t)(v) << 8)
+#define LD_FLAG_WAVES(v) ((uint32_t)(v) << 12)
 
 typedef struct ld_shape {
   int32_t batch;          /* B >= 1 */
