@@ -48,6 +48,11 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-kernel-pass", action="store_true")
     ap.add_argument("--layers-detail", action="store_true", help="print per-layer times to stderr")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE counter files into the traffic summary")
+    ap.add_argument("--counter-commands", default="", help="commands that produced the counter files")
     return ap.parse_args()
 
 
@@ -79,8 +84,83 @@ def layer_bytes(w, l, S_in, d):
     return kv + qo, kv + qo + s_io
 
 
+ATTN_SOURCE = os.path.join(ROOT, "hybrid_head_sparse_retrieval_amd", "csrc", "ld_attention.hip")
+COPY_BYTES = 1 << 30
+
+
+def source_hash(path=ATTN_SOURCE):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"k_attention_{workload}_traffic.json")
+
+
+def copy_calibration():
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {COPY_BYTES} bytes 3 times")
+
+
+def _counter_per_dispatch(csv_path, name_part, counter):
+    """Mean value per dispatch of `counter` over dispatches whose kernel name holds name_part."""
+    import csv
+    vals = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                key = r["Dispatch_Id"]
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return (sum(vals.values()) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def summarize_counters(args):
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.summarize_counters
+    fk, nd = _counter_per_dispatch(fetch_csv, "k_attention", "FETCH_SIZE")
+    wk, _ = _counter_per_dispatch(write_csv, "k_attention", "WRITE_SIZE")
+    cf, _ = _counter_per_dispatch(cfetch_csv, "copy", "FETCH_SIZE")
+    cw, _ = _counter_per_dispatch(cwrite_csv, "copy", "WRITE_SIZE")
+    f_factor = cf * 1024.0 / COPY_BYTES      # counter KiB of a known-size copy over its bytes
+    w_factor = cw * 1024.0 / COPY_BYTES
+    fetch_b = fk * 1024.0 / f_factor
+    write_b = wk * 1024.0 / w_factor
+    out = {"kernel": "k_attention", "workload": args.workload, "dispatches": nd,
+           "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+           "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1), "copy_bytes": COPY_BYTES,
+           "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+           "traffic_bytes_per_launch": int(fetch_b + write_b),
+           "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
+           "source_sha256_16": source_hash(), "commands": args.counter_commands}
+    os.makedirs(os.path.dirname(traffic_path(args.workload)), exist_ok=True)
+    with open(traffic_path(args.workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def load_traffic(workload):
+    """Measured HBM bytes per attention launch, or None when absent or taken on other code."""
+    try:
+        with open(traffic_path(workload)) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    return t["traffic_bytes_per_launch"] if t.get("source_sha256_16") == source_hash() else None
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path).", file=sys.stderr)
@@ -181,7 +261,7 @@ def main():
         avg_bytes = float(np.mean(attn_bytes))
         achieved = avg_bytes / (avg_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(w.name),
                 "kernel": "k_attention<128,4>" if d == 128 and w.group_size == 4 else "k_attention",
                 "avg_launch_us": round(avg_us, 2), "avg_bytes_per_launch": int(avg_bytes),
                 "launches_timed": L}

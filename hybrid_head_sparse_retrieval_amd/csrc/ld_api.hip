@@ -14,16 +14,60 @@ using namespace ld;
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
+constexpr int kSelChunkScores = 4096;   // scores per select chunk workgroup
+
+struct SelArrays {
+  size_t tickets, hist1, hist2;                       // zero between calls
+  size_t sel_info, chunk_cnt, chunk_off, cand_key, cand_idx;
+  int C;
+  int64_t ncap;
+};
+
 struct LayerLayout {
-  int slots, P, W;
-  size_t attn_tickets, hist1;                       // zero between calls
-  size_t sel_info, logits, part_ml, part_acc, bitmaps;
+  int slots, P, P1, W;
+  size_t attn_tickets, attn_tickets_l1;               // zero between calls
+  SelArrays sel;
+  size_t logits, part_ml, part_acc, l1_ml, l1_acc, bitmaps;
   size_t total;
 };
 
 struct SelLayout {
-  size_t tickets, hist1, sel_info, total;
+  SelArrays sel;
+  size_t total;
 };
+
+// Per-row selection scratch for `rows` rows of at most n scores.
+template <typename Take>
+SelArrays sel_arrays(int rows, int n, Take take) {
+  SelArrays a{};
+  a.C = (n + kSelChunkScores - 1) / kSelChunkScores;
+  a.ncap = (int64_t)a.C * kSelChunkScores;
+  a.tickets = take((size_t)rows * 4);
+  a.hist1 = take((size_t)rows * kHist1Bins * 4);
+  a.hist2 = take((size_t)rows * kHist2Bins * 4);
+  a.sel_info = take((size_t)rows * 16);
+  a.chunk_cnt = take((size_t)rows * a.C * 8);
+  a.chunk_off = take((size_t)rows * a.C * 4);
+  a.cand_key = take((size_t)rows * a.ncap * 4);
+  a.cand_idx = take((size_t)rows * a.ncap * 4);
+  return a;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+void fill_sel(SelParams& sp, const SelArrays& a, void* ws) {
+  sp.C = a.C;
+  sp.hist1 = at<uint32_t>(ws, a.hist1);
+  sp.hist2 = at<uint32_t>(ws, a.hist2);
+  sp.tickets = at<uint32_t>(ws, a.tickets);
+  sp.sel_info = at<uint32_t>(ws, a.sel_info);
+  sp.chunk_cnt = at<uint32_t>(ws, a.chunk_cnt);
+  sp.chunk_off = at<uint32_t>(ws, a.chunk_off);
+  sp.cand_key = at<uint32_t>(ws, a.cand_key);
+  sp.cand_idx = at<uint32_t>(ws, a.cand_idx);
+  sp.ncap = a.ncap;
+}
 
 bool shape_ok(const ld_shape* s, ld_status* why) {
   *why = LD_ERR_INVALID_ARGUMENT;
@@ -52,12 +96,15 @@ LayerLayout layer_layout(const ld_shape* s) {
   L.W = (N + 31) / 32;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  L.P1 = (L.P + kMergeRun - 1) / kMergeRun;
   L.attn_tickets = take((size_t)s->batch * s->num_kv_heads * 4);
-  L.hist1 = take((size_t)L.slots * kHist1Bins * 4);
-  L.sel_info = take((size_t)L.slots * 16);
+  L.attn_tickets_l1 = take((size_t)s->batch * s->num_kv_heads * L.P1 * 4);
+  L.sel = sel_arrays(L.slots, N, take);
   L.logits = take((size_t)L.slots * N * 4);
   L.part_ml = take((size_t)L.slots * L.P * 8);
   L.part_acc = take((size_t)L.slots * L.P * s->head_dim * 4);
+  L.l1_ml = take((size_t)L.slots * L.P1 * 8);
+  L.l1_acc = take((size_t)L.slots * L.P1 * s->head_dim * 4);
   L.bitmaps = take((size_t)L.slots * L.W * 4);
   L.total = o;
   return L;
@@ -65,20 +112,14 @@ LayerLayout layer_layout(const ld_shape* s) {
 
 SelLayout sel_layout(int rows, int n) {
   SelLayout L{};
-  (void)n;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
-  L.tickets = take((size_t)rows * 4);
-  L.hist1 = take((size_t)rows * kHist1Bins * 4);
-  L.sel_info = take((size_t)rows * 16);
+  L.sel = sel_arrays(rows, n, take);
   L.total = o;
   return L;
 }
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-template <typename T>
-T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
 // Rows per attention split (256 << (v-1), override v in flag bits 8..11) and waves
 // per workgroup (flag bits 12..13: 1 = 4 waves, 2 = 8 waves). Automatic choice: 8
@@ -184,9 +225,13 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   ap.part_acc = at<float>(ws, L.part_acc);
   ap.P = L.P;
   ap.tickets = at<uint32_t>(ws, L.attn_tickets);
+  ap.tickets_l1 = at<uint32_t>(ws, L.attn_tickets_l1);
+  ap.l1_ml = at<float>(ws, L.l1_ml);
+  ap.l1_acc = at<float>(ws, L.l1_acc);
+  ap.P1 = L.P1;
   ap.do_topk = do_topk ? 1 : 0;
-  ap.hist1 = at<uint32_t>(ws, L.hist1);
-  ap.sel_info = at<uint32_t>(ws, L.sel_info);
+  ap.hist1 = at<uint32_t>(ws, L.sel.hist1);
+  ap.sel_info = at<uint32_t>(ws, L.sel.sel_info);
   ap.k_dense = k;
   ap.s_indptr = s_indptr;
   const dim3 grid((unsigned)((int64_t)B * ng * ap.nsplit));
@@ -197,15 +242,12 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     SelParams sp{};
     sp.mode = 1;
     sp.nrows = B * nret;
-    sp.C = 0;
     sp.logits = ap.logits; sp.Hq = Hq; sp.seq_len = N; sp.kv_indptr = shape->kv_indptr;
     sp.s_out = s_out; sp.s_indptr = s_indptr; sp.k_dense = k;
     sp.bitmaps = bitmaps; sp.W = L.W;
     sp.nret = nret;
     std::memcpy(sp.heads, ret_heads, sizeof(ret_heads));
-    sp.hist1 = at<uint32_t>(ws, L.hist1);
-    sp.tickets = nullptr;
-    sp.sel_info = at<uint32_t>(ws, L.sel_info);
+    fill_sel(sp, L.sel, ws);
     if (launch_select(sp, st, false) != hipSuccess) return LD_ERR_HIP;
   }
   return LD_OK;
@@ -289,12 +331,10 @@ ld_status ld_topk_select(const float* scores, int32_t rows, int32_t n, int64_t r
   SelParams sp{};
   sp.mode = 0;
   sp.nrows = rows;
-  sp.C = (n + kSelChunk - 1) / kSelChunk;
+  sp.Ch = (n + kSelChunk - 1) / kSelChunk;
   sp.scores = scores; sp.row_stride = row_stride; sp.n = n; sp.k = k;
   sp.idx_out = idx_out; sp.val_out = val_out;
-  sp.hist1 = at<uint32_t>(workspace, L.hist1);
-  sp.tickets = at<uint32_t>(workspace, L.tickets);
-  sp.sel_info = at<uint32_t>(workspace, L.sel_info);
+  fill_sel(sp, L.sel, workspace);
   return launch_select(sp, stream, true) == hipSuccess ? LD_OK : LD_ERR_HIP;
 }
 

@@ -89,10 +89,114 @@ struct AttnSmem {
       float w[G][kMaxSplits];        // split maxima, then split weights
       float lp[G][kMaxSplits];       // split sums
       float inv_l[G];
+      float mtot[G];
+      float ltot[G];
       float4 part[TPCOL > 1 ? TPCOL - 1 : 1][COLS];   // partial column sums of the merge
     } cmb;
   } u;
 };
+
+// Merge `cnt` split partials (max in log2 units, sum, unnormalised output) of every
+// active head of the group, taken from src_ml/src_acc at positions s0.. of each head's
+// row of `stride` partials. FINAL: write O = sum acc_p w_p / sum l_p w_p as bf16.
+// Otherwise: write one merged partial at position `upos` of the level-1 arrays
+// (device-coherent, for the merge that follows in another workgroup).
+template <int D, int G, int NW, bool FINAL>
+__device__ __forceinline__ void merge_splits(AttnSmem<D, G, NW>& sm, const AttnParams& p, uint32_t act,
+                                             int hq0, const float* src_ml, const float* src_acc,
+                                             int stride, int s0, int cnt, float* dst_ml, float* dst_acc,
+                                             int upos) {
+  using Smem = AttnSmem<D, G, NW>;
+  constexpr int NT = 64 * NW;
+  constexpr int COLS = Smem::COLS;
+  constexpr int TPCOL = Smem::TPCOL;    // threads per column, each over a share of the splits
+  constexpr int PF = 16;                // partial columns fetched per round
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = tid % COLS, part = tid / COLS;
+  const int j = col / (D / 4), d0 = (col % (D / 4)) * 4;
+  const bool live = part < TPCOL && (act >> j & 1u);
+  const int s_lo = (cnt * part) / TPCOL;
+  const int s_hi = (cnt * (part + 1)) / TPCOL;
+  const __amdgpu_buffer_rsrc_t rr = rsrc(src_acc + ((size_t)(hq0 + j) * stride + s0) * D);
+  float4 x[PF];
+  if (live) {
+#pragma unroll
+    for (int q = 0; q < PF; ++q)
+      if (s_lo + q < s_hi) x[q] = ld_dev4_b(rr, ((s_lo + q) * D + d0) * 4);
+  }
+  // maxima and sums of every (head, split) in one round
+  for (int i = tid; i < G * cnt; i += NT) {
+    const int jj = i / cnt, ss = i % cnt;
+    if (act >> jj & 1u) {
+      const size_t ms = ((size_t)(hq0 + jj) * stride + s0 + ss) * 2;
+      sm.u.cmb.w[jj][ss] = ld_dev(src_ml + ms);
+      sm.u.cmb.lp[jj][ss] = ld_dev(src_ml + ms + 1);
+    }
+  }
+  __syncthreads();
+  for (int jj = wave; jj < G; jj += NW) {
+    if (!(act >> jj & 1u)) continue;
+    float M = -LD_INF;
+    for (int ss = lane; ss < cnt; ss += 64) M = fmaxf(M, sm.u.cmb.w[jj][ss]);
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float mu = (M == -LD_INF) ? 0.f : M;
+    float L = 0.f;
+    for (int ss = lane; ss < cnt; ss += 64) {
+      const float w = exp2_fast(sm.u.cmb.w[jj][ss] - mu);
+      sm.u.cmb.w[jj][ss] = w;
+      L += sm.u.cmb.lp[jj][ss] * w;
+    }
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+    if (lane == 0) {
+      sm.u.cmb.inv_l[jj] = 1.f / L;
+      sm.u.cmb.mtot[jj] = M;
+      sm.u.cmb.ltot[jj] = L;
+    }
+  }
+  __syncthreads();
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (live) {
+    for (int sb = s_lo; sb < s_hi; sb += PF) {
+#pragma unroll
+      for (int q = 0; q < PF; ++q) {
+        if (sb + q < s_hi) {
+          const float w = sm.u.cmb.w[j][sb + q];
+          o.x = fmaf(x[q].x, w, o.x); o.y = fmaf(x[q].y, w, o.y);
+          o.z = fmaf(x[q].z, w, o.z); o.w = fmaf(x[q].w, w, o.w);
+        }
+      }
+      if (sb + PF < s_hi) {
+#pragma unroll
+        for (int q = 0; q < PF; ++q)
+          if (sb + PF + q < s_hi) x[q] = ld_dev4_b(rr, ((sb + PF + q) * D + d0) * 4);
+      }
+    }
+  }
+  if (TPCOL > 1 && live && part > 0) sm.u.cmb.part[part - 1][col] = o;
+  __syncthreads();
+  if (live && part == 0) {
+#pragma unroll
+    for (int q = 1; q < TPCOL; ++q) {
+      const float4 y = sm.u.cmb.part[q - 1][col];
+      o.x += y.x; o.y += y.y; o.z += y.z; o.w += y.w;
+    }
+    if (FINAL) {
+      const float il = sm.u.cmb.inv_l[j];
+      ushort4 r;
+      r.x = f32_to_bf16(o.x * il); r.y = f32_to_bf16(o.y * il);
+      r.z = f32_to_bf16(o.z * il); r.w = f32_to_bf16(o.w * il);
+      *reinterpret_cast<ushort4*>(p.out + (size_t)(hq0 + j) * D + d0) = r;
+    } else {
+      const size_t us = (size_t)(hq0 + j) * p.P1 + upos;
+      st_dev4_b(rsrc(dst_acc + (size_t)(hq0 + j) * p.P1 * D), (upos * D + d0) * 4, o);
+      if (d0 == 0) {
+        st_dev(dst_ml + us * 2 + 0, sm.u.cmb.mtot[j]);
+        st_dev(dst_ml + us * 2 + 1, sm.u.cmb.ltot[j]);
+      }
+    }
+  }
+  __syncthreads();
+}
 
 template <int D, int G, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams p) {
@@ -444,86 +548,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     }
   }
 
-  // ---- ticket: the last split of (b, g) merges all partials
-  if (!arrive_last(p.tickets + b * p.Hkv + g, (uint32_t)nsplit_b, &sm.misc[0])) return;
-  if (tid == 0) p.tickets[b * p.Hkv + g] = 0u;
-
-  const int np = nsplit_b;
-  {
-    constexpr int COLS = Smem::COLS;
-    constexpr int TPCOL = Smem::TPCOL;    // threads per column, each over a share of splits
-    constexpr int PF = 16;                // partial columns fetched per round
-    const int col = tid % COLS, part = tid / COLS;
-    const int j = col / (D / 4), d0 = (col % (D / 4)) * 4;
-    const bool live = part < TPCOL && (act >> j & 1u);
-    const int s_lo = (np * part) / TPCOL;
-    const int s_hi = (np * (part + 1)) / TPCOL;
-    const __amdgpu_buffer_rsrc_t rr = rsrc(p.part_acc + (size_t)(hq0 + j) * p.P * D);
-    float4 x[PF];
-    if (live) {
-#pragma unroll
-      for (int q = 0; q < PF; ++q)
-        if (s_lo + q < s_hi) x[q] = ld_dev4_b(rr, ((s_lo + q) * D + d0) * 4);
-    }
-    // maxima and sums of every (head, split) in one round
-    for (int i = tid; i < G * np; i += NT) {
-      const int jj = i / np, ss = i % np;
-      if (act >> jj & 1u) {
-        const size_t ms = ((size_t)(hq0 + jj) * p.P + ss) * 2;
-        sm.u.cmb.w[jj][ss] = ld_dev(p.part_ml + ms);
-        sm.u.cmb.lp[jj][ss] = ld_dev(p.part_ml + ms + 1);
-      }
-    }
-    __syncthreads();
-    for (int jj = wave; jj < G; jj += NW) {
-      if (!(act >> jj & 1u)) continue;
-      float M = -LD_INF;
-      for (int ss = lane; ss < np; ss += 64) M = fmaxf(M, sm.u.cmb.w[jj][ss]);
-      for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-      const float mu = (M == -LD_INF) ? 0.f : M;
-      float L = 0.f;
-      for (int ss = lane; ss < np; ss += 64) {
-        const float w = exp2_fast(sm.u.cmb.w[jj][ss] - mu);
-        sm.u.cmb.w[jj][ss] = w;
-        L += sm.u.cmb.lp[jj][ss] * w;
-      }
-      for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
-      if (lane == 0) sm.u.cmb.inv_l[jj] = 1.f / L;
-    }
-    __syncthreads();
-    // O[d] = sum_p acc_p[d] * w_p / L over columns of 4 dims
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (live) {
-      for (int s0 = s_lo; s0 < s_hi; s0 += PF) {
-#pragma unroll
-        for (int q = 0; q < PF; ++q) {
-          if (s0 + q < s_hi) {
-            const float w = sm.u.cmb.w[j][s0 + q];
-            o.x = fmaf(x[q].x, w, o.x); o.y = fmaf(x[q].y, w, o.y);
-            o.z = fmaf(x[q].z, w, o.z); o.w = fmaf(x[q].w, w, o.w);
-          }
-        }
-        if (s0 + PF < s_hi) {
-#pragma unroll
-          for (int q = 0; q < PF; ++q)
-            if (s0 + PF + q < s_hi) x[q] = ld_dev4_b(rr, ((s0 + PF + q) * D + d0) * 4);
-        }
-      }
-    }
-    if (TPCOL > 1 && live && part > 0) sm.u.cmb.part[part - 1][col] = o;
-    __syncthreads();
-    if (live && part == 0) {
-#pragma unroll
-      for (int q = 1; q < TPCOL; ++q) {
-        const float4 y = sm.u.cmb.part[q - 1][col];
-        o.x += y.x; o.y += y.y; o.z += y.z; o.w += y.w;
-      }
-      const float il = sm.u.cmb.inv_l[j];
-      ushort4 r;
-      r.x = f32_to_bf16(o.x * il); r.y = f32_to_bf16(o.y * il);
-      r.z = f32_to_bf16(o.z * il); r.w = f32_to_bf16(o.w * il);
-      *reinterpret_cast<ushort4*>(p.out + (size_t)(hq0 + j) * D + d0) = r;
-    }
+  // ---- two-level merge: the last split of each run of kMergeRun splits merges the run
+  // into a level-1 partial while other splits still stream; the last run of (b, g)
+  // merges the level-1 partials into O. One run only: straight into O.
+  const int nu = (nsplit_b + kMergeRun - 1) / kMergeRun;
+  const int u = split / kMergeRun;
+  uint32_t* t2 = p.tickets + b * p.Hkv + g;
+  if (nu == 1) {
+    if (!arrive_last(t2, (uint32_t)nsplit_b, &sm.misc[0])) return;
+    if (tid == 0) *t2 = 0u;
+    merge_splits<D, G, NW, true>(sm, p, act, hq0, p.part_ml, p.part_acc, p.P, 0, nsplit_b, nullptr, nullptr, 0);
+  } else {
+    uint32_t* t1 = p.tickets_l1 + (size_t)(b * p.Hkv + g) * p.P1 + u;
+    const int ucnt = min(kMergeRun, nsplit_b - u * kMergeRun);
+    if (!arrive_last(t1, (uint32_t)ucnt, &sm.misc[0])) return;
+    if (tid == 0) *t1 = 0u;
+    merge_splits<D, G, NW, false>(sm, p, act, hq0, p.part_ml, p.part_acc, p.P, u * kMergeRun, ucnt,
+                                  p.l1_ml, p.l1_acc, u);
+    if (!arrive_last(t2, (uint32_t)nu, &sm.misc[0])) return;
+    if (tid == 0) *t2 = 0u;
+    merge_splits<D, G, NW, true>(sm, p, act, hq0, p.l1_ml, p.l1_acc, p.P1, 0, nu, nullptr, nullptr, 0);
   }
 
   // ---- first selection digit for each retrieval head (fused histogram complete)

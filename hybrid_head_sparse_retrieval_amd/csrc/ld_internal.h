@@ -18,6 +18,7 @@ constexpr int kHist3Bins = 1024;       // digit 3: key bits 9..0
 constexpr int kMaxSeq = 1 << 21;       // seq_len limit
 constexpr int kMaxSelChunks = kMaxSeq / kSelChunk;   // 4096
 constexpr int kMaxSplits = 1024;       // attention splits per sequence
+constexpr int kMergeRun = 16;          // splits merged by one first-level merge
 constexpr int kBitmapWordsPerBlock = 4096;           // bitmap-build LDS tile (16 KiB)
 
 // ---------------------------------------------------------------- parameters
@@ -47,6 +48,10 @@ struct AttnParams {
   float* part_acc;        // [B*Hq][P][D]
   int P;                  // partial stride in splits
   uint32_t* tickets;      // [B*Hkv], zero between calls
+  uint32_t* tickets_l1;   // [B*Hkv][P1], zero between calls
+  float* l1_ml;           // [B*Hq][P1][2]  first-level merged partials
+  float* l1_acc;          // [B*Hq][P1][D]
+  int P1;                 // first-level partial stride (ceil(P / kMergeRun))
   // fused first selection digit (only when do_topk)
   int do_topk;
   uint32_t* hist1;        // [B*Hq][kHist1Bins], zero between calls
@@ -59,7 +64,8 @@ struct AttnParams {
 struct SelParams {
   int mode;               // 0: standalone rows, 1: retrieval rows of a layer
   int nrows;              // rows launched
-  int C;                  // chunk-grid stride (chunks per row at max length)
+  int C;                  // chunk-grid stride of the select passes (4096 scores per chunk)
+  int Ch;                 // chunk-grid stride of the standalone histogram (512 per chunk)
   // standalone
   const float* scores; int64_t row_stride; int n; int k; int32_t* idx_out; float* val_out;
   // layer rows: row r -> (b = r / nret, h = heads[r % nret])
@@ -67,10 +73,16 @@ struct SelParams {
   int32_t* s_out; const int64_t* s_indptr; int k_dense;
   uint32_t* bitmaps; int W;
   int nret; uint8_t heads[64];
-  // workspace
+  // workspace (per row slot)
   uint32_t* hist1;        // [slots][kHist1Bins], zero between calls
+  uint32_t* hist2;        // [slots][kHist2Bins], zero between calls
   uint32_t* tickets;      // [slots], zero between calls
-  uint32_t* sel_info;     // [slots][4]: b1, k1
+  uint32_t* sel_info;     // [slots][4]: b1, k1, T, i_tie
+  uint32_t* chunk_cnt;    // [slots][C][2]: keys above b1, candidates
+  uint32_t* chunk_off;    // [slots][C]: output offset of each chunk
+  uint32_t* cand_key;     // [slots][ncap]
+  uint32_t* cand_idx;     // [slots][ncap]
+  int64_t ncap;
 };
 
 // Build membership bitmaps of sparse heads from S rows.

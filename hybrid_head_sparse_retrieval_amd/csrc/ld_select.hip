@@ -8,14 +8,14 @@
 //      heads, or k_sel_hist over 512-score chunks for standalone rows); the last
 //      workgroup of the row picks the bin b1 holding the k-th largest key;
 //   2. k_topk_row, one 1024-thread workgroup per row: the keys of bin b1 (the
-//      candidates) go to LDS with their digit-2 histogram, digits 2 and 3 give the
-//      exact threshold key T, and the highest index i_tie among the keys equal to T
-//      that are kept (ties go to lower indices); then every thread writes its
-//      selected indices (key > T, or key == T and index <= i_tie) at its offset from
-//      one workgroup scan, in ascending order, plus one membership bitmap word.
-// Each wave owns 4096 consecutive scores of a 32768-score segment, so a row of up to
-// 32K scores stays in registers between the passes; longer rows are re-read per pass.
-// Only integer atomics are used, so the result is deterministic.
+//      candidates) go to LDS with their digit-2 histogram; digits 2 and 3 give the
+//      exact threshold key T and the highest index i_tie among the keys equal to T
+//      that are kept (ties go to lower indices); every wave then writes its selected
+//      indices (key > T, or key == T and index <= i_tie) in ascending order at its
+//      offset from one scan over the wave totals, plus the membership bitmap words.
+// Each wave reads 2048 consecutive scores per 32768-score segment in coalesced 1 KB
+// loads; a row of one segment stays in registers between the passes, longer rows
+// are re-read. Only integer atomics are used, so the result is deterministic.
 
 #include "ld_device.h"
 
@@ -103,19 +103,18 @@ __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
 
 // ------------------------------------------------- one workgroup per row
 
-constexpr int kRowThreads = 512;
+constexpr int kRowThreads = 1024;
 constexpr int kRowWaves = kRowThreads / 64;
-constexpr int kRounds = 16;                     // 256-score rounds per wave per segment
-constexpr int kWaveSpan = kRounds * 256;        // 4096 scores per wave per segment
+constexpr int kRounds = 8;                      // 256-score rounds per wave per segment
+constexpr int kWaveSpan = kRounds * 256;        // 2048 scores per wave per segment
 constexpr int kSeg = kRowWaves * kWaveSpan;     // 32768 scores per segment
 constexpr int kCandCap = 8192;                  // candidates kept in LDS
 
-// Keys of this lane's scores of segment sg: round r holds indices
-// sg*kSeg + wave*kWaveSpan + r*256 + lane*4 + e (coalesced 1 KB per wave load);
-// positions past the end of the row get key 0 and are masked by index.
+// Keys of this lane's scores of one segment: round r holds indices
+// wbase + r*256 + lane*4 + e; positions past the row end get key 0 (masked by index).
 __device__ __forceinline__ void load_keys(const float* __restrict__ sc, int n, int wbase, int lane,
                                           uint32_t (&key)[kRounds][4]) {
-  // wave-uniform test, so that the fast path issues all loads before any wait
+  // wave-uniform test, so that the fast path issues every load before any wait
   const bool whole = wbase + kWaveSpan <= n && (reinterpret_cast<uintptr_t>(sc + wbase) & 15u) == 0;
   if (whole) {
     float4 x[kRounds];
@@ -137,34 +136,57 @@ __device__ __forceinline__ void load_keys(const float* __restrict__ sc, int n, i
   }
 }
 
-// Candidate histograms (keys of digit-1 bin b1) by `mode`:
-//   0: digit 2 == b2            -> histogram of digit 3
-//   1: key == T                 -> histogram of index bits 20..11
-//   2: key == T, index bin binA -> histogram of index bits 10..0
-__device__ __forceinline__ void cand_hist_one(int mode, uint32_t kv, uint32_t ix, uint32_t b2, uint32_t T,
-                                              uint32_t binA, uint32_t* hist) {
-  if (mode == 0) {
-    if (((kv >> 10) & 0x7ffu) == b2) atomicAdd(&hist[kv & 0x3ffu], 1u);
-  } else if (mode == 1) {
-    if (kv == T) atomicAdd(&hist[ix >> 11], 1u);
-  } else {
-    if (kv == T && (ix >> 11) == binA) atomicAdd(&hist[ix & 0x7ffu], 1u);
-  }
+// Bit (4r + e) set for the keys of this lane that satisfy the predicate.
+template <typename P>
+__device__ __forceinline__ uint32_t key_mask(const uint32_t (&key)[kRounds][4], int wbase, int lane, int n,
+                                             P pred) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = wbase + r * 256 + lane * 4 + e;
+      m |= (uint32_t)(i < n && pred(key[r][e], (uint32_t)i)) << (4 * r + e);
+    }
+  return m;
 }
 
+__device__ __forceinline__ uint32_t key_at(const uint32_t (&key)[kRounds][4], int bit) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v = (bit == 4 * r + e) ? key[r][e] : v;
+  return v;
+}
+
+__device__ __forceinline__ int wave_excl_scan(int x, int lane, int& total) {
+  int v = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  total = __shfl(v, 63, 64);
+  return v - x;
+}
+
+struct RowSmem {
+  uint32_t hist[2048];
+  uint32_t ckey[kCandCap];
+  uint32_t cidx[kCandCap];
+  int tmp[kRowWaves];
+  uint32_t res[2];
+  uint32_t ncand;
+};
+
 __global__ __launch_bounds__(kRowThreads) void k_topk_row(const SelParams p) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t ckey[kCandCap];
-  __shared__ uint32_t cidx[kCandCap];
-  __shared__ int tmp[kRowWaves];
-  __shared__ uint32_t res[2];
-  __shared__ uint32_t ncand_s;
+  __shared__ RowSmem sm;
   const RowView v = row_view(p, blockIdx.x);
   const int n = v.n, kk = v.k;
   if (n < 1 || kk < 1) return;
   const float* __restrict__ sc = v.sc;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
   const int slot = v.slot;
   const uint32_t b1 = p.sel_info[slot * 4 + 0];
   const uint32_t k1 = p.sel_info[slot * 4 + 1];
@@ -172,71 +194,65 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const SelParams p) {
 
   uint32_t key[kRounds][4];
 
-  // ---- pass 1: candidates of bin b1 and their digit-2 histogram
-  for (int i = tid; i < 2048; i += kRowThreads) hist[i] = 0;
-  if (tid == 0) ncand_s = 0;
+  // ---- pass 1: candidates of bin b1 (LDS) and their digit-2 histogram
+  for (int i = tid; i < 2048; i += kRowThreads) sm.hist[i] = 0;
+  if (tid == 0) sm.ncand = 0;
   __syncthreads();
   for (int sg = 0; sg < nseg; ++sg) {
     const int wbase = sg * kSeg + wave * kWaveSpan;
     load_keys(sc, n, wbase, lane, key);
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      bool c[4];
-      uint64_t bal[4];
-      uint32_t cnt = 0, before = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ix = wbase + r * 256 + lane * 4 + e;
-        c[e] = ix < n && (key[r][e] >> 21) == b1;
-        bal[e] = __ballot(c[e]);
-        cnt += (uint32_t)__popcll(bal[e]);
-        before += (uint32_t)__popcll(bal[e] & lt_mask);
-      }
-      if (cnt) {                               // one LDS atomic per wave and round
-        uint32_t wb = 0;
-        if (lane == 0) wb = atomicAdd(&ncand_s, cnt);
-        wb = __shfl(wb, 0, 64) + before;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (c[e]) {
-            if (wb < (uint32_t)kCandCap) {
-              ckey[wb] = key[r][e];
-              cidx[wb] = (uint32_t)(wbase + r * 256 + lane * 4 + e);
-            }
-            ++wb;
-            atomicAdd(&hist[(key[r][e] >> 10) & 0x7ffu], 1u);
-          }
+    uint32_t cm = key_mask(key, wbase, lane, n, [&](uint32_t kv, uint32_t) { return (kv >> 21) == b1; });
+    int wtot;
+    const int before = wave_excl_scan(__popc(cm), lane, wtot);
+    if (wtot) {
+      uint32_t wb = 0;
+      if (lane == 0) wb = atomicAdd(&sm.ncand, (uint32_t)wtot);
+      uint32_t q = __shfl(wb, 0, 64) + (uint32_t)before;
+      while (cm) {
+        const int bit = __builtin_ctz(cm);
+        cm &= cm - 1u;
+        const uint32_t kv = key_at(key, bit);
+        if (q < (uint32_t)kCandCap) {
+          sm.ckey[q] = kv;
+          sm.cidx[q] = (uint32_t)(wbase + (bit >> 2) * 256 + lane * 4 + (bit & 3));
         }
+        ++q;
+        atomicAdd(&sm.hist[(kv >> 10) & 0x7ffu], 1u);
       }
     }
   }
-  if (tid == 0) { res[0] = 0; res[1] = 0; }
+  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
   __syncthreads();
-  const uint32_t ncand = ncand_s;
+  const uint32_t ncand = sm.ncand;
   const bool in_lds = ncand <= (uint32_t)kCandCap;
-  find_bin_from_top<2048, kRowThreads>([&](int i) { return hist[i]; }, k1, tmp, res);
-  const uint32_t b2 = res[0];
-  const uint32_t k2 = k1 - res[1];
+  find_bin_from_top<2048, kRowThreads>([&](int i) { return sm.hist[i]; }, k1, sm.tmp, sm.res);
+  const uint32_t b2 = sm.res[0];
+  const uint32_t k2 = k1 - sm.res[1];
 
+  // candidate histograms: mode 0 digit 3 of bin (b1, b2); 1 index bits 20..11 of keys
+  // == T; 2 index bits 10..0 of keys == T in index bin binA
   auto cand_hist = [&](int mode, uint32_t T, uint32_t binA) {
-    for (int i = tid; i < 2048; i += kRowThreads) hist[i] = 0;
-    if (tid == 0) { res[0] = 0; res[1] = 0; }
+    for (int i = tid; i < 2048; i += kRowThreads) sm.hist[i] = 0;
+    if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
     __syncthreads();
+    auto one = [&](uint32_t kv, uint32_t ix) {
+      if (mode == 0) { if (((kv >> 10) & 0x7ffu) == b2) atomicAdd(&sm.hist[kv & 0x3ffu], 1u); }
+      else if (mode == 1) { if (kv == T) atomicAdd(&sm.hist[ix >> 11], 1u); }
+      else { if (kv == T && (ix >> 11) == binA) atomicAdd(&sm.hist[ix & 0x7ffu], 1u); }
+    };
     if (in_lds) {
-      for (int q = tid; q < (int)ncand; q += kRowThreads)
-        cand_hist_one(mode, ckey[q], cidx[q], b2, T, binA, hist);
+      for (uint32_t q = tid; q < ncand; q += kRowThreads) one(sm.ckey[q], sm.cidx[q]);
     } else {
       // a one-segment row is still in registers; longer rows are re-read
       for (int sg = 0; sg < nseg; ++sg) {
         const int wbase = sg * kSeg + wave * kWaveSpan;
         if (nseg > 1) load_keys(sc, n, wbase, lane, key);
-#pragma unroll
-        for (int r = 0; r < kRounds; ++r)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int ix = wbase + r * 256 + lane * 4 + e;
-            if (ix < n && (key[r][e] >> 21) == b1) cand_hist_one(mode, key[r][e], (uint32_t)ix, b2, T, binA, hist);
-          }
+        uint32_t cm = key_mask(key, wbase, lane, n, [&](uint32_t kv, uint32_t) { return (kv >> 21) == b1; });
+        while (cm) {
+          const int bit = __builtin_ctz(cm);
+          cm &= cm - 1u;
+          one(key_at(key, bit), (uint32_t)(wbase + (bit >> 2) * 256 + lane * 4 + (bit & 3)));
+        }
       }
     }
     __syncthreads();
@@ -245,10 +261,10 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const SelParams p) {
   // ---- digit 3
   __syncthreads();
   cand_hist(0, 0u, 0u);
-  find_bin_from_top<1024, kRowThreads>([&](int i) { return hist[i]; }, k2, tmp, res);
-  const uint32_t b3 = res[0];
-  const uint32_t e_take = k2 - res[1];          // keys equal to T that are kept
-  const uint32_t nties = hist[b3];
+  find_bin_from_top<1024, kRowThreads>([&](int i) { return sm.hist[i]; }, k2, sm.tmp, sm.res);
+  const uint32_t b3 = sm.res[0];
+  const uint32_t e_take = k2 - sm.res[1];       // keys equal to T that are kept
+  const uint32_t nties = sm.hist[b3];
   const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
   __syncthreads();
 
@@ -257,13 +273,13 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const SelParams p) {
   if (e_take < nties) {
     // indices are < 2^21: digit A = bits 20..11 (1024 bins), digit B = bits 10..0
     cand_hist(1, T, 0u);
-    find_bin_from_top<1024, kRowThreads>([&](int i) { return hist[1023 - i]; }, e_take, tmp, res);
-    const uint32_t binA = 1023u - res[0];
-    const uint32_t eB = e_take - res[1];
+    find_bin_from_top<1024, kRowThreads>([&](int i) { return sm.hist[1023 - i]; }, e_take, sm.tmp, sm.res);
+    const uint32_t binA = 1023u - sm.res[0];
+    const uint32_t eB = e_take - sm.res[1];
     __syncthreads();
     cand_hist(2, T, binA);
-    find_bin_from_top<2048, kRowThreads>([&](int i) { return hist[2047 - i]; }, eB, tmp, res);
-    i_tie = (binA << 11) | (2047u - res[0]);
+    find_bin_from_top<2048, kRowThreads>([&](int i) { return sm.hist[2047 - i]; }, eB, sm.tmp, sm.res);
+    i_tie = (binA << 11) | (2047u - sm.res[0]);
     __syncthreads();
   }
 
@@ -272,57 +288,42 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const SelParams p) {
   for (int sg = 0; sg < nseg; ++sg) {
     const int wbase = sg * kSeg + wave * kWaveSpan;
     if (nseg > 1) load_keys(sc, n, wbase, lane, key);
-    uint32_t fl[kRounds];                       // 4 selection bits per round
-    uint32_t wtot = 0;
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      fl[r] = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t ix = (uint32_t)(wbase + r * 256 + lane * 4 + e);
-        const bool f = (int)ix < n && (key[r][e] > T || (key[r][e] == T && ix <= i_tie));
-        fl[r] |= (uint32_t)f << e;
-      }
-      wtot += (uint32_t)__popc(fl[r]);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) wtot += __shfl_xor(wtot, o, 64);
-    // wave blocks are contiguous in index order: exclusive scan of the wave totals
-    if (lane == 0) tmp[wave] = (int)wtot;
+    const uint32_t fm = key_mask(key, wbase, lane, n, [&](uint32_t kv, uint32_t ix) {
+      return kv > T || (kv == T && ix <= i_tie);
+    });
+    // waves hold consecutive index blocks: exclusive scan of the wave totals
+    int wtot;
+    (void)wave_excl_scan(__popc(fm), lane, wtot);
+    if (lane == 0) sm.tmp[wave] = wtot;
     __syncthreads();
     int woff = 0, stot = 0;
 #pragma unroll
     for (int w = 0; w < kRowWaves; ++w) {
-      woff += (w < wave) ? tmp[w] : 0;
-      stot += tmp[w];
+      woff += (w < wave) ? sm.tmp[w] : 0;
+      stot += sm.tmp[w];
     }
     __syncthreads();
     int pos = run + woff;
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
-      // lanes before this one, then this lane's elements in order
-      int before = 0, rtot = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint64_t b = __ballot((fl[r] >> e) & 1u);
-        before += __popcll(b & lt_mask);
-        rtot += __popcll(b);
-      }
+      const uint32_t nib = (fm >> (4 * r)) & 0xfu;
+      int rtot;
+      const int before = wave_excl_scan(__popc(nib), lane, rtot);
       int j = pos + before;
       const int i0 = wbase + r * 256 + lane * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if ((fl[r] >> e) & 1u) {
-          if (j < kk) {
-            v.out[j] = i0 + e;
-            if (v.vout) v.vout[j] = sc[i0 + e];
-          }
-          ++j;
+      uint32_t m = nib;
+      while (m) {
+        const int e = __builtin_ctz(m);
+        m &= m - 1u;
+        if (j < kk) {
+          v.out[j] = i0 + e;
+          if (v.vout) v.vout[j] = sc[i0 + e];
         }
+        ++j;
       }
       pos += rtot;
       if (v.bm) {                               // 8 lanes x 4 bits = one 32-bit word
-        uint32_t w = fl[r] << ((lane & 7) * 4);
+        uint32_t w = nib << ((lane & 7) * 4);
         w |= __shfl_xor(w, 1, 64);
         w |= __shfl_xor(w, 2, 64);
         w |= __shfl_xor(w, 4, 64);
@@ -398,8 +399,11 @@ __global__ __launch_bounds__(kThreads) void k_zero(uint4* p16, size_t n16, uint8
 }  // namespace
 
 hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist) {
-  if (with_hist)
-    hipLaunchKernelGGL(k_sel_hist, dim3((unsigned)p.nrows * (unsigned)p.C), dim3(kThreads), 0, st, p);
+  if (with_hist) {
+    SelParams ph = p;
+    ph.C = p.Ch;
+    hipLaunchKernelGGL(k_sel_hist, dim3((unsigned)p.nrows * (unsigned)p.Ch), dim3(kThreads), 0, st, ph);
+  }
   hipLaunchKernelGGL(k_topk_row, dim3((unsigned)p.nrows), dim3(kRowThreads), 0, st, p);
   return hipGetLastError();
 }
