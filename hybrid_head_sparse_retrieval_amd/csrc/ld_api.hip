@@ -1,6 +1,7 @@
 // Host side of liblychee_decode.so: argument validation, workspace layout and the
 // launch sequence of one layer (declared in include/lychee_decode.h).
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -14,11 +15,10 @@ using namespace ld;
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
-constexpr int kSelChunkScores = 4096;   // scores per select chunk workgroup
 
 struct SelArrays {
-  size_t tickets, hist1, hist2;                       // zero between calls
-  size_t sel_info, chunk_cnt, chunk_off, cand_key, cand_idx;
+  size_t tickets, hist1, hist2, depart, err;          // zero between calls
+  size_t sel_info, span_cnt, span_off, cand;
   int C;
   int64_t ncap;
 };
@@ -40,16 +40,17 @@ struct SelLayout {
 template <typename Take>
 SelArrays sel_arrays(int rows, int n, Take take) {
   SelArrays a{};
-  a.C = (n + kSelChunkScores - 1) / kSelChunkScores;
-  a.ncap = (int64_t)a.C * kSelChunkScores;
+  a.C = (n + kSelSpan - 1) / kSelSpan;
+  a.ncap = (int64_t)a.C * kSelSpan;
   a.tickets = take((size_t)rows * 4);
   a.hist1 = take((size_t)rows * kHist1Bins * 4);
   a.hist2 = take((size_t)rows * kHist2Bins * 4);
+  a.depart = take((size_t)rows * 4);
+  a.err = take(4);
   a.sel_info = take((size_t)rows * 16);
-  a.chunk_cnt = take((size_t)rows * a.C * 8);
-  a.chunk_off = take((size_t)rows * a.C * 4);
-  a.cand_key = take((size_t)rows * a.ncap * 4);
-  a.cand_idx = take((size_t)rows * a.ncap * 4);
+  a.span_cnt = take((size_t)rows * a.C * 8);
+  a.span_off = take((size_t)rows * a.C * 4);
+  a.cand = take((size_t)rows * a.ncap * 8);
   return a;
 }
 
@@ -61,11 +62,12 @@ void fill_sel(SelParams& sp, const SelArrays& a, void* ws) {
   sp.hist1 = at<uint32_t>(ws, a.hist1);
   sp.hist2 = at<uint32_t>(ws, a.hist2);
   sp.tickets = at<uint32_t>(ws, a.tickets);
+  sp.depart = at<uint32_t>(ws, a.depart);
+  sp.err = at<uint32_t>(ws, a.err);
   sp.sel_info = at<uint32_t>(ws, a.sel_info);
-  sp.chunk_cnt = at<uint32_t>(ws, a.chunk_cnt);
-  sp.chunk_off = at<uint32_t>(ws, a.chunk_off);
-  sp.cand_key = at<uint32_t>(ws, a.cand_key);
-  sp.cand_idx = at<uint32_t>(ws, a.cand_idx);
+  sp.span_cnt = at<uint32_t>(ws, a.span_cnt);
+  sp.span_off = at<uint32_t>(ws, a.span_off);
+  sp.cand = at<uint64_t>(ws, a.cand);
   sp.ncap = a.ncap;
 }
 
@@ -121,21 +123,35 @@ SelLayout sel_layout(int rows, int n) {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+  cache[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
 // Rows per attention split (256 << (v-1), override v in flag bits 8..11) and waves
-// per workgroup (flag bits 12..13: 1 = 4 waves, 2 = 8 waves). Automatic choice: 8
-// waves and the smallest split of at least 512 rows that keeps the launch at or below
-// 512 workgroups (two per compute unit over the launch), capped so that no sequence
-// needs more than kMaxSplits splits.
+// per workgroup (flag bits 12..13: 1 = 4 waves, 2 = 8 waves). Automatic choice: 4
+// waves and the smallest split of at least 256 rows that keeps the launch within one
+// round of resident workgroups (two 4-wave workgroups per compute unit: the kernel
+// holds over 128 VGPRs per lane), capped so that no sequence needs more than
+// kMaxSplits splits.
 void choose_split(int N, int64_t groups_total, uint32_t flags, int* ts_out, int* waves_out) {
   const int wv = (int)((flags >> 12) & 0x3u);
-  const int waves = (wv == 1) ? 4 : 8;
+  const int waves = (wv == 2) ? 8 : 4;
   const int v = (int)((flags >> 8) & 0xfu);
   int ts;
   if (v >= 1 && v <= 4) {
     ts = 256 << (v - 1);
   } else {
-    ts = waves == 8 ? 512 : 256;
-    while (ts < kMaxSplitRows && groups_total * (int64_t)((N + ts - 1) / ts) > 512) ts <<= 1;
+    const int64_t resident = (int64_t)cu_count() * (waves == 8 ? 1 : 2);
+    ts = 256;
+    while (ts < kMaxSplitRows && groups_total * (int64_t)((N + ts - 1) / ts) > resident) ts <<= 1;
   }
   while ((N + ts - 1) / ts > kMaxSplits && ts < kMaxSplitRows) ts <<= 1;
   *ts_out = ts;

@@ -110,19 +110,21 @@ __device__ __forceinline__ void merge_splits(AttnSmem<D, G, NW>& sm, const AttnP
   constexpr int NT = 64 * NW;
   constexpr int COLS = Smem::COLS;
   constexpr int TPCOL = Smem::TPCOL;    // threads per column, each over a share of the splits
-  constexpr int PF = 16;                // partial columns fetched per round
+  constexpr int PF = 32;                // partial columns fetched per round
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = tid % COLS, part = tid / COLS;
   const int j = col / (D / 4), d0 = (col % (D / 4)) * 4;
   const bool live = part < TPCOL && (act >> j & 1u);
   const int s_lo = (cnt * part) / TPCOL;
   const int s_hi = (cnt * (part + 1)) / TPCOL;
-  const __amdgpu_buffer_rsrc_t rr = rsrc(src_acc + ((size_t)(hq0 + j) * stride + s0) * D);
+  // one workgroup-uniform resource (a per-lane base would need a waterfall loop)
+  const __amdgpu_buffer_rsrc_t rr = rsrc(src_acc + ((size_t)hq0 * stride + s0) * D);
+  const int jrow = j * stride * D;      // this column's head row, in floats
   float4 x[PF];
   if (live) {
 #pragma unroll
     for (int q = 0; q < PF; ++q)
-      if (s_lo + q < s_hi) x[q] = ld_dev4_b(rr, ((s_lo + q) * D + d0) * 4);
+      if (s_lo + q < s_hi) x[q] = ld_dev4_b(rr, (jrow + (s_lo + q) * D + d0) * 4);
   }
   // maxima and sums of every (head, split) in one round
   for (int i = tid; i < G * cnt; i += NT) {
@@ -138,7 +140,7 @@ __device__ __forceinline__ void merge_splits(AttnSmem<D, G, NW>& sm, const AttnP
     if (!(act >> jj & 1u)) continue;
     float M = -LD_INF;
     for (int ss = lane; ss < cnt; ss += 64) M = fmaxf(M, sm.u.cmb.w[jj][ss]);
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    M = wave_max_f(M);
     const float mu = (M == -LD_INF) ? 0.f : M;
     float L = 0.f;
     for (int ss = lane; ss < cnt; ss += 64) {
@@ -146,7 +148,7 @@ __device__ __forceinline__ void merge_splits(AttnSmem<D, G, NW>& sm, const AttnP
       sm.u.cmb.w[jj][ss] = w;
       L += sm.u.cmb.lp[jj][ss] * w;
     }
-    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+    L = wave_sum_f(L);
     if (lane == 0) {
       sm.u.cmb.inv_l[jj] = 1.f / L;
       sm.u.cmb.mtot[jj] = M;
@@ -168,7 +170,7 @@ __device__ __forceinline__ void merge_splits(AttnSmem<D, G, NW>& sm, const AttnP
       if (sb + PF < s_hi) {
 #pragma unroll
         for (int q = 0; q < PF; ++q)
-          if (sb + PF + q < s_hi) x[q] = ld_dev4_b(rr, ((sb + PF + q) * D + d0) * 4);
+          if (sb + PF + q < s_hi) x[q] = ld_dev4_b(rr, (jrow + (sb + PF + q) * D + d0) * 4);
       }
     }
   }
@@ -188,7 +190,7 @@ __device__ __forceinline__ void merge_splits(AttnSmem<D, G, NW>& sm, const AttnP
       *reinterpret_cast<ushort4*>(p.out + (size_t)(hq0 + j) * D + d0) = r;
     } else {
       const size_t us = (size_t)(hq0 + j) * p.P1 + upos;
-      st_dev4_b(rsrc(dst_acc + (size_t)(hq0 + j) * p.P1 * D), (upos * D + d0) * 4, o);
+      st_dev4_b(rsrc(dst_acc + (size_t)hq0 * p.P1 * D), ((j * p.P1 + upos) * D + d0) * 4, o);
       if (d0 == 0) {
         st_dev(dst_ml + us * 2 + 0, sm.u.cmb.mtot[j]);
         st_dev(dst_ml + us * 2 + 1, sm.u.cmb.ltot[j]);
@@ -411,8 +413,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
         cm = fmaxf(cm, tl[t][r]);
       }
     }
-    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    cm = max_xor32(max_xor16(cm));
     const float mn = fmaxf(m_lane, cm);
     const float mu = (mn == -LD_INF) ? 0.f : mn;
     const float alpha = exp2_fast(m_lane - mu);       // 0 when m_lane was -inf
@@ -488,17 +489,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   __syncthreads();   // the LDS union is reused below
 
   // ---- wave totals: sum of head mr over the 4 k-groups; outputs over row pairs
-  l_lane += __shfl_xor(l_lane, 16, 64);
-  l_lane += __shfl_xor(l_lane, 32, 64);
+  l_lane = add_xor32(add_xor16(l_lane));
 #pragma unroll
   for (int j = 0; j < G; ++j)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[j][e] += __shfl_xor(acc[j][e], 8, 64);
+    for (int e = 0; e < EPL; ++e) acc[j][e] += xor8_f(acc[j][e]);
   if (RP == 2) {
 #pragma unroll
     for (int j = 0; j < G; ++j)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[j][e] += __shfl_xor(acc[j][e], 16, 64);
+      for (int e = 0; e < EPL; ++e) acc[j][e] = add_xor16(acc[j][e]);
   }
   constexpr int RSTEP = 8 / RP;               // row slots folded into one part
   if ((rg % RSTEP) == 0) {
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       a.x += x.x * sc; a.y += x.y * sc; a.z += x.z * sc; a.w += x.w * sc;
     }
     const size_t pslot = (size_t)(hq0 + j) * p.P + split;
-    st_dev4_b(rsrc(p.part_acc + (size_t)(hq0 + j) * p.P * D), (split * D + d0) * 4, a);
+    st_dev4_b(rsrc(p.part_acc + (size_t)hq0 * p.P * D), ((j * p.P + split) * D + d0) * 4, a);
     if (d0 == 0) {
       st_dev(p.part_ml + pslot * 2 + 0, M);
       st_dev(p.part_ml + pslot * 2 + 1, L);

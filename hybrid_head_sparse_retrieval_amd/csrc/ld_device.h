@@ -71,11 +71,18 @@ __device__ __forceinline__ bool arrive_last(uint32_t* ticket, uint32_t target, i
   return *flag != 0;
 }
 
-// DPP lane moves inside a row of 16 lanes.
+// ---- cross-lane steps without the LDS crossbar: DPP moves inside rows of 16 lanes,
+// row broadcasts, and the gfx950 row-pair / half-wave swaps.
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
+template <int CTRL, int ROWS = 0xf, bool ZERO = false>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, ZERO);
+}
+
 // Sum over each aligned group of 8 lanes; every lane of the group receives the same
 // (bitwise identical) total: xor-1, xor-2 quad permutes, then the half-row mirror.
 __device__ __forceinline__ float sum8(float v) {
@@ -84,26 +91,72 @@ __device__ __forceinline__ float sum8(float v) {
   v += dpp_f<0x141>(v);   // row_half_mirror
   return v;
 }
+__device__ __forceinline__ int sum8_i(int v) {
+  v += dpp_i<0xB1>(v);
+  v += dpp_i<0x4E>(v);
+  v += dpp_i<0x141>(v);
+  return v;
+}
 
-__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+// Partner 8 lanes away inside the row of 16 (row_ror:8 is lane ^ 8 there).
+__device__ __forceinline__ float xor8_f(float v) { return dpp_f<0x128>(v); }
 
-// Exclusive scan over the 256 threads of a workgroup (thread order). `tmp` is
-// __shared__ int[4]. Returns the exclusive prefix; `total` receives the sum.
-__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) tmp[wave] = x;
-  __syncthreads();
-  int w0 = tmp[0], w1 = tmp[1], w2 = tmp[2], w3 = tmp[3];
-  __syncthreads();
-  int off = (wave > 0 ? w0 : 0) + (wave > 1 ? w1 : 0) + (wave > 2 ? w2 : 0);
-  total = w0 + w1 + w2 + w3;
-  return off + x - v;
+// Values of a lane and of its partner 16 (32) lanes away: v_permlane16_swap
+// (v_permlane32_swap) of v with itself leaves the even-row (lower-half) value in the
+// first result and the odd-row (upper-half) value in the second, in both lanes of the
+// pair, so an operation on the two is bitwise the same in both.
+__device__ __forceinline__ float add_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Max / sum over the 64 lanes, the same value in every lane.
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, xor8_f(v));
+  v = max_xor16(v);
+  return max_xor32(v);
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v = sum8(v);
+  v += xor8_f(v);
+  v = add_xor16(v);
+  return add_xor32(v);
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each row of 16
+// (zero fill), then lane 15 of a row added to rows 1 and 3 and lane 31 to rows 2, 3.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  v += dpp_i<0x111, 0xf, true>(v);   // row_shr:1
+  v += dpp_i<0x112, 0xf, true>(v);   // row_shr:2
+  v += dpp_i<0x114, 0xf, true>(v);   // row_shr:4
+  v += dpp_i<0x118, 0xf, true>(v);   // row_shr:8
+  v += dpp_i<0x142, 0xa>(v);         // row_bcast:15
+  v += dpp_i<0x143, 0xc>(v);         // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ int wave_total(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_sum(v), 63);
+}
+// Exclusive prefix sum over the wave; `total` receives the wave's sum.
+__device__ __forceinline__ int wave_excl_scan(int x, int& total) {
+  const int inc = wave_incl_sum(x);
+  total = __builtin_amdgcn_readlane(inc, 63);
+  return inc - x;
 }
 
 // Find the digit bin that holds the k-th largest key, with all NT threads of the
@@ -121,12 +174,10 @@ __device__ __forceinline__ void find_bin_from_top(F cnt, uint32_t k, int* tmp, u
   for (int i = 0; i < PER; ++i) { c[i] = cnt(t * PER + i); s += c[i]; }
   // keys in the bins of higher threads: exclusive suffix sum (totals stay below 2^31)
   const int lane = t & 63, wave = t >> 6;
-  int x = (int)s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_down(x, o, 64);
-    if (lane + o < 64) x += y;
-  }
+  // keys in this lane's bins and the bins of higher lanes of the wave
+  const int inc = wave_incl_sum((int)s);
+  const int wtot = __builtin_amdgcn_readlane(inc, 63);
+  const int x = wtot - inc + (int)s;
   if (lane == 0) tmp[wave] = x;
   __syncthreads();
   int above_waves = 0;

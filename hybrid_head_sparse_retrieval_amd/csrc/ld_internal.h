@@ -17,8 +17,10 @@ constexpr int kHist2Bins = 2048;       // digit 2: key bits 20..10
 constexpr int kHist3Bins = 1024;       // digit 3: key bits 9..0
 constexpr int kMaxSeq = 1 << 21;       // seq_len limit
 constexpr int kMaxSelChunks = kMaxSeq / kSelChunk;   // 4096
+constexpr int kSelSpan = 16384;        // scores per candidate / write workgroup (1024 x 16)
+constexpr int kMaxSelSpans = kMaxSeq / kSelSpan;     // 128
 constexpr int kMaxSplits = 1024;       // attention splits per sequence
-constexpr int kMergeRun = 16;          // splits merged by one first-level merge
+constexpr int kMergeRun = 64;          // splits merged by one first-level merge
 constexpr int kBitmapWordsPerBlock = 4096;           // bitmap-build LDS tile (16 KiB)
 
 // ---------------------------------------------------------------- parameters
@@ -64,7 +66,7 @@ struct AttnParams {
 struct SelParams {
   int mode;               // 0: standalone rows, 1: retrieval rows of a layer
   int nrows;              // rows launched
-  int C;                  // chunk-grid stride of the select passes (4096 scores per chunk)
+  int C;                  // span-grid stride of the select passes (kSelSpan scores per span)
   int Ch;                 // chunk-grid stride of the standalone histogram (512 per chunk)
   // standalone
   const float* scores; int64_t row_stride; int n; int k; int32_t* idx_out; float* val_out;
@@ -76,13 +78,14 @@ struct SelParams {
   // workspace (per row slot)
   uint32_t* hist1;        // [slots][kHist1Bins], zero between calls
   uint32_t* hist2;        // [slots][kHist2Bins], zero between calls
-  uint32_t* tickets;      // [slots], zero between calls
+  uint32_t* tickets;      // [slots] arrivals, zero between calls
+  uint32_t* depart;       // [slots] departures from the row barrier, zero between calls
+  uint32_t* err;          // set when a row barrier gave up waiting (never expected)
   uint32_t* sel_info;     // [slots][4]: b1, k1, T, i_tie
-  uint32_t* chunk_cnt;    // [slots][C][2]: keys above b1, candidates
-  uint32_t* chunk_off;    // [slots][C]: output offset of each chunk
-  uint32_t* cand_key;     // [slots][ncap]
-  uint32_t* cand_idx;     // [slots][ncap]
-  int64_t ncap;
+  uint32_t* span_cnt;     // [slots][C][2]: keys above bin b1, candidates (keys in bin b1)
+  uint32_t* span_off;     // [slots][C]: output offset of each span
+  uint64_t* cand;         // [slots][ncap]: (index << 32 | key) of the candidates, per span
+  int64_t ncap;           // C * kSelSpan
 };
 
 // Build membership bitmaps of sparse heads from S rows.

@@ -3,19 +3,22 @@
 // workspace fill).
 //
 // Selection is an exact three-digit radix select on order-preserving 32-bit keys
-// (digit 1 = bits 31..21, digit 2 = bits 20..10, digit 3 = bits 9..0):
+// (digit 1 = bits 31..21, digit 2 = bits 20..10, digit 3 = bits 9..0), over spans
+// of 16384 scores, one 1024-thread workgroup per span:
 //   1. digit-1 histogram of the row (fused into the attention kernel for retrieval
 //      heads, or k_sel_hist over 512-score chunks for standalone rows); the last
 //      workgroup of the row picks the bin b1 holding the k-th largest key;
-//   2. k_topk_row, one 1024-thread workgroup per row: the keys of bin b1 (the
-//      candidates) go to LDS with their digit-2 histogram; digits 2 and 3 give the
-//      exact threshold key T and the highest index i_tie among the keys equal to T
-//      that are kept (ties go to lower indices); every wave then writes its selected
-//      indices (key > T, or key == T and index <= i_tie) in ascending order at its
-//      offset from one scan over the wave totals, plus the membership bitmap words.
-// Each wave reads 2048 consecutive scores per 32768-score segment in coalesced 1 KB
-// loads; a row of one segment stays in registers between the passes, longer rows
-// are re-read. Only integer atomics are used, so the result is deterministic.
+//   2. k_sel_cand: each span counts its keys above bin b1 and stores its keys of bin
+//      b1 (the candidates) with their digit-2 histogram; the last span of the row
+//      finds digit 2, then from the candidates digit 3 (threshold key T), the highest
+//      kept index i_tie among the keys equal to T (ties go to lower indices) and the
+//      number of kept keys of every span, hence each span's output offset;
+//   3. k_sel_write: each span writes its kept indices (key > T, or key == T and
+//      index <= i_tie) in ascending order at its offset, plus its membership bitmap
+//      words.
+// Only integer atomics are used, so the result is deterministic.
+
+#include <atomic>
 
 #include "ld_device.h"
 
@@ -101,238 +104,451 @@ __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
   for (int i = tid; i < kHist1Bins; i += kThreads) gh[i] = 0u;
 }
 
-// ------------------------------------------------- one workgroup per row
+// ------------------------------------------------ spans of kSelSpan scores
 
-constexpr int kRowThreads = 1024;
-constexpr int kRowWaves = kRowThreads / 64;
-constexpr int kRounds = 8;                      // 256-score rounds per wave per segment
-constexpr int kWaveSpan = kRounds * 256;        // 2048 scores per wave per segment
-constexpr int kSeg = kRowWaves * kWaveSpan;     // 32768 scores per segment
-constexpr int kCandCap = 8192;                  // candidates kept in LDS
+constexpr int kSpanThreads = 1024;
+constexpr int kSpanWaves = kSpanThreads / 64;
+constexpr int kSpanRounds = kSelSpan / (4 * kSpanThreads);   // float4 loads per thread
+constexpr int kFineCap = 4096;                                // fine candidates kept in LDS
+constexpr int kMaxSpins = 1 << 22;                            // bound of the row-barrier wait
+constexpr int kSpecSlots = 4;                                 // candidates fetched early per thread
+static_assert(kSpanRounds == 4, "one 16-bit lane mask per span");
 
-// Keys of this lane's scores of one segment: round r holds indices
-// wbase + r*256 + lane*4 + e; positions past the row end get key 0 (masked by index).
-__device__ __forceinline__ void load_keys(const float* __restrict__ sc, int n, int wbase, int lane,
-                                          uint32_t (&key)[kRounds][4]) {
-  // wave-uniform test, so that the fast path issues every load before any wait
-  const bool whole = wbase + kWaveSpan <= n && (reinterpret_cast<uintptr_t>(sc + wbase) & 15u) == 0;
+// Keys of this thread's scores of span `base`: round r holds indices
+// base + r*4096 + tid*4 + e; positions at or past n get key 0 (masked by index).
+__device__ __forceinline__ void load_span(const float* __restrict__ sc, int n, int base, int tid,
+                                          uint32_t (&key)[kSpanRounds][4]) {
+  // workgroup-uniform test, so that the fast path issues every load before any wait
+  const bool whole = base + kSelSpan <= n && (reinterpret_cast<uintptr_t>(sc + base) & 15u) == 0;
   if (whole) {
-    float4 x[kRounds];
+    float4 x[kSpanRounds];
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) x[r] = *reinterpret_cast<const float4*>(sc + wbase + r * 256 + lane * 4);
+    for (int r = 0; r < kSpanRounds; ++r)
+      x[r] = *reinterpret_cast<const float4*>(sc + base + r * 4 * kSpanThreads + tid * 4);
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
+    for (int r = 0; r < kSpanRounds; ++r) {
       key[r][0] = score_key(x[r].x); key[r][1] = score_key(x[r].y);
       key[r][2] = score_key(x[r].z); key[r][3] = score_key(x[r].w);
     }
   } else {
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r)
+    for (int r = 0; r < kSpanRounds; ++r)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = wbase + r * 256 + lane * 4 + e;
+        const int i = base + r * 4 * kSpanThreads + tid * 4 + e;
         key[r][e] = (i < n) ? score_key(sc[i]) : 0u;
       }
   }
 }
 
-// Bit (4r + e) set for the keys of this lane that satisfy the predicate.
-template <typename P>
-__device__ __forceinline__ uint32_t key_mask(const uint32_t (&key)[kRounds][4], int wbase, int lane, int n,
-                                             P pred) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int r = 0; r < kRounds; ++r)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = wbase + r * 256 + lane * 4 + e;
-      m |= (uint32_t)(i < n && pred(key[r][e], (uint32_t)i)) << (4 * r + e);
-    }
-  return m;
+__device__ __forceinline__ int span_index(int base, int tid, int bit) {
+  return base + (bit >> 2) * 4 * kSpanThreads + tid * 4 + (bit & 3);
 }
 
-__device__ __forceinline__ uint32_t key_at(const uint32_t (&key)[kRounds][4], int bit) {
+__device__ __forceinline__ uint32_t span_key(const uint32_t (&key)[kSpanRounds][4], int bit) {
   uint32_t v = 0;
 #pragma unroll
-  for (int r = 0; r < kRounds; ++r)
+  for (int r = 0; r < kSpanRounds; ++r)
 #pragma unroll
     for (int e = 0; e < 4; ++e) v = (bit == 4 * r + e) ? key[r][e] : v;
   return v;
 }
 
-__device__ __forceinline__ int wave_excl_scan(int x, int lane, int& total) {
-  int v = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(v, o, 64);
-    if (lane >= o) v += y;
-  }
-  total = __shfl(v, 63, 64);
-  return v - x;
-}
+__device__ __forceinline__ int wave_sum(int x) { return wave_total(x); }
 
-struct RowSmem {
+struct SpanSmem {
   uint32_t hist[2048];
-  uint32_t ckey[kCandCap];
-  uint32_t cidx[kCandCap];
-  int tmp[kRowWaves];
+  uint64_t fine[kFineCap];           // (index << 32 | key) of keys in bins (b1, b2)
+  uint32_t above[kMaxSelSpans];      // per span: keys above bin b1
+  uint32_t ncd[kMaxSelSpans];        // per span: candidates
+  uint32_t cnt2[kMaxSelSpans];       // per span: candidates above bin b2
+  uint32_t cnt3[kMaxSelSpans];       // per span: kept keys of bin (b1, b2)
+  int tmp[kSpanWaves];
   uint32_t res[2];
-  uint32_t ncand;
+  uint32_t misc[4];                  // candidate count, above count, fine count
+  uint64_t wtot[kSpanWaves];
+  int flag;
 };
 
-__global__ __launch_bounds__(kRowThreads) void k_topk_row(const SelParams p) {
-  __shared__ RowSmem sm;
-  const RowView v = row_view(p, blockIdx.x);
-  const int n = v.n, kk = v.k;
-  if (n < 1 || kk < 1) return;
-  const float* __restrict__ sc = v.sc;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int slot = v.slot;
-  const uint32_t b1 = p.sel_info[slot * 4 + 0];
-  const uint32_t k1 = p.sel_info[slot * 4 + 1];
-  const int nseg = (n + kSeg - 1) / kSeg;
+// Pass over the candidates of a row (keys of bin b1 stored per span) from position
+// `start` of each span on, spread over the 16 waves: f(key, index) per candidate, then
+// done(span, wave total) once per wave and span with the wave-wide sum of what f
+// returned.
+template <typename F, typename Done>
+__device__ __forceinline__ void for_candidates(const uint64_t* __restrict__ cand, const uint32_t* ncd, int nsp,
+                                               int start, int lane, int wave, F f, Done done) {
+  const int wpc = nsp >= kSpanWaves ? 1 : kSpanWaves / nsp;   // waves per span
+  const int first = wave / wpc, slice = wave % wpc;
+  for (int c = first; c < nsp; c += kSpanWaves / wpc) {
+    const int cnt = (int)ncd[c];
+    const uint64_t* cp = cand + (size_t)c * kSelSpan;
+    int acc = 0;
+    int q = start + slice * 64 + lane;
+    for (; q + 3 * wpc * 64 < cnt; q += 4 * wpc * 64) {
+      uint64_t x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = ld_dev(cp + q + u * wpc * 64);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += f((uint32_t)x[u], (uint32_t)(x[u] >> 32));
+    }
+    for (; q < cnt; q += wpc * 64) {
+      const uint64_t x = ld_dev(cp + q);
+      acc += f((uint32_t)x, (uint32_t)(x >> 32));
+    }
+    done(c, wave_sum(acc));
+  }
+}
 
-  uint32_t key[kRounds][4];
-
-  // ---- pass 1: candidates of bin b1 (LDS) and their digit-2 histogram
-  for (int i = tid; i < 2048; i += kRowThreads) sm.hist[i] = 0;
-  if (tid == 0) sm.ncand = 0;
+// Phase 1 of a span: count its keys above bin b1, store its keys of bin b1 (the
+// candidates, device-coherent) and add their digit-2 histogram to gh2; the span's
+// two counts go to span_cnt. Every thread of the workgroup calls it.
+__device__ __forceinline__ void span_candidates(const SelParams& p, int slot, int c, int n, uint32_t b1,
+                                                const uint32_t (&key)[kSpanRounds][4], uint64_t* cand,
+                                                uint32_t* gh2, SpanSmem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int base = c * kSelSpan;
+  for (int i = tid; i < 2048; i += kSpanThreads) sm.hist[i] = 0;
+  if (tid == 0) { sm.misc[0] = 0; sm.misc[1] = 0; }
+  uint32_t cm = 0;
+  int na = 0;
+#pragma unroll
+  for (int rr = 0; rr < kSpanRounds; ++rr)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = base + rr * 4 * kSpanThreads + tid * 4 + e < n;
+      const uint32_t d1 = key[rr][e] >> 21;
+      na += (in && d1 > b1) ? 1 : 0;
+      cm |= (uint32_t)(in && d1 == b1) << (4 * rr + e);
+    }
   __syncthreads();
-  for (int sg = 0; sg < nseg; ++sg) {
-    const int wbase = sg * kSeg + wave * kWaveSpan;
-    load_keys(sc, n, wbase, lane, key);
-    uint32_t cm = key_mask(key, wbase, lane, n, [&](uint32_t kv, uint32_t) { return (kv >> 21) == b1; });
-    int wtot;
-    const int before = wave_excl_scan(__popc(cm), lane, wtot);
-    if (wtot) {
-      uint32_t wb = 0;
-      if (lane == 0) wb = atomicAdd(&sm.ncand, (uint32_t)wtot);
-      uint32_t q = __shfl(wb, 0, 64) + (uint32_t)before;
-      while (cm) {
-        const int bit = __builtin_ctz(cm);
-        cm &= cm - 1u;
-        const uint32_t kv = key_at(key, bit);
-        if (q < (uint32_t)kCandCap) {
-          sm.ckey[q] = kv;
-          sm.cidx[q] = (uint32_t)(wbase + (bit >> 2) * 256 + lane * 4 + (bit & 3));
-        }
-        ++q;
-        atomicAdd(&sm.hist[(kv >> 10) & 0x7ffu], 1u);
-      }
+  int wtot;
+  const int before = wave_excl_scan(__popc(cm), wtot);
+  na = wave_sum(na);
+  if (lane == 0) atomicAdd(&sm.misc[1], (uint32_t)na);
+  if (wtot) {
+    uint32_t wb = 0;
+    if (lane == 0) wb = atomicAdd(&sm.misc[0], (uint32_t)wtot);
+    uint32_t q = (uint32_t)__builtin_amdgcn_readlane((int)wb, 0) + (uint32_t)before;
+    while (cm) {
+      const int bit = __builtin_ctz(cm);
+      cm &= cm - 1u;
+      const uint32_t kv = span_key(key, bit);
+      st_dev(cand + base + q, ((uint64_t)(uint32_t)span_index(base, tid, bit) << 32) | kv);
+      ++q;
+      atomicAdd(&sm.hist[(kv >> 10) & 0x7ffu], 1u);
     }
   }
-  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
   __syncthreads();
-  const uint32_t ncand = sm.ncand;
-  const bool in_lds = ncand <= (uint32_t)kCandCap;
-  find_bin_from_top<2048, kRowThreads>([&](int i) { return sm.hist[i]; }, k1, sm.tmp, sm.res);
+  for (int i = tid; i < 2048; i += kSpanThreads)
+    if (sm.hist[i]) atomicAdd(gh2 + i, sm.hist[i]);
+  if (tid == 0) {
+    st_dev(p.span_cnt + ((size_t)slot * p.C + c) * 2 + 0, sm.misc[1]);
+    st_dev(p.span_cnt + ((size_t)slot * p.C + c) * 2 + 1, sm.misc[0]);
+  }
+}
+
+// Phase 2, once phase 1 of every span of the row is complete: digits 2 and 3 give
+// the threshold key T; i_tie is the highest kept index among the keys equal to T
+// (ties go to lower indices); sm.above/cnt2/cnt3 then hold the parts of each span's
+// kept count. zero_hist: clear gh2 once read. Every thread of the workgroup calls it.
+__device__ __forceinline__ void row_threshold(const SelParams& p, int slot, int nsp, uint32_t b1, uint32_t k1,
+                                              uint32_t* gh2, bool zero_hist, const uint64_t* cand,
+                                              SpanSmem& sm, uint32_t& T_out, uint32_t& i_tie_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; sm.misc[2] = 0; }
+  for (int i = tid; i < nsp; i += kSpanThreads) {
+    sm.above[i] = ld_dev(p.span_cnt + ((size_t)slot * p.C + i) * 2 + 0);
+    sm.ncd[i] = ld_dev(p.span_cnt + ((size_t)slot * p.C + i) * 2 + 1);
+    sm.cnt2[i] = 0;
+    sm.cnt3[i] = 0;
+  }
+  // digit-2 bins of this thread (the two that find_bin_from_top asks it for)
+  const uint32_t h0 = ld_dev(gh2 + 2 * tid), h1 = ld_dev(gh2 + 2 * tid + 1);
+  // the first `per` stored candidates of every span, fetched before their counts are
+  // known (entries past a span's count are ignored); per is a multiple of 64, so the
+  // lanes of a wave share one span
+  const int per = nsp <= 64 ? ((kSpecSlots * kSpanThreads / nsp) / 64) * 64 : 0;
+  uint64_t spec[kSpecSlots];
+#pragma unroll
+  for (int u = 0; u < kSpecSlots; ++u) {
+    const int f = u * kSpanThreads + tid;
+    const int c = per ? f / per : nsp;
+    spec[u] = (c < nsp) ? ld_dev(cand + (size_t)c * kSelSpan + (f - c * per)) : 0ull;
+  }
+  __syncthreads();
+  find_bin_from_top<2048, kSpanThreads>([&](int i) { return (i & 1) ? h1 : h0; }, k1, sm.tmp, sm.res);
   const uint32_t b2 = sm.res[0];
   const uint32_t k2 = k1 - sm.res[1];
-
-  // candidate histograms: mode 0 digit 3 of bin (b1, b2); 1 index bits 20..11 of keys
-  // == T; 2 index bits 10..0 of keys == T in index bin binA
-  auto cand_hist = [&](int mode, uint32_t T, uint32_t binA) {
-    for (int i = tid; i < 2048; i += kRowThreads) sm.hist[i] = 0;
-    if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
-    __syncthreads();
-    auto one = [&](uint32_t kv, uint32_t ix) {
-      if (mode == 0) { if (((kv >> 10) & 0x7ffu) == b2) atomicAdd(&sm.hist[kv & 0x3ffu], 1u); }
-      else if (mode == 1) { if (kv == T) atomicAdd(&sm.hist[ix >> 11], 1u); }
-      else { if (kv == T && (ix >> 11) == binA) atomicAdd(&sm.hist[ix & 0x7ffu], 1u); }
-    };
-    if (in_lds) {
-      for (uint32_t q = tid; q < ncand; q += kRowThreads) one(sm.ckey[q], sm.cidx[q]);
-    } else {
-      // a one-segment row is still in registers; longer rows are re-read
-      for (int sg = 0; sg < nseg; ++sg) {
-        const int wbase = sg * kSeg + wave * kWaveSpan;
-        if (nseg > 1) load_keys(sc, n, wbase, lane, key);
-        uint32_t cm = key_mask(key, wbase, lane, n, [&](uint32_t kv, uint32_t) { return (kv >> 21) == b1; });
-        while (cm) {
-          const int bit = __builtin_ctz(cm);
-          cm &= cm - 1u;
-          one(key_at(key, bit), (uint32_t)(wbase + (bit >> 2) * 256 + lane * 4 + (bit & 3)));
-        }
-      }
-    }
-    __syncthreads();
-  };
-
-  // ---- digit 3
+  for (int i = tid; i < 2048; i += kSpanThreads) {
+    if (zero_hist) gh2[i] = 0u;
+    sm.hist[i] = 0u;
+  }
   __syncthreads();
-  cand_hist(0, 0u, 0u);
-  find_bin_from_top<1024, kRowThreads>([&](int i) { return sm.hist[i]; }, k2, sm.tmp, sm.res);
+
+  // ---- candidates above bin b2 per span; digit-3 histogram and list of bin (b1, b2)
+  auto visit = [&](uint32_t kv, uint32_t ix) -> int {
+    const uint32_t d2 = (kv >> 10) & 0x7ffu;
+    if (d2 == b2) {
+      atomicAdd(&sm.hist[kv & 0x3ffu], 1u);
+      const uint32_t f = atomicAdd(&sm.misc[2], 1u);
+      if (f < (uint32_t)kFineCap) sm.fine[f] = ((uint64_t)ix << 32) | kv;
+    }
+    return d2 > b2 ? 1 : 0;
+  };
+#pragma unroll
+  for (int u = 0; u < kSpecSlots; ++u) {
+    const int f = u * kSpanThreads + tid;
+    const int c = per ? f / per : nsp;            // wave-uniform
+    if (c < nsp) {
+      const int a = (f - c * per < (int)sm.ncd[c]) ? visit((uint32_t)spec[u], (uint32_t)(spec[u] >> 32)) : 0;
+      const int tot = wave_sum(a);
+      if (lane == 0 && tot) atomicAdd(&sm.cnt2[c], (uint32_t)tot);
+    }
+  }
+  for_candidates(cand, sm.ncd, nsp, per, lane, wave, visit,
+      [&](int cc, int tot) { if (lane == 0 && tot) atomicAdd(&sm.cnt2[cc], (uint32_t)tot); });
+  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
+  __syncthreads();
+  const uint32_t nfine = sm.misc[2];
+  const bool fine_lds = nfine <= (uint32_t)kFineCap;
+  find_bin_from_top<1024, kSpanThreads>([&](int i) { return sm.hist[i]; }, k2, sm.tmp, sm.res);
   const uint32_t b3 = sm.res[0];
-  const uint32_t e_take = k2 - sm.res[1];       // keys equal to T that are kept
+  const uint32_t e_take = k2 - sm.res[1];         // keys equal to T that are kept
   const uint32_t nties = sm.hist[b3];
   const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
+  const uint32_t pre22 = T >> 10;
   __syncthreads();
+
+  // every key of bin (b1, b2): from the LDS list, else from the stored candidates
+  auto for_fine = [&](auto f) {
+    if (fine_lds) {
+      for (uint32_t q = tid; q < nfine; q += kSpanThreads) {
+        const uint64_t x = sm.fine[q];
+        f((uint32_t)x, (uint32_t)(x >> 32));
+      }
+    } else {
+      for_candidates(cand, sm.ncd, nsp, 0, lane, wave,
+          [&](uint32_t kv, uint32_t ix) -> int { if ((kv >> 10) == pre22) f(kv, ix); return 0; },
+          [&](int, int) {});
+    }
+  };
 
   // ---- highest kept tie index: the e_take-th smallest index among keys == T
   uint32_t i_tie = 0x7fffffffu;
   if (e_take < nties) {
     // indices are < 2^21: digit A = bits 20..11 (1024 bins), digit B = bits 10..0
-    cand_hist(1, T, 0u);
-    find_bin_from_top<1024, kRowThreads>([&](int i) { return sm.hist[1023 - i]; }, e_take, sm.tmp, sm.res);
+    for (int i = tid; i < 2048; i += kSpanThreads) sm.hist[i] = 0u;
+    if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
+    __syncthreads();
+    for_fine([&](uint32_t kv, uint32_t ix) { if (kv == T) atomicAdd(&sm.hist[ix >> 11], 1u); });
+    __syncthreads();
+    find_bin_from_top<1024, kSpanThreads>([&](int i) { return sm.hist[1023 - i]; }, e_take, sm.tmp, sm.res);
     const uint32_t binA = 1023u - sm.res[0];
     const uint32_t eB = e_take - sm.res[1];
+    for (int i = tid; i < 2048; i += kSpanThreads) sm.hist[i] = 0u;
+    if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
     __syncthreads();
-    cand_hist(2, T, binA);
-    find_bin_from_top<2048, kRowThreads>([&](int i) { return sm.hist[2047 - i]; }, eB, sm.tmp, sm.res);
+    for_fine([&](uint32_t kv, uint32_t ix) {
+      if (kv == T && (ix >> 11) == binA) atomicAdd(&sm.hist[ix & 0x7ffu], 1u);
+    });
+    __syncthreads();
+    find_bin_from_top<2048, kSpanThreads>([&](int i) { return sm.hist[2047 - i]; }, eB, sm.tmp, sm.res);
     i_tie = (binA << 11) | (2047u - sm.res[0]);
-    __syncthreads();
   }
 
-  // ---- pass 3: ascending write of the selected indices and the bitmap words
-  int run = 0;
-  for (int sg = 0; sg < nseg; ++sg) {
-    const int wbase = sg * kSeg + wave * kWaveSpan;
-    if (nseg > 1) load_keys(sc, n, wbase, lane, key);
-    const uint32_t fm = key_mask(key, wbase, lane, n, [&](uint32_t kv, uint32_t ix) {
-      return kv > T || (kv == T && ix <= i_tie);
-    });
-    // waves hold consecutive index blocks: exclusive scan of the wave totals
-    int wtot;
-    (void)wave_excl_scan(__popc(fm), lane, wtot);
-    if (lane == 0) sm.tmp[wave] = wtot;
-    __syncthreads();
-    int woff = 0, stot = 0;
+  // ---- kept keys of bin (b1, b2) per span
+  for_fine([&](uint32_t kv, uint32_t ix) {
+    if (kv > T || (kv == T && ix <= i_tie)) atomicAdd(&sm.cnt3[ix / kSelSpan], 1u);
+  });
+  __syncthreads();
+  T_out = T;
+  i_tie_out = i_tie;
+}
+
+// Phase 3 of a span: its kept indices (key > T, or key == T and index <= i_tie) in
+// ascending order from `off`, plus its membership bitmap words.
+__device__ __forceinline__ void span_write(const SelParams& p, const RowView& v, int c, uint32_t T, uint32_t i_tie,
+                                           int off, const uint32_t (&key)[kSpanRounds][4], SpanSmem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = v.n, kk = v.k;
+  const int base = c * kSelSpan;
+  uint32_t fm = 0;
 #pragma unroll
-    for (int w = 0; w < kRowWaves; ++w) {
-      woff += (w < wave) ? sm.tmp[w] : 0;
-      stot += sm.tmp[w];
-    }
-    __syncthreads();
-    int pos = run + woff;
+  for (int rr = 0; rr < kSpanRounds; ++rr)
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const uint32_t nib = (fm >> (4 * r)) & 0xfu;
-      int rtot;
-      const int before = wave_excl_scan(__popc(nib), lane, rtot);
-      int j = pos + before;
-      const int i0 = wbase + r * 256 + lane * 4;
-      uint32_t m = nib;
-      while (m) {
-        const int e = __builtin_ctz(m);
-        m &= m - 1u;
-        if (j < kk) {
-          v.out[j] = i0 + e;
-          if (v.vout) v.vout[j] = sc[i0 + e];
-        }
-        ++j;
-      }
-      pos += rtot;
-      if (v.bm) {                               // 8 lanes x 4 bits = one 32-bit word
-        uint32_t w = nib << ((lane & 7) * 4);
-        w |= __shfl_xor(w, 1, 64);
-        w |= __shfl_xor(w, 2, 64);
-        w |= __shfl_xor(w, 4, 64);
-        const int wi = i0 >> 5;
-        if ((lane & 7) == 0 && i0 < n && wi < p.W) v.bm[wi] = w;
-      }
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t ix = (uint32_t)(base + rr * 4 * kSpanThreads + tid * 4 + e);
+      const uint32_t kv = key[rr][e];
+      fm |= (uint32_t)(ix < (uint32_t)n && (kv > T || (kv == T && ix <= i_tie))) << (4 * rr + e);
     }
-    run += stot;
+  // per-round counts packed in 16-bit fields (rounds 0, 1 and rounds 2, 3); inclusive
+  // scans over the wave
+  uint32_t c01 = 0, c23 = 0;
+  c01 = (uint32_t)__popc(fm & 0xfu) | ((uint32_t)__popc((fm >> 4) & 0xfu) << 16);
+  c23 = (uint32_t)__popc((fm >> 8) & 0xfu) | ((uint32_t)__popc((fm >> 12) & 0xfu) << 16);
+  const uint32_t i01 = (uint32_t)wave_incl_sum((int)c01), i23 = (uint32_t)wave_incl_sum((int)c23);
+  const uint64_t cnt = (uint64_t)c01 | ((uint64_t)c23 << 32);
+  const uint64_t inc = (uint64_t)i01 | ((uint64_t)i23 << 32);
+  if (lane == 63) sm.wtot[wave] = inc;
+  __syncthreads();
+  uint64_t below = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kSpanWaves; ++w) {
+    const uint64_t t = sm.wtot[w];
+    below += (w < wave) ? t : 0ull;
+    all += t;
   }
+  const uint64_t mine = below + inc - cnt;        // exclusive prefix, per round
+  int run = off;
+#pragma unroll
+  for (int rr = 0; rr < kSpanRounds; ++rr) {
+    const uint32_t nib = (fm >> (4 * rr)) & 0xfu;
+    int j = run + (int)((mine >> (16 * rr)) & 0xffffu);
+    const int i0 = base + rr * 4 * kSpanThreads + tid * 4;
+    uint32_t m = nib;
+    while (m) {
+      const int e = __builtin_ctz(m);
+      m &= m - 1u;
+      if (j < kk) {
+        v.out[j] = i0 + e;
+        if (v.vout) v.vout[j] = v.sc[i0 + e];
+      }
+      ++j;
+    }
+    run += (int)((all >> (16 * rr)) & 0xffffu);
+    if (v.bm) {                                  // 8 lanes x 4 bits = one 32-bit word
+      // the 8 lanes' bits are disjoint, so their sum is their union
+      const uint32_t w = (uint32_t)sum8_i((int)(nib << ((lane & 7) * 4)));
+      const int wi = i0 >> 5;
+      if ((lane & 7) == 0 && i0 < n && wi < p.W) v.bm[wi] = w;
+    }
+  }
+}
+
+// Output offset of span c from the per-span kept counts in sm (wave 0 scans them).
+__device__ __forceinline__ int span_offsets(int nsp, SpanSmem& sm, uint32_t* off_out, int c_want) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    // lane l owns spans 2l and 2l+1 (at most 128 spans)
+    int s0 = 0, s1 = 0;
+    const int c0 = 2 * lane, c1 = 2 * lane + 1;
+    if (c0 < nsp) s0 = (int)(sm.above[c0] + sm.cnt2[c0] + sm.cnt3[c0]);
+    if (c1 < nsp) s1 = (int)(sm.above[c1] + sm.cnt2[c1] + sm.cnt3[c1]);
+    int tot;
+    const int pre = wave_excl_scan(s0 + s1, tot);
+    if (off_out) {
+      if (c0 < nsp) off_out[c0] = (uint32_t)pre;
+      if (c1 < nsp) off_out[c1] = (uint32_t)(pre + s0);
+    }
+    if (c0 == c_want) sm.misc[3] = (uint32_t)pre;
+    if (c1 == c_want) sm.misc[3] = (uint32_t)(pre + s0);
+  }
+  __syncthreads();
+  return (int)sm.misc[3];
+}
+
+// Two-kernel selection (any grid size): k_sel_cand, whose last span of a row runs
+// phase 2 and stores T, i_tie and the span offsets, then k_sel_write.
+__global__ __launch_bounds__(kSpanThreads) void k_sel_cand(const SelParams p) {
+  __shared__ SpanSmem sm;
+  const int r = blockIdx.x / p.C, c = blockIdx.x % p.C;
+  const RowView v = row_view(p, r);
+  const int n = v.n, kk = v.k;
+  if (n < 1 || kk < 1) return;
+  const int nsp = (n + kSelSpan - 1) / kSelSpan;
+  if (c >= nsp) return;
+  const int tid = threadIdx.x;
+  const int slot = v.slot;
+  const uint32_t b1 = p.sel_info[slot * 4 + 0];
+  const uint32_t k1 = p.sel_info[slot * 4 + 1];
+  uint64_t* cand = p.cand + (size_t)slot * p.ncap;
+  uint32_t* gh2 = p.hist2 + (size_t)slot * kHist2Bins;
+  uint32_t key[kSpanRounds][4];
+  load_span(v.sc, n, c * kSelSpan, tid, key);
+  span_candidates(p, slot, c, n, b1, key, cand, gh2, sm);
+  if (!arrive_last(p.tickets + slot, (uint32_t)nsp, &sm.flag)) return;
+  if (tid == 0) p.tickets[slot] = 0u;
+  uint32_t T, i_tie;
+  row_threshold(p, slot, nsp, b1, k1, gh2, true, cand, sm, T, i_tie);
+  (void)span_offsets(nsp, sm, p.span_off + (size_t)slot * p.C, -1);
+  if (tid == 0) {
+    p.sel_info[slot * 4 + 2] = T;
+    p.sel_info[slot * 4 + 3] = i_tie;
+  }
+}
+
+__global__ __launch_bounds__(kSpanThreads) void k_sel_write(const SelParams p) {
+  __shared__ SpanSmem sm;
+  const int r = blockIdx.x / p.C, c = blockIdx.x % p.C;
+  const RowView v = row_view(p, r);
+  if (v.n < 1 || v.k < 1) return;
+  const int nsp = (v.n + kSelSpan - 1) / kSelSpan;
+  if (c >= nsp) return;
+  const int slot = v.slot;
+  const uint32_t T = p.sel_info[slot * 4 + 2];
+  const uint32_t i_tie = p.sel_info[slot * 4 + 3];
+  const int off = (int)p.span_off[(size_t)slot * p.C + c];
+  uint32_t key[kSpanRounds][4];
+  load_span(v.sc, v.n, c * kSelSpan, threadIdx.x, key);
+  span_write(p, v, c, T, i_tie, off, key, sm);
+}
+
+// One-kernel selection for grids whose workgroups are all resident at once: the
+// spans of a row meet at a barrier after phase 1 (a device-coherent arrival counter,
+// with a bounded wait), then every span runs phase 2 itself and writes its part of
+// the row from the keys still in registers. The last span to leave clears the
+// arrival and departure counters and the digit-2 histogram.
+__global__ __launch_bounds__(kSpanThreads) void k_sel_fused(const SelParams p) {
+  __shared__ SpanSmem sm;
+  const int r = blockIdx.x / p.C, c = blockIdx.x % p.C;
+  const RowView v = row_view(p, r);
+  const int n = v.n, kk = v.k;
+  if (n < 1 || kk < 1) return;
+  const int nsp = (n + kSelSpan - 1) / kSelSpan;
+  if (c >= nsp) return;
+  const int tid = threadIdx.x;
+  const int slot = v.slot;
+  const uint32_t b1 = p.sel_info[slot * 4 + 0];
+  const uint32_t k1 = p.sel_info[slot * 4 + 1];
+  uint64_t* cand = p.cand + (size_t)slot * p.ncap;
+  uint32_t* gh2 = p.hist2 + (size_t)slot * kHist2Bins;
+  uint32_t key[kSpanRounds][4];
+  load_span(v.sc, n, c * kSelSpan, tid, key);
+  span_candidates(p, slot, c, n, b1, key, cand, gh2, sm);
+
+  // ---- row barrier: every span's candidates, counts and histogram are stored
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(p.tickets + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old != (uint32_t)nsp - 1u) {
+      int spins = 0;
+      while (ld_dev(p.tickets + slot) < (uint32_t)nsp) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > kMaxSpins) {               // never expected: report and go on
+          st_dev(p.err, 1u);
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  uint32_t T, i_tie;
+  row_threshold(p, slot, nsp, b1, k1, gh2, false, cand, sm, T, i_tie);
+  const int off = span_offsets(nsp, sm, nullptr, c);
+
+  // ---- departure (this span has read everything shared)
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(p.depart + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.flag = (old == (uint32_t)nsp - 1u);
+  }
+  __syncthreads();
+  if (sm.flag) {
+    if (tid == 0) { p.tickets[slot] = 0u; p.depart[slot] = 0u; }
+    for (int i = tid; i < kHist2Bins; i += kSpanThreads) gh2[i] = 0u;
+  }
+  span_write(p, v, c, T, i_tie, off, key, sm);
 }
 
 // ---------------------------------------------------- S rows -> bitmaps
@@ -398,13 +614,35 @@ __global__ __launch_bounds__(kThreads) void k_zero(uint4* p16, size_t n16, uint8
 
 }  // namespace
 
+// Workgroups of k_sel_fused that the current device holds at once.
+int64_t fused_capacity() {
+  static std::atomic<int64_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int64_t c = cache[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_sel_fused, kSpanThreads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  c = (int64_t)per_cu * cus;
+  cache[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
 hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist) {
   if (with_hist) {
     SelParams ph = p;
     ph.C = p.Ch;
     hipLaunchKernelGGL(k_sel_hist, dim3((unsigned)p.nrows * (unsigned)p.Ch), dim3(kThreads), 0, st, ph);
   }
-  hipLaunchKernelGGL(k_topk_row, dim3((unsigned)p.nrows), dim3(kRowThreads), 0, st, p);
+  const dim3 grid((unsigned)p.nrows * (unsigned)p.C);
+  if ((int64_t)p.nrows * p.C <= fused_capacity()) {
+    hipLaunchKernelGGL(k_sel_fused, grid, dim3(kSpanThreads), 0, st, p);
+  } else {
+    hipLaunchKernelGGL(k_sel_cand, grid, dim3(kSpanThreads), 0, st, p);
+    hipLaunchKernelGGL(k_sel_write, grid, dim3(kSpanThreads), 0, st, p);
+  }
   return hipGetLastError();
 }
 

@@ -101,3 +101,26 @@ def test_repeated_calls_reuse_workspace():
         torch.cuda.synchronize()
         for r in range(2):
             assert np.array_equal(idx.cpu().numpy()[r], orc.select_topk_f32(x[r], 1000 + it))
+
+
+def test_more_spans_than_resident_workgroups():
+    # 300 rows of two 16384-score spans: more workgroups than the device holds at once,
+    # so the two-kernel selection runs instead of the one-kernel row barrier
+    rng = _rng(5)
+    x = rng.normal(size=(300, 17000)).astype(np.float32)
+    x[7, :] = 1.0                                   # a constant row: ties everywhere
+    x[9, 100:200] = np.nan
+    _check(x, 5100, with_vals=False)
+
+
+def test_one_and_two_kernel_paths_agree_bitwise():
+    ld = _ld()
+    rng = _rng(6)
+    x = rng.normal(size=(300, 20000)).astype(np.float32)
+    x[:, 5000:5100] = 0.25                          # a block of ties near the threshold
+    xt = torch.as_tensor(x, device="cuda")
+    many = ld.topk_select(xt, 6000).cpu().numpy()   # 600 workgroups
+    few = ld.topk_select(xt[:5], 6000).cpu().numpy()  # 10 workgroups
+    assert np.array_equal(many[:5], few)
+    for r in (0, 4, 299):
+        assert np.array_equal(many[r], orc.select_topk_f32(x[r], 6000))
