@@ -1,6 +1,7 @@
 // Host side of liblychee_decode.so: argument validation, workspace layout and the
 // launch sequence of one layer (declared in include/lychee_decode.h).
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -28,6 +29,7 @@ struct LayerLayout {
   size_t attn_tickets, attn_tickets_l1;               // zero between calls
   SelArrays sel;
   size_t logits, part_ml, part_acc, l1_ml, l1_acc, bitmaps;
+  size_t gb_cnt, gb_rel, row_cnt, pub;                // group-barrier mode
   size_t total;
 };
 
@@ -108,6 +110,10 @@ LayerLayout layer_layout(const ld_shape* s) {
   L.l1_ml = take((size_t)L.slots * L.P1 * 8);
   L.l1_acc = take((size_t)L.slots * L.P1 * s->head_dim * 4);
   L.bitmaps = take((size_t)L.slots * L.W * 4);
+  L.gb_cnt = take((size_t)s->batch * s->num_kv_heads * 8 * 4);
+  L.gb_rel = take((size_t)s->batch * s->num_kv_heads * L.P * 128);
+  L.row_cnt = take((size_t)L.slots * 4);
+  L.pub = take((size_t)L.slots * L.P * 8);
   L.total = o;
   return L;
 }
@@ -250,11 +256,34 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   ap.sel_info = at<uint32_t>(ws, L.sel.sel_info);
   ap.k_dense = k;
   ap.s_indptr = s_indptr;
-  const dim3 grid((unsigned)((int64_t)B * ng * ap.nsplit));
-  if (launch_attention(ap, D, G, grid, st) != hipSuccess) return LD_ERR_HIP;
+  const int64_t nwg = (int64_t)B * ng * ap.nsplit;
+  // every workgroup resident at once: the splits of a group merge O and select
+  // together behind device-wide barriers inside this launch
+  // (the in-launch selection handles a group's retrieval heads one after another, so
+  // layers with several retrieval heads per group select in their own launch, where
+  // every row runs in parallel)
+  int ret_per_group = 0;
+  for (int g = 0; g < Hkv; ++g) {
+    const uint64_t gm = ((G == 64) ? ~0ull : ((1ull << G) - 1ull)) << (g * G);
+    ret_per_group = std::max(ret_per_group, __builtin_popcountll(retrieval & gm));
+  }
+  const bool gb = !(flags & LD_FLAG_SEPARATE_SELECT) && !(do_topk && ret_per_group > 1) &&
+                  nwg <= attention_capacity(D, G, ap.waves);
+  if (gb) {
+    ap.gb = 1;
+    ap.gb_cnt = at<uint32_t>(ws, L.gb_cnt);
+    ap.gb_rel = at<uint32_t>(ws, L.gb_rel);
+    ap.row_cnt = at<uint32_t>(ws, L.row_cnt);
+    ap.cand = at<uint64_t>(ws, L.sel.cand);
+    ap.ncap = L.sel.ncap;
+    ap.pub = at<uint32_t>(ws, L.pub);
+    ap.s_out = s_out;
+    ap.err = at<uint32_t>(ws, L.sel.err);
+  }
+  if (launch_attention(ap, D, G, dim3((unsigned)nwg), st) != hipSuccess) return LD_ERR_HIP;
 
   // 4. argsTopK of the retrieval rows
-  if (do_topk) {
+  if (do_topk && !gb) {
     SelParams sp{};
     sp.mode = 1;
     sp.nrows = B * nret;

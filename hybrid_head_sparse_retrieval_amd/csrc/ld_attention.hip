@@ -26,6 +26,8 @@
 // turns the fused first-digit histogram of each retrieval head into the first
 // selection digit for the argsTopK kernels.
 
+#include <atomic>
+
 #include "ld_device.h"
 
 namespace ld {
@@ -77,9 +79,12 @@ struct AttnSmem {
   int wcnt[NW];
   int misc[4];
   uint32_t res[2];
+  int scan[NW][kMaxSplitRows / (64 * NW) / 2 > 2 ? kMaxSplitRows / (64 * NW) / 2 : 2];   // wave totals of scans
+  int cnt4[NW][2];
   float pl[NW][kChunkRows][G];       // per wave: probabilities of the chunk's rows
   union {
     uint32_t hist[G][kHist1Bins];
+    uint32_t sel_hist[kHist2Bins + kHist3Bins];
     struct {
       float acc[NW][RP][G * D];      // [wave][row part][head*D + dim]
       float m[NW][G];
@@ -200,6 +205,321 @@ __device__ __forceinline__ void merge_splits(AttnSmem<D, G, NW>& sm, const AttnP
   __syncthreads();
 }
 
+// ---- group-barrier mode
+
+// O of a group from its ns split partials, spread over the group's workgroups: wave w
+// of split s merges the float4 columns (s * NW + w) + t * ns * NW; its lanes run over
+// the splits.
+template <int D, int G, int NW>
+__device__ __forceinline__ void merge_columns(const AttnParams& p, uint32_t act, int hq0, int split, int ns) {
+  constexpr int NC = G * (D / 4);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  for (int c = split * NW + wave; c < NC; c += ns * NW) {
+    const int j = c / (D / 4), d0 = (c % (D / 4)) * 4;
+    if (!(act >> j & 1u)) continue;
+    const float* ml = p.part_ml + (size_t)(hq0 + j) * p.P * 2;
+    const __amdgpu_buffer_rsrc_t rr = rsrc(p.part_acc + (size_t)(hq0 + j) * p.P * D);
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ns <= 64) {
+      float m = -LD_INF, l = 0.f;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (lane < ns) {
+        m = ld_dev(ml + lane * 2);
+        l = ld_dev(ml + lane * 2 + 1);
+        a = ld_dev4_b(rr, (lane * D + d0) * 4);
+      }
+      const float M = wave_max_f(m);
+      const float w = exp2_fast(m - ((M == -LD_INF) ? 0.f : M));   // 0 for unused lanes
+      L = l * w;
+      o = make_float4(a.x * w, a.y * w, a.z * w, a.w * w);
+    } else {
+      float M = -LD_INF;
+      for (int s2 = lane; s2 < ns; s2 += 64) M = fmaxf(M, ld_dev(ml + s2 * 2));
+      M = wave_max_f(M);
+      const float mu = (M == -LD_INF) ? 0.f : M;
+      for (int s2 = lane; s2 < ns; s2 += 64) {
+        const float w = exp2_fast(ld_dev(ml + s2 * 2) - mu);
+        L = fmaf(ld_dev(ml + s2 * 2 + 1), w, L);
+        const float4 a = ld_dev4_b(rr, (s2 * D + d0) * 4);
+        o.x = fmaf(a.x, w, o.x); o.y = fmaf(a.y, w, o.y); o.z = fmaf(a.z, w, o.z); o.w = fmaf(a.w, w, o.w);
+      }
+    }
+    L = wave_sum_f(L);
+    o.x = wave_sum_f(o.x); o.y = wave_sum_f(o.y); o.z = wave_sum_f(o.z); o.w = wave_sum_f(o.w);
+    if (lane == 0) {
+      const float il = 1.f / L;
+      ushort4 r;
+      r.x = f32_to_bf16(o.x * il); r.y = f32_to_bf16(o.y * il);
+      r.z = f32_to_bf16(o.z * il); r.w = f32_to_bf16(o.w * il);
+      *reinterpret_cast<ushort4*>(p.out + (size_t)(hq0 + j) * D + d0) = r;
+    }
+  }
+}
+
+// Exclusive prefix of 0/1 flags in row order (row = i * NT + thread) over the
+// workgroup, for IT items per thread: ex[i] = flags of earlier rows, tot[i] = flags of
+// item i over the workgroup. Two items share an int (16-bit fields).
+template <int NW, int IT>
+__device__ __forceinline__ void rows_scan(const uint32_t (&f)[IT], int (&ex)[IT], int (&tot)[IT],
+                                          int (&lds)[NW][IT / 2]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc[IT / 2], val[IT / 2];
+#pragma unroll
+  for (int q = 0; q < IT / 2; ++q) {
+    val[q] = (int)(f[2 * q] | (f[2 * q + 1] << 16));
+    inc[q] = wave_incl_sum(val[q]);
+    if (lane == 63) lds[wave][q] = inc[q];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < IT / 2; ++q) {
+    int below = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int t = lds[w][q];
+      below += (w < wave) ? t : 0;
+      all += t;
+    }
+    const int e = below + inc[q] - val[q];
+    ex[2 * q] = e & 0xffff;
+    ex[2 * q + 1] = e >> 16;
+    tot[2 * q] = all & 0xffff;
+    tot[2 * q + 1] = all >> 16;
+  }
+  __syncthreads();
+}
+
+// argsTopK of the group's retrieval heads by the workgroups of the group, each over
+// its own rows (r0 .. r0 + nrows), with one group barrier: every split finds digit 1
+// from the row's fused histogram, appends its candidates (keys whose digit 1 is b1)
+// to the row's candidate list and publishes its count of keys above bin b1; after the
+// barrier every split derives the threshold key T from the whole candidate list
+// (digits 2 and 3), its output offset from the earlier splits' counts, and writes its
+// kept rows (keys equal to T are kept in row order, so the lower indices win ties).
+template <int D, int G, int NW>
+__device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnParams& p, uint32_t ret,
+                                             int hq0, int split, int ns, int nb, int r0, int nrows,
+                                             uint32_t* gc, uint32_t* rel) {
+  constexpr int NT = 64 * NW;
+  constexpr int IT = kMaxSplitRows / NT;        // rows per thread
+  constexpr int PB1 = kHist1Bins / NT;          // digit-1 bins per thread
+  constexpr int SPEC = G <= 4 ? 24 : 8;         // candidates fetched per thread before the count
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  uint32_t sel = 0;
+  int kk[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    kk[j] = 0;
+    if (ret >> j & 1u) {
+      const int slot = hq0 + j;
+      int k = p.k_dense;
+      if (p.s_indptr) k = (int)(p.s_indptr[slot + 1] - p.s_indptr[slot]);
+      kk[j] = min(k, nb);
+      if (kk[j] >= 1) sel |= 1u << j;
+    }
+  }
+  if (!sel) return;
+
+  // ---- keys of this split's rows; digit 1 of every selecting head
+  uint32_t key[G][IT];
+  uint32_t b1[G], k1[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    b1[j] = 0; k1[j] = 0;
+    if (!(sel >> j & 1u)) continue;
+    const float* lgj = p.logits + (size_t)(hq0 + j) * p.seq_len + r0;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int r = i * NT + tid;
+      key[j][i] = (r < nrows) ? score_key(lgj[r]) : 0u;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    if (!(sel >> j & 1u)) continue;
+    uint32_t h[PB1];
+    const uint32_t* hg = p.hist1 + (size_t)(hq0 + j) * kHist1Bins + tid * PB1;
+#pragma unroll
+    for (int q = 0; q < PB1; ++q) h[q] = ld_dev(hg + q);
+    if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
+    __syncthreads();
+    find_bin_regs<kHist1Bins, NT>(h, (uint32_t)kk[j], sm.wcnt, sm.res);
+    b1[j] = sm.res[0];
+    k1[j] = (uint32_t)kk[j] - sm.res[1];
+    __syncthreads();
+  }
+
+  // ---- append the candidates to the row's list; publish the count above bin b1
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    if (!(sel >> j & 1u)) continue;
+    const int slot = hq0 + j;
+    uint32_t cm = 0;
+    int na = 0;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const bool v = i * NT + tid < nrows;
+      const uint32_t d1 = key[j][i] >> 21;
+      na += (v && d1 > b1[j]) ? 1 : 0;
+      cm |= (uint32_t)(v && d1 == b1[j]) << i;
+    }
+    int wt;
+    const int before = wave_excl_scan(__popc(cm), wt);
+    const int wa = wave_total(na);
+    if (lane == 0) { sm.scan[wave][0] = wt; sm.scan[wave][1] = wa; }
+    __syncthreads();
+    int woff = 0, tot = 0, atot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      woff += (w < wave) ? sm.scan[w][0] : 0;
+      tot += sm.scan[w][0];
+      atot += sm.scan[w][1];
+    }
+    if (tid == 0) {
+      sm.misc[2] = tot ? (int)__hip_atomic_fetch_add(p.row_cnt + slot, (uint32_t)tot, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT) : 0;
+      st_dev(p.pub + ((size_t)slot * p.P + split) * 2, (uint32_t)atot);
+    }
+    __syncthreads();
+    uint64_t* cl = p.cand + (size_t)slot * p.ncap + sm.misc[2] + woff + before;
+    int q = 0;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      if (cm >> i & 1u) {
+        st_dev(cl + q, ((uint64_t)(uint32_t)(r0 + i * NT + tid) << 32) | key[j][i]);
+        ++q;
+      }
+    }
+    __syncthreads();    // sm.scan / sm.misc reuse
+  }
+  group_barrier(gc + 1, rel, split, ns, 2u, p.err, &sm.misc[1]);
+
+  // ---- per head: threshold from the whole candidate list, offset, write
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    if (!(sel >> j & 1u)) continue;
+    const int slot = hq0 + j;
+    const uint64_t* cl = p.cand + (size_t)slot * p.ncap;
+    // fetched before the count is known; entries past it are ignored
+    uint64_t cv[SPEC];
+#pragma unroll
+    for (int u = 0; u < SPEC; ++u) cv[u] = ld_dev(cl + u * NT + tid);
+    const int ncand = (int)ld_dev(p.row_cnt + slot);
+    int above = 0;                                  // keys above bin b1 in earlier splits
+    for (int s2 = tid; s2 < split; s2 += NT) above += (int)ld_dev(p.pub + ((size_t)slot * p.P + s2) * 2);
+    uint32_t* h2 = sm.u.sel_hist;                   // [kHist2Bins]
+    uint32_t* h3 = h2 + kHist2Bins;                 // [kHist3Bins]
+    for (int i = tid; i < kHist2Bins + kHist3Bins; i += NT) h2[i] = 0u;
+    if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
+    __syncthreads();
+    // visit(f): every candidate once (the fetched ones from registers)
+    auto for_cands = [&](auto f) {
+#pragma unroll
+      for (int u = 0; u < SPEC; ++u)
+        if (u * NT + tid < ncand) f((uint32_t)cv[u], (uint32_t)(cv[u] >> 32));
+      for (int q0 = SPEC * NT; q0 < ncand; q0 += 8 * NT) {
+        uint64_t x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = (q0 + u * NT + tid < ncand) ? ld_dev(cl + q0 + u * NT + tid) : 0ull;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (q0 + u * NT + tid < ncand) f((uint32_t)x[u], (uint32_t)(x[u] >> 32));
+      }
+    };
+    for_cands([&](uint32_t kv, uint32_t) { atomicAdd(&h2[(kv >> 10) & 0x7ffu], 1u); });
+    __syncthreads();
+    find_bin_from_top<kHist2Bins, NT>([&](int i) { return h2[i]; }, k1[j], sm.wcnt, sm.res);
+    const uint32_t b2 = sm.res[0];
+    const uint32_t k2 = k1[j] - sm.res[1];
+    const uint32_t pre = (b1[j] << 11) | b2;
+    if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
+    __syncthreads();
+    for_cands([&](uint32_t kv, uint32_t) { if ((kv >> 10) == pre) atomicAdd(&h3[kv & 0x3ffu], 1u); });
+    __syncthreads();
+    find_bin_from_top<kHist3Bins, NT>([&](int i) { return h3[i]; }, k2, sm.wcnt, sm.res);
+    const uint32_t T = (pre << 10) | sm.res[0];
+    const int et = (int)(k2 - sm.res[1]);           // keys equal to T that are kept
+    // candidates of earlier splits above and equal to T; keys equal to T here
+    int ga = 0, ge = 0, me = 0;
+    const uint32_t lo = (uint32_t)r0, hi = (uint32_t)(r0 + nrows);
+    for_cands([&](uint32_t kv, uint32_t ix) {
+      const int early = ix < lo ? 1 : 0, here = (ix >= lo && ix < hi) ? 1 : 0;
+      const int gt1 = kv > T ? 1 : 0, eq1 = kv == T ? 1 : 0;
+      ga += early & gt1;
+      ge += early & eq1;
+      me += here & eq1;
+    });
+    {
+      // the four sums in one exchange
+      const int w0 = wave_total(above), w1 = wave_total(ga), w2 = wave_total(ge), w3 = wave_total(me);
+      if (lane == 0) { sm.scan[wave][0] = w0; sm.scan[wave][1] = w1; }
+      if (lane == 0) { sm.cnt4[wave][0] = w2; sm.cnt4[wave][1] = w3; }
+      __syncthreads();
+      above = 0; ga = 0; ge = 0; me = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        above += sm.scan[w][0]; ga += sm.scan[w][1]; ge += sm.cnt4[w][0]; me += sm.cnt4[w][1];
+      }
+      __syncthreads();
+    }
+    const int off = above + ga + min(et, ge);       // kept rows of earlier splits
+    const int keep_e = max(0, min(et - ge, me));    // kept keys equal to T here
+    uint32_t gt[IT], eq[IT], kp[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const bool v = i * NT + tid < nrows;
+      gt[i] = (v && key[j][i] > T) ? 1u : 0u;
+      eq[i] = (v && key[j][i] == T) ? 1u : 0u;
+    }
+    if (keep_e == me) {
+#pragma unroll
+      for (int i = 0; i < IT; ++i) kp[i] = gt[i] | eq[i];
+    } else if (keep_e == 0) {
+#pragma unroll
+      for (int i = 0; i < IT; ++i) kp[i] = gt[i];
+    } else {
+      int ex[IT], tot[IT];
+      rows_scan<NW, IT>(eq, ex, tot, sm.scan);
+      int before = 0;
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        kp[i] = gt[i] | ((eq[i] && before + ex[i] < keep_e) ? 1u : 0u);
+        before += tot[i];
+      }
+    }
+    int ex[IT], tot[IT];
+    rows_scan<NW, IT>(kp, ex, tot, sm.scan);
+    int64_t so;
+    int klen;
+    if (p.s_indptr) { so = p.s_indptr[slot]; klen = (int)(p.s_indptr[slot + 1] - so); }
+    else { so = (int64_t)slot * p.k_dense; klen = p.k_dense; }
+    klen = min(klen, nb);
+    int32_t* out = p.s_out + so;
+    uint32_t* bm = p.bitmaps ? p.bitmaps + (size_t)slot * p.W : nullptr;
+    int base = off;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int r = i * NT + tid;
+      const int pos = base + ex[i];
+      if (kp[i] && pos < klen) out[pos] = r0 + r;
+      base += tot[i];
+      if (bm) {
+        const uint64_t bal = __ballot(kp[i] != 0u);
+        // first row of this lane's word; words past this split's rows are another
+        // split's (splits are whole words: r0 and the split size are multiples of 32)
+        const int rr = i * NT + wave * 64 + (lane & 32);
+        const int row32 = r0 + rr;
+        if ((lane & 31) == 0 && rr < nrows && (row32 >> 5) < p.W)
+          bm[row32 >> 5] = (uint32_t)(bal >> (lane & 32));
+      }
+    }
+    __syncthreads();    // LDS histograms reused by the next head
+  }
+}
+
 template <int D, int G, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams p) {
   constexpr int NT = 64 * NW;
@@ -318,8 +638,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   }
 
   // ---- membership of each row of the tile, and the visit list
-  if (do_hist) {
-    for (int i = tid; i < G * kHist1Bins; i += NT) (&sm.u.hist[0][0])[i] = 0;
+  if (do_hist && ret) {
+    for (int j = 0; j < G; ++j)
+      if (ret >> j & 1u)
+        for (int i = tid; i < kHist1Bins / 4; i += NT) reinterpret_cast<uint4*>(sm.u.hist[j])[i] = make_uint4(0, 0, 0, 0);
   }
   if (spm) {
     constexpr int IT = kMaxSplitRows / NT;
@@ -478,12 +800,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   }
 
   // ---- flush the fused selection histogram
-  if (do_hist) {
+  if (do_hist && ret) {
     __syncthreads();
-    for (int i = tid; i < G * kHist1Bins; i += NT) {
-      const int j = i / kHist1Bins, bin = i % kHist1Bins;
-      const uint32_t cnt = sm.u.hist[j][bin];
-      if (cnt) atomicAdd(p.hist1 + (size_t)(hq0 + j) * kHist1Bins + bin, cnt);
+    for (int j = 0; j < G; ++j) {
+      if (!(ret >> j & 1u)) continue;
+      uint32_t* hg = p.hist1 + (size_t)(hq0 + j) * kHist1Bins;
+      for (int i = tid; i < kHist1Bins / 4; i += NT) {
+        const uint4 c = reinterpret_cast<const uint4*>(sm.u.hist[j])[i];
+        if (c.x) atomicAdd(hg + 4 * i + 0, c.x);
+        if (c.y) atomicAdd(hg + 4 * i + 1, c.y);
+        if (c.z) atomicAdd(hg + 4 * i + 2, c.z);
+        if (c.w) atomicAdd(hg + 4 * i + 3, c.w);
+      }
     }
   }
   __syncthreads();   // the LDS union is reused below
@@ -548,6 +876,37 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     }
   }
 
+  if (p.gb) {
+    uint32_t* gc = p.gb_cnt + (size_t)(b * p.Hkv + g) * 8;
+    uint32_t* rel = p.gb_rel + (size_t)(b * p.Hkv + g) * p.P * kRelStride;
+    group_barrier(gc, rel, split, nsplit_b, 1u, p.err, &sm.misc[1]);
+    merge_columns<D, G, NW>(p, act, hq0, split, nsplit_b);
+    if (do_hist && ret) group_select<D, G, NW>(sm, p, ret, hq0, split, nsplit_b, nb, r0, nrows, gc, rel);
+    // departure: the last workgroup of the group to leave clears the counters, the
+    // release words and the row histograms for the next call (every workgroup's own
+    // stores, release words included, are complete before it counts itself out)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(gc + 4, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm.misc[0] = (old == (uint32_t)nsplit_b - 1u);
+    }
+    __syncthreads();
+    if (sm.misc[0]) {
+      if (tid < 5) gc[tid] = 0u;
+      for (int s2 = tid; s2 < nsplit_b; s2 += NT) rel[(size_t)s2 * kRelStride] = 0u;
+      if (do_hist) {
+        for (int j = 0; j < G; ++j) {
+          if (!(ret >> j & 1u)) continue;
+          const size_t slot = (size_t)(hq0 + j);
+          for (int i = tid; i < kHist1Bins; i += NT) p.hist1[slot * kHist1Bins + i] = 0u;
+          if (tid == 0) p.row_cnt[slot] = 0u;
+        }
+      }
+    }
+    return;
+  }
+
   // ---- two-level merge: the last split of each run of kMergeRun splits merges the run
   // into a level-1 partial while other splits still stream; the last run of (b, g)
   // merges the level-1 partials into O. One run only: straight into O.
@@ -597,6 +956,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 }
 
 template <int D, int G>
+int64_t capacity_dg(int waves) {
+  int per_cu = 0;
+  hipError_t e;
+  if (waves == 8)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attention<D, G, 8>, 512, 0);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attention<D, G, 4>, 256, 0);
+  return e == hipSuccess ? per_cu : 0;
+}
+
+template <int D, int G>
 hipError_t launch_dg(const AttnParams& p, dim3 grid, hipStream_t st) {
   if (p.waves == 8)
     hipLaunchKernelGGL((k_attention<D, G, 8>), grid, dim3(512), 0, st, p);
@@ -606,6 +976,39 @@ hipError_t launch_dg(const AttnParams& p, dim3 grid, hipStream_t st) {
 }
 
 }  // namespace
+
+int64_t attention_capacity(int D, int G, int waves) {
+  // cached per device and (D, G, waves)
+  static std::atomic<int64_t> cache[64][2][4][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  const int di = D == 128 ? 1 : 0;
+  const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+  const int wi = waves == 8 ? 1 : 0;
+  int64_t c = cache[dev][di][gi][wi].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int64_t per_cu = 0;
+  if (D == 128) {
+    switch (G) {
+      case 1: per_cu = capacity_dg<128, 1>(waves); break;
+      case 2: per_cu = capacity_dg<128, 2>(waves); break;
+      case 4: per_cu = capacity_dg<128, 4>(waves); break;
+      case 8: per_cu = capacity_dg<128, 8>(waves); break;
+    }
+  } else {
+    switch (G) {
+      case 1: per_cu = capacity_dg<64, 1>(waves); break;
+      case 2: per_cu = capacity_dg<64, 2>(waves); break;
+      case 4: per_cu = capacity_dg<64, 4>(waves); break;
+      case 8: per_cu = capacity_dg<64, 8>(waves); break;
+    }
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  c = per_cu * cus;
+  cache[dev][di][gi][wi].store(c, std::memory_order_relaxed);
+  return c;
+}
 
 hipError_t launch_attention(const AttnParams& p, int D, int G, dim3 grid, hipStream_t st) {
   if (D == 128) {

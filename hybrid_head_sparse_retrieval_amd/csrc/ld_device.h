@@ -195,4 +195,82 @@ __device__ __forceinline__ void find_bin_from_top(F cnt, uint32_t k, int* tmp, u
   __syncthreads();
 }
 
+// find_bin_from_top over counts held by the threads themselves: thread t holds the
+// counts of bins t*PER .. t*PER+PER-1 in c[].
+template <int NB, int NT>
+__device__ __forceinline__ void find_bin_regs(const uint32_t (&c)[NB / NT], uint32_t k, int* tmp, uint32_t* res) {
+  constexpr int PER = NB / NT;
+  constexpr int NWV = NT / 64;
+  const int t = threadIdx.x;
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s += c[i];
+  const int lane = t & 63, wave = t >> 6;
+  const int inc = wave_incl_sum((int)s);
+  const int wtot = __builtin_amdgcn_readlane(inc, 63);
+  const int x = wtot - inc + (int)s;
+  if (lane == 0) tmp[wave] = x;
+  __syncthreads();
+  int above_waves = 0;
+#pragma unroll
+  for (int i = 0; i < NWV; ++i) above_waves += (i > wave) ? tmp[i] : 0;
+  __syncthreads();
+  uint32_t run = (uint32_t)(above_waves + x - (int)s);
+  if (run < k && run + s >= k) {
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (run + c[i] >= k) { res[0] = (uint32_t)(t * PER + i); res[1] = run; break; }
+      run += c[i];
+    }
+  }
+  __syncthreads();
+}
+
+// Sum over the NT threads of a workgroup, returned to every thread. tmp: __shared__
+// int[NT / 64].
+template <int NT>
+__device__ __forceinline__ int block_sum(int v, int* tmp) {
+  const int w = wave_total(v);
+  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = w;
+  __syncthreads();
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) s += tmp[i];
+  __syncthreads();
+  return s;
+}
+
+// Barrier number k (1, 2, ...) of the ns workgroups of a group, all resident at once.
+// Arrivals are counted in *cnt once each workgroup's earlier stores and atomics are
+// complete; the last to arrive writes k into every member's own release word (one
+// 128-byte line each, rel[s * kRelStride]), and the others poll only their own word,
+// with a read-modify-write (performed where the release lands, never a stale copy).
+// The wait is bounded; giving up sets *err.
+constexpr int kRelStride = 32;
+__device__ __forceinline__ void group_barrier(uint32_t* cnt, uint32_t* rel, int me, int ns, uint32_t k,
+                                              uint32_t* err, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = (old == (uint32_t)ns - 1u);
+  }
+  __syncthreads();
+  if (*flag) {
+    for (int s = tid; s < ns; s += (int)blockDim.x) st_dev(rel + (size_t)s * kRelStride, k);
+  } else if (tid == 0) {
+    uint32_t* mine = rel + (size_t)me * kRelStride;
+    int spins = 0;
+    while (__hip_atomic_fetch_or(mine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < k) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kMaxSpins) {
+        st_dev(err, 1u);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 }  // namespace ld

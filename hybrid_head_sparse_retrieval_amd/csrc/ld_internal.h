@@ -22,6 +22,7 @@ constexpr int kMaxSelSpans = kMaxSeq / kSelSpan;     // 128
 constexpr int kMaxSplits = 1024;       // attention splits per sequence
 constexpr int kMergeRun = 64;          // splits merged by one first-level merge
 constexpr int kBitmapWordsPerBlock = 4096;           // bitmap-build LDS tile (16 KiB)
+constexpr int kMaxSpins = 1 << 22;     // bound of a barrier wait (polls with a short sleep)
 
 // ---------------------------------------------------------------- parameters
 
@@ -43,7 +44,7 @@ struct AttnParams {
   int nsplit;             // splits per sequence at seq_len (grid stride)
   int ngroups;            // KV groups launched
   uint8_t groups[64];     // their ids
-  const uint32_t* bitmaps;   // [B*Hq][W] membership bits of sparse heads
+  uint32_t* bitmaps;      // [B*Hq][W] membership bits (read: sparse heads; written: selecting heads)
   int W;
   float* logits;          // [B*Hq][seq_len] scores of retrieval heads, or null
   float* part_ml;         // [B*Hq][P][2]  (max in log2 units, sum)
@@ -60,6 +61,18 @@ struct AttnParams {
   uint32_t* sel_info;     // [B*Hq][4]
   int k_dense;
   const int64_t* s_indptr;
+  // group-barrier mode (every workgroup of the launch resident at once): the splits of
+  // a group meet after storing their partials, merge O column by column and run the
+  // selection of the group's retrieval heads over their own rows
+  int gb;
+  uint32_t* gb_cnt;       // [B*Hkv][8] barrier counters, zero between calls
+  uint32_t* gb_rel;       // [B*Hkv][P] release words, one per 128 bytes, zero between calls
+  uint32_t* row_cnt;      // [B*Hq] candidates appended to each row's list, zero between calls
+  uint64_t* cand;         // [B*Hq][ncap] (index << 32 | key) of the candidates
+  int64_t ncap;
+  uint32_t* pub;          // [B*Hq][P][2] per split: keys above bin b1
+  int32_t* s_out;         // S rows written for selecting heads
+  uint32_t* err;          // set when a barrier gave up waiting (never expected)
 };
 
 // argsTopK over rows. Row slots index the per-row workspace arrays.
@@ -105,6 +118,7 @@ struct CopyParams {
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_attention(const AttnParams& p, int D, int G, dim3 grid, hipStream_t st);
+int64_t attention_capacity(int D, int G, int waves);   // workgroups resident at once
 hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist);
 hipError_t launch_bitmap_build(const BitmapParams& p, int rows, hipStream_t st);
 hipError_t launch_copy_rows(const CopyParams& p, int rows, hipStream_t st);

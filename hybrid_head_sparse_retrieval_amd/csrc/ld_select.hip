@@ -110,7 +110,6 @@ constexpr int kSpanThreads = 1024;
 constexpr int kSpanWaves = kSpanThreads / 64;
 constexpr int kSpanRounds = kSelSpan / (4 * kSpanThreads);   // float4 loads per thread
 constexpr int kFineCap = 4096;                                // fine candidates kept in LDS
-constexpr int kMaxSpins = 1 << 22;                            // bound of the row-barrier wait
 constexpr int kSpecSlots = 4;                                 // candidates fetched early per thread
 static_assert(kSpanRounds == 4, "one 16-bit lane mask per span");
 
@@ -523,7 +522,8 @@ __global__ __launch_bounds__(kSpanThreads) void k_sel_fused(const SelParams p) {
     const uint32_t old = __hip_atomic_fetch_add(p.tickets + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old != (uint32_t)nsp - 1u) {
       int spins = 0;
-      while (ld_dev(p.tickets + slot) < (uint32_t)nsp) {
+      // read-modify-write polls are performed where the arrivals are counted
+      while (__hip_atomic_fetch_add(p.tickets + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)nsp) {
         __builtin_amdgcn_s_sleep(2);
         if (++spins > kMaxSpins) {               // never expected: report and go on
           st_dev(p.err, 1u);

@@ -75,7 +75,13 @@ enum {
   /* The caller promises that s_in is the s_out written by the previous call on this
      workspace with the same shape, so the workspace's per-head membership bitmaps
      already describe s_in and need not be rebuilt. */
-  LD_FLAG_S_CHAINED = 1u << 1
+  LD_FLAG_S_CHAINED = 1u << 1,
+  /* Launch-shape override: merge the split partials and run argsTopK in their own
+     steps after the attention launch, even when the whole launch fits on the device
+     at once (where, by default, the splits of each KV group meet at device-wide
+     barriers and do both themselves). S is the same either way; O may differ by
+     fp32 rounding. */
+  LD_FLAG_SEPARATE_SELECT = 1u << 2
 };
 /* Optional launch-shape overrides (0 = automatic): rows per attention split =
    256 << (v - 1) for v = 1..4 in bits 8..11, and waves per attention workgroup in

@@ -20,7 +20,7 @@ def _ld():
 
 
 def run_layers(B, Hq, Hkv, d, lens, masks, seed, k=None, csr=False, chain=True, split=0,
-               check=True, frac=0.3):
+               check=True, frac=0.3, extra_flags=0):
     """Run len(masks) layers on the GPU and check every layer against the oracle."""
     ld = _ld()
     dev = "cuda"
@@ -53,7 +53,7 @@ def run_layers(B, Hq, Hkv, d, lens, masks, seed, k=None, csr=False, chain=True, 
         q, kk, vv = qc.to(dev), kc.to(dev), vc.to(dev)
         S_before = S.cpu().numpy().copy()
         out = torch.empty_like(q)
-        flags = (ld.FLAG_S_CHAINED if (chain and l > 0) else 0) | ld.flag_split_rows(split)
+        flags = (ld.FLAG_S_CHAINED if (chain and l > 0) else 0) | ld.flag_split_rows(split) | extra_flags
         ld.hybrid_layer(q, kk, vv, masks[l], kmax, S if l > 0 else None, s_out=S, s_indptr=s_indptr,
                         scores_out=scores, out=out, flags=flags, workspace=ws,
                         kv_indptr=kv_indptr, seq_len=N)
@@ -192,3 +192,66 @@ def test_retrieval_decode_subset_of_heads_leaves_others():
             assert np.all(np.diff(S[0, h].cpu().numpy()) > 0)
         else:
             assert torch.all(out[0, h] == 7.0) and torch.all(S[0, h] == -5)
+
+
+@pytest.mark.parametrize("case", [
+    (1, 8, 2, 128, [5000], [0xFF, 0b00100001, 0, 0b1000], 21, False),
+    (2, 32, 8, 128, [3000, 4100], wl.seeded_masks(22, 3, 32, 2), 22, True),
+])
+def test_separate_merge_and_select_steps(case):
+    # the same layers with the split merge and argsTopK run as their own launches
+    ld = _ld()
+    B, Hq, Hkv, d, lens, masks, seed, csr = case
+    run_layers(B, Hq, Hkv, d, lens, masks, seed, csr=csr, extra_flags=ld.FLAG_SEPARATE_SELECT)
+
+
+def test_in_launch_and_separate_select_agree():
+    ld = _ld()
+    args = (2, 8, 2, 128, [2600, 6100], [0xFF, 0b01000010, 0, 0b00010000], 23)
+    a = run_layers(*args, csr=True, check=False)
+    b = run_layers(*args, csr=True, check=False, extra_flags=ld.FLAG_SEPARATE_SELECT)
+    for (oa, sa), (ob, sb) in zip(a, b):
+        assert np.array_equal(sa, sb), "selected sets differ between the two launch modes"
+        da = gh.bf16_tensor_to_f64(oa)
+        db = gh.bf16_tensor_to_f64(ob)
+        assert np.abs(da - db).max() <= gh.MAX_ABS
+
+
+@pytest.mark.parametrize("entry,mask", [("layer", 0xFF), ("layer-separate", 0xFF),
+                                        ("retrieval", 0x11), ("retrieval", 0x22)])
+def test_ties_at_the_threshold_span_splits(entry, mask):
+    # every third key row of a KV head is the same vector, aligned with the group's
+    # queries: 2000 equal top scores per head, of which the k = 1800 lowest rows win
+    ld = _ld()
+    dev = "cuda"
+    Hq, Hkv, d, n, k = 8, 2, 128, 6000, 1800
+    q, kc, vc = wl.random_qkv(1, Hq, Hkv, d, n, 24)
+    G = Hq // Hkv
+    for g in range(Hkv):
+        u = q[0, g * G:(g + 1) * G].float().mean(0)
+        u = 10.0 * u / u.norm()
+        kc[g, 0::3] = u.to(kc.dtype)
+    qd, kd, vd = q.to(dev), kc.to(dev), vc.to(dev)
+    shape = ld.make_shape(qd, kd)
+    ws = ld.Workspace(shape, k, dev)
+    S = torch.zeros((1, Hq, k), dtype=torch.int32, device=dev)
+    scores = torch.empty((1, Hq, n), dtype=torch.float32, device=dev)
+    # one retrieval head per KV group (0x11, 0x22) selects inside the attention launch
+    out = torch.zeros_like(qd)
+    if entry == "retrieval":
+        ld.retrieval_decode(qd, kd, vd, mask, k, s_out=S, scores_out=scores, out=out, workspace=ws)
+    else:
+        flags = ld.FLAG_SEPARATE_SELECT if entry == "layer-separate" else 0
+        ld.hybrid_layer(qd, kd, vd, mask, k, None, s_out=S, scores_out=scores, out=out, flags=flags,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()
+    Sh = S.cpu().numpy()
+    heads = [h for h in range(Hq) if mask >> h & 1]
+    for h in heads:
+        exact = orc.select_topk_f32(sc[0, h], k)
+        assert np.array_equal(Sh[0, h], exact)
+        assert np.array_equal(Sh[0, h], np.arange(0, 3 * k, 3)), "ties must go to the lowest rows"
+    O_ref, _, _ = orc.hybrid_layer_bf16(wl.bf16_bits(q), wl.bf16_bits(kc), wl.bf16_bits(vc),
+                                        [0, n], [True] * Hq, [k], None)
+    gh.check_outputs(out, O_ref, [(0, h) for h in heads])
