@@ -13,10 +13,10 @@ algorithmic bytes of a layer are
                             |union of the group's S rows|*2*d*2
   + Q and O (B*Hq*d*2 each) + S reads of sparse heads and S writes of retrieval
   heads (k_b*4 each).
-The roofline object is for the attention kernel (the dominant kernel): its
-algorithmic bytes (KV + Q + O) per launch over its average launch duration, timed
-with HIP events on the launch stream in a pass where each layer's attention kernel
-runs alone (LD_FLAG_SKIP_TOPK; the untimed full layer follows to advance S).
+The roofline object is for the attention kernel (the dominant kernel; it also
+merges the splits and, for layers with one retrieval head per KV group, selects S):
+its algorithmic bytes (KV + Q + O) per launch over its average launch duration, timed
+with HIP events on the launch stream, one layer call at a time.
 """
 from __future__ import annotations
 
@@ -208,21 +208,52 @@ def main():
     step_bytes = float(sum(total_bytes))
     log(f"[bench] algorithmic bytes/step {step_bytes / 1e9:.3f} GB")
 
-    # ---- warmup + timed steps
+    # ---- warmup + timed steps (events between steps, on the launch stream)
     for _ in range(args.warmup):
         step.run(inputs)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
+    sev[0].record()
+    for i in range(args.steps):
         step.run(inputs)
-    ev1.record()
+        sev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
+    per_step = np.array([sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps)])
+    ms_step = sev[0].elapsed_time(sev[-1]) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step; "
+        f"p10 {np.percentile(per_step, 10) * 1e3:.1f}, p50 {np.median(per_step) * 1e3:.1f}, "
+        f"p90 {np.percentile(per_step, 90) * 1e3:.1f} us)")
+
+    # ---- the same step captured once in a HIP graph and replayed
+    ms_graph = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step.run(inputs)           # eager pass on the capture stream first
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cap):
+                step.run(inputs)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        gev0, gev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gev0.record()
+        for _ in range(args.steps):
+            g.replay()
+        gev1.record()
+        torch.cuda.synchronize()
+        ms_graph = gev0.elapsed_time(gev1) / args.steps
+        log(f"[bench] graph replay: {ms_graph * 1e3:.1f} us/step")
+        del g
+    except Exception as e:  # capture is a secondary figure; report and go on
+        log(f"[bench] graph capture unavailable: {e}")
 
     # ---- per-layer times inside full steps
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
@@ -238,7 +269,11 @@ def main():
             log(f"  layer {l:2d} mask={w.retrieval_masks[l]:#x} {per_layer[l]:8.1f} us "
                 f"{total_bytes[l] / per_layer[l] / 1e3:8.1f} GB/s")
 
-    # ---- attention kernel alone, per layer (HIP events on the launch stream)
+    # ---- the attention launch of every layer, timed alone with HIP events on the launch
+    # stream (a GPU-side wait first keeps the host's launch latency out of the span).
+    # Layers whose call is the attention launch alone (in-launch merge and selection)
+    # give its duration; the few that also run a separate selection launch are timed
+    # with it, so their span is an upper bound of the attention launch.
     roof = None
     if not args.no_kernel_pass:
         ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -247,12 +282,10 @@ def main():
             d_rep = []
             for l in range(L):
                 q, kc, vc = inputs[l]
-                # a GPU-side wait keeps the host's launch latency out of the timed span
                 torch.cuda._sleep(200000)
                 ka.record()
-                step.layer(l, q, kc, vc, extra_flags=ld.FLAG_SKIP_TOPK)
+                step.layer(l, q, kc, vc)
                 kb.record()
-                step.layer(l, q, kc, vc)          # untimed: advances S and the bitmaps
                 torch.cuda.synchronize()
                 d_rep.append(ka.elapsed_time(kb) * 1e3)
             durs.append(d_rep)
@@ -262,10 +295,10 @@ def main():
         achieved = avg_bytes / (avg_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(w.name),
-                "kernel": "k_attention<128,4>" if d == 128 and w.group_size == 4 else "k_attention",
+                "kernel": "k_attention<128,4,4>" if d == 128 and w.group_size == 4 else "k_attention",
                 "avg_launch_us": round(avg_us, 2), "avg_bytes_per_launch": int(avg_bytes),
                 "launches_timed": L}
-        log(f"[bench] attention kernel: avg {avg_us:.1f} us/launch, {achieved:.0f} GB/s "
+        log(f"[bench] attention launch: avg {avg_us:.1f} us, {achieved:.0f} GB/s "
             f"({achieved / HBM_PEAK_GBS * 100:.1f}% of peak)")
 
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -279,6 +312,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
+        "ms_per_step_graph": round(ms_graph, 4) if ms_graph else None,
         "us_per_layer": round(ms_step * 1e3 / L, 2),
         "pct_of_hbm_peak": round(value / HBM_PEAK_GBS * 100, 2),
         "us_layer0": round(float(per_layer[0]), 2),
