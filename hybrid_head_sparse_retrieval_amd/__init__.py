@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = ("ld_status_string", "ld_workspace_size", "ld_topk_workspace_
 
 
 def flag_split_rows(v: int) -> int:
-    """Rows per attention split = 256 << (v - 1), v in 1..4 (0 = automatic)."""
+    """Rows per attention split = 256 << (v - 1), v in 1..5 (0 = automatic)."""
     return (int(v) & 0xF) << 8
 
 
@@ -82,6 +82,12 @@ def load_library():
     if not os.path.exists(path):
         raise LycheeDecodeUnavailable(
             f"{path} is missing; build it with `python -m hybrid_head_sparse_retrieval_amd.build`")
+    # torch brings its own HIP runtime; load it first so that the library binds to the
+    # same runtime (and so the same device context) as the tensors it is handed
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, i64, u32, u64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                   ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t)

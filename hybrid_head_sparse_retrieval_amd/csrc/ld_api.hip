@@ -95,7 +95,7 @@ LayerLayout layer_layout(const ld_shape* s) {
   LayerLayout L{};
   const int N = s->seq_len;
   L.slots = s->batch * s->num_q_heads;
-  L.P = (N + 255) / 256;
+  L.P = (N + 63) / 64;
   if (L.P > kMaxSplits) L.P = kMaxSplits;
   L.W = (N + 31) / 32;
   size_t o = 0;
@@ -141,27 +141,51 @@ int cu_count() {
   return c;
 }
 
-// Rows per attention split (256 << (v-1), override v in flag bits 8..11) and waves
-// per workgroup (flag bits 12..13: 1 = 4 waves, 2 = 8 waves). Automatic choice: 4
-// waves and the smallest split of at least 256 rows that keeps the launch within one
-// round of resident workgroups (two 4-wave workgroups per compute unit: the kernel
-// holds over 128 VGPRs per lane), capped so that no sequence needs more than
-// kMaxSplits splits.
-void choose_split(int N, int64_t groups_total, uint32_t flags, int* ts_out, int* waves_out) {
-  const int wv = (int)((flags >> 12) & 0x3u);
-  const int waves = (wv == 2) ? 8 : 4;
+// Waves per attention workgroup: flag bits 12..13 (1 = 4 waves, 2 = 8 waves); 4 by
+// default.
+int choose_waves(uint32_t flags) { return (((flags >> 12) & 0x3u) == 2u) ? 8 : 4; }
+
+// Rows per split for the groups that stream every row (ts_d) and for the groups of
+// sparse heads, which visit only the union of their rows (ts_s). Flag bits 8..11 = v
+// (1..5) force 256 << (v-1) rows for both. Otherwise both finish together and the grid
+// fits in one round of resident workgroups (`capacity`): a streaming split of ts_d rows
+// costs as much as a gathering split of ts_s rows of estimated union density rho, plus,
+// when the group selects inside the launch, the selection's fixed latency counted as
+// `sel_rows` rows of streaming. The smallest ts_s that fits gives the most parallelism.
+// Returns false when no choice fits (the caller then takes one uniform size).
+constexpr int kSelRows = 384;
+bool choose_splits(int N, int B, int ng_dense, int ng_sparse, double rho, int sel_rows, int64_t capacity,
+                   uint32_t flags, int* ts_d, int* ts_s) {
   const int v = (int)((flags >> 8) & 0xfu);
-  int ts;
-  if (v >= 1 && v <= 4) {
-    ts = 256 << (v - 1);
-  } else {
-    const int64_t resident = (int64_t)cu_count() * (waves == 8 ? 1 : 2);
-    ts = 256;
-    while (ts < kMaxSplitRows && groups_total * (int64_t)((N + ts - 1) / ts) > resident) ts <<= 1;
+  auto nsp = [&](int ts) { return (int64_t)((N + ts - 1) / ts); };
+  if (v >= 1 && v <= 5) {
+    *ts_d = *ts_s = 256 << (v - 1);
+    return true;
   }
+  for (int s = 256; s <= kMaxSplitRows; s += 64) {
+    int d = (int)(rho * s) - sel_rows;
+    d = std::max(192, std::min(kMaxSplitRows, (d + 63) / 64 * 64));
+    if (ng_dense == 0) d = s;
+    if (ng_sparse == 0) { d = s; }
+    if (nsp(d) > kMaxSplits || nsp(s) > kMaxSplits) continue;
+    const int64_t wgs = (int64_t)B * (ng_dense * nsp(d) + ng_sparse * nsp(s));
+    if (wgs <= capacity) {
+      *ts_d = d;
+      *ts_s = s;
+      return true;
+    }
+  }
+  return false;
+}
+
+// Uniform split size when the grid cannot fit one round: the smallest power of two
+// from 256 rows that keeps each sequence within kMaxSplits splits and, if possible,
+// the grid within `capacity`.
+int uniform_split(int N, int64_t groups_total, int64_t capacity) {
+  int ts = 256;
+  while (ts < kMaxSplitRows && groups_total * (int64_t)((N + ts - 1) / ts) > capacity) ts <<= 1;
   while ((N + ts - 1) / ts > kMaxSplits && ts < kMaxSplitRows) ts <<= 1;
-  *ts_out = ts;
-  *waves_out = waves;
+  return ts;
 }
 
 // Core of the three layer entry points.
@@ -233,14 +257,36 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   ap.B = B; ap.Hq = Hq; ap.Hkv = Hkv; ap.seq_len = N;
   ap.scale = scale;
   ap.active = active; ap.retrieval = retrieval;
-  int ng = 0;
-  for (int g = 0; g < Hkv; ++g) {
-    const uint64_t gm = ((G == 64) ? ~0ull : ((1ull << G) - 1ull)) << (g * G);
-    if (active & gm) ap.groups[ng++] = (uint8_t)g;
+  // groups that stream (they serve a retrieval head) first, then groups of sparse heads
+  int ng = 0, ng_dense = 0, ret_per_group = 0, sp_per_group = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int g = 0; g < Hkv; ++g) {
+      const uint64_t gm = ((G == 64) ? ~0ull : ((1ull << G) - 1ull)) << (g * G);
+      if (!(active & gm)) continue;
+      const bool streams = (retrieval & gm) != 0;
+      if (streams != (pass == 0)) continue;
+      ap.groups[ng++] = (uint8_t)g;
+      ret_per_group = std::max(ret_per_group, __builtin_popcountll(retrieval & gm));
+      sp_per_group = std::max(sp_per_group, __builtin_popcountll(active & ~retrieval & gm));
+    }
+    if (pass == 0) ng_dense = ng;
   }
   ap.ngroups = ng;
-  choose_split(N, (int64_t)B * ng, flags, &ap.ts, &ap.waves);
-  ap.nsplit = (N + ap.ts - 1) / ap.ts;
+  ap.ng_dense = ng_dense;
+  ap.waves = choose_waves(flags);
+  // The in-launch selection handles a group's retrieval heads one after another, so
+  // layers with several retrieval heads per group select in their own launch, where
+  // every row runs in parallel.
+  const bool want_gb = !(flags & LD_FLAG_SEPARATE_SELECT) && !(do_topk && ret_per_group > 1);
+  const int64_t capacity = attention_capacity(D, G, ap.waves);
+  // union density of a sparse group's rows if its heads' sets were independent
+  const double kf = std::min(1.0, (double)k / (double)N);
+  const double rho = 1.0 - std::pow(1.0 - kf, (double)std::max(1, sp_per_group));
+  const int sel_rows = (want_gb && do_topk) ? kSelRows : 0;
+  if (!choose_splits(N, B, ng_dense, ng - ng_dense, rho, sel_rows, capacity, flags, &ap.ts_d, &ap.ts_s))
+    ap.ts_d = ap.ts_s = uniform_split(N, (int64_t)B * ng, capacity);
+  ap.nsplit_d = (N + ap.ts_d - 1) / ap.ts_d;
+  ap.nsplit_s = (N + ap.ts_s - 1) / ap.ts_s;
   ap.bitmaps = bitmaps; ap.W = L.W;
   ap.logits = scores_out ? scores_out : (do_topk ? at<float>(ws, L.logits) : nullptr);
   ap.part_ml = at<float>(ws, L.part_ml);
@@ -256,19 +302,10 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   ap.sel_info = at<uint32_t>(ws, L.sel.sel_info);
   ap.k_dense = k;
   ap.s_indptr = s_indptr;
-  const int64_t nwg = (int64_t)B * ng * ap.nsplit;
-  // every workgroup resident at once: the splits of a group merge O and select
+  const int64_t nwg = (int64_t)B * ((int64_t)ng_dense * ap.nsplit_d + (int64_t)(ng - ng_dense) * ap.nsplit_s);
+  // every workgroup resident at once: the splits of a group merge O (and select)
   // together behind device-wide barriers inside this launch
-  // (the in-launch selection handles a group's retrieval heads one after another, so
-  // layers with several retrieval heads per group select in their own launch, where
-  // every row runs in parallel)
-  int ret_per_group = 0;
-  for (int g = 0; g < Hkv; ++g) {
-    const uint64_t gm = ((G == 64) ? ~0ull : ((1ull << G) - 1ull)) << (g * G);
-    ret_per_group = std::max(ret_per_group, __builtin_popcountll(retrieval & gm));
-  }
-  const bool gb = !(flags & LD_FLAG_SEPARATE_SELECT) && !(do_topk && ret_per_group > 1) &&
-                  nwg <= attention_capacity(D, G, ap.waves);
+  const bool gb = want_gb && nwg <= capacity;
   if (gb) {
     ap.gb = 1;
     ap.gb_cnt = at<uint32_t>(ws, L.gb_cnt);

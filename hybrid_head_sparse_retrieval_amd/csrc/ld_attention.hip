@@ -334,7 +334,7 @@ __device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnP
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int r = i * NT + tid;
-      key[j][i] = (r < nrows) ? score_key(lgj[r]) : 0u;
+      key[j][i] = (r < nrows) ? score_key(ld_dev(lgj + r)) : 0u;
     }
   }
 #pragma unroll
@@ -435,6 +435,7 @@ __device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnP
     const uint32_t b2 = sm.res[0];
     const uint32_t k2 = k1[j] - sm.res[1];
     const uint32_t pre = (b1[j] << 11) | b2;
+    __syncthreads();    // every wave has read the result before it is cleared
     if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
     __syncthreads();
     for_cands([&](uint32_t kv, uint32_t) { if ((kv >> 10) == pre) atomicAdd(&h3[kv & 0x3ffu], 1u); });
@@ -537,10 +538,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   const bool do_hist = p.do_topk != 0;
 
   int bid = blockIdx.x;
-  const int split = bid % p.nsplit;
-  bid /= p.nsplit;
-  const int gi = bid % p.ngroups;
-  const int b = bid / p.ngroups;
+  const int dense_blocks = p.B * p.ng_dense * p.nsplit_d;
+  int split, gi, b, ts;
+  if (bid < dense_blocks) {
+    split = bid % p.nsplit_d;
+    bid /= p.nsplit_d;
+    gi = bid % p.ng_dense;
+    b = bid / p.ng_dense;
+    ts = p.ts_d;
+  } else {
+    const int ngs = p.ngroups - p.ng_dense;
+    bid -= dense_blocks;
+    split = bid % p.nsplit_s;
+    bid /= p.nsplit_s;
+    gi = p.ng_dense + bid % ngs;
+    b = bid / ngs;
+    ts = p.ts_s;
+  }
   const int g = p.groups[gi];
 
   int64_t tok0;
@@ -556,10 +570,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   nb = min(nb, p.seq_len);
   if (tok0 < 0 || tok0 >= p.total_tokens) nb = 0;
   else if ((int64_t)nb > p.total_tokens - tok0) nb = (int)(p.total_tokens - tok0);
-  const int nsplit_b = (nb + p.ts - 1) / p.ts;
+  const int nsplit_b = (nb + ts - 1) / ts;
   if (nb <= 0 || split >= nsplit_b) return;
-  const int r0 = split * p.ts;
-  const int nrows = min(p.ts, nb - r0);
+  const int r0 = split * ts;
+  const int nrows = min(ts, nb - r0);
 
   // Head roles inside the group (bit j <-> query head g*G + j).
   uint32_t act = 0, ret = 0;

@@ -10,7 +10,7 @@ namespace ld {
 // ---------------------------------------------------------------- constants
 
 constexpr int kThreads = 256;          // every kernel runs 4 wave64s per workgroup
-constexpr int kMaxSplitRows = 2048;    // largest attention split (rows per workgroup)
+constexpr int kMaxSplitRows = 4096;    // largest attention split (rows per workgroup)
 constexpr int kSelChunk = 512;         // scores per select workgroup (2 per thread)
 constexpr int kHist1Bins = 2048;       // digit 1: key bits 31..21
 constexpr int kHist2Bins = 2048;       // digit 2: key bits 20..10
@@ -39,10 +39,13 @@ struct AttnParams {
   float scale;            // logit scale
   uint64_t active;        // heads computed by this launch
   uint64_t retrieval;     // heads attending to every row (subset of active)
-  int ts;                 // rows per split (multiple of 256)
+  // Groups that stream every row (they serve a retrieval head) come first in groups[]
+  // and use splits of ts_d rows; groups of sparse heads use splits of ts_s rows.
+  int ts_d, ts_s;         // rows per split (multiples of 64)
+  int nsplit_d, nsplit_s; // splits per sequence at seq_len (grid strides)
   int waves;              // waves per workgroup (4 or 8)
-  int nsplit;             // splits per sequence at seq_len (grid stride)
   int ngroups;            // KV groups launched
+  int ng_dense;           // the first ng_dense of them stream
   uint8_t groups[64];     // their ids
   uint32_t* bitmaps;      // [B*Hq][W] membership bits (read: sparse heads; written: selecting heads)
   int W;

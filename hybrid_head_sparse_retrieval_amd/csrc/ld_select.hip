@@ -344,6 +344,7 @@ __device__ __forceinline__ void row_threshold(const SelParams& p, int slot, int 
     find_bin_from_top<1024, kSpanThreads>([&](int i) { return sm.hist[1023 - i]; }, e_take, sm.tmp, sm.res);
     const uint32_t binA = 1023u - sm.res[0];
     const uint32_t eB = e_take - sm.res[1];
+    __syncthreads();    // every wave has read the result before it is cleared
     for (int i = tid; i < 2048; i += kSpanThreads) sm.hist[i] = 0u;
     if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
     __syncthreads();

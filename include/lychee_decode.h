@@ -84,9 +84,10 @@ enum {
   LD_FLAG_SEPARATE_SELECT = 1u << 2
 };
 /* Optional launch-shape overrides (0 = automatic): rows per attention split =
-   256 << (v - 1) for v = 1..4 in bits 8..11, and waves per attention workgroup in
-   bits 12..13 (1 = 4 waves, 2 = 8 waves). Results do not depend on them beyond fp32
-   rounding. */
+   256 << (v - 1) for v = 1..5 in bits 8..11, for every KV group (automatic: groups
+   serving a retrieval head get smaller splits than groups of sparse heads, so both
+   finish together), and waves per attention workgroup in bits 12..13 (1 = 4 waves,
+   2 = 8 waves). Results do not depend on them beyond fp32 rounding. */
 #define LD_FLAG_SPLIT_ROWS(v) ((uint32_t)(v) << 8)
 #define LD_FLAG_WAVES(v) ((uint32_t)(v) << 12)
 

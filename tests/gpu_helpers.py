@@ -36,12 +36,20 @@ def check_outputs(O_gpu_bf16, O_ref, heads, what=""):
     return worst
 
 
-def check_selected_row(S_gpu_row, scores_gpu_row_f32, scores_ref_f64, k):
+def check_selected_row(S_gpu_row, scores_gpu_row_f32, scores_ref_f64, k, what=""):
     """(a) bit-exact vs the oracle's selection on the GPU's own fp32 scores;
     (b) vs the oracle's fp64 selection, differences only inside the tie zone."""
     S_gpu_row = np.asarray(S_gpu_row, dtype=np.int64)
     exact = orc.select_topk_f32(np.asarray(scores_gpu_row_f32, dtype=np.float32), k)
-    assert np.array_equal(S_gpu_row, exact), "GPU selection differs from the oracle on identical fp32 scores"
+    if not np.array_equal(S_gpu_row, exact):
+        extra = np.setdiff1d(S_gpu_row, exact)[:6]
+        missing = np.setdiff1d(exact, S_gpu_row)[:6]
+        sc = np.asarray(scores_gpu_row_f32, dtype=np.float32)
+        kth = np.sort(sc)[::-1][k - 1]
+        raise AssertionError(
+            f"{what}GPU selection differs from the oracle on identical fp32 scores: len {S_gpu_row.size} vs {k}, "
+            f"extra {extra.tolist()} (scores {sc[extra].tolist()}), missing {missing.tolist()} "
+            f"(scores {sc[missing].tolist()}), k-th score {kth!r}")
     ref = orc.select_topk(scores_ref_f64, k)
     diff = np.setxor1d(S_gpu_row, ref)
     if diff.size:

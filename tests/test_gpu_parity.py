@@ -72,7 +72,8 @@ def run_layers(B, Hq, Hkv, d, lens, masks, seed, k=None, csr=False, chain=True, 
         for b in range(B):
             for h in range(Hq):
                 if ret[h]:
-                    gh.check_selected_row(S_dict[(b, h)], sc[b, h, :lens[b]], sc_ref[(b, h)], kb[b])
+                    gh.check_selected_row(S_dict[(b, h)], sc[b, h, :lens[b]], sc_ref[(b, h)], kb[b],
+                                          what=f"layer {l} (b, h) = {(b, h)}: ")
                 else:
                     assert np.array_equal(S_dict[(b, h)], S_in[(b, h)]), "sparse row changed"
     return results
@@ -108,7 +109,7 @@ def test_small_and_tail_lengths(n):
     run_layers(1, 4, 2, 128, [n], [0xF, 0b0001, 0], 10 + n, k=k)
 
 
-@pytest.mark.parametrize("split", [1, 2, 3, 4])
+@pytest.mark.parametrize("split", [1, 2, 3, 4, 5])
 def test_split_size_invariance(split):
     run_layers(1, 8, 2, 128, [6000], [0xFF, 0b00000010, 0], 11, split=split)
 
