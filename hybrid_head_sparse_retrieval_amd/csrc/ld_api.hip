@@ -29,7 +29,8 @@ struct LayerLayout {
   size_t attn_tickets, attn_tickets_l1;               // zero between calls
   SelArrays sel;
   size_t logits, part_ml, part_acc, l1_ml, l1_acc, bitmaps;
-  size_t gb_cnt, gb_rel, row_cnt, pub;                // group-barrier mode
+  size_t gb_cnt, gb_rel, row_cnt, gb_cand, pub;       // group-barrier mode
+  int64_t sub_cap;
   size_t total;
 };
 
@@ -45,7 +46,7 @@ SelArrays sel_arrays(int rows, int n, Take take) {
   a.C = (n + kSelSpan - 1) / kSelSpan;
   a.ncap = (int64_t)a.C * kSelSpan;
   a.tickets = take((size_t)rows * 4);
-  a.hist1 = take((size_t)rows * kHist1Bins * 4);
+  a.hist1 = take((size_t)rows * kRep * kHist1Bins * 4);
   a.hist2 = take((size_t)rows * kHist2Bins * 4);
   a.depart = take((size_t)rows * 4);
   a.err = take(4);
@@ -110,9 +111,13 @@ LayerLayout layer_layout(const ld_shape* s) {
   L.l1_ml = take((size_t)L.slots * L.P1 * 8);
   L.l1_acc = take((size_t)L.slots * L.P1 * s->head_dim * 4);
   L.bitmaps = take((size_t)L.slots * L.W * 4);
-  L.gb_cnt = take((size_t)s->batch * s->num_kv_heads * 8 * 4);
+  L.gb_cnt = take((size_t)s->batch * s->num_kv_heads * kGbCounters * 4);
   L.gb_rel = take((size_t)s->batch * s->num_kv_heads * L.P * 128);
-  L.row_cnt = take((size_t)L.slots * 4);
+  L.row_cnt = take((size_t)L.slots * kRep * 4);
+  // candidates of the workgroups of one replica: at most ceil(ns / kRep) splits of at
+  // most kMaxSplitRows rows, i.e. below N / kRep + 2 * kMaxSplitRows
+  L.sub_cap = ((int64_t)(N + kRep - 1) / kRep + 2 * kMaxSplitRows + 63) / 64 * 64;
+  L.gb_cand = take((size_t)L.slots * kRep * L.sub_cap * 8);
   L.pub = take((size_t)L.slots * L.P * 8);
   L.total = o;
   return L;
@@ -309,10 +314,10 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   if (gb) {
     ap.gb = 1;
     ap.gb_cnt = at<uint32_t>(ws, L.gb_cnt);
-    ap.gb_rel = at<uint32_t>(ws, L.gb_rel);
+    ap.gb_rel = at<uint64_t>(ws, L.gb_rel);
     ap.row_cnt = at<uint32_t>(ws, L.row_cnt);
-    ap.cand = at<uint64_t>(ws, L.sel.cand);
-    ap.ncap = L.sel.ncap;
+    ap.cand = at<uint64_t>(ws, L.gb_cand);
+    ap.sub_cap = L.sub_cap;
     ap.pub = at<uint32_t>(ws, L.pub);
     ap.s_out = s_out;
     ap.err = at<uint32_t>(ws, L.sel.err);

@@ -41,18 +41,12 @@ constexpr int kChunkRows = kTile * kTPC;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// 128-bit device-coherent (sc1) access through a buffer resource over `base`.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
-}
-constexpr int kSc1 = 16;   // cache-policy bit of sc1 for buffer instructions
 __device__ __forceinline__ float4 ld_dev4_b(__amdgpu_buffer_rsrc_t r, int byte_off) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kSc1);
   return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
@@ -78,9 +72,11 @@ struct AttnSmem {
   uint16_t list[kMaxSplitRows];      // token row (within the tile) of each visit position
   int wcnt[NW];
   int misc[4];
+  uint64_t relw;                     // release word seen by thread 0
   uint32_t res[2];
   int scan[NW][kMaxSplitRows / (64 * NW) / 2 > 2 ? kMaxSplitRows / (64 * NW) / 2 : 2];   // wave totals of scans
   int cnt4[NW][2];
+  int ncnt[kRep];                    // candidate counts of the sub-lists
   float pl[NW][kChunkRows][G];       // per wave: probabilities of the chunk's rows
   union {
     uint32_t hist[G][kHist1Bins];
@@ -291,80 +287,80 @@ __device__ __forceinline__ void rows_scan(const uint32_t (&f)[IT], int (&ex)[IT]
   __syncthreads();
 }
 
-// argsTopK of the group's retrieval heads by the workgroups of the group, each over
-// its own rows (r0 .. r0 + nrows), with one group barrier: every split finds digit 1
-// from the row's fused histogram, appends its candidates (keys whose digit 1 is b1)
-// to the row's candidate list and publishes its count of keys above bin b1; after the
-// barrier every split derives the threshold key T from the whole candidate list
-// (digits 2 and 3), its output offset from the earlier splits' counts, and writes its
-// kept rows (keys equal to T are kept in row order, so the lower indices win ties).
+// k of the row: the row's selection length, at most the sequence length nb.
+__device__ __forceinline__ int select_k(const AttnParams& p, int slot, int nb) {
+  int kk = p.k_dense;
+  if (p.s_indptr) kk = (int)(p.s_indptr[slot + 1] - p.s_indptr[slot]);
+  return min(kk, nb);
+}
+
+// Digit 1 of the row's threshold from its digit-1 histogram (the sum of the kRep
+// replicas), taken once per group by the workgroup that completed the group's first
+// barrier, and published to the group as stage 2 of the release words:
+// bits 8..18 = the bin b1, bits 32..63 = k1, the keys still to take from bin b1.
+template <int D, int G, int NW>
+__device__ __forceinline__ void publish_digit1(AttnSmem<D, G, NW>& sm, const AttnParams& p, int slot, int kk,
+                                               uint64_t* rel, int ns) {
+  constexpr int NT = 64 * NW;
+  constexpr int PB1 = kHist1Bins / NT;          // digit-1 bins per thread
+  const int tid = threadIdx.x;
+  uint32_t* hs = sm.u.sel_hist;                 // free until the selection below
+  hist1_sum(hs, p.hist1, slot);
+  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
+  __syncthreads();
+  uint32_t h[PB1];
+#pragma unroll
+  for (int q = 0; q < PB1; ++q) h[q] = hs[tid * PB1 + q];
+  find_bin_regs<kHist1Bins, NT>(h, (uint32_t)kk, sm.wcnt, sm.res);
+  const uint32_t b1 = sm.res[0], k1 = (uint32_t)kk - sm.res[1];
+  __syncthreads();
+  group_publish(rel, ns, 2ull | ((uint64_t)b1 << 8) | ((uint64_t)k1 << 32));
+}
+
+// argsTopK of the group's one retrieval head by the workgroups of the group, each over
+// its own rows (r0 .. r0 + nrows), with one more group barrier: every split takes
+// digit 1 (b1, k1) from its release word, appends its candidates (keys whose digit 1
+// is b1) to the candidate sub-list of its replica and publishes its count of keys
+// above bin b1; after the barrier every split derives the threshold key T from all
+// candidates (digits 2 and 3), its output offset from the earlier splits' counts, and
+// writes its kept rows (keys equal to T are kept in row order, so the lower indices
+// win ties).
 template <int D, int G, int NW>
 __device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnParams& p, uint32_t ret,
-                                             int hq0, int split, int ns, int nb, int r0, int nrows,
-                                             uint32_t* gc, uint32_t* rel) {
+                                             int hq0, int split, int ns, int bid0, int nb, int r0, int nrows,
+                                             uint32_t* gc, uint64_t* rel) {
   constexpr int NT = 64 * NW;
   constexpr int IT = kMaxSplitRows / NT;        // rows per thread
-  constexpr int PB1 = kHist1Bins / NT;          // digit-1 bins per thread
-  constexpr int SPEC = G <= 4 ? 24 : 8;         // candidates fetched per thread before the count
+  constexpr int SPEC = 32;                      // candidates fetched per thread before the counts
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  uint32_t sel = 0;
-  int kk[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    kk[j] = 0;
-    if (ret >> j & 1u) {
-      const int slot = hq0 + j;
-      int k = p.k_dense;
-      if (p.s_indptr) k = (int)(p.s_indptr[slot + 1] - p.s_indptr[slot]);
-      kk[j] = min(k, nb);
-      if (kk[j] >= 1) sel |= 1u << j;
-    }
-  }
-  if (!sel) return;
+  // the group's one retrieval head (the launch takes this path only when there is one)
+  const int slot = hq0 + __builtin_ctz(ret);
+  const int kk = select_k(p, slot, nb);
+  if (kk < 1) return;                           // the same in every split of the group
 
-  // ---- keys of this split's rows; digit 1 of every selecting head
-  uint32_t key[G][IT];
-  uint32_t b1[G], k1[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    b1[j] = 0; k1[j] = 0;
-    if (!(sel >> j & 1u)) continue;
-    const float* lgj = p.logits + (size_t)(hq0 + j) * p.seq_len + r0;
+  // ---- keys of this split's rows; digit 1
+  uint32_t key[IT];
+  {
+    const float* lg = p.logits + (size_t)slot * p.seq_len + r0;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int r = i * NT + tid;
-      key[j][i] = (r < nrows) ? score_key(ld_dev(lgj + r)) : 0u;
+      key[i] = (r < nrows) ? score_key(ld_dev(lg + r)) : 0u;
     }
   }
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    if (!(sel >> j & 1u)) continue;
-    uint32_t h[PB1];
-    const uint32_t* hg = p.hist1 + (size_t)(hq0 + j) * kHist1Bins + tid * PB1;
-#pragma unroll
-    for (int q = 0; q < PB1; ++q) h[q] = ld_dev(hg + q);
-    if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
-    __syncthreads();
-    find_bin_regs<kHist1Bins, NT>(h, (uint32_t)kk[j], sm.wcnt, sm.res);
-    b1[j] = sm.res[0];
-    k1[j] = (uint32_t)kk[j] - sm.res[1];
-    __syncthreads();
-  }
-
-  // ---- append the candidates to the row's list; publish the count above bin b1
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    if (!(sel >> j & 1u)) continue;
-    const int slot = hq0 + j;
+  const uint64_t w1 = group_wait(rel, split, 2u, p.err, &sm.relw);
+  const uint32_t b1 = (uint32_t)(w1 >> 8) & 0x7ffu, k1 = (uint32_t)(w1 >> 32);
+  {
+    // ---- append the candidates to the row's list; publish the count above bin b1
     uint32_t cm = 0;
     int na = 0;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const bool v = i * NT + tid < nrows;
-      const uint32_t d1 = key[j][i] >> 21;
-      na += (v && d1 > b1[j]) ? 1 : 0;
-      cm |= (uint32_t)(v && d1 == b1[j]) << i;
+      const uint32_t d1 = key[i] >> 21;
+      na += (v && d1 > b1) ? 1 : 0;
+      cm |= (uint32_t)(v && d1 == b1) << i;
     }
     int wt;
     const int before = wave_excl_scan(__popc(cm), wt);
@@ -378,147 +374,151 @@ __device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnP
       tot += sm.scan[w][0];
       atot += sm.scan[w][1];
     }
+    const int rep = rep_of_block();
     if (tid == 0) {
-      sm.misc[2] = tot ? (int)__hip_atomic_fetch_add(p.row_cnt + slot, (uint32_t)tot, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT) : 0;
+      sm.misc[2] = tot ? (int)__hip_atomic_fetch_add(p.row_cnt + (size_t)slot * kRep + rep, (uint32_t)tot,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
       st_dev(p.pub + ((size_t)slot * p.P + split) * 2, (uint32_t)atot);
     }
     __syncthreads();
-    uint64_t* cl = p.cand + (size_t)slot * p.ncap + sm.misc[2] + woff + before;
+    uint64_t* cl = p.cand + ((size_t)slot * kRep + rep) * p.sub_cap + sm.misc[2] + woff + before;
     int q = 0;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       if (cm >> i & 1u) {
-        st_dev(cl + q, ((uint64_t)(uint32_t)(r0 + i * NT + tid) << 32) | key[j][i]);
+        st_dev(cl + q, ((uint64_t)(uint32_t)(r0 + i * NT + tid) << 32) | key[i]);
         ++q;
       }
     }
-    __syncthreads();    // sm.scan / sm.misc reuse
   }
-  group_barrier(gc + 1, rel, split, ns, 2u, p.err, &sm.misc[1]);
+  group_barrier(gc + (kRep + 1), rel, split, ns, bid0, 3u, p.err, &sm.misc[1], &sm.relw);
 
-  // ---- per head: threshold from the whole candidate list, offset, write
+  // ---- threshold from the whole candidate list, offset, write
+  // The candidates sit in kRep sub-lists; the first PER entries of each are fetched
+  // before the counts are known (entries past a count are ignored): register u holds
+  // entry (u / kRep) * NT + tid of sub-list u % kRep.
+  static_assert(SPEC % kRep == 0, "speculative loads cover the sub-lists evenly");
+  constexpr int PER = SPEC / kRep * NT;
+  const uint64_t* cl = p.cand + (size_t)slot * kRep * p.sub_cap;
+  uint64_t cv[SPEC];
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    if (!(sel >> j & 1u)) continue;
-    const int slot = hq0 + j;
-    const uint64_t* cl = p.cand + (size_t)slot * p.ncap;
-    // fetched before the count is known; entries past it are ignored
-    uint64_t cv[SPEC];
+  for (int u = 0; u < SPEC; ++u) cv[u] = ld_dev(cl + (size_t)(u % kRep) * p.sub_cap + (u / kRep) * NT + tid);
+  if (tid < kRep) sm.ncnt[tid] = (int)ld_dev(p.row_cnt + (size_t)slot * kRep + tid);
+  int above = 0;                                  // keys above bin b1 in earlier splits
+  for (int s2 = tid; s2 < split; s2 += NT) above += (int)ld_dev(p.pub + ((size_t)slot * p.P + s2) * 2);
+  uint32_t* h2 = sm.u.sel_hist;                   // [kHist2Bins]
+  uint32_t* h3 = h2 + kHist2Bins;                 // [kHist3Bins]
+  for (int i = tid; i < kHist2Bins + kHist3Bins; i += NT) h2[i] = 0u;
+  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
+  __syncthreads();
+  const int* ncnt = sm.ncnt;
+  // visit(f): every candidate once (the fetched ones from registers)
+  auto for_cands = [&](auto f) {
 #pragma unroll
-    for (int u = 0; u < SPEC; ++u) cv[u] = ld_dev(cl + u * NT + tid);
-    const int ncand = (int)ld_dev(p.row_cnt + slot);
-    int above = 0;                                  // keys above bin b1 in earlier splits
-    for (int s2 = tid; s2 < split; s2 += NT) above += (int)ld_dev(p.pub + ((size_t)slot * p.P + s2) * 2);
-    uint32_t* h2 = sm.u.sel_hist;                   // [kHist2Bins]
-    uint32_t* h3 = h2 + kHist2Bins;                 // [kHist3Bins]
-    for (int i = tid; i < kHist2Bins + kHist3Bins; i += NT) h2[i] = 0u;
-    if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
-    __syncthreads();
-    // visit(f): every candidate once (the fetched ones from registers)
-    auto for_cands = [&](auto f) {
-#pragma unroll
-      for (int u = 0; u < SPEC; ++u)
-        if (u * NT + tid < ncand) f((uint32_t)cv[u], (uint32_t)(cv[u] >> 32));
-      for (int q0 = SPEC * NT; q0 < ncand; q0 += 8 * NT) {
+    for (int u = 0; u < SPEC; ++u)
+      if ((u / kRep) * NT + tid < ncnt[u % kRep]) f((uint32_t)cv[u], (uint32_t)(cv[u] >> 32));
+    for (int r = 0; r < kRep; ++r) {
+      const uint64_t* cr = cl + (size_t)r * p.sub_cap;
+      const int n = ncnt[r];
+      for (int q0 = PER; q0 < n; q0 += 8 * NT) {
         uint64_t x[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = (q0 + u * NT + tid < ncand) ? ld_dev(cl + q0 + u * NT + tid) : 0ull;
+        for (int u = 0; u < 8; ++u) x[u] = (q0 + u * NT + tid < n) ? ld_dev(cr + q0 + u * NT + tid) : 0ull;
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (q0 + u * NT + tid < ncand) f((uint32_t)x[u], (uint32_t)(x[u] >> 32));
+          if (q0 + u * NT + tid < n) f((uint32_t)x[u], (uint32_t)(x[u] >> 32));
       }
-    };
-    for_cands([&](uint32_t kv, uint32_t) { atomicAdd(&h2[(kv >> 10) & 0x7ffu], 1u); });
+    }
+  };
+  for_cands([&](uint32_t kv, uint32_t) { atomicAdd(&h2[(kv >> 10) & 0x7ffu], 1u); });
+  __syncthreads();
+  find_bin_from_top<kHist2Bins, NT>([&](int i) { return h2[i]; }, k1, sm.wcnt, sm.res);
+  const uint32_t b2 = sm.res[0];
+  const uint32_t k2 = k1 - sm.res[1];
+  const uint32_t pre = (b1 << 11) | b2;
+  __syncthreads();    // every wave has read the result before it is cleared
+  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
+  __syncthreads();
+  for_cands([&](uint32_t kv, uint32_t) { if ((kv >> 10) == pre) atomicAdd(&h3[kv & 0x3ffu], 1u); });
+  __syncthreads();
+  find_bin_from_top<kHist3Bins, NT>([&](int i) { return h3[i]; }, k2, sm.wcnt, sm.res);
+  const uint32_t T = (pre << 10) | sm.res[0];
+  const int et = (int)(k2 - sm.res[1]);           // keys equal to T that are kept
+  // candidates of earlier splits above and equal to T; keys equal to T here
+  int ga = 0, ge = 0, me = 0;
+  const uint32_t lo = (uint32_t)r0, hi = (uint32_t)(r0 + nrows);
+  for_cands([&](uint32_t kv, uint32_t ix) {
+    const int early = ix < lo ? 1 : 0, here = (ix >= lo && ix < hi) ? 1 : 0;
+    const int gt1 = kv > T ? 1 : 0, eq1 = kv == T ? 1 : 0;
+    ga += early & gt1;
+    ge += early & eq1;
+    me += here & eq1;
+  });
+  {
+    // the four sums in one exchange
+    const int w0 = wave_total(above), w1 = wave_total(ga), w2 = wave_total(ge), w3 = wave_total(me);
+    if (lane == 0) { sm.scan[wave][0] = w0; sm.scan[wave][1] = w1; }
+    if (lane == 0) { sm.cnt4[wave][0] = w2; sm.cnt4[wave][1] = w3; }
     __syncthreads();
-    find_bin_from_top<kHist2Bins, NT>([&](int i) { return h2[i]; }, k1[j], sm.wcnt, sm.res);
-    const uint32_t b2 = sm.res[0];
-    const uint32_t k2 = k1[j] - sm.res[1];
-    const uint32_t pre = (b1[j] << 11) | b2;
-    __syncthreads();    // every wave has read the result before it is cleared
-    if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
+    above = 0; ga = 0; ge = 0; me = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      above += sm.scan[w][0]; ga += sm.scan[w][1]; ge += sm.cnt4[w][0]; me += sm.cnt4[w][1];
+    }
     __syncthreads();
-    for_cands([&](uint32_t kv, uint32_t) { if ((kv >> 10) == pre) atomicAdd(&h3[kv & 0x3ffu], 1u); });
-    __syncthreads();
-    find_bin_from_top<kHist3Bins, NT>([&](int i) { return h3[i]; }, k2, sm.wcnt, sm.res);
-    const uint32_t T = (pre << 10) | sm.res[0];
-    const int et = (int)(k2 - sm.res[1]);           // keys equal to T that are kept
-    // candidates of earlier splits above and equal to T; keys equal to T here
-    int ga = 0, ge = 0, me = 0;
-    const uint32_t lo = (uint32_t)r0, hi = (uint32_t)(r0 + nrows);
-    for_cands([&](uint32_t kv, uint32_t ix) {
-      const int early = ix < lo ? 1 : 0, here = (ix >= lo && ix < hi) ? 1 : 0;
-      const int gt1 = kv > T ? 1 : 0, eq1 = kv == T ? 1 : 0;
-      ga += early & gt1;
-      ge += early & eq1;
-      me += here & eq1;
-    });
-    {
-      // the four sums in one exchange
-      const int w0 = wave_total(above), w1 = wave_total(ga), w2 = wave_total(ge), w3 = wave_total(me);
-      if (lane == 0) { sm.scan[wave][0] = w0; sm.scan[wave][1] = w1; }
-      if (lane == 0) { sm.cnt4[wave][0] = w2; sm.cnt4[wave][1] = w3; }
-      __syncthreads();
-      above = 0; ga = 0; ge = 0; me = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        above += sm.scan[w][0]; ga += sm.scan[w][1]; ge += sm.cnt4[w][0]; me += sm.cnt4[w][1];
-      }
-      __syncthreads();
-    }
-    const int off = above + ga + min(et, ge);       // kept rows of earlier splits
-    const int keep_e = max(0, min(et - ge, me));    // kept keys equal to T here
-    uint32_t gt[IT], eq[IT], kp[IT];
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const bool v = i * NT + tid < nrows;
-      gt[i] = (v && key[j][i] > T) ? 1u : 0u;
-      eq[i] = (v && key[j][i] == T) ? 1u : 0u;
-    }
-    if (keep_e == me) {
-#pragma unroll
-      for (int i = 0; i < IT; ++i) kp[i] = gt[i] | eq[i];
-    } else if (keep_e == 0) {
-#pragma unroll
-      for (int i = 0; i < IT; ++i) kp[i] = gt[i];
-    } else {
-      int ex[IT], tot[IT];
-      rows_scan<NW, IT>(eq, ex, tot, sm.scan);
-      int before = 0;
-#pragma unroll
-      for (int i = 0; i < IT; ++i) {
-        kp[i] = gt[i] | ((eq[i] && before + ex[i] < keep_e) ? 1u : 0u);
-        before += tot[i];
-      }
-    }
-    int ex[IT], tot[IT];
-    rows_scan<NW, IT>(kp, ex, tot, sm.scan);
-    int64_t so;
-    int klen;
-    if (p.s_indptr) { so = p.s_indptr[slot]; klen = (int)(p.s_indptr[slot + 1] - so); }
-    else { so = (int64_t)slot * p.k_dense; klen = p.k_dense; }
-    klen = min(klen, nb);
-    int32_t* out = p.s_out + so;
-    uint32_t* bm = p.bitmaps ? p.bitmaps + (size_t)slot * p.W : nullptr;
-    int base = off;
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const int r = i * NT + tid;
-      const int pos = base + ex[i];
-      if (kp[i] && pos < klen) out[pos] = r0 + r;
-      base += tot[i];
-      if (bm) {
-        const uint64_t bal = __ballot(kp[i] != 0u);
-        // first row of this lane's word; words past this split's rows are another
-        // split's (splits are whole words: r0 and the split size are multiples of 32)
-        const int rr = i * NT + wave * 64 + (lane & 32);
-        const int row32 = r0 + rr;
-        if ((lane & 31) == 0 && rr < nrows && (row32 >> 5) < p.W)
-          bm[row32 >> 5] = (uint32_t)(bal >> (lane & 32));
-      }
-    }
-    __syncthreads();    // LDS histograms reused by the next head
   }
+  const int off = above + ga + min(et, ge);       // kept rows of earlier splits
+  const int keep_e = max(0, min(et - ge, me));    // kept keys equal to T here
+  uint32_t gt[IT], eq[IT], kp[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const bool v = i * NT + tid < nrows;
+    gt[i] = (v && key[i] > T) ? 1u : 0u;
+    eq[i] = (v && key[i] == T) ? 1u : 0u;
+  }
+  if (keep_e == me) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) kp[i] = gt[i] | eq[i];
+  } else if (keep_e == 0) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) kp[i] = gt[i];
+  } else {
+    int ex[IT], tot[IT];
+    rows_scan<NW, IT>(eq, ex, tot, sm.scan);
+    int before = 0;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      kp[i] = gt[i] | ((eq[i] && before + ex[i] < keep_e) ? 1u : 0u);
+      before += tot[i];
+    }
+  }
+  int ex[IT], tot[IT];
+  rows_scan<NW, IT>(kp, ex, tot, sm.scan);
+  int64_t so;
+  int klen;
+  if (p.s_indptr) { so = p.s_indptr[slot]; klen = (int)(p.s_indptr[slot + 1] - so); }
+  else { so = (int64_t)slot * p.k_dense; klen = p.k_dense; }
+  klen = min(klen, nb);
+  int32_t* out = p.s_out + so;
+  uint32_t* bm = p.bitmaps ? p.bitmaps + (size_t)slot * p.W : nullptr;
+  int base = off;
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int r = i * NT + tid;
+    const int pos = base + ex[i];
+    if (kp[i] && pos < klen) out[pos] = r0 + r;
+    base += tot[i];
+    if (bm) {
+      const uint64_t bal = __ballot(kp[i] != 0u);
+      // first row of this lane's word; words past this split's rows are another
+      // split's (splits are whole words: r0 and the split size are multiples of 32)
+      const int rr = i * NT + wave * 64 + (lane & 32);
+      const int row32 = r0 + rr;
+      if ((lane & 31) == 0 && rr < nrows && (row32 >> 5) < p.W)
+        bm[row32 >> 5] = (uint32_t)(bal >> (lane & 32));
+    }
+  }
+  __syncthreads();
 }
 
 template <int D, int G, int NW>
@@ -539,9 +539,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 
   int bid = blockIdx.x;
   const int dense_blocks = p.B * p.ng_dense * p.nsplit_d;
-  int split, gi, b, ts;
+  int split, gi, b, ts, bid0;                 // bid0: id of the group's first split
   if (bid < dense_blocks) {
     split = bid % p.nsplit_d;
+    bid0 = bid - split;
     bid /= p.nsplit_d;
     gi = bid % p.ng_dense;
     b = bid / p.ng_dense;
@@ -550,6 +551,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     const int ngs = p.ngroups - p.ng_dense;
     bid -= dense_blocks;
     split = bid % p.nsplit_s;
+    bid0 = dense_blocks + bid - split;
     bid /= p.nsplit_s;
     gi = p.ng_dense + bid % ngs;
     b = bid / ngs;
@@ -601,12 +603,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   // ---- per-wave streaming state (tiles wave, wave+4, ...; kTPC tiles per chunk)
   const uint16_t* kbase = p.kc + (size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D;
   const uint16_t* vbase = p.vc + (size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D;
+  // Stream mode: the waves take interleaved 16-row tiles of the split. Gather mode:
+  // each wave owns a contiguous block of the split's rows and visits the members of
+  // its own block (its own visit list at lbase, nl_w entries), so the list needs no
+  // workgroup-wide step.
   int nlist = nrows;
+  int lbase = 0, nl_w = 0;
   auto chunks_of = [&](int n) {
     const int ntiles = (n + kTile - 1) / kTile;
     const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
     return (my_tiles + kTPC - 1) / kTPC;
   };
+  auto tbase = [&](int c, int t) -> int {
+    return dense ? (wave + NW * (c * kTPC + t)) * kTile : lbase + (c * kTPC + t) * kTile;
+  };
+  int lim = nrows;                            // visit positions below lim are valid
 
   const bool head_lane = mr < G;
   const bool ret_lane = head_lane && ((ret >> mr) & 1u);
@@ -626,9 +637,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   auto load_chunk = [&](int c, uint4 (&kd)[kTPC][KCH], uint4 (&vd)[RSC][NV]) {
 #pragma unroll
     for (int t = 0; t < kTPC; ++t) {
-      const int tb = (wave + NW * (c * kTPC + t)) * kTile;
+      const int tb = tbase(c, t);
       const int pa = tb + mr;                 // A-operand row of this lane
-      const bool va = pa < nlist;
+      const bool va = pa < lim;
       const uint16_t* kp = kbase + (size_t)(va ? row_of(pa) : 0) * D + mk * 8;
 #pragma unroll
       for (int kk = 0; kk < KCH; ++kk)
@@ -636,7 +647,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int pv = tb + h2 * 8 + rg;      // P.V row of this lane
-        const bool vv = pv < nlist;
+        const bool vv = pv < lim;
         const uint16_t* vp = vbase + (size_t)(vv ? row_of(pv) : 0) * D + li * 8;
 #pragma unroll
         for (int c2 = 0; c2 < NV; ++c2)
@@ -657,7 +668,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       if (ret >> j & 1u)
         for (int i = tid; i < kHist1Bins / 4; i += NT) reinterpret_cast<uint4*>(sm.u.hist[j])[i] = make_uint4(0, 0, 0, 0);
   }
-  if (spm) {
+  if (spm && dense) {
     constexpr int IT = kMaxSplitRows / NT;
     uint32_t mrow[IT];
 #pragma unroll
@@ -676,42 +687,53 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       }
       mrow[it] = m;
     }
-    if (dense) {
 #pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int r = it * NT + tid;
-        if (r < nrows) sm.hmp[r] = (uint8_t)mrow[it];
-      }
-    } else {
-      int total = 0;
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        if (it * NT >= nrows) break;
-        const int r = it * NT + tid;
-        const bool f = r < nrows && mrow[it] != 0;
-        const uint64_t bal = __ballot(f);
-        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) sm.wcnt[wave] = __popcll(bal);
-        __syncthreads();
-        int woff = 0, tot = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          woff += (w < wave) ? sm.wcnt[w] : 0;
-          tot += sm.wcnt[w];
-        }
-        if (f) {
-          sm.list[total + woff + pre] = (uint16_t)r;
-          sm.hmp[total + woff + pre] = (uint8_t)mrow[it];
-        }
-        total += tot;
-        __syncthreads();
-      }
-      nlist = total;
+    for (int it = 0; it < IT; ++it) {
+      const int r = it * NT + tid;
+      if (r < nrows) sm.hmp[r] = (uint8_t)mrow[it];
     }
+  }
+  if (spm && !dense) {
+    // rows owned by this wave: [lbase, lbase + R) of the split, 64 per ballot
+    constexpr int CH = kMaxSplitRows / (64 * NW);
+    const int R = ((ts + 64 * NW - 1) / (64 * NW)) * 64;
+    lbase = wave * R;
+    const int rend = min(nrows, lbase + R);
+    uint32_t mrow[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int r = lbase + c * 64 + lane;
+      uint32_t m = 0;
+      if (r < rend) {
+        const int row = r0 + r;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          if (spm >> j & 1) {
+            const uint32_t w = p.bitmaps[(size_t)(hq0 + j) * p.W + (row >> 5)];
+            m |= ((w >> (row & 31)) & 1u) << j;
+          }
+        }
+      }
+      mrow[c] = m;
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (lbase + c * 64 >= rend) break;
+      const uint64_t bal = __ballot(mrow[c] != 0u);
+      const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+      if (mrow[c]) {
+        sm.list[lbase + cnt + pre] = (uint16_t)(lbase + c * 64 + lane);
+        sm.hmp[lbase + cnt + pre] = (uint8_t)mrow[c];
+      }
+      cnt += __popcll(bal);
+    }
+    nl_w = cnt;
+    lim = lbase + nl_w;
   }
   __syncthreads();
 
-  int nchunks = chunks_of(nlist);
+  int nchunks = dense ? chunks_of(nlist) : (nl_w + kChunkRows - 1) / kChunkRows;
   if (!dense) {
     if (nchunks > 0) load_chunk(0, kr[0], vr[0]);
     if (nchunks > 1) load_chunk(1, kr[1], vr[1]);
@@ -731,7 +753,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     float cm = -LD_INF;
 #pragma unroll
     for (int t = 0; t < kTPC; ++t) {
-      const int tb = (wave + NW * (c * kTPC + t)) * kTile;
+      const int tb = tbase(c, t);
       const int pos0 = tb + 4 * mk;
       uint32_t hm4 = 0;
       if (spm) hm4 = *reinterpret_cast<const uint32_t*>(&sm.hmp[pos0]);
@@ -739,9 +761,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       for (int r = 0; r < 4; ++r) {
         const int pos = pos0 + r;
         const uint32_t hm = spm ? ((hm4 >> (8 * r)) & 0xffu) : ret;
-        const bool mem = head_lane && pos < nlist && ((hm >> mr) & 1u);
+        const bool mem = head_lane && pos < lim && ((hm >> mr) & 1u);
         const float s = dacc[t][r] * scale;
-        if (ret_lane && pos < nlist) {
+        if (ret_lane && pos < lim) {
           if (lg) lg[pos] = s;                           // stream mode: pos is the row
           if (do_hist) atomicAdd(&sm.u.hist[mr][score_key(s) >> 21], 1u);
         }
@@ -818,7 +840,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     __syncthreads();
     for (int j = 0; j < G; ++j) {
       if (!(ret >> j & 1u)) continue;
-      uint32_t* hg = p.hist1 + (size_t)(hq0 + j) * kHist1Bins;
+      uint32_t* hg = hist1_mine(p.hist1, hq0 + j);
       for (int i = tid; i < kHist1Bins / 4; i += NT) {
         const uint4 c = reinterpret_cast<const uint4*>(sm.u.hist[j])[i];
         if (c.x) atomicAdd(hg + 4 * i + 0, c.x);
@@ -891,30 +913,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   }
 
   if (p.gb) {
-    uint32_t* gc = p.gb_cnt + (size_t)(b * p.Hkv + g) * 8;
-    uint32_t* rel = p.gb_rel + (size_t)(b * p.Hkv + g) * p.P * kRelStride;
-    group_barrier(gc, rel, split, nsplit_b, 1u, p.err, &sm.misc[1]);
-    merge_columns<D, G, NW>(p, act, hq0, split, nsplit_b);
-    if (do_hist && ret) group_select<D, G, NW>(sm, p, ret, hq0, split, nsplit_b, nb, r0, nrows, gc, rel);
-    // departure: the last workgroup of the group to leave clears the counters, the
-    // release words and the row histograms for the next call (every workgroup's own
-    // stores, release words included, are complete before it counts itself out)
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(gc + 4, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      sm.misc[0] = (old == (uint32_t)nsplit_b - 1u);
+    uint32_t* gc = p.gb_cnt + (size_t)(b * p.Hkv + g) * kGbCounters;
+    uint64_t* rel = p.gb_rel + (size_t)(b * p.Hkv + g) * p.P * kRelStride;
+    if (group_barrier(gc, rel, split, nsplit_b, bid0, 1u, p.err, &sm.misc[1], &sm.relw) && do_hist && ret) {
+      const int slot = hq0 + __builtin_ctz(ret), kk = select_k(p, slot, nb);
+      if (kk >= 1) publish_digit1<D, G, NW>(sm, p, slot, kk, rel, nsplit_b);
     }
-    __syncthreads();
-    if (sm.misc[0]) {
-      if (tid < 5) gc[tid] = 0u;
-      for (int s2 = tid; s2 < nsplit_b; s2 += NT) rel[(size_t)s2 * kRelStride] = 0u;
+    merge_columns<D, G, NW>(p, act, hq0, split, nsplit_b);
+    if (do_hist && ret) group_select<D, G, NW>(sm, p, ret, hq0, split, nsplit_b, bid0, nb, r0, nrows, gc, rel);
+    // departure: the last workgroup of the group to leave clears the counters, the
+    // release words, the row histograms and candidate counts for the next call (every
+    // workgroup's own stores, release words included, are complete before it counts
+    // itself out)
+    if (group_arrive(gc + 3 * (kRep + 1), nsplit_b, bid0, &sm.misc[1])) {
+      for (int i = tid; i < kGbCounters; i += NT) gc[i] = 0u;
+      for (int s2 = tid; s2 < nsplit_b; s2 += NT) rel[(size_t)s2 * kRelStride] = 0ull;
       if (do_hist) {
         for (int j = 0; j < G; ++j) {
           if (!(ret >> j & 1u)) continue;
           const size_t slot = (size_t)(hq0 + j);
-          for (int i = tid; i < kHist1Bins; i += NT) p.hist1[slot * kHist1Bins + i] = 0u;
-          if (tid == 0) p.row_cnt[slot] = 0u;
+          for (int i = tid; i < kRep * kHist1Bins; i += NT) p.hist1[slot * kRep * kHist1Bins + i] = 0u;
+          if (tid < kRep) p.row_cnt[slot * kRep + tid] = 0u;
         }
       }
     }
@@ -948,22 +967,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     for (int j = 0; j < G; ++j) {
       if (!(ret >> j & 1u)) continue;
       const int slot = hq0 + j;
-      uint32_t* hist = p.hist1 + (size_t)slot * kHist1Bins;
+      uint32_t* hist = p.hist1 + (size_t)slot * kRep * kHist1Bins;
       int kk = p.k_dense;
       if (p.s_indptr) kk = (int)(p.s_indptr[slot + 1] - p.s_indptr[slot]);
       kk = min(kk, nb);
+      uint32_t* hs = sm.u.sel_hist;
+      __syncthreads();    // the LDS union is free
+      if (kk >= 1) hist1_sum(hs, p.hist1, slot);
       if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
       __syncthreads();
-      if (kk >= 1) {
-        find_bin_from_top<kHist1Bins, NT>([&](int i) { return ld_dev(hist + i); }, (uint32_t)kk,
-                                          sm.wcnt, sm.res);
-      }
+      if (kk >= 1)
+        find_bin_from_top<kHist1Bins, NT>([&](int i) { return hs[i]; }, (uint32_t)kk, sm.wcnt, sm.res);
       __syncthreads();
       if (tid == 0) {
         p.sel_info[slot * 4 + 0] = sm.res[0];
         p.sel_info[slot * 4 + 1] = (uint32_t)kk - sm.res[1];   // still needed from bin b1
       }
-      for (int i = tid; i < kHist1Bins; i += NT) hist[i] = 0u;
+      for (int i = tid; i < kRep * kHist1Bins; i += NT) hist[i] = 0u;
       __syncthreads();
     }
   }

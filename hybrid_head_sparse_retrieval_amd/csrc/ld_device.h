@@ -240,37 +240,111 @@ __device__ __forceinline__ int block_sum(int v, int* tmp) {
   return s;
 }
 
-// Barrier number k (1, 2, ...) of the ns workgroups of a group, all resident at once.
-// Arrivals are counted in *cnt once each workgroup's earlier stores and atomics are
-// complete; the last to arrive writes k into every member's own release word (one
-// 128-byte line each, rel[s * kRelStride]), and the others poll only their own word,
-// with a read-modify-write (performed where the release lands, never a stale copy).
-// The wait is bounded; giving up sets *err.
-constexpr int kRelStride = 32;
-__device__ __forceinline__ void group_barrier(uint32_t* cnt, uint32_t* rel, int me, int ns, uint32_t k,
-                                              uint32_t* err, int* flag) {
+// The kRep replicas of a shared counter or histogram are indexed by workgroup id % kRep
+// (the XCD it runs on), so that the atomics of the workgroups of one XCD meet in one
+// replica and no address sees more than its share.
+__device__ __forceinline__ int rep_of_block() { return (int)(blockIdx.x % kRep); }
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 128-bit device-coherent (sc1) access through a buffer resource over `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+constexpr int kSc1 = 16;   // cache-policy bit of sc1 for buffer instructions
+
+// Digit-1 histogram rows: writers add to their replica; hist1_sum (every thread of the
+// workgroup) writes the sum of the kRep replicas of row `slot` to lds[kHist1Bins],
+// with 128-bit loads that are contiguous across the lanes. The caller synchronises
+// before reading lds.
+__device__ __forceinline__ uint32_t* hist1_mine(uint32_t* h1, int slot) {
+  return h1 + ((size_t)slot * kRep + rep_of_block()) * kHist1Bins;
+}
+__device__ __forceinline__ void hist1_sum(uint32_t* lds, const uint32_t* h1, int slot) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(h1 + (size_t)slot * kRep * kHist1Bins);
+  for (int i = threadIdx.x; i < kHist1Bins / 4; i += (int)blockDim.x) {
+    u32x4_t a = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < kRep; ++q) a += __builtin_amdgcn_raw_buffer_load_b128(r, (q * kHist1Bins + 4 * i) * 4, 0, kSc1);
+    lds[4 * i + 0] = a.x;
+    lds[4 * i + 1] = a.y;
+    lds[4 * i + 2] = a.z;
+    lds[4 * i + 3] = a.w;
+  }
+}
+
+// Arrival count of the ns workgroups with ids bid0 .. bid0+ns-1, all resident at once:
+// counted per replica (cnt[0..kRep-1]), then per group (cnt[kRep]) by the last arrival
+// of each replica, so that no counter sees more than ceil(ns / kRep) or kRep atomics.
+// Every thread calls it after its earlier stores and atomics; true in every thread of
+// the workgroup whose arrival completes the group.
+__device__ __forceinline__ bool group_arrive(uint32_t* cnt, int ns, int bid0, int* flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (old == (uint32_t)ns - 1u);
+  if (threadIdx.x == 0) {
+    const int r = rep_of_block();
+    const int first = ((r - bid0) % kRep + kRep) % kRep;     // first member with this residue
+    const int nr = first < ns ? (ns - first + kRep - 1) / kRep : 0;
+    const int nres = ns < kRep ? ns : kRep;
+    bool last = false;
+    const uint32_t old = __hip_atomic_fetch_add(cnt + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1u == (uint32_t)nr) {
+      const uint32_t o2 = __hip_atomic_fetch_add(cnt + kRep, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = (o2 + 1u == (uint32_t)nres);
+    }
+    *flag = last ? 1 : 0;
   }
   __syncthreads();
-  if (*flag) {
-    for (int s = tid; s < ns; s += (int)blockDim.x) st_dev(rel + (size_t)s * kRelStride, k);
-  } else if (tid == 0) {
-    uint32_t* mine = rel + (size_t)me * kRelStride;
+  return *flag != 0;
+}
+
+// Release words of a group: one 64-bit word per member, one 128-byte line each
+// (rel[s * kRelStride]). Bits 0..7 hold the stage the group has reached; the rest is
+// a payload that comes with that stage.
+constexpr int kRelStride = 16;
+__device__ __forceinline__ uint32_t rel_stage(uint64_t w) { return (uint32_t)(w & 0xffu); }
+
+// Every member's release word := w. Each word is written by thread s % blockDim.x, so
+// that later writes by the same workgroup land after earlier ones.
+__device__ __forceinline__ void group_publish(uint64_t* rel, int ns, uint64_t w) {
+  for (int s = threadIdx.x; s < ns; s += (int)blockDim.x) st_dev(rel + (size_t)s * kRelStride, w);
+}
+
+// Waits until this member's release word reaches stage k and returns it (in every
+// thread). Thread 0 polls with a read-modify-write, performed where the release lands
+// and never on a stale copy. The wait is bounded; giving up sets *err.
+__device__ __forceinline__ uint64_t group_wait(uint64_t* rel, int me, uint32_t k, uint32_t* err, uint64_t* slot) {
+  if (threadIdx.x == 0) {
+    uint64_t* mine = rel + (size_t)me * kRelStride;
     int spins = 0;
-    while (__hip_atomic_fetch_or(mine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < k) {
+    uint64_t w;
+    while (rel_stage(w = __hip_atomic_fetch_or(mine, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < k) {
       __builtin_amdgcn_s_sleep(2);
       if (++spins > kMaxSpins) {
         st_dev(err, 1u);
         break;
       }
     }
+    *slot = w;
   }
   __syncthreads();
+  const uint64_t w = *slot;
+  __syncthreads();
+  return w;
+}
+
+// Barrier at stage k of the ns workgroups of a group (ids bid0 .. bid0+ns-1), all
+// resident at once: the workgroup whose arrival completes the group publishes stage k
+// to every member; the others wait for it. Returns true in the workgroup that
+// completed the group.
+__device__ __forceinline__ bool group_barrier(uint32_t* cnt, uint64_t* rel, int me, int ns, int bid0, uint32_t k,
+                                              uint32_t* err, int* flag, uint64_t* slot) {
+  if (group_arrive(cnt, ns, bid0, flag)) {
+    group_publish(rel, ns, (uint64_t)k);
+    return true;
+  }
+  group_wait(rel, me, k, err, slot);
+  return false;
 }
 
 }  // namespace ld

@@ -23,6 +23,9 @@ constexpr int kMaxSplits = 1024;       // attention splits per sequence
 constexpr int kMergeRun = 64;          // splits merged by one first-level merge
 constexpr int kBitmapWordsPerBlock = 4096;           // bitmap-build LDS tile (16 KiB)
 constexpr int kMaxSpins = 1 << 22;     // bound of a barrier wait (polls with a short sleep)
+constexpr int kRep = 8;                // replicas of shared counters and histograms (workgroup id % kRep,
+                                       // which is the XCD the workgroup runs on)
+constexpr int kGbCounters = 48;        // per KV group: 4 barriers x (kRep + 1) counters, rounded up
 
 // ---------------------------------------------------------------- parameters
 
@@ -60,7 +63,7 @@ struct AttnParams {
   int P1;                 // first-level partial stride (ceil(P / kMergeRun))
   // fused first selection digit (only when do_topk)
   int do_topk;
-  uint32_t* hist1;        // [B*Hq][kHist1Bins], zero between calls
+  uint32_t* hist1;        // [B*Hq][kRep][kHist1Bins] (summed over replicas), zero between calls
   uint32_t* sel_info;     // [B*Hq][4]
   int k_dense;
   const int64_t* s_indptr;
@@ -68,11 +71,11 @@ struct AttnParams {
   // a group meet after storing their partials, merge O column by column and run the
   // selection of the group's retrieval heads over their own rows
   int gb;
-  uint32_t* gb_cnt;       // [B*Hkv][8] barrier counters, zero between calls
-  uint32_t* gb_rel;       // [B*Hkv][P] release words, one per 128 bytes, zero between calls
-  uint32_t* row_cnt;      // [B*Hq] candidates appended to each row's list, zero between calls
-  uint64_t* cand;         // [B*Hq][ncap] (index << 32 | key) of the candidates
-  int64_t ncap;
+  uint32_t* gb_cnt;       // [B*Hkv][kGbCounters] barrier counters, zero between calls
+  uint64_t* gb_rel;       // [B*Hkv][P] release words, one per 128 bytes, zero between calls
+  uint32_t* row_cnt;      // [B*Hq][kRep] candidates appended to each sub-list, zero between calls
+  uint64_t* cand;         // [B*Hq][kRep][sub_cap] (index << 32 | key) of the candidates
+  int64_t sub_cap;
   uint32_t* pub;          // [B*Hq][P][2] per split: keys above bin b1
   int32_t* s_out;         // S rows written for selecting heads
   uint32_t* err;          // set when a barrier gave up waiting (never expected)
@@ -92,7 +95,7 @@ struct SelParams {
   uint32_t* bitmaps; int W;
   int nret; uint8_t heads[64];
   // workspace (per row slot)
-  uint32_t* hist1;        // [slots][kHist1Bins], zero between calls
+  uint32_t* hist1;        // [slots][kRep][kHist1Bins] (summed over replicas), zero between calls
   uint32_t* hist2;        // [slots][kHist2Bins], zero between calls
   uint32_t* tickets;      // [slots] arrivals, zero between calls
   uint32_t* depart;       // [slots] departures from the row barrier, zero between calls

@@ -89,19 +89,22 @@ __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
     if (i < v.n) atomicAdd(&hist[score_key(v.sc[i]) >> 21], 1u);
   }
   __syncthreads();
-  uint32_t* gh = p.hist1 + (size_t)v.slot * kHist1Bins;
+  uint32_t* gh = hist1_mine(p.hist1, v.slot);
   for (int i = tid; i < kHist1Bins; i += kThreads)
     if (hist[i]) atomicAdd(gh + i, hist[i]);
   const uint32_t nch = (uint32_t)((v.n + kSelChunk - 1) / kSelChunk);
   if (!arrive_last(p.tickets + v.slot, nch, &flag)) return;
   if (tid == 0) { res[0] = 0; res[1] = 0; p.tickets[v.slot] = 0; }
+  __syncthreads();    // every thread is done with its own counts in hist
+  hist1_sum(hist, p.hist1, v.slot);
   __syncthreads();
-  find_bin_from_top<kHist1Bins, kThreads>([&](int i) { return ld_dev(gh + i); }, (uint32_t)v.k, tmp, res);
+  find_bin_from_top<kHist1Bins, kThreads>([&](int i) { return hist[i]; }, (uint32_t)v.k, tmp, res);
   if (tid == 0) {
     p.sel_info[v.slot * 4 + 0] = res[0];
     p.sel_info[v.slot * 4 + 1] = (uint32_t)v.k - res[1];
   }
-  for (int i = tid; i < kHist1Bins; i += kThreads) gh[i] = 0u;
+  uint32_t* all = p.hist1 + (size_t)v.slot * kRep * kHist1Bins;
+  for (int i = tid; i < kRep * kHist1Bins; i += kThreads) all[i] = 0u;
 }
 
 // ------------------------------------------------ spans of kSelSpan scores

@@ -124,3 +124,28 @@ def test_one_and_two_kernel_paths_agree_bitwise():
     assert np.array_equal(many[:5], few)
     for r in (0, 4, 299):
         assert np.array_equal(many[r], orc.select_topk_f32(x[r], 6000))
+
+
+def test_in_launch_selection_repeated_fresh_workspaces():
+    # selection inside the attention launch (one retrieval head per KV group): the S
+    # rows equal the oracle's selection on the launch's own fp32 logits, call after
+    # call with fresh workspaces (a regression test for a race between waves that
+    # share the bin-search result)
+    import workloads as wl
+    ld = _ld()
+    dev = "cuda"
+    B, Hq, Hkv, d, n, k = 2, 4, 4, 64, 3000, 900
+    q, kc, vc = wl.random_qkv(B, Hq, Hkv, d, B * n, 200)
+    qd, kd, vd = q.to(dev), kc.to(dev), vc.to(dev)
+    shape = ld.make_shape(qd, kd, None, n)
+    for trial in range(4):
+        ws = ld.Workspace(shape, k, dev)
+        S = torch.zeros((B, Hq, k), dtype=torch.int32, device=dev)
+        scores = torch.full((B, Hq, n), float("nan"), dtype=torch.float32, device=dev)
+        ld.hybrid_layer(qd, kd, vd, 0xF, k, None, s_out=S, scores_out=scores, workspace=ws, seq_len=n,
+                        flags=ld.flag_waves(1))
+        torch.cuda.synchronize()
+        sc, Sh = scores.cpu().numpy(), S.cpu().numpy()
+        for b in range(B):
+            for h in range(Hq):
+                assert np.array_equal(Sh[b, h], orc.select_topk_f32(sc[b, h], k)), (trial, b, h)
