@@ -279,15 +279,16 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   ap.ngroups = ng;
   ap.ng_dense = ng_dense;
   ap.waves = choose_waves(flags);
-  // The in-launch selection handles a group's retrieval heads one after another, so
-  // layers with several retrieval heads per group select in their own launch, where
-  // every row runs in parallel.
-  const bool want_gb = !(flags & LD_FLAG_SEPARATE_SELECT) && !(do_topk && ret_per_group > 1);
+  // The in-launch selection handles one retrieval head per group; layers with several
+  // retrieval heads in a group select in a launch of their own, where every row runs
+  // in parallel (the attention launch still merges behind group barriers).
+  const bool want_gb = !(flags & LD_FLAG_SEPARATE_SELECT);
+  const bool in_select = want_gb && do_topk && ret_per_group <= 1;
   const int64_t capacity = attention_capacity(D, G, ap.waves);
   // union density of a sparse group's rows if its heads' sets were independent
   const double kf = std::min(1.0, (double)k / (double)N);
   const double rho = 1.0 - std::pow(1.0 - kf, (double)std::max(1, sp_per_group));
-  const int sel_rows = (want_gb && do_topk) ? kSelRows : 0;
+  const int sel_rows = in_select ? kSelRows : 0;
   if (!choose_splits(N, B, ng_dense, ng - ng_dense, rho, sel_rows, capacity, flags, &ap.ts_d, &ap.ts_s))
     ap.ts_d = ap.ts_s = uniform_split(N, (int64_t)B * ng, capacity);
   ap.nsplit_d = (N + ap.ts_d - 1) / ap.ts_d;
@@ -313,6 +314,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   const bool gb = want_gb && nwg <= capacity;
   if (gb) {
     ap.gb = 1;
+    ap.gb_select = in_select ? 1 : 0;
     ap.gb_cnt = at<uint32_t>(ws, L.gb_cnt);
     ap.gb_rel = at<uint64_t>(ws, L.gb_rel);
     ap.row_cnt = at<uint32_t>(ws, L.row_cnt);
@@ -325,7 +327,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   if (launch_attention(ap, D, G, dim3((unsigned)nwg), st) != hipSuccess) return LD_ERR_HIP;
 
   // 4. argsTopK of the retrieval rows
-  if (do_topk && !gb) {
+  if (do_topk && !(gb && in_select)) {
     SelParams sp{};
     sp.mode = 1;
     sp.nrows = B * nret;

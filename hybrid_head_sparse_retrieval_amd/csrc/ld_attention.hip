@@ -287,6 +287,25 @@ __device__ __forceinline__ void rows_scan(const uint32_t (&f)[IT], int (&ex)[IT]
   __syncthreads();
 }
 
+// Digit 1 of row `slot` (bin b1 and k1, the keys still to take from it) from the sum
+// of its histogram replicas, stored in sel_info for the selection launch.
+template <int D, int G, int NW>
+__device__ __forceinline__ void digit1_info(AttnSmem<D, G, NW>& sm, const AttnParams& p, int slot, int kk) {
+  constexpr int NT = 64 * NW;
+  const int tid = threadIdx.x;
+  uint32_t* hs = sm.u.sel_hist;
+  __syncthreads();    // the LDS union is free
+  if (kk >= 1) hist1_sum(hs, p.hist1, slot);
+  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
+  __syncthreads();
+  if (kk >= 1) find_bin_from_top<kHist1Bins, NT>([&](int i) { return hs[i]; }, (uint32_t)kk, sm.wcnt, sm.res);
+  __syncthreads();
+  if (tid == 0) {
+    p.sel_info[slot * 4 + 0] = sm.res[0];
+    p.sel_info[slot * 4 + 1] = (uint32_t)kk - sm.res[1];
+  }
+}
+
 // k of the row: the row's selection length, at most the sequence length nb.
 __device__ __forceinline__ int select_k(const AttnParams& p, int slot, int nb) {
   int kk = p.k_dense;
@@ -915,26 +934,41 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   if (p.gb) {
     uint32_t* gc = p.gb_cnt + (size_t)(b * p.Hkv + g) * kGbCounters;
     uint64_t* rel = p.gb_rel + (size_t)(b * p.Hkv + g) * p.P * kRelStride;
-    if (group_barrier(gc, rel, split, nsplit_b, bid0, 1u, p.err, &sm.misc[1], &sm.relw) && do_hist && ret) {
-      const int slot = hq0 + __builtin_ctz(ret), kk = select_k(p, slot, nb);
-      if (kk >= 1) publish_digit1<D, G, NW>(sm, p, slot, kk, rel, nsplit_b);
+    const bool rl = group_barrier(gc, rel, split, nsplit_b, bid0, 1u, p.err, &sm.misc[1], &sm.relw);
+    if (do_hist && ret && p.gb_select) {
+      if (rl) {
+        // the only reader of the row's histogram: clears it once digit 1 is out
+        const int slot = hq0 + __builtin_ctz(ret), kk = select_k(p, slot, nb);
+        if (kk >= 1) publish_digit1<D, G, NW>(sm, p, slot, kk, rel, nsplit_b);
+        hist1_clear(p.hist1, slot);
+      }
+      merge_columns<D, G, NW>(p, act, hq0, split, nsplit_b);
+      group_select<D, G, NW>(sm, p, ret, hq0, split, nsplit_b, bid0, nb, r0, nrows, gc, rel);
+    } else {
+      // digit 1 of the i-th retrieval row of the group by split i (mod the splits)
+      if (do_hist && ret) {
+        int i = 0;
+        for (int j = 0; j < G; ++j) {
+          if (!(ret >> j & 1u)) continue;
+          if (i % nsplit_b == split) {
+            digit1_info<D, G, NW>(sm, p, hq0 + j, select_k(p, hq0 + j, nb));
+            hist1_clear(p.hist1, hq0 + j);
+          }
+          ++i;
+        }
+      }
+      merge_columns<D, G, NW>(p, act, hq0, split, nsplit_b);
     }
-    merge_columns<D, G, NW>(p, act, hq0, split, nsplit_b);
-    if (do_hist && ret) group_select<D, G, NW>(sm, p, ret, hq0, split, nsplit_b, bid0, nb, r0, nrows, gc, rel);
     // departure: the last workgroup of the group to leave clears the counters, the
-    // release words, the row histograms and candidate counts for the next call (every
-    // workgroup's own stores, release words included, are complete before it counts
-    // itself out)
+    // release words and candidate counts for the next call (every workgroup's own
+    // stores, release words included, are complete before it counts itself out; the
+    // row histograms were cleared by their readers)
     if (group_arrive(gc + 3 * (kRep + 1), nsplit_b, bid0, &sm.misc[1])) {
       for (int i = tid; i < kGbCounters; i += NT) gc[i] = 0u;
       for (int s2 = tid; s2 < nsplit_b; s2 += NT) rel[(size_t)s2 * kRelStride] = 0ull;
-      if (do_hist) {
-        for (int j = 0; j < G; ++j) {
-          if (!(ret >> j & 1u)) continue;
-          const size_t slot = (size_t)(hq0 + j);
-          for (int i = tid; i < kRep * kHist1Bins; i += NT) p.hist1[slot * kRep * kHist1Bins + i] = 0u;
-          if (tid < kRep) p.row_cnt[slot * kRep + tid] = 0u;
-        }
+      if (do_hist && tid < kRep) {
+        for (int j = 0; j < G; ++j)
+          if (ret >> j & 1u) p.row_cnt[(size_t)(hq0 + j) * kRep + tid] = 0u;
       }
     }
     return;
@@ -967,23 +1001,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     for (int j = 0; j < G; ++j) {
       if (!(ret >> j & 1u)) continue;
       const int slot = hq0 + j;
-      uint32_t* hist = p.hist1 + (size_t)slot * kRep * kHist1Bins;
-      int kk = p.k_dense;
-      if (p.s_indptr) kk = (int)(p.s_indptr[slot + 1] - p.s_indptr[slot]);
-      kk = min(kk, nb);
-      uint32_t* hs = sm.u.sel_hist;
-      __syncthreads();    // the LDS union is free
-      if (kk >= 1) hist1_sum(hs, p.hist1, slot);
-      if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
-      __syncthreads();
-      if (kk >= 1)
-        find_bin_from_top<kHist1Bins, NT>([&](int i) { return hs[i]; }, (uint32_t)kk, sm.wcnt, sm.res);
-      __syncthreads();
-      if (tid == 0) {
-        p.sel_info[slot * 4 + 0] = sm.res[0];
-        p.sel_info[slot * 4 + 1] = (uint32_t)kk - sm.res[1];   // still needed from bin b1
-      }
-      for (int i = tid; i < kRep * kHist1Bins; i += NT) hist[i] = 0u;
+      digit1_info<D, G, NW>(sm, p, slot, select_k(p, slot, nb));
+      hist1_clear(p.hist1, slot);
       __syncthreads();
     }
   }

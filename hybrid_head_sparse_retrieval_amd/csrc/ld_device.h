@@ -260,6 +260,11 @@ constexpr int kSc1 = 16;   // cache-policy bit of sc1 for buffer instructions
 __device__ __forceinline__ uint32_t* hist1_mine(uint32_t* h1, int slot) {
   return h1 + ((size_t)slot * kRep + rep_of_block()) * kHist1Bins;
 }
+// Clears the kRep replicas of row `slot` (every thread of the workgroup).
+__device__ __forceinline__ void hist1_clear(uint32_t* h1, int slot) {
+  uint4* r = reinterpret_cast<uint4*>(h1 + (size_t)slot * kRep * kHist1Bins);
+  for (int i = threadIdx.x; i < kRep * kHist1Bins / 4; i += (int)blockDim.x) r[i] = make_uint4(0u, 0u, 0u, 0u);
+}
 __device__ __forceinline__ void hist1_sum(uint32_t* lds, const uint32_t* h1, int slot) {
   const __amdgpu_buffer_rsrc_t r = rsrc(h1 + (size_t)slot * kRep * kHist1Bins);
   for (int i = threadIdx.x; i < kHist1Bins / 4; i += (int)blockDim.x) {

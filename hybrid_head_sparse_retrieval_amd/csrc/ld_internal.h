@@ -69,8 +69,11 @@ struct AttnParams {
   const int64_t* s_indptr;
   // group-barrier mode (every workgroup of the launch resident at once): the splits of
   // a group meet after storing their partials, merge O column by column and run the
-  // selection of the group's retrieval heads over their own rows
+  // selection of the group's retrieval head over their own rows (gb_select = 1), or
+  // only take digit 1 of each retrieval row for a selection launch that follows
+  // (gb_select = 0)
   int gb;
+  int gb_select;
   uint32_t* gb_cnt;       // [B*Hkv][kGbCounters] barrier counters, zero between calls
   uint64_t* gb_rel;       // [B*Hkv][P] release words, one per 128 bytes, zero between calls
   uint32_t* row_cnt;      // [B*Hq][kRep] candidates appended to each sub-list, zero between calls

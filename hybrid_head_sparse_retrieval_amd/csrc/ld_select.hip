@@ -103,8 +103,7 @@ __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
     p.sel_info[v.slot * 4 + 0] = res[0];
     p.sel_info[v.slot * 4 + 1] = (uint32_t)v.k - res[1];
   }
-  uint32_t* all = p.hist1 + (size_t)v.slot * kRep * kHist1Bins;
-  for (int i = tid; i < kRep * kHist1Bins; i += kThreads) all[i] = 0u;
+  hist1_clear(p.hist1, v.slot);
 }
 
 // ------------------------------------------------ spans of kSelSpan scores

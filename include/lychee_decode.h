@@ -79,8 +79,8 @@ enum {
   /* Launch-shape override: merge the split partials and run argsTopK in their own
      steps after the attention launch, even when the whole launch fits on the device
      at once (where, by default, the splits of each KV group meet at device-wide
-     barriers and do both themselves). S is the same either way; O may differ by
-     fp32 rounding. */
+     barriers, merge O themselves and, when the group has one retrieval head, select
+     its S too). S is the same either way; O may differ by fp32 rounding. */
   LD_FLAG_SEPARATE_SELECT = 1u << 2
 };
 /* Optional launch-shape overrides (0 = automatic): rows per attention split =
