@@ -117,7 +117,7 @@ LayerLayout layer_layout(const ld_shape* s) {
   // candidates of the workgroups of one replica: at most ceil(ns / kRep) splits of at
   // most kMaxSplitRows rows, i.e. below N / kRep + 2 * kMaxSplitRows
   L.sub_cap = ((int64_t)(N + kRep - 1) / kRep + 2 * kMaxSplitRows + 63) / 64 * 64;
-  L.gb_cand = take((size_t)L.slots * kRep * L.sub_cap * 8);
+  L.gb_cand = take((size_t)L.slots * kRep * L.sub_cap * 4);
   L.pub = take((size_t)L.slots * L.P * 8);
   L.total = o;
   return L;
@@ -318,7 +318,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     ap.gb_cnt = at<uint32_t>(ws, L.gb_cnt);
     ap.gb_rel = at<uint64_t>(ws, L.gb_rel);
     ap.row_cnt = at<uint32_t>(ws, L.row_cnt);
-    ap.cand = at<uint64_t>(ws, L.gb_cand);
+    ap.cand = at<uint32_t>(ws, L.gb_cand);
     ap.sub_cap = L.sub_cap;
     ap.pub = at<uint32_t>(ws, L.pub);
     ap.s_out = s_out;

@@ -38,6 +38,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTile = 16;        // rows per MFMA tile
 constexpr int kTPC = 1;          // tiles per chunk per wave
 constexpr int kChunkRows = kTile * kTPC;
+constexpr int kCandLds = 8192;     // selection candidates staged in LDS
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -80,7 +81,10 @@ struct AttnSmem {
   float pl[NW][kChunkRows][G];       // per wave: probabilities of the chunk's rows
   union {
     uint32_t hist[G][kHist1Bins];
-    uint32_t sel_hist[kHist2Bins + kHist3Bins];
+    struct {
+      uint32_t hist[kHist2Bins + kHist3Bins];
+      uint32_t cand[kCandLds];       // the row's candidates, when they fit
+    } sel;
     struct {
       float acc[NW][RP][G * D];      // [wave][row part][head*D + dim]
       float m[NW][G];
@@ -293,7 +297,7 @@ template <int D, int G, int NW>
 __device__ __forceinline__ void digit1_info(AttnSmem<D, G, NW>& sm, const AttnParams& p, int slot, int kk) {
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x;
-  uint32_t* hs = sm.u.sel_hist;
+  uint32_t* hs = sm.u.sel.hist;
   __syncthreads();    // the LDS union is free
   if (kk >= 1) hist1_sum(hs, p.hist1, slot);
   if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
@@ -323,7 +327,7 @@ __device__ __forceinline__ void publish_digit1(AttnSmem<D, G, NW>& sm, const Att
   constexpr int NT = 64 * NW;
   constexpr int PB1 = kHist1Bins / NT;          // digit-1 bins per thread
   const int tid = threadIdx.x;
-  uint32_t* hs = sm.u.sel_hist;                 // free until the selection below
+  uint32_t* hs = sm.u.sel.hist;                 // free until the selection below
   hist1_sum(hs, p.hist1, slot);
   if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
   __syncthreads();
@@ -400,12 +404,14 @@ __device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnP
       st_dev(p.pub + ((size_t)slot * p.P + split) * 2, (uint32_t)atot);
     }
     __syncthreads();
-    uint64_t* cl = p.cand + ((size_t)slot * kRep + rep) * p.sub_cap + sm.misc[2] + woff + before;
+    // a candidate shares digit 1 with the others: it is stored as its split and the
+    // low 21 bits of its key
+    uint32_t* cl = p.cand + ((size_t)slot * kRep + rep) * p.sub_cap + sm.misc[2] + woff + before;
     int q = 0;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       if (cm >> i & 1u) {
-        st_dev(cl + q, ((uint64_t)(uint32_t)(r0 + i * NT + tid) << 32) | key[i]);
+        st_dev(cl + q, ((uint32_t)split << 21) | (key[i] & 0x1fffffu));
         ++q;
       }
     }
@@ -415,41 +421,56 @@ __device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnP
   // ---- threshold from the whole candidate list, offset, write
   // The candidates sit in kRep sub-lists; the first PER entries of each are fetched
   // before the counts are known (entries past a count are ignored): register u holds
-  // entry (u / kRep) * NT + tid of sub-list u % kRep.
+  // entry (u / kRep) * NT + tid of sub-list u % kRep. All of them then go to LDS
+  // (sub-list after sub-list) when they fit, and the passes below read them there.
   static_assert(SPEC % kRep == 0, "speculative loads cover the sub-lists evenly");
   constexpr int PER = SPEC / kRep * NT;
-  const uint64_t* cl = p.cand + (size_t)slot * kRep * p.sub_cap;
-  uint64_t cv[SPEC];
+  const uint32_t* cl = p.cand + (size_t)slot * kRep * p.sub_cap;
+  uint32_t cv[SPEC];
 #pragma unroll
   for (int u = 0; u < SPEC; ++u) cv[u] = ld_dev(cl + (size_t)(u % kRep) * p.sub_cap + (u / kRep) * NT + tid);
   if (tid < kRep) sm.ncnt[tid] = (int)ld_dev(p.row_cnt + (size_t)slot * kRep + tid);
   int above = 0;                                  // keys above bin b1 in earlier splits
   for (int s2 = tid; s2 < split; s2 += NT) above += (int)ld_dev(p.pub + ((size_t)slot * p.P + s2) * 2);
-  uint32_t* h2 = sm.u.sel_hist;                   // [kHist2Bins]
+  uint32_t* h2 = sm.u.sel.hist;                   // [kHist2Bins]
   uint32_t* h3 = h2 + kHist2Bins;                 // [kHist3Bins]
+  uint32_t* cs = sm.u.sel.cand;                   // [kCandLds]
   for (int i = tid; i < kHist2Bins + kHist3Bins; i += NT) h2[i] = 0u;
   if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
   __syncthreads();
-  const int* ncnt = sm.ncnt;
-  // visit(f): every candidate once (the fetched ones from registers)
-  auto for_cands = [&](auto f) {
+  int total = 0;
 #pragma unroll
-    for (int u = 0; u < SPEC; ++u)
-      if ((u / kRep) * NT + tid < ncnt[u % kRep]) f((uint32_t)cv[u], (uint32_t)(cv[u] >> 32));
+  for (int r = 0; r < kRep; ++r) total += sm.ncnt[r];
+  const bool in_lds = total <= kCandLds;
+  if (in_lds) {
+    int off = 0;
+#pragma unroll
     for (int r = 0; r < kRep; ++r) {
-      const uint64_t* cr = cl + (size_t)r * p.sub_cap;
-      const int n = ncnt[r];
-      for (int q0 = PER; q0 < n; q0 += 8 * NT) {
-        uint64_t x[8];
+      const int n = sm.ncnt[r];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = (q0 + u * NT + tid < n) ? ld_dev(cr + q0 + u * NT + tid) : 0ull;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (q0 + u * NT + tid < n) f((uint32_t)x[u], (uint32_t)(x[u] >> 32));
+      for (int v = 0; v < SPEC / kRep; ++v) {
+        const int o = v * NT + tid;
+        if (o < n) cs[off + o] = cv[v * kRep + r];
+      }
+      for (int o = PER + tid; o < n; o += NT) cs[off + o] = ld_dev(cl + (size_t)r * p.sub_cap + o);
+      off += n;
+    }
+    __syncthreads();
+  }
+  // visit(f): every candidate once, as its split and its full key
+  auto for_cands = [&](auto f) {
+    auto g = [&](uint32_t e) { f((b1 << 21) | (e & 0x1fffffu), (int)(e >> 21)); };
+    if (in_lds) {
+#pragma unroll 4
+      for (int i = tid; i < total; i += NT) g(cs[i]);
+    } else {
+      for (int r = 0; r < kRep; ++r) {
+        const int n = sm.ncnt[r];
+        for (int o = tid; o < n; o += NT) g(ld_dev(cl + (size_t)r * p.sub_cap + o));
       }
     }
   };
-  for_cands([&](uint32_t kv, uint32_t) { atomicAdd(&h2[(kv >> 10) & 0x7ffu], 1u); });
+  for_cands([&](uint32_t kv, int) { atomicAdd(&h2[(kv >> 10) & 0x7ffu], 1u); });
   __syncthreads();
   find_bin_from_top<kHist2Bins, NT>([&](int i) { return h2[i]; }, k1, sm.wcnt, sm.res);
   const uint32_t b2 = sm.res[0];
@@ -458,16 +479,15 @@ __device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnP
   __syncthreads();    // every wave has read the result before it is cleared
   if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
   __syncthreads();
-  for_cands([&](uint32_t kv, uint32_t) { if ((kv >> 10) == pre) atomicAdd(&h3[kv & 0x3ffu], 1u); });
+  for_cands([&](uint32_t kv, int) { if ((kv >> 10) == pre) atomicAdd(&h3[kv & 0x3ffu], 1u); });
   __syncthreads();
   find_bin_from_top<kHist3Bins, NT>([&](int i) { return h3[i]; }, k2, sm.wcnt, sm.res);
   const uint32_t T = (pre << 10) | sm.res[0];
   const int et = (int)(k2 - sm.res[1]);           // keys equal to T that are kept
   // candidates of earlier splits above and equal to T; keys equal to T here
   int ga = 0, ge = 0, me = 0;
-  const uint32_t lo = (uint32_t)r0, hi = (uint32_t)(r0 + nrows);
-  for_cands([&](uint32_t kv, uint32_t ix) {
-    const int early = ix < lo ? 1 : 0, here = (ix >= lo && ix < hi) ? 1 : 0;
+  for_cands([&](uint32_t kv, int s2) {
+    const int early = s2 < split ? 1 : 0, here = s2 == split ? 1 : 0;
     const int gt1 = kv > T ? 1 : 0, eq1 = kv == T ? 1 : 0;
     ga += early & gt1;
     ge += early & eq1;

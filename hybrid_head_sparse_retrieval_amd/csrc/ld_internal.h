@@ -77,7 +77,7 @@ struct AttnParams {
   uint32_t* gb_cnt;       // [B*Hkv][kGbCounters] barrier counters, zero between calls
   uint64_t* gb_rel;       // [B*Hkv][P] release words, one per 128 bytes, zero between calls
   uint32_t* row_cnt;      // [B*Hq][kRep] candidates appended to each sub-list, zero between calls
-  uint64_t* cand;         // [B*Hq][kRep][sub_cap] (index << 32 | key) of the candidates
+  uint32_t* cand;         // [B*Hq][kRep][sub_cap] candidates: split << 21 | low 21 bits of the key
   int64_t sub_cap;
   uint32_t* pub;          // [B*Hq][P][2] per split: keys above bin b1
   int32_t* s_out;         // S rows written for selecting heads
