@@ -256,3 +256,34 @@ def test_ties_at_the_threshold_span_splits(entry, mask):
     O_ref, _, _ = orc.hybrid_layer_bf16(wl.bf16_bits(q), wl.bf16_bits(kc), wl.bf16_bits(vc),
                                         [0, n], [True] * Hq, [k], None)
     gh.check_outputs(out, O_ref, [(0, h) for h in heads])
+
+
+@pytest.mark.parametrize("stride", [1, 2])
+def test_more_candidates_than_lds_holds(stride):
+    # every stride-th key row of a KV head is the same vector: 20000 / stride equal top
+    # scores per retrieval head share one digit-1 bin, more candidates than the
+    # in-launch selection stages in LDS (8192), so it reads them from the sub-lists
+    ld = _ld()
+    dev = "cuda"
+    Hq, Hkv, d, n, k = 8, 2, 128, 20000, 6000
+    q, kc, vc = wl.random_qkv(1, Hq, Hkv, d, n, 25)
+    G = Hq // Hkv
+    for g in range(Hkv):
+        u = q[0, g * G:(g + 1) * G].float().mean(0)
+        u = 10.0 * u / u.norm()
+        kc[g, 0::stride] = u.to(kc.dtype)
+    qd, kd, vd = q.to(dev), kc.to(dev), vc.to(dev)
+    ws = ld.Workspace(ld.make_shape(qd, kd), k, dev)
+    S = torch.zeros((1, Hq, k), dtype=torch.int32, device=dev)
+    scores = torch.empty((1, Hq, n), dtype=torch.float32, device=dev)
+    out = torch.zeros_like(qd)
+    ld.retrieval_decode(qd, kd, vd, 0x11, k, s_out=S, scores_out=scores, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()
+    Sh = S.cpu().numpy()
+    for h in (0, 4):
+        assert np.array_equal(Sh[0, h], orc.select_topk_f32(sc[0, h], k))
+        assert np.array_equal(Sh[0, h], np.arange(0, stride * k, stride)), "ties must go to the lowest rows"
+    O_ref, _, _ = orc.hybrid_layer_bf16(wl.bf16_bits(q), wl.bf16_bits(kc), wl.bf16_bits(vc),
+                                        [0, n], [True] * Hq, [k], None)
+    gh.check_outputs(out, O_ref, [(0, 0), (0, 4)])
