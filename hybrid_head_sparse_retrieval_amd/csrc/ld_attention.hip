@@ -707,25 +707,38 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       if (ret >> j & 1u)
         for (int i = tid; i < kHist1Bins / 4; i += NT) reinterpret_cast<uint4*>(sm.u.hist[j])[i] = make_uint4(0, 0, 0, 0);
   }
+  // Membership words: every lane loads one bitmap word per sparse head (the words
+  // that cover the wave's rows), and each 64-row step takes its two words from lanes
+  // 2c and 2c+1 (r0 and the wave's first row are multiples of 32, so row bit = lane).
+  auto row_bits = [&](const uint32_t (&bw)[G], int c) -> uint32_t {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      if (spm >> j & 1) {
+        const uint32_t lo = __builtin_amdgcn_readlane(bw[j], 2 * c);
+        const uint32_t hi = __builtin_amdgcn_readlane(bw[j], 2 * c + 1);
+        m |= (((lane < 32 ? lo : hi) >> (lane & 31)) & 1u) << j;
+      }
+    }
+    return m;
+  };
   if (spm && dense) {
+    // thread rows it * NT + tid: the wave's rows of step it are words
+    // (r0 + it * NT + wave * 64) / 32 + {0, 1}
     constexpr int IT = kMaxSplitRows / NT;
+    static_assert(2 * IT <= 64, "one word per lane");
+    uint32_t bw[G];
+    {
+      const int it = lane >> 1;
+      const int word = ((r0 + it * NT + wave * 64) >> 5) + (lane & 1);
+      const bool ok = lane < 2 * IT && it * NT + wave * 64 < nrows && word < p.W;
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        bw[j] = ((spm >> j & 1) && ok) ? p.bitmaps[(size_t)(hq0 + j) * p.W + word] : 0u;
+    }
     uint32_t mrow[IT];
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int r = it * NT + tid;
-      uint32_t m = ret;
-      if (r < nrows) {
-        const int row = r0 + r;
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          if (spm >> j & 1) {
-            const uint32_t w = p.bitmaps[(size_t)(hq0 + j) * p.W + (row >> 5)];
-            m |= ((w >> (row & 31)) & 1u) << j;
-          }
-        }
-      }
-      mrow[it] = m;
-    }
+    for (int it = 0; it < IT; ++it) mrow[it] = ret | row_bits(bw, it);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int r = it * NT + tid;
@@ -735,25 +748,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   if (spm && !dense) {
     // rows owned by this wave: [lbase, lbase + R) of the split, 64 per ballot
     constexpr int CH = kMaxSplitRows / (64 * NW);
+    static_assert(2 * CH <= 64, "one word per lane");
     const int R = ((ts + 64 * NW - 1) / (64 * NW)) * 64;
     lbase = wave * R;
     const int rend = min(nrows, lbase + R);
+    uint32_t bw[G];
+    {
+      const int word = ((r0 + lbase) >> 5) + lane;
+      const bool ok = lane < 2 * CH && lbase + 32 * lane < rend && word < p.W;
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        bw[j] = ((spm >> j & 1) && ok) ? p.bitmaps[(size_t)(hq0 + j) * p.W + word] : 0u;
+    }
     uint32_t mrow[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int r = lbase + c * 64 + lane;
-      uint32_t m = 0;
-      if (r < rend) {
-        const int row = r0 + r;
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          if (spm >> j & 1) {
-            const uint32_t w = p.bitmaps[(size_t)(hq0 + j) * p.W + (row >> 5)];
-            m |= ((w >> (row & 31)) & 1u) << j;
-          }
-        }
-      }
-      mrow[c] = m;
+      mrow[c] = r < rend ? row_bits(bw, c) : 0u;
     }
     int cnt = 0;
 #pragma unroll
