@@ -113,7 +113,7 @@ LayerLayout layer_layout(const ld_shape* s) {
   L.bitmaps = take((size_t)L.slots * L.W * 4);
   L.gb_cnt = take((size_t)s->batch * s->num_kv_heads * kGbCounters * 4);
   L.gb_rel = take((size_t)s->batch * s->num_kv_heads * L.P * 128);
-  L.row_cnt = take((size_t)L.slots * kRep * 4);
+  L.row_cnt = take((size_t)2 * L.slots * kRep * 4);
   // candidates of the workgroups of one replica: at most ceil(ns / kRep) splits of at
   // most kMaxSplitRows rows, i.e. below N / kRep + 2 * kMaxSplitRows
   L.sub_cap = ((int64_t)(N + kRep - 1) / kRep + 2 * kMaxSplitRows + 63) / 64 * 64;

@@ -319,11 +319,11 @@ __device__ __forceinline__ int select_k(const AttnParams& p, int slot, int nb) {
 
 // Digit 1 of the row's threshold from its digit-1 histogram (the sum of the kRep
 // replicas), taken once per group by the workgroup that completed the group's first
-// barrier, and published to the group as stage 2 of the release words:
-// bits 8..18 = the bin b1, bits 32..63 = k1, the keys still to take from bin b1.
+// barrier, and published to the group as stage 2 of the release words, with the
+// payload b1 (the bin, bits 0..31) and k1 (the keys still to take from it, bits 32..63).
 template <int D, int G, int NW>
 __device__ __forceinline__ void publish_digit1(AttnSmem<D, G, NW>& sm, const AttnParams& p, int slot, int kk,
-                                               uint64_t* rel, int ns) {
+                                               uint64_t* rel, int ns, uint32_t epoch) {
   constexpr int NT = 64 * NW;
   constexpr int PB1 = kHist1Bins / NT;          // digit-1 bins per thread
   const int tid = threadIdx.x;
@@ -337,7 +337,7 @@ __device__ __forceinline__ void publish_digit1(AttnSmem<D, G, NW>& sm, const Att
   find_bin_regs<kHist1Bins, NT>(h, (uint32_t)kk, sm.wcnt, sm.res);
   const uint32_t b1 = sm.res[0], k1 = (uint32_t)kk - sm.res[1];
   __syncthreads();
-  group_publish(rel, ns, 2ull | ((uint64_t)b1 << 8) | ((uint64_t)k1 << 32));
+  group_publish(rel, ns, rel_word(epoch, 2u), (uint64_t)b1 | ((uint64_t)k1 << 32));
 }
 
 // argsTopK of the group's one retrieval head by the workgroups of the group, each over
@@ -351,7 +351,7 @@ __device__ __forceinline__ void publish_digit1(AttnSmem<D, G, NW>& sm, const Att
 template <int D, int G, int NW>
 __device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnParams& p, uint32_t ret,
                                              int hq0, int split, int ns, int bid0, int nb, int r0, int nrows,
-                                             uint32_t* gc, uint64_t* rel) {
+                                             uint32_t* gc, uint64_t* rel, uint32_t epoch) {
   constexpr int NT = 64 * NW;
   constexpr int IT = kMaxSplitRows / NT;        // rows per thread
   constexpr int SPEC = 32;                      // candidates fetched per thread before the counts
@@ -372,8 +372,9 @@ __device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnP
       key[i] = (r < nrows) ? score_key(ld_dev(lg + r)) : 0u;
     }
   }
-  const uint64_t w1 = group_wait(rel, split, 2u, p.err, &sm.relw);
-  const uint32_t b1 = (uint32_t)(w1 >> 8) & 0x7ffu, k1 = (uint32_t)(w1 >> 32);
+  const uint64_t w1 = group_wait_payload(rel, split, rel_word(epoch, 2u), p.err, &sm.relw);
+  const uint32_t b1 = (uint32_t)w1 & 0x7ffu, k1 = (uint32_t)(w1 >> 32);
+  uint32_t* rcnt = p.row_cnt + ((size_t)(epoch & 1u) * p.B * p.Hq + slot) * kRep;   // this call's counts
   {
     // ---- append the candidates to the row's list; publish the count above bin b1
     uint32_t cm = 0;
@@ -399,7 +400,7 @@ __device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnP
     }
     const int rep = rep_of_block();
     if (tid == 0) {
-      sm.misc[2] = tot ? (int)__hip_atomic_fetch_add(p.row_cnt + (size_t)slot * kRep + rep, (uint32_t)tot,
+      sm.misc[2] = tot ? (int)__hip_atomic_fetch_add(rcnt + rep, (uint32_t)tot,
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
       st_dev(p.pub + ((size_t)slot * p.P + split) * 2, (uint32_t)atot);
     }
@@ -416,7 +417,7 @@ __device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnP
       }
     }
   }
-  group_barrier(gc + (kRep + 1), rel, split, ns, bid0, 3u, p.err, &sm.misc[1], &sm.relw);
+  group_barrier(gc + (kRep + 1), rel, split, ns, bid0, rel_word(epoch, 3u), p.err, &sm.misc[1]);
 
   // ---- threshold from the whole candidate list, offset, write
   // The candidates sit in kRep sub-lists; the first PER entries of each are fetched
@@ -429,7 +430,7 @@ __device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnP
   uint32_t cv[SPEC];
 #pragma unroll
   for (int u = 0; u < SPEC; ++u) cv[u] = ld_dev(cl + (size_t)(u % kRep) * p.sub_cap + (u / kRep) * NT + tid);
-  if (tid < kRep) sm.ncnt[tid] = (int)ld_dev(p.row_cnt + (size_t)slot * kRep + tid);
+  if (tid < kRep) sm.ncnt[tid] = (int)ld_dev(rcnt + tid);
   int above = 0;                                  // keys above bin b1 in earlier splits
   for (int s2 = tid; s2 < split; s2 += NT) above += (int)ld_dev(p.pub + ((size_t)slot * p.P + s2) * 2);
   uint32_t* h2 = sm.u.sel.hist;                   // [kHist2Bins]
@@ -783,6 +784,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   }
   __syncthreads();
 
+  // the group's epoch for the in-launch barriers, fetched here (after the membership
+  // words, before the first gathered rows) so that it has long arrived when the
+  // workgroup reaches its first barrier
+  const uint32_t epoch0 = p.gb ? ld_dev(p.gb_cnt + (size_t)(b * p.Hkv + g) * kGbCounters + kEpochWord) : 0u;
   int nchunks = dense ? chunks_of(nlist) : (nl_w + kChunkRows - 1) / kChunkRows;
   if (!dense) {
     if (nchunks > 0) load_chunk(0, kr[0], vr[0]);
@@ -965,16 +970,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   if (p.gb) {
     uint32_t* gc = p.gb_cnt + (size_t)(b * p.Hkv + g) * kGbCounters;
     uint64_t* rel = p.gb_rel + (size_t)(b * p.Hkv + g) * p.P * kRelStride;
-    const bool rl = group_barrier(gc, rel, split, nsplit_b, bid0, 1u, p.err, &sm.misc[1], &sm.relw);
+    // This call's epoch of the group (read in the prologue, before arriving; the
+    // workgroup that completes the first barrier advances it for the next call).
+    const uint32_t epoch = epoch0 + 1u;
+    const bool rl = group_barrier(gc, rel, split, nsplit_b, bid0, rel_word(epoch, 1u), p.err, &sm.misc[1]);
+    if (rl) {
+      if (tid == 0) st_dev(gc + kEpochWord, epoch);
+      // the next call's candidate counts of the group's rows start at zero
+      if (tid < G * kRep)
+        p.row_cnt[((size_t)((epoch + 1u) & 1u) * p.B * p.Hq + hq0) * kRep + tid] = 0u;
+    }
     if (do_hist && ret && p.gb_select) {
       if (rl) {
         // the only reader of the row's histogram: clears it once digit 1 is out
         const int slot = hq0 + __builtin_ctz(ret), kk = select_k(p, slot, nb);
-        if (kk >= 1) publish_digit1<D, G, NW>(sm, p, slot, kk, rel, nsplit_b);
+        if (kk >= 1) publish_digit1<D, G, NW>(sm, p, slot, kk, rel, nsplit_b, epoch);
         hist1_clear(p.hist1, slot);
       }
       merge_columns<D, G, NW>(p, act, hq0, split, nsplit_b);
-      group_select<D, G, NW>(sm, p, ret, hq0, split, nsplit_b, bid0, nb, r0, nrows, gc, rel);
+      group_select<D, G, NW>(sm, p, ret, hq0, split, nsplit_b, bid0, nb, r0, nrows, gc, rel, epoch);
     } else {
       // digit 1 of the i-th retrieval row of the group by split i (mod the splits)
       if (do_hist && ret) {
@@ -990,18 +1004,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       }
       merge_columns<D, G, NW>(p, act, hq0, split, nsplit_b);
     }
-    // departure: the last workgroup of the group to leave clears the counters, the
-    // release words and candidate counts for the next call (every workgroup's own
-    // stores, release words included, are complete before it counts itself out; the
-    // row histograms were cleared by their readers)
-    if (group_arrive(gc + 3 * (kRep + 1), nsplit_b, bid0, &sm.misc[1])) {
-      for (int i = tid; i < kGbCounters; i += NT) gc[i] = 0u;
-      for (int s2 = tid; s2 < nsplit_b; s2 += NT) rel[(size_t)s2 * kRelStride] = 0ull;
-      if (do_hist && tid < kRep) {
-        for (int j = 0; j < G; ++j)
-          if (ret >> j & 1u) p.row_cnt[(size_t)(hq0 + j) * kRep + tid] = 0u;
-      }
-    }
+    // nothing to clear on the way out: barrier counters return to zero by themselves,
+    // release words carry the epoch, histograms are cleared by their readers and the
+    // next call's counts were cleared above
     return;
   }
 

@@ -281,8 +281,9 @@ __device__ __forceinline__ void hist1_sum(uint32_t* lds, const uint32_t* h1, int
 // Arrival count of the ns workgroups with ids bid0 .. bid0+ns-1, all resident at once:
 // counted per replica (cnt[0..kRep-1]), then per group (cnt[kRep]) by the last arrival
 // of each replica, so that no counter sees more than ceil(ns / kRep) or kRep atomics.
-// Every thread calls it after its earlier stores and atomics; true in every thread of
-// the workgroup whose arrival completes the group.
+// A counter is back at zero once its arrivals are complete. Every thread calls it after
+// its earlier stores, loads and atomics; true in every thread of the workgroup whose
+// arrival completes the group.
 __device__ __forceinline__ bool group_arrive(uint32_t* cnt, int ns, int bid0, int* flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -294,8 +295,12 @@ __device__ __forceinline__ bool group_arrive(uint32_t* cnt, int ns, int bid0, in
     bool last = false;
     const uint32_t old = __hip_atomic_fetch_add(cnt + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old + 1u == (uint32_t)nr) {
+      // the replica is complete: its counter is free again for the next call, and so
+      // is the group count once the group is complete
+      st_dev(cnt + r, 0u);
       const uint32_t o2 = __hip_atomic_fetch_add(cnt + kRep, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last = (o2 + 1u == (uint32_t)nres);
+      if (last) st_dev(cnt + kRep, 0u);
     }
     *flag = last ? 1 : 0;
   }
@@ -303,52 +308,66 @@ __device__ __forceinline__ bool group_arrive(uint32_t* cnt, int ns, int bid0, in
   return *flag != 0;
 }
 
-// Release words of a group: one 64-bit word per member, one 128-byte line each
-// (rel[s * kRelStride]). Bits 0..7 hold the stage the group has reached; the rest is
-// a payload that comes with that stage.
+// Release words of a group: one 64-bit word per member, on a 128-byte line of its own
+// (rel[s * kRelStride]), and a 64-bit payload word next to it. A word holds the call's
+// epoch in bits 32..63 and the stage the group has reached in bits 0..7, so words never
+// need clearing: every call of a group waits for values of its own epoch, one above
+// the previous call's.
 constexpr int kRelStride = 16;
-__device__ __forceinline__ uint32_t rel_stage(uint64_t w) { return (uint32_t)(w & 0xffu); }
+__device__ __forceinline__ uint64_t rel_word(uint32_t epoch, uint32_t stage) {
+  return ((uint64_t)epoch << 32) | stage;
+}
 
-// Every member's release word := w. Each word is written by thread s % blockDim.x, so
-// that later writes by the same workgroup land after earlier ones.
+// Every member's release word := w (each by thread s % blockDim.x). With a payload,
+// the payload words are written first and complete before any release word is.
 __device__ __forceinline__ void group_publish(uint64_t* rel, int ns, uint64_t w) {
   for (int s = threadIdx.x; s < ns; s += (int)blockDim.x) st_dev(rel + (size_t)s * kRelStride, w);
 }
+__device__ __forceinline__ void group_publish(uint64_t* rel, int ns, uint64_t w, uint64_t payload) {
+  for (int s = threadIdx.x; s < ns; s += (int)blockDim.x) st_dev(rel + (size_t)s * kRelStride + 1, payload);
+  __builtin_amdgcn_s_waitcnt(0);
+  group_publish(rel, ns, w);
+}
 
-// Waits until this member's release word reaches stage k and returns it (in every
-// thread). Thread 0 polls with a read-modify-write, performed where the release lands
-// and never on a stale copy. The wait is bounded; giving up sets *err.
-__device__ __forceinline__ uint64_t group_wait(uint64_t* rel, int me, uint32_t k, uint32_t* err, uint64_t* slot) {
+// Waits until this member's release word reaches w (epoch and stage). Thread 0 polls
+// with a read-modify-write, performed where the release lands and never on a stale
+// copy. The wait is bounded; giving up sets *err.
+__device__ __forceinline__ void group_wait(uint64_t* rel, int me, uint64_t w, uint32_t* err) {
   if (threadIdx.x == 0) {
     uint64_t* mine = rel + (size_t)me * kRelStride;
     int spins = 0;
-    uint64_t w;
-    while (rel_stage(w = __hip_atomic_fetch_or(mine, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < k) {
+    while (__hip_atomic_fetch_or(mine, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < w) {
       __builtin_amdgcn_s_sleep(2);
       if (++spins > kMaxSpins) {
         st_dev(err, 1u);
         break;
       }
     }
-    *slot = w;
   }
   __syncthreads();
-  const uint64_t w = *slot;
+}
+// The same, then the payload that came with the release word (in every thread).
+__device__ __forceinline__ uint64_t group_wait_payload(uint64_t* rel, int me, uint64_t w, uint32_t* err,
+                                                       uint64_t* slot) {
+  group_wait(rel, me, w, err);
+  if (threadIdx.x == 0) *slot = ld_dev(rel + (size_t)me * kRelStride + 1);
   __syncthreads();
-  return w;
+  const uint64_t v = *slot;
+  __syncthreads();
+  return v;
 }
 
-// Barrier at stage k of the ns workgroups of a group (ids bid0 .. bid0+ns-1), all
-// resident at once: the workgroup whose arrival completes the group publishes stage k
+// Barrier of the ns workgroups of a group (ids bid0 .. bid0+ns-1), all resident at
+// once, at release word w: the workgroup whose arrival completes the group publishes w
 // to every member; the others wait for it. Returns true in the workgroup that
 // completed the group.
-__device__ __forceinline__ bool group_barrier(uint32_t* cnt, uint64_t* rel, int me, int ns, int bid0, uint32_t k,
-                                              uint32_t* err, int* flag, uint64_t* slot) {
+__device__ __forceinline__ bool group_barrier(uint32_t* cnt, uint64_t* rel, int me, int ns, int bid0, uint64_t w,
+                                              uint32_t* err, int* flag) {
   if (group_arrive(cnt, ns, bid0, flag)) {
-    group_publish(rel, ns, (uint64_t)k);
+    group_publish(rel, ns, w);
     return true;
   }
-  group_wait(rel, me, k, err, slot);
+  group_wait(rel, me, w, err);
   return false;
 }
 

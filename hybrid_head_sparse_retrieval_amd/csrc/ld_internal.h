@@ -25,7 +25,8 @@ constexpr int kBitmapWordsPerBlock = 4096;           // bitmap-build LDS tile (1
 constexpr int kMaxSpins = 1 << 22;     // bound of a barrier wait (polls with a short sleep)
 constexpr int kRep = 8;                // replicas of shared counters and histograms (workgroup id % kRep,
                                        // which is the XCD the workgroup runs on)
-constexpr int kGbCounters = 48;        // per KV group: 4 barriers x (kRep + 1) counters, rounded up
+constexpr int kGbCounters = 48;        // per KV group: barrier counters (kRep + 1 each) and the epoch
+constexpr int kEpochWord = 40;         // the group's epoch: in-launch barrier calls so far
 
 // ---------------------------------------------------------------- parameters
 
@@ -74,9 +75,10 @@ struct AttnParams {
   // (gb_select = 0)
   int gb;
   int gb_select;
-  uint32_t* gb_cnt;       // [B*Hkv][kGbCounters] barrier counters, zero between calls
+  uint32_t* gb_cnt;       // [B*Hkv][kGbCounters] barrier counters (zero between calls) and epochs
   uint64_t* gb_rel;       // [B*Hkv][P] release words, one per 128 bytes, zero between calls
-  uint32_t* row_cnt;      // [B*Hq][kRep] candidates appended to each sub-list, zero between calls
+  uint32_t* row_cnt;      // [2][B*Hq][kRep] candidates appended to each sub-list; the half of the
+                          // epoch's parity is zero when a call starts
   uint32_t* cand;         // [B*Hq][kRep][sub_cap] candidates: split << 21 | low 21 bits of the key
   int64_t sub_cap;
   uint32_t* pub;          // [B*Hq][P][2] per split: keys above bin b1

@@ -38,9 +38,10 @@
  *  - Workspace: caller-owned device memory of at least ld_workspace_size() bytes
  *    (ld_topk_workspace_size() for ld_topk_select), 256-byte aligned. It must be
  *    zeroed once with ld_workspace_init() before its first use; every completed call
- *    leaves it zeroed again, except for the S bitmaps that LD_FLAG_S_CHAINED relies
- *    on. Calls that share a workspace must be ordered (same stream); concurrent
- *    calls need separate workspaces.
+ *    leaves it ready for the next one (its counters back at zero, per-KV-group call
+ *    epochs advanced, the S bitmaps that LD_FLAG_S_CHAINED relies on kept). Calls that
+ *    share a workspace must be ordered (same stream); concurrent calls need separate
+ *    workspaces.
  *  - Errors: arguments are validated on the host before any launch; a failing check
  *    returns an error code and launches nothing. Launch failures return LD_ERR_HIP.
  *    Faults inside kernels surface at the caller's next synchronisation. Per-sequence

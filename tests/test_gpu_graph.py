@@ -1,7 +1,7 @@
 """A decode step captured in a HIP graph and replayed gives the eager step's O and S
 bit for bit on every replay (the launches take only by-value arguments and leave the
-workspace counters zeroed after every call, so a replayed step starts from the same
-state as an eager one)."""
+workspace ready for the next call: counters at zero, per-group call epochs advanced,
+which changes no arithmetic)."""
 import numpy as np
 import pytest
 
