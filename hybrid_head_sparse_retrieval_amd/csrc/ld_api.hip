@@ -158,7 +158,7 @@ int choose_waves(uint32_t flags) { return (((flags >> 12) & 0x3u) == 2u) ? 8 : 4
 // when the group selects inside the launch, the selection's fixed latency counted as
 // `sel_rows` rows of streaming. The smallest ts_s that fits gives the most parallelism.
 // Returns false when no choice fits (the caller then takes one uniform size).
-constexpr int kSelRows = 384;
+constexpr int kSelRows = 512;
 bool choose_splits(int N, int B, int ng_dense, int ng_sparse, double rho, int sel_rows, int64_t capacity,
                    uint32_t flags, int* ts_d, int* ts_s) {
   const int v = (int)((flags >> 8) & 0xfu);
