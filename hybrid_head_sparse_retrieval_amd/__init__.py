@@ -25,10 +25,10 @@ FLAG_SKIP_TOPK = 1
 FLAG_S_CHAINED = 2
 FLAG_SEPARATE_SELECT = 4
 _STATUS = {1: "invalid argument", 2: "unsupported shape", 3: "workspace missing or too small",
-           4: "HIP launch failed"}
+           4: "HIP launch or copy failed", 5: "a bounded wait between workgroups gave up"}
 EXPORTED_SYMBOLS = ("ld_status_string", "ld_workspace_size", "ld_topk_workspace_size",
-                    "ld_workspace_init", "ld_retrieval_decode", "ld_sparse_decode",
-                    "ld_hybrid_layer", "ld_topk_select")
+                    "ld_workspace_init", "ld_workspace_check", "ld_retrieval_decode",
+                    "ld_sparse_decode", "ld_hybrid_layer", "ld_topk_select")
 
 
 def flag_split_rows(v: int) -> int:
@@ -100,6 +100,8 @@ def load_library():
     lib.ld_topk_workspace_size.argtypes = [i32, i32]
     lib.ld_workspace_init.restype = i32
     lib.ld_workspace_init.argtypes = [vp, sz, vp]
+    lib.ld_workspace_check.restype = i32
+    lib.ld_workspace_check.argtypes = [vp, sz, vp]
     lib.ld_retrieval_decode.restype = i32
     lib.ld_retrieval_decode.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.ld_sparse_decode.restype = i32
@@ -176,6 +178,12 @@ class _WS:
 
     def ptr(self) -> int:
         return self.buf.data_ptr()
+
+    def check(self) -> None:
+        """Raise LycheeDecodeError when a bounded wait inside a launch gave up since the
+        last check (then those calls' results are unreliable); clears the flag.
+        Synchronises the current stream."""
+        _check(load_library().ld_workspace_check(self.ptr(), self.nbytes, _stream()), "ld_workspace_check")
 
 
 class Workspace(_WS):

@@ -39,17 +39,22 @@ struct SelLayout {
   size_t total;
 };
 
+// Every workspace starts with a header line whose first word is the wait flag that
+// kernels set when a bounded wait gives up (read and cleared by ld_workspace_check).
+constexpr size_t kHeaderBytes = 256;
+constexpr size_t kErrOffset = 0;
+
 // Per-row selection scratch for `rows` rows of at most n scores.
 template <typename Take>
 SelArrays sel_arrays(int rows, int n, Take take) {
   SelArrays a{};
+  a.err = kErrOffset;
   a.C = (n + kSelSpan - 1) / kSelSpan;
   a.ncap = (int64_t)a.C * kSelSpan;
   a.tickets = take((size_t)rows * 4);
   a.hist1 = take((size_t)rows * kRep * kHist1Bins * 4);
   a.hist2 = take((size_t)rows * kHist2Bins * 4);
   a.depart = take((size_t)rows * 4);
-  a.err = take(4);
   a.sel_info = take((size_t)rows * 16);
   a.span_cnt = take((size_t)rows * a.C * 8);
   a.span_off = take((size_t)rows * a.C * 4);
@@ -102,6 +107,7 @@ LayerLayout layer_layout(const ld_shape* s) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   L.P1 = (L.P + kMergeRun - 1) / kMergeRun;
+  take(kHeaderBytes);
   L.attn_tickets = take((size_t)s->batch * s->num_kv_heads * 4);
   L.attn_tickets_l1 = take((size_t)s->batch * s->num_kv_heads * L.P1 * 4);
   L.sel = sel_arrays(L.slots, N, take);
@@ -127,6 +133,7 @@ SelLayout sel_layout(int rows, int n) {
   SelLayout L{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  take(kHeaderBytes);
   L.sel = sel_arrays(rows, n, take);
   L.total = o;
   return L;
@@ -352,7 +359,8 @@ const char* ld_status_string(ld_status status) {
     case LD_ERR_INVALID_ARGUMENT: return "invalid argument";
     case LD_ERR_UNSUPPORTED: return "unsupported shape";
     case LD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
-    case LD_ERR_HIP: return "HIP launch failed";
+    case LD_ERR_HIP: return "HIP launch or copy failed";
+    case LD_ERR_DEVICE_WAIT: return "a bounded wait between workgroups gave up";
   }
   return "unknown status";
 }
@@ -371,6 +379,18 @@ size_t ld_topk_workspace_size(int32_t rows, int32_t n) {
 ld_status ld_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!workspace || workspace_bytes == 0) return LD_ERR_WORKSPACE;
   return launch_zero(workspace, workspace_bytes, stream) == hipSuccess ? LD_OK : LD_ERR_HIP;
+}
+
+ld_status ld_workspace_check(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace || workspace_bytes < kHeaderBytes || ((uintptr_t)workspace & 15u)) return LD_ERR_WORKSPACE;
+  uint32_t flag = 0;
+  if (hipMemcpyAsync(&flag, static_cast<char*>(workspace) + kErrOffset, sizeof(flag), hipMemcpyDeviceToHost,
+                     stream) != hipSuccess)
+    return LD_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return LD_ERR_HIP;
+  if (flag == 0) return LD_OK;
+  if (launch_zero(workspace, 16, stream) != hipSuccess) return LD_ERR_HIP;
+  return LD_ERR_DEVICE_WAIT;
 }
 
 ld_status ld_retrieval_decode(const ld_shape* shape, uint64_t head_mask, const void* q,

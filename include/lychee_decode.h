@@ -65,7 +65,9 @@ enum {
   LD_ERR_INVALID_ARGUMENT = 1,  /* null pointer, bad size, misalignment, k out of range */
   LD_ERR_UNSUPPORTED = 2,       /* head_dim not 64/128, group size not 1/2/4/8, Hq > 64 */
   LD_ERR_WORKSPACE = 3,         /* workspace missing or smaller than required */
-  LD_ERR_HIP = 4                /* a HIP launch failed */
+  LD_ERR_HIP = 4,               /* a HIP launch or copy failed */
+  LD_ERR_DEVICE_WAIT = 5        /* a bounded wait between workgroups gave up (see
+                                   ld_workspace_check) */
 };
 
 /* Flags (bitwise OR). */
@@ -120,6 +122,15 @@ size_t ld_topk_workspace_size(int32_t rows, int32_t n);
 
 /* Zero a workspace (a fill kernel on `stream`; safe to capture in a HIP graph). */
 ld_status ld_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Report and clear the workspace's wait flag (either kind of workspace). Workgroups
+   that meet inside a launch wait for each other with a bounded spin; one that gives up
+   sets the flag and carries on, so the results of the calls since the last check are
+   then unreliable. Returns LD_ERR_DEVICE_WAIT when the flag was set, LD_OK when not,
+   LD_ERR_WORKSPACE for a missing or too small workspace, LD_ERR_HIP when the copy
+   fails. Copies 4 bytes to the host on `stream` and synchronises it; not for use
+   inside a HIP graph capture. */
+ld_status ld_workspace_check(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Retrieval heads (method step 3): for every head h with bit h of head_mask set,
    O[b][h] = softmax(q K^T * scale) V over all N_b rows of its KV head, and, when

@@ -76,6 +76,7 @@ def run_layers(B, Hq, Hkv, d, lens, masks, seed, k=None, csr=False, chain=True, 
                                           what=f"layer {l} (b, h) = {(b, h)}: ")
                 else:
                     assert np.array_equal(S_dict[(b, h)], S_in[(b, h)]), "sparse row changed"
+    ws.check()    # no bounded wait between workgroups gave up
     return results
 
 
@@ -287,3 +288,17 @@ def test_more_candidates_than_lds_holds(stride):
     O_ref, _, _ = orc.hybrid_layer_bf16(wl.bf16_bits(q), wl.bf16_bits(kc), wl.bf16_bits(vc),
                                         [0, n], [True] * Hq, [k], None)
     gh.check_outputs(out, O_ref, [(0, 0), (0, 4)])
+
+
+def test_wait_flag_is_reported_and_cleared():
+    # the flag that a kernel sets when a bounded wait gives up: set it from the host,
+    # then the check reports it once and clears it
+    ld = _ld()
+    q, kc, vc = wl.random_qkv(1, 4, 4, 64, 1024, 26)
+    shape = ld.make_shape(q.cuda(), kc.cuda())
+    for ws in (ld.Workspace(shape, 307, "cuda"), ld.TopkWorkspace(2, 1024, "cuda")):
+        ws.check()
+        ws.buf[0:4] = torch.tensor([1, 0, 0, 0], dtype=torch.uint8, device="cuda")
+        with pytest.raises(ld.LycheeDecodeError, match="bounded wait"):
+            ws.check()
+        ws.check()
