@@ -62,11 +62,12 @@ class Shape(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("seq_len", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
         ("total_tokens", ctypes.c_int64),
         ("kv_indptr", ctypes.c_void_p),
         ("softmax_scale", ctypes.c_float),
-        ("reserved1", ctypes.c_int32),
+        ("pages_per_seq", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p),
     ]
 
 
@@ -133,17 +134,20 @@ def _check(status: int, where: str):
         raise LycheeDecodeError(status, where)
 
 
-def make_shape(q, k_cache, kv_indptr=None, seq_len=None, scale=None) -> Shape:
-    """ld_shape from tensors: q [B][Hq][d], k_cache [Hkv][T][d]."""
+def make_shape(q, k_cache, kv_indptr=None, seq_len=None, scale=None, block_table=None,
+               page_size: int = 0) -> Shape:
+    """ld_shape from tensors: q [B][Hq][d], k_cache [Hkv][T][d]. Paged KV: block_table is
+    an int32 device tensor [B][pages_per_seq] of page ids into the T / page_size pages of
+    k_cache and v_cache; seq_len (and kv_indptr for ragged lengths) give the lengths."""
     B, Hq, d = q.shape
     Hkv, T, d2 = k_cache.shape
     if d2 != d:
         raise ValueError("head_dim of q and k_cache differ")
-    if kv_indptr is None:
+    if kv_indptr is None and block_table is None:
         n = seq_len if seq_len is not None else T // B
     else:
         if seq_len is None:
-            raise ValueError("seq_len (max sequence length) is required with kv_indptr")
+            raise ValueError("seq_len (max sequence length) is required with kv_indptr or block_table")
         n = seq_len
     s = Shape()
     s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim = B, Hq, Hkv, d
@@ -151,6 +155,14 @@ def make_shape(q, k_cache, kv_indptr=None, seq_len=None, scale=None) -> Shape:
     s.total_tokens = int(T)
     s.kv_indptr = _ptr(kv_indptr)
     s.softmax_scale = float(scale) if scale is not None else 0.0
+    if block_table is not None:
+        torch = _torch()
+        _req(block_table, torch.int32, "block_table")
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be [B][pages_per_seq]")
+        s.page_size = int(page_size)
+        s.pages_per_seq = int(block_table.shape[1])
+        s.block_table = block_table.data_ptr()
     return s
 
 
@@ -231,11 +243,11 @@ def _prep(q, k_cache, v_cache, out, kv_indptr):
 
 def retrieval_decode(q, k_cache, v_cache, head_mask: int, k: int, *, s_out=None, s_indptr=None,
                      scores_out=None, out=None, workspace: Optional[Workspace] = None,
-                     kv_indptr=None, seq_len=None, scale=None):
+                     kv_indptr=None, seq_len=None, scale=None, block_table=None, page_size: int = 0):
     """Retrieval heads: full attention (+ argsTopK into s_out when given). Returns out."""
     torch = _torch()
     out = _prep(q, k_cache, v_cache, out, kv_indptr)
-    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale)
+    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size)
     _opt(s_out, torch.int32, "s_out"); _opt(s_indptr, torch.int64, "s_indptr")
     _opt(scores_out, torch.float32, "scores_out")
     ws = workspace or Workspace(shape, k, q.device)
@@ -248,11 +260,11 @@ def retrieval_decode(q, k_cache, v_cache, head_mask: int, k: int, *, s_out=None,
 
 def sparse_decode(q, k_cache, v_cache, head_mask: int, k: int, s_in, *, s_indptr=None, out=None,
                   flags: int = 0, workspace: Optional[Workspace] = None, kv_indptr=None,
-                  seq_len=None, scale=None):
+                  seq_len=None, scale=None, block_table=None, page_size: int = 0):
     """Sparse heads: attention over K[S], V[S]. Returns out."""
     torch = _torch()
     out = _prep(q, k_cache, v_cache, out, kv_indptr)
-    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale)
+    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size)
     _req(s_in, torch.int32, "s_in"); _opt(s_indptr, torch.int64, "s_indptr")
     ws = workspace or Workspace(shape, k, q.device)
     _check(load_library().ld_sparse_decode(
@@ -265,12 +277,12 @@ def sparse_decode(q, k_cache, v_cache, head_mask: int, k: int, s_in, *, s_indptr
 def hybrid_layer(q, k_cache, v_cache, retrieval_mask: int, k: int, s, *, s_out=None,
                  s_indptr=None, scores_out=None, out=None, flags: int = 0,
                  workspace: Optional[Workspace] = None, kv_indptr=None, seq_len=None,
-                 scale=None):
+                 scale=None, block_table=None, page_size: int = 0):
     """One layer of the recurrence. `s` is S^{l} (None for an all-retrieval layer);
     S^{l+1} is written to `s_out` (default: in place into `s`). Returns out."""
     torch = _torch()
     out = _prep(q, k_cache, v_cache, out, kv_indptr)
-    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale)
+    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size)
     _opt(s, torch.int32, "s"); _opt(s_out, torch.int32, "s_out")
     _opt(s_indptr, torch.int64, "s_indptr"); _opt(scores_out, torch.float32, "scores_out")
     if s_out is None:

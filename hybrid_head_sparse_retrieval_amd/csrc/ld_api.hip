@@ -83,14 +83,24 @@ bool shape_ok(const ld_shape* s, ld_status* why) {
   *why = LD_ERR_INVALID_ARGUMENT;
   if (!s) return false;
   if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->seq_len < 1) return false;
-  if (s->reserved0 != 0 || s->reserved1 != 0 || s->total_tokens < 0) return false;
+  if (s->total_tokens < 0) return false;
+  if (s->page_size != 0) {
+    // paged KV: a power-of-two page of 16..4096 rows, a block table that covers seq_len,
+    // and a pool of whole pages
+    const int ps = s->page_size;
+    if (ps < 16 || ps > 4096 || (ps & (ps - 1)) != 0 || !s->block_table) return false;
+    if ((int64_t)s->pages_per_seq * ps < s->seq_len || s->total_tokens <= 0 || s->total_tokens % ps != 0)
+      return false;
+  } else if (s->pages_per_seq != 0 || s->block_table) {
+    return false;
+  }
   if (s->seq_len > kMaxSeq) { *why = LD_ERR_UNSUPPORTED; return false; }
   if (s->num_q_heads > 64) { *why = LD_ERR_UNSUPPORTED; return false; }
   if (s->num_q_heads % s->num_kv_heads != 0) return false;
   const int G = s->num_q_heads / s->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) { *why = LD_ERR_UNSUPPORTED; return false; }
   if (s->head_dim != 64 && s->head_dim != 128) { *why = LD_ERR_UNSUPPORTED; return false; }
-  if (!s->kv_indptr && s->total_tokens != 0 &&
+  if (!s->kv_indptr && s->page_size == 0 && s->total_tokens != 0 &&
       s->total_tokens < (int64_t)s->batch * s->seq_len)
     return false;
   if (!(std::isfinite(s->softmax_scale))) return false;
@@ -266,6 +276,12 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   ap.kv_indptr = shape->kv_indptr;
   ap.kv_head_stride = T * D;
   ap.total_tokens = T;
+  if (shape->page_size) {
+    ap.block_table = shape->block_table;
+    ap.page_shift = __builtin_ctz((unsigned)shape->page_size);
+    ap.pages_per_seq = shape->pages_per_seq;
+    ap.npages = T >> ap.page_shift;
+  }
   ap.B = B; ap.Hq = Hq; ap.Hkv = Hkv; ap.seq_len = N;
   ap.scale = scale;
   ap.active = active; ap.retrieval = retrieval;

@@ -78,6 +78,7 @@ struct AttnSmem {
   int scan[NW][kMaxSplitRows / (64 * NW) / 2 > 2 ? kMaxSplitRows / (64 * NW) / 2 : 2];   // wave totals of scans
   int cnt4[NW][2];
   int ncnt[kRep];                    // candidate counts of the sub-lists
+  int pages[kMaxSplitRows / 16 + 1]; // paged KV: page ids of the split's rows
   float pl[NW][kChunkRows][G];       // per wave: probabilities of the chunk's rows
   union {
     uint32_t hist[G][kHist1Bins];
@@ -599,6 +600,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   }
   const int g = p.groups[gi];
 
+  const bool paged = p.page_shift != 0;
   int64_t tok0;
   int nb;
   if (p.kv_indptr) {
@@ -608,10 +610,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     tok0 = (int64_t)b * p.seq_len;
     nb = p.seq_len;
   }
-  // never read past the cache or the per-row scratch, whatever kv_indptr holds
+  // never read past the cache or the per-row scratch, whatever kv_indptr holds (paged
+  // rows are clamped to the pool through their page ids)
   nb = min(nb, p.seq_len);
-  if (tok0 < 0 || tok0 >= p.total_tokens) nb = 0;
-  else if ((int64_t)nb > p.total_tokens - tok0) nb = (int)(p.total_tokens - tok0);
+  if (paged) {
+    tok0 = 0;
+  } else if (tok0 < 0 || tok0 >= p.total_tokens) {
+    nb = 0;
+  } else if ((int64_t)nb > p.total_tokens - tok0) {
+    nb = (int)(p.total_tokens - tok0);
+  }
   const int nsplit_b = (nb + ts - 1) / ts;
   if (nb <= 0 || split >= nsplit_b) return;
   const int r0 = split * ts;
@@ -643,6 +651,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   // ---- per-wave streaming state (tiles wave, wave+4, ...; kTPC tiles per chunk)
   const uint16_t* kbase = p.kc + (size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D;
   const uint16_t* vbase = p.vc + (size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D;
+  // Paged KV: the page ids of the split's rows go to LDS once; row r of the split (a
+  // row of the sequence: r0 + r) is then pool row page << shift | offset.
+  const int pshift = p.page_shift, pmask = (1 << pshift) - 1;
+  const int pg0 = r0 >> pshift;
+  if (paged) {
+    const int npg = ((r0 + nrows - 1) >> pshift) - pg0 + 1;
+    const int32_t* bt = p.block_table + (size_t)b * p.pages_per_seq + pg0;
+    for (int i = tid; i < npg; i += NT) {
+      const int64_t id = bt[i];
+      sm.pages[i] = (int)(id < 0 ? 0 : (id >= p.npages ? p.npages - 1 : id));
+    }
+    __syncthreads();
+  }
+  // element offset of row r of the split from kbase / vbase (paged: from the head's pool)
+  auto row_off = [&](int r) -> ptrdiff_t {
+    if (!paged) return (ptrdiff_t)r * D;
+    const int i = r0 + r;
+    return (((ptrdiff_t)sm.pages[(i >> pshift) - pg0] << pshift) + (i & pmask) - r0) * D;
+  };
   // Stream mode: the waves take interleaved 16-row tiles of the split. Gather mode:
   // each wave owns a contiguous block of the split's rows and visits the members of
   // its own block (its own visit list at lbase, nl_w entries), so the list needs no
@@ -680,7 +707,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       const int tb = tbase(c, t);
       const int pa = tb + mr;                 // A-operand row of this lane
       const bool va = pa < lim;
-      const uint16_t* kp = kbase + (size_t)(va ? row_of(pa) : 0) * D + mk * 8;
+      const uint16_t* kp = kbase + row_off(va ? row_of(pa) : 0) + mk * 8;
 #pragma unroll
       for (int kk = 0; kk < KCH; ++kk)
         kd[t][kk] = va ? *reinterpret_cast<const uint4*>(kp + kk * 32) : make_uint4(0, 0, 0, 0);
@@ -688,7 +715,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       for (int h2 = 0; h2 < 2; ++h2) {
         const int pv = tb + h2 * 8 + rg;      // P.V row of this lane
         const bool vv = pv < lim;
-        const uint16_t* vp = vbase + (size_t)(vv ? row_of(pv) : 0) * D + li * 8;
+        const uint16_t* vp = vbase + row_off(vv ? row_of(pv) : 0) + li * 8;
 #pragma unroll
         for (int c2 = 0; c2 < NV; ++c2)
           vd[t * 2 + h2][c2] = vv ? *reinterpret_cast<const uint4*>(vp + c2 * 64) : make_uint4(0, 0, 0, 0);

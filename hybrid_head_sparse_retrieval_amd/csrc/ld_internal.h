@@ -39,6 +39,11 @@ struct AttnParams {
   const int64_t* kv_indptr;
   int64_t kv_head_stride; // T*D elements
   int64_t total_tokens;   // T
+  // paged KV (page_shift > 0): logical row i of sequence b is pool row
+  // block_table[b * pages_per_seq + (i >> page_shift)] << page_shift | (i & page - 1)
+  const int32_t* block_table;
+  int page_shift, pages_per_seq;
+  int64_t npages;
   int B, Hq, Hkv, seq_len;
   float scale;            // logit scale
   uint64_t active;        // heads computed by this launch

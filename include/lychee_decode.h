@@ -100,13 +100,22 @@ typedef struct ld_shape {
   int32_t num_kv_heads;   /* Hkv, divides Hq; Hq/Hkv in {1,2,4,8} */
   int32_t head_dim;       /* d in {64, 128} */
   int32_t seq_len;        /* N (uniform) or max_b N_b (ragged), 1..2097152 */
-  int32_t reserved0;      /* must be 0 */
+  int32_t page_size;      /* 0: each sequence's K/V rows are contiguous (from kv_indptr[b],
+                             or b*seq_len). Else paged KV: a power of two in 16..4096;
+                             logical row i of sequence b is pool row
+                             block_table[b][i / page_size] * page_size + i % page_size. */
   int64_t total_tokens;   /* T: token rows per KV head in K/V (the head stride, in
                              rows); 0 selects batch*seq_len. Must cover every
-                             sequence's rows. */
-  const int64_t* kv_indptr; /* device [B+1] token offsets, or NULL for uniform N */
+                             sequence's rows. Paged: the pool's rows, a multiple of
+                             page_size (required). */
+  const int64_t* kv_indptr; /* device [B+1] token offsets, or NULL for uniform N. Paged:
+                               only the lengths N_b = kv_indptr[b+1] - kv_indptr[b]. */
   float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim) */
-  int32_t reserved1;      /* must be 0 */
+  int32_t pages_per_seq;  /* paged: row stride of block_table, >= ceil(seq_len/page_size);
+                             else 0 */
+  const int32_t* block_table; /* paged: device [B][pages_per_seq] page ids in
+                                 0 .. total_tokens/page_size - 1 (ids outside are
+                                 clamped); else NULL */
 } ld_shape;
 
 /* Human-readable text of a status code (static storage). */

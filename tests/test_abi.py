@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         assert lib.ld_status_string(code)
     assert lib.ld_status_string(99) == b"unknown status"
 
@@ -46,6 +46,9 @@ def _shape(**kw):
     return s
 
 
+FAKE = 0x10000  # a 16-byte-aligned non-null address; never dereferenced (validation fails first)
+
+
 def test_workspace_size(lib):
     s = _shape()
     n = lib.ld_workspace_size(ctypes.byref(s), 9830)
@@ -55,15 +58,22 @@ def test_workspace_size(lib):
     assert lib.ld_workspace_size(ctypes.byref(s2), 9830) > n
     # invalid shapes give 0
     for bad in (dict(head_dim=96), dict(num_kv_heads=5), dict(num_q_heads=65, num_kv_heads=65),
-                dict(seq_len=0), dict(batch=0), dict(reserved0=1), dict(num_kv_heads=2)):
+                dict(seq_len=0), dict(batch=0), dict(num_kv_heads=2),
+                # paged KV: page size not a power of two in 16..4096, no table, a table that
+                # does not cover seq_len, a pool of partial pages, table fields without paging
+                dict(page_size=48, pages_per_seq=1024, block_table=FAKE, total_tokens=1 << 20),
+                dict(page_size=8, pages_per_seq=4096, block_table=FAKE, total_tokens=1 << 20),
+                dict(page_size=64, pages_per_seq=512, block_table=None, total_tokens=1 << 20),
+                dict(page_size=64, pages_per_seq=511, block_table=FAKE, total_tokens=1 << 20),
+                dict(page_size=64, pages_per_seq=512, block_table=FAKE, total_tokens=(1 << 20) + 32),
+                dict(page_size=0, pages_per_seq=512), dict(page_size=0, block_table=FAKE)):
         assert lib.ld_workspace_size(ctypes.byref(_shape(**bad)), 10) == 0, bad
+    paged = _shape(page_size=64, pages_per_seq=512, block_table=FAKE, total_tokens=1 << 20)
+    assert lib.ld_workspace_size(ctypes.byref(paged), 10) > 0
     assert lib.ld_workspace_size(ctypes.byref(s), 0) == 0
     assert lib.ld_workspace_size(ctypes.byref(s), 32769) == 0
     assert lib.ld_topk_workspace_size(4, 1000) > 0
     assert lib.ld_topk_workspace_size(0, 1000) == 0
-
-
-FAKE = 0x10000  # a 16-byte-aligned non-null address; never dereferenced (validation fails first)
 
 
 def _hyb(lib, shape, **kw):
