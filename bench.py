@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_32k")
     ap.add_argument("--split", type=int, default=0, help="rows per split = 256<<(v-1), 0 = auto")
     ap.add_argument("--waves", type=int, default=0, help="attention waves per workgroup: 1 = 4, 2 = 8, 0 = auto")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="paged KV: rows per page (power of two, 16..4096); 0 = contiguous")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -108,6 +110,38 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     log(f"[bench] copied {COPY_BYTES} bytes 3 times")
+
+
+def paged_inputs(torch, w, inputs, page):
+    """The same layers with K/V moved into pools of `page`-row pages in a seeded random
+    order: (q, k_pool, v_pool, block_table, page) per layer."""
+    offs = w.kv_offsets()
+    B = w.batch
+    npp = [(int(offs[b + 1] - offs[b]) + page - 1) // page for b in range(B)]
+    pps, total = max(npp), sum(npp)
+    rng = np.random.default_rng(12345)
+    out, cache = [], {}
+    for l, (q, kc, vc) in enumerate(inputs):
+        key = (kc.data_ptr(), vc.data_ptr())
+        if key not in cache:
+            perm = rng.permutation(total)
+            Hkv, T, d = kc.shape
+            kp = torch.zeros((Hkv, total * page, d), dtype=kc.dtype, device=kc.device)
+            vp = torch.zeros_like(kp)
+            bt = np.zeros((B, pps), dtype=np.int32)
+            j = 0
+            for b in range(B):
+                for i in range(npp[b]):
+                    pid = int(perm[j]); j += 1
+                    bt[b, i] = pid
+                    r0 = int(offs[b]) + i * page
+                    r1 = min(int(offs[b + 1]), r0 + page)
+                    kp[:, pid * page: pid * page + r1 - r0] = kc[:, r0:r1]
+                    vp[:, pid * page: pid * page + r1 - r0] = vc[:, r0:r1]
+            cache[key] = (kp, vp, torch.as_tensor(bt, device=kc.device))
+        kp, vp, bt = cache[key]
+        out.append((q, kp, vp, bt, page))
+    return out
 
 
 def copy_bandwidth(torch, reps=5):
@@ -223,6 +257,11 @@ def main():
     log(f"[bench] inputs generated in {time.time() - t0:.1f}s "
         f"({sum(t.numel() * 2 for t in (inputs[0][1], inputs[0][2])) * w.kv_layers() / 1e9:.2f} GB KV)")
 
+    logical = inputs
+    if args.page_size:
+        inputs = paged_inputs(torch, w, inputs, args.page_size)
+        log(f"[bench] paged KV: {args.page_size}-row pages in a shuffled pool")
+
     split_flag = ld.flag_split_rows(args.split) | ld.flag_waves(args.waves)
     step = DecodeStep(w.batch, w.num_q_heads, w.num_kv_heads, d, w.seq_lens, w.k_per_seq,
                       w.retrieval_masks, csr=w.ragged_csr, device=dev, split_flag=split_flag)
@@ -231,8 +270,11 @@ def main():
     attn_bytes, total_bytes = [], []
     for l in range(L):
         S_in = step.s_rows() if l > 0 else None
-        q, kc, vc = inputs[l]
-        step.layer(l, q, kc, vc)
+        q, kc, vc = inputs[l][:3]
+        if len(inputs[l]) > 3:
+            step.layer(l, q, kc, vc, block_table=inputs[l][3], page_size=inputs[l][4])
+        else:
+            step.layer(l, q, kc, vc)
         a, t = layer_bytes(w, l, S_in, d) if l > 0 else layer_bytes(w, l, None, d)
         attn_bytes.append(a)
         total_bytes.append(t)
@@ -369,7 +411,8 @@ def main():
                    "seq_len": w.seq_lens[0] if w.batch == 1 else list(w.seq_lens),
                    "k": w.k_per_seq[0] if w.batch == 1 else list(w.k_per_seq),
                    "retrieval_heads_after_layer0": sum(bin(m).count("1") for m in w.retrieval_masks[1:]),
-                   "split_rows": "auto" if args.split == 0 else 256 << (args.split - 1)},
+                   "split_rows": "auto" if args.split == 0 else 256 << (args.split - 1),
+                   "kv_layout": f"paged {args.page_size}-row pages" if args.page_size else "contiguous"},
         "roofline": roof,
         # sparse layers that read the first layer's cache again may be served from the
         # 256 MB last-level cache, so their GB/s can exceed the HBM figure
@@ -380,7 +423,7 @@ def main():
 
     # ---- CPU oracle baseline on a bounded sample of the same workload
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, inputs, total_bytes, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, logical, total_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -62,22 +62,29 @@ class DecodeStep:
             self.workspace = Workspace(shape, self.k_arg, self.device)
         return self.workspace
 
-    def layer(self, l: int, q, kc, vc, extra_flags: int = 0, scores_out=None):
-        """Launch layer l (asynchronous)."""
+    def layer(self, l: int, q, kc, vc, extra_flags: int = 0, scores_out=None, block_table=None,
+              page_size: int = 0):
+        """Launch layer l (asynchronous). Paged KV: kc/vc are page pools and block_table
+        maps each sequence's pages."""
         flags = (FLAG_S_CHAINED if l > 0 else 0) | self.split_flag | extra_flags
         return hybrid_layer(q, kc, vc, self.masks[l], self.k_arg, self.S if l > 0 else None,
                             s_out=self.S, s_indptr=self.s_indptr, scores_out=scores_out,
                             out=self.outs[l], flags=flags, workspace=self._ws(q, kc),
-                            kv_indptr=self.kv_indptr, seq_len=self.N)
+                            kv_indptr=self.kv_indptr, seq_len=self.N, block_table=block_table,
+                            page_size=page_size)
 
     def run(self, layers: List, events: Optional[list] = None):
-        """One decode step. layers[l] = (q, k, v) device tensors. If `events` is a list of
-        L+1 torch.cuda.Event, they are recorded between layers."""
+        """One decode step. layers[l] = (q, k, v) device tensors, or (q, k_pool, v_pool,
+        block_table, page_size) for paged KV. If `events` is a list of L+1
+        torch.cuda.Event, they are recorded between layers."""
         for l in range(self.L):
             if events is not None:
                 events[l].record()
-            q, kc, vc = layers[l]
-            self.layer(l, q, kc, vc)
+            q, kc, vc = layers[l][:3]
+            if len(layers[l]) > 3:
+                self.layer(l, q, kc, vc, block_table=layers[l][3], page_size=layers[l][4])
+            else:
+                self.layer(l, q, kc, vc)
         if events is not None:
             events[self.L].record()
         return self.outs
