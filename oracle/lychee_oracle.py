@@ -42,6 +42,8 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64",
+    "fp8_e4m3_to_f64",
+    "hybrid_layer_fp8",
     "softmax_attention",
     "select_topk",
     "select_topk_f32",
@@ -66,6 +68,25 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+def fp8_e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Exact value of 8-bit E4M3 floating-point codes (uint8), the OCP 8-bit floating
+    point format used for quantised KV caches: 1 sign bit, 4 exponent bits with bias 7,
+    3 mantissa bits. Exponent field 0 encodes subnormals m/8 * 2^-6; the codes with all
+    exponent and mantissa bits set (0x7F, 0xFF) are NaN; there are no infinities, so
+    the largest magnitude is 1.75 * 2^8 = 448.
+
+    The pages name quantised KV only as a combinable extension; the format is the
+    reading taken here.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & (c & 0x7 == 7), np.nan, mag)
+    return sign * mag
 
 
 def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray,
@@ -184,6 +205,15 @@ def hybrid_layer_bf16(q_bits, k_bits, v_bits, kv_offsets, retrieval, k_per_seq, 
     return hybrid_layer_f64(bf16_bits_to_f64(q_bits), bf16_bits_to_f64(k_bits),
                             bf16_bits_to_f64(v_bits), kv_offsets, retrieval, k_per_seq,
                             S_in, scale=scale, active=active)
+
+
+def hybrid_layer_fp8(q_bits, k_codes, v_codes, k_scale, v_scale, kv_offsets, retrieval, k_per_seq,
+                     S_in, scale=None, active=None):
+    """hybrid_layer_f64 with a quantised KV cache: K = k_scale * E4M3(k_codes) and
+    V = v_scale * E4M3(v_codes) (one scale per tensor), Q from bf16 bits."""
+    return hybrid_layer_f64(bf16_bits_to_f64(q_bits), float(k_scale) * fp8_e4m3_to_f64(k_codes),
+                            float(v_scale) * fp8_e4m3_to_f64(v_codes), kv_offsets, retrieval,
+                            k_per_seq, S_in, scale=scale, active=active)
 
 
 def decode_step_f64(layers: List[Tuple[np.ndarray, np.ndarray, np.ndarray]],

@@ -298,3 +298,50 @@ def test_hybrid_layer_bf16_matches_widened_f64():
     O2, S2, _ = orc.hybrid_layer_f64(orc.bf16_bits_to_f64(qb), orc.bf16_bits_to_f64(kb),
                                      orc.bf16_bits_to_f64(vb), [0, n], [True] * Hq, [9], None)
     assert np.array_equal(O1, O2)
+
+
+# ---- quantised KV: E4M3 decode and the fp8 layer
+
+def test_fp8_e4m3_known_codes():
+    # values fixed by the format's definition (bias 7, 3 mantissa bits, subnormals at
+    # exponent 0, S.1111.111 NaN, no infinities)
+    known = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5,
+             0x38: 1.0, 0x39: 1.125, 0x3C: 1.5, 0x40: 2.0, 0x78: 256.0, 0x7E: 448.0,
+             0xB8: -1.0, 0xFE: -448.0, 0xC0: -2.0}
+    for c, v in known.items():
+        assert orc.fp8_e4m3_to_f64(np.uint8(c)) == v, hex(c)
+    assert np.signbit(orc.fp8_e4m3_to_f64(np.uint8(0x80)))
+    assert np.isnan(orc.fp8_e4m3_to_f64(np.uint8(0x7F))) and np.isnan(orc.fp8_e4m3_to_f64(np.uint8(0xFF)))
+
+
+def test_fp8_e4m3_order_symmetry_and_count():
+    codes = np.arange(256, dtype=np.uint8)
+    v = orc.fp8_e4m3_to_f64(codes)
+    pos = v[:0x7F]                                # 0x00 .. 0x7E
+    assert np.all(np.diff(pos) > 0), "positive codes increase strictly"
+    assert np.array_equal(v[0x80:0xFF], -pos)     # sign-magnitude
+    finite = v[np.isfinite(v)]
+    assert finite.size == 254 and np.unique(finite).size == 253   # +0 and -0 are equal
+    # every value is a multiple of the smallest subnormal and fits bf16 exactly
+    assert np.all(np.mod(finite, 2.0 ** -9) == 0)
+    f32 = finite.astype(np.float32)
+    assert np.array_equal((f32.view(np.uint32) & np.uint32(0xFFFF)), np.zeros(254, np.uint32))
+
+
+def test_fp8_layer_scales_are_exact_factors():
+    # doubling k_scale doubles every logit exactly; doubling v_scale doubles every output
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv, d, n = 1, 4, 2, 64, 300
+    qb = (rng.standard_normal((B, Hq, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    kc = rng.integers(0, 256, size=(Hkv, n, d)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(Hkv, n, d)).astype(np.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x38                # no NaN codes
+    vc[(vc & 0x7F) == 0x7F] = 0x38
+    args = ([0, n], [True] * Hq, [90], None)
+    O1, S1, sc1 = orc.hybrid_layer_fp8(qb, kc, vc, 1.0, 1.0, *args)
+    O2, S2, sc2 = orc.hybrid_layer_fp8(qb, kc, vc, 1.0, 2.0, *args)
+    _, S3, sc3 = orc.hybrid_layer_fp8(qb, kc, vc, 2.0, 1.0, *args)
+    assert np.array_equal(O2, 2.0 * O1)
+    for key in sc1:
+        assert np.array_equal(sc3[key], 2.0 * sc1[key])
+        assert np.array_equal(S1[key], S3[key]) and np.array_equal(S1[key], S2[key])
