@@ -68,6 +68,10 @@ class Shape(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("pages_per_seq", ctypes.c_int32),
         ("block_table", ctypes.c_void_p),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -135,10 +139,12 @@ def _check(status: int, where: str):
 
 
 def make_shape(q, k_cache, kv_indptr=None, seq_len=None, scale=None, block_table=None,
-               page_size: int = 0) -> Shape:
+               page_size: int = 0, k_scale=None, v_scale=None) -> Shape:
     """ld_shape from tensors: q [B][Hq][d], k_cache [Hkv][T][d]. Paged KV: block_table is
     an int32 device tensor [B][pages_per_seq] of page ids into the T / page_size pages of
-    k_cache and v_cache; seq_len (and kv_indptr for ragged lengths) give the lengths."""
+    k_cache and v_cache; seq_len (and kv_indptr for ragged lengths) give the lengths.
+    Quantised KV: k_cache / v_cache of dtype uint8 (or float8_e4m3fn) hold E4M3 codes,
+    and k_scale / v_scale (default 1) their per-tensor dequantisation scales."""
     B, Hq, d = q.shape
     Hkv, T, d2 = k_cache.shape
     if d2 != d:
@@ -155,6 +161,10 @@ def make_shape(q, k_cache, kv_indptr=None, seq_len=None, scale=None, block_table
     s.total_tokens = int(T)
     s.kv_indptr = _ptr(kv_indptr)
     s.softmax_scale = float(scale) if scale is not None else 0.0
+    if _is_fp8(k_cache):
+        s.kv_dtype = 1
+        s.k_scale = float(k_scale) if k_scale is not None else 1.0
+        s.v_scale = float(v_scale) if v_scale is not None else 1.0
     if block_table is not None:
         torch = _torch()
         _req(block_table, torch.int32, "block_table")
@@ -227,11 +237,17 @@ def _opt(t, dtype, name):
     return None if t is None else _req(t, dtype, name)
 
 
+def _is_fp8(t) -> bool:
+    torch = _torch()
+    return t.dtype == torch.uint8 or t.dtype == getattr(torch, "float8_e4m3fn", None)
+
+
 def _prep(q, k_cache, v_cache, out, kv_indptr):
     torch = _torch()
     _req(q, torch.bfloat16, "q")
-    _req(k_cache, torch.bfloat16, "k_cache")
-    _req(v_cache, torch.bfloat16, "v_cache")
+    kv_dtype = k_cache.dtype if _is_fp8(k_cache) else torch.bfloat16
+    _req(k_cache, kv_dtype, "k_cache")
+    _req(v_cache, kv_dtype, "v_cache")
     if k_cache.shape != v_cache.shape:
         raise ValueError("k_cache and v_cache shapes differ")
     if out is None:
@@ -243,11 +259,12 @@ def _prep(q, k_cache, v_cache, out, kv_indptr):
 
 def retrieval_decode(q, k_cache, v_cache, head_mask: int, k: int, *, s_out=None, s_indptr=None,
                      scores_out=None, out=None, workspace: Optional[Workspace] = None,
-                     kv_indptr=None, seq_len=None, scale=None, block_table=None, page_size: int = 0):
+                     kv_indptr=None, seq_len=None, scale=None, block_table=None, page_size: int = 0,
+                     k_scale=None, v_scale=None):
     """Retrieval heads: full attention (+ argsTopK into s_out when given). Returns out."""
     torch = _torch()
     out = _prep(q, k_cache, v_cache, out, kv_indptr)
-    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size)
+    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size, k_scale, v_scale)
     _opt(s_out, torch.int32, "s_out"); _opt(s_indptr, torch.int64, "s_indptr")
     _opt(scores_out, torch.float32, "scores_out")
     ws = workspace or Workspace(shape, k, q.device)
@@ -260,11 +277,12 @@ def retrieval_decode(q, k_cache, v_cache, head_mask: int, k: int, *, s_out=None,
 
 def sparse_decode(q, k_cache, v_cache, head_mask: int, k: int, s_in, *, s_indptr=None, out=None,
                   flags: int = 0, workspace: Optional[Workspace] = None, kv_indptr=None,
-                  seq_len=None, scale=None, block_table=None, page_size: int = 0):
+                  seq_len=None, scale=None, block_table=None, page_size: int = 0, k_scale=None,
+                  v_scale=None):
     """Sparse heads: attention over K[S], V[S]. Returns out."""
     torch = _torch()
     out = _prep(q, k_cache, v_cache, out, kv_indptr)
-    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size)
+    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size, k_scale, v_scale)
     _req(s_in, torch.int32, "s_in"); _opt(s_indptr, torch.int64, "s_indptr")
     ws = workspace or Workspace(shape, k, q.device)
     _check(load_library().ld_sparse_decode(
@@ -277,12 +295,12 @@ def sparse_decode(q, k_cache, v_cache, head_mask: int, k: int, s_in, *, s_indptr
 def hybrid_layer(q, k_cache, v_cache, retrieval_mask: int, k: int, s, *, s_out=None,
                  s_indptr=None, scores_out=None, out=None, flags: int = 0,
                  workspace: Optional[Workspace] = None, kv_indptr=None, seq_len=None,
-                 scale=None, block_table=None, page_size: int = 0):
+                 scale=None, block_table=None, page_size: int = 0, k_scale=None, v_scale=None):
     """One layer of the recurrence. `s` is S^{l} (None for an all-retrieval layer);
     S^{l+1} is written to `s_out` (default: in place into `s`). Returns out."""
     torch = _torch()
     out = _prep(q, k_cache, v_cache, out, kv_indptr)
-    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size)
+    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size, k_scale, v_scale)
     _opt(s, torch.int32, "s"); _opt(s_out, torch.int32, "s_out")
     _opt(s_indptr, torch.int64, "s_indptr"); _opt(scores_out, torch.float32, "scores_out")
     if s_out is None:

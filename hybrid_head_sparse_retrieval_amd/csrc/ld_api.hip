@@ -94,6 +94,13 @@ bool shape_ok(const ld_shape* s, ld_status* why) {
   } else if (s->pages_per_seq != 0 || s->block_table) {
     return false;
   }
+  if (s->reserved != 0) return false;
+  if (s->kv_dtype == 1) {
+    if (!(s->k_scale > 0.f) || !(s->v_scale > 0.f) || !std::isfinite(s->k_scale) || !std::isfinite(s->v_scale))
+      return false;
+  } else if (s->kv_dtype != 0 || s->k_scale != 0.f || s->v_scale != 0.f) {
+    return false;
+  }
   if (s->seq_len > kMaxSeq) { *why = LD_ERR_UNSUPPORTED; return false; }
   if (s->num_q_heads > 64) { *why = LD_ERR_UNSUPPORTED; return false; }
   if (s->num_q_heads % s->num_kv_heads != 0) return false;
@@ -270,8 +277,10 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   // 3. attention (+ fused first selection digit)
   AttnParams ap{};
   ap.q = static_cast<const uint16_t*>(q);
-  ap.kc = static_cast<const uint16_t*>(kc);
-  ap.vc = static_cast<const uint16_t*>(vc);
+  ap.kc = kc;
+  ap.vc = vc;
+  ap.kv_fp8 = shape->kv_dtype == 1 ? 1 : 0;
+  ap.v_scale = ap.kv_fp8 ? shape->v_scale : 1.f;
   ap.out = static_cast<uint16_t*>(out);
   ap.kv_indptr = shape->kv_indptr;
   ap.kv_head_stride = T * D;
@@ -283,7 +292,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     ap.npages = T >> ap.page_shift;
   }
   ap.B = B; ap.Hq = Hq; ap.Hkv = Hkv; ap.seq_len = N;
-  ap.scale = scale;
+  ap.scale = ap.kv_fp8 ? scale * shape->k_scale : scale;
   ap.active = active; ap.retrieval = retrieval;
   // groups that stream (they serve a retrieval head) first, then groups of sparse heads
   int ng = 0, ng_dense = 0, ret_per_group = 0, sp_per_group = 0;
@@ -307,7 +316,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   // in parallel (the attention launch still merges behind group barriers).
   const bool want_gb = !(flags & LD_FLAG_SEPARATE_SELECT);
   const bool in_select = want_gb && do_topk && ret_per_group <= 1;
-  const int64_t capacity = attention_capacity(D, G, ap.waves);
+  const int64_t capacity = attention_capacity(D, G, ap.waves, ap.kv_fp8 != 0);
   // union density of a sparse group's rows if its heads' sets were independent
   const double kf = std::min(1.0, (double)k / (double)N);
   const double rho = 1.0 - std::pow(1.0 - kf, (double)std::max(1, sp_per_group));

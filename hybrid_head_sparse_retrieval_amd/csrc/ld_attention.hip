@@ -156,7 +156,7 @@ __device__ __forceinline__ void merge_splits(AttnSmem<D, G, NW>& sm, const AttnP
     }
     L = wave_sum_f(L);
     if (lane == 0) {
-      sm.u.cmb.inv_l[jj] = 1.f / L;
+      sm.u.cmb.inv_l[jj] = p.v_scale / L;
       sm.u.cmb.mtot[jj] = M;
       sm.u.cmb.ltot[jj] = L;
     }
@@ -250,7 +250,7 @@ __device__ __forceinline__ void merge_columns(const AttnParams& p, uint32_t act,
     L = wave_sum_f(L);
     o.x = wave_sum_f(o.x); o.y = wave_sum_f(o.y); o.z = wave_sum_f(o.z); o.w = wave_sum_f(o.w);
     if (lane == 0) {
-      const float il = 1.f / L;
+      const float il = p.v_scale / L;
       ushort4 r;
       r.x = f32_to_bf16(o.x * il); r.y = f32_to_bf16(o.y * il);
       r.z = f32_to_bf16(o.z * il); r.w = f32_to_bf16(o.w * il);
@@ -562,7 +562,9 @@ __device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnP
   __syncthreads();
 }
 
-template <int D, int G, int NW>
+// F8: K and V hold E4M3 codes (one byte per element, dequantised exactly to bf16 /
+// fp32 in registers; their per-tensor scales are folded into p.scale and p.v_scale).
+template <int D, int G, int NW, bool F8>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams p) {
   constexpr int NT = 64 * NW;
   constexpr int KCH = D / 32;        // MFMA k-steps per row
@@ -649,8 +651,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   }
 
   // ---- per-wave streaming state (tiles wave, wave+4, ...; kTPC tiles per chunk)
-  const uint16_t* kbase = p.kc + (size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D;
-  const uint16_t* vbase = p.vc + (size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D;
+  constexpr int EB = F8 ? 1 : 2;              // bytes per K/V element
+  const char* kbase = static_cast<const char*>(p.kc) + ((size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D) * EB;
+  const char* vbase = static_cast<const char*>(p.vc) + ((size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D) * EB;
   // Paged KV: the page ids of the split's rows go to LDS once; row r of the split (a
   // row of the sequence: r0 + r) is then pool row page << shift | offset.
   const int pshift = p.page_shift, pmask = (1 << pshift) - 1;
@@ -707,18 +710,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       const int tb = tbase(c, t);
       const int pa = tb + mr;                 // A-operand row of this lane
       const bool va = pa < lim;
-      const uint16_t* kp = kbase + row_off(va ? row_of(pa) : 0) + mk * 8;
+      const char* kp = kbase + (row_off(va ? row_of(pa) : 0) + mk * 8) * EB;
 #pragma unroll
-      for (int kk = 0; kk < KCH; ++kk)
-        kd[t][kk] = va ? *reinterpret_cast<const uint4*>(kp + kk * 32) : make_uint4(0, 0, 0, 0);
+      for (int kk = 0; kk < KCH; ++kk) {
+        if constexpr (F8) {
+          const uint2 c = va ? *reinterpret_cast<const uint2*>(kp + kk * 32) : make_uint2(0, 0);
+          kd[t][kk] = make_uint4(c.x, c.y, 0, 0);
+        } else {
+          kd[t][kk] = va ? *reinterpret_cast<const uint4*>(kp + kk * 64) : make_uint4(0, 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int pv = tb + h2 * 8 + rg;      // P.V row of this lane
         const bool vv = pv < lim;
-        const uint16_t* vp = vbase + row_off(vv ? row_of(pv) : 0) + li * 8;
+        const char* vp = vbase + (row_off(vv ? row_of(pv) : 0) + li * 8) * EB;
 #pragma unroll
-        for (int c2 = 0; c2 < NV; ++c2)
-          vd[t * 2 + h2][c2] = vv ? *reinterpret_cast<const uint4*>(vp + c2 * 64) : make_uint4(0, 0, 0, 0);
+        for (int c2 = 0; c2 < NV; ++c2) {
+          if constexpr (F8) {
+            const uint2 c = vv ? *reinterpret_cast<const uint2*>(vp + c2 * 64) : make_uint2(0, 0);
+            vd[t * 2 + h2][c2] = make_uint4(c.x, c.y, 0, 0);
+          } else {
+            vd[t * 2 + h2][c2] = vv ? *reinterpret_cast<const uint4*>(vp + c2 * 128) : make_uint4(0, 0, 0, 0);
+          }
+        }
       }
     }
   };
@@ -828,7 +843,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     for (int t = 0; t < kTPC; ++t) {
       dacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KCH; ++kk) dacc[t] = mfma_bf16(kd[t][kk], qb[kk], dacc[t]);
+      for (int kk = 0; kk < KCH; ++kk) {
+        if constexpr (F8) dacc[t] = mfma_bf16(fp8x8_to_bf16x8(kd[t][kk].x, kd[t][kk].y), qb[kk], dacc[t]);
+        else dacc[t] = mfma_bf16(kd[t][kk], qb[kk], dacc[t]);
+      }
     }
     // scores of head mr for rows tb + 4*mk + r
     float tl[kTPC][4];
@@ -889,11 +907,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       float vf[EPL];
 #pragma unroll
       for (int c2 = 0; c2 < NV; ++c2) {
-        const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vd[rs][c2]);
+        if constexpr (F8) {
+          fp8x4_to_f32(vd[rs][c2].x, &vf[c2 * 8]);
+          fp8x4_to_f32(vd[rs][c2].y, &vf[c2 * 8 + 4]);
+        } else {
+          const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vd[rs][c2]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          vf[c2 * 8 + 2 * q] = bf_lo(vw[q]);
-          vf[c2 * 8 + 2 * q + 1] = bf_hi(vw[q]);
+          for (int q = 0; q < 4; ++q) {
+            vf[c2 * 8 + 2 * q] = bf_lo(vw[q]);
+            vf[c2 * 8 + 2 * q + 1] = bf_hi(vw[q]);
+          }
         }
       }
 #pragma unroll
@@ -1071,58 +1094,67 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   }
 }
 
-template <int D, int G>
-int64_t capacity_dg(int waves) {
+template <int D, int G, bool F8>
+int64_t capacity_dgf(int waves) {
   int per_cu = 0;
   hipError_t e;
   if (waves == 8)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attention<D, G, 8>, 512, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attention<D, G, 8, F8>, 512, 0);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attention<D, G, 4>, 256, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attention<D, G, 4, F8>, 256, 0);
   return e == hipSuccess ? per_cu : 0;
 }
+template <int D, int G>
+int64_t capacity_dg(int waves, bool fp8) {
+  return fp8 ? capacity_dgf<D, G, true>(waves) : capacity_dgf<D, G, false>(waves);
+}
 
+template <int D, int G, bool F8>
+hipError_t launch_dgf(const AttnParams& p, dim3 grid, hipStream_t st) {
+  if (p.waves == 8)
+    hipLaunchKernelGGL((k_attention<D, G, 8, F8>), grid, dim3(512), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_attention<D, G, 4, F8>), grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
 template <int D, int G>
 hipError_t launch_dg(const AttnParams& p, dim3 grid, hipStream_t st) {
-  if (p.waves == 8)
-    hipLaunchKernelGGL((k_attention<D, G, 8>), grid, dim3(512), 0, st, p);
-  else
-    hipLaunchKernelGGL((k_attention<D, G, 4>), grid, dim3(256), 0, st, p);
-  return hipGetLastError();
+  return p.kv_fp8 ? launch_dgf<D, G, true>(p, grid, st) : launch_dgf<D, G, false>(p, grid, st);
 }
 
 }  // namespace
 
-int64_t attention_capacity(int D, int G, int waves) {
-  // cached per device and (D, G, waves)
-  static std::atomic<int64_t> cache[64][2][4][2];
+int64_t attention_capacity(int D, int G, int waves, bool fp8) {
+  // cached per device and (D, G, waves, KV format)
+  static std::atomic<int64_t> cache[64][2][4][2][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   const int di = D == 128 ? 1 : 0;
   const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
   const int wi = waves == 8 ? 1 : 0;
-  int64_t c = cache[dev][di][gi][wi].load(std::memory_order_relaxed);
+  const int fi = fp8 ? 1 : 0;
+  int64_t c = cache[dev][di][gi][wi][fi].load(std::memory_order_relaxed);
   if (c > 0) return c;
   int64_t per_cu = 0;
   if (D == 128) {
     switch (G) {
-      case 1: per_cu = capacity_dg<128, 1>(waves); break;
-      case 2: per_cu = capacity_dg<128, 2>(waves); break;
-      case 4: per_cu = capacity_dg<128, 4>(waves); break;
-      case 8: per_cu = capacity_dg<128, 8>(waves); break;
+      case 1: per_cu = capacity_dg<128, 1>(waves, fp8); break;
+      case 2: per_cu = capacity_dg<128, 2>(waves, fp8); break;
+      case 4: per_cu = capacity_dg<128, 4>(waves, fp8); break;
+      case 8: per_cu = capacity_dg<128, 8>(waves, fp8); break;
     }
   } else {
     switch (G) {
-      case 1: per_cu = capacity_dg<64, 1>(waves); break;
-      case 2: per_cu = capacity_dg<64, 2>(waves); break;
-      case 4: per_cu = capacity_dg<64, 4>(waves); break;
-      case 8: per_cu = capacity_dg<64, 8>(waves); break;
+      case 1: per_cu = capacity_dg<64, 1>(waves, fp8); break;
+      case 2: per_cu = capacity_dg<64, 2>(waves, fp8); break;
+      case 4: per_cu = capacity_dg<64, 4>(waves, fp8); break;
+      case 8: per_cu = capacity_dg<64, 8>(waves, fp8); break;
     }
   }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   c = per_cu * cus;
-  cache[dev][di][gi][wi].store(c, std::memory_order_relaxed);
+  cache[dev][di][gi][wi][fi].store(c, std::memory_order_relaxed);
   return c;
 }
 

@@ -13,6 +13,25 @@ namespace ld {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // bf16 pair in one dword -> the two floats (bf16 is the top half of a binary32).
+// E4M3 codes (four per word, lowest byte first) to fp32, exactly, by the hardware
+// conversion of the OCP 8-bit format.
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = hi[0]; f[3] = hi[1];
+}
+// Eight E4M3 codes to eight bf16 (exact: every E4M3 value has at most 4 significant
+// bits and an exponent inside bf16's range, so the fp32 value's upper half is it).
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  float f[8];
+  fp8x4_to_f32(w0, f);
+  fp8x4_to_f32(w1, f + 4);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = (__float_as_uint(f[2 * i + 1]) & 0xffff0000u) | (__float_as_uint(f[2 * i]) >> 16);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -33,8 +33,10 @@ constexpr int kEpochWord = 40;         // the group's epoch: in-launch barrier c
 // Attention over one layer: workgroup = (sequence b, KV group, split of rows).
 struct AttnParams {
   const uint16_t* q;      // bf16 [B][Hq][D]
-  const uint16_t* kc;     // bf16 [Hkv][T][D]
-  const uint16_t* vc;
+  const void* kc;         // [Hkv][T][D], bf16, or E4M3 codes when kv_fp8
+  const void* vc;
+  int kv_fp8;
+  float v_scale;          // factor on O (the V dequantisation scale; 1 for bf16)
   uint16_t* out;          // bf16 [B][Hq][D]
   const int64_t* kv_indptr;
   int64_t kv_head_stride; // T*D elements
@@ -134,7 +136,7 @@ struct CopyParams {
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_attention(const AttnParams& p, int D, int G, dim3 grid, hipStream_t st);
-int64_t attention_capacity(int D, int G, int waves);   // workgroups resident at once
+int64_t attention_capacity(int D, int G, int waves, bool fp8);   // workgroups resident at once
 hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist);
 hipError_t launch_bitmap_build(const BitmapParams& p, int rows, hipStream_t st);
 hipError_t launch_copy_rows(const CopyParams& p, int rows, hipStream_t st);

@@ -116,6 +116,12 @@ typedef struct ld_shape {
   const int32_t* block_table; /* paged: device [B][pages_per_seq] page ids in
                                  0 .. total_tokens/page_size - 1 (ids outside are
                                  clamped); else NULL */
+  int32_t kv_dtype;       /* 0: K and V are bf16. 1: K and V are 8-bit E4M3 codes (OCP
+                             format: bias 7, no infinities), one byte per element, and
+                             the values are k_scale * code and v_scale * code. */
+  float k_scale;          /* kv_dtype 1: K dequantisation scale (> 0); else 0 */
+  float v_scale;          /* kv_dtype 1: V dequantisation scale (> 0); else 0 */
+  int32_t reserved;       /* must be 0 */
 } ld_shape;
 
 /* Human-readable text of a status code (static storage). */

@@ -66,10 +66,16 @@ def test_workspace_size(lib):
                 dict(page_size=64, pages_per_seq=512, block_table=None, total_tokens=1 << 20),
                 dict(page_size=64, pages_per_seq=511, block_table=FAKE, total_tokens=1 << 20),
                 dict(page_size=64, pages_per_seq=512, block_table=FAKE, total_tokens=(1 << 20) + 32),
-                dict(page_size=0, pages_per_seq=512), dict(page_size=0, block_table=FAKE)):
+                dict(page_size=0, pages_per_seq=512), dict(page_size=0, block_table=FAKE),
+                # quantised KV: unknown format, missing or bad scales, scales without it
+                dict(kv_dtype=2), dict(kv_dtype=1), dict(kv_dtype=1, k_scale=1.0, v_scale=-1.0),
+                dict(kv_dtype=1, k_scale=float("inf"), v_scale=1.0), dict(kv_dtype=0, k_scale=1.0),
+                dict(reserved=1)):
         assert lib.ld_workspace_size(ctypes.byref(_shape(**bad)), 10) == 0, bad
     paged = _shape(page_size=64, pages_per_seq=512, block_table=FAKE, total_tokens=1 << 20)
     assert lib.ld_workspace_size(ctypes.byref(paged), 10) > 0
+    fp8 = _shape(kv_dtype=1, k_scale=0.5, v_scale=2.0)
+    assert lib.ld_workspace_size(ctypes.byref(fp8), 10) > 0
     assert lib.ld_workspace_size(ctypes.byref(s), 0) == 0
     assert lib.ld_workspace_size(ctypes.byref(s), 32769) == 0
     assert lib.ld_topk_workspace_size(4, 1000) > 0
