@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_32k")
     ap.add_argument("--split", type=int, default=0, help="rows per split = 256<<(v-1), 0 = auto")
     ap.add_argument("--waves", type=int, default=0, help="attention waves per workgroup: 1 = 4, 2 = 8, 0 = auto")
+    ap.add_argument("--kv", choices=("bf16", "fp8"), default="bf16",
+                    help="KV cache format: bf16, or 8-bit E4M3 codes (unit scales)")
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged KV: rows per page (power of two, 16..4096); 0 = contiguous")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -64,8 +66,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def layer_bytes(w, l, S_in, d):
-    """Algorithmic bytes of layer l given S^{l} (dict {(b,h): indices}) -> (attention, total)."""
+def layer_bytes(w, l, S_in, d, kv_elem=2):
+    """Algorithmic bytes of layer l given S^{l} (dict {(b,h): indices}) -> (attention, total).
+    kv_elem: bytes per K/V element (2 for bf16, 1 for E4M3 codes)."""
     B, Hq, Hkv = w.batch, w.num_q_heads, w.num_kv_heads
     G = Hq // Hkv
     mask = w.retrieval_masks[l]
@@ -75,10 +78,10 @@ def layer_bytes(w, l, S_in, d):
         for g in range(Hkv):
             heads = range(g * G, (g + 1) * G)
             if any(mask >> h & 1 for h in heads):
-                kv += 2 * n * d * 2
+                kv += 2 * n * d * kv_elem
             else:
                 u = np.unique(np.concatenate([S_in[(b, h)] for h in heads]))
-                kv += int(u.size) * 2 * d * 2
+                kv += int(u.size) * 2 * d * kv_elem
     qo = 2 * B * Hq * d * 2
     s_io = 0
     for b in range(B):
@@ -258,6 +261,19 @@ def main():
         f"({sum(t.numel() * 2 for t in (inputs[0][1], inputs[0][2])) * w.kv_layers() / 1e9:.2f} GB KV)")
 
     logical = inputs
+    kv_elem = 2
+    if args.kv == "fp8":
+        # E4M3 codes of the same draws (round to nearest even); the oracle leg keeps bf16
+        cache = {}
+        q8 = []
+        for (q, kc, vc) in inputs:
+            key = (kc.data_ptr(), vc.data_ptr())
+            if key not in cache:
+                cache[key] = (kc.float().to(torch.float8_e4m3fn).view(torch.uint8),
+                              vc.float().to(torch.float8_e4m3fn).view(torch.uint8))
+            q8.append((q,) + cache[key])
+        inputs, kv_elem = q8, 1
+        log("[bench] KV cache as E4M3 codes (unit scales)")
     if args.page_size:
         inputs = paged_inputs(torch, w, inputs, args.page_size)
         log(f"[bench] paged KV: {args.page_size}-row pages in a shuffled pool")
@@ -275,7 +291,7 @@ def main():
             step.layer(l, q, kc, vc, block_table=inputs[l][3], page_size=inputs[l][4])
         else:
             step.layer(l, q, kc, vc)
-        a, t = layer_bytes(w, l, S_in, d) if l > 0 else layer_bytes(w, l, None, d)
+        a, t = layer_bytes(w, l, S_in, d, kv_elem) if l > 0 else layer_bytes(w, l, None, d, kv_elem)
         attn_bytes.append(a)
         total_bytes.append(t)
     torch.cuda.synchronize()
@@ -404,7 +420,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if args.kv == "bf16" else "bf16 q, e4m3 kv",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "layers": L, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim": d,
@@ -412,7 +428,8 @@ def main():
                    "k": w.k_per_seq[0] if w.batch == 1 else list(w.k_per_seq),
                    "retrieval_heads_after_layer0": sum(bin(m).count("1") for m in w.retrieval_masks[1:]),
                    "split_rows": "auto" if args.split == 0 else 256 << (args.split - 1),
-                   "kv_layout": f"paged {args.page_size}-row pages" if args.page_size else "contiguous"},
+                   "kv_layout": f"paged {args.page_size}-row pages" if args.page_size else "contiguous",
+                   "kv_format": args.kv},
         "roofline": roof,
         # sparse layers that read the first layer's cache again may be served from the
         # 256 MB last-level cache, so their GB/s can exceed the HBM figure
@@ -423,7 +440,8 @@ def main():
 
     # ---- CPU oracle baseline on a bounded sample of the same workload
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, logical, total_bytes, args.cpu_seconds)
+        oracle_inputs = logical if args.kv == "bf16" else q8
+        result["cpu_baseline"] = cpu_baseline(w, oracle_inputs, total_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
@@ -432,6 +450,7 @@ def cpu_baseline(w, inputs, total_bytes, target_s):
     target_s seconds of CPU work; report GB/s of algorithmic bytes processed."""
     from oracle import lychee_oracle as orc
     import workloads as wl
+    import torch
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -442,10 +461,15 @@ def cpu_baseline(w, inputs, total_bytes, target_s):
     spent, done, nbytes = 0.0, 0, 0
     for l in range(w.layers):
         q, kc, vc = inputs[l]
-        qb, kb_, vb = wl.bf16_bits(q), wl.bf16_bits(kc), wl.bf16_bits(vc)
         ret = [bool(w.retrieval_masks[l] >> h & 1) for h in range(w.num_q_heads)]
-        t0 = time.perf_counter()
-        _, S, _ = orc.hybrid_layer_bf16(qb, kb_, vb, offs, ret, w.k_per_seq, S)
+        if kc.dtype == torch.uint8:
+            k8, v8 = kc.cpu().numpy(), vc.cpu().numpy()
+            t0 = time.perf_counter()
+            _, S, _ = orc.hybrid_layer_fp8(wl.bf16_bits(q), k8, v8, 1.0, 1.0, offs, ret, w.k_per_seq, S)
+        else:
+            qb, kb_, vb = wl.bf16_bits(q), wl.bf16_bits(kc), wl.bf16_bits(vc)
+            t0 = time.perf_counter()
+            _, S, _ = orc.hybrid_layer_bf16(qb, kb_, vb, offs, ret, w.k_per_seq, S)
         spent += time.perf_counter() - t0
         done += 1
         nbytes += total_bytes[l]
