@@ -36,8 +36,8 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTile = 16;        // rows per MFMA tile
-constexpr int kTPC = 1;          // tiles per chunk per wave
-constexpr int kChunkRows = kTile * kTPC;
+constexpr int kMaxTPC = 2;       // tiles per chunk per wave, at most
+constexpr int kChunkRows = kTile * kMaxTPC;
 constexpr int kCandLds = 8192;     // selection candidates staged in LDS
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -79,7 +79,7 @@ struct AttnSmem {
   int cnt4[NW][2];
   int ncnt[kRep];                    // candidate counts of the sub-lists
   int pages[kMaxSplitRows / 16 + 1]; // paged KV: page ids of the split's rows
-  float pl[NW][kChunkRows][G];       // per wave: probabilities of the chunk's rows
+  float pl[NW][kChunkRows][G];       // per wave: probabilities of the chunk's rows (up to)
   union {
     uint32_t hist[G][kHist1Bins];
     struct {
@@ -570,7 +570,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   constexpr int KCH = D / 32;        // MFMA k-steps per row
   constexpr int EPL = D / 8;         // dims per lane in the P.V layout
   constexpr int NV = D / 64;         // 16-byte V loads per lane per row
-  constexpr int RSC = 2 * kTPC;      // P.V row steps (8 rows) per chunk
+  // tiles per chunk per wave: two with E4M3 codes, so that a wave keeps as many bytes
+  // in flight as with bf16
+  constexpr int TPC = F8 ? 2 : 1;
+  constexpr int CROWS = kTile * TPC;
+  constexpr int RSC = 2 * TPC;      // P.V row steps (8 rows) per chunk
   using Smem = AttnSmem<D, G, NW>;
   constexpr int RP = Smem::RP;
   __shared__ Smem sm;
@@ -650,7 +654,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       qb[kk] = make_uint4(0, 0, 0, 0);
   }
 
-  // ---- per-wave streaming state (tiles wave, wave+4, ...; kTPC tiles per chunk)
+  // ---- per-wave streaming state (tiles wave, wave+4, ...; TPC tiles per chunk)
   constexpr int EB = F8 ? 1 : 2;              // bytes per K/V element
   const char* kbase = static_cast<const char*>(p.kc) + ((size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D) * EB;
   const char* vbase = static_cast<const char*>(p.vc) + ((size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D) * EB;
@@ -682,10 +686,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   auto chunks_of = [&](int n) {
     const int ntiles = (n + kTile - 1) / kTile;
     const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
-    return (my_tiles + kTPC - 1) / kTPC;
+    return (my_tiles + TPC - 1) / TPC;
   };
   auto tbase = [&](int c, int t) -> int {
-    return dense ? (wave + NW * (c * kTPC + t)) * kTile : lbase + (c * kTPC + t) * kTile;
+    return dense ? (wave + NW * (c * TPC + t)) * kTile : lbase + (c * TPC + t) * kTile;
   };
   int lim = nrows;                            // visit positions below lim are valid
 
@@ -701,12 +705,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
 
-  uint4 kr[3][kTPC][KCH], vr[3][RSC][NV];
+  uint4 kr[3][TPC][KCH], vr[3][RSC][NV];
 
   auto row_of = [&](int pos) -> int { return dense ? pos : (int)sm.list[pos]; };
-  auto load_chunk = [&](int c, uint4 (&kd)[kTPC][KCH], uint4 (&vd)[RSC][NV]) {
+  auto load_chunk = [&](int c, uint4 (&kd)[TPC][KCH], uint4 (&vd)[RSC][NV]) {
 #pragma unroll
-    for (int t = 0; t < kTPC; ++t) {
+    for (int t = 0; t < TPC; ++t) {
       const int tb = tbase(c, t);
       const int pa = tb + mr;                 // A-operand row of this lane
       const bool va = pa < lim;
@@ -830,17 +834,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   // words, before the first gathered rows) so that it has long arrived when the
   // workgroup reaches its first barrier
   const uint32_t epoch0 = p.gb ? ld_dev(p.gb_cnt + (size_t)(b * p.Hkv + g) * kGbCounters + kEpochWord) : 0u;
-  int nchunks = dense ? chunks_of(nlist) : (nl_w + kChunkRows - 1) / kChunkRows;
+  int nchunks = dense ? chunks_of(nlist) : (nl_w + CROWS - 1) / CROWS;
   if (!dense) {
     if (nchunks > 0) load_chunk(0, kr[0], vr[0]);
     if (nchunks > 1) load_chunk(1, kr[1], vr[1]);
   }
 
-  auto compute_chunk = [&](int c, const uint4 (&kd)[kTPC][KCH], const uint4 (&vd)[RSC][NV]) {
+  auto compute_chunk = [&](int c, const uint4 (&kd)[TPC][KCH], const uint4 (&vd)[RSC][NV]) {
     // q . K on the matrix cores
-    f32x4_t dacc[kTPC];
+    f32x4_t dacc[TPC];
 #pragma unroll
-    for (int t = 0; t < kTPC; ++t) {
+    for (int t = 0; t < TPC; ++t) {
       dacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KCH; ++kk) {
@@ -849,10 +853,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       }
     }
     // scores of head mr for rows tb + 4*mk + r
-    float tl[kTPC][4];
+    float tl[TPC][4];
     float cm = -LD_INF;
 #pragma unroll
-    for (int t = 0; t < kTPC; ++t) {
+    for (int t = 0; t < TPC; ++t) {
       const int tb = tbase(c, t);
       const int pos0 = tb + 4 * mk;
       uint32_t hm4 = 0;
@@ -879,7 +883,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     m_lane = mn;
     float ps = 0.f;
 #pragma unroll
-    for (int t = 0; t < kTPC; ++t)
+    for (int t = 0; t < TPC; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float pr = exp2_fast(tl[t][r] - mu);
