@@ -44,6 +44,7 @@ __all__ = [
     "bf16_bits_to_f64",
     "fp8_e4m3_to_f64",
     "hybrid_layer_fp8",
+    "select_topk_blocks",
     "softmax_attention",
     "select_topk",
     "select_topk_f32",
@@ -127,6 +128,29 @@ def select_topk_f32(scores_f32: np.ndarray, k: int) -> np.ndarray:
     s = np.asarray(scores_f32)
     assert s.dtype == np.float32
     return select_topk(s, k)
+
+
+def select_topk_blocks(scores: np.ndarray, k: int, block: int = 64) -> np.ndarray:
+    """Token-block selection of HySparse (section 3 Methodology): the full layer's
+    scores are reduced to one score per block of `block` consecutive tokens, the block
+    maximum, and the k / block blocks with the largest block scores are kept; their
+    tokens form the set handed to the sparse layers. Block scores are ranked like token
+    scores (select_topk: larger first, lower block index first on ties, NaN lowest; a
+    block's maximum ignores NaN unless every score in it is NaN). Returns the token
+    indices of the kept blocks in ascending order (exactly k of them).
+
+    Reading taken: the pages give the block maximum and k/B blocks (B = 64); this form
+    requires n and k to be multiples of the block size.
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.size
+    assert n % block == 0 and k % block == 0 and 0 < k <= n
+    blocks = s.reshape(n // block, block)
+    with np.errstate(invalid="ignore"):
+        allnan = np.all(np.isnan(blocks), axis=1)
+        bmax = np.where(allnan, np.nan, np.nanmax(np.where(np.isnan(blocks), -np.inf, blocks), axis=1))
+    kept = select_topk(bmax, k // block)
+    return (kept[:, None] * block + np.arange(block)[None, :]).reshape(-1)
 
 
 def retrieval_head(q, K, V, k: int, scale: float):

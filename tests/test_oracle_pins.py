@@ -345,3 +345,37 @@ def test_fp8_layer_scales_are_exact_factors():
     for key in sc1:
         assert np.array_equal(sc3[key], 2.0 * sc1[key])
         assert np.array_equal(S1[key], S3[key]) and np.array_equal(S1[key], S2[key])
+
+
+# ---- HySparse token-block selection
+
+def _blocks_brute(scores, k, block):
+    n = len(scores)
+    cand = []
+    for j in range(n // block):
+        vals = [float(x) for x in scores[j * block:(j + 1) * block] if not math.isnan(float(x))]
+        best = max(vals) if vals else float("nan")
+        cand.append((math.isnan(best), -(best if not math.isnan(best) else 0.0) + 0.0, j))
+    kept = sorted(j for (_, _, j) in sorted(cand)[:k // block])
+    return np.array([j * block + r for j in kept for r in range(block)], dtype=np.int64)
+
+
+def test_block_selection_brute_force_with_ties_and_nans():
+    rng = np.random.default_rng(11)
+    for it in range(60):
+        block = int(rng.choice([2, 4, 8]))
+        nb = int(rng.integers(2, 12))
+        n = nb * block
+        k = block * int(rng.integers(1, nb + 1))
+        s = rng.choice([-1.0, 0.0, -0.0, 0.5, 2.0, np.nan], size=n)
+        assert np.array_equal(orc.select_topk_blocks(s, k, block), _blocks_brute(s, k, block)), it
+
+
+def test_block_selection_reduces_to_token_selection_and_known_case():
+    rng = np.random.default_rng(12)
+    s = rng.standard_normal(40)
+    assert np.array_equal(orc.select_topk_blocks(s, 7, 1), orc.select_topk(s, 7))
+    ramp = np.arange(256, dtype=np.float64)
+    assert np.array_equal(orc.select_topk_blocks(ramp, 128, 64), np.arange(128, 256))
+    spike = np.zeros(256); spike[5] = 9.0          # one high token lifts its whole block
+    assert np.array_equal(orc.select_topk_blocks(spike, 64, 64), np.arange(0, 64))
