@@ -17,13 +17,14 @@ __all__ = [
     "LycheeDecodeError", "LycheeDecodeUnavailable", "library_path", "load_library",
     "Shape", "workspace_bytes", "topk_workspace_bytes", "Workspace", "TopkWorkspace",
     "retrieval_decode", "sparse_decode", "hybrid_layer", "topk_select",
-    "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "FLAG_SEPARATE_SELECT", "flag_split_rows", "flag_waves", "EXPORTED_SYMBOLS",
+    "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "FLAG_SEPARATE_SELECT", "FLAG_BLOCK_SELECT", "flag_split_rows", "flag_waves", "EXPORTED_SYMBOLS",
 ]
 
 LD_OK = 0
 FLAG_SKIP_TOPK = 1
 FLAG_S_CHAINED = 2
 FLAG_SEPARATE_SELECT = 4
+FLAG_BLOCK_SELECT = 8
 _STATUS = {1: "invalid argument", 2: "unsupported shape", 3: "workspace missing or too small",
            4: "HIP launch or copy failed", 5: "a bounded wait between workgroups gave up"}
 EXPORTED_SYMBOLS = ("ld_status_string", "ld_workspace_size", "ld_topk_workspace_size",

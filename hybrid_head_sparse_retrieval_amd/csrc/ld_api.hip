@@ -30,6 +30,7 @@ struct LayerLayout {
   SelArrays sel;
   size_t logits, part_ml, part_acc, l1_ml, l1_acc, bitmaps;
   size_t gb_cnt, gb_rel, row_cnt, gb_cand, pub;       // group-barrier mode
+  size_t blk_scores, blk_idx;                         // token-block selection
   int64_t sub_cap;
   size_t total;
 };
@@ -142,6 +143,8 @@ LayerLayout layer_layout(const ld_shape* s) {
   L.sub_cap = ((int64_t)(N + kRep - 1) / kRep + 2 * kMaxSplitRows + 63) / 64 * 64;
   L.gb_cand = take((size_t)L.slots * kRep * L.sub_cap * 4);
   L.pub = take((size_t)L.slots * L.P * 8);
+  L.blk_scores = take((size_t)L.slots * ((N + kBlock - 1) / kBlock) * 4);
+  L.blk_idx = take((size_t)L.slots * ((N + kBlock - 1) / kBlock) * 4);
   L.total = o;
   return L;
 }
@@ -234,6 +237,8 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   if (k < 1 || k > N) return LD_ERR_INVALID_ARGUMENT;
   const uint64_t sparse = active & ~retrieval;
   const bool do_topk = want_topk && retrieval != 0;
+  const bool block = do_topk && (flags & LD_FLAG_BLOCK_SELECT);
+  if (block && (k % kBlock != 0 || N % kBlock != 0 || shape->kv_indptr || s_indptr)) return LD_ERR_INVALID_ARGUMENT;
   if (sparse && !s_in) return LD_ERR_INVALID_ARGUMENT;
   if (do_topk && !s_out) return LD_ERR_INVALID_ARGUMENT;
   if ((s_in && ((uintptr_t)s_in & 3u)) || (s_out && ((uintptr_t)s_out & 3u))) return LD_ERR_INVALID_ARGUMENT;
@@ -315,7 +320,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   // retrieval heads in a group select in a launch of their own, where every row runs
   // in parallel (the attention launch still merges behind group barriers).
   const bool want_gb = !(flags & LD_FLAG_SEPARATE_SELECT);
-  const bool in_select = want_gb && do_topk && ret_per_group <= 1;
+  const bool in_select = want_gb && do_topk && !block && ret_per_group <= 1;
   const int64_t capacity = attention_capacity(D, G, ap.waves, ap.kv_fp8 != 0);
   // union density of a sparse group's rows if its heads' sets were independent
   const double kf = std::min(1.0, (double)k / (double)N);
@@ -335,7 +340,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   ap.l1_ml = at<float>(ws, L.l1_ml);
   ap.l1_acc = at<float>(ws, L.l1_acc);
   ap.P1 = L.P1;
-  ap.do_topk = do_topk ? 1 : 0;
+  ap.do_topk = (do_topk && !block) ? 1 : 0;     // block selection needs the logits only
   ap.hist1 = at<uint32_t>(ws, L.sel.hist1);
   ap.sel_info = at<uint32_t>(ws, L.sel.sel_info);
   ap.k_dense = k;
@@ -358,8 +363,30 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   }
   if (launch_attention(ap, D, G, dim3((unsigned)nwg), st) != hipSuccess) return LD_ERR_HIP;
 
-  // 4. argsTopK of the retrieval rows
-  if (do_topk && !(gb && in_select)) {
+  // 4. argsTopK of the retrieval rows: by token blocks (block maxima, then the same
+  // radix select over the block scores, then the kept blocks' tokens), or by tokens
+  if (block) {
+    BlockParams bk{};
+    bk.logits = ap.logits; bk.seq_len = N;
+    bk.scores = at<float>(ws, L.blk_scores);
+    bk.kept = at<int32_t>(ws, L.blk_idx);
+    bk.rows = B * nret; bk.nblk = N / kBlock; bk.kblk = k / kBlock;
+    bk.s_out = s_out; bk.k_dense = k;
+    bk.bitmaps = bitmaps; bk.W = L.W;
+    bk.Hq = Hq; bk.nret = nret;
+    std::memcpy(bk.heads, ret_heads, sizeof(ret_heads));
+    if (launch_block_max(bk, bk.rows, st) != hipSuccess) return LD_ERR_HIP;
+    SelParams sp{};
+    sp.mode = 0;
+    sp.nrows = bk.rows;
+    sp.Ch = (bk.nblk + kSelChunk - 1) / kSelChunk;
+    sp.scores = bk.scores; sp.row_stride = bk.nblk; sp.n = bk.nblk; sp.k = bk.kblk;
+    sp.idx_out = at<int32_t>(ws, L.blk_idx); sp.val_out = nullptr;
+    fill_sel(sp, L.sel, ws);
+    sp.C = (bk.nblk + kSelSpan - 1) / kSelSpan;    // spans of this row length
+    if (launch_select(sp, st, true) != hipSuccess) return LD_ERR_HIP;
+    if (launch_block_expand(bk, bk.rows, st) != hipSuccess) return LD_ERR_HIP;
+  } else if (do_topk && !(gb && in_select)) {
     SelParams sp{};
     sp.mode = 1;
     sp.nrows = B * nret;

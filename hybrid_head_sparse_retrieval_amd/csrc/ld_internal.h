@@ -133,6 +133,19 @@ struct CopyParams {
   int Hq; int nsp; uint8_t heads[64];
 };
 
+// Token-block selection (HySparse): block maxima of retrieval rows' logits, and the
+// kept blocks' tokens written as S rows and membership bitmaps.
+struct BlockParams {
+  const float* logits; int seq_len;       // [B*Hq][seq_len] logits of the layer
+  float* scores;                          // [rows][nblk] block maxima
+  const int32_t* kept;                    // [rows][kblk] kept blocks, ascending
+  int rows, nblk, kblk;                   // retrieval rows, blocks per row, blocks kept per row
+  int32_t* s_out; int k_dense;            // S rows [B][Hq][k_dense], k_dense = kblk * kBlock
+  uint32_t* bitmaps; int W;
+  int Hq; int nret; uint8_t heads[64];    // row r -> (b = r / nret, h = heads[r % nret])
+};
+constexpr int kBlock = 64;                // tokens per block
+
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_attention(const AttnParams& p, int D, int G, dim3 grid, hipStream_t st);
@@ -141,5 +154,7 @@ hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist);
 hipError_t launch_bitmap_build(const BitmapParams& p, int rows, hipStream_t st);
 hipError_t launch_copy_rows(const CopyParams& p, int rows, hipStream_t st);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t st);
+hipError_t launch_block_max(const BlockParams& p, int rows, hipStream_t st);
+hipError_t launch_block_expand(const BlockParams& p, int rows, hipStream_t st);
 
 }  // namespace ld

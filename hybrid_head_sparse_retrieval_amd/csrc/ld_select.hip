@@ -615,7 +615,58 @@ __global__ __launch_bounds__(kThreads) void k_zero(uint4* p16, size_t n16, uint8
   if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
 }
 
+// ------------------------------------------------------- token-block selection
+
+// One wave per block: the block maximum of a retrieval row's logits (NaN only when
+// every logit of the block is NaN; fmaxf keeps the number of a NaN / number pair).
+__global__ __launch_bounds__(kThreads) void k_block_max(const BlockParams p) {
+  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (wave >= (int64_t)p.rows * p.nblk) return;               // whole waves leave together
+  const int lane = threadIdx.x & 63;
+  const int r = (int)(wave / p.nblk), j = (int)(wave % p.nblk);
+  const int b = r / p.nret, h = p.heads[r % p.nret];
+  const float* lg = p.logits + ((size_t)b * p.Hq + h) * p.seq_len + (size_t)j * kBlock;
+  float m = lg[lane];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) p.scores[(size_t)r * p.nblk + j] = m;
+}
+
+// One workgroup per retrieval row: S = the tokens of the kept blocks in ascending
+// order, and the row's membership bitmap = exactly those tokens.
+__global__ __launch_bounds__(kThreads) void k_block_expand(const BlockParams p) {
+  const int r = blockIdx.x;
+  const int b = r / p.nret, h = p.heads[r % p.nret];
+  const int slot = b * p.Hq + h;
+  const int32_t* kept = p.kept + (size_t)r * p.kblk;
+  int32_t* out = p.s_out + (size_t)slot * p.k_dense;
+  for (int i = threadIdx.x; i < p.kblk * kBlock; i += kThreads) out[i] = kept[i / kBlock] * kBlock + (i % kBlock);
+  if (p.bitmaps) {
+    uint32_t* bm = p.bitmaps + (size_t)slot * p.W;
+    for (int w = threadIdx.x; w < p.W; w += kThreads) bm[w] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < p.kblk; i += kThreads) {
+      const int w0 = kept[i] * (kBlock / 32);
+#pragma unroll
+      for (int q = 0; q < kBlock / 32; ++q)
+        if (w0 + q < p.W) bm[w0 + q] = 0xffffffffu;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_block_max(const BlockParams& p, int rows, hipStream_t st) {
+  const int64_t waves = (int64_t)rows * p.nblk;
+  const unsigned grid = (unsigned)((waves + kThreads / 64 - 1) / (kThreads / 64));
+  hipLaunchKernelGGL(k_block_max, dim3(grid), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_expand(const BlockParams& p, int rows, hipStream_t st) {
+  hipLaunchKernelGGL(k_block_expand, dim3((unsigned)rows), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
 
 // Workgroups of k_sel_fused that the current device holds at once.
 int64_t fused_capacity() {

@@ -84,7 +84,13 @@ enum {
      at once (where, by default, the splits of each KV group meet at device-wide
      barriers, merge O themselves and, when the group has one retrieval head, select
      its S too). S is the same either way; O may differ by fp32 rounding. */
-  LD_FLAG_SEPARATE_SELECT = 1u << 2
+  LD_FLAG_SEPARATE_SELECT = 1u << 2,
+  /* Token-block selection (HySparse, section 3): a retrieval head keeps the k/64 blocks
+     of 64 consecutive tokens with the largest block maxima of its logits (ties to the
+     lower block, NaN lowest) and S = their tokens in ascending order. Requires k and
+     seq_len to be multiples of 64, uniform sequences (kv_indptr NULL) and dense S
+     (s_indptr NULL); otherwise the call returns LD_ERR_INVALID_ARGUMENT. */
+  LD_FLAG_BLOCK_SELECT = 1u << 3
 };
 /* Optional launch-shape overrides (0 = automatic): rows per attention split =
    256 << (v - 1) for v = 1..5 in bits 8..11, for every KV group (automatic: groups
