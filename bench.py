@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--waves", type=int, default=0, help="attention waves per workgroup: 1 = 4, 2 = 8, 0 = auto")
     ap.add_argument("--kv", choices=("bf16", "fp8"), default="bf16",
                     help="KV cache format: bf16, or 8-bit E4M3 codes (unit scales)")
+    ap.add_argument("--block-select", action="store_true",
+                    help="retrieval heads keep 64-token blocks by block maximum (HySparse form)")
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged KV: rows per page (power of two, 16..4096); 0 = contiguous")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -279,6 +281,11 @@ def main():
         log(f"[bench] paged KV: {args.page_size}-row pages in a shuffled pool")
 
     split_flag = ld.flag_split_rows(args.split) | ld.flag_waves(args.waves)
+    if args.block_select:
+        if any(k % 64 for k in w.k_per_seq) or any(n % 64 for n in w.seq_lens) or w.batch > 1:
+            log("[bench] --block-select needs one sequence with k and N multiples of 64")
+            sys.exit(2)
+        split_flag |= ld.FLAG_BLOCK_SELECT
     step = DecodeStep(w.batch, w.num_q_heads, w.num_kv_heads, d, w.seq_lens, w.k_per_seq,
                       w.retrieval_masks, csr=w.ragged_csr, device=dev, split_flag=split_flag)
 
@@ -429,7 +436,8 @@ def main():
                    "retrieval_heads_after_layer0": sum(bin(m).count("1") for m in w.retrieval_masks[1:]),
                    "split_rows": "auto" if args.split == 0 else 256 << (args.split - 1),
                    "kv_layout": f"paged {args.page_size}-row pages" if args.page_size else "contiguous",
-                   "kv_format": args.kv},
+                   "kv_format": args.kv,
+                   "selection": "64-token blocks" if args.block_select else "tokens"},
         "roofline": roof,
         # sparse layers that read the first layer's cache again may be served from the
         # 256 MB last-level cache, so their GB/s can exceed the HBM figure
