@@ -28,13 +28,15 @@ def _decoded_bf16(codes):
 
 
 @pytest.mark.parametrize("case", [
-    # (B, Hq, Hkv, d, n, masks)
-    (1, 8, 2, 128, 5000, [0xFF, 0x11, 0x00]),
-    (1, 4, 4, 64, 2100, [0xF, 0x2]),
-    (1, 16, 2, 128, 3000, [0xFFFF, 0x0101]),
+    # (B, Hq, Hkv, d, n, masks, waves flag)
+    (1, 8, 2, 128, 5000, [0xFF, 0x11, 0x00], 0),
+    (1, 8, 2, 128, 5000, [0xFF, 0x11, 0x00], 2),
+    (1, 4, 4, 64, 2100, [0xF, 0x2], 0),
+    (1, 16, 2, 128, 3000, [0xFFFF, 0x0101], 0),
+    (1, 16, 2, 128, 3000, [0xFFFF, 0x0101], 2),
 ])
 def test_fp8_unit_scales_equal_bf16_of_decoded(case):
-    B, Hq, Hkv, d, n, masks = case
+    B, Hq, Hkv, d, n, masks, waves = case
     ld = _ld()
     dev = "cuda"
     k = int(0.3 * n)
@@ -49,7 +51,7 @@ def test_fp8_unit_scales_equal_bf16_of_decoded(case):
         if wsa is None:
             wsa = ld.Workspace(ld.make_shape(qd, k8.to(dev)), k, dev)
             wsb = ld.Workspace(ld.make_shape(qd, kb.to(dev)), k, dev)
-        flags = ld.FLAG_S_CHAINED if l else 0
+        flags = (ld.FLAG_S_CHAINED if l else 0) | ld.flag_waves(waves)
         oa = ld.hybrid_layer(qd, k8.to(dev), v8.to(dev), mask, k, Sa if l else None, s_out=Sa, flags=flags,
                              workspace=wsa)
         ob = ld.hybrid_layer(qd, kb.to(dev), vb.to(dev), mask, k, Sb if l else None, s_out=Sb, flags=flags,
