@@ -45,6 +45,7 @@ __all__ = [
     "fp8_e4m3_to_f64",
     "hybrid_layer_fp8",
     "select_topk_blocks",
+    "hysparse_sparse_layer",
     "softmax_attention",
     "select_topk",
     "select_topk_f32",
@@ -238,6 +239,46 @@ def hybrid_layer_fp8(q_bits, k_codes, v_codes, k_scale, v_scale, kv_offsets, ret
     return hybrid_layer_f64(bf16_bits_to_f64(q_bits), float(k_scale) * fp8_e4m3_to_f64(k_codes),
                             float(v_scale) * fp8_e4m3_to_f64(v_codes), kv_offsets, retrieval,
                             k_per_seq, S_in, scale=scale, active=active)
+
+
+def hysparse_sparse_layer(Q, K, V, kv_offsets, S_in, Kw, Vw, gate, scale=None):
+    """A HySparse sparse layer ([HS] section 3 Methodology): each query head runs two
+    branches and mixes them with a sigmoid gate.
+
+    Block-sparse branch: sparse_head over rows S_in[(b, h)] of the shared cache K, V
+    ([Hkv][T][d], sequence b at kv_offsets[b]:kv_offsets[b+1]), i.e. the KV cache and
+    the selection of the preceding full layer.
+    Window branch: softmax_attention over the layer's own cache Kw, Vw ([Hkv][B*W][d];
+    rows b*W:(b+1)*W hold the last W tokens of sequence b).
+    Output: O = w * O_sparse + (1 - w) * O_window with w = 1 / (1 + exp(-gate[b][h])).
+
+    Readings taken: one scalar gate per (sequence, query head), given as an input (the
+    pages fix the sigmoid, not the gate's producer); w multiplies the sparse branch and
+    1 - w the window branch. Returns O [B][Hq][d].
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    Kw = np.asarray(Kw, dtype=np.float64)
+    Vw = np.asarray(Vw, dtype=np.float64)
+    gate = np.asarray(gate, dtype=np.float64)
+    B, Hq, d = Q.shape
+    Hkv = K.shape[0]
+    G = Hq // Hkv
+    W = Kw.shape[1] // B
+    assert Kw.shape[1] == B * W and W >= 1
+    if scale is None:
+        scale = default_scale(d)
+    O = np.empty((B, Hq, d))
+    for b in range(B):
+        lo, hi = int(kv_offsets[b]), int(kv_offsets[b + 1])
+        for h in range(Hq):
+            g = h // G
+            o_s, _ = sparse_head(Q[b, h], K[g, lo:hi], V[g, lo:hi], S_in[(b, h)], scale)
+            o_w, _ = softmax_attention(Q[b, h], Kw[g, b * W:(b + 1) * W], Vw[g, b * W:(b + 1) * W], scale)
+            w = 1.0 / (1.0 + math.exp(-gate[b, h]))
+            O[b, h] = w * o_s + (1.0 - w) * o_w
+    return O
 
 
 def decode_step_f64(layers: List[Tuple[np.ndarray, np.ndarray, np.ndarray]],

@@ -379,3 +379,65 @@ def test_block_selection_reduces_to_token_selection_and_known_case():
     assert np.array_equal(orc.select_topk_blocks(ramp, 128, 64), np.arange(128, 256))
     spike = np.zeros(256); spike[5] = 9.0          # one high token lifts its whole block
     assert np.array_equal(orc.select_topk_blocks(spike, 64, 64), np.arange(0, 64))
+
+
+# ---- HySparse sparse layer: sigmoid-gated block-sparse and window branches
+
+def test_hysparse_single_row_branches_closed_form():
+    # |S| = 1 and W = 1: each branch's softmax has one term, so the branch outputs are
+    # the selected V row and the window V row; w = sigmoid(+-ln 3) = 3/4 and 1/4.
+    B, Hq, Hkv, d = 2, 4, 2, 4
+    offs = [0, 5, 12]
+    rng = np.random.default_rng(5)
+    Q = rng.standard_normal((B, Hq, d))
+    K = rng.standard_normal((Hkv, 12, d))
+    V = np.zeros((Hkv, 12, d))
+    V[0, 3] = [4, 0, -8, 2]          # sequence 0, KV head 0, local row 3
+    V[1, 1] = [8, 4, 0, -4]          # sequence 0, KV head 1, local row 1
+    V[0, 5 + 6] = [-4, 4, 4, 8]      # sequence 1, KV head 0, local row 6
+    V[1, 5 + 0] = [0, 0, 12, 4]      # sequence 1, KV head 1, local row 0
+    Kw = rng.standard_normal((Hkv, B, d))
+    Vw = np.array([[[0, 8, 4, -2], [4, 0, 0, 0]], [[-8, 0, 4, 4], [0, -4, 0, 8]]], dtype=float)
+    S = {(0, 0): [3], (0, 1): [3], (0, 2): [1], (0, 3): [1],
+         (1, 0): [6], (1, 1): [6], (1, 2): [0], (1, 3): [0]}
+    ln3 = math.log(3.0)
+    gate = np.array([[ln3, -ln3, ln3, -ln3], [-ln3, ln3, ln3, -ln3]])
+    O = orc.hysparse_sparse_layer(Q, K, V, offs, S, Kw, Vw, gate)
+    want = np.array([
+        [[3, 2, -5, 1], [1, 6, 1, -1], [4, 3, 1, -2], [-4, 1, 3, 2]],
+        [[2, 1, 1, 2], [-2, 3, 3, 6], [0, -1, 9, 5], [0, -3, 3, 7]],
+    ], dtype=float)
+    np.testing.assert_allclose(O, want, atol=1e-12, rtol=0)
+
+
+def test_hysparse_branches_agree_when_the_window_is_the_selection():
+    # When the window cache holds the sequence's last W rows of the shared cache and S
+    # selects exactly those rows, both branches are the same softmax, so the gate
+    # cannot change the output; saturated gates pick one branch.
+    B, Hq, Hkv, d, N, W = 2, 4, 2, 16, 40, 6
+    rng = np.random.default_rng(8)
+    Q = rng.standard_normal((B, Hq, d))
+    K = rng.standard_normal((Hkv, B * N, d))
+    V = rng.standard_normal((Hkv, B * N, d))
+    offs = [0, N, 2 * N]
+    Kw = np.concatenate([K[:, b * N + N - W:(b + 1) * N] for b in range(B)], axis=1)
+    Vw = np.concatenate([V[:, b * N + N - W:(b + 1) * N] for b in range(B)], axis=1)
+    S = {(b, h): np.arange(N - W, N) for b in range(B) for h in range(Hq)}
+    ref = None
+    for gate in (np.zeros((B, Hq)), rng.standard_normal((B, Hq)) * 4):
+        O = orc.hysparse_sparse_layer(Q, K, V, offs, S, Kw, Vw, gate)
+        if ref is None:
+            ref = O
+        np.testing.assert_allclose(O, ref, atol=1e-13, rtol=0)
+    S2 = {(b, h): rng.choice(N, 9, replace=False) for b in range(B) for h in range(Hq)}
+    hi = orc.hysparse_sparse_layer(Q, K, V, offs, S2, Kw, Vw, np.full((B, Hq), 60.0))
+    lo = orc.hysparse_sparse_layer(Q, K, V, offs, S2, Kw, Vw, np.full((B, Hq), -60.0))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            o_s, _ = orc.sparse_head(Q[b, h], K[g, b * N:(b + 1) * N], V[g, b * N:(b + 1) * N],
+                                     S2[(b, h)], 1 / math.sqrt(d))
+            o_w, _ = orc.softmax_attention(Q[b, h], K[g, b * N + N - W:(b + 1) * N],
+                                           V[g, b * N + N - W:(b + 1) * N], 1 / math.sqrt(d))
+            np.testing.assert_allclose(hi[b, h], o_s, atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lo[b, h], o_w, atol=1e-12, rtol=0)
