@@ -17,6 +17,7 @@ __all__ = [
     "LycheeDecodeError", "LycheeDecodeUnavailable", "library_path", "load_library",
     "Shape", "workspace_bytes", "topk_workspace_bytes", "Workspace", "TopkWorkspace",
     "retrieval_decode", "sparse_decode", "hybrid_layer", "topk_select",
+    "hysparse_workspace_bytes", "HySparseWorkspace", "hysparse_layer",
     "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "FLAG_SEPARATE_SELECT", "FLAG_BLOCK_SELECT", "flag_split_rows", "flag_waves", "EXPORTED_SYMBOLS",
 ]
 
@@ -29,7 +30,8 @@ _STATUS = {1: "invalid argument", 2: "unsupported shape", 3: "workspace missing 
            4: "HIP launch or copy failed", 5: "a bounded wait between workgroups gave up"}
 EXPORTED_SYMBOLS = ("ld_status_string", "ld_workspace_size", "ld_topk_workspace_size",
                     "ld_workspace_init", "ld_workspace_check", "ld_retrieval_decode",
-                    "ld_sparse_decode", "ld_hybrid_layer", "ld_topk_select")
+                    "ld_sparse_decode", "ld_hybrid_layer", "ld_topk_select",
+                    "ld_hysparse_workspace_size", "ld_hysparse_layer")
 
 
 def flag_split_rows(v: int) -> int:
@@ -114,6 +116,10 @@ def load_library():
     lib.ld_sparse_decode.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, u32, vp, sz, vp]
     lib.ld_hybrid_layer.restype = i32
     lib.ld_hybrid_layer.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, vp, vp, u32, vp, sz, vp]
+    lib.ld_hysparse_workspace_size.restype = sz
+    lib.ld_hysparse_workspace_size.argtypes = [sp, i32, i32]
+    lib.ld_hysparse_layer.restype = i32
+    lib.ld_hysparse_layer.argtypes = [sp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, u32, vp, sz, vp]
     lib.ld_topk_select.restype = i32
     lib.ld_topk_select.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp, sz, vp]
     _lib = lib
@@ -216,6 +222,20 @@ class Workspace(_WS):
         super().__init__(workspace_bytes(shape, k_max), device)
 
 
+def hysparse_workspace_bytes(shape: Shape, k_max: int, window_len: int) -> int:
+    n = load_library().ld_hysparse_workspace_size(ctypes.byref(shape), int(k_max), int(window_len))
+    if n == 0:
+        raise LycheeDecodeError(1, "ld_hysparse_workspace_size")
+    return int(n)
+
+
+class HySparseWorkspace(_WS):
+    """Zero-initialised device workspace for hysparse_layer."""
+
+    def __init__(self, shape: Shape, k_max: int, window_len: int, device="cuda"):
+        super().__init__(hysparse_workspace_bytes(shape, k_max, window_len), device)
+
+
 class TopkWorkspace(_WS):
     def __init__(self, rows: int, n: int, device="cuda"):
         super().__init__(topk_workspace_bytes(rows, n), device)
@@ -311,6 +331,36 @@ def hybrid_layer(q, k_cache, v_cache, retrieval_mask: int, k: int, s, *, s_out=N
         ctypes.byref(shape), int(retrieval_mask), q.data_ptr(), k_cache.data_ptr(),
         v_cache.data_ptr(), int(k), _ptr(s), _ptr(s_out), _ptr(s_indptr), _ptr(scores_out),
         out.data_ptr(), int(flags), ws.ptr(), ws.nbytes, _stream()), "ld_hybrid_layer")
+    return out
+
+
+def hysparse_layer(q, k_cache, v_cache, k: int, s_in, k_window, v_window, gate, *, s_indptr=None,
+                   out=None, flags: int = 0, workspace: Optional[HySparseWorkspace] = None,
+                   kv_indptr=None, seq_len=None, scale=None, block_table=None, page_size: int = 0,
+                   k_scale=None, v_scale=None):
+    """HySparse sparse layer: block-sparse attention over rows S of the shared cache,
+    window attention over the layer's own cache k_window/v_window [Hkv][B*W][d] (the
+    last W tokens of each sequence), combined as w*O_s + (1-w)*O_w, w = sigmoid(gate)
+    with gate fp32 [B][Hq]. Returns out."""
+    torch = _torch()
+    out = _prep(q, k_cache, v_cache, out, kv_indptr)
+    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size, k_scale, v_scale)
+    _req(s_in, torch.int32, "s_in"); _opt(s_indptr, torch.int64, "s_indptr")
+    _req(k_window, torch.bfloat16, "k_window"); _req(v_window, torch.bfloat16, "v_window")
+    _req(gate, torch.float32, "gate")
+    B, Hq = q.shape[0], q.shape[1]
+    if k_window.shape != v_window.shape or k_window.dim() != 3 or k_window.shape[0] != shape.num_kv_heads \
+            or k_window.shape[1] % B != 0 or k_window.shape[2] != q.shape[2]:
+        raise ValueError("k_window/v_window must be [Hkv][B*W][d] and match each other")
+    if gate.numel() != B * Hq:
+        raise ValueError("gate must hold B*Hq values")
+    W = k_window.shape[1] // B
+    ws = workspace or HySparseWorkspace(shape, k, W, q.device)
+    _check(load_library().ld_hysparse_layer(
+        ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), int(k),
+        s_in.data_ptr(), _ptr(s_indptr), k_window.data_ptr(), v_window.data_ptr(), int(W),
+        gate.data_ptr(), out.data_ptr(), int(flags), ws.ptr(), ws.nbytes, _stream()),
+        "ld_hysparse_layer")
     return out
 
 

@@ -423,6 +423,80 @@ size_t ld_workspace_size(const ld_shape* shape, int32_t k_max) {
   return layer_layout(shape).total;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The HySparse layer's workspace: the layer workspace of the shared cache, the two
+// branch outputs, and a layer workspace of the window cache.
+struct HysLayout {
+  ld_shape wshape;
+  size_t main, o_s, o_w, win, total;
+};
+bool hys_layout(const ld_shape* s, int32_t window_len, HysLayout* H) {
+  ld_status why;
+  if (!shape_ok(s, &why) || window_len < 1 || window_len > 4096) return false;
+  H->wshape = ld_shape{};
+  H->wshape.batch = s->batch; H->wshape.num_q_heads = s->num_q_heads;
+  H->wshape.num_kv_heads = s->num_kv_heads; H->wshape.head_dim = s->head_dim;
+  H->wshape.seq_len = window_len;
+  H->wshape.total_tokens = (int64_t)s->batch * window_len;
+  H->wshape.softmax_scale = s->softmax_scale;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  const size_t obytes = (size_t)s->batch * s->num_q_heads * s->head_dim * 2;
+  H->main = take(layer_layout(s).total);
+  H->o_s = take(obytes);
+  H->o_w = take(obytes);
+  H->win = take(layer_layout(&H->wshape).total);
+  H->total = o;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ld_hysparse_workspace_size(const ld_shape* shape, int32_t k_max, int32_t window_len) {
+  HysLayout H;
+  if (!shape || k_max < 1 || k_max > shape->seq_len || !hys_layout(shape, window_len, &H)) return 0;
+  return H.total;
+}
+
+ld_status ld_hysparse_layer(const ld_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, int32_t k, const int32_t* s_in,
+                            const int64_t* s_indptr, const void* k_window,
+                            const void* v_window, int32_t window_len, const float* gate,
+                            void* out, uint32_t flags, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  HysLayout H;
+  ld_status why;
+  if (!shape) return LD_ERR_INVALID_ARGUMENT;
+  if (!shape_ok(shape, &why)) return why;
+  if (!hys_layout(shape, window_len, &H)) return LD_ERR_INVALID_ARGUMENT;
+  // every check of the window branch is made here, before the first launch
+  if (!s_in || !k_window || !v_window || !gate || !out || ((uintptr_t)gate & 3u)) return LD_ERR_INVALID_ARGUMENT;
+  if (!aligned16(k_window) || !aligned16(v_window)) return LD_ERR_INVALID_ARGUMENT;
+  if (flags & ~(uint32_t)LD_FLAG_S_CHAINED) return LD_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < H.total || ((uintptr_t)workspace & 15u)) return LD_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const int Hq = shape->num_q_heads;
+  const uint64_t all = (Hq == 64) ? ~0ull : ((1ull << Hq) - 1ull);
+  void* o_s = ws + H.o_s;
+  void* o_w = ws + H.o_w;
+  // block-sparse branch on the shared cache, then the window branch on the own cache
+  ld_status st = run_layer(shape, all, 0ull, q, k_cache, v_cache, k, s_in, nullptr, s_indptr, nullptr, o_s,
+                           flags, false, ws + H.main, H.o_s - H.main, stream);
+  if (st != LD_OK) return st;
+  st = run_layer(&H.wshape, all, all, q, k_window, v_window, 1, nullptr, nullptr, nullptr, nullptr, o_w, 0u,
+                 false, ws + H.win, H.total - H.win, stream);
+  if (st != LD_OK) return st;
+  return launch_gate_fuse(static_cast<const uint16_t*>(o_s), static_cast<const uint16_t*>(o_w), gate,
+                          static_cast<uint16_t*>(out), shape->batch * Hq, shape->head_dim, stream) == hipSuccess
+             ? LD_OK
+             : LD_ERR_HIP;
+}
+
 size_t ld_topk_workspace_size(int32_t rows, int32_t n) {
   if (rows < 1 || n < 1 || n > kMaxSeq) return 0;
   return sel_layout(rows, n).total;

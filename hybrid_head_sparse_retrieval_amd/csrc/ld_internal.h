@@ -155,6 +155,9 @@ hipError_t launch_bitmap_build(const BitmapParams& p, int rows, hipStream_t st);
 hipError_t launch_copy_rows(const CopyParams& p, int rows, hipStream_t st);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t st);
 hipError_t launch_block_max(const BlockParams& p, int rows, hipStream_t st);
+// out = w * a + (1 - w) * c per element, w = sigmoid(gate[row]); a, c, out bf16 [rows][d]
+hipError_t launch_gate_fuse(const uint16_t* a, const uint16_t* c, const float* gate, uint16_t* out, int rows,
+                            int d, hipStream_t st);
 hipError_t launch_block_expand(const BlockParams& p, int rows, hipStream_t st);
 
 }  // namespace ld

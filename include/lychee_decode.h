@@ -174,6 +174,25 @@ ld_status ld_sparse_decode(const ld_shape* shape, uint64_t head_mask,
                            void* out, uint32_t flags,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* HySparse sparse layer (HySparse: A Hybrid Sparse Attention Architecture, section 3).
+   Every query head h of sequence b combines two branches through a sigmoid gate:
+     O_s = softmax(q K[S]^T * scale) V[S] over S row (b,h) of s_in, on k_cache/v_cache
+           (the full layer's cache, shared; as ld_sparse_decode, paged or E4M3 allowed),
+     O_w = softmax(q Kw^T * scale) Vw over the layer's own window cache: the last
+           window_len tokens of the sequence, bf16 [Hkv][B*window_len][d] in
+           k_window/v_window (rows of sequence b from b*window_len),
+     O   = w * O_s + (1 - w) * O_w with w = 1 / (1 + exp(-gate[b][h])), gate device
+           fp32 [B][Hq]; O_s and O_w are rounded to bf16 before they are combined.
+   window_len in 1..4096. The workspace must hold ld_hysparse_workspace_size() bytes
+   (zeroed once, as for the other entry points). flags: LD_FLAG_S_CHAINED. */
+size_t ld_hysparse_workspace_size(const ld_shape* shape, int32_t k_max, int32_t window_len);
+ld_status ld_hysparse_layer(const ld_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, int32_t k, const int32_t* s_in,
+                            const int64_t* s_indptr, const void* k_window,
+                            const void* v_window, int32_t window_len, const float* gate,
+                            void* out, uint32_t flags, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
 /* One full layer of the recurrence (method steps 3 and 4) for all Hq heads:
    retrieval heads (bits of retrieval_mask) attend to all rows and write their
    argsTopK rows into s_out; sparse heads attend to S row (b,h) of s_in and S^{l+1} =

@@ -112,6 +112,31 @@ def test_invalid_arguments_are_rejected(lib):
     assert _hyb(lib, _shape(softmax_scale=float("inf"))) == INV
 
 
+def test_hysparse_workspace_and_arguments(lib):
+    s = _shape()
+    n = lib.ld_hysparse_workspace_size(ctypes.byref(s), 9830, 128)
+    assert n > lib.ld_workspace_size(ctypes.byref(s), 9830) and n % 256 == 0
+    for w in (0, -1, 4097):
+        assert lib.ld_hysparse_workspace_size(ctypes.byref(s), 9830, w) == 0
+    assert lib.ld_hysparse_workspace_size(ctypes.byref(_shape(head_dim=96)), 10, 128) == 0
+
+    def hys(shape, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, kk=10, s_in=FAKE, s_indptr=None, kw=FAKE, vw=FAKE, w=128,
+                 gate=FAKE, out=FAKE, flags=0, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return lib.ld_hysparse_layer(ctypes.byref(shape), a["q"], a["k"], a["v"], a["kk"], a["s_in"],
+                                     a["s_indptr"], a["kw"], a["vw"], a["w"], a["gate"], a["out"],
+                                     a["flags"], a["ws"], a["wsb"], None)
+    INV, UNS, WSE = 1, 2, 3
+    assert hys(s, w=0) == INV and hys(s, w=4097) == INV
+    assert hys(s, kw=None) == INV and hys(s, gate=None) == INV and hys(s, s_in=None) == INV
+    assert hys(s, vw=FAKE + 8) == INV                       # misaligned window cache
+    assert hys(s, gate=FAKE + 2) == INV
+    assert hys(s, flags=8) == INV                           # block selection is the full layer's
+    assert hys(s, ws=None) == WSE and hys(s, wsb=1 << 20) == WSE
+    assert hys(_shape(head_dim=80)) == UNS
+
+
 def test_topk_invalid_arguments(lib):
     f = lib.ld_topk_select
     assert f(None, 1, 10, 10, 3, FAKE, None, FAKE, 1 << 30, None) == 1
