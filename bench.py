@@ -49,6 +49,10 @@ def parse():
                     help="KV cache format: bf16, or 8-bit E4M3 codes (unit scales)")
     ap.add_argument("--block-select", action="store_true",
                     help="retrieval heads keep 64-token blocks by block maximum (HySparse form)")
+    ap.add_argument("--swa-window", type=int, default=0,
+                    help="HySparse: sparse layers add a gated sliding-window branch over their own "
+                         "cache of this many tokens (workloads whose sparse layers share the first "
+                         "layer's cache)")
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged KV: rows per page (power of two, 16..4096); 0 = contiguous")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -286,19 +290,41 @@ def main():
             log("[bench] --block-select needs one sequence with k and N multiples of 64")
             sys.exit(2)
         split_flag |= ld.FLAG_BLOCK_SELECT
+    windows = None
+    W = args.swa_window
+    if W:
+        if not w.shared_kv_from_layer0 or w.ragged_csr or not 1 <= W <= 4096 \
+                or any(w.retrieval_masks[1:]):
+            log("[bench] --swa-window needs a workload whose later layers are sparse layers on the "
+                "first layer's cache, dense S and 1 <= W <= 4096")
+            sys.exit(2)
+        windows = [None]
+        gen = torch.Generator(device="cpu")
+        for l in range(1, L):
+            gen.manual_seed(wl.stream_seed("window", w.name, l))
+            kw = torch.randn((w.num_kv_heads, w.batch * W, d), generator=gen).to(torch.bfloat16).to(dev)
+            vw = torch.randn((w.num_kv_heads, w.batch * W, d), generator=gen).to(torch.bfloat16).to(dev)
+            gate = torch.randn((w.batch, w.num_q_heads), generator=gen).to(dev)
+            windows.append((kw, vw, gate))
+        log(f"[bench] sparse layers add a {W}-token window branch and a sigmoid gate")
     step = DecodeStep(w.batch, w.num_q_heads, w.num_kv_heads, d, w.seq_lens, w.k_per_seq,
-                      w.retrieval_masks, csr=w.ragged_csr, device=dev, split_flag=split_flag)
+                      w.retrieval_masks, csr=w.ragged_csr, device=dev, split_flag=split_flag,
+                      window_len=W)
 
     # ---- accounting pass (untimed): S before every layer -> algorithmic bytes
     attn_bytes, total_bytes = [], []
     for l in range(L):
         S_in = step.s_rows() if l > 0 else None
         q, kc, vc = inputs[l][:3]
+        win = windows[l] if windows else None
         if len(inputs[l]) > 3:
-            step.layer(l, q, kc, vc, block_table=inputs[l][3], page_size=inputs[l][4])
+            step.layer(l, q, kc, vc, block_table=inputs[l][3], page_size=inputs[l][4], window=win)
         else:
-            step.layer(l, q, kc, vc)
+            step.layer(l, q, kc, vc, window=win)
         a, t = layer_bytes(w, l, S_in, d, kv_elem) if l > 0 else layer_bytes(w, l, None, d, kv_elem)
+        if win is not None:   # the window cache and the gate
+            extra = 2 * w.num_kv_heads * w.batch * W * d * 2 + w.batch * w.num_q_heads * 4
+            a, t = a + extra, t + extra
         attn_bytes.append(a)
         total_bytes.append(t)
     torch.cuda.synchronize()
@@ -307,14 +333,14 @@ def main():
 
     # ---- warmup + timed steps (events between steps, on the launch stream)
     for _ in range(args.warmup):
-        step.run(inputs)
+        step.run(inputs, windows=windows)
     torch.cuda.synchronize()
     sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     sev[0].record()
     for i in range(args.steps):
-        step.run(inputs)
+        step.run(inputs, windows=windows)
         sev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -331,10 +357,10 @@ def main():
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap):
-            step.run(inputs)           # eager pass on the capture stream first
+            step.run(inputs, windows=windows)           # eager pass on the capture stream first
             torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=cap):
-                step.run(inputs)
+                step.run(inputs, windows=windows)
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
         for _ in range(args.warmup):
@@ -363,7 +389,7 @@ def main():
         # the first pass is a warm-up (its first layer has been seen to take tens of ms)
         pre.record()
         torch.cuda._sleep(4_000_000)
-        step.run(inputs, events=evs)
+        step.run(inputs, events=evs, windows=windows)
         torch.cuda.synchronize()
         span = np.array([evs[l].elapsed_time(evs[l + 1]) for l in range(L)]) * 1e3
         if args.layers_detail:
@@ -437,7 +463,8 @@ def main():
                    "split_rows": "auto" if args.split == 0 else 256 << (args.split - 1),
                    "kv_layout": f"paged {args.page_size}-row pages" if args.page_size else "contiguous",
                    "kv_format": args.kv,
-                   "selection": "64-token blocks" if args.block_select else "tokens"},
+                   "selection": "64-token blocks" if args.block_select else "tokens",
+                   "swa_window": W or None},
         "roofline": roof,
         # sparse layers that read the first layer's cache again may be served from the
         # 256 MB last-level cache, so their GB/s can exceed the HBM figure
@@ -447,7 +474,9 @@ def main():
     }
 
     # ---- CPU oracle baseline on a bounded sample of the same workload
-    if not args.no_cpu_baseline:
+    if W and not args.no_cpu_baseline:
+        log("[bench] no CPU baseline with --swa-window (the oracle leg times the plain layers)")
+    elif not args.no_cpu_baseline:
         oracle_inputs = logical if args.kv == "bf16" else q8
         result["cpu_baseline"] = cpu_baseline(w, oracle_inputs, total_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)

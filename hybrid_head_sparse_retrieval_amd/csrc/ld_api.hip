@@ -225,7 +225,8 @@ int uniform_split(int N, int64_t groups_total, int64_t capacity) {
 ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, const void* q,
                     const void* kc, const void* vc, int32_t k, const int32_t* s_in,
                     int32_t* s_out, const int64_t* s_indptr, float* scores_out, void* out,
-                    uint32_t flags, bool want_topk, void* ws, size_t ws_bytes, hipStream_t st) {
+                    uint32_t flags, bool want_topk, void* ws, size_t ws_bytes, hipStream_t st,
+                    const float* gate = nullptr, const float* o_win = nullptr) {
   ld_status why;
   if (!shape_ok(shape, &why)) return why;
   const int B = shape->batch, Hq = shape->num_q_heads, Hkv = shape->num_kv_heads;
@@ -287,6 +288,8 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   ap.kv_fp8 = shape->kv_dtype == 1 ? 1 : 0;
   ap.v_scale = ap.kv_fp8 ? shape->v_scale : 1.f;
   ap.out = static_cast<uint16_t*>(out);
+  ap.gate = gate;
+  ap.o_win = o_win;
   ap.kv_indptr = shape->kv_indptr;
   ap.kv_head_stride = T * D;
   ap.total_tokens = T;
@@ -427,28 +430,18 @@ size_t ld_workspace_size(const ld_shape* shape, int32_t k_max) {
 
 namespace {
 
-// The HySparse layer's workspace: the layer workspace of the shared cache, the two
-// branch outputs, and a layer workspace of the window cache.
+// The HySparse layer's workspace: a layer workspace of the shared cache, then the
+// window branch's fp32 output.
 struct HysLayout {
-  ld_shape wshape;
-  size_t main, o_s, o_w, win, total;
+  size_t main, o_w, total;
 };
 bool hys_layout(const ld_shape* s, int32_t window_len, HysLayout* H) {
   ld_status why;
   if (!shape_ok(s, &why) || window_len < 1 || window_len > 4096) return false;
-  H->wshape = ld_shape{};
-  H->wshape.batch = s->batch; H->wshape.num_q_heads = s->num_q_heads;
-  H->wshape.num_kv_heads = s->num_kv_heads; H->wshape.head_dim = s->head_dim;
-  H->wshape.seq_len = window_len;
-  H->wshape.total_tokens = (int64_t)s->batch * window_len;
-  H->wshape.softmax_scale = s->softmax_scale;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
-  const size_t obytes = (size_t)s->batch * s->num_q_heads * s->head_dim * 2;
   H->main = take(layer_layout(s).total);
-  H->o_s = take(obytes);
-  H->o_w = take(obytes);
-  H->win = take(layer_layout(&H->wshape).total);
+  H->o_w = take((size_t)s->batch * s->num_q_heads * s->head_dim * 4);
   H->total = o;
   return true;
 }
@@ -474,27 +467,32 @@ ld_status ld_hysparse_layer(const ld_shape* shape, const void* q, const void* k_
   if (!shape) return LD_ERR_INVALID_ARGUMENT;
   if (!shape_ok(shape, &why)) return why;
   if (!hys_layout(shape, window_len, &H)) return LD_ERR_INVALID_ARGUMENT;
-  // every check of the window branch is made here, before the first launch
-  if (!s_in || !k_window || !v_window || !gate || !out || ((uintptr_t)gate & 3u)) return LD_ERR_INVALID_ARGUMENT;
+  // every check is made before the first launch
+  if (!q || !aligned16(q) || !s_in || ((uintptr_t)s_in & 3u) || !k_window || !v_window || !gate || !out ||
+      ((uintptr_t)gate & 3u))
+    return LD_ERR_INVALID_ARGUMENT;
+  if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return LD_ERR_INVALID_ARGUMENT;
   if (!aligned16(k_window) || !aligned16(v_window)) return LD_ERR_INVALID_ARGUMENT;
   if (flags & ~(uint32_t)LD_FLAG_S_CHAINED) return LD_ERR_INVALID_ARGUMENT;
+  if (k < 1 || k > shape->seq_len) return LD_ERR_INVALID_ARGUMENT;
   if (!workspace || workspace_bytes < H.total || ((uintptr_t)workspace & 15u)) return LD_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   const int Hq = shape->num_q_heads;
   const uint64_t all = (Hq == 64) ? ~0ull : ((1ull << Hq) - 1ull);
-  void* o_s = ws + H.o_s;
-  void* o_w = ws + H.o_w;
-  // block-sparse branch on the shared cache, then the window branch on the own cache
-  ld_status st = run_layer(shape, all, 0ull, q, k_cache, v_cache, k, s_in, nullptr, s_indptr, nullptr, o_s,
-                           flags, false, ws + H.main, H.o_s - H.main, stream);
-  if (st != LD_OK) return st;
-  st = run_layer(&H.wshape, all, all, q, k_window, v_window, 1, nullptr, nullptr, nullptr, nullptr, o_w, 0u,
-                 false, ws + H.win, H.total - H.win, stream);
-  if (st != LD_OK) return st;
-  return launch_gate_fuse(static_cast<const uint16_t*>(o_s), static_cast<const uint16_t*>(o_w), gate,
-                          static_cast<uint16_t*>(out), shape->batch * Hq, shape->head_dim, stream) == hipSuccess
-             ? LD_OK
-             : LD_ERR_HIP;
+  float* o_w = reinterpret_cast<float*>(ws + H.o_w);
+  // window branch first; the block-sparse launch mixes it in when it writes O
+  WindowParams wp{};
+  wp.q = static_cast<const uint16_t*>(q);
+  wp.kw = static_cast<const uint16_t*>(k_window);
+  wp.vw = static_cast<const uint16_t*>(v_window);
+  wp.o = o_w;
+  wp.B = shape->batch; wp.Hq = Hq; wp.Hkv = shape->num_kv_heads; wp.D = shape->head_dim;
+  wp.W = window_len;
+  wp.scale = shape->softmax_scale > 0.f ? shape->softmax_scale : 1.0f / std::sqrt((float)shape->head_dim);
+  if (launch_window(wp, stream) != hipSuccess) return LD_ERR_HIP;
+  return run_layer(shape, all, 0ull, q, k_cache, v_cache, k, s_in, nullptr, s_indptr, nullptr, out, flags,
+                   false, ws + H.main, H.o_w - H.main, stream, gate, o_w);
 }
 
 size_t ld_topk_workspace_size(int32_t rows, int32_t n) {

@@ -102,6 +102,22 @@ struct AttnSmem {
   } u;
 };
 
+// Four output columns of row `row` (b * Hq + h): o * il as bf16, or, with the HySparse
+// gate set, w * o * il + (1 - w) * o_win with w = sigmoid(gate[row]).
+template <int D>
+__device__ __forceinline__ void store_o(const AttnParams& p, int row, int d0, float4 o, float il) {
+  float x = o.x * il, y = o.y * il, z = o.z * il, t = o.w * il;
+  if (p.gate) {
+    const float w = 1.f / (1.f + expf(-p.gate[row]));
+    const float4 c = *reinterpret_cast<const float4*>(p.o_win + (size_t)row * D + d0);
+    x = fmaf(w, x - c.x, c.x); y = fmaf(w, y - c.y, c.y);
+    z = fmaf(w, z - c.z, c.z); t = fmaf(w, t - c.w, c.w);
+  }
+  ushort4 r;
+  r.x = f32_to_bf16(x); r.y = f32_to_bf16(y); r.z = f32_to_bf16(z); r.w = f32_to_bf16(t);
+  *reinterpret_cast<ushort4*>(p.out + (size_t)row * D + d0) = r;
+}
+
 // Merge `cnt` split partials (max in log2 units, sum, unnormalised output) of every
 // active head of the group, taken from src_ml/src_acc at positions s0.. of each head's
 // row of `stride` partials. FINAL: write O = sum acc_p w_p / sum l_p w_p as bf16.
@@ -189,11 +205,7 @@ __device__ __forceinline__ void merge_splits(AttnSmem<D, G, NW>& sm, const AttnP
       o.x += y.x; o.y += y.y; o.z += y.z; o.w += y.w;
     }
     if (FINAL) {
-      const float il = sm.u.cmb.inv_l[j];
-      ushort4 r;
-      r.x = f32_to_bf16(o.x * il); r.y = f32_to_bf16(o.y * il);
-      r.z = f32_to_bf16(o.z * il); r.w = f32_to_bf16(o.w * il);
-      *reinterpret_cast<ushort4*>(p.out + (size_t)(hq0 + j) * D + d0) = r;
+      store_o<D>(p, hq0 + j, d0, o, sm.u.cmb.inv_l[j]);
     } else {
       const size_t us = (size_t)(hq0 + j) * p.P1 + upos;
       st_dev4_b(rsrc(dst_acc + (size_t)hq0 * p.P1 * D), ((j * p.P1 + upos) * D + d0) * 4, o);
@@ -249,13 +261,7 @@ __device__ __forceinline__ void merge_columns(const AttnParams& p, uint32_t act,
     }
     L = wave_sum_f(L);
     o.x = wave_sum_f(o.x); o.y = wave_sum_f(o.y); o.z = wave_sum_f(o.z); o.w = wave_sum_f(o.w);
-    if (lane == 0) {
-      const float il = p.v_scale / L;
-      ushort4 r;
-      r.x = f32_to_bf16(o.x * il); r.y = f32_to_bf16(o.y * il);
-      r.z = f32_to_bf16(o.z * il); r.w = f32_to_bf16(o.w * il);
-      *reinterpret_cast<ushort4*>(p.out + (size_t)(hq0 + j) * D + d0) = r;
-    }
+    if (lane == 0) store_o<D>(p, hq0 + j, d0, o, p.v_scale / L);
   }
 }
 

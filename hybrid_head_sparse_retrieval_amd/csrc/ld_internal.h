@@ -38,6 +38,10 @@ struct AttnParams {
   int kv_fp8;
   float v_scale;          // factor on O (the V dequantisation scale; 1 for bf16)
   uint16_t* out;          // bf16 [B][Hq][D]
+  // HySparse gate (or null): O is written as w * O + (1 - w) * o_win[row] with
+  // w = sigmoid(gate[row]), row = b * Hq + h; o_win fp32 [B*Hq][D]
+  const float* gate;
+  const float* o_win;
   const int64_t* kv_indptr;
   int64_t kv_head_stride; // T*D elements
   int64_t total_tokens;   // T
@@ -155,9 +159,17 @@ hipError_t launch_bitmap_build(const BitmapParams& p, int rows, hipStream_t st);
 hipError_t launch_copy_rows(const CopyParams& p, int rows, hipStream_t st);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t st);
 hipError_t launch_block_max(const BlockParams& p, int rows, hipStream_t st);
-// out = w * a + (1 - w) * c per element, w = sigmoid(gate[row]); a, c, out bf16 [rows][d]
-hipError_t launch_gate_fuse(const uint16_t* a, const uint16_t* c, const float* gate, uint16_t* out, int rows,
-                            int d, hipStream_t st);
+// Sliding-window branch of a HySparse sparse layer: o[b*Hq+h] = softmax(q kw^T * scale) vw
+// over the W rows of sequence b in kw/vw [Hkv][B*W][D] (bf16), fp32 out.
+struct WindowParams {
+  const uint16_t* q;
+  const uint16_t* kw;
+  const uint16_t* vw;
+  float* o;
+  int B, Hq, Hkv, D, W;
+  float scale;
+};
+hipError_t launch_window(const WindowParams& p, hipStream_t st);
 hipError_t launch_block_expand(const BlockParams& p, int rows, hipStream_t st);
 
 }  // namespace ld

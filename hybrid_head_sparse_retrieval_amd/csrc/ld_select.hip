@@ -654,25 +654,7 @@ __global__ __launch_bounds__(kThreads) void k_block_expand(const BlockParams p) 
   }
 }
 
-// HySparse gate: out = w * a + (1 - w) * c with w = sigmoid(gate) per row.
-__global__ __launch_bounds__(kThreads) void k_gate_fuse(const uint16_t* a, const uint16_t* c, const float* gate,
-                                                        uint16_t* out, int rows, int d) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= (int64_t)rows * d) return;
-  const float w = 1.f / (1.f + expf(-gate[i / d]));
-  const float x = bf_lo(a[i]), y = bf_lo(c[i]);
-  out[i] = f32_to_bf16(w * x + (1.f - w) * y);
-}
-
 }  // namespace
-
-hipError_t launch_gate_fuse(const uint16_t* a, const uint16_t* c, const float* gate, uint16_t* out, int rows,
-                            int d, hipStream_t st) {
-  const int64_t n = (int64_t)rows * d;
-  hipLaunchKernelGGL(k_gate_fuse, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, st, a, c,
-                     gate, out, rows, d);
-  return hipGetLastError();
-}
 
 hipError_t launch_block_max(const BlockParams& p, int rows, hipStream_t st) {
   const int64_t waves = (int64_t)rows * p.nblk;

@@ -5,7 +5,9 @@ seeds S; every later layer reads S^{l} and writes S^{l+1} in place (retrieval ro
 replaced, sparse rows untouched). After layer 0 the workspace's membership bitmaps
 track S, so later layers pass LD_FLAG_S_CHAINED and never re-read S.
 HySparse-style stacks (section 3 of the HySparse page) pass the full layer's K/V
-for the sparse layers; nothing else changes.
+for the sparse layers; with window_len > 0 a sparse layer given its own window cache
+and gate runs the gated block-sparse + sliding-window layer instead, on a workspace
+whose leading part is the full layer's, so the chained bitmaps carry over.
 """
 from __future__ import annotations
 
@@ -13,7 +15,8 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (FLAG_S_CHAINED, Workspace, hybrid_layer, make_shape)
+from . import (FLAG_S_CHAINED, HySparseWorkspace, Workspace, hybrid_layer, hysparse_layer,
+               make_shape)
 
 
 class DecodeStep:
@@ -21,7 +24,7 @@ class DecodeStep:
 
     def __init__(self, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  seq_lens: Sequence[int], k_per_seq: Sequence[int], retrieval_masks: Sequence[int],
-                 csr: bool = False, device="cuda", split_flag: int = 0):
+                 csr: bool = False, device="cuda", split_flag: int = 0, window_len: int = 0):
         import torch
         self.torch = torch
         self.B, self.Hq, self.Hkv, self.d = batch, num_q_heads, num_kv_heads, head_dim
@@ -35,6 +38,7 @@ class DecodeStep:
         self.L = len(self.masks)
         self.device = device
         self.split_flag = split_flag
+        self.window_len = int(window_len)
         ragged = len(set(self.seq_lens)) > 1 or csr
         offs = np.concatenate([[0], np.cumsum(self.seq_lens)]).astype(np.int64)
         self.kv_offsets = offs
@@ -59,32 +63,47 @@ class DecodeStep:
     def _ws(self, q, kc):
         if self.workspace is None:
             shape = make_shape(q, kc, self.kv_indptr, self.N)
-            self.workspace = Workspace(shape, self.k_arg, self.device)
+            if self.window_len:
+                self.workspace = HySparseWorkspace(shape, self.k_arg, self.window_len, self.device)
+            else:
+                self.workspace = Workspace(shape, self.k_arg, self.device)
         return self.workspace
 
     def layer(self, l: int, q, kc, vc, extra_flags: int = 0, scores_out=None, block_table=None,
-              page_size: int = 0):
+              page_size: int = 0, window=None):
         """Launch layer l (asynchronous). Paged KV: kc/vc are page pools and block_table
-        maps each sequence's pages."""
+        maps each sequence's pages. window = (k_window, v_window, gate) runs a layer
+        without retrieval heads as the gated block-sparse + window layer."""
         flags = (FLAG_S_CHAINED if l > 0 else 0) | self.split_flag | extra_flags
+        if window is not None:
+            if l == 0 or self.masks[l] or not self.window_len:
+                raise ValueError("window branches need a sparse layer after the first and window_len")
+            if self.s_indptr is not None:
+                raise ValueError("window branches are set up for dense S")
+            return hysparse_layer(q, kc, vc, self.k_arg, self.S, window[0], window[1], window[2],
+                                  out=self.outs[l], flags=FLAG_S_CHAINED, workspace=self._ws(q, kc),
+                                  kv_indptr=self.kv_indptr, seq_len=self.N, block_table=block_table,
+                                  page_size=page_size)
         return hybrid_layer(q, kc, vc, self.masks[l], self.k_arg, self.S if l > 0 else None,
                             s_out=self.S, s_indptr=self.s_indptr, scores_out=scores_out,
                             out=self.outs[l], flags=flags, workspace=self._ws(q, kc),
                             kv_indptr=self.kv_indptr, seq_len=self.N, block_table=block_table,
                             page_size=page_size)
 
-    def run(self, layers: List, events: Optional[list] = None):
+    def run(self, layers: List, events: Optional[list] = None, windows: Optional[list] = None):
         """One decode step. layers[l] = (q, k, v) device tensors, or (q, k_pool, v_pool,
-        block_table, page_size) for paged KV. If `events` is a list of L+1
-        torch.cuda.Event, they are recorded between layers."""
+        block_table, page_size) for paged KV. windows[l]: (k_window, v_window, gate) or
+        None per layer. If `events` is a list of L+1 torch.cuda.Event, they are
+        recorded between layers."""
         for l in range(self.L):
             if events is not None:
                 events[l].record()
             q, kc, vc = layers[l][:3]
+            win = windows[l] if windows is not None else None
             if len(layers[l]) > 3:
-                self.layer(l, q, kc, vc, block_table=layers[l][3], page_size=layers[l][4])
+                self.layer(l, q, kc, vc, block_table=layers[l][3], page_size=layers[l][4], window=win)
             else:
-                self.layer(l, q, kc, vc)
+                self.layer(l, q, kc, vc, window=win)
         if events is not None:
             events[self.L].record()
         return self.outs

@@ -182,9 +182,14 @@ ld_status ld_sparse_decode(const ld_shape* shape, uint64_t head_mask,
            window_len tokens of the sequence, bf16 [Hkv][B*window_len][d] in
            k_window/v_window (rows of sequence b from b*window_len),
      O   = w * O_s + (1 - w) * O_w with w = 1 / (1 + exp(-gate[b][h])), gate device
-           fp32 [B][Hq]; O_s and O_w are rounded to bf16 before they are combined.
+           fp32 [B][Hq]; both branches stay fp32 until O is rounded to bf16.
+   The window branch runs first (a small launch); the block-sparse attention launch
+   mixes it in where it writes O.
    window_len in 1..4096. The workspace must hold ld_hysparse_workspace_size() bytes
-   (zeroed once, as for the other entry points). flags: LD_FLAG_S_CHAINED. */
+   (zeroed once, as for the other entry points). It starts with a layer workspace of
+   `shape`, so the same buffer serves ld_hybrid_layer for the full layer, and a sparse
+   layer passing LD_FLAG_S_CHAINED (the only flag taken) reuses the bitmaps that the full
+   layer's selection left there. Errors are found before the first launch. */
 size_t ld_hysparse_workspace_size(const ld_shape* shape, int32_t k_max, int32_t window_len);
 ld_status ld_hysparse_layer(const ld_shape* shape, const void* q, const void* k_cache,
                             const void* v_cache, int32_t k, const int32_t* s_in,

@@ -107,3 +107,38 @@ def test_hysparse_layer_rejects_bad_arguments():
     ws = ld.HySparseWorkspace(shape, 64, 16, dev)
     with pytest.raises(ld.LycheeDecodeError, match="invalid argument"):
         ld.hysparse_layer(qd, kd, vd, 64, S, kw, kw, gate, flags=ld.FLAG_BLOCK_SELECT, workspace=ws)
+
+
+def test_full_layer_then_hysparse_layers_share_one_workspace():
+    """A HySparse block through the step runner: the full layer (all heads retrieval,
+    64-token block selection) writes S and the bitmaps into the leading part of the
+    HySparse workspace; the sparse layers chain from them and add their window
+    branches. Every sparse layer matches the oracle on the full layer's S."""
+    from hybrid_head_sparse_retrieval_amd.step import DecodeStep
+    ld = _ld()
+    dev = "cuda"
+    B, Hq, Hkv, d, N, k, W, L = 1, 16, 4, 128, 8192, 2048, 128, 3
+    step = DecodeStep(B, Hq, Hkv, d, [N], [k], [(1 << Hq) - 1] + [0] * (L - 1), device=dev,
+                      split_flag=ld.FLAG_BLOCK_SELECT, window_len=W)
+    q0, kc, vc = wl.random_qkv(B, Hq, Hkv, d, N, 1000)
+    kd, vd = kc.to(dev), vc.to(dev)
+    layers, windows, host = [(q0.to(dev), kd, vd)], [None], []
+    for l in range(1, L):
+        q, _, _ = wl.random_qkv(B, Hq, Hkv, d, 1, 1000 + l)
+        _, kw, vw = wl.random_qkv(B, Hq, Hkv, d, B * W, 1100 + l)
+        gate = torch.randn((B, Hq), generator=torch.Generator().manual_seed(wl.stream_seed("gate", 1000, l)))
+        layers.append((q.to(dev), kd, vd))
+        windows.append((kw.to(dev), vw.to(dev), gate.to(dev)))
+        host.append((q, kw, vw, gate))
+    outs = step.run(layers, windows=windows)
+    torch.cuda.synchronize()
+    S = step.s_rows()
+    for l in range(1, L):
+        q, kw, vw, gate = host[l - 1]
+        O_ref = orc.hysparse_sparse_layer(gh.bf16_tensor_to_f64(q), gh.bf16_tensor_to_f64(kc),
+                                          gh.bf16_tensor_to_f64(vc), [0, N], S, gh.bf16_tensor_to_f64(kw),
+                                          gh.bf16_tensor_to_f64(vw), gate.numpy().astype(np.float64))
+        gh.check_outputs(outs[l], O_ref, [(0, h) for h in range(Hq)], f"hysparse block layer {l}")
+    for h in range(Hq):
+        assert S[(0, h)].size == k and np.all(S[(0, h)] % 64 == np.arange(k) % 64)
+    step.workspace.check()
