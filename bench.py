@@ -405,19 +405,22 @@ def main():
 
     # ---- roofline of the attention launch. Each layer call is one attention launch
     # (merge and selection inside it), except layers with several retrieval heads in one
-    # KV group, which add a selection launch. The per-layer spans above come from HIP
-    # events recorded between the layers of full steps on the launch stream, so they
-    # also hold the gap between launches: the figure is a lower bound of the kernel's.
+    # KV group, which add a selection launch. The launch duration is the timed steps'
+    # mean (HIP events around every step on the launch stream) over the step's L
+    # attention launches: the step also holds those selection launches and the gaps
+    # between launches, so the figure is a lower bound of the kernel's rate. (The
+    # per-layer spans above carry the cost of an event between every two layers, a few
+    # us each, and are reported for the layer mix only.)
     roof = None
     if not args.no_kernel_pass:
-        avg_us = float(np.mean(per_layer))
+        avg_us = ms_step * 1e3 / L
         avg_bytes = float(np.mean(attn_bytes))
         achieved = avg_bytes / (avg_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(w.name),
                 "kernel": "k_attention<128,4,4>" if d == 128 and w.group_size == 4 else "k_attention",
                 "avg_launch_us": round(avg_us, 2), "avg_bytes_per_launch": int(avg_bytes),
-                "launches_timed": L * reps}
+                "launches_timed": L * args.steps}
         log(f"[bench] attention launch: avg {avg_us:.1f} us, {achieved:.0f} GB/s "
             f"({achieved / HBM_PEAK_GBS * 100:.1f}% of peak)")
 
