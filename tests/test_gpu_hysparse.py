@@ -25,6 +25,8 @@ def _ld():
     ([8192, 8192], 32, 8, 128, 2048, 128, 971),
     ([3000, 777, 2048], 4, 4, 64, 300, 1, 972),
     ([5000, 1400], 8, 1, 128, 1000, 300, 973),
+    ([6000], 8, 2, 128, 1500, 4096, 974),       # the largest window
+    ([2500, 2500], 4, 2, 64, 800, 200, 975),
 ])
 def test_hysparse_layer_matches_oracle(case):
     lens, Hq, Hkv, d, k, W, seed = case
@@ -142,3 +144,42 @@ def test_full_layer_then_hysparse_layers_share_one_workspace():
     for h in range(Hq):
         assert S[(0, h)].size == k and np.all(S[(0, h)] % 64 == np.arange(k) % 64)
     step.workspace.check()
+
+
+def test_hysparse_layer_on_paged_e4m3_shared_cache():
+    """The block-sparse branch reads a paged pool of E4M3 codes with per-tensor scales
+    (the full layer's cache); the window cache stays bf16. Output vs the oracle on the
+    decoded values."""
+    ld = _ld()
+    dev = "cuda"
+    B, Hq, Hkv, d, N, k, W, page = 2, 8, 2, 128, 4096, 1200, 128, 64
+    k_scale, v_scale = 0.75, 1.5
+    q, kc, vc = wl.random_qkv(B, Hq, Hkv, d, B * N, 990)
+    _, kw, vw = wl.random_qkv(B, Hq, Hkv, d, B * W, 991)
+    k8 = kc.float().to(torch.float8_e4m3fn).view(torch.uint8)
+    v8 = vc.float().to(torch.float8_e4m3fn).view(torch.uint8)
+    # pool of pages in a seeded order; block_table[b][i] = pool page of page i of sequence b
+    npp = N // page
+    perm = np.random.default_rng(wl.stream_seed("pages", 990)).permutation(B * npp)
+    table = perm.reshape(B, npp).astype(np.int32)
+    kp = torch.empty_like(k8)
+    vp = torch.empty_like(v8)
+    for b in range(B):
+        for i in range(npp):
+            src = slice(b * N + i * page, b * N + (i + 1) * page)
+            dst = slice(int(table[b, i]) * page, (int(table[b, i]) + 1) * page)
+            kp[:, dst] = k8[:, src]
+            vp[:, dst] = v8[:, src]
+    S_h = np.stack([wl.random_sorted_sets(wl.stream_seed("S", 990, b), N, k, Hq) for b in range(B)])
+    gate = torch.randn((B, Hq), generator=torch.Generator().manual_seed(wl.stream_seed("gate", 990))) * 2.0
+    bt = torch.as_tensor(table, device=dev)
+    out = ld.hysparse_layer(q.to(dev), kp.to(dev), vp.to(dev), k, torch.as_tensor(S_h, device=dev), kw.to(dev),
+                            vw.to(dev), gate.to(dev), seq_len=N, block_table=bt, page_size=page,
+                            k_scale=k_scale, v_scale=v_scale)
+    torch.cuda.synchronize()
+    K = k_scale * orc.fp8_e4m3_to_f64(k8.numpy())
+    V = v_scale * orc.fp8_e4m3_to_f64(v8.numpy())
+    O_ref = orc.hysparse_sparse_layer(gh.bf16_tensor_to_f64(q), K, V, [0, N, 2 * N], gh.s_rows_to_dict(S_h, B, Hq),
+                                      gh.bf16_tensor_to_f64(kw), gh.bf16_tensor_to_f64(vw),
+                                      gate.numpy().astype(np.float64))
+    gh.check_outputs(out, O_ref, [(b, h) for b in range(B) for h in range(Hq)], "hysparse paged e4m3")
