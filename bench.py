@@ -416,9 +416,14 @@ def main():
         avg_us = ms_step * 1e3 / L
         avg_bytes = float(np.mean(attn_bytes))
         achieved = avg_bytes / (avg_us * 1e-6) / 1e9
+        # the counters are taken on the default configuration (bf16 contiguous KV, token
+        # selection, automatic launch shape); other configurations report none
+        default_cfg = (args.kv == "bf16" and not args.page_size and not args.block_select and not W
+                       and not args.split and not args.waves)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(w.name),
-                "kernel": "k_attention<128,4,4>" if d == 128 and w.group_size == 4 else "k_attention",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic(w.name) if default_cfg else None,
+                "kernel": f"k_attention (d={d}, G={w.group_size}, {'E4M3' if args.kv == 'fp8' else 'bf16'} KV)",
                 "avg_launch_us": round(avg_us, 2), "avg_bytes_per_launch": int(avg_bytes),
                 "launches_timed": L * args.steps}
         log(f"[bench] attention launch: avg {avg_us:.1f} us, {achieved:.0f} GB/s "
