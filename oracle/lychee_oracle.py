@@ -16,7 +16,9 @@ Sources (cited by page title and passage):
         Selection and KV Cache Sharing", section 3 Methodology (sparse layers reuse
         the full layer's token selection and KV cache).
   [TSA] "Token Sparse Attention: Efficient Long-Context Inference" (skill page),
-        Step 3 (the budget is clamped to the sequence length: k = min(k, seq_len)).
+        Step 3 (the budget is clamped to the sequence length: k = min(k, seq_len)),
+        "Core Concept" and Steps 2-3 (compress to the top-k tokens, dense attention
+        among them, scatter back to the sequence).
 
 Readings taken where the pages are silent (each is listed in the design notes):
   * Head type and the token set S are per *query* head; under grouped KV heads,
@@ -46,6 +48,7 @@ __all__ = [
     "hybrid_layer_fp8",
     "select_topk_blocks",
     "hysparse_sparse_layer",
+    "tsa_attention",
     "softmax_attention",
     "select_topk",
     "select_topk_f32",
@@ -279,6 +282,49 @@ def hysparse_sparse_layer(Q, K, V, kv_offsets, S_in, Kw, Vw, gate, scale=None):
             w = 1.0 / (1.0 + math.exp(-gate[b, h]))
             O[b, h] = w * o_s + (1.0 - w) * o_w
     return O
+
+
+def tsa_attention(Q, K, V, scores, k: int, scale=None, causal: bool = False, zero_fill: bool = True):
+    """Token Sparse Attention, compress -> dense -> scatter ([TSA] "Core Concept" and
+    Steps 2-3), for every (sequence b, query head h) of a prefill of T tokens.
+
+    Q: [Hq][B*T][d]; K, V: [Hkv][B*T][d] (query head h reads KV head h // (Hq // Hkv));
+    scores: [B][Hq][T] per-token importance of each head.
+    Compress: I = argsTopK(scores[b][h], min(k, T)) (select_topk order, ascending).
+    Dense: among the selected tokens only, O_i = softmax_j(q_{I_i} . k_{I_j} * scale) v_{I_j};
+    causal: only keys with I_j <= I_i.
+    Scatter: row I_i of the output gets O_i; every other row is zero (zero_fill) or NaN
+    (left to the caller).
+
+    Readings taken: the scores are an input (the page's scoring formulas are not legible);
+    no mask unless causal is asked for (the page's listing applies none).
+    Returns (out [Hq][B*T][d], idx {(b, h): ascending int64 indices}).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    sc = np.asarray(scores)
+    Hq, BT, d = Q.shape
+    Hkv = K.shape[0]
+    G = Hq // Hkv
+    B, _, T = sc.shape
+    assert BT == B * T
+    if scale is None:
+        scale = default_scale(d)
+    kk = min(int(k), T)                          # [TSA] Step 3 clamp
+    out = np.zeros((Hq, BT, d)) if zero_fill else np.full((Hq, BT, d), np.nan)
+    idx = {}
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            I = select_topk(sc[b, h], kk)
+            idx[(b, h)] = I
+            rows = b * T + I
+            Ks, Vs = K[g, rows], V[g, rows]
+            for i in range(kk):
+                keys = np.arange(kk) if not causal else np.arange(i + 1)   # I ascending: I_j <= I_i iff j <= i
+                out[h, rows[i]], _ = softmax_attention(Q[h, rows[i]], Ks[keys], Vs[keys], scale)
+    return out, idx
 
 
 def decode_step_f64(layers: List[Tuple[np.ndarray, np.ndarray, np.ndarray]],

@@ -441,3 +441,53 @@ def test_hysparse_branches_agree_when_the_window_is_the_selection():
                                            V[g, b * N + N - W:(b + 1) * N], 1 / math.sqrt(d))
             np.testing.assert_allclose(hi[b, h], o_s, atol=1e-12, rtol=0)
             np.testing.assert_allclose(lo[b, h], o_w, atol=1e-12, rtol=0)
+
+
+# ---- Token Sparse Attention: compress -> dense -> scatter
+
+def test_tsa_full_budget_reduces_to_library_attention():
+    # k = T keeps every token, so the layer is plain attention of the sequence (with the
+    # query head's KV head repeated), which torch's scaled_dot_product_attention computes
+    torch = pytest.importorskip("torch")
+    B, Hq, Hkv, T, d = 2, 4, 2, 9, 8
+    rng = np.random.default_rng(31)
+    Q = rng.standard_normal((Hq, B * T, d))
+    K = rng.standard_normal((Hkv, B * T, d))
+    V = rng.standard_normal((Hkv, B * T, d))
+    sc = rng.standard_normal((B, Hq, T))
+    for causal in (False, True):
+        out, idx = orc.tsa_attention(Q, K, V, sc, T, causal=causal)
+        q = torch.tensor(Q).reshape(Hq, B, T, d).permute(1, 0, 2, 3)
+        kk = torch.tensor(K).reshape(Hkv, B, T, d).permute(1, 0, 2, 3).repeat_interleave(Hq // Hkv, dim=1)
+        vv = torch.tensor(V).reshape(Hkv, B, T, d).permute(1, 0, 2, 3).repeat_interleave(Hq // Hkv, dim=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, is_causal=causal)
+        ref = ref.permute(1, 0, 2, 3).reshape(Hq, B * T, d).numpy()
+        np.testing.assert_allclose(out, ref, atol=1e-12, rtol=0)
+        assert all(np.array_equal(i, np.arange(T)) for i in idx.values())
+
+
+def test_tsa_scatter_and_equal_keys_closed_form():
+    # equal keys make every softmax uniform: a selected row gets the mean of the V rows it
+    # may attend to, placed at its own position; unselected rows stay zero (or NaN when
+    # the caller keeps them)
+    B, Hq, Hkv, T, d = 1, 2, 1, 6, 3
+    Q = np.random.default_rng(2).standard_normal((Hq, T, d))
+    K = np.ones((Hkv, T, d))
+    V = np.arange(T * d, dtype=float).reshape(1, T, d) * np.array([1.0, -2.0, 0.5])
+    sc = np.array([[[0.1, 5.0, -1.0, 5.0, 2.0, 0.0],        # head 0 keeps 1, 3, 4 (the tie 1/3 both in)
+                    [9.0, 1.0, 1.0, 1.0, 1.0, 8.0]]])       # head 1 keeps 0, 5 and index 1 (ties -> lower)
+    out, idx = orc.tsa_attention(Q, K, V, sc, 3)
+    assert idx[(0, 0)].tolist() == [1, 3, 4] and idx[(0, 1)].tolist() == [0, 1, 5]
+    for h, I in ((0, [1, 3, 4]), (1, [0, 1, 5])):
+        for t in range(T):
+            want = V[0, I].mean(axis=0) if t in I else np.zeros(d)
+            np.testing.assert_allclose(out[h, t], want, atol=1e-12, rtol=0)
+    out_c, _ = orc.tsa_attention(Q, K, V, sc, 3, causal=True)
+    for h, I in ((0, [1, 3, 4]), (1, [0, 1, 5])):
+        for i, t in enumerate(I):
+            np.testing.assert_allclose(out_c[h, t], V[0, I[:i + 1]].mean(axis=0), atol=1e-12, rtol=0)
+    kept, _ = orc.tsa_attention(Q, K, V, sc, 3, zero_fill=False)
+    assert np.isnan(kept[0, [0, 2, 5]]).all() and not np.isnan(kept[0, [1, 3, 4]]).any()
+    # a budget above T is clamped to T
+    full, idx2 = orc.tsa_attention(Q, K, V, sc, 50)
+    assert all(i.size == T for i in idx2.values())
