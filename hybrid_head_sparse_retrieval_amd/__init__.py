@@ -18,6 +18,7 @@ __all__ = [
     "Shape", "workspace_bytes", "topk_workspace_bytes", "Workspace", "TopkWorkspace",
     "retrieval_decode", "sparse_decode", "hybrid_layer", "topk_select",
     "hysparse_workspace_bytes", "HySparseWorkspace", "hysparse_layer",
+    "tsa_workspace_bytes", "TsaWorkspace", "tsa_attention", "TSA_CAUSAL", "TSA_ZERO_FILL",
     "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "FLAG_SEPARATE_SELECT", "FLAG_BLOCK_SELECT", "flag_split_rows", "flag_waves", "EXPORTED_SYMBOLS",
 ]
 
@@ -26,12 +27,15 @@ FLAG_SKIP_TOPK = 1
 FLAG_S_CHAINED = 2
 FLAG_SEPARATE_SELECT = 4
 FLAG_BLOCK_SELECT = 8
+TSA_CAUSAL = 1
+TSA_ZERO_FILL = 2
 _STATUS = {1: "invalid argument", 2: "unsupported shape", 3: "workspace missing or too small",
            4: "HIP launch or copy failed", 5: "a bounded wait between workgroups gave up"}
 EXPORTED_SYMBOLS = ("ld_status_string", "ld_workspace_size", "ld_topk_workspace_size",
                     "ld_workspace_init", "ld_workspace_check", "ld_retrieval_decode",
                     "ld_sparse_decode", "ld_hybrid_layer", "ld_topk_select",
-                    "ld_hysparse_workspace_size", "ld_hysparse_layer")
+                    "ld_hysparse_workspace_size", "ld_hysparse_layer",
+                    "ld_tsa_workspace_size", "ld_tsa_attention")
 
 
 def flag_split_rows(v: int) -> int:
@@ -120,6 +124,10 @@ def load_library():
     lib.ld_hysparse_workspace_size.argtypes = [sp, i32, i32]
     lib.ld_hysparse_layer.restype = i32
     lib.ld_hysparse_layer.argtypes = [sp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, u32, vp, sz, vp]
+    lib.ld_tsa_workspace_size.restype = sz
+    lib.ld_tsa_workspace_size.argtypes = [sp]
+    lib.ld_tsa_attention.restype = i32
+    lib.ld_tsa_attention.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, u32, vp, sz, vp]
     lib.ld_topk_select.restype = i32
     lib.ld_topk_select.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp, sz, vp]
     _lib = lib
@@ -234,6 +242,33 @@ class HySparseWorkspace(_WS):
 
     def __init__(self, shape: Shape, k_max: int, window_len: int, device="cuda"):
         super().__init__(hysparse_workspace_bytes(shape, k_max, window_len), device)
+
+
+def tsa_shape(q, k_cache, batch: int, scale=None) -> Shape:
+    """ld_shape of a prefill: q [Hq][B*T][d], k_cache [Hkv][B*T][d], B = batch."""
+    Hq, BT, d = (int(x) for x in q.shape)
+    if BT % batch:
+        raise ValueError("q rows are not a multiple of the batch")
+    s = Shape()
+    s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim = int(batch), Hq, int(k_cache.shape[0]), d
+    s.seq_len = BT // batch
+    s.total_tokens = BT
+    s.softmax_scale = float(scale) if scale is not None else 0.0
+    return s
+
+
+def tsa_workspace_bytes(shape: Shape) -> int:
+    n = load_library().ld_tsa_workspace_size(ctypes.byref(shape))
+    if n == 0:
+        raise LycheeDecodeError(1, "ld_tsa_workspace_size")
+    return int(n)
+
+
+class TsaWorkspace(_WS):
+    """Zero-initialised device workspace for tsa_attention."""
+
+    def __init__(self, shape: Shape, device="cuda"):
+        super().__init__(tsa_workspace_bytes(shape), device)
 
 
 class TopkWorkspace(_WS):
@@ -362,6 +397,40 @@ def hysparse_layer(q, k_cache, v_cache, k: int, s_in, k_window, v_window, gate, 
         gate.data_ptr(), out.data_ptr(), int(flags), ws.ptr(), ws.nbytes, _stream()),
         "ld_hysparse_layer")
     return out
+
+
+def tsa_attention(q, k_cache, v_cache, scores, k: int, *, idx_out=None, out=None, causal: bool = False,
+                  zero_fill: bool = True, workspace: Optional[TsaWorkspace] = None, scale=None):
+    """Token Sparse Attention over a prefill: per (sequence, head) the top-k tokens of
+    `scores` [B][Hq][T] (fp32), dense attention among them, scattered to their rows of
+    `out` [Hq][B*T][d]. q [Hq][B*T][d], k_cache / v_cache [Hkv][B*T][d] (bf16).
+    Returns (out, idx_out [B][Hq][min(k, T)] int32 ascending)."""
+    torch = _torch()
+    _req(q, torch.bfloat16, "q"); _req(k_cache, torch.bfloat16, "k_cache"); _req(v_cache, torch.bfloat16, "v_cache")
+    _req(scores, torch.float32, "scores")
+    if scores.dim() != 3 or q.dim() != 3 or k_cache.shape != v_cache.shape:
+        raise ValueError("scores must be [B][Hq][T]; q, k_cache, v_cache 3-D with equal K/V shapes")
+    B, Hq, T = (int(x) for x in scores.shape)
+    if q.shape[0] != Hq or q.shape[1] != B * T or k_cache.shape[1] != B * T or k_cache.shape[2] != q.shape[2]:
+        raise ValueError("q must be [Hq][B*T][d] and k_cache [Hkv][B*T][d] for scores [B][Hq][T]")
+    shape = tsa_shape(q, k_cache, B, scale)
+    kk = min(int(k), T)
+    if idx_out is None:
+        idx_out = torch.empty((B, Hq, kk), dtype=torch.int32, device=q.device)
+    _req(idx_out, torch.int32, "idx_out")
+    if idx_out.numel() != B * Hq * kk:
+        raise ValueError("idx_out must hold B*Hq*min(k, T) entries")
+    if out is None:
+        out = torch.empty_like(q)
+    _req(out, torch.bfloat16, "out")
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    flags = (TSA_CAUSAL if causal else 0) | (TSA_ZERO_FILL if zero_fill else 0)
+    ws = workspace or TsaWorkspace(shape, q.device)
+    _check(load_library().ld_tsa_attention(
+        ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), scores.data_ptr(), int(k),
+        idx_out.data_ptr(), out.data_ptr(), int(flags), ws.ptr(), ws.nbytes, _stream()), "ld_tsa_attention")
+    return out, idx_out
 
 
 def topk_select(scores, k: int, *, idx_out=None, val_out=None,

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblychee_decode.so")
-SOURCES = ["ld_api.hip", "ld_attention.hip", "ld_select.hip", "ld_window.hip"]
+SOURCES = ["ld_api.hip", "ld_attention.hip", "ld_select.hip", "ld_window.hip", "ld_tsa.hip"]
 
 ARCH = "gfx950"
 COMMON = [

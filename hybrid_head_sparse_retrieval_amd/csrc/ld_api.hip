@@ -495,6 +495,59 @@ ld_status ld_hysparse_layer(const ld_shape* shape, const void* q, const void* k_
                    false, ws + H.main, H.o_w - H.main, stream, gate, o_w);
 }
 
+size_t ld_tsa_workspace_size(const ld_shape* shape) {
+  ld_status why;
+  if (!shape || !shape_ok(shape, &why) || shape->kv_indptr || shape->page_size || shape->kv_dtype) return 0;
+  return sel_layout(shape->batch * shape->num_q_heads, shape->seq_len).total;
+}
+
+ld_status ld_tsa_attention(const ld_shape* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const float* scores, int32_t k, int32_t* idx_out,
+                           void* out, uint32_t flags, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  ld_status why;
+  if (!shape) return LD_ERR_INVALID_ARGUMENT;
+  if (!shape_ok(shape, &why)) return why;
+  // one contiguous bf16 layout of the prefill: no ragged batch, paging or 8-bit codes
+  if (shape->kv_indptr || shape->page_size || shape->kv_dtype) return LD_ERR_UNSUPPORTED;
+  const int B = shape->batch, Hq = shape->num_q_heads, D = shape->head_dim, T = shape->seq_len;
+  if (shape->total_tokens != 0 && shape->total_tokens != (int64_t)B * T) return LD_ERR_INVALID_ARGUMENT;
+  if (!q || !k_cache || !v_cache || !scores || !idx_out || !out || k < 1) return LD_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      ((uintptr_t)scores & 3u) || ((uintptr_t)idx_out & 3u))
+    return LD_ERR_INVALID_ARGUMENT;
+  if (flags & ~(uint32_t)(LD_TSA_CAUSAL | LD_TSA_ZERO_FILL)) return LD_ERR_INVALID_ARGUMENT;
+  const int rows = B * Hq;
+  const SelLayout L = sel_layout(rows, T);
+  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 15u)) return LD_ERR_WORKSPACE;
+  const int kk = std::min(k, T);
+  // 1. rows that receive no output are zero when asked for
+  if ((flags & LD_TSA_ZERO_FILL) &&
+      launch_zero(out, (size_t)Hq * B * T * D * 2, stream) != hipSuccess)
+    return LD_ERR_HIP;
+  // 2. compress: argsTopK of every head's scores
+  SelParams sp{};
+  sp.mode = 0;
+  sp.nrows = rows;
+  sp.Ch = (T + kSelChunk - 1) / kSelChunk;
+  sp.scores = scores; sp.row_stride = T; sp.n = T; sp.k = kk;
+  sp.idx_out = idx_out; sp.val_out = nullptr;
+  fill_sel(sp, L.sel, workspace);
+  if (launch_select(sp, stream, true) != hipSuccess) return LD_ERR_HIP;
+  // 3. dense attention among the selected tokens, scattered to their rows
+  TsaParams tp{};
+  tp.q = static_cast<const uint16_t*>(q);
+  tp.k = static_cast<const uint16_t*>(k_cache);
+  tp.v = static_cast<const uint16_t*>(v_cache);
+  tp.idx = idx_out;
+  tp.out = static_cast<uint16_t*>(out);
+  tp.B = B; tp.Hq = Hq; tp.Hkv = shape->num_kv_heads; tp.D = D; tp.T = T; tp.kk = kk;
+  tp.qtiles = (kk + tsa_queries_per_block() - 1) / tsa_queries_per_block();
+  tp.scale = shape->softmax_scale > 0.f ? shape->softmax_scale : 1.0f / std::sqrt((float)D);
+  tp.causal = (flags & LD_TSA_CAUSAL) ? 1 : 0;
+  return launch_tsa(tp, stream) == hipSuccess ? LD_OK : LD_ERR_HIP;
+}
+
 size_t ld_topk_workspace_size(int32_t rows, int32_t n) {
   if (rows < 1 || n < 1 || n > kMaxSeq) return 0;
   return sel_layout(rows, n).total;

@@ -170,6 +170,23 @@ struct WindowParams {
   float scale;
 };
 hipError_t launch_window(const WindowParams& p, hipStream_t st);
+
+// Token Sparse Attention dense stage: for row b * Hq + h with selected positions
+// idx[row][0..kk) (ascending), out[h][b*T + idx[i]] = softmax_j(q_i . k_j * scale) v_j
+// over the selected rows (j <= i when causal). q, out [Hq][B*T][D]; k, v [Hkv][B*T][D].
+struct TsaParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* idx;
+  uint16_t* out;
+  int B, Hq, Hkv, D, T, kk;
+  int qtiles;             // ceil(kk / tsa_queries_per_block())
+  float scale;
+  int causal;
+};
+hipError_t launch_tsa(const TsaParams& p, hipStream_t st);
+int tsa_queries_per_block();
 hipError_t launch_block_expand(const BlockParams& p, int rows, hipStream_t st);
 
 }  // namespace ld

@@ -198,6 +198,29 @@ ld_status ld_hysparse_layer(const ld_shape* shape, const void* q, const void* k_
                             void* out, uint32_t flags, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* Token Sparse Attention, compress -> dense -> scatter ("Token Sparse Attention:
+   Efficient Long-Context Inference", Core Concept and Steps 2-3), over a prefill of T
+   tokens per sequence. For every sequence b and query head h (KV head h / (Hq/Hkv)):
+     I   = argsTopK(scores[b*Hq + h][0..T), min(k, T)), the order of ld_topk_select,
+           written ascending to idx_out[b*Hq + h][0..min(k,T)) (int32, device);
+     O_i = softmax_j(q_{I_i} . k_{I_j} * scale) v_{I_j} over the selected tokens only
+           (flags & LD_TSA_CAUSAL: only I_j <= I_i);
+     out row I_i of (h, b) = O_i (bf16); the other rows are zero with LD_TSA_ZERO_FILL,
+           else left as the caller wrote them (the page keeps the residual there).
+   Layouts (device, bf16, contiguous): q and out [Hq][B*T][d]; k_cache and v_cache
+   [Hkv][B*T][d]; scores fp32 [B*Hq][T]. shape: batch, num_q_heads, num_kv_heads,
+   head_dim (64 or 128), seq_len = T (1..2^21), softmax_scale (0 = 1/sqrt(d)),
+   total_tokens 0 or B*T; kv_indptr, paging and kv_dtype must be unset
+   (LD_ERR_UNSUPPORTED otherwise). The workspace holds ld_tsa_workspace_size() bytes,
+   zeroed once. Asynchronous on `stream`; errors are found before the first launch. */
+#define LD_TSA_CAUSAL 1u
+#define LD_TSA_ZERO_FILL 2u
+size_t ld_tsa_workspace_size(const ld_shape* shape);
+ld_status ld_tsa_attention(const ld_shape* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const float* scores, int32_t k, int32_t* idx_out,
+                           void* out, uint32_t flags, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /* One full layer of the recurrence (method steps 3 and 4) for all Hq heads:
    retrieval heads (bits of retrieval_mask) attend to all rows and write their
    argsTopK rows into s_out; sparse heads attend to S row (b,h) of s_in and S^{l+1} =

@@ -137,6 +137,29 @@ def test_hysparse_workspace_and_arguments(lib):
     assert hys(_shape(head_dim=80)) == UNS
 
 
+def test_tsa_workspace_and_arguments(lib):
+    s = _shape(seq_len=4096, total_tokens=4096)
+    assert lib.ld_tsa_workspace_size(ctypes.byref(s)) >= lib.ld_topk_workspace_size(32, 4096) > 0
+    for bad in (dict(head_dim=96), dict(kv_dtype=1, k_scale=1.0, v_scale=1.0),
+                dict(page_size=64, pages_per_seq=512, block_table=FAKE, total_tokens=1 << 20)):
+        assert lib.ld_tsa_workspace_size(ctypes.byref(_shape(**bad))) == 0, bad
+
+    def tsa(shape, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, sc=FAKE, kk=64, idx=FAKE, out=FAKE, flags=0, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return lib.ld_tsa_attention(ctypes.byref(shape), a["q"], a["k"], a["v"], a["sc"], a["kk"], a["idx"],
+                                    a["out"], a["flags"], a["ws"], a["wsb"], None)
+    INV, UNS, WSE = 1, 2, 3
+    assert tsa(s, q=None) == INV and tsa(s, sc=None) == INV and tsa(s, idx=None) == INV
+    assert tsa(s, kk=0) == INV
+    assert tsa(s, k=FAKE + 4) == INV and tsa(s, sc=FAKE + 2) == INV
+    assert tsa(s, flags=4) == INV
+    assert tsa(_shape(seq_len=4096, total_tokens=4095)) == INV
+    assert tsa(s, ws=None) == WSE and tsa(s, wsb=1024) == WSE
+    assert tsa(_shape(seq_len=4096, total_tokens=4096, head_dim=80)) == UNS
+    assert tsa(_shape(kv_dtype=1, k_scale=1.0, v_scale=1.0)) == UNS
+
+
 def test_topk_invalid_arguments(lib):
     f = lib.ld_topk_select
     assert f(None, 1, 10, 10, 3, FAKE, None, FAKE, 1 << 30, None) == 1

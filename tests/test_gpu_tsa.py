@@ -1,0 +1,86 @@
+"""Token Sparse Attention (compress -> dense -> scatter) through the C ABI: the selected
+positions equal the oracle's selection on the same fp32 scores bit for bit, every
+selected row of the output matches the oracle, and every other row is zero (zero fill)
+or keeps what the caller wrote."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import lychee_oracle as orc
+from tests import gpu_helpers as gh
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _ld():
+    import hybrid_head_sparse_retrieval_amd as ld
+    ld.load_library()
+    return ld
+
+
+def _inputs(B, Hq, Hkv, d, T, seed):
+    g = torch.Generator().manual_seed(wl.stream_seed("tsa", seed))
+    q = torch.randn((Hq, B * T, d), generator=g).to(torch.bfloat16)
+    k = torch.randn((Hkv, B * T, d), generator=g).to(torch.bfloat16)
+    v = torch.randn((Hkv, B * T, d), generator=g).to(torch.bfloat16)
+    sc = torch.randn((B, Hq, T), generator=g)
+    return q, k, v, sc
+
+
+def _check(ld, B, Hq, Hkv, d, T, k, causal, seed, zero_fill=True):
+    dev = "cuda"
+    q, kc, vc, sc = _inputs(B, Hq, Hkv, d, T, seed)
+    sentinel = torch.full_like(q, 7.0)
+    out, idx = ld.tsa_attention(q.to(dev), kc.to(dev), vc.to(dev), sc.to(dev), k, out=sentinel.to(dev),
+                                causal=causal, zero_fill=zero_fill)
+    torch.cuda.synchronize()
+    ref, ref_idx = orc.tsa_attention(gh.bf16_tensor_to_f64(q), gh.bf16_tensor_to_f64(kc),
+                                     gh.bf16_tensor_to_f64(vc), sc.numpy(), k, causal=causal,
+                                     zero_fill=zero_fill)
+    idx = idx.cpu().numpy()
+    got = gh.bf16_tensor_to_f64(out.cpu())
+    kk = min(k, T)
+    for b in range(B):
+        for h in range(Hq):
+            assert np.array_equal(idx[b, h], ref_idx[(b, h)]), f"selection (b={b}, h={h})"
+            rows = b * T + ref_idx[(b, h)]
+            # selected rows: the attention output, to the usual tolerances
+            err = np.abs(got[h, rows] - ref[h, rows])
+            rel = np.linalg.norm(got[h, rows] - ref[h, rows]) / np.linalg.norm(ref[h, rows])
+            assert err.max() <= gh.MAX_ABS and rel <= gh.REL_L2, f"(b={b}, h={h}): {err.max():.3e} {rel:.3e}"
+            others = np.setdiff1d(np.arange(b * T, (b + 1) * T), rows)
+            want = 0.0 if zero_fill else 7.0
+            assert np.all(got[h, others] == want), f"unselected rows (b={b}, h={h})"
+    assert idx.shape == (B, Hq, kk)
+
+
+@pytest.mark.parametrize("case", [
+    # (B, Hq, Hkv, d, T, k, causal)
+    (1, 4, 2, 128, 2000, 300, False),
+    (1, 4, 2, 128, 2000, 300, True),
+    (2, 8, 2, 64, 1000, 130, True),
+    (2, 4, 4, 64, 1000, 130, False),
+    (1, 2, 1, 128, 96, 96, True),        # every token kept
+    (1, 2, 1, 128, 50, 80, False),       # budget above T: clamped
+    (1, 2, 2, 128, 700, 1, True),        # one token
+    (1, 8, 2, 128, 20000, 1024, True),   # the page's budget range, several tiles and query blocks
+])
+def test_tsa_matches_oracle(case):
+    B, Hq, Hkv, d, T, k, causal = case
+    _check(_ld(), B, Hq, Hkv, d, T, k, causal, seed=B * 100000 + T * 7 + k + int(causal))
+
+
+def test_tsa_keeps_unselected_rows_without_zero_fill():
+    _check(_ld(), 1, 4, 2, 128, 1500, 200, True, seed=77, zero_fill=False)
+
+
+def test_tsa_ties_go_to_lower_positions():
+    """Constant scores: every head keeps the first k positions."""
+    ld = _ld()
+    dev = "cuda"
+    q, kc, vc, _ = _inputs(1, 4, 2, 128, 1000, 5)
+    sc = torch.zeros((1, 4, 1000))
+    _, idx = ld.tsa_attention(q.to(dev), kc.to(dev), vc.to(dev), sc.to(dev), 100, causal=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy()[0], np.tile(np.arange(100), (4, 1)))
