@@ -248,6 +248,9 @@ def main():
     ld.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload in TSA_WORKLOADS:
+        tsa_bench(args, torch, ld, dev)
+        return
     w = wl.get_workload(args.workload)
     L, d = w.layers, w.head_dim
     log(f"[bench] workload {w.name}: B={w.batch} L={L} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
@@ -488,6 +491,130 @@ def main():
         oracle_inputs = logical if args.kv == "bf16" else q8
         result["cpu_baseline"] = cpu_baseline(w, oracle_inputs, total_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+# Token Sparse Attention over a prefill (the page's budget range of 512-1024 kept tokens
+# per head, at its 128K context), Llama-3-8B head layout, causal, with the residual form
+# of the scatter (unselected rows keep what the caller wrote, so no zero fill).
+TSA_WORKLOADS = {
+    "tsa_llama3_8b_128k": dict(B=1, Hq=32, Hkv=8, d=128, T=131072, k=1024, causal=True),
+}
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, vendor figure
+
+
+def tsa_bench(args, torch, ld, dev):
+    """Time the Token Sparse Attention layer call (selection + dense stage) and the
+    dense stage alone (sets given), report the dense kernel against the matrix-core
+    roofline, and time the oracle on a few heads."""
+    import workloads as wl
+    c = TSA_WORKLOADS[args.workload]
+    B, Hq, Hkv, d, T, k, causal = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"], c["k"], c["causal"]
+    kk = min(k, T)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.stream_seed("tsa", args.workload))
+    q = torch.randn((Hq, B * T, d), generator=gen, device=dev).to(torch.bfloat16)
+    kc = torch.randn((Hkv, B * T, d), generator=gen, device=dev).to(torch.bfloat16)
+    vc = torch.randn((Hkv, B * T, d), generator=gen, device=dev).to(torch.bfloat16)
+    scores = torch.randn((B, Hq, T), generator=gen, device=dev)
+    out = torch.zeros_like(q)
+    idx = torch.empty((B, Hq, kk), dtype=torch.int32, device=dev)
+    ws = ld.TsaWorkspace(ld.tsa_shape(q, kc, B), k, dev)
+    log(f"[bench] {args.workload}: B={B} Hq={Hq} Hkv={Hkv} d={d} T={T} k={k} causal={causal}")
+
+    def layer():
+        ld.tsa_attention(q, kc, vc, scores, k, idx_out=idx, out=out, causal=causal, zero_fill=False, workspace=ws)
+
+    def dense():
+        ld.tsa_attention(q, kc, vc, None, k, idx_out=idx, out=out, causal=causal, zero_fill=False, workspace=ws,
+                         given_idx=True, batch=B)
+
+    def timed(fn, n):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3   # us
+
+    us_layer = timed(layer, args.steps)
+    us_dense = timed(dense, args.steps)
+    # matrix work of the dense stage: 2 d flops for q.k and 2 d for p.v per allowed pair
+    pairs = B * Hq * (kk * (kk + 1) // 2 if causal else kk * kk)
+    flops = 4.0 * d * pairs
+    tflops = flops / (us_dense * 1e-6) / 1e12
+    # bytes the layer must move: the scores, the kept rows of q, k, v (k, v once per KV
+    # group's union of kept rows) and the scattered output rows
+    idx_h = idx.cpu().numpy()
+    G = Hq // Hkv
+    kv_rows = sum(np.unique(idx_h[b, g * G:(g + 1) * G]).size for b in range(B) for g in range(Hkv))
+    layer_bytes_ = scores.numel() * 4 + Hq * B * kk * d * 2 * 2 + kv_rows * d * 2 * 2 + idx_h.size * 4
+    log(f"[bench] layer {us_layer:.1f} us, dense stage {us_dense:.1f} us = {tflops:.1f} TFLOP/s")
+    result = {
+        "metric": "token-sparse prefill attention layer time (select + dense + scatter)",
+        "value": round(us_layer, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_layer / 1e3, 4),
+        "us_dense_stage": round(us_dense, 2),
+        "us_selection": round(us_layer - us_dense, 2),
+        "algorithmic_bytes_per_layer": int(layer_bytes_),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "seq_len": T, "k": k, "causal": causal, "scatter": "residual (no zero fill)"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": f"k_tsa (d={d})", "avg_launch_us": round(us_dense, 2),
+                     "flops_per_launch": int(flops), "launches_timed": args.steps},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = tsa_cpu_baseline(q, kc, vc, scores, k, causal, us_layer, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def tsa_cpu_baseline(q, kc, vc, scores, k, causal, us_layer, target_s):
+    """The oracle on the first heads of the layer (one sequence) until about target_s
+    seconds of CPU work, scaled to the whole layer."""
+    from oracle import lychee_oracle as orc
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    Hq, BT, d = q.shape
+    Hkv = kc.shape[0]
+    G = Hq // Hkv
+    B, _, T = scores.shape
+    spent, heads = 0.0, 0
+    for h in range(Hq):
+        g = h // G
+        qh = orc.bf16_bits_to_f64(wl.bf16_bits(q[h:h + 1, :T]))
+        kh = orc.bf16_bits_to_f64(wl.bf16_bits(kc[g:g + 1, :T]))
+        vh = orc.bf16_bits_to_f64(wl.bf16_bits(vc[g:g + 1, :T]))
+        sh = scores[0:1, h:h + 1].cpu().numpy()
+        t0 = time.perf_counter()
+        orc.tsa_attention(qh, kh, vh, sh, k, causal=causal, zero_fill=False)
+        spent += time.perf_counter() - t0
+        heads += 1
+        log(f"[bench] oracle head {h}: cumulative {spent:.1f}s")
+        if spent >= target_s:
+            break
+    per_layer_us = spent / heads * (B * Hq) * 1e6
+    return {"value": round(per_layer_us, 1), "unit": "us", "cores": int(threads), "kind": "oracle",
+            "cpu_model": _cpu_model(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "sample": f"heads 0..{heads - 1} of {B * Hq} (sequence 0), fp64 NumPy oracle, {spent:.1f} s, "
+                      f"scaled to the layer's {B * Hq} heads"}
 
 
 def cpu_baseline(w, inputs, total_bytes, target_s):

@@ -18,7 +18,7 @@ __all__ = [
     "Shape", "workspace_bytes", "topk_workspace_bytes", "Workspace", "TopkWorkspace",
     "retrieval_decode", "sparse_decode", "hybrid_layer", "topk_select",
     "hysparse_workspace_bytes", "HySparseWorkspace", "hysparse_layer",
-    "tsa_workspace_bytes", "TsaWorkspace", "tsa_attention", "TSA_CAUSAL", "TSA_ZERO_FILL",
+    "tsa_workspace_bytes", "TsaWorkspace", "tsa_attention", "TSA_CAUSAL", "TSA_ZERO_FILL", "TSA_GIVEN_IDX",
     "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "FLAG_SEPARATE_SELECT", "FLAG_BLOCK_SELECT", "flag_split_rows", "flag_waves", "EXPORTED_SYMBOLS",
 ]
 
@@ -29,6 +29,7 @@ FLAG_SEPARATE_SELECT = 4
 FLAG_BLOCK_SELECT = 8
 TSA_CAUSAL = 1
 TSA_ZERO_FILL = 2
+TSA_GIVEN_IDX = 4
 _STATUS = {1: "invalid argument", 2: "unsupported shape", 3: "workspace missing or too small",
            4: "HIP launch or copy failed", 5: "a bounded wait between workgroups gave up"}
 EXPORTED_SYMBOLS = ("ld_status_string", "ld_workspace_size", "ld_topk_workspace_size",
@@ -125,7 +126,7 @@ def load_library():
     lib.ld_hysparse_layer.restype = i32
     lib.ld_hysparse_layer.argtypes = [sp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, u32, vp, sz, vp]
     lib.ld_tsa_workspace_size.restype = sz
-    lib.ld_tsa_workspace_size.argtypes = [sp]
+    lib.ld_tsa_workspace_size.argtypes = [sp, i32]
     lib.ld_tsa_attention.restype = i32
     lib.ld_tsa_attention.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, u32, vp, sz, vp]
     lib.ld_topk_select.restype = i32
@@ -257,8 +258,8 @@ def tsa_shape(q, k_cache, batch: int, scale=None) -> Shape:
     return s
 
 
-def tsa_workspace_bytes(shape: Shape) -> int:
-    n = load_library().ld_tsa_workspace_size(ctypes.byref(shape))
+def tsa_workspace_bytes(shape: Shape, k: int) -> int:
+    n = load_library().ld_tsa_workspace_size(ctypes.byref(shape), int(k))
     if n == 0:
         raise LycheeDecodeError(1, "ld_tsa_workspace_size")
     return int(n)
@@ -267,8 +268,8 @@ def tsa_workspace_bytes(shape: Shape) -> int:
 class TsaWorkspace(_WS):
     """Zero-initialised device workspace for tsa_attention."""
 
-    def __init__(self, shape: Shape, device="cuda"):
-        super().__init__(tsa_workspace_bytes(shape), device)
+    def __init__(self, shape: Shape, k: int, device="cuda"):
+        super().__init__(tsa_workspace_bytes(shape, k), device)
 
 
 class TopkWorkspace(_WS):
@@ -400,17 +401,29 @@ def hysparse_layer(q, k_cache, v_cache, k: int, s_in, k_window, v_window, gate, 
 
 
 def tsa_attention(q, k_cache, v_cache, scores, k: int, *, idx_out=None, out=None, causal: bool = False,
-                  zero_fill: bool = True, workspace: Optional[TsaWorkspace] = None, scale=None):
+                  zero_fill: bool = True, workspace: Optional[TsaWorkspace] = None, scale=None,
+                  given_idx: bool = False, batch: Optional[int] = None):
     """Token Sparse Attention over a prefill: per (sequence, head) the top-k tokens of
     `scores` [B][Hq][T] (fp32), dense attention among them, scattered to their rows of
     `out` [Hq][B*T][d]. q [Hq][B*T][d], k_cache / v_cache [Hkv][B*T][d] (bf16).
-    Returns (out, idx_out [B][Hq][min(k, T)] int32 ascending)."""
+    given_idx: skip the selection and use idx_out as given (scores may be None; then
+    `batch` gives B). Returns (out, idx_out [B][Hq][min(k, T)] int32 ascending)."""
     torch = _torch()
     _req(q, torch.bfloat16, "q"); _req(k_cache, torch.bfloat16, "k_cache"); _req(v_cache, torch.bfloat16, "v_cache")
-    _req(scores, torch.float32, "scores")
-    if scores.dim() != 3 or q.dim() != 3 or k_cache.shape != v_cache.shape:
-        raise ValueError("scores must be [B][Hq][T]; q, k_cache, v_cache 3-D with equal K/V shapes")
-    B, Hq, T = (int(x) for x in scores.shape)
+    if scores is not None:
+        _req(scores, torch.float32, "scores")
+        if scores.dim() != 3:
+            raise ValueError("scores must be [B][Hq][T]")
+        B, Hq, T = (int(x) for x in scores.shape)
+    elif given_idx and batch:
+        B, Hq = int(batch), int(q.shape[0])
+        T = int(q.shape[1]) // B
+    else:
+        raise ValueError("scores are required unless given_idx is set with batch")
+    if q.dim() != 3 or k_cache.shape != v_cache.shape or k_cache.dim() != 3:
+        raise ValueError("q, k_cache, v_cache must be 3-D with equal K/V shapes")
+    if given_idx and idx_out is None:
+        raise ValueError("given_idx needs idx_out")
     if q.shape[0] != Hq or q.shape[1] != B * T or k_cache.shape[1] != B * T or k_cache.shape[2] != q.shape[2]:
         raise ValueError("q must be [Hq][B*T][d] and k_cache [Hkv][B*T][d] for scores [B][Hq][T]")
     shape = tsa_shape(q, k_cache, B, scale)
@@ -425,10 +438,10 @@ def tsa_attention(q, k_cache, v_cache, scores, k: int, *, idx_out=None, out=None
     _req(out, torch.bfloat16, "out")
     if out.shape != q.shape:
         raise ValueError("out must have the shape of q")
-    flags = (TSA_CAUSAL if causal else 0) | (TSA_ZERO_FILL if zero_fill else 0)
-    ws = workspace or TsaWorkspace(shape, q.device)
+    flags = (TSA_CAUSAL if causal else 0) | (TSA_ZERO_FILL if zero_fill else 0) | (TSA_GIVEN_IDX if given_idx else 0)
+    ws = workspace or TsaWorkspace(shape, k, q.device)
     _check(load_library().ld_tsa_attention(
-        ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), scores.data_ptr(), int(k),
+        ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), _ptr(scores), int(k),
         idx_out.data_ptr(), out.data_ptr(), int(flags), ws.ptr(), ws.nbytes, _stream()), "ld_tsa_attention")
     return out, idx_out
 

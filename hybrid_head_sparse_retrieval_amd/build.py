@@ -28,6 +28,11 @@ COMMON = [
 ]
 
 
+# per-source options: the dense-attention kernel keeps its matrix-core accumulators in
+# VGPRs, so the online-softmax rescale works on them in place
+EXTRA = {"ld_tsa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -56,7 +61,7 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     cmds = []
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmd = [hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if save_temps:
             cmd.insert(1, "--save-temps")
         objs.append(obj)

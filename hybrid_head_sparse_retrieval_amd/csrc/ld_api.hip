@@ -66,6 +66,15 @@ SelArrays sel_arrays(int rows, int n, Take take) {
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
+// Scores per workgroup of the standalone digit-1 histogram: 512, doubled while the
+// grid would exceed about 2048 workgroups (long rows), at most 16384.
+void set_hist_chunks(SelParams& sp, int64_t rows, int n) {
+  int c = kSelChunk;
+  while (c < 16384 && rows * ((n + c - 1) / c) > 2048) c <<= 1;
+  sp.hchunk = c;
+  sp.Ch = (n + c - 1) / c;
+}
+
 void fill_sel(SelParams& sp, const SelArrays& a, void* ws) {
   sp.C = a.C;
   sp.hist1 = at<uint32_t>(ws, a.hist1);
@@ -382,7 +391,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     SelParams sp{};
     sp.mode = 0;
     sp.nrows = bk.rows;
-    sp.Ch = (bk.nblk + kSelChunk - 1) / kSelChunk;
+    set_hist_chunks(sp, B * nret, bk.nblk);
     sp.scores = bk.scores; sp.row_stride = bk.nblk; sp.n = bk.nblk; sp.k = bk.kblk;
     sp.idx_out = at<int32_t>(ws, L.blk_idx); sp.val_out = nullptr;
     fill_sel(sp, L.sel, ws);
@@ -495,10 +504,38 @@ ld_status ld_hysparse_layer(const ld_shape* shape, const void* q, const void* k_
                    false, ws + H.main, H.o_w - H.main, stream, gate, o_w);
 }
 
-size_t ld_tsa_workspace_size(const ld_shape* shape) {
+}  // extern "C"
+
+namespace {
+
+// The TSA workspace: the selection's arrays, then the key splits' partials.
+struct TsaLayout {
+  size_t ml, o, total;
+  int nsplit, split_keys;
+};
+TsaLayout tsa_layout(const ld_shape* s, int k) {
+  TsaLayout L{};
+  const int rows = s->batch * s->num_q_heads, kk = std::min(k, s->seq_len);
+  size_t o = align_up(sel_layout(rows, s->seq_len).total);
+  size_t part = 0;
+  tsa_splits(rows, kk, s->head_dim, &L.nsplit, &L.split_keys, &part);
+  const size_t ml_bytes = part / (size_t)(s->head_dim + 2) * 2;   // the (max, sum) pairs
+  L.ml = o;
+  o = align_up(o + ml_bytes);
+  L.o = o;
+  o = align_up(o + (part - ml_bytes));
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ld_tsa_workspace_size(const ld_shape* shape, int32_t k) {
   ld_status why;
-  if (!shape || !shape_ok(shape, &why) || shape->kv_indptr || shape->page_size || shape->kv_dtype) return 0;
-  return sel_layout(shape->batch * shape->num_q_heads, shape->seq_len).total;
+  if (!shape || !shape_ok(shape, &why) || shape->kv_indptr || shape->page_size || shape->kv_dtype || k < 1) return 0;
+  return tsa_layout(shape, k).total;
 }
 
 ld_status ld_tsa_attention(const ld_shape* shape, const void* q, const void* k_cache,
@@ -512,28 +549,32 @@ ld_status ld_tsa_attention(const ld_shape* shape, const void* q, const void* k_c
   if (shape->kv_indptr || shape->page_size || shape->kv_dtype) return LD_ERR_UNSUPPORTED;
   const int B = shape->batch, Hq = shape->num_q_heads, D = shape->head_dim, T = shape->seq_len;
   if (shape->total_tokens != 0 && shape->total_tokens != (int64_t)B * T) return LD_ERR_INVALID_ARGUMENT;
-  if (!q || !k_cache || !v_cache || !scores || !idx_out || !out || k < 1) return LD_ERR_INVALID_ARGUMENT;
+  const bool given = (flags & LD_TSA_GIVEN_IDX) != 0;
+  if (!q || !k_cache || !v_cache || (!scores && !given) || !idx_out || !out || k < 1) return LD_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       ((uintptr_t)scores & 3u) || ((uintptr_t)idx_out & 3u))
     return LD_ERR_INVALID_ARGUMENT;
-  if (flags & ~(uint32_t)(LD_TSA_CAUSAL | LD_TSA_ZERO_FILL)) return LD_ERR_INVALID_ARGUMENT;
+  if (flags & ~(uint32_t)(LD_TSA_CAUSAL | LD_TSA_ZERO_FILL | LD_TSA_GIVEN_IDX)) return LD_ERR_INVALID_ARGUMENT;
   const int rows = B * Hq;
   const SelLayout L = sel_layout(rows, T);
-  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 15u)) return LD_ERR_WORKSPACE;
+  const TsaLayout TL = tsa_layout(shape, k);
+  if (!workspace || workspace_bytes < TL.total || ((uintptr_t)workspace & 15u)) return LD_ERR_WORKSPACE;
   const int kk = std::min(k, T);
   // 1. rows that receive no output are zero when asked for
   if ((flags & LD_TSA_ZERO_FILL) &&
       launch_zero(out, (size_t)Hq * B * T * D * 2, stream) != hipSuccess)
     return LD_ERR_HIP;
-  // 2. compress: argsTopK of every head's scores
-  SelParams sp{};
-  sp.mode = 0;
-  sp.nrows = rows;
-  sp.Ch = (T + kSelChunk - 1) / kSelChunk;
-  sp.scores = scores; sp.row_stride = T; sp.n = T; sp.k = kk;
-  sp.idx_out = idx_out; sp.val_out = nullptr;
-  fill_sel(sp, L.sel, workspace);
-  if (launch_select(sp, stream, true) != hipSuccess) return LD_ERR_HIP;
+  // 2. compress: argsTopK of every head's scores (unless the caller gives the sets)
+  if (!given) {
+    SelParams sp{};
+    sp.mode = 0;
+    sp.nrows = rows;
+    set_hist_chunks(sp, rows, T);
+    sp.scores = scores; sp.row_stride = T; sp.n = T; sp.k = kk;
+    sp.idx_out = idx_out; sp.val_out = nullptr;
+    fill_sel(sp, L.sel, workspace);
+    if (launch_select(sp, stream, true) != hipSuccess) return LD_ERR_HIP;
+  }
   // 3. dense attention among the selected tokens, scattered to their rows
   TsaParams tp{};
   tp.q = static_cast<const uint16_t*>(q);
@@ -545,6 +586,10 @@ ld_status ld_tsa_attention(const ld_shape* shape, const void* q, const void* k_c
   tp.qtiles = (kk + tsa_queries_per_block() - 1) / tsa_queries_per_block();
   tp.scale = shape->softmax_scale > 0.f ? shape->softmax_scale : 1.0f / std::sqrt((float)D);
   tp.causal = (flags & LD_TSA_CAUSAL) ? 1 : 0;
+  tp.nsplit = TL.nsplit;
+  tp.split_keys = TL.split_keys;
+  tp.part_ml = at<float>(workspace, TL.ml);
+  tp.part_o = at<float>(workspace, TL.o);
   return launch_tsa(tp, stream) == hipSuccess ? LD_OK : LD_ERR_HIP;
 }
 
@@ -617,7 +662,7 @@ ld_status ld_topk_select(const float* scores, int32_t rows, int32_t n, int64_t r
   SelParams sp{};
   sp.mode = 0;
   sp.nrows = rows;
-  sp.Ch = (n + kSelChunk - 1) / kSelChunk;
+  set_hist_chunks(sp, rows, n);
   sp.scores = scores; sp.row_stride = row_stride; sp.n = n; sp.k = k;
   sp.idx_out = idx_out; sp.val_out = val_out;
   fill_sel(sp, L.sel, workspace);

@@ -102,7 +102,8 @@ struct SelParams {
   int mode;               // 0: standalone rows, 1: retrieval rows of a layer
   int nrows;              // rows launched
   int C;                  // span-grid stride of the select passes (kSelSpan scores per span)
-  int Ch;                 // chunk-grid stride of the standalone histogram (512 per chunk)
+  int Ch;                 // chunk-grid stride of the standalone histogram (hchunk scores per chunk)
+  int hchunk;             // scores per histogram workgroup (a multiple of kSelChunk)
   // standalone
   const float* scores; int64_t row_stride; int n; int k; int32_t* idx_out; float* val_out;
   // layer rows: row r -> (b = r / nret, h = heads[r % nret])
@@ -184,9 +185,18 @@ struct TsaParams {
   int qtiles;             // ceil(kk / tsa_queries_per_block())
   float scale;
   int causal;
+  // key splits: workgroup (row, query block, split s) takes selected keys
+  // [s * split_keys, (s + 1) * split_keys); with nsplit > 1 the partials go to
+  // part_ml [rows][qtiles][nsplit][queries per block][2] and part_o [..][D], merged by a
+  // second launch
+  int nsplit, split_keys;
+  float* part_ml;
+  float* part_o;
 };
 hipError_t launch_tsa(const TsaParams& p, hipStream_t st);
 int tsa_queries_per_block();
+// Key splits for kk selected keys of `rows` rows, and the bytes of their partials.
+void tsa_splits(int64_t rows, int kk, int D, int* nsplit, int* split_keys, size_t* part_bytes);
 hipError_t launch_block_expand(const BlockParams& p, int rows, hipStream_t st);
 
 }  // namespace ld

@@ -79,20 +79,19 @@ __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
   __shared__ int flag;
   const int r = blockIdx.x / p.C, c = blockIdx.x % p.C;
   const RowView v = row_view(p, r);
-  if (c * kSelChunk >= v.n || v.k < 1) return;
+  const int hc = p.hchunk;
+  if (c * hc >= v.n || v.k < 1) return;
   const int tid = threadIdx.x;
   for (int i = tid; i < kHist1Bins; i += kThreads) hist[i] = 0;
   __syncthreads();
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int i = c * kSelChunk + h * kThreads + tid;
-    if (i < v.n) atomicAdd(&hist[score_key(v.sc[i]) >> 21], 1u);
-  }
+  const int hi = min(v.n, (c + 1) * hc);
+#pragma unroll 4
+  for (int i = c * hc + tid; i < hi; i += kThreads) atomicAdd(&hist[score_key(v.sc[i]) >> 21], 1u);
   __syncthreads();
   uint32_t* gh = hist1_mine(p.hist1, v.slot);
   for (int i = tid; i < kHist1Bins; i += kThreads)
     if (hist[i]) atomicAdd(gh + i, hist[i]);
-  const uint32_t nch = (uint32_t)((v.n + kSelChunk - 1) / kSelChunk);
+  const uint32_t nch = (uint32_t)((v.n + hc - 1) / hc);
   if (!arrive_last(p.tickets + v.slot, nch, &flag)) return;
   if (tid == 0) { res[0] = 0; res[1] = 0; p.tickets[v.slot] = 0; }
   __syncthreads();    // every thread is done with its own counts in hist

@@ -7,11 +7,17 @@
 // (v_mfma_f32_16x16x32_bf16). A workgroup takes 64 selected queries of one head, 16 per
 // wave; it walks the head's selected keys in tiles of 32 gathered rows staged in LDS
 // (K row-major for the q.k product, V transposed so that the P.V product reads 8
-// consecutive keys of one dimension per lane). The softmax runs online in log2 units;
-// P goes through LDS (bf16) from the product's output layout to the operand layout.
+// consecutive keys of one dimension per lane), two tiles deep: while one tile is
+// computed the next is stored and the one after is loaded, at positions staged in LDS
+// 2048 at a time. The softmax runs online in log2 units; P goes through the wave's own
+// LDS rows (bf16) from the product's output layout to the operand layout.
 // With the causal mask a key is allowed when its position is not after the query's;
 // since I is ascending, that is key index <= query index, so tiles past the
-// workgroup's last query are skipped.
+// workgroup's last query are skipped. Long key ranges are cut into splits of
+// split_keys keys run by workgroups of their own; a merge launch combines their
+// partials (max, sum, unnormalised O) per query.
+
+#include <type_traits>
 
 #include "ld_device.h"
 
@@ -22,6 +28,7 @@ namespace {
 constexpr int kTsaWaves = 4;
 constexpr int kTsaQ = 16 * kTsaWaves;   // queries per workgroup
 constexpr int kTsaKeys = 32;            // keys per tile
+constexpr int kTsaIdx = 2048;           // selected positions staged in LDS at a time
 constexpr float kTsaLog2e = 1.4426950408889634f;
 
 typedef __bf16 tsa_bf16x8_t __attribute__((ext_vector_type(8)));
@@ -37,70 +44,129 @@ struct TsaSmem {
   static constexpr int KS = D + 8;          // K tile row stride (elements)
   static constexpr int VS = kTsaKeys + 8;   // transposed V tile row stride
   static constexpr int PS = kTsaKeys + 8;   // P row stride
-  uint16_t kt[kTsaKeys * KS];
-  uint16_t vt[D * VS];
-  uint16_t pl[kTsaWaves][16 * PS];
+  // (16-byte aligned so that operand reads are single 16-byte LDS reads)
+  alignas(16) uint16_t kt[2][kTsaKeys * KS];   // two tiles: one computed, one being filled
+  alignas(16) uint16_t vt[2][D * VS + (D / 8) * 32];   // rows at vrow(dim)
+  alignas(16) uint16_t pl[kTsaWaves][16 * PS];
+  // Row of dimension `dim` in vt: each group of 8 dimensions starts 32 elements (16
+  // banks) after the previous group's end, so that consecutive groups fall in opposite
+  // bank halves and the transposed stores and the operand reads are conflict-free.
+  static __device__ __forceinline__ int vrow(int dim) { return dim * VS + (dim >> 3) * 32; }
   int qpos[kTsaQ];
+  int kidx[kTsaIdx];                        // selected positions of the current key chunk
 };
 
-// Max / sum over the 16 lanes that share lane >> 4.
-__device__ __forceinline__ float max16(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
-  return v;
+// bf16 bits of x, rounded to nearest even by the hardware conversion (the softmax
+// weights are finite and in [0, 1]).
+__device__ __forceinline__ uint16_t tsa_bf16(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+// A lane's value moved by a DPP row pattern that every lane reads in range (so the
+// move can fold into the instruction that consumes it).
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
 }
 
-// Tile t of the selected keys: thread tid loads LPT 16-byte pieces of K and V rows
-// (rows past kk repeat the last selected row; their keys are masked).
-template <int D, int LPT>
-__device__ __forceinline__ void tsa_load(const uint16_t* Kg, const uint16_t* Vg, const int32_t* I, int kk, int t,
-                                         int tid, uint4 (&kreg)[LPT], uint4 (&vreg)[LPT]) {
+// Max / sum over the 16 lanes that share lane >> 4 (one DPP row).
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp_row<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_row<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_row<0x141>(v));   // row_half_mirror
+  return fmaxf(v, dpp_row<0x128>(v));  // row_ror:8
+}
+__device__ __forceinline__ float sum16(float v) {
+  v = sum8(v);
+  return v + xor8_f(v);
+}
+
+// LDS written by lanes of this wave becomes visible to the wave's other lanes (the
+// wave's LDS operations run in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Tile t of the key chunk: K as LPT 16-byte pieces of rows per thread (row-major,
+// coalesced); V as pairs of rows (2p, 2p + 1) at one 16-byte column piece, so that
+// the transposed store writes whole words (two keys of one dimension). Rows past the
+// chunk's nk keys repeat its last key; they are masked.
+template <int D>
+struct TsaRegs {
+  static constexpr int LPT = kTsaKeys * (D / 8) / (kTsaWaves * 64);        // K pieces per thread
+  static constexpr int VITEMS = (kTsaKeys / 2) * (D / 8);                   // V row pairs x pieces
+  static constexpr int LPV = (VITEMS + kTsaWaves * 64 - 1) / (kTsaWaves * 64);
+  uint4 k[LPT];
+  uint4 v[LPV][2];
+};
+
+template <int D>
+__device__ __forceinline__ void tsa_load(const uint16_t* Kg, const uint16_t* Vg, const int* kidx, int nk, int t,
+                                         int tid, TsaRegs<D>& R) {
+  using RG = TsaRegs<D>;
+  const int base = t * kTsaKeys;
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) {
+  for (int i = 0; i < RG::LPT; ++i) {
     const int u = tid + i * kTsaWaves * 64;
     const int r = u / (D / 8), c = u % (D / 8);
-    const size_t pos = (size_t)I[min(t * kTsaKeys + r, kk - 1)];
-    kreg[i] = *reinterpret_cast<const uint4*>(Kg + pos * D + c * 8);
-    vreg[i] = *reinterpret_cast<const uint4*>(Vg + pos * D + c * 8);
+    const size_t pos = (size_t)kidx[min(base + r, nk - 1)];
+    R.k[i] = *reinterpret_cast<const uint4*>(Kg + pos * D + c * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < RG::LPV; ++i) {
+    const int u = tid + i * kTsaWaves * 64;
+    if (u < RG::VITEMS) {
+      const int rp = u % (kTsaKeys / 2), c = u / (kTsaKeys / 2);
+      const size_t p0 = (size_t)kidx[min(base + 2 * rp, nk - 1)];
+      const size_t p1 = (size_t)kidx[min(base + 2 * rp + 1, nk - 1)];
+      R.v[i][0] = *reinterpret_cast<const uint4*>(Vg + p0 * D + c * 8);
+      R.v[i][1] = *reinterpret_cast<const uint4*>(Vg + p1 * D + c * 8);
+    }
   }
 }
 
-// The loaded pieces to LDS: K row-major, V transposed.
-template <int D, int LPT>
-__device__ __forceinline__ void tsa_store(TsaSmem<D>& sm, int tid, const uint4 (&kreg)[LPT],
-                                          const uint4 (&vreg)[LPT]) {
+// The loaded pieces to LDS buffer `buf`: K row-major, V transposed (word j of a pair
+// holds dimension c * 8 + j of keys 2p and 2p + 1).
+template <int D>
+__device__ __forceinline__ void tsa_store(TsaSmem<D>& sm, int buf, int tid, const TsaRegs<D>& R) {
+  using RG = TsaRegs<D>;
   constexpr int KS = TsaSmem<D>::KS, VS = TsaSmem<D>::VS;
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) {
+  for (int i = 0; i < RG::LPT; ++i) {
     const int u = tid + i * kTsaWaves * 64;
     const int r = u / (D / 8), c = u % (D / 8);
-    *reinterpret_cast<uint4*>(&sm.kt[r * KS + c * 8]) = make_uint4(kreg[i].x, kreg[i].y, kreg[i].z, kreg[i].w);
-    const uint32_t w0 = vreg[i].x, w1 = vreg[i].y, w2 = vreg[i].z, w3 = vreg[i].w;
-    uint16_t* vc = &sm.vt[(c * 8) * VS + r];
-    vc[0 * VS] = (uint16_t)(w0 & 0xffffu); vc[1 * VS] = (uint16_t)(w0 >> 16);
-    vc[2 * VS] = (uint16_t)(w1 & 0xffffu); vc[3 * VS] = (uint16_t)(w1 >> 16);
-    vc[4 * VS] = (uint16_t)(w2 & 0xffffu); vc[5 * VS] = (uint16_t)(w2 >> 16);
-    vc[6 * VS] = (uint16_t)(w3 & 0xffffu); vc[7 * VS] = (uint16_t)(w3 >> 16);
+    *reinterpret_cast<uint4*>(&sm.kt[buf][r * KS + c * 8]) = make_uint4(R.k[i].x, R.k[i].y, R.k[i].z, R.k[i].w);
+  }
+#pragma unroll
+  for (int i = 0; i < RG::LPV; ++i) {
+    const int u = tid + i * kTsaWaves * 64;
+    if (u < RG::VITEMS) {
+      const int rp = u % (kTsaKeys / 2), c = u / (kTsaKeys / 2);
+      const uint32_t a[4] = {R.v[i][0].x, R.v[i][0].y, R.v[i][0].z, R.v[i][0].w};
+      const uint32_t b[4] = {R.v[i][1].x, R.v[i][1].y, R.v[i][1].z, R.v[i][1].w};
+      uint32_t* col = reinterpret_cast<uint32_t*>(&sm.vt[buf][TsaSmem<D>::vrow(c * 8) + 2 * rp]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {   // dims c*8 .. c*8+7 share one bank half
+        col[(2 * w) * (VS / 2)] = (a[w] & 0xffffu) | (b[w] << 16);
+        col[(2 * w + 1) * (VS / 2)] = (a[w] >> 16) | (b[w] & 0xffff0000u);
+      }
+    }
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
   using Smem = TsaSmem<D>;
+  constexpr int NT = kTsaWaves * 64;
   constexpr int KS = Smem::KS, VS = Smem::VS, PS = Smem::PS;
   constexpr int KC = D / 32;                                  // k-steps over the head dimension
   constexpr int NO = D / 16;                                  // 16-dim output tiles
-  constexpr int LPT = kTsaKeys * (D / 8) / (kTsaWaves * 64);  // 16-byte loads per thread per tile
-  static_assert(LPT >= 1, "a tile fills the workgroup's loads");
+  static_assert(TsaRegs<D>::LPT >= 1, "a tile fills the workgroup's loads");
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;                   // operand row / k-group
-  const int row = blockIdx.x / p.qtiles, qt = blockIdx.x % p.qtiles;
+  const int sp = blockIdx.x % p.nsplit;                       // key split of this workgroup
+  const int row = blockIdx.x / p.nsplit / p.qtiles, qt = blockIdx.x / p.nsplit % p.qtiles;
   const int b = row / p.Hq, h = row % p.Hq, g = h / (p.Hq / p.Hkv);
   const int kk = p.kk;
   const int32_t* I = p.idx + (size_t)row * kk;
@@ -110,8 +176,9 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
   const uint16_t* Kg = p.k + (size_t)g * plane + seq0 * D;
   const uint16_t* Vg = p.v + (size_t)g * plane + seq0 * D;
   const int q0 = qt * kTsaQ;
+  auto clampT = [&](int x) { return min(max(x, 0), p.T - 1); };   // caller-given sets stay inside
 
-  if (tid < kTsaQ) sm.qpos[tid] = (q0 + tid < kk) ? I[q0 + tid] : -1;
+  if (tid < kTsaQ) sm.qpos[tid] = (q0 + tid < kk) ? clampT(I[q0 + tid]) : -1;
   __syncthreads();
   // q operand: query lr of the wave, dims kc * 32 + 8 * lq
   const int qp = sm.qpos[wave * 16 + lr];
@@ -121,11 +188,10 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
     qa[kc] = (qp >= 0) ? *reinterpret_cast<const uint4*>(Qh + (size_t)qp * D + kc * 32 + 8 * lq)
                        : make_uint4(0, 0, 0, 0);
 
-  int ntiles = (kk + kTsaKeys - 1) / kTsaKeys;
-  if (p.causal) ntiles = min(ntiles, (min(q0 + kTsaQ, kk) + kTsaKeys - 1) / kTsaKeys);
-
-  uint4 kreg[LPT], vreg[LPT];
-
+  const int nkeys = p.causal ? min(q0 + kTsaQ, kk) : kk;     // keys any query here may see
+  const int k_lo = sp * p.split_keys;                         // this split's keys: [k_lo, k_hi)
+  const int k_hi = min(nkeys, k_lo + p.split_keys);
+  if (k_lo >= k_hi) return;                                   // the same in every thread
   const float sl = p.scale * kTsaLog2e;
   float m[4], lsum[4];
   tsa_f32x4_t o[NO];
@@ -134,56 +200,97 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
 #pragma unroll
   for (int n = 0; n < NO; ++n) o[n] = tsa_f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int qrow0 = q0 + wave * 16 + 4 * lq;   // query index of output row r: qrow0 + r
+  TsaRegs<D> R;
 
-  if (ntiles > 0) tsa_load<D, LPT>(Kg, Vg, I, kk, 0, tid, kreg, vreg);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();                 // the previous tile's LDS reads are done
-    tsa_store<D, LPT>(sm, tid, kreg, vreg);
+  for (int cb = k_lo; cb < k_hi; cb += kTsaIdx) {
+    const int nk = min(kTsaIdx, k_hi - cb);
+    const int nt = (nk + kTsaKeys - 1) / kTsaKeys;
+    __syncthreads();                             // the previous chunk is done with LDS
+#pragma unroll 8
+    for (int i = tid; i < nk; i += NT) sm.kidx[i] = clampT(I[cb + i]);
     __syncthreads();
-    if (t + 1 < ntiles) tsa_load<D, LPT>(Kg, Vg, I, kk, t + 1, tid, kreg, vreg);
-    // S = Q K^T over the tile's two 16-key halves: element r of s[st] is query
-    // qrow0 + r against key t * 32 + st * 16 + lr
-    tsa_f32x4_t s[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      s[st] = tsa_f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const uint4 kb = *reinterpret_cast<const uint4*>(&sm.kt[(st * 16 + lr) * KS + kc * 32 + 8 * lq]);
-        s[st] = mfma16(qa[kc], kb, s[st]);
-      }
-    }
-    float x[2][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float mt = -LD_INF;
+    tsa_load<D>(Kg, Vg, sm.kidx, nk, 0, tid, R);
+    tsa_store<D>(sm, 0, tid, R);
+    if (nt > 1) tsa_load<D>(Kg, Vg, sm.kidx, nk, 1, tid, R);
+    // tiles in pairs, so that each step's LDS buffer is a compile-time constant
+    auto step = [&](int t, auto bufc) {
+      constexpr int buf = decltype(bufc)::value;
+      __syncthreads();                           // tile t is in buf; the other buffer is free
+      if (t + 1 < nt) tsa_store<D>(sm, buf ^ 1, tid, R);
+      if (t + 2 < nt) tsa_load<D>(Kg, Vg, sm.kidx, nk, t + 2, tid, R);
+      // S = Q K^T over the tile's two 16-key halves: element r of s[st] is query
+      // qrow0 + r against key cb + t * 32 + st * 16 + lr
+      tsa_f32x4_t s[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int key = t * kTsaKeys + st * 16 + lr;
-        const bool ok = key < kk && (!p.causal || key <= qrow0 + r);
-        x[st][r] = ok ? s[st][r] * sl : -LD_INF;
-        mt = fmaxf(mt, x[st][r]);
+        s[st] = tsa_f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const uint4 kb =
+              *reinterpret_cast<const uint4*>(&sm.kt[buf][(st * 16 + lr) * KS + kc * 32 + 8 * lq]);
+          s[st] = mfma16(qa[kc], kb, s[st]);
+        }
       }
-      mt = max16(mt);
-      const float mn = fmaxf(m[r], mt);
-      const float mu = (mn == -LD_INF) ? 0.f : mn;
-      const float alpha = exp2_fast(m[r] - mu);       // 0 while nothing was allowed
-      const float p0 = exp2_fast(x[0][r] - mu), p1 = exp2_fast(x[1][r] - mu);
-      lsum[r] = fmaf(lsum[r], alpha, p0 + p1);
-      m[r] = mn;
+      float alpha[4];
 #pragma unroll
-      for (int n = 0; n < NO; ++n) o[n][r] *= alpha;
-      sm.pl[wave][(4 * lq + r) * PS + lr] = f32_to_bf16(p0);
-      sm.pl[wave][(4 * lq + r) * PS + 16 + lr] = f32_to_bf16(p1);
-    }
-    __syncthreads();                 // P of the wave is in LDS
-    // O += P V: P row lr (query), keys 8 * lq .. + 7; V^T row n * 16 + lr (dim), same keys
-    const uint4 pa = *reinterpret_cast<const uint4*>(&sm.pl[wave][lr * PS + 8 * lq]);
+      for (int r = 0; r < 4; ++r) {
+        float x[2];
+        float mt = -LD_INF;
 #pragma unroll
-    for (int n = 0; n < NO; ++n) {
-      const uint4 vb = *reinterpret_cast<const uint4*>(&sm.vt[(n * 16 + lr) * VS + 8 * lq]);
-      o[n] = mfma16(pa, vb, o[n]);
+        for (int st = 0; st < 2; ++st) {
+          const int key = cb + t * kTsaKeys + st * 16 + lr;
+          const bool ok = key < k_hi && (!p.causal || key <= qrow0 + r);
+          x[st] = ok ? s[st][r] * sl : -LD_INF;
+          mt = fmaxf(mt, x[st]);
+        }
+        mt = max16(mt);
+        const float mn = fmaxf(m[r], mt);
+        const float mu = (mn == -LD_INF) ? 0.f : mn;
+        alpha[r] = (mn > m[r]) ? exp2_fast(m[r] - mu) : 1.f;   // 0 while nothing was allowed
+        const float p0 = exp2_fast(x[0] - mu), p1 = exp2_fast(x[1] - mu);
+        lsum[r] = fmaf(lsum[r], alpha[r], p0 + p1);
+        m[r] = mn;
+        sm.pl[wave][(4 * lq + r) * PS + lr] = tsa_bf16(p0);
+        sm.pl[wave][(4 * lq + r) * PS + 16 + lr] = tsa_bf16(p1);
+      }
+      // rescale the rows whose running max grew (once the maxima settle, no wave does)
+      if (__builtin_amdgcn_ballot_w64((alpha[0] != 1.f) | (alpha[1] != 1.f) | (alpha[2] != 1.f) | (alpha[3] != 1.f))) {
+#pragma unroll
+        for (int n = 0; n < NO; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[n][r] *= alpha[r];
+      }
+      wave_lds_sync();                           // P of this wave is in LDS
+      // O += P V: P row lr (query), keys 8 * lq .. + 7; V^T row n * 16 + lr (dim), same keys
+      const uint4 pa = *reinterpret_cast<const uint4*>(&sm.pl[wave][lr * PS + 8 * lq]);
+#pragma unroll
+      for (int n = 0; n < NO; ++n) {
+        const uint4 vb = *reinterpret_cast<const uint4*>(&sm.vt[buf][Smem::vrow(n * 16 + lr) + 8 * lq]);
+        o[n] = mfma16(pa, vb, o[n]);
+      }
+      wave_lds_sync();                           // P is read before the next tile rewrites it
+    };
+    for (int t = 0; t < nt; t += 2) {
+      step(t, std::integral_constant<int, 0>{});
+      if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1>{});
     }
+  }
+  if (p.nsplit > 1) {
+    // this split's partial: row max (log2 units), row sum and unnormalised O per query
+    const size_t unit = ((size_t)row * p.qtiles + qt) * p.nsplit + sp;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float L = sum16(lsum[r]);
+      const int ql = wave * 16 + 4 * lq + r;
+      if (lr == 0) {
+        p.part_ml[(unit * kTsaQ + ql) * 2 + 0] = m[r];
+        p.part_ml[(unit * kTsaQ + ql) * 2 + 1] = L;
+      }
+      float* po = p.part_o + (unit * kTsaQ + ql) * D;
+#pragma unroll
+      for (int n = 0; n < NO; ++n) po[n * 16 + lr] = o[n][r];
+    }
+    return;
   }
   // O / l, scattered to the queries' own rows
 #pragma unroll
@@ -199,17 +306,102 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
   }
 }
 
+// Merge of the key splits of one (row, query block): O = sum_s o_s 2^(m_s - M) / L with
+// M = max_s m_s and L = sum_s l_s 2^(m_s - M), written as bf16 to the queries' rows.
+// A wave takes 4 queries at a time, a lane DL adjacent dimensions of each; every load
+// of the 4 queries is issued before the first use.
+template <int D>
+__global__ __launch_bounds__(kTsaWaves * 64) void k_tsa_merge(TsaParams p) {
+  constexpr int DL = D / 64;
+  constexpr int QW = 4;                                        // queries per step of a wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x / p.qtiles, qt = blockIdx.x % p.qtiles;
+  const int b = row / p.Hq, h = row % p.Hq;
+  const int kk = p.kk, q0 = qt * kTsaQ;
+  const int nkeys = p.causal ? min(q0 + kTsaQ, kk) : kk;
+  const int ns = (nkeys + p.split_keys - 1) / p.split_keys;   // splits that ran (1..8)
+  const int32_t* I = p.idx + (size_t)row * kk;
+  const size_t base = ((size_t)row * p.qtiles + qt) * p.nsplit;
+  uint16_t* out = p.out + (size_t)h * p.B * p.T * D + (size_t)b * p.T * D;
+  for (int qs = wave * QW; qs < kTsaQ; qs += kTsaWaves * QW) {
+    float ml[QW][8][2], po[QW][8][DL];
+#pragma unroll
+    for (int j = 0; j < QW; ++j)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const size_t u = (base + min(s, ns - 1)) * kTsaQ + qs + j;
+        ml[j][s][0] = p.part_ml[u * 2];
+        ml[j][s][1] = p.part_ml[u * 2 + 1];
+#pragma unroll
+        for (int e = 0; e < DL; ++e) po[j][s][e] = p.part_o[u * D + lane * DL + e];
+      }
+#pragma unroll
+    for (int j = 0; j < QW; ++j) {
+      const int qi = q0 + qs + j;
+      if (qi >= kk) break;
+      float M = -LD_INF;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) M = (s < ns) ? fmaxf(M, ml[j][s][0]) : M;
+      const float mu = (M == -LD_INF) ? 0.f : M;
+      float L = 0.f, acc[DL];
+#pragma unroll
+      for (int e = 0; e < DL; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (s < ns) {
+          const float w = exp2_fast(ml[j][s][0] - mu);         // 0 for a split without keys
+          L = fmaf(ml[j][s][1], w, L);
+#pragma unroll
+          for (int e = 0; e < DL; ++e) acc[e] = fmaf(po[j][s][e], w, acc[e]);
+        }
+      }
+      const int pos = min(max(I[qi], 0), p.T - 1);
+      const float il = 1.f / L;
+#pragma unroll
+      for (int e = 0; e < DL; ++e) out[(size_t)pos * D + lane * DL + e] = tsa_bf16(acc[e] * il);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_tsa(const TsaParams& p, hipStream_t st) {
-  const dim3 grid((unsigned)((size_t)p.B * p.Hq * p.qtiles)), block(kTsaWaves * 64);
+  const dim3 grid((unsigned)((size_t)p.B * p.Hq * p.qtiles * p.nsplit)), block(kTsaWaves * 64);
   if (p.D == 128)
     hipLaunchKernelGGL(k_tsa<128>, grid, block, 0, st, p);
   else
     hipLaunchKernelGGL(k_tsa<64>, grid, block, 0, st, p);
+  if (p.nsplit > 1) {
+    const dim3 mgrid((unsigned)((size_t)p.B * p.Hq * p.qtiles));
+    if (p.D == 128)
+      hipLaunchKernelGGL(k_tsa_merge<128>, mgrid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL(k_tsa_merge<64>, mgrid, block, 0, st, p);
+  }
   return hipGetLastError();
 }
 
 int tsa_queries_per_block() { return kTsaQ; }
+
+// Key splits only when the (row, query block) workgroups alone would leave most of
+// the chip idle (fewer than 512 of them): splits of kTsaSplitKeys keys or more, at
+// most 8 per query block, while their partials take at most 256 MiB. Otherwise one
+// workgroup walks all keys (measured faster than splitting plus the merge once the
+// chip is full).
+void tsa_splits(int64_t rows, int kk, int D, int* nsplit, int* split_keys, size_t* part_bytes) {
+  constexpr int kTsaSplitKeys = 8 * kTsaKeys;
+  const int64_t qtiles = (kk + kTsaQ - 1) / kTsaQ;
+  int ks = max(kTsaSplitKeys, ((kk + 7) / 8 + kTsaKeys - 1) / kTsaKeys * kTsaKeys);
+  int ns = (kk + ks - 1) / ks;
+  size_t bytes = (size_t)rows * qtiles * ns * kTsaQ * (D + 2) * 4;
+  if (ns <= 1 || rows * qtiles >= 512 || bytes > ((size_t)256 << 20)) {
+    ns = 1;
+    ks = kk;
+    bytes = 0;
+  }
+  *nsplit = ns;
+  *split_keys = ks;
+  *part_bytes = bytes;
+}
 
 }  // namespace ld

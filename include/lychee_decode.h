@@ -211,11 +211,15 @@ ld_status ld_hysparse_layer(const ld_shape* shape, const void* q, const void* k_
    [Hkv][B*T][d]; scores fp32 [B*Hq][T]. shape: batch, num_q_heads, num_kv_heads,
    head_dim (64 or 128), seq_len = T (1..2^21), softmax_scale (0 = 1/sqrt(d)),
    total_tokens 0 or B*T; kv_indptr, paging and kv_dtype must be unset
-   (LD_ERR_UNSUPPORTED otherwise). The workspace holds ld_tsa_workspace_size() bytes,
-   zeroed once. Asynchronous on `stream`; errors are found before the first launch. */
+   (LD_ERR_UNSUPPORTED otherwise). The workspace holds ld_tsa_workspace_size(shape, k)
+   bytes for a budget k (or any smaller one), zeroed once. Asynchronous on `stream`; errors are found before the first launch.
+   flags & LD_TSA_GIVEN_IDX: no selection; idx_out already holds the caller's sets
+   (ascending distinct positions in 0..T-1, min(k,T) per row; positions outside the
+   sequence are clamped to it) and scores may be NULL. */
 #define LD_TSA_CAUSAL 1u
 #define LD_TSA_ZERO_FILL 2u
-size_t ld_tsa_workspace_size(const ld_shape* shape);
+#define LD_TSA_GIVEN_IDX 4u
+size_t ld_tsa_workspace_size(const ld_shape* shape, int32_t k);
 ld_status ld_tsa_attention(const ld_shape* shape, const void* q, const void* k_cache,
                            const void* v_cache, const float* scores, int32_t k, int32_t* idx_out,
                            void* out, uint32_t flags, void* workspace, size_t workspace_bytes,

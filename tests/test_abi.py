@@ -139,10 +139,11 @@ def test_hysparse_workspace_and_arguments(lib):
 
 def test_tsa_workspace_and_arguments(lib):
     s = _shape(seq_len=4096, total_tokens=4096)
-    assert lib.ld_tsa_workspace_size(ctypes.byref(s)) >= lib.ld_topk_workspace_size(32, 4096) > 0
+    assert lib.ld_tsa_workspace_size(ctypes.byref(s), 1024) >= lib.ld_topk_workspace_size(32, 4096) > 0
+    assert lib.ld_tsa_workspace_size(ctypes.byref(s), 0) == 0
     for bad in (dict(head_dim=96), dict(kv_dtype=1, k_scale=1.0, v_scale=1.0),
                 dict(page_size=64, pages_per_seq=512, block_table=FAKE, total_tokens=1 << 20)):
-        assert lib.ld_tsa_workspace_size(ctypes.byref(_shape(**bad))) == 0, bad
+        assert lib.ld_tsa_workspace_size(ctypes.byref(_shape(**bad)), 64) == 0, bad
 
     def tsa(shape, **kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, sc=FAKE, kk=64, idx=FAKE, out=FAKE, flags=0, ws=FAKE, wsb=1 << 40)
@@ -153,7 +154,7 @@ def test_tsa_workspace_and_arguments(lib):
     assert tsa(s, q=None) == INV and tsa(s, sc=None) == INV and tsa(s, idx=None) == INV
     assert tsa(s, kk=0) == INV
     assert tsa(s, k=FAKE + 4) == INV and tsa(s, sc=FAKE + 2) == INV
-    assert tsa(s, flags=4) == INV
+    assert tsa(s, flags=8) == INV                           # unknown flag
     assert tsa(_shape(seq_len=4096, total_tokens=4095)) == INV
     assert tsa(s, ws=None) == WSE and tsa(s, wsb=1024) == WSE
     assert tsa(_shape(seq_len=4096, total_tokens=4096, head_dim=80)) == UNS

@@ -84,3 +84,16 @@ def test_tsa_ties_go_to_lower_positions():
     _, idx = ld.tsa_attention(q.to(dev), kc.to(dev), vc.to(dev), sc.to(dev), 100, causal=True)
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy()[0], np.tile(np.arange(100), (4, 1)))
+
+
+def test_tsa_given_sets_equal_selected_sets():
+    """With the sets given (no selection launch) the output equals the call that
+    selects the same sets."""
+    ld = _ld()
+    dev = "cuda"
+    q, kc, vc, sc = _inputs(1, 4, 2, 128, 3000, 91)
+    qd, kd, vd = q.to(dev), kc.to(dev), vc.to(dev)
+    out1, idx = ld.tsa_attention(qd, kd, vd, sc.to(dev), 500, causal=True)
+    out2, _ = ld.tsa_attention(qd, kd, vd, None, 500, idx_out=idx.clone(), causal=True, given_idx=True, batch=1)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
