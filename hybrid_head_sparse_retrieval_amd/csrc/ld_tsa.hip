@@ -165,8 +165,15 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;                   // operand row / k-group
-  const int sp = blockIdx.x % p.nsplit;                       // key split of this workgroup
-  const int row = blockIdx.x / p.nsplit / p.qtiles, qt = blockIdx.x / p.nsplit % p.qtiles;
+  // key split, row and query block of this workgroup. Query blocks go out in the order
+  // 0, 1, .., then from the last one down, each over all rows: with causal masks the
+  // workgroups that share a compute unit (launched half a grid apart) then pair a short
+  // block with a long one.
+  const int sp = blockIdx.x % p.nsplit;
+  const int rows = p.B * p.Hq;
+  const int wi = blockIdx.x / p.nsplit, jq = wi / rows, row = wi % rows;
+  const int half = (p.qtiles + 1) / 2;
+  const int qt = jq < half ? jq : p.qtiles - 1 - (jq - half);
   const int b = row / p.Hq, h = row % p.Hq, g = h / (p.Hq / p.Hkv);
   const int kk = p.kk;
   const int32_t* I = p.idx + (size_t)row * kk;
@@ -232,27 +239,40 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
         }
       }
       float alpha[4];
+      // online softmax of the tile's rows; `masked` checks every key (tiles at the end
+      // of the range or on the causal diagonal), the interior tiles skip the checks
+      auto rows_softmax = [&](auto masked) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x[2];
-        float mt = -LD_INF;
+        for (int r = 0; r < 4; ++r) {
+          float x[2];
+          float mt = -LD_INF;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int key = cb + t * kTsaKeys + st * 16 + lr;
-          const bool ok = key < k_hi && (!p.causal || key <= qrow0 + r);
-          x[st] = ok ? s[st][r] * sl : -LD_INF;
-          mt = fmaxf(mt, x[st]);
+          for (int st = 0; st < 2; ++st) {
+            if constexpr (decltype(masked)::value) {
+              const int key = cb + t * kTsaKeys + st * 16 + lr;
+              const bool ok = key < k_hi && (!p.causal || key <= qrow0 + r);
+              x[st] = ok ? s[st][r] * sl : -LD_INF;
+            } else {
+              x[st] = s[st][r] * sl;
+            }
+            mt = fmaxf(mt, x[st]);
+          }
+          mt = max16(mt);
+          const float mn = fmaxf(m[r], mt);
+          const float mu = (mn == -LD_INF) ? 0.f : mn;
+          alpha[r] = (mn > m[r]) ? exp2_fast(m[r] - mu) : 1.f;   // 0 while nothing was allowed
+          const float p0 = exp2_fast(x[0] - mu), p1 = exp2_fast(x[1] - mu);
+          lsum[r] = fmaf(lsum[r], alpha[r], p0 + p1);
+          m[r] = mn;
+          sm.pl[wave][(4 * lq + r) * PS + lr] = tsa_bf16(p0);
+          sm.pl[wave][(4 * lq + r) * PS + 16 + lr] = tsa_bf16(p1);
         }
-        mt = max16(mt);
-        const float mn = fmaxf(m[r], mt);
-        const float mu = (mn == -LD_INF) ? 0.f : mn;
-        alpha[r] = (mn > m[r]) ? exp2_fast(m[r] - mu) : 1.f;   // 0 while nothing was allowed
-        const float p0 = exp2_fast(x[0] - mu), p1 = exp2_fast(x[1] - mu);
-        lsum[r] = fmaf(lsum[r], alpha[r], p0 + p1);
-        m[r] = mn;
-        sm.pl[wave][(4 * lq + r) * PS + lr] = tsa_bf16(p0);
-        sm.pl[wave][(4 * lq + r) * PS + 16 + lr] = tsa_bf16(p1);
-      }
+      };
+      const int kt0 = cb + t * kTsaKeys;   // the tile's first key; the wave's first query is q0 + 16 * wave
+      if (kt0 + kTsaKeys <= k_hi && (!p.causal || kt0 + kTsaKeys - 1 <= q0 + wave * 16))
+        rows_softmax(std::false_type{});
+      else
+        rows_softmax(std::true_type{});
       // rescale the rows whose running max grew (once the maxima settle, no wave does)
       if (__builtin_amdgcn_ballot_w64((alpha[0] != 1.f) | (alpha[1] != 1.f) | (alpha[2] != 1.f) | (alpha[3] != 1.f))) {
 #pragma unroll
