@@ -616,19 +616,25 @@ __global__ __launch_bounds__(kThreads) void k_zero(uint4* p16, size_t n16, uint8
 
 // ------------------------------------------------------- token-block selection
 
-// One wave per block: the block maximum of a retrieval row's logits (NaN only when
-// every logit of the block is NaN; fmaxf keeps the number of a NaN / number pair).
+// Block maxima of retrieval rows' logits, one block per 16 lanes: each lane takes 4
+// consecutive logits and the DPP row reduction combines the 16 (NaN only when every
+// logit of the block is NaN; fmaxf keeps the number of a NaN / number pair). The
+// logits may be a caller's buffer with 4-byte alignment only, so the loads are single
+// floats.
+static_assert(kBlock == 64, "a block is one 16-lane row of 16-byte loads");
 __global__ __launch_bounds__(kThreads) void k_block_max(const BlockParams p) {
-  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (wave >= (int64_t)p.rows * p.nblk) return;               // whole waves leave together
-  const int lane = threadIdx.x & 63;
-  const int r = (int)(wave / p.nblk), j = (int)(wave % p.nblk);
+  const int64_t blk = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 4;   // the same in a 16-lane row
+  if (blk >= (int64_t)p.rows * p.nblk) return;                 // whole rows of 16 lanes leave together
+  const int li = threadIdx.x & 15;
+  const int r = (int)(blk / p.nblk), j = (int)(blk % p.nblk);
   const int b = r / p.nret, h = p.heads[r % p.nret];
-  const float* lg = p.logits + ((size_t)b * p.Hq + h) * p.seq_len + (size_t)j * kBlock;
-  float m = lg[lane];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if (lane == 0) p.scores[(size_t)r * p.nblk + j] = m;
+  const float* x = p.logits + ((size_t)b * p.Hq + h) * p.seq_len + (size_t)j * kBlock + li * 4;
+  float m = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  m = fmaxf(m, dpp_f<0xB1>(m));    // quad_perm [1,0,3,2]
+  m = fmaxf(m, dpp_f<0x4E>(m));    // quad_perm [2,3,0,1]
+  m = fmaxf(m, dpp_f<0x141>(m));   // row_half_mirror
+  m = fmaxf(m, xor8_f(m));         // row_ror:8
+  if (li == 0) p.scores[(size_t)r * p.nblk + j] = m;
 }
 
 // One workgroup per retrieval row: S = the tokens of the kept blocks in ascending
@@ -656,8 +662,8 @@ __global__ __launch_bounds__(kThreads) void k_block_expand(const BlockParams p) 
 }  // namespace
 
 hipError_t launch_block_max(const BlockParams& p, int rows, hipStream_t st) {
-  const int64_t waves = (int64_t)rows * p.nblk;
-  const unsigned grid = (unsigned)((waves + kThreads / 64 - 1) / (kThreads / 64));
+  const int64_t lanes = (int64_t)rows * p.nblk * 16;
+  const unsigned grid = (unsigned)((lanes + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(k_block_max, dim3(grid), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
