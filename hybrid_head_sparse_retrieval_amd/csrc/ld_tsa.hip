@@ -13,9 +13,10 @@
 // LDS rows (bf16) from the product's output layout to the operand layout.
 // With the causal mask a key is allowed when its position is not after the query's;
 // since I is ascending, that is key index <= query index, so tiles past the
-// workgroup's last query are skipped. Long key ranges are cut into splits of
-// split_keys keys run by workgroups of their own; a merge launch combines their
-// partials (max, sum, unnormalised O) per query.
+// workgroup's last query are skipped. When the (row, query block) workgroups are too
+// few to fill the chip, the keys are cut into splits of split_keys keys run by
+// workgroups of their own, and a merge launch combines their partials (max, sum,
+// unnormalised O) per query.
 
 #include <type_traits>
 
