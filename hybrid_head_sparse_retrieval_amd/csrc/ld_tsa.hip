@@ -9,8 +9,9 @@
 // (K row-major for the q.k product, V transposed so that the P.V product reads 8
 // consecutive keys of one dimension per lane), two tiles deep: while one tile is
 // computed the next is stored and the one after is loaded, at positions staged in LDS
-// 2048 at a time. The softmax runs online in log2 units; P goes through the wave's own
-// LDS rows (bf16) from the product's output layout to the operand layout.
+// 2048 at a time. Both products run transposed (S^T = K Q^T, O^T = V^T P^T): the score
+// layout of S^T is the operand layout of P^T, so P stays in registers, and a lane's
+// softmax state is that of one query. The softmax runs online in log2 units.
 // With the causal mask a key is allowed when its position is not after the query's;
 // since I is ascending, that is key index <= query index, so tiles past the
 // workgroup's last query are skipped. When the (row, query block) workgroups are too
@@ -44,11 +45,9 @@ template <int D>
 struct TsaSmem {
   static constexpr int KS = D + 8;          // K tile row stride (elements)
   static constexpr int VS = kTsaKeys + 8;   // transposed V tile row stride
-  static constexpr int PS = kTsaKeys + 8;   // P row stride
   // (16-byte aligned so that operand reads are single 16-byte LDS reads)
   alignas(16) uint16_t kt[2][kTsaKeys * KS];   // two tiles: one computed, one being filled
   alignas(16) uint16_t vt[2][D * VS + (D / 8) * 32];   // rows at vrow(dim)
-  alignas(16) uint16_t pl[kTsaWaves][16 * PS];
   // Row of dimension `dim` in vt: each group of 8 dimensions starts 32 elements (16
   // banks) after the previous group's end, so that consecutive groups fall in opposite
   // bank halves and the transposed stores and the operand reads are conflict-free.
@@ -60,33 +59,6 @@ struct TsaSmem {
 // bf16 bits of x, rounded to nearest even by the hardware conversion (the softmax
 // weights are finite and in [0, 1]).
 __device__ __forceinline__ uint16_t tsa_bf16(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
-
-// A lane's value moved by a DPP row pattern that every lane reads in range (so the
-// move can fold into the instruction that consumes it).
-template <int CTRL>
-__device__ __forceinline__ float dpp_row(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
-}
-
-// Max / sum over the 16 lanes that share lane >> 4 (one DPP row).
-__device__ __forceinline__ float max16(float v) {
-  v = fmaxf(v, dpp_row<0xB1>(v));    // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_row<0x4E>(v));    // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_row<0x141>(v));   // row_half_mirror
-  return fmaxf(v, dpp_row<0x128>(v));  // row_ror:8
-}
-__device__ __forceinline__ float sum16(float v) {
-  v = sum8(v);
-  return v + xor8_f(v);
-}
-
-// LDS written by lanes of this wave becomes visible to the wave's other lanes (the
-// wave's LDS operations run in order; this keeps the compiler from moving them).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Tile t of the key chunk: K as LPT 16-byte pieces of rows per thread (row-major,
 // coalesced); V as pairs of rows (2p, 2p + 1) at one 16-byte column piece, so that
@@ -159,7 +131,7 @@ template <int D>
 __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
   using Smem = TsaSmem<D>;
   constexpr int NT = kTsaWaves * 64;
-  constexpr int KS = Smem::KS, VS = Smem::VS, PS = Smem::PS;
+  constexpr int KS = Smem::KS;
   constexpr int KC = D / 32;                                  // k-steps over the head dimension
   constexpr int NO = D / 16;                                  // 16-dim output tiles
   static_assert(TsaRegs<D>::LPT >= 1, "a tile fills the workgroup's loads");
@@ -201,13 +173,15 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
   const int k_hi = min(nkeys, k_lo + p.split_keys);
   if (k_lo >= k_hi) return;                                   // the same in every thread
   const float sl = p.scale * kTsaLog2e;
-  float m[4], lsum[4];
+  // The products run transposed, so that a lane holds one query: S^T = K Q^T gives lane
+  // (lr, lq) the scores of query lr against keys 4 lq + r of each 16-key half, which is
+  // already the operand layout of P^T in O^T = V^T P^T; element r of o[n] is dimension
+  // n * 16 + 4 lq + r of query lr. The lanes lr, lr + 16, lr + 32, lr + 48 share a query.
+  float m = -LD_INF, lsum = 0.f;               // running max (log2 units) and partial sum
   tsa_f32x4_t o[NO];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) { m[r] = -LD_INF; lsum[r] = 0.f; }
-#pragma unroll
   for (int n = 0; n < NO; ++n) o[n] = tsa_f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int qrow0 = q0 + wave * 16 + 4 * lq;   // query index of output row r: qrow0 + r
+  const int qi = q0 + wave * 16 + lr;          // this lane's query
   TsaRegs<D> R;
 
   for (int cb = k_lo; cb < k_hi; cb += kTsaIdx) {
@@ -226,103 +200,110 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
       __syncthreads();                           // tile t is in buf; the other buffer is free
       if (t + 1 < nt) tsa_store<D>(sm, buf ^ 1, tid, R);
       if (t + 2 < nt) tsa_load<D>(Kg, Vg, sm.kidx, nk, t + 2, tid, R);
-      // S = Q K^T over the tile's two 16-key halves: element r of s[st] is query
-      // qrow0 + r against key cb + t * 32 + st * 16 + lr
+      // S^T = K Q^T over the tile's two 16-key halves: element r of s[st] is key
+      // cb + t * 32 + st * 16 + 4 lq + r against query qi
       tsa_f32x4_t s[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         s[st] = tsa_f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          const uint4 kb =
+          const uint4 ka =
               *reinterpret_cast<const uint4*>(&sm.kt[buf][(st * 16 + lr) * KS + kc * 32 + 8 * lq]);
-          s[st] = mfma16(qa[kc], kb, s[st]);
+          s[st] = mfma16(ka, qa[kc], s[st]);
         }
       }
-      float alpha[4];
-      // online softmax of the tile's rows; `masked` checks every key (tiles at the end
-      // of the range or on the causal diagonal), the interior tiles skip the checks
-      auto rows_softmax = [&](auto masked) {
+      const int kt0 = cb + t * kTsaKeys;   // the tile's first key; the wave's first query is q0 + 16 * wave
+      float x[2][4];
+      // `masked` checks every key (tiles at the end of the range or on the causal
+      // diagonal); the interior tiles skip the checks
+      auto scores = [&](auto masked) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (decltype(masked)::value) {
+              const int key = kt0 + st * 16 + 4 * lq + r;
+              const bool ok = key < k_hi && (!p.causal || key <= qi);
+              x[st][r] = ok ? s[st][r] * sl : -LD_INF;
+            } else {
+              x[st][r] = s[st][r] * sl;
+            }
+          }
+      };
+      if (kt0 + kTsaKeys <= k_hi && (!p.causal || kt0 + kTsaKeys - 1 <= q0 + wave * 16))
+        scores(std::false_type{});
+      else
+        scores(std::true_type{});
+      float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+      mt = max_xor32(max_xor16(mt));             // over the query's four lanes
+      const float mn = fmaxf(m, mt);
+      const float mu = (mn == -LD_INF) ? 0.f : mn;
+      const float alpha = (mn > m) ? exp2_fast(m - mu) : 1.f;   // 0 while nothing was allowed
+      float pr[2][4];
+      float ps = 0.f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float x[2];
-          float mt = -LD_INF;
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            if constexpr (decltype(masked)::value) {
-              const int key = cb + t * kTsaKeys + st * 16 + lr;
-              const bool ok = key < k_hi && (!p.causal || key <= qrow0 + r);
-              x[st] = ok ? s[st][r] * sl : -LD_INF;
-            } else {
-              x[st] = s[st][r] * sl;
-            }
-            mt = fmaxf(mt, x[st]);
-          }
-          mt = max16(mt);
-          const float mn = fmaxf(m[r], mt);
-          const float mu = (mn == -LD_INF) ? 0.f : mn;
-          alpha[r] = (mn > m[r]) ? exp2_fast(m[r] - mu) : 1.f;   // 0 while nothing was allowed
-          const float p0 = exp2_fast(x[0] - mu), p1 = exp2_fast(x[1] - mu);
-          lsum[r] = fmaf(lsum[r], alpha[r], p0 + p1);
-          m[r] = mn;
-          sm.pl[wave][(4 * lq + r) * PS + lr] = tsa_bf16(p0);
-          sm.pl[wave][(4 * lq + r) * PS + 16 + lr] = tsa_bf16(p1);
+          pr[st][r] = exp2_fast(x[st][r] - mu);
+          ps += pr[st][r];
         }
-      };
-      const int kt0 = cb + t * kTsaKeys;   // the tile's first key; the wave's first query is q0 + 16 * wave
-      if (kt0 + kTsaKeys <= k_hi && (!p.causal || kt0 + kTsaKeys - 1 <= q0 + wave * 16))
-        rows_softmax(std::false_type{});
-      else
-        rows_softmax(std::true_type{});
-      // rescale the rows whose running max grew (once the maxima settle, no wave does)
-      if (__builtin_amdgcn_ballot_w64((alpha[0] != 1.f) | (alpha[1] != 1.f) | (alpha[2] != 1.f) | (alpha[3] != 1.f))) {
+      lsum = fmaf(lsum, alpha, ps);
+      m = mn;
+      // rescale when some query of the wave has a larger max (rare once the maxima settle)
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
         for (int n = 0; n < NO; ++n)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[n][r] *= alpha[r];
+          for (int r = 0; r < 4; ++r) o[n][r] *= alpha;
       }
-      wave_lds_sync();                           // P of this wave is in LDS
-      // O += P V: P row lr (query), keys 8 * lq .. + 7; V^T row n * 16 + lr (dim), same keys
-      const uint4 pa = *reinterpret_cast<const uint4*>(&sm.pl[wave][lr * PS + 8 * lq]);
+      // P^T operand: k slots 8 lq .. 8 lq + 7 hold keys 4 lq .. + 3 of both halves
+      uint4 pb;
+      pb.x = (uint32_t)tsa_bf16(pr[0][0]) | ((uint32_t)tsa_bf16(pr[0][1]) << 16);
+      pb.y = (uint32_t)tsa_bf16(pr[0][2]) | ((uint32_t)tsa_bf16(pr[0][3]) << 16);
+      pb.z = (uint32_t)tsa_bf16(pr[1][0]) | ((uint32_t)tsa_bf16(pr[1][1]) << 16);
+      pb.w = (uint32_t)tsa_bf16(pr[1][2]) | ((uint32_t)tsa_bf16(pr[1][3]) << 16);
+      // O^T += V^T P^T: V^T row n * 16 + lr (dimension), the same keys in the same order
 #pragma unroll
       for (int n = 0; n < NO; ++n) {
-        const uint4 vb = *reinterpret_cast<const uint4*>(&sm.vt[buf][Smem::vrow(n * 16 + lr) + 8 * lq]);
-        o[n] = mfma16(pa, vb, o[n]);
+        const uint16_t* vr = &sm.vt[buf][Smem::vrow(n * 16 + lr)];
+        const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * lq);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * lq);
+        o[n] = mfma16(make_uint4(v0.x, v0.y, v1.x, v1.y), pb, o[n]);
       }
-      wave_lds_sync();                           // P is read before the next tile rewrites it
     };
     for (int t = 0; t < nt; t += 2) {
       step(t, std::integral_constant<int, 0>{});
       if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1>{});
     }
   }
+  const float L = add_xor32(add_xor16(lsum));   // the query's sum over its four lanes
   if (p.nsplit > 1) {
-    // this split's partial: row max (log2 units), row sum and unnormalised O per query
+    // this split's partial: max (log2 units), sum and unnormalised O of each query
     const size_t unit = ((size_t)row * p.qtiles + qt) * p.nsplit + sp;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float L = sum16(lsum[r]);
-      const int ql = wave * 16 + 4 * lq + r;
-      if (lr == 0) {
-        p.part_ml[(unit * kTsaQ + ql) * 2 + 0] = m[r];
-        p.part_ml[(unit * kTsaQ + ql) * 2 + 1] = L;
-      }
-      float* po = p.part_o + (unit * kTsaQ + ql) * D;
-#pragma unroll
-      for (int n = 0; n < NO; ++n) po[n * 16 + lr] = o[n][r];
+    const int ql = wave * 16 + lr;
+    if (lq == 0) {
+      p.part_ml[(unit * kTsaQ + ql) * 2 + 0] = m;
+      p.part_ml[(unit * kTsaQ + ql) * 2 + 1] = L;
     }
+    float* po = p.part_o + (unit * kTsaQ + ql) * D + 4 * lq;
+#pragma unroll
+    for (int n = 0; n < NO; ++n)
+      *reinterpret_cast<float4*>(po + n * 16) = make_float4(o[n][0], o[n][1], o[n][2], o[n][3]);
     return;
   }
-  // O / l, scattered to the queries' own rows
+  // O / L, scattered to the query's own row (4 dimensions per lane and output tile)
+  if (qi < kk) {
+    const float il = 1.f / L;
+    uint16_t* dst = p.out + (size_t)h * plane + (seq0 + (size_t)sm.qpos[wave * 16 + lr]) * D + 4 * lq;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float L = sum16(lsum[r]);
-    const int qi = qrow0 + r;
-    if (qi < kk) {
-      const float il = 1.f / L;
-      uint16_t* dst = p.out + (size_t)h * plane + (seq0 + (size_t)sm.qpos[wave * 16 + 4 * lq + r]) * D;
-#pragma unroll
-      for (int n = 0; n < NO; ++n) dst[n * 16 + lr] = f32_to_bf16(o[n][r] * il);
+    for (int n = 0; n < NO; ++n) {
+      uint2 w;
+      w.x = (uint32_t)tsa_bf16(o[n][0] * il) | ((uint32_t)tsa_bf16(o[n][1] * il) << 16);
+      w.y = (uint32_t)tsa_bf16(o[n][2] * il) | ((uint32_t)tsa_bf16(o[n][3] * il) << 16);
+      *reinterpret_cast<uint2*>(dst + n * 16) = w;
     }
   }
 }
