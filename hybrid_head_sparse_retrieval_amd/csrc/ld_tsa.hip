@@ -5,11 +5,11 @@
 //
 // This is a dense contraction, so both products run on the matrix cores
 // (v_mfma_f32_16x16x32_bf16). A workgroup takes 64 selected queries of one head, 16 per
-// wave; it walks the head's selected keys in tiles of 32 gathered rows staged in LDS
-// (K row-major for the q.k product, V transposed so that the P.V product reads 8
+// wave; it walks the head's selected keys in tiles of 64 gathered rows staged in LDS
+// (K row-major for the q.k product, V transposed so that the P.V product reads runs of
 // consecutive keys of one dimension per lane), two tiles deep: while one tile is
 // computed the next is stored and the one after is loaded, at positions staged in LDS
-// 2048 at a time. Both products run transposed (S^T = K Q^T, O^T = V^T P^T): the score
+// 1024 at a time. Both products run transposed (S^T = K Q^T, O^T = V^T P^T): the score
 // layout of S^T is the operand layout of P^T, so P stays in registers, and a lane's
 // softmax state is that of one query. The softmax runs online in log2 units.
 // With the causal mask a key is allowed when its position is not after the query's;
@@ -29,8 +29,8 @@ namespace {
 
 constexpr int kTsaWaves = 4;
 constexpr int kTsaQ = 16 * kTsaWaves;   // queries per workgroup
-constexpr int kTsaKeys = 32;            // keys per tile
-constexpr int kTsaIdx = 2048;           // selected positions staged in LDS at a time
+constexpr int kTsaKeys = 64;            // keys per tile
+constexpr int kTsaIdx = 1024;           // selected positions staged in LDS at a time
 constexpr float kTsaLog2e = 1.4426950408889634f;
 
 typedef __bf16 tsa_bf16x8_t __attribute__((ext_vector_type(8)));
@@ -200,11 +200,12 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
       __syncthreads();                           // tile t is in buf; the other buffer is free
       if (t + 1 < nt) tsa_store<D>(sm, buf ^ 1, tid, R);
       if (t + 2 < nt) tsa_load<D>(Kg, Vg, sm.kidx, nk, t + 2, tid, R);
-      // S^T = K Q^T over the tile's two 16-key halves: element r of s[st] is key
-      // cb + t * 32 + st * 16 + 4 lq + r against query qi
-      tsa_f32x4_t s[2];
+      // S^T = K Q^T over the tile's 16-key quarters: element r of s[st] is key
+      // cb + t * 64 + st * 16 + 4 lq + r against query qi
+      constexpr int NST = kTsaKeys / 16;
+      tsa_f32x4_t s[NST];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < NST; ++st) {
         s[st] = tsa_f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
@@ -214,12 +215,12 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
         }
       }
       const int kt0 = cb + t * kTsaKeys;   // the tile's first key; the wave's first query is q0 + 16 * wave
-      float x[2][4];
+      float x[NST][4];
       // `masked` checks every key (tiles at the end of the range or on the causal
       // diagonal); the interior tiles skip the checks
       auto scores = [&](auto masked) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < NST; ++st)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if constexpr (decltype(masked)::value) {
@@ -235,16 +236,18 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
         scores(std::false_type{});
       else
         scores(std::true_type{});
-      float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+      float mt = -LD_INF;
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+        mt = fmaxf(mt, fmaxf(fmaxf(x[st][0], x[st][1]), fmaxf(x[st][2], x[st][3])));
       mt = max_xor32(max_xor16(mt));             // over the query's four lanes
       const float mn = fmaxf(m, mt);
       const float mu = (mn == -LD_INF) ? 0.f : mn;
       const float alpha = (mn > m) ? exp2_fast(m - mu) : 1.f;   // 0 while nothing was allowed
-      float pr[2][4];
+      float pr[NST][4];
       float ps = 0.f;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < NST; ++st)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           pr[st][r] = exp2_fast(x[st][r] - mu);
@@ -259,19 +262,23 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[n][r] *= alpha;
       }
-      // P^T operand: k slots 8 lq .. 8 lq + 7 hold keys 4 lq .. + 3 of both halves
-      uint4 pb;
-      pb.x = (uint32_t)tsa_bf16(pr[0][0]) | ((uint32_t)tsa_bf16(pr[0][1]) << 16);
-      pb.y = (uint32_t)tsa_bf16(pr[0][2]) | ((uint32_t)tsa_bf16(pr[0][3]) << 16);
-      pb.z = (uint32_t)tsa_bf16(pr[1][0]) | ((uint32_t)tsa_bf16(pr[1][1]) << 16);
-      pb.w = (uint32_t)tsa_bf16(pr[1][2]) | ((uint32_t)tsa_bf16(pr[1][3]) << 16);
-      // O^T += V^T P^T: V^T row n * 16 + lr (dimension), the same keys in the same order
+      // O^T += V^T P^T per 32-key half hh: P^T k slots 8 lq .. 8 lq + 7 hold keys
+      // 32 hh + 4 lq .. + 3 of its two quarters; the V^T row n * 16 + lr (dimension) is
+      // read at the same keys in the same order
 #pragma unroll
-      for (int n = 0; n < NO; ++n) {
-        const uint16_t* vr = &sm.vt[buf][Smem::vrow(n * 16 + lr)];
-        const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * lq);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * lq);
-        o[n] = mfma16(make_uint4(v0.x, v0.y, v1.x, v1.y), pb, o[n]);
+      for (int hh = 0; hh < NST / 2; ++hh) {
+        uint4 pb;
+        pb.x = (uint32_t)tsa_bf16(pr[2 * hh][0]) | ((uint32_t)tsa_bf16(pr[2 * hh][1]) << 16);
+        pb.y = (uint32_t)tsa_bf16(pr[2 * hh][2]) | ((uint32_t)tsa_bf16(pr[2 * hh][3]) << 16);
+        pb.z = (uint32_t)tsa_bf16(pr[2 * hh + 1][0]) | ((uint32_t)tsa_bf16(pr[2 * hh + 1][1]) << 16);
+        pb.w = (uint32_t)tsa_bf16(pr[2 * hh + 1][2]) | ((uint32_t)tsa_bf16(pr[2 * hh + 1][3]) << 16);
+#pragma unroll
+        for (int n = 0; n < NO; ++n) {
+          const uint16_t* vr = &sm.vt[buf][Smem::vrow(n * 16 + lr) + 32 * hh];
+          const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * lq);
+          const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * lq);
+          o[n] = mfma16(make_uint4(v0.x, v0.y, v1.x, v1.y), pb, o[n]);
+        }
       }
     };
     for (int t = 0; t < nt; t += 2) {
@@ -391,7 +398,7 @@ int tsa_queries_per_block() { return kTsaQ; }
 // workgroup walks all keys (measured faster than splitting plus the merge once the
 // chip is full).
 void tsa_splits(int64_t rows, int kk, int D, int* nsplit, int* split_keys, size_t* part_bytes) {
-  constexpr int kTsaSplitKeys = 8 * kTsaKeys;
+  constexpr int kTsaSplitKeys = 256;
   const int64_t qtiles = (kk + kTsaQ - 1) / kTsaQ;
   int ks = max(kTsaSplitKeys, ((kk + 7) / 8 + kTsaKeys - 1) / kTsaKeys * kTsaKeys);
   int ns = (kk + ks - 1) / ks;
