@@ -98,7 +98,15 @@ __device__ __forceinline__ void tsa_load(const uint16_t* Kg, const uint16_t* Vg,
   }
 }
 
-// The loaded pieces to LDS buffer `buf`: K row-major, V transposed (word j of a pair
+// LDS row of key r of a tile: within each 32-key half, key 8a + 4q + b goes to row
+// 16q + 4a + b, so that the q.k product's quarter q (LDS rows 16q .. 16q + 15, read as
+// 16 consecutive rows) leaves lane group a holding keys 8a + 4q .. + 3, and the two
+// quarters of a half together give each lane group 8 consecutive keys for P.V.
+__device__ __forceinline__ int tsa_krow(int r) {
+  return (r & ~31) | (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3);
+}
+
+// The loaded pieces to LDS buffer `buf`: K rows permuted by tsa_krow, V transposed (word j of a pair
 // holds dimension c * 8 + j of keys 2p and 2p + 1).
 template <int D>
 __device__ __forceinline__ void tsa_store(TsaSmem<D>& sm, int buf, int tid, const TsaRegs<D>& R) {
@@ -108,7 +116,8 @@ __device__ __forceinline__ void tsa_store(TsaSmem<D>& sm, int buf, int tid, cons
   for (int i = 0; i < RG::LPT; ++i) {
     const int u = tid + i * kTsaWaves * 64;
     const int r = u / (D / 8), c = u % (D / 8);
-    *reinterpret_cast<uint4*>(&sm.kt[buf][r * KS + c * 8]) = make_uint4(R.k[i].x, R.k[i].y, R.k[i].z, R.k[i].w);
+    *reinterpret_cast<uint4*>(&sm.kt[buf][tsa_krow(r) * KS + c * 8]) =
+        make_uint4(R.k[i].x, R.k[i].y, R.k[i].z, R.k[i].w);
   }
 #pragma unroll
   for (int i = 0; i < RG::LPV; ++i) {
@@ -200,8 +209,9 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
       __syncthreads();                           // tile t is in buf; the other buffer is free
       if (t + 1 < nt) tsa_store<D>(sm, buf ^ 1, tid, R);
       if (t + 2 < nt) tsa_load<D>(Kg, Vg, sm.kidx, nk, t + 2, tid, R);
-      // S^T = K Q^T over the tile's 16-key quarters: element r of s[st] is key
-      // cb + t * 64 + st * 16 + 4 lq + r against query qi
+      // S^T = K Q^T over the tile's four 16-row quarters (LDS rows st * 16 ..): element
+      // r of s[st] is key cb + t * 64 + 32 (st >> 1) + 8 lq + 4 (st & 1) + r against
+      // query qi
       constexpr int NST = kTsaKeys / 16;
       tsa_f32x4_t s[NST];
 #pragma unroll
@@ -224,7 +234,7 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if constexpr (decltype(masked)::value) {
-              const int key = kt0 + st * 16 + 4 * lq + r;
+              const int key = kt0 + 32 * (st >> 1) + 8 * lq + 4 * (st & 1) + r;
               const bool ok = key < k_hi && (!p.causal || key <= qi);
               x[st][r] = ok ? s[st][r] * sl : -LD_INF;
             } else {
@@ -263,8 +273,8 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
           for (int r = 0; r < 4; ++r) o[n][r] *= alpha;
       }
       // O^T += V^T P^T per 32-key half hh: P^T k slots 8 lq .. 8 lq + 7 hold keys
-      // 32 hh + 4 lq .. + 3 of its two quarters; the V^T row n * 16 + lr (dimension) is
-      // read at the same keys in the same order
+      // 32 hh + 8 lq .. + 7 (quarter 2 hh, then 2 hh + 1); the V^T row n * 16 + lr
+      // (dimension) is read at the same keys, 16 consecutive bytes
 #pragma unroll
       for (int hh = 0; hh < NST / 2; ++hh) {
         uint4 pb;
@@ -274,10 +284,8 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
         pb.w = (uint32_t)tsa_bf16(pr[2 * hh + 1][2]) | ((uint32_t)tsa_bf16(pr[2 * hh + 1][3]) << 16);
 #pragma unroll
         for (int n = 0; n < NO; ++n) {
-          const uint16_t* vr = &sm.vt[buf][Smem::vrow(n * 16 + lr) + 32 * hh];
-          const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * lq);
-          const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * lq);
-          o[n] = mfma16(make_uint4(v0.x, v0.y, v1.x, v1.y), pb, o[n]);
+          const uint4 va = *reinterpret_cast<const uint4*>(&sm.vt[buf][Smem::vrow(n * 16 + lr) + 32 * hh + 8 * lq]);
+          o[n] = mfma16(va, pb, o[n]);
         }
       }
     };
