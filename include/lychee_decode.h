@@ -212,7 +212,8 @@ ld_status ld_hysparse_layer(const ld_shape* shape, const void* q, const void* k_
    head_dim (64 or 128), seq_len = T (1..2^21), softmax_scale (0 = 1/sqrt(d)),
    total_tokens 0 or B*T; kv_indptr, paging and kv_dtype must be unset
    (LD_ERR_UNSUPPORTED otherwise). The workspace holds ld_tsa_workspace_size(shape, k)
-   bytes for a budget k (or any smaller one), zeroed once. Asynchronous on `stream`; errors are found before the first launch.
+   bytes for a budget k (or any smaller one), zeroed once. Asynchronous on `stream`;
+   errors are found before the first launch.
    flags & LD_TSA_GIVEN_IDX: no selection; idx_out already holds the caller's sets
    (ascending distinct positions in 0..T-1, min(k,T) per row; positions outside the
    sequence are clamped to it) and scores may be NULL. */
@@ -232,7 +233,8 @@ ld_status ld_tsa_attention(const ld_shape* shape, const void* q, const void* k_c
    NULL only when every head is a retrieval head (layer 0, method step 1). A KV head
    whose query heads include a retrieval head streams its whole cache once for all of
    them; a KV head serving only sparse heads reads the union of their sets once.
-   flags: LD_FLAG_SKIP_TOPK, LD_FLAG_S_CHAINED, LD_FLAG_SPLIT_ROWS(). scores_out as in
+   flags: LD_FLAG_SKIP_TOPK, LD_FLAG_S_CHAINED, LD_FLAG_SEPARATE_SELECT,
+   LD_FLAG_BLOCK_SELECT, LD_FLAG_SPLIT_ROWS(), LD_FLAG_WAVES(). scores_out as in
    ld_retrieval_decode (retrieval heads only; may be NULL). */
 ld_status ld_hybrid_layer(const ld_shape* shape, uint64_t retrieval_mask,
                           const void* q, const void* k_cache, const void* v_cache,
