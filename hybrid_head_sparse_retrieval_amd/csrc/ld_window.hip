@@ -5,11 +5,12 @@
 // writes O, mixing both through the sigmoid gate.
 //
 // One workgroup of four waves per (sequence, query head): wave w takes the window's
-// 64-token rounds w, w + 4, ... For a round, lane t computes the logit of token t (it
-// reads its key row), and the lanes then split the head dimension for P·V over
-// coalesced value rows, the weights broadcast from the lane that owns them; every load
-// of a round is issued before the first use, so a round waits for memory once. The
-// waves' online-softmax states are merged through LDS at the end.
+// 32-token rounds w, w + 4, ... For a round, lanes t and t + 32 compute the two halves
+// of the logit of token t (each reads half its key row), and the lanes then split the
+// head dimension for P·V over coalesced value rows, the weights broadcast from the lane
+// that owns them; every load of a round is issued before the first use, so a round
+// waits for memory once. The waves' online-softmax states are merged through LDS at the
+// end.
 
 #include "ld_device.h"
 
@@ -39,41 +40,46 @@ __global__ __launch_bounds__(kWinWaves * 64) void k_window(WindowParams p) {
   float acc[DL];
 #pragma unroll
   for (int j = 0; j < DL; ++j) acc[j] = 0.f;
-  for (int t0 = wave * 64; t0 < p.W; t0 += kWinWaves * 64) {
-    const int t = t0 + lane;
-    // the lane's key row and, for its DL dims, the round's 64 value rows (rows past the
-    // window repeat the last row and get weight 0)
-    uint4 kr[D / 8];
-    uint32_t vv[64];
-    const uint4* kp = reinterpret_cast<const uint4*>(K + (size_t)min(t, p.W - 1) * D);
+  constexpr int RT = 32;        // tokens per round; lanes t and t + 32 split the token's dot product
+  constexpr int HD = D / 2;     // dimensions per half
+  const int tl = lane & 31, half = lane >> 5;
+  for (int t0 = wave * RT; t0 < p.W; t0 += kWinWaves * RT) {
+    const int t = t0 + tl;
+    // half of the lane's key row and, for its DL dims, the round's 32 value rows (rows
+    // past the window repeat the last row and get weight 0)
+    uint4 kr[HD / 8];
+    uint32_t vv[RT];
+    const uint4* kp = reinterpret_cast<const uint4*>(K + (size_t)min(t, p.W - 1) * D + half * HD);
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i) kr[i] = kp[i];
+    for (int i = 0; i < HD / 8; ++i) kr[i] = kp[i];
 #pragma unroll
-    for (int u = 0; u < 64; ++u) {
+    for (int u = 0; u < RT; ++u) {
       const uint16_t* vr = V + (size_t)min(t0 + u, p.W - 1) * D + lane * DL;
       vv[u] = (DL == 2) ? *reinterpret_cast<const uint32_t*>(vr) : (uint32_t)*vr;
     }
     float a = 0.f;
+    const float* qh = &qs[half * HD];
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
+    for (int i = 0; i < HD / 8; ++i) {
       const uint4 v = kr[i];
-      const float4 q0 = *reinterpret_cast<const float4*>(&qs[i * 8]);
-      const float4 q1 = *reinterpret_cast<const float4*>(&qs[i * 8 + 4]);
+      const float4 q0 = *reinterpret_cast<const float4*>(&qh[i * 8]);
+      const float4 q1 = *reinterpret_cast<const float4*>(&qh[i * 8 + 4]);
       a = fmaf(bf_lo(v.x & 0xffffu), q0.x, a); a = fmaf(bf_lo(v.x >> 16), q0.y, a);
       a = fmaf(bf_lo(v.y & 0xffffu), q0.z, a); a = fmaf(bf_lo(v.y >> 16), q0.w, a);
       a = fmaf(bf_lo(v.z & 0xffffu), q1.x, a); a = fmaf(bf_lo(v.z >> 16), q1.y, a);
       a = fmaf(bf_lo(v.w & 0xffffu), q1.z, a); a = fmaf(bf_lo(v.w >> 16), q1.w, a);
     }
+    a = add_xor32(a);                            // both halves of the dot product, in both lanes
     const float s = (t < p.W) ? a * p.scale : -LD_INF;
     const float mn = fmaxf(m, wave_max_f(s));   // finite: the round holds token t0
     const float pt = (t < p.W) ? expf(s - mn) : 0.f;
     const float corr = (m == -LD_INF) ? 0.f : expf(m - mn);
-    l = fmaf(l, corr, wave_sum_f(pt));
+    l = fmaf(l, corr, wave_sum_f(half == 0 ? pt : 0.f));   // each token once
 #pragma unroll
     for (int j = 0; j < DL; ++j) acc[j] *= corr;
     const uint32_t pb = __float_as_uint(pt);
 #pragma unroll
-    for (int u = 0; u < 64; ++u) {
+    for (int u = 0; u < RT; ++u) {
       const float pu = __uint_as_float(__builtin_amdgcn_readlane(pb, u));
       acc[0] = fmaf(pu, bf_lo(vv[u] & 0xffffu), acc[0]);
       if (DL == 2) acc[DL - 1] = fmaf(pu, bf_lo(vv[u] >> 16), acc[DL - 1]);
