@@ -97,3 +97,8 @@ def test_tsa_given_sets_equal_selected_sets():
     out2, _ = ld.tsa_attention(qd, kd, vd, None, 500, idx_out=idx.clone(), causal=True, given_idx=True, batch=1)
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+def test_tsa_at_the_longest_sequence():
+    """T = 2^21 tokens (the longest sequence the selection takes), two heads, small k."""
+    _check(_ld(), 1, 2, 1, 64, 1 << 21, 100, True, seed=2024)
