@@ -27,6 +27,7 @@ def _ld():
     ([5000, 1400], 8, 1, 128, 1000, 300, 973),
     ([6000], 8, 2, 128, 1500, 4096, 974),       # the largest window
     ([2500, 2500], 4, 2, 64, 800, 200, 975),
+    ([2048], 64, 8, 64, 256, 16, 976),          # 64 query heads: every bit of the head masks
 ])
 def test_hysparse_layer_matches_oracle(case):
     lens, Hq, Hkv, d, k, W, seed = case
