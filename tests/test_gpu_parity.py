@@ -87,6 +87,7 @@ def run_layers(B, Hq, Hkv, d, lens, masks, seed, k=None, csr=False, chain=True, 
     (1, 16, 2, 128, [1100], [0xFFFF, 0x0101, 0], 3),                 # GQA 8:1
     (1, 8, 4, 64, [2049], [0xFF, 0b01000010, 0], 4),                 # GQA 2:1, tail of 1 row
     (1, 32, 8, 128, [4096], wl.seeded_masks(5, 3, 32, 2), 5),        # Llama head shape
+    (1, 64, 8, 128, [3000], [(1 << 64) - 1, (1 << 63) | 1, 0], 6),   # 64 query heads: every mask bit
 ])
 def test_layers_match_oracle(case):
     B, Hq, Hkv, d, lens, masks, seed = case
