@@ -65,6 +65,8 @@ def _check(ld, B, Hq, Hkv, d, T, k, causal, seed, zero_fill=True):
     (1, 2, 1, 128, 50, 80, False),       # budget above T: clamped
     (1, 2, 2, 128, 700, 1, True),        # one token
     (1, 8, 2, 128, 20000, 1024, True),   # the page's budget range, several tiles and query blocks
+    (1, 4, 2, 64, 3000, 700, False),     # a small grid: key splits and their merge, d = 64
+    (1, 4, 2, 64, 3000, 700, True),
 ])
 def test_tsa_matches_oracle(case):
     B, Hq, Hkv, d, T, k, causal = case
