@@ -105,6 +105,97 @@ __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
   hist1_clear(p.hist1, v.slot);
 }
 
+// ------------------------------------------------ short standalone rows
+
+// A standalone row of at most kSmallRow scores in one workgroup: the keys stay in
+// registers (kSmallPer contiguous ones per thread), three digit histograms in LDS give
+// the threshold key T and the number k3 of keys equal to T to keep (the lowest
+// indices), and two workgroup scans place the kept indices in ascending order.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallPer = 4;
+constexpr int kSmallRow = kSmallThreads * kSmallPer;
+
+// Exclusive prefix of x over the workgroup (thread order); wsum: __shared__ int[16].
+__device__ __forceinline__ int block_excl_scan(int x, int* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int wt;
+  const int before = wave_excl_scan(x, wt);
+  if (lane == 0) wsum[wave] = wt;
+  __syncthreads();
+  int off = 0;
+#pragma unroll
+  for (int w = 0; w < kSmallThreads / 64; ++w) off += (w < wave) ? wsum[w] : 0;
+  __syncthreads();
+  return off + before;
+}
+
+__global__ __launch_bounds__(kSmallThreads) void k_sel_small(const SelParams p) {
+  __shared__ uint32_t hist[kHist1Bins];
+  __shared__ int tmp[kSmallThreads / 64];
+  __shared__ int wsum[kSmallThreads / 64];
+  __shared__ uint32_t res[2];
+  const int tid = threadIdx.x;
+  const RowView v = row_view(p, blockIdx.x);
+  const int n = v.n;
+  const uint32_t k = (uint32_t)v.k;
+  uint32_t key[kSmallPer];
+  bool in[kSmallPer];
+#pragma unroll
+  for (int e = 0; e < kSmallPer; ++e) {
+    const int i = tid * kSmallPer + e;
+    in[e] = i < n;
+    key[e] = in[e] ? score_key(v.sc[i]) : 0u;
+  }
+  // digit i: the histogram of the keys that match the digits above, and the bin that
+  // holds the k-th largest of them
+  auto digit = [&](int nb, int shift, uint32_t mask, int pshift, uint32_t prefix, uint32_t kk, uint32_t* bin,
+                   uint32_t* left) {
+    for (int i = tid; i < nb; i += kSmallThreads) hist[i] = 0u;
+    if (tid == 0) { res[0] = 0u; res[1] = 0u; }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e)
+      if (in[e] && (pshift >= 32 || (key[e] >> pshift) == prefix)) atomicAdd(&hist[(key[e] >> shift) & mask], 1u);
+    __syncthreads();
+    if (nb == kHist1Bins)
+      find_bin_from_top<kHist1Bins, kSmallThreads>([&](int i) { return hist[i]; }, kk, tmp, res);
+    else
+      find_bin_from_top<kHist3Bins, kSmallThreads>([&](int i) { return hist[i]; }, kk, tmp, res);
+    *bin = res[0];
+    *left = kk - res[1];
+    __syncthreads();
+  };
+  uint32_t b1, k1, b2, k2, b3, k3;
+  digit(kHist1Bins, 21, 0x7ffu, 32, 0u, k, &b1, &k1);
+  digit(kHist2Bins, 10, 0x7ffu, 21, b1, k1, &b2, &k2);
+  digit(kHist3Bins, 0, 0x3ffu, 10, (b1 << 11) | b2, k2, &b3, &k3);
+  const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
+  // keys equal to T before this thread's, then the kept keys before this thread's
+  int eq = 0;
+#pragma unroll
+  for (int e = 0; e < kSmallPer; ++e) eq += (in[e] && key[e] == T) ? 1 : 0;
+  int eq_before = block_excl_scan(eq, wsum);
+  bool kf[kSmallPer];
+  int kc = 0;
+#pragma unroll
+  for (int e = 0; e < kSmallPer; ++e) {
+    const bool tie = in[e] && key[e] == T;
+    kf[e] = in[e] && (key[e] > T || (tie && (uint32_t)eq_before < k3));
+    eq_before += tie ? 1 : 0;
+    kc += kf[e] ? 1 : 0;
+  }
+  int q = block_excl_scan(kc, wsum);
+#pragma unroll
+  for (int e = 0; e < kSmallPer; ++e) {
+    if (kf[e]) {
+      const int i = tid * kSmallPer + e;
+      v.out[q] = i;
+      if (v.vout) v.vout[q] = v.sc[i];
+      ++q;
+    }
+  }
+}
+
 // ------------------------------------------------ spans of kSelSpan scores
 
 constexpr int kSpanThreads = 1024;
@@ -690,6 +781,10 @@ int64_t fused_capacity() {
 }
 
 hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist) {
+  if (with_hist && p.mode == 0 && p.n <= kSmallRow) {
+    hipLaunchKernelGGL(k_sel_small, dim3((unsigned)p.nrows), dim3(kSmallThreads), 0, st, p);
+    return hipGetLastError();
+  }
   if (with_hist) {
     SelParams ph = p;
     ph.C = p.Ch;
