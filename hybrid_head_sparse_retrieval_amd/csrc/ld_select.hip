@@ -72,6 +72,22 @@ __device__ __forceinline__ RowView row_view(const SelParams& p, int r) {
 
 // ------------------------------------------------------------- digit-1 histogram
 
+// Digit-1 counts of NB * 4 * kThreads scores from s (16-byte aligned): every load is
+// issued before the first count, so the chunk waits for memory once.
+template <int NB>
+__device__ __forceinline__ void hist1_whole(const float* __restrict__ s, uint32_t* hist, int tid) {
+  float4 x[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) x[u] = reinterpret_cast<const float4*>(s)[u * kThreads + tid];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    atomicAdd(&hist[score_key(x[u].x) >> 21], 1u);
+    atomicAdd(&hist[score_key(x[u].y) >> 21], 1u);
+    atomicAdd(&hist[score_key(x[u].z) >> 21], 1u);
+    atomicAdd(&hist[score_key(x[u].w) >> 21], 1u);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
   __shared__ uint32_t hist[kHist1Bins];
   __shared__ int tmp[4];
@@ -84,9 +100,22 @@ __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
   const int tid = threadIdx.x;
   for (int i = tid; i < kHist1Bins; i += kThreads) hist[i] = 0;
   __syncthreads();
-  const int hi = min(v.n, (c + 1) * hc);
+  const int lo = c * hc, hi = min(v.n, lo + hc);
+  const float* s = v.sc + lo;
+  constexpr int kVec = 4 * kThreads;   // scores per round of float4 loads
+  if (hi - lo == hc && hc % kVec == 0 && (reinterpret_cast<uintptr_t>(s) & 15u) == 0) {
+    // a whole chunk (hc is a power of two): rounds of up to 8 float4 loads per thread
+    for (int j = 0; j < hc / kVec;) {
+      const int left = hc / kVec - j;
+      if (left >= 8) { hist1_whole<8>(s + j * kVec, hist, tid); j += 8; }
+      else if (left >= 4) { hist1_whole<4>(s + j * kVec, hist, tid); j += 4; }
+      else if (left >= 2) { hist1_whole<2>(s + j * kVec, hist, tid); j += 2; }
+      else { hist1_whole<1>(s + j * kVec, hist, tid); j += 1; }
+    }
+  } else {
 #pragma unroll 4
-  for (int i = c * hc + tid; i < hi; i += kThreads) atomicAdd(&hist[score_key(v.sc[i]) >> 21], 1u);
+    for (int i = lo + tid; i < hi; i += kThreads) atomicAdd(&hist[score_key(v.sc[i]) >> 21], 1u);
+  }
   __syncthreads();
   uint32_t* gh = hist1_mine(p.hist1, v.slot);
   for (int i = tid; i < kHist1Bins; i += kThreads)

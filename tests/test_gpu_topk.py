@@ -113,6 +113,15 @@ def test_more_spans_than_resident_workgroups():
     _check(x, 5100, with_vals=False)
 
 
+@pytest.mark.parametrize("rows,n,k", [
+    (32, 131072, 1024),    # 8192-score digit-1 chunks: one round of 8 float4 loads per thread
+    (8, 131072, 40000),    # 2048-score chunks
+    (40, 16385, 5000),     # rows whose starts are not 16-byte aligned take the scalar loads
+])
+def test_digit1_chunk_sizes(rows, n, k):
+    _check(_rng(7 + rows).normal(size=(rows, n)).astype(np.float32), k, with_vals=False)
+
+
 def test_one_and_two_kernel_paths_agree_bitwise():
     ld = _ld()
     rng = _rng(6)
