@@ -104,3 +104,41 @@ def test_tsa_given_sets_equal_selected_sets():
 def test_tsa_at_the_longest_sequence():
     """T = 2^21 tokens (the longest sequence the selection takes), two heads, small k."""
     _check(_ld(), 1, 2, 1, 64, 1 << 21, 100, True, seed=2024)
+
+
+def test_tsa_at_the_bench_configuration():
+    """The timed configuration: B = 1, 32 query and 8 KV heads, d = 128, T = 131072,
+    k = 1024 per head, causal, residual scatter. Every head's selection equals the
+    oracle's bit for bit; the dense stage of every head is checked against the oracle
+    run on that head's selected rows alone (attention among the selected tokens is all
+    the dense stage computes, and the ascending order keeps the causal order); a sample
+    of unselected rows keeps what the caller wrote."""
+    ld = _ld()
+    dev = "cuda"
+    B, Hq, Hkv, d, T, k = 1, 32, 8, 128, 131072, 1024
+    g = torch.Generator(device=dev).manual_seed(wl.stream_seed("tsa-bench", T, k))
+    q = torch.randn((Hq, B * T, d), generator=g, device=dev).to(torch.bfloat16)
+    kc = torch.randn((Hkv, B * T, d), generator=g, device=dev).to(torch.bfloat16)
+    vc = torch.randn((Hkv, B * T, d), generator=g, device=dev).to(torch.bfloat16)
+    sc = torch.randn((B, Hq, T), generator=g, device=dev)
+    out = torch.full_like(q, 7.0)
+    out, idx = ld.tsa_attention(q, kc, vc, sc, k, out=out, causal=True, zero_fill=False)
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    sc_h = sc.cpu().numpy()
+    rng = np.random.default_rng(3)
+    for h in range(Hq):
+        want = orc.select_topk_f32(sc_h[0, h], k)
+        assert np.array_equal(idx_h[0, h], want), f"selection of head {h}"
+        sel = torch.as_tensor(want, device=dev)
+        gk = h // (Hq // Hkv)
+        qs = gh.bf16_tensor_to_f64(q[h, sel].cpu())[None]
+        ks = gh.bf16_tensor_to_f64(kc[gk, sel].cpu())[None]
+        vs = gh.bf16_tensor_to_f64(vc[gk, sel].cpu())[None]
+        ref, _ = orc.tsa_attention(qs, ks, vs, np.zeros((1, 1, k)), k, causal=True)
+        got = gh.bf16_tensor_to_f64(out[h, sel].cpu())
+        err = np.abs(got - ref[0])
+        rel = np.linalg.norm(got - ref[0]) / np.linalg.norm(ref[0])
+        assert err.max() <= gh.MAX_ABS and rel <= gh.REL_L2, f"head {h}: {err.max():.3e} {rel:.3e}"
+        others = np.setdiff1d(rng.integers(0, T, size=2048), want)
+        assert torch.all(out[h, torch.as_tensor(others, device=dev)] == 7.0), f"unselected rows of head {h}"
