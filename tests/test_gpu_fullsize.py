@@ -106,3 +106,67 @@ def test_fullsize_step(name, layers):
                 assert err <= gh.MAX_ABS and rel <= gh.REL_L2, (name, l, b, h, err, rel)
                 checked += 1
     assert checked >= 3 * len(sampled_layers), checked
+
+
+def test_hysparse_block_with_block_selection_and_window():
+    """The HySparse group as timed with block selection and a 128-token window branch
+    (N = 131072, k = 4096, 1 full + 6 sparse layers on the full layer's cache): every
+    head's S equals the oracle's block selection on the layer's own fp32 logits, sampled
+    full-layer heads match the oracle's attention, every head of the first and the last
+    sparse layer matches the oracle's gated layer, and S passes through the sparse
+    layers unchanged."""
+    import hybrid_head_sparse_retrieval_amd as ld
+    from hybrid_head_sparse_retrieval_amd.step import DecodeStep
+    ld.load_library()
+    w = wl.get_workload("hysparse_7layer")
+    dev = "cuda"
+    B, Hq, Hkv, d, L, N, W = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.layers, w.max_seq, 128
+    G = Hq // Hkv
+    k = w.k_per_seq[0]
+    x0 = wl.make_layer_inputs(w, 0, device=dev)
+    kc, vc = x0.k, x0.v
+    qs = [x0.q] + [wl.make_layer_inputs(w, l, device=dev).q for l in range(1, L)]
+    windows = [None]
+    gen = torch.Generator(device="cpu")
+    for l in range(1, L):
+        gen.manual_seed(wl.stream_seed("window", w.name, l))
+        kw = torch.randn((Hkv, B * W, d), generator=gen).to(torch.bfloat16).to(dev)
+        vw = torch.randn((Hkv, B * W, d), generator=gen).to(torch.bfloat16).to(dev)
+        gate = torch.randn((B, Hq), generator=gen).to(dev)
+        windows.append((kw, vw, gate))
+    step = DecodeStep(B, Hq, Hkv, d, w.seq_lens, w.k_per_seq, w.retrieval_masks, device=dev,
+                      split_flag=ld.FLAG_BLOCK_SELECT, window_len=W)
+    scores = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device=dev)
+    step.layer(0, qs[0], kc, vc, scores_out=scores)
+    torch.cuda.synchronize()
+    S0 = step.s_rows()
+    sc = scores.cpu().numpy()
+    for h in range(Hq):
+        assert np.array_equal(S0[(0, h)], orc.select_topk_blocks(sc[0, h], k)), f"block selection of head {h}"
+    K = orc.bf16_bits_to_f64(wl.bf16_bits(kc))
+    V = orc.bf16_bits_to_f64(wl.bf16_bits(vc))
+    scale = orc.default_scale(d)
+    O0 = orc.bf16_bits_to_f64(wl.bf16_bits(step.outs[0]))
+    q0 = orc.bf16_bits_to_f64(wl.bf16_bits(qs[0]))
+    for h in (0, 13, 31):
+        O, _, _ = orc.retrieval_head(q0[0, h], K[h // G], V[h // G], k, scale)
+        err = np.abs(O0[0, h] - O).max()
+        rel = np.linalg.norm(O0[0, h] - O) / np.linalg.norm(O)
+        assert err <= gh.MAX_ABS and rel <= gh.REL_L2, ("full layer", h, err, rel)
+    for l in range(1, L):
+        step.layer(l, qs[l], kc, vc, window=windows[l])
+        torch.cuda.synchronize()
+        S = step.s_rows()
+        for h in range(Hq):
+            assert np.array_equal(S[(0, h)], S0[(0, h)]), f"layer {l} changed the S row of head {h}"
+        if l not in (1, L - 1):
+            continue
+        kw, vw, gate = windows[l]
+        ref = orc.hysparse_sparse_layer(orc.bf16_bits_to_f64(wl.bf16_bits(qs[l])), K, V, [0, N], S0,
+                                        orc.bf16_bits_to_f64(wl.bf16_bits(kw)),
+                                        orc.bf16_bits_to_f64(wl.bf16_bits(vw)), gate.cpu().numpy(), scale)
+        got = orc.bf16_bits_to_f64(wl.bf16_bits(step.outs[l]))
+        for h in range(Hq):
+            err = np.abs(got[0, h] - ref[0, h]).max()
+            rel = np.linalg.norm(got[0, h] - ref[0, h]) / np.linalg.norm(ref[0, h])
+            assert err <= gh.MAX_ABS and rel <= gh.REL_L2, ("sparse layer", l, h, err, rel)
