@@ -35,13 +35,19 @@ def _check_rows(S_rows, lens, B, Hq):
             assert s[0] >= 0 and s[-1] < lens[b]
 
 
-@pytest.mark.parametrize("name,layers", [
-    ("llama3_8b_32k", None),
-    ("qwen3_8b_128k", 8),
-    ("ragged_b8", 6),
-    ("hysparse_7layer", None),
+def _e4m3(x):
+    """E4M3 codes (uint8) of the same draws, rounded to nearest even by torch."""
+    return x.float().to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+@pytest.mark.parametrize("name,layers,kv", [
+    ("llama3_8b_32k", None, "bf16"),
+    ("qwen3_8b_128k", 8, "bf16"),
+    ("ragged_b8", 6, "bf16"),
+    ("hysparse_7layer", None, "bf16"),
+    ("llama3_8b_32k", 8, "e4m3"),        # 8-bit E4M3 KV codes with unit scales
 ])
-def test_fullsize_step(name, layers):
+def test_fullsize_step(name, layers, kv):
     import hybrid_head_sparse_retrieval_amd as ld
     from hybrid_head_sparse_retrieval_amd.step import DecodeStep
     ld.load_library()
@@ -54,9 +60,17 @@ def test_fullsize_step(name, layers):
     inputs = []
     for l in range(L):
         x = wl.make_layer_inputs(w, l, device=dev)
+        if x.k is not None and kv == "e4m3":
+            x.k, x.v = _e4m3(x.k), _e4m3(x.v)
         inputs.append((x.q, x.k, x.v) if x.k is not None else (x.q, inputs[0][1], inputs[0][2]))
     step = DecodeStep(B, Hq, Hkv, d, w.seq_lens, w.k_per_seq, w.retrieval_masks,
                       csr=w.ragged_csr, device=dev)
+    if kv == "e4m3":
+        def kv_f64(t):
+            return orc.fp8_e4m3_to_f64(t.cpu().numpy())
+    else:
+        def kv_f64(t):
+            return orc.bf16_bits_to_f64(wl.bf16_bits(t))
     lens = list(w.seq_lens)
     offs = w.kv_offsets()
     scores = torch.full((B, Hq, w.max_seq), float("nan"), dtype=torch.float32, device=dev)
@@ -90,8 +104,8 @@ def test_fullsize_step(name, layers):
                 g = h // G
                 if (b, g) not in kv_cache:
                     lo, hi = int(offs[b]), int(offs[b + 1])
-                    Kg = orc.bf16_bits_to_f64(wl.bf16_bits(kc[g, lo:hi]))
-                    Vg = orc.bf16_bits_to_f64(wl.bf16_bits(vc[g, lo:hi]))
+                    Kg = kv_f64(kc[g, lo:hi])
+                    Vg = kv_f64(vc[g, lo:hi])
                     kv_cache[(b, g)] = (Kg, Vg)
                 Kg, Vg = kv_cache[(b, g)]
                 qh = orc.bf16_bits_to_f64(qb[b, h])
