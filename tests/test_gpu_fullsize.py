@@ -40,14 +40,37 @@ def _e4m3(x):
     return x.float().to(torch.float8_e4m3fn).view(torch.uint8)
 
 
-@pytest.mark.parametrize("name,layers,kv", [
-    ("llama3_8b_32k", None, "bf16"),
-    ("qwen3_8b_128k", 8, "bf16"),
-    ("ragged_b8", 6, "bf16"),
-    ("hysparse_7layer", None, "bf16"),
-    ("llama3_8b_32k", 8, "e4m3"),        # 8-bit E4M3 KV codes with unit scales
+def _paged(kc, vc, offs, page, seed):
+    """K/V moved into pools of `page`-row pages in a seeded random order, with the
+    block table that maps each sequence's pages."""
+    B = len(offs) - 1
+    npp = [(int(offs[b + 1] - offs[b]) + page - 1) // page for b in range(B)]
+    perm = np.random.default_rng(seed).permutation(sum(npp))
+    Hkv, _, d = kc.shape
+    kp = torch.zeros((Hkv, sum(npp) * page, d), dtype=kc.dtype, device=kc.device)
+    vp = torch.zeros_like(kp)
+    bt = np.zeros((B, max(npp)), dtype=np.int32)
+    j = 0
+    for b in range(B):
+        for i in range(npp[b]):
+            pid = int(perm[j]); j += 1
+            bt[b, i] = pid
+            r0 = int(offs[b]) + i * page
+            r1 = min(int(offs[b + 1]), r0 + page)
+            kp[:, pid * page: pid * page + r1 - r0] = kc[:, r0:r1]
+            vp[:, pid * page: pid * page + r1 - r0] = vc[:, r0:r1]
+    return kp, vp, torch.as_tensor(bt, device=kc.device)
+
+
+@pytest.mark.parametrize("name,layers,kv,page", [
+    ("llama3_8b_32k", None, "bf16", 0),
+    ("qwen3_8b_128k", 8, "bf16", 0),
+    ("ragged_b8", 6, "bf16", 0),
+    ("hysparse_7layer", None, "bf16", 0),
+    ("llama3_8b_32k", 8, "e4m3", 0),      # 8-bit E4M3 KV codes with unit scales
+    ("qwen3_8b_128k", 4, "e4m3", 64),     # E4M3 codes in 64-row pages of a shuffled pool
 ])
-def test_fullsize_step(name, layers, kv):
+def test_fullsize_step(name, layers, kv, page):
     import hybrid_head_sparse_retrieval_amd as ld
     from hybrid_head_sparse_retrieval_amd.step import DecodeStep
     ld.load_library()
@@ -82,7 +105,12 @@ def test_fullsize_step(name, layers, kv):
     for l in range(L):
         q, kc, vc = inputs[l]
         S_before = step.s_rows() if l > 0 else None
-        step.layer(l, q, kc, vc, scores_out=scores)
+        if page:
+            kp, vp, bt = _paged(kc, vc, w.kv_offsets(), page, seed=l)
+            step.layer(l, q, kp, vp, scores_out=scores, block_table=bt, page_size=page)
+            del kp, vp
+        else:
+            step.layer(l, q, kc, vc, scores_out=scores)
         torch.cuda.synchronize()
         S_after = step.s_rows()
         _check_rows(S_after, lens, B, Hq)
