@@ -294,6 +294,26 @@ def _opt(t, dtype, name):
     return None if t is None else _req(t, dtype, name)
 
 
+def _sizes(shape, q, out, k, kv_indptr=None, s_bufs=(), s_indptr=None, scores_out=None):
+    """Sizes of the caller's buffers against the shape: the kernels write them without
+    bounds of their own. CSR S rows are sized by device-side offsets, so only the offset
+    array is checked for them."""
+    B, Hq = int(shape.batch), int(shape.num_q_heads)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q [B][Hq][d]")
+    if kv_indptr is not None and kv_indptr.numel() != B + 1:
+        raise ValueError("kv_indptr must hold B+1 offsets")
+    if s_indptr is not None:
+        if s_indptr.numel() != B * Hq + 1:
+            raise ValueError("s_indptr must hold B*Hq+1 offsets")
+    else:
+        for name, t in s_bufs:
+            if t is not None and t.numel() < B * Hq * int(k):
+                raise ValueError(f"{name} must hold B*Hq*k indices ([B][Hq][k])")
+    if scores_out is not None and scores_out.numel() < B * Hq * int(shape.seq_len):
+        raise ValueError("scores_out must hold B*Hq*seq_len values ([B][Hq][seq_len])")
+
+
 def _is_fp8(t) -> bool:
     torch = _torch()
     return t.dtype == torch.uint8 or t.dtype == getattr(torch, "float8_e4m3fn", None)
@@ -324,6 +344,7 @@ def retrieval_decode(q, k_cache, v_cache, head_mask: int, k: int, *, s_out=None,
     shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size, k_scale, v_scale)
     _opt(s_out, torch.int32, "s_out"); _opt(s_indptr, torch.int64, "s_indptr")
     _opt(scores_out, torch.float32, "scores_out")
+    _sizes(shape, q, out, k, kv_indptr, [("s_out", s_out)], s_indptr, scores_out)
     ws = workspace or Workspace(shape, k, q.device)
     _check(load_library().ld_retrieval_decode(
         ctypes.byref(shape), int(head_mask), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -341,6 +362,7 @@ def sparse_decode(q, k_cache, v_cache, head_mask: int, k: int, s_in, *, s_indptr
     out = _prep(q, k_cache, v_cache, out, kv_indptr)
     shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size, k_scale, v_scale)
     _req(s_in, torch.int32, "s_in"); _opt(s_indptr, torch.int64, "s_indptr")
+    _sizes(shape, q, out, k, kv_indptr, [("s_in", s_in)], s_indptr)
     ws = workspace or Workspace(shape, k, q.device)
     _check(load_library().ld_sparse_decode(
         ctypes.byref(shape), int(head_mask), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -362,6 +384,7 @@ def hybrid_layer(q, k_cache, v_cache, retrieval_mask: int, k: int, s, *, s_out=N
     _opt(s_indptr, torch.int64, "s_indptr"); _opt(scores_out, torch.float32, "scores_out")
     if s_out is None:
         s_out = s
+    _sizes(shape, q, out, k, kv_indptr, [("s", s), ("s_out", s_out)], s_indptr, scores_out)
     ws = workspace or Workspace(shape, k, q.device)
     _check(load_library().ld_hybrid_layer(
         ctypes.byref(shape), int(retrieval_mask), q.data_ptr(), k_cache.data_ptr(),
@@ -390,6 +413,7 @@ def hysparse_layer(q, k_cache, v_cache, k: int, s_in, k_window, v_window, gate, 
         raise ValueError("k_window/v_window must be [Hkv][B*W][d] and match each other")
     if gate.numel() != B * Hq:
         raise ValueError("gate must hold B*Hq values")
+    _sizes(shape, q, out, k, kv_indptr, [("s_in", s_in)], s_indptr)
     W = k_window.shape[1] // B
     ws = workspace or HySparseWorkspace(shape, k, W, q.device)
     _check(load_library().ld_hysparse_layer(
@@ -461,6 +485,9 @@ def topk_select(scores, k: int, *, idx_out=None, val_out=None,
     if idx_out is None:
         idx_out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
     _req(idx_out, torch.int32, "idx_out"); _opt(val_out, torch.float32, "val_out")
+    for name, t in (("idx_out", idx_out), ("val_out", val_out)):
+        if t is not None and t.numel() < rows * int(k):
+            raise ValueError(f"{name} must hold rows*k entries")
     ws = workspace or TopkWorkspace(rows, n, scores.device)
     _check(load_library().ld_topk_select(
         scores.data_ptr(), int(rows), int(n), int(row_stride), int(k), idx_out.data_ptr(),

@@ -303,3 +303,27 @@ def test_wait_flag_is_reported_and_cleared():
         with pytest.raises(ld.LycheeDecodeError, match="bounded wait"):
             ws.check()
         ws.check()
+
+
+def test_undersized_buffers_are_rejected_before_launch():
+    import hybrid_head_sparse_retrieval_amd as ld
+    ld.load_library()
+    dev = "cuda"
+    B, Hq, Hkv, d, n, k = 1, 8, 2, 128, 512, 100
+    q = torch.zeros((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    kc = torch.zeros((Hkv, B * n, d), dtype=torch.bfloat16, device=dev)
+    S = torch.zeros((B, Hq, k), dtype=torch.int32, device=dev)
+    small = torch.zeros((B, Hq, k - 1), dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError, match="s_out"):
+        ld.hybrid_layer(q, kc, kc, 0xFF, k, None, s_out=small)
+    with pytest.raises(ValueError, match="s_in"):
+        ld.sparse_decode(q, kc, kc, 0xFF, k, small)
+    with pytest.raises(ValueError, match="scores_out"):
+        ld.retrieval_decode(q, kc, kc, 0xFF, k, s_out=S,
+                            scores_out=torch.zeros((B, Hq, n - 1), dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError, match="out must"):
+        ld.hybrid_layer(q, kc, kc, 0xFF, k, None, s_out=S, out=torch.zeros((B, Hq - 1, d), dtype=torch.bfloat16,
+                                                                           device=dev))
+    with pytest.raises(ValueError, match="kv_indptr"):
+        ld.hybrid_layer(q, kc, kc, 0xFF, k, None, s_out=S, seq_len=n,
+                        kv_indptr=torch.zeros(3, dtype=torch.int64, device=dev))

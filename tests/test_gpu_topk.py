@@ -158,3 +158,12 @@ def test_in_launch_selection_repeated_fresh_workspaces():
         for b in range(B):
             for h in range(Hq):
                 assert np.array_equal(Sh[b, h], orc.select_topk_f32(sc[b, h], k)), (trial, b, h)
+
+
+def test_undersized_outputs_are_rejected_before_launch():
+    ld = _ld()
+    x = torch.zeros((3, 1000), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="idx_out"):
+        ld.topk_select(x, 10, idx_out=torch.empty(29, dtype=torch.int32, device="cuda"))
+    with pytest.raises(ValueError, match="val_out"):
+        ld.topk_select(x, 10, val_out=torch.empty(29, dtype=torch.float32, device="cuda"))
