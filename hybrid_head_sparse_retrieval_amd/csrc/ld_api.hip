@@ -67,11 +67,12 @@ template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
 // Scores per workgroup of the standalone digit-1 histogram: 512, doubled while the
-// grid would exceed about 512 workgroups (long rows), at most 16384, so that each
-// workgroup's fixed work (clearing and flushing 2048 bins) is spread over many scores.
+// grid would exceed about 256 workgroups (long rows), at most 16384, so that each
+// workgroup's fixed work (clearing and flushing 2048 bins) is spread over many scores
+// (for 32 rows of 131072 scores, 256 workgroups measured faster than 128 or 512).
 void set_hist_chunks(SelParams& sp, int64_t rows, int n) {
   int c = kSelChunk;
-  while (c < 16384 && rows * ((n + c - 1) / c) > 512) c <<= 1;
+  while (c < 16384 && rows * ((n + c - 1) / c) > 256) c <<= 1;
   sp.hchunk = c;
   sp.Ch = (n + c - 1) / c;
 }
