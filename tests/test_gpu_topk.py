@@ -114,8 +114,12 @@ def test_more_spans_than_resident_workgroups():
 
 
 @pytest.mark.parametrize("rows,n,k", [
-    (32, 131072, 1024),    # 8192-score digit-1 chunks: one round of 8 float4 loads per thread
-    (8, 131072, 40000),    # 2048-score chunks
+    # digit-1 chunks are sized for about 256 workgroups; each case takes one load width
+    (32, 131072, 1024),    # 16384-score chunks: two rounds of 8 float4 loads per thread
+    (40, 40960, 12000),    # 8192-score chunks: one round of 8
+    (8, 131072, 40000),    # 4096-score chunks: one round of 4
+    (3, 131072, 39321),    # 2048-score chunks: one round of 2
+    (50, 5000, 1500),      # 1024-score chunks: one float4 per thread, the ragged last chunk scalar
     (40, 16385, 5000),     # rows whose starts are not 16-byte aligned take the scalar loads
 ])
 def test_digit1_chunk_sizes(rows, n, k):
