@@ -184,17 +184,15 @@ int cu_count() {
   return c;
 }
 
-// Waves per attention workgroup: flag bits 12..13 (1 = 4 waves, 2 = 8 waves); 4 by
-// default.
 // Waves per attention workgroup: flag bits 12..13 = 1 or 2 force 4 or 8. Otherwise 8 for
-// a bf16 cache of a single sequence of at most 32K rows whose layer streams some group
-// (measured at 32K: layers with retrieval heads 1 us faster, sparse-only layers
-// unchanged; at 128K, in ragged batches and with E4M3 codes 8 waves were slower), else 4.
-int choose_waves(uint32_t flags, int B, int N, int ng_dense, bool fp8) {
+// a bf16 cache of a single sequence of at most 32K rows (measured at 32K: 1.21 against
+// 1.23 ms per step with 4 waves; at 128K, in ragged batches and with E4M3 codes 8 waves
+// were slower), else 4.
+int choose_waves(uint32_t flags, int B, int N, bool fp8) {
   const uint32_t v = (flags >> 12) & 0x3u;
   if (v == 1u) return 4;
   if (v == 2u) return 8;
-  return (B == 1 && N <= 32768 && ng_dense > 0 && !fp8) ? 8 : 4;
+  return (B == 1 && N <= 32768 && !fp8) ? 8 : 4;
 }
 
 // Rows per split for the groups that stream every row (ts_d) and for the groups of
@@ -338,7 +336,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   }
   ap.ngroups = ng;
   ap.ng_dense = ng_dense;
-  ap.waves = choose_waves(flags, B, N, ng_dense, ap.kv_fp8 != 0);
+  ap.waves = choose_waves(flags, B, N, ap.kv_fp8 != 0);
   // The in-launch selection handles one retrieval head per group; layers with several
   // retrieval heads in a group select in a launch of their own, where every row runs
   // in parallel (the attention launch still merges behind group barriers).
