@@ -19,7 +19,7 @@ __all__ = [
     "retrieval_decode", "sparse_decode", "hybrid_layer", "topk_select",
     "hysparse_workspace_bytes", "HySparseWorkspace", "hysparse_layer",
     "tsa_workspace_bytes", "TsaWorkspace", "tsa_attention", "TSA_CAUSAL", "TSA_ZERO_FILL", "TSA_GIVEN_IDX",
-    "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "FLAG_SEPARATE_SELECT", "FLAG_BLOCK_SELECT", "flag_split_rows", "flag_waves", "EXPORTED_SYMBOLS",
+    "hybrid_layer_noalloc", "NOALLOC_SCRATCH_BYTES", "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "FLAG_SEPARATE_SELECT", "FLAG_BLOCK_SELECT", "flag_split_rows", "flag_waves", "EXPORTED_SYMBOLS",
 ]
 
 LD_OK = 0
@@ -31,12 +31,14 @@ TSA_CAUSAL = 1
 TSA_ZERO_FILL = 2
 TSA_GIVEN_IDX = 4
 _STATUS = {1: "invalid argument", 2: "unsupported shape", 3: "workspace missing or too small",
-           4: "HIP launch or copy failed", 5: "a bounded wait between workgroups gave up"}
+           4: "HIP launch or copy failed", 5: "a bounded wait between workgroups gave up",
+           6: "the shape needs more scratch than the library's static buffer holds"}
+NOALLOC_SCRATCH_BYTES = 128 << 20     # LD_NOALLOC_SCRATCH_BYTES
 EXPORTED_SYMBOLS = ("ld_status_string", "ld_workspace_size", "ld_topk_workspace_size",
                     "ld_workspace_init", "ld_workspace_check", "ld_retrieval_decode",
                     "ld_sparse_decode", "ld_hybrid_layer", "ld_topk_select",
                     "ld_hysparse_workspace_size", "ld_hysparse_layer",
-                    "ld_tsa_workspace_size", "ld_tsa_attention")
+                    "ld_tsa_workspace_size", "ld_tsa_attention", "ld_hybrid_layer_noalloc")
 
 
 def flag_split_rows(v: int) -> int:
@@ -121,6 +123,8 @@ def load_library():
     lib.ld_sparse_decode.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, u32, vp, sz, vp]
     lib.ld_hybrid_layer.restype = i32
     lib.ld_hybrid_layer.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, vp, vp, u32, vp, sz, vp]
+    lib.ld_hybrid_layer_noalloc.restype = i32
+    lib.ld_hybrid_layer_noalloc.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, vp, vp, u32, vp]
     lib.ld_hysparse_workspace_size.restype = sz
     lib.ld_hysparse_workspace_size.argtypes = [sp, i32, i32]
     lib.ld_hysparse_layer.restype = i32
@@ -390,6 +394,27 @@ def hybrid_layer(q, k_cache, v_cache, retrieval_mask: int, k: int, s, *, s_out=N
         ctypes.byref(shape), int(retrieval_mask), q.data_ptr(), k_cache.data_ptr(),
         v_cache.data_ptr(), int(k), _ptr(s), _ptr(s_out), _ptr(s_indptr), _ptr(scores_out),
         out.data_ptr(), int(flags), ws.ptr(), ws.nbytes, _stream()), "ld_hybrid_layer")
+    return out
+
+
+def hybrid_layer_noalloc(q, k_cache, v_cache, retrieval_mask: int, k: int, s, *, out, s_out=None,
+                         s_indptr=None, scores_out=None, flags: int = 0, kv_indptr=None, seq_len=None,
+                         scale=None, block_table=None, page_size: int = 0, k_scale=None, v_scale=None):
+    """hybrid_layer on the library's static per-device scratch: no workspace, and nothing
+    is allocated here either (`out` is required). Calls on one device must not overlap.
+    Returns out."""
+    torch = _torch()
+    _prep(q, k_cache, v_cache, out, kv_indptr)
+    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size, k_scale, v_scale)
+    _opt(s, torch.int32, "s"); _opt(s_out, torch.int32, "s_out")
+    _opt(s_indptr, torch.int64, "s_indptr"); _opt(scores_out, torch.float32, "scores_out")
+    if s_out is None:
+        s_out = s
+    _sizes(shape, q, out, k, kv_indptr, [("s", s), ("s_out", s_out)], s_indptr, scores_out)
+    _check(load_library().ld_hybrid_layer_noalloc(
+        ctypes.byref(shape), int(retrieval_mask), q.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), int(k), _ptr(s), _ptr(s_out), _ptr(s_indptr), _ptr(scores_out),
+        out.data_ptr(), int(flags), _stream()), "ld_hybrid_layer_noalloc")
     return out
 
 

@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "lychee_decode.h"
 #include "ld_internal.h"
@@ -32,6 +33,7 @@ struct LayerLayout {
   size_t gb_cnt, gb_rel, row_cnt, gb_cand, pub;       // group-barrier mode
   size_t blk_scores, blk_idx;                         // token-block selection
   int64_t sub_cap;
+  size_t ctrl_end;                                    // end of the arrays that start at zero
   size_t total;
 };
 
@@ -45,21 +47,30 @@ struct SelLayout {
 constexpr size_t kHeaderBytes = 256;
 constexpr size_t kErrOffset = 0;
 
-// Per-row selection scratch for `rows` rows of at most n scores.
+// Per-row selection scratch for `rows` rows of at most n scores: first the arrays that
+// must be zero when a call starts (sel_ctrl), then the others (sel_data).
 template <typename Take>
-SelArrays sel_arrays(int rows, int n, Take take) {
-  SelArrays a{};
+void sel_ctrl(SelArrays& a, int rows, Take take) {
   a.err = kErrOffset;
-  a.C = (n + kSelSpan - 1) / kSelSpan;
-  a.ncap = (int64_t)a.C * kSelSpan;
   a.tickets = take((size_t)rows * 4);
   a.hist1 = take((size_t)rows * kRep * kHist1Bins * 4);
   a.hist2 = take((size_t)rows * kHist2Bins * 4);
   a.depart = take((size_t)rows * 4);
+}
+template <typename Take>
+void sel_data(SelArrays& a, int rows, int n, Take take) {
+  a.C = (n + kSelSpan - 1) / kSelSpan;
+  a.ncap = (int64_t)a.C * kSelSpan;
   a.sel_info = take((size_t)rows * 16);
   a.span_cnt = take((size_t)rows * a.C * 8);
   a.span_off = take((size_t)rows * a.C * 4);
   a.cand = take((size_t)rows * a.ncap * 8);
+}
+template <typename Take>
+SelArrays sel_arrays(int rows, int n, Take take) {
+  SelArrays a{};
+  sel_ctrl(a, rows, take);
+  sel_data(a, rows, n, take);
   return a;
 }
 
@@ -137,18 +148,22 @@ LayerLayout layer_layout(const ld_shape* s) {
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   L.P1 = (L.P + kMergeRun - 1) / kMergeRun;
   take(kHeaderBytes);
+  // arrays that hold zero when a call starts (every call leaves them so); they come first
+  // so that one fill over [kHeaderBytes, ctrl_end) restores them
   L.attn_tickets = take((size_t)s->batch * s->num_kv_heads * 4);
   L.attn_tickets_l1 = take((size_t)s->batch * s->num_kv_heads * L.P1 * 4);
-  L.sel = sel_arrays(L.slots, N, take);
+  sel_ctrl(L.sel, L.slots, take);
+  L.gb_cnt = take((size_t)s->batch * s->num_kv_heads * kGbCounters * 4);
+  L.gb_rel = take((size_t)s->batch * s->num_kv_heads * L.P * 128);
+  L.row_cnt = take((size_t)2 * L.slots * kRep * 4);
+  L.ctrl_end = o;
+  sel_data(L.sel, L.slots, N, take);
   L.logits = take((size_t)L.slots * N * 4);
   L.part_ml = take((size_t)L.slots * L.P * 8);
   L.part_acc = take((size_t)L.slots * L.P * s->head_dim * 4);
   L.l1_ml = take((size_t)L.slots * L.P1 * 8);
   L.l1_acc = take((size_t)L.slots * L.P1 * s->head_dim * 4);
   L.bitmaps = take((size_t)L.slots * L.W * 4);
-  L.gb_cnt = take((size_t)s->batch * s->num_kv_heads * kGbCounters * 4);
-  L.gb_rel = take((size_t)s->batch * s->num_kv_heads * L.P * 128);
-  L.row_cnt = take((size_t)2 * L.slots * kRep * 4);
   // candidates of the workgroups of one replica: at most ceil(ns / kRep) splits of at
   // most kMaxSplitRows rows, i.e. below N / kRep + 2 * kMaxSplitRows
   L.sub_cap = ((int64_t)(N + kRep - 1) / kRep + 2 * kMaxSplitRows + 63) / 64 * 64;
@@ -244,7 +259,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
                     const void* kc, const void* vc, int32_t k, const int32_t* s_in,
                     int32_t* s_out, const int64_t* s_indptr, float* scores_out, void* out,
                     uint32_t flags, bool want_topk, void* ws, size_t ws_bytes, hipStream_t st,
-                    const float* gate = nullptr, const float* o_win = nullptr) {
+                    const float* gate = nullptr, const float* o_win = nullptr, bool clear_ctrl = false) {
   ld_status why;
   if (!shape_ok(shape, &why)) return why;
   const int B = shape->batch, Hq = shape->num_q_heads, Hkv = shape->num_kv_heads;
@@ -278,6 +293,11 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     if (retrieval >> h & 1ull) ret_heads[nret++] = (uint8_t)h;
   }
   uint32_t* bitmaps = at<uint32_t>(ws, L.bitmaps);
+
+  // 0. a buffer that other shapes' calls may have used: its counters, histograms and
+  // release words start from zero (a fill kernel, so the call stays capturable)
+  if (clear_ctrl && launch_zero(at<char>(ws, kHeaderBytes), L.ctrl_end - kHeaderBytes, st) != hipSuccess)
+    return LD_ERR_HIP;
 
   // 1. membership bitmaps of the sparse heads (unless the caller chains them)
   if (nsp && !(flags & LD_FLAG_S_CHAINED)) {
@@ -434,6 +454,7 @@ const char* ld_status_string(ld_status status) {
     case LD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case LD_ERR_HIP: return "HIP launch or copy failed";
     case LD_ERR_DEVICE_WAIT: return "a bounded wait between workgroups gave up";
+    case LD_ERR_SCRATCH_LIMIT: return "the shape needs more scratch than the library's static buffer holds";
   }
   return "unknown status";
 }
@@ -676,6 +697,55 @@ ld_status ld_topk_select(const float* scores, int32_t rows, int32_t n, int64_t r
   sp.idx_out = idx_out; sp.val_out = val_out;
   fill_sel(sp, L.sel, workspace);
   return launch_select(sp, stream, true) == hipSuccess ? LD_OK : LD_ERR_HIP;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free entry
+
+namespace {
+
+// Scratch of ld_hybrid_layer_noalloc: one copy per device, held until the process ends.
+// Host code never uses the array's name as an address: each device's address comes
+// from hipGetSymbolAddress (scratch_on_device).
+static __device__ __align__(256) unsigned char scratch[LD_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+// Device address of the current device's scratch, looked up once per device.
+ld_status scratch_on_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return LD_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LD_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ld_status ld_hybrid_layer_noalloc(const ld_shape* shape, uint64_t retrieval_mask, const void* q,
+                                  const void* k_cache, const void* v_cache, int32_t k,
+                                  const int32_t* s_in, int32_t* s_out, const int64_t* s_indptr,
+                                  float* scores_out, void* out, uint32_t flags, hipStream_t stream) {
+  ld_status why;
+  if (!shape_ok(shape, &why)) return why;
+  const int Hq = shape->num_q_heads;
+  const uint64_t all = (Hq == 64) ? ~0ull : ((1ull << Hq) - 1ull);
+  if (retrieval_mask & ~all) return LD_ERR_INVALID_ARGUMENT;
+  if (layer_layout(shape).total > (size_t)LD_NOALLOC_SCRATCH_BYTES) return LD_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if ((why = scratch_on_device(&ws)) != LD_OK) return why;
+  return run_layer(shape, all, retrieval_mask, q, k_cache, v_cache, k, s_in, s_out, s_indptr, scores_out, out,
+                   flags, !(flags & LD_FLAG_SKIP_TOPK), ws, (size_t)LD_NOALLOC_SCRATCH_BYTES, stream, nullptr,
+                   nullptr, true);
 }
 
 }  // extern "C"

@@ -66,8 +66,10 @@ enum {
   LD_ERR_UNSUPPORTED = 2,       /* head_dim not 64/128, group size not 1/2/4/8, Hq > 64 */
   LD_ERR_WORKSPACE = 3,         /* workspace missing or smaller than required */
   LD_ERR_HIP = 4,               /* a HIP launch or copy failed */
-  LD_ERR_DEVICE_WAIT = 5        /* a bounded wait between workgroups gave up (see
+  LD_ERR_DEVICE_WAIT = 5,       /* a bounded wait between workgroups gave up (see
                                    ld_workspace_check) */
+  LD_ERR_SCRATCH_LIMIT = 6      /* ld_hybrid_layer_noalloc: the shape's scratch exceeds
+                                   LD_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Flags (bitwise OR). */
@@ -251,6 +253,26 @@ ld_status ld_hybrid_layer(const ld_shape* shape, uint64_t retrieval_mask,
 ld_status ld_topk_select(const float* scores, int32_t rows, int32_t n, int64_t row_stride,
                          int32_t k, int32_t* idx_out, float* val_out,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ld_hybrid_layer without a workspace, for callers that cannot allocate device memory:
+   code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+   Same arguments, results and errors as ld_hybrid_layer, except that the scratch is a
+   static buffer inside the library of LD_NOALLOC_SCRATCH_BYTES (128 MiB) per device,
+   held from the first call on a device until the process ends. Shapes whose
+   ld_workspace_size exceeds it return LD_ERR_SCRATCH_LIMIT before any launch (for
+   example B = 1, Hq = 32, d = 128 fits up to about N = 200K). The call allocates and
+   frees nothing; it launches a small fill kernel that clears the buffer's counters
+   and histograms, then the layer's kernels. Every call on a device shares that
+   device's buffer, which keeps the last call's contents: calls that overlap on one
+   device (other streams, other threads) race and must be ordered by the caller.
+   LD_FLAG_S_CHAINED is valid only when the previous call on the device wrote s_in with
+   the same shape. The wait flag of ld_workspace_check is not reported for this buffer. */
+#define LD_NOALLOC_SCRATCH_BYTES (128u << 20)
+ld_status ld_hybrid_layer_noalloc(const ld_shape* shape, uint64_t retrieval_mask,
+                                  const void* q, const void* k_cache, const void* v_cache,
+                                  int32_t k, const int32_t* s_in, int32_t* s_out,
+                                  const int64_t* s_indptr, float* scores_out, void* out,
+                                  uint32_t flags, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         assert lib.ld_status_string(code)
     assert lib.ld_status_string(99) == b"unknown status"
 
@@ -110,6 +110,24 @@ def test_invalid_arguments_are_rejected(lib):
     assert _hyb(lib, _shape(seq_len=(1 << 21) + 1)) == UNS
     # scale must be finite
     assert _hyb(lib, _shape(softmax_scale=float("inf"))) == INV
+
+
+def test_noalloc_rejects_before_any_device_call(lib):
+    """The allocation-free layer validates the shape and its scratch size on the host
+    first: a shape larger than the static buffer, or an invalid one, never reaches
+    the device (no GPU here, so a call that passed validation would return LD_ERR_HIP)."""
+    INV, UNS, LIMIT = 1, 2, 6
+
+    def na(shape, mask=1):
+        return lib.ld_hybrid_layer_noalloc(ctypes.byref(shape), mask, FAKE, FAKE, FAKE, 10, FAKE, FAKE,
+                                           None, None, FAKE, 0, None)
+    big = _shape(seq_len=1 << 20)
+    assert lib.ld_workspace_size(ctypes.byref(big), 10) > ld.NOALLOC_SCRATCH_BYTES
+    assert na(big) == LIMIT
+    fits = _shape()
+    assert lib.ld_workspace_size(ctypes.byref(fits), 9830) <= ld.NOALLOC_SCRATCH_BYTES
+    assert na(_shape(head_dim=80)) == UNS
+    assert na(fits, mask=1 << 40) == INV
 
 
 def test_hysparse_workspace_and_arguments(lib):
