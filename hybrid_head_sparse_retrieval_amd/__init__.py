@@ -82,6 +82,7 @@ class Shape(ctypes.Structure):
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
         ("reserved", ctypes.c_int32),
+        ("s_capacity", ctypes.c_int64),
     ]
 
 
@@ -134,7 +135,7 @@ def load_library():
     lib.ld_tsa_attention.restype = i32
     lib.ld_tsa_attention.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, u32, vp, sz, vp]
     lib.ld_topk_select.restype = i32
-    lib.ld_topk_select.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp, sz, vp]
+    lib.ld_topk_select.argtypes = [vp, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -318,6 +319,19 @@ def _sizes(shape, q, out, k, kv_indptr=None, s_bufs=(), s_indptr=None, scores_ou
         raise ValueError("scores_out must hold B*Hq*seq_len values ([B][Hq][seq_len])")
 
 
+def _clamp_k(shape, k, s_indptr, s_bufs) -> int:
+    """The pages' budget clamp k = min(k, seq_len) (Token Sparse Attention skill page,
+    Step 3; LycheeDecode skill page, Step 1), and, for CSR S, the S buffers' capacity
+    that bounds every row on the device."""
+    k = min(int(k), int(shape.seq_len))
+    if k < 1:
+        raise ValueError("k must be at least 1")
+    if s_indptr is not None:
+        caps = [t.numel() for _, t in s_bufs if t is not None]
+        shape.s_capacity = min(caps) if caps else 0
+    return k
+
+
 def _is_fp8(t) -> bool:
     torch = _torch()
     return t.dtype == torch.uint8 or t.dtype == getattr(torch, "float8_e4m3fn", None)
@@ -348,6 +362,7 @@ def retrieval_decode(q, k_cache, v_cache, head_mask: int, k: int, *, s_out=None,
     shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size, k_scale, v_scale)
     _opt(s_out, torch.int32, "s_out"); _opt(s_indptr, torch.int64, "s_indptr")
     _opt(scores_out, torch.float32, "scores_out")
+    k = _clamp_k(shape, k, s_indptr, [("s_out", s_out)])
     _sizes(shape, q, out, k, kv_indptr, [("s_out", s_out)], s_indptr, scores_out)
     ws = workspace or Workspace(shape, k, q.device)
     _check(load_library().ld_retrieval_decode(
@@ -366,6 +381,7 @@ def sparse_decode(q, k_cache, v_cache, head_mask: int, k: int, s_in, *, s_indptr
     out = _prep(q, k_cache, v_cache, out, kv_indptr)
     shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size, k_scale, v_scale)
     _req(s_in, torch.int32, "s_in"); _opt(s_indptr, torch.int64, "s_indptr")
+    k = _clamp_k(shape, k, s_indptr, [("s_in", s_in)])
     _sizes(shape, q, out, k, kv_indptr, [("s_in", s_in)], s_indptr)
     ws = workspace or Workspace(shape, k, q.device)
     _check(load_library().ld_sparse_decode(
@@ -388,6 +404,7 @@ def hybrid_layer(q, k_cache, v_cache, retrieval_mask: int, k: int, s, *, s_out=N
     _opt(s_indptr, torch.int64, "s_indptr"); _opt(scores_out, torch.float32, "scores_out")
     if s_out is None:
         s_out = s
+    k = _clamp_k(shape, k, s_indptr, [("s", s), ("s_out", s_out)])
     _sizes(shape, q, out, k, kv_indptr, [("s", s), ("s_out", s_out)], s_indptr, scores_out)
     ws = workspace or Workspace(shape, k, q.device)
     _check(load_library().ld_hybrid_layer(
@@ -410,6 +427,7 @@ def hybrid_layer_noalloc(q, k_cache, v_cache, retrieval_mask: int, k: int, s, *,
     _opt(s_indptr, torch.int64, "s_indptr"); _opt(scores_out, torch.float32, "scores_out")
     if s_out is None:
         s_out = s
+    k = _clamp_k(shape, k, s_indptr, [("s", s), ("s_out", s_out)])
     _sizes(shape, q, out, k, kv_indptr, [("s", s), ("s_out", s_out)], s_indptr, scores_out)
     _check(load_library().ld_hybrid_layer_noalloc(
         ctypes.byref(shape), int(retrieval_mask), q.data_ptr(), k_cache.data_ptr(),
@@ -438,6 +456,7 @@ def hysparse_layer(q, k_cache, v_cache, k: int, s_in, k_window, v_window, gate, 
         raise ValueError("k_window/v_window must be [Hkv][B*W][d] and match each other")
     if gate.numel() != B * Hq:
         raise ValueError("gate must hold B*Hq values")
+    k = _clamp_k(shape, k, s_indptr, [("s_in", s_in)])
     _sizes(shape, q, out, k, kv_indptr, [("s_in", s_in)], s_indptr)
     W = k_window.shape[1] // B
     ws = workspace or HySparseWorkspace(shape, k, W, q.device)
@@ -495,9 +514,14 @@ def tsa_attention(q, k_cache, v_cache, scores, k: int, *, idx_out=None, out=None
     return out, idx_out
 
 
-def topk_select(scores, k: int, *, idx_out=None, val_out=None,
-                workspace: Optional[TopkWorkspace] = None):
-    """argsTopK of each row of a 2-D fp32 tensor; ascending indices [rows][k] (int32)."""
+def topk_select(scores, k: int, *, idx_out=None, val_out=None, n_per_row=None, k_per_row=None,
+                idx_indptr=None, workspace: Optional[TopkWorkspace] = None):
+    """argsTopK of each row of a 2-D fp32 tensor [rows][n]. Row r holds
+    n_r = n_per_row[r] (int32 device tensor, default n) scores and keeps
+    k_r = min(k_per_row[r] (default k), n_r) indices, in ascending order. Output: dense
+    [rows][k] int32 (rows with k_r < k keep their tail), or CSR into the 1-D idx_out at
+    offsets idx_indptr (int64 device tensor [rows+1]; capacity per row, which also
+    bounds k_r). Returns idx_out."""
     torch = _torch()
     if scores.dim() != 2:
         raise ValueError("scores must be 2-D [rows][n]")
@@ -507,14 +531,39 @@ def topk_select(scores, k: int, *, idx_out=None, val_out=None,
         raise ValueError("scores must have unit stride along each row")
     if not scores.is_cuda or scores.dtype != torch.float32:
         raise ValueError("scores must be a float32 device tensor")
-    if idx_out is None:
-        idx_out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    k = int(k)
+    if k < 1:
+        raise ValueError("k must be at least 1")
+    for name, t in (("n_per_row", n_per_row), ("k_per_row", k_per_row)):
+        _opt(t, torch.int32, name)
+        if t is not None and t.numel() != rows:
+            raise ValueError(f"{name} must hold one entry per row")
+    if idx_indptr is not None:
+        _req(idx_indptr, torch.int64, "idx_indptr")
+        if idx_indptr.numel() != rows + 1:
+            raise ValueError("idx_indptr must hold rows+1 offsets")
+        if idx_out is None:
+            raise ValueError("CSR output needs idx_out")
+        # device-side offsets bound the kernels' writes: check them once here
+        off = idx_indptr.cpu()
+        need = int(off[-1])
+        if int(off[0]) < 0 or bool((off[1:] < off[:-1]).any()):
+            raise ValueError("idx_indptr must be non-negative and non-decreasing")
+        cap = need
+    else:
+        if idx_out is None:
+            idx_out = torch.empty((rows, min(k, n)), dtype=torch.int32, device=scores.device)
+            k_stride = min(k, n)
+        else:
+            k_stride = k
+        cap = rows * k_stride
+        k = k_stride
     _req(idx_out, torch.int32, "idx_out"); _opt(val_out, torch.float32, "val_out")
     for name, t in (("idx_out", idx_out), ("val_out", val_out)):
-        if t is not None and t.numel() < rows * int(k):
-            raise ValueError(f"{name} must hold rows*k entries")
+        if t is not None and t.numel() < cap:
+            raise ValueError(f"{name} must hold {cap} entries")
     ws = workspace or TopkWorkspace(rows, n, scores.device)
     _check(load_library().ld_topk_select(
-        scores.data_ptr(), int(rows), int(n), int(row_stride), int(k), idx_out.data_ptr(),
-        _ptr(val_out), ws.ptr(), ws.nbytes, _stream()), "ld_topk_select")
+        scores.data_ptr(), int(rows), int(n), int(row_stride), _ptr(n_per_row), int(k), _ptr(k_per_row),
+        idx_out.data_ptr(), _ptr(idx_indptr), _ptr(val_out), ws.ptr(), ws.nbytes, _stream()), "ld_topk_select")
     return idx_out

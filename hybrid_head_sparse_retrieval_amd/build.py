@@ -16,7 +16,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblychee_decode.so")
-SOURCES = ["ld_api.hip", "ld_attention.hip", "ld_select.hip", "ld_window.hip", "ld_tsa.hip"]
+# (source, object, extra options): the attention kernels compile once per KV group size
+UNITS = [("ld_api.hip", "ld_api.o", []), ("ld_select.hip", "ld_select.o", []),
+         ("ld_window.hip", "ld_window.o", []), ("ld_tsa.hip", "ld_tsa.o", [])] + \
+        [("ld_attention.hip", f"ld_attention_g{g}.o", [f"-DLD_ATTN_G={g}"]) for g in (1, 2, 4, 8)]
+SOURCES = sorted({u[0] for u in UNITS})
 
 ARCH = "gfx950"
 COMMON = [
@@ -59,9 +63,9 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     cmds = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmd = [hipcc, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    for src, oname, opts in UNITS:
+        obj = os.path.join(BUILD, oname)
+        cmd = [hipcc, *COMMON, *EXTRA.get(src, []), *opts, "-c", os.path.join(CSRC, src), "-o", obj]
         if save_temps:
             cmd.insert(1, "--save-temps")
         objs.append(obj)

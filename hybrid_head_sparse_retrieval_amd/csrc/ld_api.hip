@@ -30,9 +30,9 @@ struct LayerLayout {
   size_t attn_tickets, attn_tickets_l1;               // zero between calls
   SelArrays sel;
   size_t logits, part_ml, part_acc, l1_ml, l1_acc, bitmaps;
-  size_t gb_cnt, gb_rel, row_cnt, gb_cand, pub;       // group-barrier mode
+  size_t gb_rel;                                      // selectors' release flags
+  size_t sel_cnt, sel_cand, sel_pub;                  // in-launch selection
   size_t blk_scores, blk_idx;                         // token-block selection
-  int64_t sub_cap;
   size_t ctrl_end;                                    // end of the arrays that start at zero
   size_t total;
 };
@@ -117,7 +117,7 @@ bool shape_ok(const ld_shape* s, ld_status* why) {
   } else if (s->pages_per_seq != 0 || s->block_table) {
     return false;
   }
-  if (s->reserved != 0) return false;
+  if (s->reserved != 0 || s->s_capacity < 0) return false;
   if (s->kv_dtype == 1) {
     if (!(s->k_scale > 0.f) || !(s->v_scale > 0.f) || !std::isfinite(s->k_scale) || !std::isfinite(s->v_scale))
       return false;
@@ -153,9 +153,8 @@ LayerLayout layer_layout(const ld_shape* s) {
   L.attn_tickets = take((size_t)s->batch * s->num_kv_heads * 4);
   L.attn_tickets_l1 = take((size_t)s->batch * s->num_kv_heads * L.P1 * 4);
   sel_ctrl(L.sel, L.slots, take);
-  L.gb_cnt = take((size_t)s->batch * s->num_kv_heads * kGbCounters * 4);
   L.gb_rel = take((size_t)s->batch * s->num_kv_heads * L.P * 128);
-  L.row_cnt = take((size_t)2 * L.slots * kRep * 4);
+  L.sel_cnt = take((size_t)L.slots * 2 * 4);
   L.ctrl_end = o;
   sel_data(L.sel, L.slots, N, take);
   L.logits = take((size_t)L.slots * N * 4);
@@ -164,11 +163,8 @@ LayerLayout layer_layout(const ld_shape* s) {
   L.l1_ml = take((size_t)L.slots * L.P1 * 8);
   L.l1_acc = take((size_t)L.slots * L.P1 * s->head_dim * 4);
   L.bitmaps = take((size_t)L.slots * L.W * 4);
-  // candidates of the workgroups of one replica: at most ceil(ns / kRep) splits of at
-  // most kMaxSplitRows rows, i.e. below N / kRep + 2 * kMaxSplitRows
-  L.sub_cap = ((int64_t)(N + kRep - 1) / kRep + 2 * kMaxSplitRows + 63) / 64 * 64;
-  L.gb_cand = take((size_t)L.slots * kRep * L.sub_cap * 4);
-  L.pub = take((size_t)L.slots * L.P * 8);
+  L.sel_cand = take((size_t)L.slots * N * 4);
+  L.sel_pub = take((size_t)L.slots * kMaxParts * 8);
   L.blk_scores = take((size_t)L.slots * ((N + kBlock - 1) / kBlock) * 4);
   L.blk_idx = take((size_t)L.slots * ((N + kBlock - 1) / kBlock) * 4);
   L.total = o;
@@ -199,15 +195,57 @@ int cu_count() {
   return c;
 }
 
-// Waves per attention workgroup: flag bits 12..13 = 1 or 2 force 4 or 8. Otherwise 8 for
-// a bf16 cache of a single sequence of at most 32K rows (measured at 32K: 1.21 against
-// 1.23 ms per step with 4 waves; at 128K, in ragged batches and with E4M3 codes 8 waves
-// were slower), else 4.
-int choose_waves(uint32_t flags, int B, int N, bool fp8) {
+}  // namespace
+
+namespace ld {
+
+int64_t attention_capacity(int D, int G, int waves, bool fp8) {
+  // cached per device and (D, G, waves, KV format)
+  static std::atomic<int64_t> cache[64][2][4][2][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  const int di = D == 128 ? 1 : 0;
+  const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+  const int wi = waves == 8 ? 1 : 0;
+  const int fi = fp8 ? 1 : 0;
+  int64_t c = cache[dev][di][gi][wi][fi].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int64_t per_cu = 0;
+  switch (G) {
+    case 1: per_cu = attention_capacity_g<1>(D, waves, fp8); break;
+    case 2: per_cu = attention_capacity_g<2>(D, waves, fp8); break;
+    case 4: per_cu = attention_capacity_g<4>(D, waves, fp8); break;
+    case 8: per_cu = attention_capacity_g<8>(D, waves, fp8); break;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  c = per_cu * cus;
+  cache[dev][di][gi][wi][fi].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+hipError_t launch_attention(const AttnParams& p, int D, int G, dim3 grid, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_attention_g<1>(p, D, grid, st);
+    case 2: return launch_attention_g<2>(p, D, grid, st);
+    case 4: return launch_attention_g<4>(p, D, grid, st);
+    case 8: return launch_attention_g<8>(p, D, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ld
+
+namespace {
+
+using namespace ld;
+
+// Waves per attention workgroup: flag bits 12..13 = 1 or 2 force 4 or 8; otherwise 4
+// (two workgroups per compute unit: with the group's last arrivals finishing it, the
+// 32K step measured 1.24 ms with 4 waves against 1.30 ms with 8).
+int choose_waves(uint32_t flags) {
   const uint32_t v = (flags >> 12) & 0x3u;
-  if (v == 1u) return 4;
-  if (v == 2u) return 8;
-  return (B == 1 && N <= 32768 && !fp8) ? 8 : 4;
+  return v == 2u ? 8 : 4;
 }
 
 // Rows per split for the groups that stream every row (ts_d) and for the groups of
@@ -274,6 +312,8 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   const bool block = do_topk && (flags & LD_FLAG_BLOCK_SELECT);
   if (block && (k % kBlock != 0 || N % kBlock != 0 || shape->kv_indptr || s_indptr)) return LD_ERR_INVALID_ARGUMENT;
   if (sparse && !s_in) return LD_ERR_INVALID_ARGUMENT;
+  if (s_indptr && ((uintptr_t)s_indptr & 7u || shape->s_capacity < 1)) return LD_ERR_INVALID_ARGUMENT;
+  const int64_t s_cap = s_indptr ? shape->s_capacity : (int64_t)B * Hq * k;
   if (do_topk && !s_out) return LD_ERR_INVALID_ARGUMENT;
   if ((s_in && ((uintptr_t)s_in & 3u)) || (s_out && ((uintptr_t)s_out & 3u))) return LD_ERR_INVALID_ARGUMENT;
   if (scores_out && ((uintptr_t)scores_out & 3u)) return LD_ERR_INVALID_ARGUMENT;
@@ -302,7 +342,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   // 1. membership bitmaps of the sparse heads (unless the caller chains them)
   if (nsp && !(flags & LD_FLAG_S_CHAINED)) {
     BitmapParams bp{};
-    bp.s = s_in; bp.s_indptr = s_indptr; bp.k_dense = k;
+    bp.s = s_in; bp.s_indptr = s_indptr; bp.k_dense = k; bp.s_cap = s_cap;
     bp.kv_indptr = shape->kv_indptr; bp.seq_len = N;
     bp.Hq = Hq; bp.nsp = nsp;
     std::memcpy(bp.heads, sp_heads, sizeof(sp_heads));
@@ -313,7 +353,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   // 2. S^{l+1} = S^{l} for sparse heads when the output buffer is a different one
   if (nsp && s_out && s_out != s_in) {
     CopyParams cp{};
-    cp.src = s_in; cp.dst = s_out; cp.s_indptr = s_indptr; cp.k_dense = k;
+    cp.src = s_in; cp.dst = s_out; cp.s_indptr = s_indptr; cp.k_dense = k; cp.s_cap = s_cap;
     cp.Hq = Hq; cp.nsp = nsp;
     std::memcpy(cp.heads, sp_heads, sizeof(sp_heads));
     if (launch_copy_rows(cp, B * nsp, st) != hipSuccess) return LD_ERR_HIP;
@@ -348,7 +388,8 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
       if (!(active & gm)) continue;
       const bool streams = (retrieval & gm) != 0;
       if (streams != (pass == 0)) continue;
-      ap.groups[ng++] = (uint8_t)g;
+      ++ng;
+      (streams ? ap.dense_groups : ap.sparse_groups) |= 1ull << g;
       ret_per_group = std::max(ret_per_group, __builtin_popcountll(retrieval & gm));
       sp_per_group = std::max(sp_per_group, __builtin_popcountll(active & ~retrieval & gm));
     }
@@ -356,16 +397,50 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   }
   ap.ngroups = ng;
   ap.ng_dense = ng_dense;
-  ap.waves = choose_waves(flags, B, N, ap.kv_fp8 != 0);
-  // The in-launch selection handles one retrieval head per group; layers with several
-  // retrieval heads in a group select in a launch of their own, where every row runs
-  // in parallel (the attention launch still merges behind group barriers).
-  const bool want_gb = !(flags & LD_FLAG_SEPARATE_SELECT);
-  const bool in_select = want_gb && do_topk && !block && ret_per_group <= 1;
+  ap.waves = choose_waves(flags);
+  // Finisher mode (default): the last split of each KV group to arrive merges O, and
+  // the retrieval rows are selected inside the launch by the splits that arrive just
+  // before it. At most a quarter of the resident capacity may wait for its group's last
+  // arrival at once, so every wait ends. Separate mode (LD_FLAG_SEPARATE_SELECT, or
+  // chosen here when the in-launch selectors would be too few for the rows): ticket
+  // merge inside the launch and the selection in launches of their own.
   const int64_t capacity = attention_capacity(D, G, ap.waves, ap.kv_fp8 != 0);
+  bool fin = !(flags & LD_FLAG_SEPARATE_SELECT);
+  bool in_select = fin && do_topk && !block;
+  const int sel_groups = B * ng_dense;
+  // Merge helpers and selectors wait for their group's last split: up to 8 workgroups
+  // per group merge O (half the budget at most); of the rest, few rows share up to
+  // kMaxParts selectors each (enough for one pass of 16 keys per thread), many rows get
+  // one selector each (sel_cap per group; 0: the last arrival selects every row).
+  {
+    const int64_t budget = capacity / 4;
+    const int64_t rows = (int64_t)B * nret;
+    const int64_t groups_total = std::max<int64_t>(1, (int64_t)B * ng);
+    ap.merge_w = (int)std::max<int64_t>(1, std::min<int64_t>(8, 1 + budget / 2 / groups_total));
+    const int64_t sel_budget = budget - (int64_t)(ap.merge_w - 1) * groups_total;
+    const int64_t pass = 16LL * 64 * ap.waves;
+    const int64_t want = std::max<int64_t>(2, (N + pass - 1) / pass);
+    if (rows > 0 && 2 * rows <= sel_budget) {
+      // parts <= threads / 8, so that each part's sub-list has 8 readers when they gather
+      ap.sel_parts = (int)std::min<int64_t>({(int64_t)kMaxParts, sel_budget / rows, want, 64LL * ap.waves / 8});
+      ap.sel_cap = G * ap.sel_parts;
+    } else {
+      ap.sel_parts = 1;
+      ap.sel_cap = (int)std::min<int64_t>(G, std::max<int64_t>(0, sel_budget) / std::max(1, sel_groups));
+    }
+    // Rows that would get under half the parts one pass needs (a full-attention layer's
+    // 32 heads at 32K rows get 2 of 8): the selection launches, with many workgroups per
+    // row, finish sooner (measured at 32K and 128K rows: 82 vs 90 and 170 vs 285 us).
+    if (in_select && rows > 0 && 2 * (int64_t)ap.sel_parts < want) {
+      fin = false;
+      in_select = false;
+    }
+  }
+  ap.fin = fin ? 1 : 0;
   // union density of a sparse group's rows if its heads' sets were independent
   const double kf = std::min(1.0, (double)k / (double)N);
   const double rho = 1.0 - std::pow(1.0 - kf, (double)std::max(1, sp_per_group));
+  // the selection's latency after a streaming group's last split, in streamed rows
   const int sel_rows = in_select ? kSelRows : 0;
   if (!choose_splits(N, B, ng_dense, ng - ng_dense, rho, sel_rows, capacity, flags, &ap.ts_d, &ap.ts_s))
     ap.ts_d = ap.ts_s = uniform_split(N, (int64_t)B * ng, capacity);
@@ -386,22 +461,14 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   ap.sel_info = at<uint32_t>(ws, L.sel.sel_info);
   ap.k_dense = k;
   ap.s_indptr = s_indptr;
+  ap.s_cap = s_cap;
+  ap.s_out = s_out;
+  ap.gb_rel = at<uint64_t>(ws, L.gb_rel);
+  ap.sel_cnt = at<uint32_t>(ws, L.sel_cnt);
+  ap.sel_cand = at<uint32_t>(ws, L.sel_cand);
+  ap.sel_pub = at<uint64_t>(ws, L.sel_pub);
+  ap.err = at<uint32_t>(ws, L.sel.err);
   const int64_t nwg = (int64_t)B * ((int64_t)ng_dense * ap.nsplit_d + (int64_t)(ng - ng_dense) * ap.nsplit_s);
-  // every workgroup resident at once: the splits of a group merge O (and select)
-  // together behind device-wide barriers inside this launch
-  const bool gb = want_gb && nwg <= capacity;
-  if (gb) {
-    ap.gb = 1;
-    ap.gb_select = in_select ? 1 : 0;
-    ap.gb_cnt = at<uint32_t>(ws, L.gb_cnt);
-    ap.gb_rel = at<uint64_t>(ws, L.gb_rel);
-    ap.row_cnt = at<uint32_t>(ws, L.row_cnt);
-    ap.cand = at<uint32_t>(ws, L.gb_cand);
-    ap.sub_cap = L.sub_cap;
-    ap.pub = at<uint32_t>(ws, L.pub);
-    ap.s_out = s_out;
-    ap.err = at<uint32_t>(ws, L.sel.err);
-  }
   if (launch_attention(ap, D, G, dim3((unsigned)nwg), st) != hipSuccess) return LD_ERR_HIP;
 
   // 4. argsTopK of the retrieval rows: by token blocks (block maxima, then the same
@@ -427,12 +494,12 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     sp.C = (bk.nblk + kSelSpan - 1) / kSelSpan;    // spans of this row length
     if (launch_select(sp, st, true) != hipSuccess) return LD_ERR_HIP;
     if (launch_block_expand(bk, bk.rows, st) != hipSuccess) return LD_ERR_HIP;
-  } else if (do_topk && !(gb && in_select)) {
+  } else if (do_topk && !in_select) {
     SelParams sp{};
     sp.mode = 1;
     sp.nrows = B * nret;
     sp.logits = ap.logits; sp.Hq = Hq; sp.seq_len = N; sp.kv_indptr = shape->kv_indptr;
-    sp.s_out = s_out; sp.s_indptr = s_indptr; sp.k_dense = k;
+    sp.s_out = s_out; sp.s_indptr = s_indptr; sp.k_dense = k; sp.s_cap = s_cap;
     sp.bitmaps = bitmaps; sp.W = L.W;
     sp.nret = nret;
     std::memcpy(sp.heads, ret_heads, sizeof(ret_heads));
@@ -680,12 +747,13 @@ ld_status ld_hybrid_layer(const ld_shape* shape, uint64_t retrieval_mask, const 
 }
 
 ld_status ld_topk_select(const float* scores, int32_t rows, int32_t n, int64_t row_stride,
-                         int32_t k, int32_t* idx_out, float* val_out, void* workspace,
+                         const int32_t* n_per_row, int32_t k, const int32_t* k_per_row, int32_t* idx_out,
+                         const int64_t* idx_indptr, float* val_out, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
-  if (!scores || !idx_out || rows < 1 || n < 1 || n > kMaxSeq || k < 1 || k > n ||
-      row_stride < n)
+  if (!scores || !idx_out || rows < 1 || n < 1 || n > kMaxSeq || k < 1 || row_stride < n)
     return LD_ERR_INVALID_ARGUMENT;
-  if (((uintptr_t)scores & 3u) || ((uintptr_t)idx_out & 3u) || (val_out && ((uintptr_t)val_out & 3u)))
+  if (((uintptr_t)scores & 3u) || ((uintptr_t)idx_out & 3u) || (val_out && ((uintptr_t)val_out & 3u)) ||
+      ((uintptr_t)n_per_row & 3u) || ((uintptr_t)k_per_row & 3u) || ((uintptr_t)idx_indptr & 7u))
     return LD_ERR_INVALID_ARGUMENT;
   const SelLayout L = sel_layout(rows, n);
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 15u)) return LD_ERR_WORKSPACE;
@@ -695,6 +763,7 @@ ld_status ld_topk_select(const float* scores, int32_t rows, int32_t n, int64_t r
   set_hist_chunks(sp, rows, n);
   sp.scores = scores; sp.row_stride = row_stride; sp.n = n; sp.k = k;
   sp.idx_out = idx_out; sp.val_out = val_out;
+  sp.n_per_row = n_per_row; sp.k_per_row = k_per_row; sp.idx_indptr = idx_indptr;
   fill_sel(sp, L.sel, workspace);
   return launch_select(sp, stream, true) == hipSuccess ? LD_OK : LD_ERR_HIP;
 }

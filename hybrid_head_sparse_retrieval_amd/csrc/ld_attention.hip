@@ -41,6 +41,7 @@ constexpr int kChunkRows = kTile * kMaxTPC;
 constexpr int kCandLds = 8192;     // selection candidates staged in LDS
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
@@ -72,6 +73,9 @@ struct AttnSmem {
   uint8_t hmp[kMaxSplitRows];        // membership mask (bit j = head g*G+j) per visit position
   uint16_t list[kMaxSplitRows];      // token row (within the tile) of each visit position
   int wcnt[NW];
+  int tmp4[NW][4];
+  int poff[kMaxParts + 1];           // selection: candidate sub-list offsets, part order
+  int pcnt[kMaxParts];               // selection: each part's keys above bin b1
   int misc[4];
   uint64_t relw;                     // release word seen by thread 0
   uint32_t res[2];
@@ -148,13 +152,28 @@ __device__ __forceinline__ void merge_splits(AttnSmem<D, G, NW>& sm, const AttnP
     for (int q = 0; q < PF; ++q)
       if (s_lo + q < s_hi) x[q] = ld_dev4_b(rr, (jrow + (s_lo + q) * D + d0) * 4);
   }
-  // maxima and sums of every (head, split) in one round
-  for (int i = tid; i < G * cnt; i += NT) {
-    const int jj = i / cnt, ss = i % cnt;
-    if (act >> jj & 1u) {
-      const size_t ms = ((size_t)(hq0 + jj) * stride + s0 + ss) * 2;
-      sm.u.cmb.w[jj][ss] = ld_dev(src_ml + ms);
-      sm.u.cmb.lp[jj][ss] = ld_dev(src_ml + ms + 1);
+  // maxima and sums of every (head, split), as (max, sum) pairs of 8 bytes: issued in
+  // one round with the partials above
+  {
+    // bounded to the group's rows: positions past them read 0
+    const __amdgpu_buffer_rsrc_t rm = rsrc_n(src_ml + (size_t)hq0 * stride * 2, G * stride * 2 * 4);
+    for (int i0 = 0; i0 < G * cnt; i0 += 4 * NT) {
+      u32x2_t ml[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * NT + tid;
+        const int jj = i / cnt, ss = i % cnt;
+        ml[u] = __builtin_amdgcn_raw_buffer_load_b64(rm, ((jj * stride + s0 + ss) * 2) * 4, 0, kSc1);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * NT + tid;
+        const int jj = i / cnt, ss = i % cnt;
+        if (i < G * cnt && (act >> jj & 1u)) {
+          sm.u.cmb.w[jj][ss] = __uint_as_float(ml[u].x);
+          sm.u.cmb.lp[jj][ss] = __uint_as_float(ml[u].y);
+        }
+      }
     }
   }
   __syncthreads();
@@ -218,86 +237,6 @@ __device__ __forceinline__ void merge_splits(AttnSmem<D, G, NW>& sm, const AttnP
   __syncthreads();
 }
 
-// ---- group-barrier mode
-
-// O of a group from its ns split partials, spread over the group's workgroups: wave w
-// of split s merges the float4 columns (s * NW + w) + t * ns * NW; its lanes run over
-// the splits.
-template <int D, int G, int NW>
-__device__ __forceinline__ void merge_columns(const AttnParams& p, uint32_t act, int hq0, int split, int ns) {
-  constexpr int NC = G * (D / 4);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  for (int c = split * NW + wave; c < NC; c += ns * NW) {
-    const int j = c / (D / 4), d0 = (c % (D / 4)) * 4;
-    if (!(act >> j & 1u)) continue;
-    const float* ml = p.part_ml + (size_t)(hq0 + j) * p.P * 2;
-    const __amdgpu_buffer_rsrc_t rr = rsrc(p.part_acc + (size_t)(hq0 + j) * p.P * D);
-    float L = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (ns <= 64) {
-      float m = -LD_INF, l = 0.f;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (lane < ns) {
-        m = ld_dev(ml + lane * 2);
-        l = ld_dev(ml + lane * 2 + 1);
-        a = ld_dev4_b(rr, (lane * D + d0) * 4);
-      }
-      const float M = wave_max_f(m);
-      const float w = exp2_fast(m - ((M == -LD_INF) ? 0.f : M));   // 0 for unused lanes
-      L = l * w;
-      o = make_float4(a.x * w, a.y * w, a.z * w, a.w * w);
-    } else {
-      float M = -LD_INF;
-      for (int s2 = lane; s2 < ns; s2 += 64) M = fmaxf(M, ld_dev(ml + s2 * 2));
-      M = wave_max_f(M);
-      const float mu = (M == -LD_INF) ? 0.f : M;
-      for (int s2 = lane; s2 < ns; s2 += 64) {
-        const float w = exp2_fast(ld_dev(ml + s2 * 2) - mu);
-        L = fmaf(ld_dev(ml + s2 * 2 + 1), w, L);
-        const float4 a = ld_dev4_b(rr, (s2 * D + d0) * 4);
-        o.x = fmaf(a.x, w, o.x); o.y = fmaf(a.y, w, o.y); o.z = fmaf(a.z, w, o.z); o.w = fmaf(a.w, w, o.w);
-      }
-    }
-    L = wave_sum_f(L);
-    o.x = wave_sum_f(o.x); o.y = wave_sum_f(o.y); o.z = wave_sum_f(o.z); o.w = wave_sum_f(o.w);
-    if (lane == 0) store_o<D>(p, hq0 + j, d0, o, p.v_scale / L);
-  }
-}
-
-// Exclusive prefix of 0/1 flags in row order (row = i * NT + thread) over the
-// workgroup, for IT items per thread: ex[i] = flags of earlier rows, tot[i] = flags of
-// item i over the workgroup. Two items share an int (16-bit fields).
-template <int NW, int IT>
-__device__ __forceinline__ void rows_scan(const uint32_t (&f)[IT], int (&ex)[IT], int (&tot)[IT],
-                                          int (&lds)[NW][IT / 2]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc[IT / 2], val[IT / 2];
-#pragma unroll
-  for (int q = 0; q < IT / 2; ++q) {
-    val[q] = (int)(f[2 * q] | (f[2 * q + 1] << 16));
-    inc[q] = wave_incl_sum(val[q]);
-    if (lane == 63) lds[wave][q] = inc[q];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < IT / 2; ++q) {
-    int below = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int t = lds[w][q];
-      below += (w < wave) ? t : 0;
-      all += t;
-    }
-    const int e = below + inc[q] - val[q];
-    ex[2 * q] = e & 0xffff;
-    ex[2 * q + 1] = e >> 16;
-    tot[2 * q] = all & 0xffff;
-    tot[2 * q + 1] = all >> 16;
-  }
-  __syncthreads();
-}
-
 // Digit 1 of row `slot` (bin b1 and k1, the keys still to take from it) from the sum
 // of its histogram replicas, stored in sel_info for the selection launch.
 template <int D, int G, int NW>
@@ -319,253 +258,405 @@ __device__ __forceinline__ void digit1_info(AttnSmem<D, G, NW>& sm, const AttnPa
 
 // k of the row: the row's selection length, at most the sequence length nb.
 __device__ __forceinline__ int select_k(const AttnParams& p, int slot, int nb) {
-  int kk = p.k_dense;
-  if (p.s_indptr) kk = (int)(p.s_indptr[slot + 1] - p.s_indptr[slot]);
+  int64_t so;
+  int kk;
+  s_row(p.s_indptr, p.k_dense, p.s_cap, slot, &so, &kk);
   return min(kk, nb);
 }
 
-// Digit 1 of the row's threshold from its digit-1 histogram (the sum of the kRep
-// replicas), taken once per group by the workgroup that completed the group's first
-// barrier, and published to the group as stage 2 of the release words, with the
-// payload b1 (the bin, bits 0..31) and k1 (the keys still to take from it, bits 32..63).
+// Output columns [c_lo, c_hi) (float4 columns, head-major) of the group's active heads
+// from its ns split partials (max in log2 units, sum, unnormalised output), by one
+// workgroup without a barrier: TP adjacent lanes share each column, each folds every
+// TP-th split into an online-softmax state (its loads issued a round at a time), and the
+// lanes combine their states by shuffles; the first lane of the column writes O.
 template <int D, int G, int NW>
-__device__ __forceinline__ void publish_digit1(AttnSmem<D, G, NW>& sm, const AttnParams& p, int slot, int kk,
-                                               uint64_t* rel, int ns, uint32_t epoch) {
+__device__ __forceinline__ void merge_final(const AttnParams& p, uint32_t act, int hq0, int ns, int c_lo,
+                                            int c_hi) {
   constexpr int NT = 64 * NW;
-  constexpr int PB1 = kHist1Bins / NT;          // digit-1 bins per thread
+  constexpr int CH = 8;                         // splits per lane and round
+  const int ncol = max(1, c_hi - c_lo);
+  int TP = 1;                                   // lanes per column: a power of two, <= 64
+  while (TP < 64 && TP * 2 * ncol <= NT) TP <<= 1;
   const int tid = threadIdx.x;
-  uint32_t* hs = sm.u.sel.hist;                 // free until the selection below
-  hist1_sum(hs, p.hist1, slot);
-  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
-  __syncthreads();
-  uint32_t h[PB1];
+  const int c = c_lo + tid / TP, r = tid & (TP - 1);
+  const int j = c / (D / 4), d0 = (c % (D / 4)) * 4;
+  const bool live = c < c_hi && (act >> j & 1u);
+  float m = -LD_INF, l = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (live) {
+    const __amdgpu_buffer_rsrc_t ra = rsrc_n(p.part_acc + (size_t)(hq0 + j) * p.P * D, ns * D * 4);
+    const __amdgpu_buffer_rsrc_t rm = rsrc_n(p.part_ml + (size_t)(hq0 + j) * p.P * 2, ns * 2 * 4);
+    for (int s0 = r; s0 < ns; s0 += TP * CH) {
+      float4 a[CH];
+      u32x2_t ml[CH];
 #pragma unroll
-  for (int q = 0; q < PB1; ++q) h[q] = hs[tid * PB1 + q];
-  find_bin_regs<kHist1Bins, NT>(h, (uint32_t)kk, sm.wcnt, sm.res);
-  const uint32_t b1 = sm.res[0], k1 = (uint32_t)kk - sm.res[1];
-  __syncthreads();
-  group_publish(rel, ns, rel_word(epoch, 2u), (uint64_t)b1 | ((uint64_t)k1 << 32));
+      for (int u = 0; u < CH; ++u) {
+        const int sp = s0 + u * TP;             // past ns: the bound reads 0 (masked below)
+        a[u] = ld_dev4_b(ra, (sp * D + d0) * 4);
+        ml[u] = __builtin_amdgcn_raw_buffer_load_b64(rm, sp * 8, 0, kSc1);
+      }
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        if (s0 + u * TP >= ns) break;
+        const float ms = __uint_as_float(ml[u].x), ls = __uint_as_float(ml[u].y);
+        const float mn = fmaxf(m, ms);
+        const float mu = (mn == -LD_INF) ? 0.f : mn;
+        const float wo = exp2_fast(m - mu), wn = exp2_fast(ms - mu);   // 0 for -inf maxima
+        l = l * wo + ls * wn;
+        o.x = o.x * wo + a[u].x * wn; o.y = o.y * wo + a[u].y * wn;
+        o.z = o.z * wo + a[u].z * wn; o.w = o.w * wo + a[u].w * wn;
+        m = mn;
+      }
+    }
+  }
+  // combine the TP lanes of the column (all lanes take part in the shuffles)
+  for (int off = 1; off < TP; off <<= 1) {
+    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+    const float ox = __shfl_xor(o.x, off), oy = __shfl_xor(o.y, off);
+    const float oz = __shfl_xor(o.z, off), ow = __shfl_xor(o.w, off);
+    const float mn = fmaxf(m, m2);
+    const float mu = (mn == -LD_INF) ? 0.f : mn;
+    const float w1 = exp2_fast(m - mu), w2 = exp2_fast(m2 - mu);
+    l = l * w1 + l2 * w2;
+    o.x = o.x * w1 + ox * w2; o.y = o.y * w1 + oy * w2;
+    o.z = o.z * w1 + oz * w2; o.w = o.w * w1 + ow * w2;
+    m = mn;
+  }
+  if (live && r == 0) store_o<D>(p, hq0 + j, d0, o, p.v_scale / l);
 }
 
-// argsTopK of the group's one retrieval head by the workgroups of the group, each over
-// its own rows (r0 .. r0 + nrows), with one more group barrier: every split takes
-// digit 1 (b1, k1) from its release word, appends its candidates (keys whose digit 1
-// is b1) to the candidate sub-list of its replica and publishes its count of keys
-// above bin b1; after the barrier every split derives the threshold key T from all
-// candidates (digits 2 and 3), its output offset from the earlier splits' counts, and
-// writes its kept rows (keys equal to T are kept in row order, so the lower indices
-// win ties).
-template <int D, int G, int NW>
-__device__ __forceinline__ void group_select(AttnSmem<D, G, NW>& sm, const AttnParams& p, uint32_t ret,
-                                             int hq0, int split, int ns, int bid0, int nb, int r0, int nrows,
-                                             uint32_t* gc, uint64_t* rel, uint32_t epoch) {
-  constexpr int NT = 64 * NW;
-  constexpr int IT = kMaxSplitRows / NT;        // rows per thread
-  constexpr int SPEC = 32;                      // candidates fetched per thread before the counts
+// ---- selection of one retrieval row by one workgroup
+
+// Exclusive prefix, in row order, of the per-(item, wave) counts buf[i * NW + w]
+// (IT items of NT rows, item-major, at most NT entries): the prefixes replace the counts
+// and the total is returned in every thread. The caller synchronises after writing
+// the counts.
+template <int NW, int IT>
+__device__ __forceinline__ int scan_item_counts(int* buf, int* tmp) {
+  constexpr int NE = IT * NW;
+  static_assert(NE <= 64 * NW, "one entry per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int v = tid < NE ? buf[tid] : 0;
+  int wt;
+  const int ex = wave_excl_scan(v, wt);
+  if (lane == 0) tmp[wave] = wt;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int x = tmp[w];
+    before += (w < wave) ? x : 0;
+    all += x;
+  }
+  if (tid < NE) buf[tid] = before + ex;
+  __syncthreads();
+  return all;
+}
 
-  // the group's one retrieval head (the launch takes this path only when there is one)
-  const int slot = hq0 + __builtin_ctz(ret);
+// Sums over the workgroup of four counts, in every thread (tmp: LDS int[NW][4]).
+template <int NW>
+__device__ __forceinline__ int4 wg_sum4(int4 v, int (*tmp)[4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int a = wave_total(v.x), b = wave_total(v.y), c = wave_total(v.z), d = wave_total(v.w);
+  if (lane == 0) { tmp[wave][0] = a; tmp[wave][1] = b; tmp[wave][2] = c; tmp[wave][3] = d; }
+  __syncthreads();
+  int4 s = make_int4(0, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < NW; ++i) { s.x += tmp[i][0]; s.y += tmp[i][1]; s.z += tmp[i][2]; s.w += tmp[i][3]; }
+  __syncthreads();
+  return s;
+}
+
+// argsTopK of row `slot` (method step 3), part `part` of `parts`: the parts are
+// workgroups that each hold a contiguous share of the row's keys (order-preserving images
+// of the fp32 logits, which every split of the KV group has stored device-coherently, with
+// its digit-1 counts, before the parts start). Each part takes digit 1 (bits 31..21 of
+// the threshold key T) from the summed histogram replicas, counts its keys above that
+// bin and stores its keys in the bin (the candidates, key bits 20..0, in row order) in a
+// sub-list of its own; after the parts meet (every part is already running, so the wait
+// ends), each gathers every part's candidates, derives digits 2 and 3 of T from them, its
+// output offset from the earlier parts' counts and candidates, and writes its kept rows
+// (keys above T, and of the keys equal to T the first ones in row order) in ascending
+// order with their membership words. The row's arrival counter starts at zero (the KV
+// group's last split clears it before the parts are released). LDS: hist
+// [kHist2Bins + kHist3Bins], cand [kCandLds], wcnt [NW], res [2], tmp4 [NW][4],
+// poff [kMaxParts + 1], pcnt [kMaxParts].
+template <int NW>
+__device__ __forceinline__ void part_select(uint32_t* hist, uint32_t* cand_lds, int* wcnt, uint32_t* res,
+                                            int (*tmp4)[4], int* poff, int* pcnt, const AttnParams& p, int slot,
+                                            int nb, int part, int parts) {
+  constexpr int NT = 64 * NW;
+  constexpr int IT = 16;                        // keys per thread per pass
+  constexpr int PASS = IT * NT;                 // rows per pass
+  constexpr int PB1 = kHist1Bins / NT;
+  constexpr int SPEC = 8;                       // candidates fetched per thread with the counts
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes under this one
   const int kk = select_k(p, slot, nb);
-  if (kk < 1) return;                           // the same in every split of the group
+  // this part's rows: [r0, r0 + ns), a whole number of NT-row items; its candidate
+  // sub-list starts at r0 of the row's list (it holds at most ns entries)
+  const int R = ((nb + parts - 1) / parts + NT - 1) / NT * NT;
+  const int r0 = min(nb, part * R);
+  const int ns = max(0, min(nb, r0 + R) - r0);
+  const int npass = (ns + PASS - 1) / PASS;
+  const float* lg = p.logits + (size_t)slot * p.seq_len + r0;
+  uint32_t* gcnt = p.sel_cnt + (size_t)slot * 2;          // [0]: parts arrived
+  uint32_t* gcand = p.sel_cand + (size_t)slot * p.seq_len;
+  uint64_t* gpub = p.sel_pub + (size_t)slot * kMaxParts;  // per part: above | candidates << 32
 
-  // ---- keys of this split's rows; digit 1
   uint32_t key[IT];
-  {
-    const float* lg = p.logits + (size_t)slot * p.seq_len + r0;
+  // device-coherent (sc1) buffer loads, all issued before the first use; rows past the
+  // part read 0 from the buffer's bound and are masked by index
+  auto load = [&](int ps) {
+    const int lim = min(ns - ps * PASS, PASS);
+    const __amdgpu_buffer_rsrc_t r = rsrc_n(lg + (size_t)ps * PASS, max(lim, 0) * 4);
+    uint32_t raw[IT];
 #pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const int r = i * NT + tid;
-      key[i] = (r < nrows) ? score_key(ld_dev(lg + r)) : 0u;
-    }
-  }
-  const uint64_t w1 = group_wait_payload(rel, split, rel_word(epoch, 2u), p.err, &sm.relw);
-  const uint32_t b1 = (uint32_t)w1 & 0x7ffu, k1 = (uint32_t)(w1 >> 32);
-  uint32_t* rcnt = p.row_cnt + ((size_t)(epoch & 1u) * p.B * p.Hq + slot) * kRep;   // this call's counts
-  {
-    // ---- append the candidates to the row's list; publish the count above bin b1
-    uint32_t cm = 0;
-    int na = 0;
+    for (int i = 0; i < IT; ++i) raw[i] = __builtin_amdgcn_raw_buffer_load_b32(r, (i * NT + tid) * 4, 0, kSc1);
 #pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const bool v = i * NT + tid < nrows;
-      const uint32_t d1 = key[i] >> 21;
-      na += (v && d1 > b1) ? 1 : 0;
-      cm |= (uint32_t)(v && d1 == b1) << i;
-    }
-    int wt;
-    const int before = wave_excl_scan(__popc(cm), wt);
-    const int wa = wave_total(na);
-    if (lane == 0) { sm.scan[wave][0] = wt; sm.scan[wave][1] = wa; }
-    __syncthreads();
-    int woff = 0, tot = 0, atot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      woff += (w < wave) ? sm.scan[w][0] : 0;
-      tot += sm.scan[w][0];
-      atot += sm.scan[w][1];
-    }
-    const int rep = rep_of_block();
-    if (tid == 0) {
-      sm.misc[2] = tot ? (int)__hip_atomic_fetch_add(rcnt + rep, (uint32_t)tot,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-      st_dev(p.pub + ((size_t)slot * p.P + split) * 2, (uint32_t)atot);
-    }
-    __syncthreads();
-    // a candidate shares digit 1 with the others: it is stored as its split and the
-    // low 21 bits of its key
-    uint32_t* cl = p.cand + ((size_t)slot * kRep + rep) * p.sub_cap + sm.misc[2] + woff + before;
-    int q = 0;
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      if (cm >> i & 1u) {
-        st_dev(cl + q, ((uint32_t)split << 21) | (key[i] & 0x1fffffu));
-        ++q;
-      }
-    }
-  }
-  group_barrier(gc + (kRep + 1), rel, split, ns, bid0, rel_word(epoch, 3u), p.err, &sm.misc[1]);
-
-  // ---- threshold from the whole candidate list, offset, write
-  // The candidates sit in kRep sub-lists; the first PER entries of each are fetched
-  // before the counts are known (entries past a count are ignored): register u holds
-  // entry (u / kRep) * NT + tid of sub-list u % kRep. All of them then go to LDS
-  // (sub-list after sub-list) when they fit, and the passes below read them there.
-  static_assert(SPEC % kRep == 0, "speculative loads cover the sub-lists evenly");
-  constexpr int PER = SPEC / kRep * NT;
-  const uint32_t* cl = p.cand + (size_t)slot * kRep * p.sub_cap;
-  uint32_t cv[SPEC];
-#pragma unroll
-  for (int u = 0; u < SPEC; ++u) cv[u] = ld_dev(cl + (size_t)(u % kRep) * p.sub_cap + (u / kRep) * NT + tid);
-  if (tid < kRep) sm.ncnt[tid] = (int)ld_dev(rcnt + tid);
-  int above = 0;                                  // keys above bin b1 in earlier splits
-  for (int s2 = tid; s2 < split; s2 += NT) above += (int)ld_dev(p.pub + ((size_t)slot * p.P + s2) * 2);
-  uint32_t* h2 = sm.u.sel.hist;                   // [kHist2Bins]
-  uint32_t* h3 = h2 + kHist2Bins;                 // [kHist3Bins]
-  uint32_t* cs = sm.u.sel.cand;                   // [kCandLds]
-  for (int i = tid; i < kHist2Bins + kHist3Bins; i += NT) h2[i] = 0u;
-  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
-  __syncthreads();
-  int total = 0;
-#pragma unroll
-  for (int r = 0; r < kRep; ++r) total += sm.ncnt[r];
-  const bool in_lds = total <= kCandLds;
-  if (in_lds) {
-    int off = 0;
-#pragma unroll
-    for (int r = 0; r < kRep; ++r) {
-      const int n = sm.ncnt[r];
-#pragma unroll
-      for (int v = 0; v < SPEC / kRep; ++v) {
-        const int o = v * NT + tid;
-        if (o < n) cs[off + o] = cv[v * kRep + r];
-      }
-      for (int o = PER + tid; o < n; o += NT) cs[off + o] = ld_dev(cl + (size_t)r * p.sub_cap + o);
-      off += n;
-    }
-    __syncthreads();
-  }
-  // visit(f): every candidate once, as its split and its full key
-  auto for_cands = [&](auto f) {
-    auto g = [&](uint32_t e) { f((b1 << 21) | (e & 0x1fffffu), (int)(e >> 21)); };
-    if (in_lds) {
-#pragma unroll 4
-      for (int i = tid; i < total; i += NT) g(cs[i]);
-    } else {
-      for (int r = 0; r < kRep; ++r) {
-        const int n = sm.ncnt[r];
-        for (int o = tid; o < n; o += NT) g(ld_dev(cl + (size_t)r * p.sub_cap + o));
-      }
-    }
+    for (int i = 0; i < IT; ++i) key[i] = score_key(__uint_as_float(raw[i]));
   };
-  for_cands([&](uint32_t kv, int) { atomicAdd(&h2[(kv >> 10) & 0x7ffu], 1u); });
+  if (kk >= 1 && npass) load(0);               // in flight with the histogram sum
+  // ---- digit 1 from the row's counts (the sum of the replicas)
+  hist1_sum(hist, p.hist1, slot);
+  if (tid == 0) { res[0] = 0; res[1] = 0; }
   __syncthreads();
-  find_bin_from_top<kHist2Bins, NT>([&](int i) { return h2[i]; }, k1, sm.wcnt, sm.res);
-  const uint32_t b2 = sm.res[0];
-  const uint32_t k2 = k1 - sm.res[1];
-  const uint32_t pre = (b1 << 11) | b2;
-  __syncthreads();    // every wave has read the result before it is cleared
-  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
-  __syncthreads();
-  for_cands([&](uint32_t kv, int) { if ((kv >> 10) == pre) atomicAdd(&h3[kv & 0x3ffu], 1u); });
-  __syncthreads();
-  find_bin_from_top<kHist3Bins, NT>([&](int i) { return h3[i]; }, k2, sm.wcnt, sm.res);
-  const uint32_t T = (pre << 10) | sm.res[0];
-  const int et = (int)(k2 - sm.res[1]);           // keys equal to T that are kept
-  // candidates of earlier splits above and equal to T; keys equal to T here
-  int ga = 0, ge = 0, me = 0;
-  for_cands([&](uint32_t kv, int s2) {
-    const int early = s2 < split ? 1 : 0, here = s2 == split ? 1 : 0;
-    const int gt1 = kv > T ? 1 : 0, eq1 = kv == T ? 1 : 0;
-    ga += early & gt1;
-    ge += early & eq1;
-    me += here & eq1;
-  });
+  if (parts == 1) hist1_clear(p.hist1, slot);   // the only reader
+  if (kk < 1) return;
+  uint32_t b1, k1;
   {
-    // the four sums in one exchange
-    const int w0 = wave_total(above), w1 = wave_total(ga), w2 = wave_total(ge), w3 = wave_total(me);
-    if (lane == 0) { sm.scan[wave][0] = w0; sm.scan[wave][1] = w1; }
-    if (lane == 0) { sm.cnt4[wave][0] = w2; sm.cnt4[wave][1] = w3; }
-    __syncthreads();
-    above = 0; ga = 0; ge = 0; me = 0;
+    uint32_t h1[PB1];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      above += sm.scan[w][0]; ga += sm.scan[w][1]; ge += sm.cnt4[w][0]; me += sm.cnt4[w][1];
-    }
+    for (int q = 0; q < PB1; ++q) h1[q] = hist[tid * PB1 + q];
+    find_bin_regs<kHist1Bins, NT>(h1, (uint32_t)kk, wcnt, res);
+    b1 = res[0];
+    k1 = (uint32_t)kk - res[1];
     __syncthreads();
   }
-  const int off = above + ga + min(et, ge);       // kept rows of earlier splits
-  const int keep_e = max(0, min(et - ge, me));    // kept keys equal to T here
-  uint32_t gt[IT], eq[IT], kp[IT];
-#pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const bool v = i * NT + tid < nrows;
-    gt[i] = (v && key[i] > T) ? 1u : 0u;
-    eq[i] = (v && key[i] == T) ? 1u : 0u;
-  }
-  if (keep_e == me) {
-#pragma unroll
-    for (int i = 0; i < IT; ++i) kp[i] = gt[i] | eq[i];
-  } else if (keep_e == 0) {
-#pragma unroll
-    for (int i = 0; i < IT; ++i) kp[i] = gt[i];
-  } else {
-    int ex[IT], tot[IT];
-    rows_scan<NW, IT>(eq, ex, tot, sm.scan);
-    int before = 0;
+  // ---- this part's keys above bin b1 (a count) and in it (its sub-list, in row order)
+  int above = 0, ncand = 0;
+  for (int ps = 0; ps < npass; ++ps) {
+    if (ps) load(ps);
+    const int lim = min(ns - ps * PASS, PASS);
+    uint32_t cm = 0;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      kp[i] = gt[i] | ((eq[i] && before + ex[i] < keep_e) ? 1u : 0u);
-      before += tot[i];
+      const bool v = i * NT + tid < lim;
+      const uint32_t d1 = key[i] >> 21;
+      above += (v & (d1 > b1)) ? 1 : 0;
+      cm |= (uint32_t)(v & (d1 == b1)) << i;
+    }
+    // positions in row order: per-(item, wave) counts, scanned
+    int* cnt = reinterpret_cast<int*>(hist);
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const uint64_t cb = __ballot((cm >> i) & 1u);
+      if (lane == 0) cnt[i * NW + wave] = __popcll(cb);
+    }
+    __syncthreads();
+    const int ctot = scan_item_counts<NW, IT>(cnt, wcnt);
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const bool c = (cm >> i) & 1u;
+      const uint64_t cb = __ballot(c);
+      if (c) st_dev(gcand + r0 + ncand + cnt[i * NW + wave] + __popcll(cb & below), key[i] & 0x1fffffu);
+    }
+    ncand += ctot;
+    __syncthreads();
+  }
+  {
+    const int4 t = wg_sum4<NW>(make_int4(above, 0, 0, 0), tmp4);
+    above = t.x;
+  }
+  if (parts > 1 && tid == 0) st_dev(gpub + part, (uint64_t)(uint32_t)above | ((uint64_t)(uint32_t)ncand << 32));
+  __builtin_amdgcn_s_waitcnt(0);                // this part's candidates and counts are stored
+  __syncthreads();
+  // ---- the parts meet
+  if (parts > 1) {
+    if (tid == 0) {
+      __hip_atomic_fetch_add(gcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int spins = 0;
+      while (__hip_atomic_fetch_add(gcnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)parts) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kMaxSpins) { st_dev(p.err, 1u); break; }
+      }
+    }
+    __syncthreads();
+    if (part == 0) hist1_clear(p.hist1, slot);  // every part has read the replicas
+  }
+  // ---- every part's candidates, gathered in part order (in LDS when they fit). Each
+  // part's sub-list is read by its own TPP threads (entry i by thread i mod TPP); the
+  // first SPEC entries per thread are fetched with the counts, before those are known
+  // (reads past a sub-list's count are ignored; the row's list bounds them).
+  const __amdgpu_buffer_rsrc_t rl = rsrc_n(gcand, p.seq_len * 4);
+  const int tpp = NT / parts;                   // threads per part (parts <= NT / 8)
+  const int gq = tid / tpp, gi = tid - gq * tpp;
+  const bool gin = gq < parts;
+  uint32_t sv[SPEC];
+  uint64_t pubv = 0;
+  if (parts > 1) {
+    if (tid < parts) pubv = ld_dev(gpub + tid);
+#pragma unroll
+    for (int u = 0; u < SPEC; ++u) {
+      const int at = gin ? gq * R + gi + u * tpp : p.seq_len;
+      sv[u] = __builtin_amdgcn_raw_buffer_load_b32(rl, at * 4, 0, kSc1);
     }
   }
-  int ex[IT], tot[IT];
-  rows_scan<NW, IT>(kp, ex, tot, sm.scan);
+  if (parts > 1) {
+    if (tid < parts) { pcnt[tid] = (int)(uint32_t)pubv; poff[tid + 1] = (int)(uint32_t)(pubv >> 32); }
+  } else if (tid == 0) {
+    pcnt[0] = 0;
+    poff[1] = ncand;
+  }
+  __syncthreads();
+  if (tid == 0) {                               // sub-list counts -> offsets in part order
+    int o = 0;
+    for (int q = 0; q < parts; ++q) { const int c = poff[q + 1]; poff[q] = o; o += c; }
+    poff[parts] = o;
+  }
+  __syncthreads();
+  const int total = poff[parts];
+  const bool in_lds = total <= kCandLds;
+  if (in_lds && gin) {
+    const int n_q = poff[gq + 1] - poff[gq];
+    uint32_t* dstq = cand_lds + poff[gq];
+    const int first = parts > 1 ? SPEC * tpp : 0;   // entries fetched above
+    if (parts > 1) {
+#pragma unroll
+      for (int u = 0; u < SPEC; ++u)
+        if (gi + u * tpp < n_q) dstq[gi + u * tpp] = sv[u];
+    }
+    for (int i0 = first; i0 < n_q; i0 += SPEC * tpp) {
+#pragma unroll
+      for (int u = 0; u < SPEC; ++u) {
+        const int i = i0 + gi + u * tpp;
+        sv[u] = __builtin_amdgcn_raw_buffer_load_b32(rl, (i < n_q ? gq * R + i : p.seq_len) * 4, 0, kSc1);
+      }
+#pragma unroll
+      for (int u = 0; u < SPEC; ++u)
+        if (i0 + gi + u * tpp < n_q) dstq[i0 + gi + u * tpp] = sv[u];
+    }
+  }
+  // earlier parts' keys above bin b1
+  int above_before = 0;
+  for (int q = 0; q < part; ++q) above_before += pcnt[q];
+  __syncthreads();
+  // candidate i of the gathered list (parts in order)
+  auto cand_at = [&](int i) -> uint32_t {
+    if (in_lds) return cand_lds[i];
+    int q = 0;
+    while (q + 1 < parts && poff[q + 1] <= i) ++q;
+    return ld_dev(gcand + (size_t)q * R + (i - poff[q]));
+  };
+  uint32_t* h2 = hist;
+  uint32_t* h3 = hist + kHist2Bins;
+  __syncthreads();
+  for (int i = tid; i < kHist2Bins + kHist3Bins; i += NT) hist[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < total; i += NT) atomicAdd(&h2[(cand_at(i) >> 10) & 0x7ffu], 1u);
+  __syncthreads();
+  find_bin_from_top<kHist2Bins, NT>([&](int i) { return h2[i]; }, k1, wcnt, res);
+  const uint32_t b2 = res[0], k2 = k1 - res[1];
+  __syncthreads();
+  if (tid == 0) { res[0] = 0; res[1] = 0; }
+  __syncthreads();
+  for (int i = tid; i < total; i += NT) {
+    const uint32_t c = cand_at(i);
+    if (((c >> 10) & 0x7ffu) == b2) atomicAdd(&h3[c & 0x3ffu], 1u);
+  }
+  __syncthreads();
+  find_bin_from_top<kHist3Bins, NT>([&](int i) { return h3[i]; }, k2, wcnt, res);
+  const uint32_t t21 = (b2 << 10) | res[0];     // T's bits 20..0
+  const uint32_t T = (b1 << 21) | t21;
+  const int et = (int)(k2 - res[1]);            // keys equal to T that are kept
+  // ---- earlier parts' candidates above / equal to T; this part's keys equal to T
+  int gt = 0, eqb = 0;
+  for (int i = tid; i < poff[part]; i += NT) {
+    const uint32_t c = cand_at(i);
+    gt += c > t21 ? 1 : 0;
+    eqb += c == t21 ? 1 : 0;
+  }
+  int eqm = 0;
+  {
+    int ps = 0;
+    do {
+      if (npass > 1) load(ps);
+      const int lim = min(ns - ps * PASS, PASS);
+#pragma unroll
+      for (int i = 0; i < IT; ++i) eqm += ((i * NT + tid < lim) & (key[i] == T)) ? 1 : 0;
+    } while (++ps < npass);
+  }
+  {
+    // above_before is already whole in every thread (from LDS)
+    const int4 t = wg_sum4<NW>(make_int4(0, gt, eqb, eqm), tmp4);
+    gt = t.y; eqb = t.z; eqm = t.w;
+  }
+  const int keep_eq = max(0, min(et - eqb, eqm));   // this part's kept keys equal to T
+  const int off = above_before + gt + min(et, eqb);
+  // ---- kept rows, ascending, with their membership words
   int64_t so;
   int klen;
-  if (p.s_indptr) { so = p.s_indptr[slot]; klen = (int)(p.s_indptr[slot + 1] - so); }
-  else { so = (int64_t)slot * p.k_dense; klen = p.k_dense; }
+  s_row(p.s_indptr, p.k_dense, p.s_cap, slot, &so, &klen);
   klen = min(klen, nb);
   int32_t* out = p.s_out + so;
   uint32_t* bm = p.bitmaps ? p.bitmaps + (size_t)slot * p.W : nullptr;
-  int base = off;
+  int* cnt = reinterpret_cast<int*>(hist);      // [IT][NW] counts, then prefixes
+  int* tcnt = cnt + IT * NW;                    // [IT][NW] tie counts, then prefixes
+  const bool eq_all = keep_eq == 0 || keep_eq == eqm;   // all of this part's ties are kept, or none
+  int kept_before = off, ties_before = 0;
+  for (int ps = 0; ps < npass; ++ps) {
+    if (npass > 1) load(ps);
+    const int lim = min(ns - ps * PASS, PASS);
+    uint32_t kpm = 0;                           // bit i: item i of this lane is kept
+    if (eq_all) {
 #pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int r = i * NT + tid;
-    const int pos = base + ex[i];
-    if (kp[i] && pos < klen) out[pos] = r0 + r;
-    base += tot[i];
-    if (bm) {
-      const uint64_t bal = __ballot(kp[i] != 0u);
-      // first row of this lane's word; words past this split's rows are another
-      // split's (splits are whole words: r0 and the split size are multiples of 32)
-      const int rr = i * NT + wave * 64 + (lane & 32);
-      const int row32 = r0 + rr;
-      if ((lane & 31) == 0 && rr < nrows && (row32 >> 5) < p.W)
-        bm[row32 >> 5] = (uint32_t)(bal >> (lane & 32));
+      for (int i = 0; i < IT; ++i) {
+        const bool v = i * NT + tid < lim;
+        kpm |= (uint32_t)(v & ((key[i] > T) | ((key[i] == T) & (keep_eq > 0)))) << i;
+      }
+    } else {
+      // the first keep_eq ties of this part in row order: ranks from per-item counts
+      uint32_t eqm_l = 0;
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const bool e = (i * NT + tid < lim) & (key[i] == T);
+        eqm_l |= (uint32_t)e << i;
+        const uint64_t eb = __ballot(e);
+        if (lane == 0) tcnt[i * NW + wave] = __popcll(eb);
+      }
+      __syncthreads();
+      const int ttot = scan_item_counts<NW, IT>(tcnt, wcnt);
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const bool e = (eqm_l >> i) & 1u;
+        const uint64_t eb = __ballot(e);
+        const int rank = ties_before + tcnt[i * NW + wave] + __popcll(eb & below);
+        const bool g = (i * NT + tid < lim) & (key[i] > T);
+        kpm |= (uint32_t)(g | (e & (rank < keep_eq))) << i;
+      }
+      ties_before += ttot;
     }
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const uint64_t kb = __ballot((kpm >> i) & 1u);
+      if (lane == 0) cnt[i * NW + wave] = __popcll(kb);
+    }
+    __syncthreads();
+    const int ktot = scan_item_counts<NW, IT>(cnt, wcnt);
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const bool kp = (kpm >> i) & 1u;
+      const uint64_t kb = __ballot(kp);
+      const int row = r0 + ps * PASS + i * NT + tid;
+      const int pos = kept_before + cnt[i * NW + wave] + __popcll(kb & below);
+      if (kp & (pos < klen)) out[pos] = row;
+      const int w0 = r0 + ps * PASS + i * NT + wave * 64;   // a multiple of 64
+      if (bm && (lane & 31) == 0 && w0 + lane < r0 + ns && ((w0 + lane) >> 5) < p.W)
+        bm[(w0 + lane) >> 5] = (uint32_t)(kb >> lane);
+    }
+    kept_before += ktot;
+    __syncthreads();                            // the count buffers are reused
   }
-  __syncthreads();
 }
 
 // F8: K and V hold E4M3 codes (one byte per element, dequantised exactly to bf16 /
@@ -592,10 +683,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 
   int bid = blockIdx.x;
   const int dense_blocks = p.B * p.ng_dense * p.nsplit_d;
-  int split, gi, b, ts, bid0;                 // bid0: id of the group's first split
+  int split, gi, b, ts;
   if (bid < dense_blocks) {
     split = bid % p.nsplit_d;
-    bid0 = bid - split;
     bid /= p.nsplit_d;
     gi = bid % p.ng_dense;
     b = bid / p.ng_dense;
@@ -604,13 +694,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     const int ngs = p.ngroups - p.ng_dense;
     bid -= dense_blocks;
     split = bid % p.nsplit_s;
-    bid0 = dense_blocks + bid - split;
     bid /= p.nsplit_s;
     gi = p.ng_dense + bid % ngs;
     b = bid / ngs;
     ts = p.ts_s;
   }
-  const int g = p.groups[gi];
+  // the gi-th launched group: the streaming ones first, then the gathering ones, each in
+  // ascending order (bit arithmetic on kernel arguments, no memory access)
+  int g;
+  {
+    uint64_t m = gi < p.ng_dense ? p.dense_groups : p.sparse_groups;
+    for (int i = gi < p.ng_dense ? gi : gi - p.ng_dense; i > 0; --i) m &= m - 1ull;
+    g = (int)__builtin_ctzll(m);
+  }
 
   const bool paged = p.page_shift != 0;
   int64_t tok0;
@@ -684,11 +780,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     return (((ptrdiff_t)sm.pages[(i >> pshift) - pg0] << pshift) + (i & pmask) - r0) * D;
   };
   // Stream mode: the waves take interleaved 16-row tiles of the split. Gather mode:
-  // each wave owns a contiguous block of the split's rows and visits the members of
-  // its own block (its own visit list at lbase, nl_w entries), so the list needs no
-  // workgroup-wide step.
+  // each wave owns a contiguous block of the split's rows [lbase, rend) and visits
+  // positions lbase .. lbase + nl_w: first the block's first `head` rows as they are
+  // (one chunk, loaded before the membership words arrive, non-members masked), then
+  // the members of the rest of its block (its own visit list), so the list needs no
+  // workgroup-wide step and memory is busy from the start.
   int nlist = nrows;
-  int lbase = 0, nl_w = 0;
+  int nl_w = 0;
+  const int gR = ((ts + 64 * NW - 1) / (64 * NW)) * 64;   // gather: rows per wave
+  const int lbase = dense ? 0 : wave * gR;
+  const int rend = dense ? nrows : min(nrows, lbase + gR);
+  const int head = dense ? 0 : min(CROWS, max(0, rend - lbase));
   auto chunks_of = [&](int n) {
     const int ntiles = (n + kTile - 1) / kTile;
     const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
@@ -697,7 +799,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   auto tbase = [&](int c, int t) -> int {
     return dense ? (wave + NW * (c * TPC + t)) * kTile : lbase + (c * TPC + t) * kTile;
   };
-  int lim = nrows;                            // visit positions below lim are valid
+  int lim = dense ? nrows : lbase + head;      // visit positions below lim are valid
 
   const bool head_lane = mr < G;
   const bool ret_lane = head_lane && ((ret >> mr) & 1u);
@@ -713,7 +815,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 
   uint4 kr[3][TPC][KCH], vr[3][RSC][NV];
 
-  auto row_of = [&](int pos) -> int { return dense ? pos : (int)sm.list[pos]; };
+  auto row_of = [&](int pos) -> int { return (dense || pos < lbase + head) ? pos : (int)sm.list[pos]; };
   auto load_chunk = [&](int c, uint4 (&kd)[TPC][KCH], uint4 (&vd)[RSC][NV]) {
 #pragma unroll
     for (int t = 0; t < TPC; ++t) {
@@ -748,10 +850,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     }
   };
 
+  // gather mode: the membership words of the wave's block, issued first so that their
+  // wait does not include the head rows' loads
+  constexpr int GCH = kMaxSplitRows / (64 * NW);   // 64-row steps of a wave's block
+  static_assert(2 * GCH <= 64, "one word per lane");
+  uint32_t gbw[G];
+  if (!dense) {
+    const int word = ((r0 + lbase) >> 5) + lane;
+    const bool ok = lane < 2 * GCH && lbase + 32 * lane < rend && word < p.W;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      gbw[j] = ((spm >> j & 1) && ok) ? p.bitmaps[(size_t)(hq0 + j) * p.W + word] : 0u;
+  }
   if (dense) {
     const int nc0 = chunks_of(nrows);
     if (nc0 > 0) load_chunk(0, kr[0], vr[0]);
     if (nc0 > 1) load_chunk(1, kr[1], vr[1]);
+  } else if (head > 0) {
+    load_chunk(0, kr[0], vr[0]);              // the head rows: no list needed
   }
 
   // ---- membership of each row of the tile, and the visit list
@@ -799,33 +915,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     }
   }
   if (spm && !dense) {
-    // rows owned by this wave: [lbase, lbase + R) of the split, 64 per ballot
-    constexpr int CH = kMaxSplitRows / (64 * NW);
-    static_assert(2 * CH <= 64, "one word per lane");
-    const int R = ((ts + 64 * NW - 1) / (64 * NW)) * 64;
-    lbase = wave * R;
-    const int rend = min(nrows, lbase + R);
-    uint32_t bw[G];
-    {
-      const int word = ((r0 + lbase) >> 5) + lane;
-      const bool ok = lane < 2 * CH && lbase + 32 * lane < rend && word < p.W;
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-        bw[j] = ((spm >> j & 1) && ok) ? p.bitmaps[(size_t)(hq0 + j) * p.W + word] : 0u;
-    }
+    // rows owned by this wave: [lbase, rend) of the split, 64 per ballot; the head rows
+    // keep their positions (their membership masks the softmax), the rest are listed
+    constexpr int CH = GCH;
     uint32_t mrow[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int r = lbase + c * 64 + lane;
-      mrow[c] = r < rend ? row_bits(bw, c) : 0u;
+      mrow[c] = r < rend ? row_bits(gbw, c) : 0u;
     }
-    int cnt = 0;
+    if (lane < head) sm.hmp[lbase + lane] = (uint8_t)mrow[0];
+    int cnt = head;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       if (lbase + c * 64 >= rend) break;
-      const uint64_t bal = __ballot(mrow[c] != 0u);
+      const bool listed = mrow[c] != 0u && (c > 0 || lane >= head);
+      const uint64_t bal = __ballot(listed);
       const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-      if (mrow[c]) {
+      if (listed) {
         sm.list[lbase + cnt + pre] = (uint16_t)(lbase + c * 64 + lane);
         sm.hmp[lbase + cnt + pre] = (uint8_t)mrow[c];
       }
@@ -836,15 +943,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   }
   __syncthreads();
 
-  // the group's epoch for the in-launch barriers, fetched here (after the membership
-  // words, before the first gathered rows) so that it has long arrived when the
-  // workgroup reaches its first barrier
-  const uint32_t epoch0 = p.gb ? ld_dev(p.gb_cnt + (size_t)(b * p.Hkv + g) * kGbCounters + kEpochWord) : 0u;
   int nchunks = dense ? chunks_of(nlist) : (nl_w + CROWS - 1) / CROWS;
-  if (!dense) {
-    if (nchunks > 0) load_chunk(0, kr[0], vr[0]);
-    if (nchunks > 1) load_chunk(1, kr[1], vr[1]);
-  }
+  if (!dense && nchunks > 1) load_chunk(1, kr[1], vr[1]);   // chunk 0 (the head) is on its way
 
   auto compute_chunk = [&](int c, const uint4 (&kd)[TPC][KCH], const uint4 (&vd)[RSC][NV]) {
     // q . K on the matrix cores
@@ -874,7 +974,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
         const bool mem = head_lane && pos < lim && ((hm >> mr) & 1u);
         const float s = dacc[t][r] * scale;
         if (ret_lane && pos < lim) {
-          if (lg) lg[pos] = s;                           // stream mode: pos is the row
+          if (lg) st_dev(lg + pos, s);                   // stream mode: pos is the row
           if (do_hist) atomicAdd(&sm.u.hist[mr][score_key(s) >> 21], 1u);
         }
         tl[t][r] = mem ? s * kLog2e : -LD_INF;
@@ -1027,46 +1127,79 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     }
   }
 
-  if (p.gb) {
-    uint32_t* gc = p.gb_cnt + (size_t)(b * p.Hkv + g) * kGbCounters;
-    uint64_t* rel = p.gb_rel + (size_t)(b * p.Hkv + g) * p.P * kRelStride;
-    // This call's epoch of the group (read in the prologue, before arriving; the
-    // workgroup that completes the first barrier advances it for the next call).
-    const uint32_t epoch = epoch0 + 1u;
-    const bool rl = group_barrier(gc, rel, split, nsplit_b, bid0, rel_word(epoch, 1u), p.err, &sm.misc[1]);
-    if (rl) {
-      if (tid == 0) st_dev(gc + kEpochWord, epoch);
-      // the next call's candidate counts of the group's rows start at zero
-      if (tid < G * kRep)
-        p.row_cnt[((size_t)((epoch + 1u) & 1u) * p.B * p.Hq + hq0) * kRep + tid] = 0u;
-    }
-    if (do_hist && ret && p.gb_select) {
-      if (rl) {
-        // the only reader of the row's histogram: clears it once digit 1 is out
-        const int slot = hq0 + __builtin_ctz(ret), kk = select_k(p, slot, nb);
-        if (kk >= 1) publish_digit1<D, G, NW>(sm, p, slot, kk, rel, nsplit_b, epoch);
-        hist1_clear(p.hist1, slot);
-      }
-      merge_columns<D, G, NW>(p, act, hq0, split, nsplit_b);
-      group_select<D, G, NW>(sm, p, ret, hq0, split, nsplit_b, bid0, nb, r0, nrows, gc, rel, epoch);
+  if (p.fin) {
+    // ---- the last arrivals of the group finish it: the last one merges O; the nsel
+    // before it each select retrieval rows of the group once it has arrived. They only
+    // wait for splits of the launch that still have work, and the host keeps their
+    // number far below the resident capacity, so every wait ends.
+    const uint32_t selm = do_hist ? ret : 0u;
+    const int nrow = __popc(selm);
+    // The group's last arrivals finish it: the last one and the nmg - 1 before it merge
+    // O, a slice of the output columns each; the nsel before those select the retrieval
+    // rows: `parts` per row when the group has enough late splits and the budget allows
+    // it, else one per row (whole rows, round robin); none: the last one selects them.
+    // Helpers and selectors wait only for the last arrival, a split of the launch that
+    // still has work; the host keeps their number below a quarter of the resident
+    // capacity, so every wait ends.
+    const int nmg = max(1, min(p.merge_w, nsplit_b));
+    const int room = min(p.sel_cap, nsplit_b - nmg);
+    int parts = nrow ? min(p.sel_parts, room / nrow) : 0;
+    int nsel;
+    if (parts >= 1) {
+      nsel = nrow * parts;
     } else {
-      // digit 1 of the i-th retrieval row of the group by split i (mod the splits)
-      if (do_hist && ret) {
-        int i = 0;
-        for (int j = 0; j < G; ++j) {
-          if (!(ret >> j & 1u)) continue;
-          if (i % nsplit_b == split) {
-            digit1_info<D, G, NW>(sm, p, hq0 + j, select_k(p, hq0 + j, nb));
-            hist1_clear(p.hist1, hq0 + j);
-          }
-          ++i;
-        }
-      }
-      merge_columns<D, G, NW>(p, act, hq0, split, nsplit_b);
+      parts = 1;
+      nsel = max(0, min(nrow, room));
     }
-    // nothing to clear on the way out: barrier counters return to zero by themselves,
-    // release words carry the epoch, histograms are cleared by their readers and the
-    // next call's counts were cleared above
+    uint32_t* tk = p.tickets + b * p.Hkv + g;
+    __builtin_amdgcn_s_waitcnt(0);            // partials, logits and counts are out
+    __syncthreads();
+    if (tid == 0)
+      sm.misc[0] = (int)__hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int t = sm.misc[0];
+    // release flags: [0, nmg - 1) merge helpers, then the selectors; set by the last
+    // arrival, cleared by their reader
+    uint64_t* rel = p.gb_rel + (size_t)(b * p.Hkv + g) * p.P * kRelStride;
+    const int late = nsplit_b - 1 - t;        // 0: the last arrival
+    constexpr int COLS = G * (D / 4);
+    int f = -1;                               // selector index
+    if (late == 0) {
+      // every split is in: clear the selecting rows' counters, release the others
+      if (tid < G && (selm >> tid & 1u)) st_dev(p.sel_cnt + (size_t)(hq0 + tid) * 2, 0u);
+      if (tid == 0) st_dev(tk, 0u);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (nmg - 1 + nsel) group_publish(rel, nmg - 1 + nsel, (uint64_t)1);
+    } else if (late < nmg + nsel) {
+      group_wait(rel, late - 1, (uint64_t)1, p.err);
+      if (tid == 0) st_dev(rel + (size_t)(late - 1) * kRelStride, (uint64_t)0);   // ready for the next call
+      if (late >= nmg) f = late - nmg;
+    } else {
+      return;
+    }
+    if (late < nmg) {
+      merge_final<D, G, NW>(p, act, hq0, nsplit_b, late * COLS / nmg, (late + 1) * COLS / nmg);
+      if (!(late == 0 && nsel == 0)) return;
+    }
+    // this workgroup's rows: with parts > 1, part f % parts of row f / parts; else rows
+    // i with i % nsel == f (the last arrival takes them all when nsel is 0)
+    int i = 0;
+    for (int j = 0; j < G; ++j) {
+      if (!(selm >> j & 1u)) continue;
+      int part = 0;
+      bool mine;
+      if (parts > 1) {
+        mine = f >= 0 && f < nsel && f / parts == i;
+        part = f % parts;
+      } else {
+        mine = nsel ? (f >= 0 && f < nsel && i % nsel == f) : (late == 0);
+      }
+      ++i;
+      if (mine)
+        part_select<NW>(sm.u.sel.hist, sm.u.sel.cand, sm.wcnt, sm.res, sm.tmp4, sm.poff, sm.pcnt, p, hq0 + j, nb,
+                        part, parts);
+    }
     return;
   }
 
@@ -1114,10 +1247,6 @@ int64_t capacity_dgf(int waves) {
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attention<D, G, 4, F8>, 256, 0);
   return e == hipSuccess ? per_cu : 0;
 }
-template <int D, int G>
-int64_t capacity_dg(int waves, bool fp8) {
-  return fp8 ? capacity_dgf<D, G, true>(waves) : capacity_dgf<D, G, false>(waves);
-}
 
 template <int D, int G, bool F8>
 hipError_t launch_dgf(const AttnParams& p, dim3 grid, hipStream_t st) {
@@ -1127,64 +1256,29 @@ hipError_t launch_dgf(const AttnParams& p, dim3 grid, hipStream_t st) {
     hipLaunchKernelGGL((k_attention<D, G, 4, F8>), grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
-template <int D, int G>
-hipError_t launch_dg(const AttnParams& p, dim3 grid, hipStream_t st) {
-  return p.kv_fp8 ? launch_dgf<D, G, true>(p, grid, st) : launch_dgf<D, G, false>(p, grid, st);
-}
 
 }  // namespace
 
-int64_t attention_capacity(int D, int G, int waves, bool fp8) {
-  // cached per device and (D, G, waves, KV format)
-  static std::atomic<int64_t> cache[64][2][4][2][2];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  const int di = D == 128 ? 1 : 0;
-  const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
-  const int wi = waves == 8 ? 1 : 0;
-  const int fi = fp8 ? 1 : 0;
-  int64_t c = cache[dev][di][gi][wi][fi].load(std::memory_order_relaxed);
-  if (c > 0) return c;
-  int64_t per_cu = 0;
-  if (D == 128) {
-    switch (G) {
-      case 1: per_cu = capacity_dg<128, 1>(waves, fp8); break;
-      case 2: per_cu = capacity_dg<128, 2>(waves, fp8); break;
-      case 4: per_cu = capacity_dg<128, 4>(waves, fp8); break;
-      case 8: per_cu = capacity_dg<128, 8>(waves, fp8); break;
-    }
-  } else {
-    switch (G) {
-      case 1: per_cu = capacity_dg<64, 1>(waves, fp8); break;
-      case 2: per_cu = capacity_dg<64, 2>(waves, fp8); break;
-      case 4: per_cu = capacity_dg<64, 4>(waves, fp8); break;
-      case 8: per_cu = capacity_dg<64, 8>(waves, fp8); break;
-    }
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  c = per_cu * cus;
-  cache[dev][di][gi][wi][fi].store(c, std::memory_order_relaxed);
-  return c;
+// This file is compiled once per KV group size (LD_ATTN_G = 1, 2, 4 or 8), so that the
+// kernel instantiations compile in parallel; the dispatch over G is in ld_api.hip.
+#ifndef LD_ATTN_G
+#error "compile ld_attention.hip with -DLD_ATTN_G=<1|2|4|8>"
+#endif
+
+template <int G>
+int64_t attention_capacity_g(int D, int waves, bool fp8) {
+  if (D == 128) return fp8 ? capacity_dgf<128, G, true>(waves) : capacity_dgf<128, G, false>(waves);
+  return fp8 ? capacity_dgf<64, G, true>(waves) : capacity_dgf<64, G, false>(waves);
 }
 
-hipError_t launch_attention(const AttnParams& p, int D, int G, dim3 grid, hipStream_t st) {
-  if (D == 128) {
-    switch (G) {
-      case 1: return launch_dg<128, 1>(p, grid, st);
-      case 2: return launch_dg<128, 2>(p, grid, st);
-      case 4: return launch_dg<128, 4>(p, grid, st);
-      case 8: return launch_dg<128, 8>(p, grid, st);
-    }
-  } else if (D == 64) {
-    switch (G) {
-      case 1: return launch_dg<64, 1>(p, grid, st);
-      case 2: return launch_dg<64, 2>(p, grid, st);
-      case 4: return launch_dg<64, 4>(p, grid, st);
-      case 8: return launch_dg<64, 8>(p, grid, st);
-    }
-  }
+template <int G>
+hipError_t launch_attention_g(const AttnParams& p, int D, dim3 grid, hipStream_t st) {
+  if (D == 128) return p.kv_fp8 ? launch_dgf<128, G, true>(p, grid, st) : launch_dgf<128, G, false>(p, grid, st);
+  if (D == 64) return p.kv_fp8 ? launch_dgf<64, G, true>(p, grid, st) : launch_dgf<64, G, false>(p, grid, st);
   return hipErrorInvalidValue;
 }
+
+template int64_t attention_capacity_g<LD_ATTN_G>(int, int, bool);
+template hipError_t launch_attention_g<LD_ATTN_G>(const AttnParams&, int, dim3, hipStream_t);
 
 }  // namespace ld

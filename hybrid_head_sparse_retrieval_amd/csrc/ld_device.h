@@ -60,6 +60,22 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// S row of query-head slot `slot`: dense [slot * k_dense, +k_dense), or the CSR row
+// [s_indptr[slot], s_indptr[slot + 1]) clipped to the s_cap entries of the S buffer, so
+// that malformed offsets never reach outside it.
+__device__ __forceinline__ void s_row(const int64_t* s_indptr, int k_dense, int64_t s_cap, int slot, int64_t* so,
+                                      int* len) {
+  if (!s_indptr) {
+    *so = (int64_t)slot * k_dense;
+    *len = k_dense;
+    return;
+  }
+  const int64_t a = min(max(s_indptr[slot], (int64_t)0), s_cap);
+  const int64_t e = min(max(s_indptr[slot + 1], a), s_cap);
+  *so = a;
+  *len = (int)min(e - a, (int64_t)0x7fffffff);
+}
+
 // Device-coherent accesses for data handed between workgroups of one launch: stores
 // write through to the device coherence point and loads read from it (sc1), so no
 // L2 writeback/invalidate fence is needed around the hand-off.
@@ -271,6 +287,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
 constexpr int kSc1 = 16;   // cache-policy bit of sc1 for buffer instructions
+// The same over `bytes` bytes from `base`: loads past them return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_n(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
 
 // Digit-1 histogram rows: writers add to their replica; hist1_sum (every thread of the
 // workgroup) writes the sum of the kRep replicas of row `slot` to lds[kHist1Bins],
@@ -286,71 +306,44 @@ __device__ __forceinline__ void hist1_clear(uint32_t* h1, int slot) {
 }
 __device__ __forceinline__ void hist1_sum(uint32_t* lds, const uint32_t* h1, int slot) {
   const __amdgpu_buffer_rsrc_t r = rsrc(h1 + (size_t)slot * kRep * kHist1Bins);
-  for (int i = threadIdx.x; i < kHist1Bins / 4; i += (int)blockDim.x) {
-    u32x4_t a = {0u, 0u, 0u, 0u};
+  // every load of the thread's columns is issued before the first sum
+  constexpr int kMaxCols = 4;                  // column groups per thread (blockDim.x >= 128)
+  const int nt = (int)blockDim.x;
+  u32x4_t a[kMaxCols][kRep];
 #pragma unroll
-    for (int q = 0; q < kRep; ++q) a += __builtin_amdgcn_raw_buffer_load_b128(r, (q * kHist1Bins + 4 * i) * 4, 0, kSc1);
-    lds[4 * i + 0] = a.x;
-    lds[4 * i + 1] = a.y;
-    lds[4 * i + 2] = a.z;
-    lds[4 * i + 3] = a.w;
+  for (int c = 0; c < kMaxCols; ++c) {
+    const int i = threadIdx.x + c * nt;
+#pragma unroll
+    for (int q = 0; q < kRep; ++q)
+      if (i < kHist1Bins / 4) a[c][q] = __builtin_amdgcn_raw_buffer_load_b128(r, (q * kHist1Bins + 4 * i) * 4, 0, kSc1);
   }
-}
-
-// Arrival count of the ns workgroups with ids bid0 .. bid0+ns-1, all resident at once:
-// counted per replica (cnt[0..kRep-1]), then per group (cnt[kRep]) by the last arrival
-// of each replica, so that no counter sees more than ceil(ns / kRep) or kRep atomics.
-// A counter is back at zero once its arrivals are complete. Every thread calls it after
-// its earlier stores, loads and atomics; true in every thread of the workgroup whose
-// arrival completes the group.
-__device__ __forceinline__ bool group_arrive(uint32_t* cnt, int ns, int bid0, int* flag) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int r = rep_of_block();
-    const int first = ((r - bid0) % kRep + kRep) % kRep;     // first member with this residue
-    const int nr = first < ns ? (ns - first + kRep - 1) / kRep : 0;
-    const int nres = ns < kRep ? ns : kRep;
-    bool last = false;
-    const uint32_t old = __hip_atomic_fetch_add(cnt + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1u == (uint32_t)nr) {
-      // the replica is complete: its counter is free again for the next call, and so
-      // is the group count once the group is complete
-      st_dev(cnt + r, 0u);
-      const uint32_t o2 = __hip_atomic_fetch_add(cnt + kRep, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = (o2 + 1u == (uint32_t)nres);
-      if (last) st_dev(cnt + kRep, 0u);
+#pragma unroll
+  for (int c = 0; c < kMaxCols; ++c) {
+    const int i = threadIdx.x + c * nt;
+    if (i < kHist1Bins / 4) {
+      u32x4_t t = a[c][0];
+#pragma unroll
+      for (int q = 1; q < kRep; ++q) t += a[c][q];
+      lds[4 * i + 0] = t.x;
+      lds[4 * i + 1] = t.y;
+      lds[4 * i + 2] = t.z;
+      lds[4 * i + 3] = t.w;
     }
-    *flag = last ? 1 : 0;
   }
-  __syncthreads();
-  return *flag != 0;
 }
 
-// Release words of a group: one 64-bit word per member, on a 128-byte line of its own
-// (rel[s * kRelStride]), and a 64-bit payload word next to it. A word holds the call's
-// epoch in bits 32..63 and the stage the group has reached in bits 0..7, so words never
-// need clearing: every call of a group waits for values of its own epoch, one above
-// the previous call's.
+// Release flags of a KV group's selectors: one 64-bit word per selector, on a 128-byte
+// line of its own (rel[s * kRelStride]), so pollers never share a line.
 constexpr int kRelStride = 16;
-__device__ __forceinline__ uint64_t rel_word(uint32_t epoch, uint32_t stage) {
-  return ((uint64_t)epoch << 32) | stage;
-}
 
-// Every member's release word := w (each by thread s % blockDim.x). With a payload,
-// the payload words are written first and complete before any release word is.
+// Every member's release word := w (each by thread s % blockDim.x).
 __device__ __forceinline__ void group_publish(uint64_t* rel, int ns, uint64_t w) {
   for (int s = threadIdx.x; s < ns; s += (int)blockDim.x) st_dev(rel + (size_t)s * kRelStride, w);
 }
-__device__ __forceinline__ void group_publish(uint64_t* rel, int ns, uint64_t w, uint64_t payload) {
-  for (int s = threadIdx.x; s < ns; s += (int)blockDim.x) st_dev(rel + (size_t)s * kRelStride + 1, payload);
-  __builtin_amdgcn_s_waitcnt(0);
-  group_publish(rel, ns, w);
-}
 
-// Waits until this member's release word reaches w (epoch and stage). Thread 0 polls
-// with a read-modify-write, performed where the release lands and never on a stale
-// copy. The wait is bounded; giving up sets *err.
+// Waits until this member's release word reaches w. Thread 0 polls with a
+// read-modify-write, performed where the release lands and never on a stale copy. The
+// wait is bounded; giving up sets *err.
 __device__ __forceinline__ void group_wait(uint64_t* rel, int me, uint64_t w, uint32_t* err) {
   if (threadIdx.x == 0) {
     uint64_t* mine = rel + (size_t)me * kRelStride;
@@ -364,30 +357,6 @@ __device__ __forceinline__ void group_wait(uint64_t* rel, int me, uint64_t w, ui
     }
   }
   __syncthreads();
-}
-// The same, then the payload that came with the release word (in every thread).
-__device__ __forceinline__ uint64_t group_wait_payload(uint64_t* rel, int me, uint64_t w, uint32_t* err,
-                                                       uint64_t* slot) {
-  group_wait(rel, me, w, err);
-  if (threadIdx.x == 0) *slot = ld_dev(rel + (size_t)me * kRelStride + 1);
-  __syncthreads();
-  const uint64_t v = *slot;
-  __syncthreads();
-  return v;
-}
-
-// Barrier of the ns workgroups of a group (ids bid0 .. bid0+ns-1), all resident at
-// once, at release word w: the workgroup whose arrival completes the group publishes w
-// to every member; the others wait for it. Returns true in the workgroup that
-// completed the group.
-__device__ __forceinline__ bool group_barrier(uint32_t* cnt, uint64_t* rel, int me, int ns, int bid0, uint64_t w,
-                                              uint32_t* err, int* flag) {
-  if (group_arrive(cnt, ns, bid0, flag)) {
-    group_publish(rel, ns, w);
-    return true;
-  }
-  group_wait(rel, me, w, err);
-  return false;
 }
 
 }  // namespace ld

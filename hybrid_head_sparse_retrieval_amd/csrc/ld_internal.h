@@ -25,74 +25,77 @@ constexpr int kBitmapWordsPerBlock = 4096;           // bitmap-build LDS tile (1
 constexpr int kMaxSpins = 1 << 22;     // bound of a barrier wait (polls with a short sleep)
 constexpr int kRep = 8;                // replicas of shared counters and histograms (workgroup id % kRep,
                                        // which is the XCD the workgroup runs on)
-constexpr int kGbCounters = 48;        // per KV group: barrier counters (kRep + 1 each) and the epoch
-constexpr int kEpochWord = 40;         // the group's epoch: in-launch barrier calls so far
+constexpr int kMaxParts = 32;          // selector workgroups per retrieval row, at most
 
 // ---------------------------------------------------------------- parameters
 
 // Attention over one layer: workgroup = (sequence b, KV group, split of rows).
 struct AttnParams {
+  // The workgroup prologue reads the first fields (split decode, sequence bounds, head
+  // roles, first loads): they come first, so that its dependent kernel-argument reads
+  // share a few scalar-cache lines.
+  int B, Hq, Hkv, seq_len;
+  // Groups that stream every row (they serve a retrieval head) come first in the grid
+  // and use splits of ts_d rows; groups of sparse heads use splits of ts_s rows.
+  int ts_d, ts_s;         // rows per split (multiples of 64)
+  int nsplit_d, nsplit_s; // splits per sequence at seq_len (grid strides)
+  int ngroups;            // KV groups launched
+  int ng_dense;           // the first ng_dense of them stream
+  int page_shift;         // paged KV (> 0): see block_table
+  int W;                  // bitmap words per row
+  uint64_t dense_groups;  // bit g: KV group g is launched and streams (ids ascending)
+  uint64_t sparse_groups; // bit g: KV group g is launched and gathers (ids ascending, after
+                          // the streaming ones)
+  uint64_t active;        // heads computed by this launch
+  uint64_t retrieval;     // heads attending to every row (subset of active)
+  const int64_t* kv_indptr;
+  int64_t kv_head_stride; // T*D elements
+  int64_t total_tokens;   // T
   const uint16_t* q;      // bf16 [B][Hq][D]
   const void* kc;         // [Hkv][T][D], bf16, or E4M3 codes when kv_fp8
   const void* vc;
+  uint32_t* bitmaps;      // [B*Hq][W] membership bits (read: sparse heads; written: selecting heads)
+  float* logits;          // [B*Hq][seq_len] scores of retrieval heads, or null
+  int do_topk;            // fused first selection digit and in-launch selection
+  float scale;            // logit scale
+  // paged KV (page_shift > 0): logical row i of sequence b is pool row
+  // block_table[b * pages_per_seq + (i >> page_shift)] << page_shift | (i & page - 1)
+  const int32_t* block_table;
+  int pages_per_seq;
   int kv_fp8;
+  int64_t npages;
   float v_scale;          // factor on O (the V dequantisation scale; 1 for bf16)
+  int waves;              // waves per workgroup (4 or 8)
   uint16_t* out;          // bf16 [B][Hq][D]
   // HySparse gate (or null): O is written as w * O + (1 - w) * o_win[row] with
   // w = sigmoid(gate[row]), row = b * Hq + h; o_win fp32 [B*Hq][D]
   const float* gate;
   const float* o_win;
-  const int64_t* kv_indptr;
-  int64_t kv_head_stride; // T*D elements
-  int64_t total_tokens;   // T
-  // paged KV (page_shift > 0): logical row i of sequence b is pool row
-  // block_table[b * pages_per_seq + (i >> page_shift)] << page_shift | (i & page - 1)
-  const int32_t* block_table;
-  int page_shift, pages_per_seq;
-  int64_t npages;
-  int B, Hq, Hkv, seq_len;
-  float scale;            // logit scale
-  uint64_t active;        // heads computed by this launch
-  uint64_t retrieval;     // heads attending to every row (subset of active)
-  // Groups that stream every row (they serve a retrieval head) come first in groups[]
-  // and use splits of ts_d rows; groups of sparse heads use splits of ts_s rows.
-  int ts_d, ts_s;         // rows per split (multiples of 64)
-  int nsplit_d, nsplit_s; // splits per sequence at seq_len (grid strides)
-  int waves;              // waves per workgroup (4 or 8)
-  int ngroups;            // KV groups launched
-  int ng_dense;           // the first ng_dense of them stream
-  uint8_t groups[64];     // their ids
-  uint32_t* bitmaps;      // [B*Hq][W] membership bits (read: sparse heads; written: selecting heads)
-  int W;
-  float* logits;          // [B*Hq][seq_len] scores of retrieval heads, or null
   float* part_ml;         // [B*Hq][P][2]  (max in log2 units, sum)
   float* part_acc;        // [B*Hq][P][D]
   int P;                  // partial stride in splits
+  int P1;                 // first-level partial stride (ceil(P / kMergeRun))
   uint32_t* tickets;      // [B*Hkv], zero between calls
   uint32_t* tickets_l1;   // [B*Hkv][P1], zero between calls
   float* l1_ml;           // [B*Hq][P1][2]  first-level merged partials
   float* l1_acc;          // [B*Hq][P1][D]
-  int P1;                 // first-level partial stride (ceil(P / kMergeRun))
-  // fused first selection digit (only when do_topk)
-  int do_topk;
   uint32_t* hist1;        // [B*Hq][kRep][kHist1Bins] (summed over replicas), zero between calls
   uint32_t* sel_info;     // [B*Hq][4]
   int k_dense;
+  // finisher mode: the last split of each (b, g) to arrive merges O; with do_topk, up to
+  // sel_cap splits that arrive just before it wait for it and then select the group's
+  // retrieval rows, one workgroup per row (otherwise the last one selects them)
+  int fin;
   const int64_t* s_indptr;
-  // group-barrier mode (every workgroup of the launch resident at once): the splits of
-  // a group meet after storing their partials, merge O column by column and run the
-  // selection of the group's retrieval head over their own rows (gb_select = 1), or
-  // only take digit 1 of each retrieval row for a selection launch that follows
-  // (gb_select = 0)
-  int gb;
-  int gb_select;
-  uint32_t* gb_cnt;       // [B*Hkv][kGbCounters] barrier counters (zero between calls) and epochs
-  uint64_t* gb_rel;       // [B*Hkv][P] release words, one per 128 bytes, zero between calls
-  uint32_t* row_cnt;      // [2][B*Hq][kRep] candidates appended to each sub-list; the half of the
-                          // epoch's parity is zero when a call starts
-  uint32_t* cand;         // [B*Hq][kRep][sub_cap] candidates: split << 21 | low 21 bits of the key
-  int64_t sub_cap;
-  uint32_t* pub;          // [B*Hq][P][2] per split: keys above bin b1
+  int64_t s_cap;          // CSR S: entries of the S buffers (rows are clipped to them)
+  int merge_w;            // workgroups that merge a KV group's O, at most
+  int sel_cap;            // selectors per KV group, at most
+  int sel_parts;          // selectors per retrieval row, at most (<= kMaxParts)
+  uint32_t* sel_cnt;      // [B*Hq][2]: parts arrived (cleared per call)
+  uint32_t* sel_cand;     // [B*Hq][seq_len] candidates (key bits 20..0), part q's from its first row
+  uint64_t* sel_pub;      // [B*Hq][kMaxParts] per part: keys above bin b1 | candidates << 32
+  uint64_t* gb_rel;       // [B*Hkv][P] release flags of the selectors (1: released; the
+                          // selector clears its flag once it has seen it)
   int32_t* s_out;         // S rows written for selecting heads
   uint32_t* err;          // set when a barrier gave up waiting (never expected)
 };
@@ -104,11 +107,15 @@ struct SelParams {
   int C;                  // span-grid stride of the select passes (kSelSpan scores per span)
   int Ch;                 // chunk-grid stride of the standalone histogram (hchunk scores per chunk)
   int hchunk;             // scores per histogram workgroup (a multiple of kSelChunk)
-  // standalone
+  // standalone: row r has n_r = n_per_row ? clamp(n_per_row[r], 0, n) : n scores and
+  // keeps k_r = min(k_per_row ? k_per_row[r] : k, row capacity, n_r) indices; rows are
+  // idx_out + r * k (capacity k) or, with idx_indptr, idx_out + idx_indptr[r] (capacity
+  // idx_indptr[r + 1] - idx_indptr[r])
   const float* scores; int64_t row_stride; int n; int k; int32_t* idx_out; float* val_out;
+  const int32_t* n_per_row; const int32_t* k_per_row; const int64_t* idx_indptr;
   // layer rows: row r -> (b = r / nret, h = heads[r % nret])
   const float* logits; int Hq; int seq_len; const int64_t* kv_indptr;
-  int32_t* s_out; const int64_t* s_indptr; int k_dense;
+  int32_t* s_out; const int64_t* s_indptr; int k_dense; int64_t s_cap;
   uint32_t* bitmaps; int W;
   int nret; uint8_t heads[64];
   // workspace (per row slot)
@@ -126,7 +133,7 @@ struct SelParams {
 
 // Build membership bitmaps of sparse heads from S rows.
 struct BitmapParams {
-  const int32_t* s; const int64_t* s_indptr; int k_dense;
+  const int32_t* s; const int64_t* s_indptr; int k_dense; int64_t s_cap;
   const int64_t* kv_indptr; int seq_len;
   int Hq; int nsp; uint8_t heads[64];   // row r -> (b = r / nsp, h = heads[r % nsp])
   uint32_t* bitmaps; int W;
@@ -134,7 +141,7 @@ struct BitmapParams {
 };
 
 struct CopyParams {
-  const int32_t* src; int32_t* dst; const int64_t* s_indptr; int k_dense;
+  const int32_t* src; int32_t* dst; const int64_t* s_indptr; int k_dense; int64_t s_cap;
   int Hq; int nsp; uint8_t heads[64];
 };
 
@@ -155,6 +162,10 @@ constexpr int kBlock = 64;                // tokens per block
 
 hipError_t launch_attention(const AttnParams& p, int D, int G, dim3 grid, hipStream_t st);
 int64_t attention_capacity(int D, int G, int waves, bool fp8);   // workgroups resident at once
+// per KV group size G (ld_attention.hip, one compilation per G): occupancy per compute
+// unit and the launch
+template <int G> int64_t attention_capacity_g(int D, int waves, bool fp8);
+template <int G> hipError_t launch_attention_g(const AttnParams& p, int D, dim3 grid, hipStream_t st);
 hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist);
 hipError_t launch_bitmap_build(const BitmapParams& p, int rows, hipStream_t st);
 hipError_t launch_copy_rows(const CopyParams& p, int rows, hipStream_t st);

@@ -39,10 +39,20 @@ __device__ __forceinline__ RowView row_view(const SelParams& p, int r) {
   RowView v;
   if (p.mode == 0) {
     v.sc = p.scores + (int64_t)r * p.row_stride;
-    v.n = p.n;
-    v.k = p.k;
-    v.out = p.idx_out + (int64_t)r * p.k;
-    v.vout = p.val_out ? p.val_out + (int64_t)r * p.k : nullptr;
+    v.n = p.n_per_row ? max(0, min(p.n_per_row[r], p.n)) : p.n;
+    int k = p.k_per_row ? p.k_per_row[r] : p.k;
+    int64_t o;
+    if (p.idx_indptr) {
+      o = p.idx_indptr[r];
+      const int64_t cap = p.idx_indptr[r + 1] - o;
+      k = (int)max((int64_t)0, min((int64_t)k, cap));
+    } else {
+      o = (int64_t)r * p.k;
+      k = min(k, p.k);
+    }
+    v.k = max(0, min(k, v.n));              // the pages' clamp k = min(k, n)
+    v.out = p.idx_out + o;
+    v.vout = p.val_out ? p.val_out + o : nullptr;
     v.bm = nullptr;
     v.slot = r;
   } else {
@@ -52,13 +62,7 @@ __device__ __forceinline__ RowView row_view(const SelParams& p, int r) {
     n = max(0, min(n, p.seq_len));
     int64_t so;
     int k;
-    if (p.s_indptr) {
-      so = p.s_indptr[slot];
-      k = (int)(p.s_indptr[slot + 1] - so);
-    } else {
-      so = (int64_t)slot * p.k_dense;
-      k = p.k_dense;
-    }
+    s_row(p.s_indptr, p.k_dense, p.s_cap, slot, &so, &k);
     v.sc = p.logits + (size_t)slot * p.seq_len;
     v.n = n;
     v.k = min(k, n);
@@ -165,6 +169,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_sel_small(const SelParams p) 
   __shared__ uint32_t res[2];
   const int tid = threadIdx.x;
   const RowView v = row_view(p, blockIdx.x);
+  if (v.n < 1 || v.k < 1) return;
   const int n = v.n;
   const uint32_t k = (uint32_t)v.k;
   uint32_t key[kSmallPer];
@@ -688,13 +693,7 @@ __global__ __launch_bounds__(kThreads) void k_bitmap_build(const BitmapParams p)
   const int w1 = min(nw, w0 + kBitmapWordsPerBlock);
   int64_t so;
   int kk;
-  if (p.s_indptr) {
-    so = p.s_indptr[slot];
-    kk = (int)(p.s_indptr[slot + 1] - so);
-  } else {
-    so = (int64_t)slot * p.k_dense;
-    kk = p.k_dense;
-  }
+  s_row(p.s_indptr, p.k_dense, p.s_cap, slot, &so, &kk);
   const int tid = threadIdx.x;
   for (int i = tid; i < w1 - w0; i += kThreads) bits[i] = 0;
   __syncthreads();
@@ -717,13 +716,7 @@ __global__ __launch_bounds__(kThreads) void k_copy_rows(const CopyParams p) {
   const int slot = b * p.Hq + h;
   int64_t so;
   int kk;
-  if (p.s_indptr) {
-    so = p.s_indptr[slot];
-    kk = (int)(p.s_indptr[slot + 1] - so);
-  } else {
-    so = (int64_t)slot * p.k_dense;
-    kk = p.k_dense;
-  }
+  s_row(p.s_indptr, p.k_dense, p.s_cap, slot, &so, &kk);
   for (int i = threadIdx.x; i < kk; i += kThreads) p.dst[so + i] = p.src[so + i];
 }
 

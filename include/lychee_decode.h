@@ -46,7 +46,8 @@
  *    returns an error code and launches nothing. Launch failures return LD_ERR_HIP.
  *    Faults inside kernels surface at the caller's next synchronisation. Per-sequence
  *    device-side values (kv_indptr, s_indptr) are preconditions: N_b >= 1 and
- *    1 <= k_{b,h} <= N_b; the kernels clamp k to N_b and never write outside a row.
+ *    1 <= k_{b,h} <= N_b; the kernels clamp k to N_b, clip CSR rows to
+ *    ld_shape.s_capacity and never write outside a row.
  */
 #ifndef LYCHEE_DECODE_H
 #define LYCHEE_DECODE_H
@@ -81,11 +82,13 @@ enum {
      workspace with the same shape, so the workspace's per-head membership bitmaps
      already describe s_in and need not be rebuilt. */
   LD_FLAG_S_CHAINED = 1u << 1,
-  /* Launch-shape override: merge the split partials and run argsTopK in their own
-     steps after the attention launch, even when the whole launch fits on the device
-     at once (where, by default, the splits of each KV group meet at device-wide
-     barriers, merge O themselves and, when the group has one retrieval head, select
-     its S too). S is the same either way; O may differ by fp32 rounding. */
+  /* Launch-shape override: merge the split partials by tickets inside the attention
+     launch and run argsTopK in launches of their own after it. By default the last
+     split of each KV group to arrive merges O (with a few helpers) and the splits that
+     arrive just before it select the group's S inside the same launch; the library
+     itself takes the separate launches when the retrieval rows are too many for the
+     in-launch selectors (e.g. a layer whose every head retrieves over a long context).
+     S is the same either way; O may differ by fp32 rounding. */
   LD_FLAG_SEPARATE_SELECT = 1u << 2,
   /* Token-block selection (HySparse, section 3): a retrieval head keeps the k/64 blocks
      of 64 consecutive tokens with the largest block maxima of its logits (ties to the
@@ -130,6 +133,10 @@ typedef struct ld_shape {
   float k_scale;          /* kv_dtype 1: K dequantisation scale (> 0); else 0 */
   float v_scale;          /* kv_dtype 1: V dequantisation scale (> 0); else 0 */
   int32_t reserved;       /* must be 0 */
+  int64_t s_capacity;     /* CSR S (s_indptr given): entries of the S buffers s_in and
+                             s_out, required >= 1; every row [s_indptr[r],
+                             s_indptr[r+1]) is clipped to [0, s_capacity), so offsets
+                             past the buffer are never read or written. Dense S: 0. */
 } ld_shape;
 
 /* Human-readable text of a status code (static storage). */
@@ -245,13 +252,23 @@ ld_status ld_hybrid_layer(const ld_shape* shape, uint64_t retrieval_mask,
                           uint32_t flags, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
-/* Standalone argsTopK (method step 3) on fp32 scores: for each of `rows` rows of `n`
-   values (row r starts at scores + r*row_stride), writes the k selected indices in
-   ascending order to idx_out[r*k .. r*k+k) and, when val_out is non-NULL, their
-   scores to val_out (same positions). Bit-exact: the result depends only on the fp32
-   values and the order stated above. Requires 1 <= k <= n, row_stride >= n. */
+/* Standalone argsTopK (method step 3) on fp32 scores, row by row. Row r has
+   n_r = n_per_row ? min(max(n_per_row[r], 0), n) : n scores starting at
+   scores + r*row_stride, and keeps k_r indices: k_r = k_per_row ? k_per_row[r] : k,
+   clamped to the row's output capacity and to n_r (the pages' k = min(k, seq_len):
+   "Token Sparse Attention" skill page, Step 3; "LycheeDecode: Head-Level KV Cache
+   Sharing" skill page, Step 1). Output rows: dense, idx_out + r*k with capacity k
+   (k_per_row values above k are clamped to k), or CSR with idx_indptr (device int64,
+   rows+1 offsets), idx_out + idx_indptr[r] with capacity idx_indptr[r+1] -
+   idx_indptr[r]. The k_r indices are written in ascending order; entries past k_r are
+   left as they were, and a row with k_r < 1 is left untouched. val_out (nullable)
+   receives their scores at the same positions. n_per_row and k_per_row are device int32
+   arrays of `rows` entries (nullable). Bit-exact: the result depends only on the fp32
+   values and the order stated above. Requires rows >= 1, 1 <= n <= 2097152, k >= 1,
+   row_stride >= n; the workspace holds ld_topk_workspace_size(rows, n) bytes. */
 ld_status ld_topk_select(const float* scores, int32_t rows, int32_t n, int64_t row_stride,
-                         int32_t k, int32_t* idx_out, float* val_out,
+                         const int32_t* n_per_row, int32_t k, const int32_t* k_per_row,
+                         int32_t* idx_out, const int64_t* idx_indptr, float* val_out,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ld_hybrid_layer without a workspace, for callers that cannot allocate device memory:

@@ -130,6 +130,29 @@ def test_noalloc_rejects_before_any_device_call(lib):
     assert na(fits, mask=1 << 40) == INV
 
 
+def test_csr_s_needs_its_capacity(lib):
+    """CSR S rows are clipped to ld_shape.s_capacity on the device; a call with CSR
+    offsets and no capacity is rejected before any launch."""
+    s = _shape()
+    assert _hyb(lib, s, s_indptr=FAKE) == 1
+    assert _hyb(lib, _shape(s_capacity=-1)) == 1
+
+
+def test_binding_clamps_k_and_sets_the_s_capacity():
+    class Buf:
+        def __init__(self, n):
+            self.n = n
+
+        def numel(self):
+            return self.n
+    s = _shape(seq_len=100)
+    assert ld._clamp_k(s, 250, None, [("s", Buf(10))]) == 100 and s.s_capacity == 0
+    assert ld._clamp_k(s, 30, object(), [("s", Buf(500)), ("s_out", Buf(400))]) == 30
+    assert s.s_capacity == 400
+    with pytest.raises(ValueError):
+        ld._clamp_k(s, 0, None, [])
+
+
 def test_hysparse_workspace_and_arguments(lib):
     s = _shape()
     n = lib.ld_hysparse_workspace_size(ctypes.byref(s), 9830, 128)
@@ -181,11 +204,19 @@ def test_tsa_workspace_and_arguments(lib):
 
 def test_topk_invalid_arguments(lib):
     f = lib.ld_topk_select
-    assert f(None, 1, 10, 10, 3, FAKE, None, FAKE, 1 << 30, None) == 1
-    assert f(FAKE, 1, 10, 10, 0, FAKE, None, FAKE, 1 << 30, None) == 1
-    assert f(FAKE, 1, 10, 10, 11, FAKE, None, FAKE, 1 << 30, None) == 1
-    assert f(FAKE, 1, 10, 9, 3, FAKE, None, FAKE, 1 << 30, None) == 1
-    assert f(FAKE, 1, 10, 10, 3, FAKE, None, FAKE, 16, None) == 3
+
+    def call(sc=FAKE, rows=1, n=10, stride=10, n_per_row=None, k=3, k_per_row=None, idx=FAKE, ind=None,
+             val=None, ws=FAKE, wsb=1 << 30):
+        return f(sc, rows, n, stride, n_per_row, k, k_per_row, idx, ind, val, ws, wsb, None)
+    assert call(sc=None) == 1 and call(idx=None) == 1
+    assert call(k=0) == 1                                   # k < 1
+    assert call(stride=9) == 1                              # rows overlap
+    assert call(n=0) == 1 and call(rows=0) == 1
+    assert call(n_per_row=FAKE + 2) == 1                    # misaligned per-row arrays
+    assert call(k_per_row=FAKE + 1) == 1
+    assert call(ind=FAKE + 4) == 1                          # int64 offsets: 8-byte aligned
+    assert call(ws=16, wsb=16) == 3
+    assert call(wsb=16) == 3
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -327,3 +327,44 @@ def test_undersized_buffers_are_rejected_before_launch():
     with pytest.raises(ValueError, match="kv_indptr"):
         ld.hybrid_layer(q, kc, kc, 0xFF, k, None, s_out=S, seq_len=n,
                         kv_indptr=torch.zeros(3, dtype=torch.int64, device=dev))
+
+
+def test_csr_rows_are_clipped_to_the_s_buffer():
+    """CSR offsets that run past the S buffer: every kernel clips each row to the buffer
+    (ld_shape.s_capacity), so nothing past it is read or written; rows inside it are
+    the oracle's selection, a clipped row keeps as many of its row's best indices as fit."""
+    ld = _ld()
+    dev = "cuda"
+    B, Hq, Hkv, d = 2, 4, 4, 64
+    lens = [700, 900]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    rows = [200] * (B * Hq)
+    ind_h = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    cap = int(ind_h[-1]) - 350                      # the last two rows run past the buffer
+    guard = torch.full((int(ind_h[-1]) + 64,), -5, dtype=torch.int32, device=dev)
+    S = guard[:cap]
+    s_indptr = torch.as_tensor(ind_h, device=dev)
+    kv_indptr = torch.as_tensor(offs, device=dev)
+    masks = [0xF, 0b0100]
+    for l, mask in enumerate(masks):
+        qc, kc, vc = wl.random_qkv(B, Hq, Hkv, d, int(offs[-1]), 900 + l)
+        out = torch.empty_like(qc, device=dev)
+        scores = torch.full((B, Hq, max(lens)), float("nan"), dtype=torch.float32, device=dev)
+        S_before = S.cpu().numpy().copy()
+        ld.hybrid_layer(qc.to(dev), kc.to(dev), vc.to(dev), mask, 200, S if l else None, s_out=S,
+                        s_indptr=s_indptr, scores_out=scores, out=out, kv_indptr=kv_indptr, seq_len=max(lens),
+                        flags=ld.FLAG_S_CHAINED if l else 0)
+        torch.cuda.synchronize()
+        g = guard.cpu().numpy()
+        assert np.all(g[cap:] == -5), f"layer {l}: entries past the S buffer were written"
+        sc = scores.cpu().numpy()
+        for b in range(B):
+            for h in range(Hq):
+                r = b * Hq + h
+                a, e = min(ind_h[r], cap), min(ind_h[r + 1], cap)
+                if not (mask >> h & 1):
+                    assert np.array_equal(g[a:e], S_before[a:e])
+                    continue
+                if e > a:
+                    want = orc.select_topk_f32(sc[b, h, :lens[b]], int(e - a))
+                    assert np.array_equal(g[a:e], want), (l, b, h)

@@ -171,3 +171,53 @@ def test_undersized_outputs_are_rejected_before_launch():
         ld.topk_select(x, 10, idx_out=torch.empty(29, dtype=torch.int32, device="cuda"))
     with pytest.raises(ValueError, match="val_out"):
         ld.topk_select(x, 10, val_out=torch.empty(29, dtype=torch.float32, device="cuda"))
+
+
+def _check_ragged(rows_np, n_r, k_r, *, csr, k_default, sentinel=-7):
+    """Rows of their own lengths n_r and budgets k_r (None: the default k), dense or CSR
+    output: every row equals the oracle on its first n_r scores with min(k_r, n_r)
+    indices (the pages' clamp), and entries past them keep the sentinel."""
+    ld = _ld()
+    rows, n = rows_np.shape
+    x = torch.as_tensor(np.ascontiguousarray(rows_np, dtype=np.float32), device="cuda")
+    nt = torch.as_tensor(np.asarray(n_r, dtype=np.int32), device="cuda")
+    kt = None if k_r is None else torch.as_tensor(np.asarray(k_r, dtype=np.int32), device="cuda")
+    want_k = [min(k_default if k_r is None else k_r[r], n_r[r]) for r in range(rows)]
+    if csr:
+        cap = [max(0, kk) + 3 for kk in want_k]            # room to spare: the tail stays
+        off = np.concatenate([[0], np.cumsum(cap)]).astype(np.int64)
+        ind = torch.as_tensor(off, device="cuda")
+        out = torch.full((int(off[-1]),), sentinel, dtype=torch.int32, device="cuda")
+        ld.topk_select(x, k_default, idx_out=out, n_per_row=nt, k_per_row=kt, idx_indptr=ind)
+        got = out.cpu().numpy()
+        rows_got = [got[off[r]:off[r + 1]] for r in range(rows)]
+    else:
+        out = torch.full((rows, k_default), sentinel, dtype=torch.int32, device="cuda")
+        ld.topk_select(x, k_default, idx_out=out, n_per_row=nt, k_per_row=kt)
+        rows_got = list(out.cpu().numpy())
+    for r in range(rows):
+        kk = max(0, min(want_k[r], len(rows_got[r])))
+        if kk >= 1:
+            want = orc.select_topk_f32(rows_np[r, :n_r[r]].astype(np.float32), kk)
+            assert np.array_equal(rows_got[r][:kk], want), f"row {r} (n {n_r[r]}, k {kk})"
+        assert np.all(rows_got[r][kk:] == sentinel), f"row {r}: entries past k_r were written"
+
+
+@pytest.mark.parametrize("n", [3000, 40000])
+def test_ragged_rows_with_their_own_k_dense_and_csr(n):
+    rng = _rng(n + 5)
+    rows = 9
+    x = rng.normal(size=(rows, n)).astype(np.float32)
+    n_r = [n, 1, n // 2, 777, n - 3, 64, 0, n // 3 + 1, 2]
+    k_r = [int(0.3 * v) for v in n_r]
+    k_r[1] = 5                                              # k above the row length: clamped to it
+    k_r[3] = 777
+    for csr in (False, True):
+        _check_ragged(x, n_r, k_r, csr=csr, k_default=max(k_r))
+        _check_ragged(x, n_r, None, csr=csr, k_default=n // 4)
+
+
+def test_k_above_n_is_clamped():
+    """k > n keeps every score (k = min(k, n), Token Sparse Attention skill page, Step 3)."""
+    x = _rng(3).normal(size=(2, 50)).astype(np.float32)
+    _check_ragged(x, [50, 50], None, csr=False, k_default=80)
