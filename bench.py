@@ -13,12 +13,13 @@ algorithmic bytes of a layer are
                             |union of the group's S rows|*2*d*2
   + Q and O (B*Hq*d*2 each) + S reads of sparse heads and S writes of retrieval
   heads (k_b*4 each).
-The roofline object is for the attention kernel (the dominant kernel; it also
-merges the splits and, for layers with one retrieval head per KV group, selects S):
-its algorithmic bytes (KV + Q + O) per launch over its average launch duration,
-timed with HIP events recorded between the layers of full steps on the launch stream.
-copy_gbs is a measured device-to-device copy (read + write bytes per second), reported
-as a practical second denominator beside the 8 TB/s figure.
+The roofline object is for the attention kernel (the dominant kernel; it also merges
+the splits and, unless a layer has too many retrieval rows, selects S): its algorithmic
+bytes (KV + Q + O) per launch over its average launch duration, timed with HIP events
+on the launch stream inside the timed steps, at the edges of the runs of layers whose
+call is that one launch (no events between those layers). copy_gbs (a device copy, read + write bytes per second) and
+read_gbs (a read-only reduction) are practical denominators beside the 8 TB/s figure.
+With the default 32K workload the 128K workload runs too and is reported under "also".
 """
 from __future__ import annotations
 
@@ -56,6 +57,9 @@ def parse():
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged KV: rows per page (power of two, 16..4096); 0 = contiguous")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--also", default="auto",
+                    help="further workloads (comma list) reported in the same line; auto = the 128K "
+                         "configuration with the default 32K run; none = no further workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-kernel-pass", action="store_true", help="omit the roofline object")
@@ -65,6 +69,9 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE counter files into the traffic summary")
     ap.add_argument("--counter-commands", default="", help="commands that produced the counter files")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="mean k_attention duration from a rocprofv3 kernel trace, over all dispatches "
+                         "and over those not followed by a selection launch (the bench's timed ones)")
     return ap.parse_args()
 
 
@@ -172,6 +179,28 @@ def copy_bandwidth(torch, reps=5):
     return 2.0 * COPY_BYTES / (ms * 1e-3) / 1e9
 
 
+READ_BYTES = 4 << 30
+
+
+def read_bandwidth(torch, reps=5):
+    """A read-only stream: the sum of READ_BYTES of fp64 zeros (a reduction that writes a
+    few bytes; the fastest of torch's reductions measured on this device), bytes read per
+    second (GB/s): a practical ceiling of a read-dominated kernel, beside the 8 TB/s."""
+    x = torch.zeros(READ_BYTES // 8, dtype=torch.float64, device="cuda")
+    for _ in range(2):
+        x.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del x
+    return READ_BYTES / (ms * 1e-3) / 1e9
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -184,14 +213,21 @@ def _cpu_model():
 
 
 def _counter_per_dispatch(csv_path, name_part, counter):
-    """Mean value per dispatch of `counter` over dispatches whose kernel name holds name_part."""
+    """Mean value per dispatch of `counter` over dispatches whose kernel name holds
+    name_part; for the attention kernel, only dispatches not followed by a selection
+    launch (the launches the bench's roofline times)."""
     import csv
-    vals = {}
+    vals, names = {}, {}
     with open(csv_path) as f:
         for r in csv.DictReader(f):
+            key = int(r["Dispatch_Id"])
+            names[key] = r["Kernel_Name"]
             if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
-                key = r["Dispatch_Id"]
                 vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    ids = sorted(names)
+    nxt = {a: names[b] for a, b in zip(ids, ids[1:])}
+    if name_part == "k_attention":
+        vals = {key: v for key, v in vals.items() if "k_sel" not in nxt.get(key, "")}
     return (sum(vals.values()) / len(vals), len(vals)) if vals else (None, 0)
 
 
@@ -228,8 +264,30 @@ def load_traffic(workload):
     return t["traffic_bytes_per_launch"] if t.get("source_sha256_16") == source_hash() else None
 
 
+def summarize_trace(path):
+    import csv
+    with open(path) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    alone, before_sel = [], []
+    for i, r in enumerate(rows):
+        if "k_attention" not in r["Kernel_Name"]:
+            continue
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        nxt = rows[i + 1]["Kernel_Name"] if i + 1 < len(rows) else ""
+        (before_sel if "k_sel" in nxt else alone).append(us)
+    out = {"kernel": "k_attention", "dispatches": len(alone) + len(before_sel),
+           "avg_us_all": round(float(np.mean(alone + before_sel)), 2) if alone or before_sel else None,
+           "dispatches_alone": len(alone), "avg_us_alone": round(float(np.mean(alone)), 2) if alone else None,
+           "dispatches_before_selection": len(before_sel),
+           "avg_us_before_selection": round(float(np.mean(before_sel)), 2) if before_sel else None}
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.summarize_counters:
         summarize_counters(args)
         return
@@ -251,7 +309,35 @@ def main():
     if args.workload in TSA_WORKLOADS:
         tsa_bench(args, torch, ld, dev)
         return
-    w = wl.get_workload(args.workload)
+    result = decode_bench(args, torch, ld, DecodeStep, wl, dev, args.workload, not args.no_cpu_baseline)
+    also = default_also(args) if args.also == "auto" else [x for x in args.also.split(",") if x and x != "none"]
+    if also:
+        # further workloads of the same metric, run after the first one (its inputs freed),
+        # with the same steps; only their headline figures are kept here
+        result["also"] = {}
+        for name in also:
+            r = decode_bench(args, torch, ld, DecodeStep, wl, dev, name, False)
+            result["also"][name] = {key: r[key] for key in ALSO_KEYS if key in r}
+    print(json.dumps(result), flush=True)
+
+
+# headline figures of the further workloads in the one JSON line
+ALSO_KEYS = ("value", "unit", "ms_per_step", "us_per_layer", "pct_of_hbm_peak", "pct_of_read",
+             "us_layer0", "us_layers_with_retrieval", "us_layers_sparse_only", "algorithmic_bytes_per_step",
+             "roofline", "config")
+
+
+def default_also(args):
+    """The 128K configuration of the same metric rides along with the default 32K run
+    (plain launch shape, bf16 contiguous KV, token selection)."""
+    plain = (args.kv == "bf16" and not args.page_size and not args.block_select and not args.swa_window
+             and not args.split and not args.waves)
+    return ["qwen3_8b_128k"] if args.workload == "llama3_8b_32k" and plain else []
+
+
+def decode_bench(args, torch, ld, DecodeStep, wl, dev, name, cpu_leg):
+    """Time one decode-step workload; returns its result object."""
+    w = wl.get_workload(name)
     L, d = w.layers, w.head_dim
     log(f"[bench] workload {w.name}: B={w.batch} L={L} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
         f"d={d} N={w.seq_lens if w.batch > 1 else w.seq_lens[0]} k={w.k_per_seq if w.batch > 1 else w.k_per_seq[0]}")
@@ -334,18 +420,52 @@ def main():
     step_bytes = float(sum(total_bytes))
     log(f"[bench] algorithmic bytes/step {step_bytes / 1e9:.3f} GB")
 
+    # ---- which layer calls are exactly one attention launch (merge and selection inside
+    # it): the roofline times those launches inside the timed steps
+    plans = []
+    for l in range(L):
+        q, kc, vc = inputs[l][:3]
+        win = windows[l] if windows else None
+        extra = {"block_table": inputs[l][3], "page_size": inputs[l][4]} if len(inputs[l]) > 3 else {}
+        plans.append(step.plan(l, q, kc, vc, window=win, **extra))
+    single = [l for l in range(L) if plans[l] is not None and plans[l]["launches"] == 1]
+    # runs [a, b) of consecutive single-launch layers: an event before a and one before b
+    runs, l = [], 0
+    while l < L:
+        if l in single:
+            a = l
+            while l < L and l in single:
+                l += 1
+            runs.append((a, l))
+        else:
+            l += 1
+
     # ---- warmup + timed steps (events between steps, on the launch stream)
     for _ in range(args.warmup):
         step.run(inputs, windows=windows)
     torch.cuda.synchronize()
     sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # per step, events at the edges of the single-launch runs (none between their layers;
+    # an edge at layer 0 or L reuses the step events)
+    rev = []
+    for i in range(args.steps):
+        ev = [None] * (L + 1)
+        for a, b in runs:
+            for e in (a, b):
+                if e not in (0, L) and ev[e] is None:
+                    ev[e] = torch.cuda.Event(enable_timing=True)
+        rev.append(ev)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     sev[0].record()
     for i in range(args.steps):
-        step.run(inputs, windows=windows)
+        step.run(inputs, windows=windows, events=rev[i])
         sev[i + 1].record()
     torch.cuda.synchronize()
+
+    def edge(i, e):
+        return sev[i] if e == 0 else (sev[i + 1] if e == L else rev[i][e])
+    single_ms = sum(edge(i, a).elapsed_time(edge(i, b)) for i in range(args.steps) for a, b in runs)
     wall = time.perf_counter() - wall0
     per_step = np.array([sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps)])
     ms_step = sev[0].elapsed_time(sev[-1]) / args.steps
@@ -406,18 +526,14 @@ def main():
             log(f"  layer {l:2d} mask={w.retrieval_masks[l]:#x} {per_layer[l]:8.1f} us "
                 f"{total_bytes[l] / per_layer[l] / 1e3:8.1f} GB/s")
 
-    # ---- roofline of the attention launch. Each layer call is one attention launch
-    # (merge and selection inside it), except layers with several retrieval heads in one
-    # KV group, which add a selection launch. The launch duration is the timed steps'
-    # mean (HIP events around every step on the launch stream) over the step's L
-    # attention launches: the step also holds those selection launches and the gaps
-    # between launches, so the figure is a lower bound of the kernel's rate. (The
-    # per-layer spans above carry the cost of an event between every two layers, a few
-    # us each, and are reported for the layer mix only.)
+    # ---- roofline of the attention launch: the layers whose call is that one launch run
+    # back to back inside the timed steps, bracketed by the events above, so their mean
+    # span is the launch's duration as the device runs it in a step (the next launch's
+    # dispatch overlaps the previous one's end)
     roof = None
-    if not args.no_kernel_pass:
-        avg_us = ms_step * 1e3 / L
-        avg_bytes = float(np.mean(attn_bytes))
+    if not args.no_kernel_pass and single:
+        avg_us = single_ms * 1e3 / (args.steps * len(single))
+        avg_bytes = float(np.mean([attn_bytes[l] for l in single]))
         achieved = avg_bytes / (avg_us * 1e-6) / 1e9
         # the counters are taken on the default configuration (bf16 contiguous KV, token
         # selection, automatic launch shape); other configurations report none
@@ -428,9 +544,11 @@ def main():
                 "traffic": load_traffic(w.name) if default_cfg else None,
                 "kernel": f"k_attention (d={d}, G={w.group_size}, {'E4M3' if args.kv == 'fp8' else 'bf16'} KV)",
                 "avg_launch_us": round(avg_us, 2), "avg_bytes_per_launch": int(avg_bytes),
-                "launches_timed": L * args.steps}
-        log(f"[bench] attention launch: avg {avg_us:.1f} us, {achieved:.0f} GB/s "
-            f"({achieved / HBM_PEAK_GBS * 100:.1f}% of peak)")
+                "launches_timed": len(single) * args.steps,
+                "layers_timed": f"{len(single)} of {L} (calls that are one attention launch)",
+                "timing": "HIP events on the launch stream at the edges of those layers inside the timed steps"}
+        log(f"[bench] attention launch: avg {avg_us:.2f} us over {len(single)} layers x {args.steps} steps, "
+            f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS * 100:.1f}% of peak)")
 
     value = step_bytes / (ms_step * 1e-3) / 1e9
     wait_ok = True
@@ -440,7 +558,8 @@ def main():
         wait_ok = False
         log(f"[bench] {e}")
     copy_gbs = copy_bandwidth(torch)
-    log(f"[bench] device copy: {copy_gbs:.0f} GB/s (read + write)")
+    read_gbs = read_bandwidth(torch)
+    log(f"[bench] device copy: {copy_gbs:.0f} GB/s (read + write); read-only reduction: {read_gbs:.0f} GB/s")
     nonzero = [l for l in range(1, L) if w.retrieval_masks[l]]
     zero = [l for l in range(1, L) if not w.retrieval_masks[l]]
     result = {
@@ -457,6 +576,8 @@ def main():
         "pct_of_hbm_peak": round(value / HBM_PEAK_GBS * 100, 2),
         "copy_gbs": round(copy_gbs, 1),
         "pct_of_copy": round(value / copy_gbs * 100, 2),
+        "read_gbs": round(read_gbs, 1),
+        "pct_of_read": round(value / read_gbs * 100, 2),
         "us_layer0": round(float(per_layer[0]), 2),
         "us_layers_with_retrieval": round(float(np.mean(per_layer[nonzero])), 2) if nonzero else None,
         "us_layers_sparse_only": round(float(np.mean(per_layer[zero])), 2) if zero else None,
@@ -485,12 +606,14 @@ def main():
     }
 
     # ---- CPU oracle baseline on a bounded sample of the same workload
-    if W and not args.no_cpu_baseline:
+    if W and cpu_leg:
         log("[bench] no CPU baseline with --swa-window (the oracle leg times the plain layers)")
-    elif not args.no_cpu_baseline:
+    elif cpu_leg:
         oracle_inputs = logical if args.kv == "bf16" else q8
-        result["cpu_baseline"] = cpu_baseline(w, oracle_inputs, total_bytes, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, oracle_inputs, total_bytes, args.cpu_seconds, ms_step)
+    del inputs, logical, step
+    torch.cuda.empty_cache()
+    return result
 
 
 # Token Sparse Attention over a prefill (the page's budget range of 512-1024 kept tokens
@@ -596,7 +719,7 @@ def tsa_cpu_baseline(q, kc, vc, scores, k, causal, us_layer, target_s):
     Hkv = kc.shape[0]
     G = Hq // Hkv
     B, _, T = scores.shape
-    spent, heads = 0.0, 0
+    spent, cpu, heads = 0.0, 0.0, 0
     while spent < target_s:      # passes over the heads until about target_s of CPU work
         for h in range(Hq):
             g = h // G
@@ -604,23 +727,27 @@ def tsa_cpu_baseline(q, kc, vc, scores, k, causal, us_layer, target_s):
             kh = orc.bf16_bits_to_f64(wl.bf16_bits(kc[g:g + 1, :T]))
             vh = orc.bf16_bits_to_f64(wl.bf16_bits(vc[g:g + 1, :T]))
             sh = scores[0:1, h:h + 1].cpu().numpy()
-            t0 = time.perf_counter()
+            t0, c0 = time.perf_counter(), time.process_time()
             orc.tsa_attention(qh, kh, vh, sh, k, causal=causal, zero_fill=False)
             spent += time.perf_counter() - t0
+            cpu += time.process_time() - c0
             heads += 1
             log(f"[bench] oracle head {h}: cumulative {spent:.1f}s")
             if spent >= target_s:
                 break
     per_layer_us = spent / heads * (B * Hq) * 1e6
-    return {"value": round(per_layer_us, 1), "unit": "us", "cores": int(threads), "kind": "oracle",
+    return {"value": round(per_layer_us, 1), "unit": "us", "cores": round(cpu / spent, 1),
+            "threads_available": int(threads), "kind": "oracle",
             "cpu_model": _cpu_model(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": f"{heads} head evaluations (sequence 0; {heads / (B * Hq):.2f} layers of {B * Hq} heads), "
                       f"fp64 NumPy oracle, {spent:.1f} s, scaled to one layer"}
 
 
-def cpu_baseline(w, inputs, total_bytes, target_s):
+def cpu_baseline(w, inputs, total_bytes, target_s, gpu_ms_step):
     """Time the fp64 oracle (as it stands) on the first layers of the step until about
-    target_s seconds of CPU work; report GB/s of algorithmic bytes processed."""
+    target_s seconds of CPU work; report GB/s of algorithmic bytes processed, the
+    oracle's ms per layer and per step (scaled from the sample's layer mix), and the
+    cores it kept busy (process CPU time over wall time)."""
     from oracle import lychee_oracle as orc
     import workloads as wl
     import torch
@@ -630,7 +757,8 @@ def cpu_baseline(w, inputs, total_bytes, target_s):
     except Exception:  # pragma: no cover
         threads = 1
     offs = w.kv_offsets()
-    spent, done, nbytes = 0.0, 0, 0
+    spent, cpu, done, nbytes = 0.0, 0.0, 0, 0
+    per_layer = {}
     # whole steps (layer 0 restarts the recurrence) until about target_s of CPU work
     while spent < target_s:
         S = None
@@ -639,23 +767,38 @@ def cpu_baseline(w, inputs, total_bytes, target_s):
             ret = [bool(w.retrieval_masks[l] >> h & 1) for h in range(w.num_q_heads)]
             if kc.dtype == torch.uint8:
                 k8, v8 = kc.cpu().numpy(), vc.cpu().numpy()
-                t0 = time.perf_counter()
+                t0, c0 = time.perf_counter(), time.process_time()
                 _, S, _ = orc.hybrid_layer_fp8(wl.bf16_bits(q), k8, v8, 1.0, 1.0, offs, ret, w.k_per_seq, S)
             else:
                 qb, kb_, vb = wl.bf16_bits(q), wl.bf16_bits(kc), wl.bf16_bits(vc)
-                t0 = time.perf_counter()
+                t0, c0 = time.perf_counter(), time.process_time()
                 _, S, _ = orc.hybrid_layer_bf16(qb, kb_, vb, offs, ret, w.k_per_seq, S)
-            spent += time.perf_counter() - t0
+            dt = time.perf_counter() - t0
+            cpu += time.process_time() - c0
+            spent += dt
+            per_layer.setdefault(l, []).append(dt)
             done += 1
             nbytes += total_bytes[l]
             log(f"[bench] oracle layer {l}: cumulative {spent:.1f}s")
             if spent >= target_s:
                 break
-    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "cpu_model": _cpu_model(),
+    # a step's time: measured layers as measured; the others as the mean of the measured
+    # layers of their kind (layer 0, layers with retrieval heads, sparse-only layers)
+    kind = lambda l: 0 if l == 0 else (1 if w.retrieval_masks[l] else 2)
+    mean_of = {}
+    for l, ts in per_layer.items():
+        mean_of.setdefault(kind(l), []).append(float(np.mean(ts)))
+    fallback = float(np.mean([t for v in mean_of.values() for t in v]))
+    step_s = sum(float(np.mean(per_layer[l])) if l in per_layer
+                 else float(np.mean(mean_of.get(kind(l), [fallback]))) for l in range(w.layers))
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": round(cpu / spent, 1),
+            "threads_available": int(threads), "kind": "oracle", "cpu_model": _cpu_model(),
             "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "ms_per_layer": round(spent / done * 1e3, 1), "ms_per_step": round(step_s * 1e3, 1),
+            "gpu_speedup_per_step": round(step_s * 1e3 / gpu_ms_step, 1),
             "sample": f"{done} layer evaluations ({done / w.layers:.2f} steps of {w.layers} layers) of {w.name} "
-                      f"({nbytes / 1e9:.2f} GB algorithmic), fp64 NumPy oracle, {spent:.1f} s"}
+                      f"({nbytes / 1e9:.2f} GB algorithmic), fp64 NumPy oracle, {spent:.1f} s wall, "
+                      f"{cpu:.1f} s CPU; ms_per_step adds unmeasured layers at the mean of their kind"}
 
 
 if __name__ == "__main__":

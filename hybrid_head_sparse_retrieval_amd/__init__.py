@@ -8,6 +8,7 @@ below without it raises ``LycheeDecodeUnavailable`` -- there is no fallback path
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import math
 import os
@@ -19,7 +20,7 @@ __all__ = [
     "retrieval_decode", "sparse_decode", "hybrid_layer", "topk_select",
     "hysparse_workspace_bytes", "HySparseWorkspace", "hysparse_layer",
     "tsa_workspace_bytes", "TsaWorkspace", "tsa_attention", "TSA_CAUSAL", "TSA_ZERO_FILL", "TSA_GIVEN_IDX",
-    "hybrid_layer_noalloc", "NOALLOC_SCRATCH_BYTES", "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "FLAG_SEPARATE_SELECT", "FLAG_BLOCK_SELECT", "flag_split_rows", "flag_waves", "EXPORTED_SYMBOLS",
+    "hybrid_layer_noalloc", "hybrid_layer_plan", "LayerPlan", "NOALLOC_SCRATCH_BYTES", "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "FLAG_SEPARATE_SELECT", "FLAG_BLOCK_SELECT", "flag_split_rows", "flag_waves", "EXPORTED_SYMBOLS",
 ]
 
 LD_OK = 0
@@ -38,7 +39,8 @@ EXPORTED_SYMBOLS = ("ld_status_string", "ld_workspace_size", "ld_topk_workspace_
                     "ld_workspace_init", "ld_workspace_check", "ld_retrieval_decode",
                     "ld_sparse_decode", "ld_hybrid_layer", "ld_topk_select",
                     "ld_hysparse_workspace_size", "ld_hysparse_layer",
-                    "ld_tsa_workspace_size", "ld_tsa_attention", "ld_hybrid_layer_noalloc")
+                    "ld_tsa_workspace_size", "ld_tsa_attention", "ld_hybrid_layer_noalloc",
+                    "ld_hybrid_layer_plan")
 
 
 def flag_split_rows(v: int) -> int:
@@ -124,6 +126,8 @@ def load_library():
     lib.ld_sparse_decode.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, u32, vp, sz, vp]
     lib.ld_hybrid_layer.restype = i32
     lib.ld_hybrid_layer.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, vp, vp, u32, vp, sz, vp]
+    lib.ld_hybrid_layer_plan.restype = i32
+    lib.ld_hybrid_layer_plan.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, vp, vp, u32, vp]
     lib.ld_hybrid_layer_noalloc.restype = i32
     lib.ld_hybrid_layer_noalloc.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, vp, vp, u32, vp]
     lib.ld_hysparse_workspace_size.restype = sz
@@ -227,6 +231,38 @@ class _WS:
         last check (then those calls' results are unreliable); clears the flag.
         Synchronises the current stream."""
         _check(load_library().ld_workspace_check(self.ptr(), self.nbytes, _stream()), "ld_workspace_check")
+
+
+# Workspaces the binding keeps for calls that pass none: one per (entry point, device,
+# stream, sizes that fix the workspace layout), reused by the later calls on the same
+# stream, which are ordered after the earlier ones; the least recently used beyond
+# _WS_CACHE_MAX are released (the allocator reuses their memory in stream order).
+_WS_CACHE: "collections.OrderedDict" = collections.OrderedDict()
+_WS_CACHE_MAX = 8
+
+
+def _default_ws(kind: str, key: tuple, make, device):
+    torch = _torch()
+    dev = torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    full = (kind, idx, _stream(), key)
+    ws = _WS_CACHE.get(full)
+    if ws is None:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(f"{kind}: pass a workspace to calls under graph capture (its first "
+                               "use on a stream allocates and clears one)")
+        ws = make()
+        _WS_CACHE[full] = ws
+        while len(_WS_CACHE) > _WS_CACHE_MAX:
+            _WS_CACHE.popitem(last=False)
+    else:
+        _WS_CACHE.move_to_end(full)
+    return ws
+
+
+def _layout_key(shape, *extra) -> tuple:
+    return (shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.seq_len,
+            shape.page_size, shape.total_tokens, shape.kv_dtype) + tuple(int(x) for x in extra)
 
 
 class Workspace(_WS):
@@ -364,7 +400,7 @@ def retrieval_decode(q, k_cache, v_cache, head_mask: int, k: int, *, s_out=None,
     _opt(scores_out, torch.float32, "scores_out")
     k = _clamp_k(shape, k, s_indptr, [("s_out", s_out)])
     _sizes(shape, q, out, k, kv_indptr, [("s_out", s_out)], s_indptr, scores_out)
-    ws = workspace or Workspace(shape, k, q.device)
+    ws = workspace or _default_ws("layer", _layout_key(shape, k), lambda: Workspace(shape, k, q.device), q.device)
     _check(load_library().ld_retrieval_decode(
         ctypes.byref(shape), int(head_mask), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         int(k), _ptr(s_out), _ptr(s_indptr), _ptr(scores_out), out.data_ptr(), ws.ptr(), ws.nbytes,
@@ -383,7 +419,7 @@ def sparse_decode(q, k_cache, v_cache, head_mask: int, k: int, s_in, *, s_indptr
     _req(s_in, torch.int32, "s_in"); _opt(s_indptr, torch.int64, "s_indptr")
     k = _clamp_k(shape, k, s_indptr, [("s_in", s_in)])
     _sizes(shape, q, out, k, kv_indptr, [("s_in", s_in)], s_indptr)
-    ws = workspace or Workspace(shape, k, q.device)
+    ws = workspace or _default_ws("layer", _layout_key(shape, k), lambda: Workspace(shape, k, q.device), q.device)
     _check(load_library().ld_sparse_decode(
         ctypes.byref(shape), int(head_mask), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         int(k), s_in.data_ptr(), _ptr(s_indptr), out.data_ptr(), int(flags), ws.ptr(), ws.nbytes,
@@ -406,12 +442,46 @@ def hybrid_layer(q, k_cache, v_cache, retrieval_mask: int, k: int, s, *, s_out=N
         s_out = s
     k = _clamp_k(shape, k, s_indptr, [("s", s), ("s_out", s_out)])
     _sizes(shape, q, out, k, kv_indptr, [("s", s), ("s_out", s_out)], s_indptr, scores_out)
-    ws = workspace or Workspace(shape, k, q.device)
+    ws = workspace or _default_ws("layer", _layout_key(shape, k), lambda: Workspace(shape, k, q.device), q.device)
     _check(load_library().ld_hybrid_layer(
         ctypes.byref(shape), int(retrieval_mask), q.data_ptr(), k_cache.data_ptr(),
         v_cache.data_ptr(), int(k), _ptr(s), _ptr(s_out), _ptr(s_indptr), _ptr(scores_out),
         out.data_ptr(), int(flags), ws.ptr(), ws.nbytes, _stream()), "ld_hybrid_layer")
     return out
+
+
+class LayerPlan(ctypes.Structure):
+    """ld_layer_plan: the launches of one ld_hybrid_layer call."""
+    _fields_ = [("launches", ctypes.c_int32), ("attention_workgroups", ctypes.c_int32),
+                ("split_rows_stream", ctypes.c_int32), ("split_rows_gather", ctypes.c_int32),
+                ("waves", ctypes.c_int32), ("select_in_launch", ctypes.c_int32),
+                ("selector_parts", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {name: int(getattr(self, name)) for name, _ in self._fields_ if name != "reserved"}
+
+
+def hybrid_layer_plan(q, k_cache, v_cache, retrieval_mask: int, k: int, s, *, s_out=None,
+                      s_indptr=None, scores_out=None, out=None, flags: int = 0, kv_indptr=None,
+                      seq_len=None, scale=None, block_table=None, page_size: int = 0, k_scale=None,
+                      v_scale=None) -> dict:
+    """What hybrid_layer would launch for the same arguments (nothing is launched):
+    kernel count, attention grid, split rows, waves, and whether S is selected inside
+    the attention launch."""
+    torch = _torch()
+    _opt(s, torch.int32, "s"); _opt(s_out, torch.int32, "s_out")
+    _opt(s_indptr, torch.int64, "s_indptr"); _opt(scores_out, torch.float32, "scores_out")
+    shape = make_shape(q, k_cache, kv_indptr, seq_len, scale, block_table, page_size, k_scale, v_scale)
+    if s_out is None:
+        s_out = s
+    k = _clamp_k(shape, k, s_indptr, [("s", s), ("s_out", s_out)])
+    out_ptr = out.data_ptr() if out is not None else q.data_ptr()
+    plan = LayerPlan()
+    _check(load_library().ld_hybrid_layer_plan(
+        ctypes.byref(shape), int(retrieval_mask), q.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), int(k), _ptr(s), _ptr(s_out), _ptr(s_indptr), _ptr(scores_out),
+        out_ptr, int(flags), ctypes.byref(plan)), "ld_hybrid_layer_plan")
+    return plan.as_dict()
 
 
 def hybrid_layer_noalloc(q, k_cache, v_cache, retrieval_mask: int, k: int, s, *, out, s_out=None,
@@ -459,7 +529,8 @@ def hysparse_layer(q, k_cache, v_cache, k: int, s_in, k_window, v_window, gate, 
     k = _clamp_k(shape, k, s_indptr, [("s_in", s_in)])
     _sizes(shape, q, out, k, kv_indptr, [("s_in", s_in)], s_indptr)
     W = k_window.shape[1] // B
-    ws = workspace or HySparseWorkspace(shape, k, W, q.device)
+    ws = workspace or _default_ws("hysparse", _layout_key(shape, k, W),
+                                  lambda: HySparseWorkspace(shape, k, W, q.device), q.device)
     _check(load_library().ld_hysparse_layer(
         ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), int(k),
         s_in.data_ptr(), _ptr(s_indptr), k_window.data_ptr(), v_window.data_ptr(), int(W),
@@ -507,7 +578,7 @@ def tsa_attention(q, k_cache, v_cache, scores, k: int, *, idx_out=None, out=None
     if out.shape != q.shape:
         raise ValueError("out must have the shape of q")
     flags = (TSA_CAUSAL if causal else 0) | (TSA_ZERO_FILL if zero_fill else 0) | (TSA_GIVEN_IDX if given_idx else 0)
-    ws = workspace or TsaWorkspace(shape, k, q.device)
+    ws = workspace or _default_ws("tsa", _layout_key(shape, k), lambda: TsaWorkspace(shape, k, q.device), q.device)
     _check(load_library().ld_tsa_attention(
         ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), _ptr(scores), int(k),
         idx_out.data_ptr(), out.data_ptr(), int(flags), ws.ptr(), ws.nbytes, _stream()), "ld_tsa_attention")
@@ -562,7 +633,7 @@ def topk_select(scores, k: int, *, idx_out=None, val_out=None, n_per_row=None, k
     for name, t in (("idx_out", idx_out), ("val_out", val_out)):
         if t is not None and t.numel() < cap:
             raise ValueError(f"{name} must hold {cap} entries")
-    ws = workspace or TopkWorkspace(rows, n, scores.device)
+    ws = workspace or _default_ws("topk", (rows, n), lambda: TopkWorkspace(rows, n, scores.device), scores.device)
     _check(load_library().ld_topk_select(
         scores.data_ptr(), int(rows), int(n), int(row_stride), _ptr(n_per_row), int(k), _ptr(k_per_row),
         idx_out.data_ptr(), _ptr(idx_indptr), _ptr(val_out), ws.ptr(), ws.nbytes, _stream()), "ld_topk_select")

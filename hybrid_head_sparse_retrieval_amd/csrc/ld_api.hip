@@ -75,7 +75,7 @@ SelArrays sel_arrays(int rows, int n, Take take) {
 }
 
 template <typename T>
-T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(ws) + off); }
 
 // Scores per workgroup of the standalone digit-1 histogram: 512, doubled while the
 // grid would exceed about 256 workgroups (long rows), at most 16384, so that each
@@ -297,7 +297,16 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
                     const void* kc, const void* vc, int32_t k, const int32_t* s_in,
                     int32_t* s_out, const int64_t* s_indptr, float* scores_out, void* out,
                     uint32_t flags, bool want_topk, void* ws, size_t ws_bytes, hipStream_t st,
-                    const float* gate = nullptr, const float* o_win = nullptr, bool clear_ctrl = false) {
+                    const float* gate = nullptr, const float* o_win = nullptr, bool clear_ctrl = false,
+                    ld_layer_plan* plan = nullptr) {
+  // plan != null: validate and decide as for a launch, count the kernels instead of
+  // launching them, and describe the attention launch in *plan
+  if (plan) *plan = ld_layer_plan{};
+#define LD_LAUNCH(expr, count)                                  \
+  do {                                                          \
+    if (plan) plan->launches += (count);                        \
+    else if ((expr) != hipSuccess) return LD_ERR_HIP;           \
+  } while (0)
   ld_status why;
   if (!shape_ok(shape, &why)) return why;
   const int B = shape->batch, Hq = shape->num_q_heads, Hkv = shape->num_kv_heads;
@@ -318,7 +327,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   if ((s_in && ((uintptr_t)s_in & 3u)) || (s_out && ((uintptr_t)s_out & 3u))) return LD_ERR_INVALID_ARGUMENT;
   if (scores_out && ((uintptr_t)scores_out & 3u)) return LD_ERR_INVALID_ARGUMENT;
   const LayerLayout L = layer_layout(shape);
-  if (!ws || ws_bytes < L.total || ((uintptr_t)ws & 15u)) return LD_ERR_WORKSPACE;
+  if (!plan && (!ws || ws_bytes < L.total || ((uintptr_t)ws & 15u))) return LD_ERR_WORKSPACE;
   if (active == 0) return LD_OK;
 
   int64_t T = shape->total_tokens;
@@ -336,8 +345,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
 
   // 0. a buffer that other shapes' calls may have used: its counters, histograms and
   // release words start from zero (a fill kernel, so the call stays capturable)
-  if (clear_ctrl && launch_zero(at<char>(ws, kHeaderBytes), L.ctrl_end - kHeaderBytes, st) != hipSuccess)
-    return LD_ERR_HIP;
+  if (clear_ctrl) LD_LAUNCH(launch_zero(at<char>(ws, kHeaderBytes), L.ctrl_end - kHeaderBytes, st), 1);
 
   // 1. membership bitmaps of the sparse heads (unless the caller chains them)
   if (nsp && !(flags & LD_FLAG_S_CHAINED)) {
@@ -348,7 +356,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     std::memcpy(bp.heads, sp_heads, sizeof(sp_heads));
     bp.bitmaps = bitmaps; bp.W = L.W;
     bp.wblocks = (L.W + kBitmapWordsPerBlock - 1) / kBitmapWordsPerBlock;
-    if (launch_bitmap_build(bp, B * nsp, st) != hipSuccess) return LD_ERR_HIP;
+    LD_LAUNCH(launch_bitmap_build(bp, B * nsp, st), 1);
   }
   // 2. S^{l+1} = S^{l} for sparse heads when the output buffer is a different one
   if (nsp && s_out && s_out != s_in) {
@@ -356,7 +364,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     cp.src = s_in; cp.dst = s_out; cp.s_indptr = s_indptr; cp.k_dense = k; cp.s_cap = s_cap;
     cp.Hq = Hq; cp.nsp = nsp;
     std::memcpy(cp.heads, sp_heads, sizeof(sp_heads));
-    if (launch_copy_rows(cp, B * nsp, st) != hipSuccess) return LD_ERR_HIP;
+    LD_LAUNCH(launch_copy_rows(cp, B * nsp, st), 1);
   }
   // 3. attention (+ fused first selection digit)
   AttnParams ap{};
@@ -469,7 +477,15 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   ap.sel_pub = at<uint64_t>(ws, L.sel_pub);
   ap.err = at<uint32_t>(ws, L.sel.err);
   const int64_t nwg = (int64_t)B * ((int64_t)ng_dense * ap.nsplit_d + (int64_t)(ng - ng_dense) * ap.nsplit_s);
-  if (launch_attention(ap, D, G, dim3((unsigned)nwg), st) != hipSuccess) return LD_ERR_HIP;
+  if (plan) {
+    plan->attention_workgroups = (int32_t)nwg;
+    plan->split_rows_stream = ng_dense ? ap.ts_d : 0;
+    plan->split_rows_gather = ng > ng_dense ? ap.ts_s : 0;
+    plan->waves = ap.waves;
+    plan->select_in_launch = in_select && nret > 0 ? 1 : 0;
+    plan->selector_parts = plan->select_in_launch ? ap.sel_parts : 0;
+  }
+  LD_LAUNCH(launch_attention(ap, D, G, dim3((unsigned)nwg), st), 1);
 
   // 4. argsTopK of the retrieval rows: by token blocks (block maxima, then the same
   // radix select over the block scores, then the kept blocks' tokens), or by tokens
@@ -483,7 +499,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     bk.bitmaps = bitmaps; bk.W = L.W;
     bk.Hq = Hq; bk.nret = nret;
     std::memcpy(bk.heads, ret_heads, sizeof(ret_heads));
-    if (launch_block_max(bk, bk.rows, st) != hipSuccess) return LD_ERR_HIP;
+    LD_LAUNCH(launch_block_max(bk, bk.rows, st), 1);
     SelParams sp{};
     sp.mode = 0;
     sp.nrows = bk.rows;
@@ -492,8 +508,8 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     sp.idx_out = at<int32_t>(ws, L.blk_idx); sp.val_out = nullptr;
     fill_sel(sp, L.sel, ws);
     sp.C = (bk.nblk + kSelSpan - 1) / kSelSpan;    // spans of this row length
-    if (launch_select(sp, st, true) != hipSuccess) return LD_ERR_HIP;
-    if (launch_block_expand(bk, bk.rows, st) != hipSuccess) return LD_ERR_HIP;
+    LD_LAUNCH(launch_select(sp, st, true), select_launches(sp, true));
+    LD_LAUNCH(launch_block_expand(bk, bk.rows, st), 1);
   } else if (do_topk && !in_select) {
     SelParams sp{};
     sp.mode = 1;
@@ -504,9 +520,10 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     sp.nret = nret;
     std::memcpy(sp.heads, ret_heads, sizeof(ret_heads));
     fill_sel(sp, L.sel, ws);
-    if (launch_select(sp, st, false) != hipSuccess) return LD_ERR_HIP;
+    LD_LAUNCH(launch_select(sp, st, false), select_launches(sp, false));
   }
   return LD_OK;
+#undef LD_LAUNCH
 }
 
 }  // namespace
@@ -744,6 +761,21 @@ ld_status ld_hybrid_layer(const ld_shape* shape, uint64_t retrieval_mask, const 
   return run_layer(shape, all, retrieval_mask, q, k_cache, v_cache, k, s_in, s_out, s_indptr,
                    scores_out, out, flags, !(flags & LD_FLAG_SKIP_TOPK), workspace,
                    workspace_bytes, stream);
+}
+
+ld_status ld_hybrid_layer_plan(const ld_shape* shape, uint64_t retrieval_mask, const void* q,
+                               const void* k_cache, const void* v_cache, int32_t k,
+                               const int32_t* s_in, int32_t* s_out, const int64_t* s_indptr,
+                               float* scores_out, void* out, uint32_t flags, ld_layer_plan* plan) {
+  if (!plan) return LD_ERR_INVALID_ARGUMENT;
+  ld_status why;
+  if (!shape_ok(shape, &why)) return why;
+  const int Hq = shape->num_q_heads;
+  const uint64_t all = (Hq == 64) ? ~0ull : ((1ull << Hq) - 1ull);
+  if (retrieval_mask & ~all) return LD_ERR_INVALID_ARGUMENT;
+  return run_layer(shape, all, retrieval_mask, q, k_cache, v_cache, k, s_in, s_out, s_indptr,
+                   scores_out, out, flags, !(flags & LD_FLAG_SKIP_TOPK), nullptr, 0, nullptr,
+                   nullptr, nullptr, false, plan);
 }
 
 ld_status ld_topk_select(const float* scores, int32_t rows, int32_t n, int64_t row_stride,

@@ -167,6 +167,8 @@ int64_t attention_capacity(int D, int G, int waves, bool fp8);   // workgroups r
 template <int G> int64_t attention_capacity_g(int D, int waves, bool fp8);
 template <int G> hipError_t launch_attention_g(const AttnParams& p, int D, dim3 grid, hipStream_t st);
 hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist);
+// kernels launch_select launches for p (1 to 3)
+int select_launches(const SelParams& p, bool with_hist);
 hipError_t launch_bitmap_build(const BitmapParams& p, int rows, hipStream_t st);
 hipError_t launch_copy_rows(const CopyParams& p, int rows, hipStream_t st);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t st);

@@ -802,6 +802,12 @@ int64_t fused_capacity() {
   return c;
 }
 
+int select_launches(const SelParams& p, bool with_hist) {
+  if (with_hist && p.mode == 0 && p.n <= kSmallRow) return 1;
+  const int fused = (int64_t)p.nrows * p.C <= fused_capacity() ? 1 : 2;
+  return (with_hist ? 1 : 0) + fused;
+}
+
 hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist) {
   if (with_hist && p.mode == 0 && p.n <= kSmallRow) {
     hipLaunchKernelGGL(k_sel_small, dim3((unsigned)p.nrows), dim3(kSmallThreads), 0, st, p);

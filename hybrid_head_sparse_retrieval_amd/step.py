@@ -15,8 +15,8 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (FLAG_S_CHAINED, HySparseWorkspace, Workspace, hybrid_layer, hysparse_layer,
-               make_shape)
+from . import (FLAG_S_CHAINED, HySparseWorkspace, Workspace, hybrid_layer, hybrid_layer_plan,
+               hysparse_layer, make_shape)
 
 
 class DecodeStep:
@@ -90,13 +90,25 @@ class DecodeStep:
                             kv_indptr=self.kv_indptr, seq_len=self.N, block_table=block_table,
                             page_size=page_size)
 
+    def plan(self, l: int, q, kc, vc, extra_flags: int = 0, block_table=None, page_size: int = 0,
+             window=None) -> Optional[dict]:
+        """The launches layer(l, ...) makes with the same arguments (see hybrid_layer_plan);
+        None for a window layer, which has its own entry point."""
+        if window is not None:
+            return None
+        flags = (FLAG_S_CHAINED if l > 0 else 0) | self.split_flag | extra_flags
+        return hybrid_layer_plan(q, kc, vc, self.masks[l], self.k_arg, self.S if l > 0 else None,
+                                 s_out=self.S, s_indptr=self.s_indptr, out=self.outs[l], flags=flags,
+                                 kv_indptr=self.kv_indptr, seq_len=self.N, block_table=block_table,
+                                 page_size=page_size)
+
     def run(self, layers: List, events: Optional[list] = None, windows: Optional[list] = None):
         """One decode step. layers[l] = (q, k, v) device tensors, or (q, k_pool, v_pool,
         block_table, page_size) for paged KV. windows[l]: (k_window, v_window, gate) or
-        None per layer. If `events` is a list of L+1 torch.cuda.Event, they are
-        recorded between layers."""
+        None per layer. If `events` is a list of L+1 torch.cuda.Event (or None entries),
+        events[l] is recorded right before layer l and events[L] after the last layer."""
         for l in range(self.L):
-            if events is not None:
+            if events is not None and events[l] is not None:
                 events[l].record()
             q, kc, vc = layers[l][:3]
             win = windows[l] if windows is not None else None
@@ -104,7 +116,7 @@ class DecodeStep:
                 self.layer(l, q, kc, vc, block_table=layers[l][3], page_size=layers[l][4], window=win)
             else:
                 self.layer(l, q, kc, vc, window=win)
-        if events is not None:
+        if events is not None and events[self.L] is not None:
             events[self.L].record()
         return self.outs
 

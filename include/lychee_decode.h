@@ -252,6 +252,29 @@ ld_status ld_hybrid_layer(const ld_shape* shape, uint64_t retrieval_mask,
                           uint32_t flags, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/* The launches ld_hybrid_layer makes for the same arguments, decided exactly as it
+   decides them, without launching anything or touching any pointer (pointers only
+   count as present or absent, so placeholders do; no workspace is needed). It queries
+   the current device's compute-unit count and occupancy. Returns what ld_hybrid_layer
+   would return for its argument checks (except the workspace check) and fills *plan:
+   for launch-shape introspection, tests and per-kernel timing. */
+typedef struct ld_layer_plan {
+  int32_t launches;             /* kernels the call launches (0 when no head is active) */
+  int32_t attention_workgroups; /* workgroups of the attention launch */
+  int32_t split_rows_stream;    /* rows per split of KV groups that stream (0: none) */
+  int32_t split_rows_gather;    /* rows per split of KV groups of sparse heads (0: none) */
+  int32_t waves;                /* waves per attention workgroup */
+  int32_t select_in_launch;     /* 1: the retrieval rows' S is selected inside the
+                                   attention launch; 0: by launches of their own, or none */
+  int32_t selector_parts;       /* in-launch selector workgroups per retrieval row, at most */
+  int32_t reserved;
+} ld_layer_plan;
+ld_status ld_hybrid_layer_plan(const ld_shape* shape, uint64_t retrieval_mask,
+                               const void* q, const void* k_cache, const void* v_cache,
+                               int32_t k, const int32_t* s_in, int32_t* s_out,
+                               const int64_t* s_indptr, float* scores_out, void* out,
+                               uint32_t flags, ld_layer_plan* plan);
+
 /* Standalone argsTopK (method step 3) on fp32 scores, row by row. Row r has
    n_r = n_per_row ? min(max(n_per_row[r], 0), n) : n scores starting at
    scores + r*row_stride, and keeps k_r indices: k_r = k_per_row ? k_per_row[r] : k,

@@ -225,3 +225,19 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ld, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(ld.LycheeDecodeUnavailable):
         ld.load_library()
+
+
+def test_layer_plan_validates_like_the_layer(lib):
+    """ld_hybrid_layer_plan applies the layer's own argument checks before it asks the
+    device anything; a missing plan pointer is rejected too."""
+    INV, UNS = 1, 2
+    plan = ld.LayerPlan()
+
+    def pl(shape, mask=1, kk=10, s_in=FAKE, p=True):
+        return lib.ld_hybrid_layer_plan(ctypes.byref(shape), mask, FAKE, FAKE, FAKE, kk, s_in, FAKE,
+                                        None, None, FAKE, 0, ctypes.byref(plan) if p else None)
+    assert pl(_shape(), p=False) == INV
+    assert pl(_shape(), kk=0) == INV
+    assert pl(_shape(), mask=1 << 40) == INV
+    assert pl(_shape(), s_in=None) == INV                   # sparse heads without S
+    assert pl(_shape(head_dim=80)) == UNS

@@ -368,3 +368,48 @@ def test_csr_rows_are_clipped_to_the_s_buffer():
                 if e > a:
                     want = orc.select_topk_f32(sc[b, h, :lens[b]], int(e - a))
                     assert np.array_equal(g[a:e], want), (l, b, h)
+
+
+def _plan_for(ld, Hq, Hkv, d, N, mask, s_in=True, flags=0):
+    dev = "cuda"
+    q = torch.empty((1, Hq, d), dtype=torch.bfloat16, device=dev)
+    kv = torch.empty((Hkv, N, d), dtype=torch.bfloat16, device=dev)
+    S = torch.empty((1, Hq, max(1, int(0.3 * N))), dtype=torch.int32, device=dev)
+    return ld.hybrid_layer_plan(q, kv, kv, mask, S.shape[2], S if s_in else None, s_out=S,
+                                flags=flags, seq_len=N)
+
+
+def test_layer_plan_describes_the_launches():
+    ld = _ld()
+    full = (1 << 32) - 1
+    # a sparse-only or one-retrieval-head layer on chained S: one attention launch that
+    # also merges O and, with a retrieval head, selects its S
+    p = _plan_for(ld, 32, 8, 128, 32768, 0, flags=ld.FLAG_S_CHAINED)
+    assert p["launches"] == 1 and p["select_in_launch"] == 0 and p["split_rows_stream"] == 0
+    p = _plan_for(ld, 32, 8, 128, 32768, 1 << 5, flags=ld.FLAG_S_CHAINED)
+    assert p["launches"] == 1 and p["select_in_launch"] == 1 and p["selector_parts"] >= 2
+    # unchained S adds the bitmap build
+    assert _plan_for(ld, 32, 8, 128, 32768, 1 << 5)["launches"] == 2
+    # the forced separate mode and a 32-head full layer at 32K select in launches of their own
+    # (the attention launch fuses the first radix digit, so the selection adds one or two)
+    p = _plan_for(ld, 32, 8, 128, 32768, 1 << 5, flags=ld.FLAG_S_CHAINED | ld.FLAG_SEPARATE_SELECT)
+    assert p["launches"] >= 2 and p["select_in_launch"] == 0
+    p = _plan_for(ld, 32, 8, 128, 32768, full, s_in=False)
+    assert p["launches"] >= 2 and p["select_in_launch"] == 0
+    assert p["attention_workgroups"] >= 8
+
+
+def test_both_sides_of_the_in_launch_selection_rule():
+    """A 32-head all-retrieval layer selects inside the launch up to some length and in
+    launches of its own past it; the lengths on both sides of that boundary (found with
+    the plan query) match the oracle."""
+    ld = _ld()
+    full = (1 << 32) - 1
+    inl = lambda n: _plan_for(ld, 32, 8, 128, n, full, s_in=False)["select_in_launch"] == 1
+    lo, hi = 1024, 65536
+    assert inl(lo) and not inl(hi)
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if inl(mid) else (lo, mid)
+    for n in (lo, hi):
+        run_layers(1, 32, 8, 128, [n], [full, 1 << 7], 40 + n % 7)
