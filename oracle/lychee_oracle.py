@@ -31,6 +31,8 @@ Readings taken where the pages are silent (each is listed in the design notes):
   * No causal mask at decode: the single query attends to all N cached rows.
   * A sparse head reads its own layer's K/V at S ([LD] step 4); for HySparse-style
     stacks the caller passes the full layer's K/V ([HS] section 3).
+  * Prefill (the extension [LD]'s future-work paragraph names): see
+    prefill_hybrid_layer for the readings of a multi-row attention matrix.
 
 Parity pins: tests/test_oracle_pins.py checks every function here against closed
 forms, hand-derived examples (tests/golden/), brute-force ranking and invariants.
@@ -49,6 +51,7 @@ __all__ = [
     "select_topk_blocks",
     "hysparse_sparse_layer",
     "tsa_attention",
+    "prefill_hybrid_layer",
     "softmax_attention",
     "select_topk",
     "select_topk_f32",
@@ -325,6 +328,68 @@ def tsa_attention(Q, K, V, scores, k: int, scale=None, causal: bool = False, zer
                 keys = np.arange(kk) if not causal else np.arange(i + 1)   # I ascending: I_j <= I_i iff j <= i
                 out[h, rows[i]], _ = softmax_attention(Q[h, rows[i]], Ks[keys], Vs[keys], scale)
     return out, idx
+
+
+def prefill_hybrid_layer(Q, K, V, batch: int, retrieval: Sequence[bool], k: int,
+                         S_in: Optional[Dict[Tuple[int, int], np.ndarray]] = None, scale=None):
+    """One layer of the hybrid-head recurrence ([LD] steps 3 and 4) applied to a prefill
+    of T prompt tokens per sequence instead of one decode token.
+
+    Q: [Hq][B*T][d]; K, V: [Hkv][B*T][d] (query head h reads KV head h // (Hq // Hkv));
+    the rows of sequence b are b*T .. b*T + T - 1, and query row t sees key rows 0..t of
+    its own sequence (the prompt is causal).
+    Retrieval head h: A = softmax(Q_h K_h^T * scale) under that mask, O = A V, and
+    S_next = argsTopK(A, k) read as the k tokens with the largest column sums of A
+    (importance_j = sum over rows t >= j of A[t, j], the attention mass token j receives
+    in the prompt), ranked like select_topk.
+    Sparse head h: row t attends to the tokens of S_in[(b, h)] at positions <= t only;
+    a row with none of them (t below the set's first token) outputs zeros. S is
+    forwarded unchanged.
+
+    Readings taken (the pages name the extension but give no formula for it): the
+    token set stays one set per head and layer, as in decoding, so that S is the same
+    object the decode recurrence hands on; with one query row (T = 1) every rule above
+    is the decode layer's. Returns (O [Hq][B*T][d], S_out {(b, h): ascending int64},
+    importance {(b, h): [T] fp64} for retrieval heads).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    Hq, BT, d = Q.shape
+    Hkv = K.shape[0]
+    G = Hq // Hkv
+    B = int(batch)
+    assert BT % B == 0 and len(retrieval) == Hq
+    T = BT // B
+    assert 1 <= k <= T
+    if scale is None:
+        scale = default_scale(d)
+    O = np.zeros((Hq, BT, d))
+    S_out: Dict[Tuple[int, int], np.ndarray] = {}
+    importance: Dict[Tuple[int, int], np.ndarray] = {}
+    for b in range(B):
+        r0 = b * T
+        for h in range(Hq):
+            g = h // G
+            Kb, Vb = K[g, r0:r0 + T], V[g, r0:r0 + T]
+            if retrieval[h]:
+                col = np.zeros(T)
+                for t in range(T):
+                    O[h, r0 + t], s = softmax_attention(Q[h, r0 + t], Kb[:t + 1], Vb[:t + 1], scale)
+                    w = np.exp(s - np.max(s))
+                    col[:t + 1] += w / np.sum(w)       # row t of A (its entries past t are 0)
+                importance[(b, h)] = col
+                S_out[(b, h)] = select_topk(col, k)
+            else:
+                assert S_in is not None, "sparse heads need S from the previous layer"
+                S = np.asarray(S_in[(b, h)], dtype=np.int64)
+                assert np.all((S >= 0) & (S < T)) and np.unique(S).size == S.size
+                for t in range(T):
+                    vis = S[S <= t]
+                    if vis.size:
+                        O[h, r0 + t], _ = softmax_attention(Q[h, r0 + t], Kb[vis], Vb[vis], scale)
+                S_out[(b, h)] = np.sort(S)
+    return O, S_out, importance
 
 
 def decode_step_f64(layers: List[Tuple[np.ndarray, np.ndarray, np.ndarray]],
