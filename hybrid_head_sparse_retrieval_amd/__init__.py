@@ -20,7 +20,7 @@ __all__ = [
     "retrieval_decode", "sparse_decode", "hybrid_layer", "topk_select",
     "hysparse_workspace_bytes", "HySparseWorkspace", "hysparse_layer",
     "tsa_workspace_bytes", "TsaWorkspace", "tsa_attention", "TSA_CAUSAL", "TSA_ZERO_FILL", "TSA_GIVEN_IDX",
-    "hybrid_layer_noalloc", "hybrid_layer_plan", "LayerPlan", "NOALLOC_SCRATCH_BYTES", "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "FLAG_SEPARATE_SELECT", "FLAG_BLOCK_SELECT", "flag_split_rows", "flag_waves", "EXPORTED_SYMBOLS",
+    "hybrid_layer_noalloc", "hybrid_layer_plan", "LayerPlan", "prefill_hybrid_layer", "PrefillWorkspace", "NOALLOC_SCRATCH_BYTES", "FLAG_SKIP_TOPK", "FLAG_S_CHAINED", "FLAG_SEPARATE_SELECT", "FLAG_BLOCK_SELECT", "flag_split_rows", "flag_waves", "EXPORTED_SYMBOLS",
 ]
 
 LD_OK = 0
@@ -40,7 +40,7 @@ EXPORTED_SYMBOLS = ("ld_status_string", "ld_workspace_size", "ld_topk_workspace_
                     "ld_sparse_decode", "ld_hybrid_layer", "ld_topk_select",
                     "ld_hysparse_workspace_size", "ld_hysparse_layer",
                     "ld_tsa_workspace_size", "ld_tsa_attention", "ld_hybrid_layer_noalloc",
-                    "ld_hybrid_layer_plan")
+                    "ld_hybrid_layer_plan", "ld_prefill_workspace_size", "ld_prefill_hybrid_layer")
 
 
 def flag_split_rows(v: int) -> int:
@@ -138,6 +138,10 @@ def load_library():
     lib.ld_tsa_workspace_size.argtypes = [sp, i32]
     lib.ld_tsa_attention.restype = i32
     lib.ld_tsa_attention.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, u32, vp, sz, vp]
+    lib.ld_prefill_workspace_size.restype = sz
+    lib.ld_prefill_workspace_size.argtypes = [sp, i32]
+    lib.ld_prefill_hybrid_layer.restype = i32
+    lib.ld_prefill_hybrid_layer.argtypes = [sp, u64, vp, vp, vp, i32, vp, vp, vp, vp, u32, vp, sz, vp]
     lib.ld_topk_select.restype = i32
     lib.ld_topk_select.argtypes = [vp, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     _lib = lib
@@ -311,6 +315,20 @@ class TsaWorkspace(_WS):
 
     def __init__(self, shape: Shape, k: int, device="cuda"):
         super().__init__(tsa_workspace_bytes(shape, k), device)
+
+
+def prefill_workspace_bytes(shape: Shape, k: int) -> int:
+    n = load_library().ld_prefill_workspace_size(ctypes.byref(shape), int(k))
+    if n == 0:
+        raise LycheeDecodeError(1, "ld_prefill_workspace_size")
+    return int(n)
+
+
+class PrefillWorkspace(_WS):
+    """Zero-initialised device workspace for prefill_hybrid_layer."""
+
+    def __init__(self, shape: Shape, k: int, device="cuda"):
+        super().__init__(prefill_workspace_bytes(shape, k), device)
 
 
 class TopkWorkspace(_WS):
@@ -536,6 +554,49 @@ def hysparse_layer(q, k_cache, v_cache, k: int, s_in, k_window, v_window, gate, 
         s_in.data_ptr(), _ptr(s_indptr), k_window.data_ptr(), v_window.data_ptr(), int(W),
         gate.data_ptr(), out.data_ptr(), int(flags), ws.ptr(), ws.nbytes, _stream()),
         "ld_hysparse_layer")
+    return out
+
+
+def prefill_hybrid_layer(q, k_cache, v_cache, retrieval_mask: int, k: int, s, *, batch: int = 1,
+                         s_out=None, importance_out=None, out=None, flags: int = 0,
+                         workspace: Optional[PrefillWorkspace] = None, scale=None):
+    """One hybrid-head layer over a causal prefill of T prompt tokens per sequence:
+    q [Hq][B*T][d], k_cache / v_cache [Hkv][B*T][d] (bf16), B = batch. Retrieval heads
+    run causal full attention and write argsTopK of their attention matrix's column sums
+    to their rows of s_out ([B][Hq][k] int32, ascending); sparse heads attend, row by row,
+    to the tokens of their row of `s` at or before the row (s is None only when every
+    head retrieves). importance_out: optional fp32 [B][Hq][T] column sums. Returns out."""
+    torch = _torch()
+    _req(q, torch.bfloat16, "q"); _req(k_cache, torch.bfloat16, "k_cache"); _req(v_cache, torch.bfloat16, "v_cache")
+    if q.dim() != 3 or k_cache.dim() != 3 or k_cache.shape != v_cache.shape:
+        raise ValueError("q, k_cache, v_cache must be 3-D with equal K/V shapes")
+    B = int(batch)
+    Hq, BT, d = (int(x) for x in q.shape)
+    if B < 1 or BT % B or k_cache.shape[1] != BT or k_cache.shape[2] != d:
+        raise ValueError("q must be [Hq][B*T][d] and k_cache [Hkv][B*T][d]")
+    T = BT // B
+    shape = tsa_shape(q, k_cache, B, scale)
+    kk = min(int(k), T)                                   # the pages' k = min(k, seq_len)
+    _opt(s, torch.int32, "s"); _opt(s_out, torch.int32, "s_out")
+    _opt(importance_out, torch.float32, "importance_out")
+    if s_out is None:
+        s_out = s
+    for name, t in (("s", s), ("s_out", s_out)):
+        if t is not None and t.numel() != B * Hq * kk:
+            raise ValueError(f"{name} must hold B*Hq*min(k, T) = {B * Hq * kk} entries")
+    if importance_out is not None and importance_out.numel() != B * Hq * T:
+        raise ValueError("importance_out must hold B*Hq*T entries")
+    if out is None:
+        out = torch.empty_like(q)
+    _req(out, torch.bfloat16, "out")
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    ws = workspace or _default_ws("prefill", _layout_key(shape, kk), lambda: PrefillWorkspace(shape, kk, q.device),
+                                  q.device)
+    _check(load_library().ld_prefill_hybrid_layer(
+        ctypes.byref(shape), int(retrieval_mask), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kk,
+        _ptr(s), _ptr(s_out), _ptr(importance_out), out.data_ptr(), int(flags), ws.ptr(), ws.nbytes, _stream()),
+        "ld_prefill_hybrid_layer")
     return out
 
 

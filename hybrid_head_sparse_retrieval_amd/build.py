@@ -18,7 +18,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblychee_decode.so")
 # (source, object, extra options): the attention kernels compile once per KV group size
 UNITS = [("ld_api.hip", "ld_api.o", []), ("ld_select.hip", "ld_select.o", []),
-         ("ld_window.hip", "ld_window.o", []), ("ld_tsa.hip", "ld_tsa.o", [])] + \
+         ("ld_window.hip", "ld_window.o", []), ("ld_tsa.hip", "ld_tsa.o", []),
+         ("ld_prefill.hip", "ld_prefill.o", [])] + \
         [("ld_attention.hip", f"ld_attention_g{g}.o", [f"-DLD_ATTN_G={g}"]) for g in (1, 2, 4, 8)]
 SOURCES = sorted({u[0] for u in UNITS})
 
@@ -34,7 +35,8 @@ COMMON = [
 
 # per-source options: the dense-attention kernel keeps its matrix-core accumulators in
 # VGPRs, so the online-softmax rescale works on them in place
-EXTRA = {"ld_tsa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"ld_tsa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "ld_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:

@@ -642,9 +642,115 @@ TsaLayout tsa_layout(const ld_shape* s, int k) {
   return L;
 }
 
+// Prefill layer workspace: the selection arrays of B*Hq rows of T scores, then the
+// retrieval rows' log-sum-exp and column sums ([B*Hq][T] fp32 each).
+struct PrefillLayout {
+  SelLayout sel;
+  size_t lse, imp, total;
+};
+PrefillLayout prefill_layout(const ld_shape* s) {
+  PrefillLayout L{};
+  const size_t rows = (size_t)s->batch * s->num_q_heads, T = (size_t)s->seq_len;
+  L.sel = sel_layout((int)rows, s->seq_len);
+  size_t o = align_up(L.sel.total);
+  L.lse = o;
+  o = align_up(o + rows * T * 4);
+  L.imp = o;
+  o = align_up(o + rows * T * 4);
+  L.total = o;
+  return L;
+}
+
+bool prefill_shape_ok(const ld_shape* s, ld_status* why) {
+  if (!s) { *why = LD_ERR_INVALID_ARGUMENT; return false; }
+  if (!shape_ok(s, why)) return false;
+  // one contiguous bf16 layout of the prompt: no ragged batch, paging or 8-bit codes
+  if (s->kv_indptr || s->page_size || s->kv_dtype) { *why = LD_ERR_UNSUPPORTED; return false; }
+  if (s->total_tokens != 0 && s->total_tokens != (int64_t)s->batch * s->seq_len) {
+    *why = LD_ERR_INVALID_ARGUMENT;
+    return false;
+  }
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t ld_prefill_workspace_size(const ld_shape* shape, int32_t k) {
+  ld_status why;
+  if (!prefill_shape_ok(shape, &why) || k < 1 || k > shape->seq_len) return 0;
+  return prefill_layout(shape).total;
+}
+
+ld_status ld_prefill_hybrid_layer(const ld_shape* shape, uint64_t retrieval_mask, const void* q,
+                                  const void* k_cache, const void* v_cache, int32_t k,
+                                  const int32_t* s_in, int32_t* s_out, float* importance_out,
+                                  void* out, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  ld_status why;
+  if (!prefill_shape_ok(shape, &why)) return why;
+  const int B = shape->batch, Hq = shape->num_q_heads, D = shape->head_dim, T = shape->seq_len;
+  const uint64_t all = (Hq == 64) ? ~0ull : ((1ull << Hq) - 1ull);
+  if (retrieval_mask & ~all) return LD_ERR_INVALID_ARGUMENT;
+  if (flags & ~(uint32_t)LD_FLAG_SKIP_TOPK) return LD_ERR_INVALID_ARGUMENT;
+  if (!q || !k_cache || !v_cache || !out || k < 1 || k > T) return LD_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return LD_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)s_in & 3u) || ((uintptr_t)s_out & 3u) || ((uintptr_t)importance_out & 3u))
+    return LD_ERR_INVALID_ARGUMENT;
+  const uint64_t sparse = all & ~retrieval_mask;
+  const bool select = retrieval_mask && !(flags & LD_FLAG_SKIP_TOPK);
+  if (sparse && !s_in) return LD_ERR_INVALID_ARGUMENT;
+  if (select && !s_out) return LD_ERR_INVALID_ARGUMENT;
+  const PrefillLayout L = prefill_layout(shape);
+  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 15u)) return LD_ERR_WORKSPACE;
+
+  uint8_t sp_heads[64], ret_heads[64];
+  int nsp = 0, nret = 0;
+  for (int h = 0; h < Hq; ++h) {
+    if (sparse >> h & 1ull) sp_heads[nsp++] = (uint8_t)h;
+    if (retrieval_mask >> h & 1ull) ret_heads[nret++] = (uint8_t)h;
+  }
+  // 1. S^{l+1} = S^{l} for sparse heads when the output buffer is a different one
+  if (nsp && s_out && s_out != s_in) {
+    CopyParams cp{};
+    cp.src = s_in; cp.dst = s_out; cp.s_indptr = nullptr; cp.k_dense = k; cp.s_cap = (int64_t)B * Hq * k;
+    cp.Hq = Hq; cp.nsp = nsp;
+    std::memcpy(cp.heads, sp_heads, sizeof(sp_heads));
+    if (launch_copy_rows(cp, B * nsp, stream) != hipSuccess) return LD_ERR_HIP;
+  }
+  // 2. causal attention of every head (retrieval rows also leave their log-sum-exp)
+  PrefillParams pp{};
+  pp.q = static_cast<const uint16_t*>(q);
+  pp.k = static_cast<const uint16_t*>(k_cache);
+  pp.v = static_cast<const uint16_t*>(v_cache);
+  pp.out = static_cast<uint16_t*>(out);
+  pp.B = B; pp.Hq = Hq; pp.Hkv = shape->num_kv_heads; pp.D = D; pp.T = T;
+  pp.qtiles = (T + 63) / 64;
+  pp.retrieval = retrieval_mask;
+  pp.s_in = s_in;
+  pp.kk = k;
+  pp.scale = shape->softmax_scale > 0.f ? shape->softmax_scale : 1.0f / std::sqrt((float)D);
+  pp.lse = select ? at<float>(workspace, L.lse) : nullptr;
+  pp.imp = importance_out ? importance_out : at<float>(workspace, L.imp);
+  pp.nret = nret;
+  std::memcpy(pp.heads, ret_heads, sizeof(ret_heads));
+  if (launch_prefill_attention(pp, stream) != hipSuccess) return LD_ERR_HIP;
+  if (!select) return LD_OK;
+  // 3. column sums of the retrieval heads' attention matrices, then S = argsTopK of them
+  if (launch_prefill_colsum(pp, stream) != hipSuccess) return LD_ERR_HIP;
+  SelParams sp{};
+  sp.mode = 1;
+  sp.nrows = B * nret;
+  set_hist_chunks(sp, sp.nrows, T);
+  sp.logits = pp.imp; sp.Hq = Hq; sp.seq_len = T; sp.kv_indptr = nullptr;
+  sp.s_out = s_out; sp.s_indptr = nullptr; sp.k_dense = k; sp.s_cap = (int64_t)B * Hq * k;
+  sp.bitmaps = nullptr; sp.W = 0;
+  sp.nret = nret;
+  std::memcpy(sp.heads, ret_heads, sizeof(ret_heads));
+  fill_sel(sp, L.sel.sel, workspace);
+  return launch_select(sp, stream, true) == hipSuccess ? LD_OK : LD_ERR_HIP;
+}
 
 size_t ld_tsa_workspace_size(const ld_shape* shape, int32_t k) {
   ld_status why;

@@ -211,5 +211,25 @@ int tsa_queries_per_block();
 // Key splits for kk selected keys of `rows` rows, and the bytes of their partials.
 void tsa_splits(int64_t rows, int kk, int D, int* nsplit, int* split_keys, size_t* part_bytes);
 hipError_t launch_block_expand(const BlockParams& p, int rows, hipStream_t st);
+// Hybrid-head layer over a causal prefill: Q [Hq][B*T][D], K/V [Hkv][B*T][D], O like Q.
+struct PrefillParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  int B, Hq, Hkv, D, T;
+  int qtiles;             // ceil(T / 64)
+  uint64_t retrieval;     // bit h: query head h attends to every earlier token
+  const int32_t* s_in;    // [B][Hq][kk] ascending token sets of the sparse heads
+  int kk;
+  float scale;
+  float* lse;             // [B*Hq][T] log2-sum-exp2 of the retrieval rows' scaled scores
+  float* imp;             // [B*Hq][T] column sums of the retrieval rows' attention matrices
+  int nret;               // retrieval heads (column-sum launch: rows b * nret + i)
+  uint8_t heads[64];      // their ids, ascending
+};
+hipError_t launch_prefill_attention(const PrefillParams& p, hipStream_t st);
+hipError_t launch_prefill_colsum(const PrefillParams& p, hipStream_t st);
+
 
 }  // namespace ld

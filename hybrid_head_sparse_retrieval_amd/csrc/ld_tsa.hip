@@ -21,129 +21,20 @@
 
 #include <type_traits>
 
-#include "ld_device.h"
+#include "ld_tile.h"
 
 namespace ld {
 
 namespace {
 
-constexpr int kTsaWaves = 4;
-constexpr int kTsaQ = 16 * kTsaWaves;   // queries per workgroup
-constexpr int kTsaKeys = 64;            // keys per tile
-constexpr int kTsaIdx = 1024;           // selected positions staged in LDS at a time
-constexpr float kTsaLog2e = 1.4426950408889634f;
-
-typedef __bf16 tsa_bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float tsa_f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ tsa_f32x4_t mfma16(const uint4& a, const uint4& b, tsa_f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(tsa_bf16x8_t, a),
-                                                 __builtin_bit_cast(tsa_bf16x8_t, b), c, 0, 0, 0);
-}
-
 template <int D>
-struct TsaSmem {
-  static constexpr int KS = D + 8;          // K tile row stride (elements)
-  static constexpr int VS = kTsaKeys + 8;   // transposed V tile row stride
-  // (16-byte aligned so that operand reads are single 16-byte LDS reads)
-  alignas(16) uint16_t kt[2][kTsaKeys * KS];   // two tiles: one computed, one being filled
-  alignas(16) uint16_t vt[2][D * VS + (D / 8) * 32];   // rows at vrow(dim)
-  // Row of dimension `dim` in vt: each group of 8 dimensions starts 32 elements (16
-  // banks) after the previous group's end, so that consecutive groups fall in opposite
-  // bank halves and the transposed stores and the operand reads are conflict-free.
-  static __device__ __forceinline__ int vrow(int dim) { return dim * VS + (dim >> 3) * 32; }
-  int qpos[kTsaQ];
-  int kidx[kTsaIdx];                        // selected positions of the current key chunk
-};
-
-// bf16 bits of x, rounded to nearest even by the hardware conversion (the softmax
-// weights are finite and in [0, 1]).
-__device__ __forceinline__ uint16_t tsa_bf16(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
-
-// Tile t of the key chunk: K as LPT 16-byte pieces of rows per thread (row-major,
-// coalesced); V as pairs of rows (2p, 2p + 1) at one 16-byte column piece, so that
-// the transposed store writes whole words (two keys of one dimension). Rows past the
-// chunk's nk keys repeat its last key; they are masked.
-template <int D>
-struct TsaRegs {
-  static constexpr int LPT = kTsaKeys * (D / 8) / (kTsaWaves * 64);        // K pieces per thread
-  static constexpr int VITEMS = (kTsaKeys / 2) * (D / 8);                   // V row pairs x pieces
-  static constexpr int LPV = (VITEMS + kTsaWaves * 64 - 1) / (kTsaWaves * 64);
-  uint4 k[LPT];
-  uint4 v[LPV][2];
-};
-
-template <int D>
-__device__ __forceinline__ void tsa_load(const uint16_t* Kg, const uint16_t* Vg, const int* kidx, int nk, int t,
-                                         int tid, TsaRegs<D>& R) {
-  using RG = TsaRegs<D>;
-  const int base = t * kTsaKeys;
-#pragma unroll
-  for (int i = 0; i < RG::LPT; ++i) {
-    const int u = tid + i * kTsaWaves * 64;
-    const int r = u / (D / 8), c = u % (D / 8);
-    const size_t pos = (size_t)kidx[min(base + r, nk - 1)];
-    R.k[i] = *reinterpret_cast<const uint4*>(Kg + pos * D + c * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < RG::LPV; ++i) {
-    const int u = tid + i * kTsaWaves * 64;
-    if (u < RG::VITEMS) {
-      const int rp = u % (kTsaKeys / 2), c = u / (kTsaKeys / 2);
-      const size_t p0 = (size_t)kidx[min(base + 2 * rp, nk - 1)];
-      const size_t p1 = (size_t)kidx[min(base + 2 * rp + 1, nk - 1)];
-      R.v[i][0] = *reinterpret_cast<const uint4*>(Vg + p0 * D + c * 8);
-      R.v[i][1] = *reinterpret_cast<const uint4*>(Vg + p1 * D + c * 8);
-    }
-  }
-}
-
-// LDS row of key r of a tile: within each 32-key half, key 8a + 4q + b goes to row
-// 16q + 4a + b, so that the q.k product's quarter q (LDS rows 16q .. 16q + 15, read as
-// 16 consecutive rows) leaves lane group a holding keys 8a + 4q .. + 3, and the two
-// quarters of a half together give each lane group 8 consecutive keys for P.V.
-__device__ __forceinline__ int tsa_krow(int r) {
-  return (r & ~31) | (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3);
-}
-
-// The loaded pieces to LDS buffer `buf`: K rows permuted by tsa_krow, V transposed (word j of a pair
-// holds dimension c * 8 + j of keys 2p and 2p + 1).
-template <int D>
-__device__ __forceinline__ void tsa_store(TsaSmem<D>& sm, int buf, int tid, const TsaRegs<D>& R) {
-  using RG = TsaRegs<D>;
-  constexpr int KS = TsaSmem<D>::KS, VS = TsaSmem<D>::VS;
-#pragma unroll
-  for (int i = 0; i < RG::LPT; ++i) {
-    const int u = tid + i * kTsaWaves * 64;
-    const int r = u / (D / 8), c = u % (D / 8);
-    *reinterpret_cast<uint4*>(&sm.kt[buf][tsa_krow(r) * KS + c * 8]) =
-        make_uint4(R.k[i].x, R.k[i].y, R.k[i].z, R.k[i].w);
-  }
-#pragma unroll
-  for (int i = 0; i < RG::LPV; ++i) {
-    const int u = tid + i * kTsaWaves * 64;
-    if (u < RG::VITEMS) {
-      const int rp = u % (kTsaKeys / 2), c = u / (kTsaKeys / 2);
-      const uint32_t a[4] = {R.v[i][0].x, R.v[i][0].y, R.v[i][0].z, R.v[i][0].w};
-      const uint32_t b[4] = {R.v[i][1].x, R.v[i][1].y, R.v[i][1].z, R.v[i][1].w};
-      uint32_t* col = reinterpret_cast<uint32_t*>(&sm.vt[buf][TsaSmem<D>::vrow(c * 8) + 2 * rp]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {   // dims c*8 .. c*8+7 share one bank half
-        col[(2 * w) * (VS / 2)] = (a[w] & 0xffffu) | (b[w] << 16);
-        col[(2 * w + 1) * (VS / 2)] = (a[w] >> 16) | (b[w] & 0xffff0000u);
-      }
-    }
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
-  using Smem = TsaSmem<D>;
-  constexpr int NT = kTsaWaves * 64;
+__global__ __launch_bounds__(kTileWaves * 64) void k_tsa(TsaParams p) {
+  using Smem = TileSmem<D>;
+  constexpr int NT = kTileWaves * 64;
   constexpr int KS = Smem::KS;
   constexpr int KC = D / 32;                                  // k-steps over the head dimension
   constexpr int NO = D / 16;                                  // 16-dim output tiles
-  static_assert(TsaRegs<D>::LPT >= 1, "a tile fills the workgroup's loads");
+  static_assert(TileRegs<D>::LPT >= 1, "a tile fills the workgroup's loads");
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;                   // operand row / k-group
@@ -164,10 +55,10 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
   const uint16_t* Qh = p.q + (size_t)h * plane + seq0 * D;
   const uint16_t* Kg = p.k + (size_t)g * plane + seq0 * D;
   const uint16_t* Vg = p.v + (size_t)g * plane + seq0 * D;
-  const int q0 = qt * kTsaQ;
+  const int q0 = qt * kTileQ;
   auto clampT = [&](int x) { return min(max(x, 0), p.T - 1); };   // caller-given sets stay inside
 
-  if (tid < kTsaQ) sm.qpos[tid] = (q0 + tid < kk) ? clampT(I[q0 + tid]) : -1;
+  if (tid < kTileQ) sm.qpos[tid] = (q0 + tid < kk) ? clampT(I[q0 + tid]) : -1;
   __syncthreads();
   // q operand: query lr of the wave, dims kc * 32 + 8 * lq
   const int qp = sm.qpos[wave * 16 + lr];
@@ -177,46 +68,46 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
     qa[kc] = (qp >= 0) ? *reinterpret_cast<const uint4*>(Qh + (size_t)qp * D + kc * 32 + 8 * lq)
                        : make_uint4(0, 0, 0, 0);
 
-  const int nkeys = p.causal ? min(q0 + kTsaQ, kk) : kk;     // keys any query here may see
+  const int nkeys = p.causal ? min(q0 + kTileQ, kk) : kk;     // keys any query here may see
   const int k_lo = sp * p.split_keys;                         // this split's keys: [k_lo, k_hi)
   const int k_hi = min(nkeys, k_lo + p.split_keys);
   if (k_lo >= k_hi) return;                                   // the same in every thread
-  const float sl = p.scale * kTsaLog2e;
+  const float sl = p.scale * kTileLog2e;
   // The products run transposed, so that a lane holds one query: S^T = K Q^T gives lane
   // (lr, lq) the scores of query lr against keys 4 lq + r of each 16-key half, which is
   // already the operand layout of P^T in O^T = V^T P^T; element r of o[n] is dimension
   // n * 16 + 4 lq + r of query lr. The lanes lr, lr + 16, lr + 32, lr + 48 share a query.
   float m = -LD_INF, lsum = 0.f;               // running max (log2 units) and partial sum
-  tsa_f32x4_t o[NO];
+  tile_f32x4_t o[NO];
 #pragma unroll
-  for (int n = 0; n < NO; ++n) o[n] = tsa_f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < NO; ++n) o[n] = tile_f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int qi = q0 + wave * 16 + lr;          // this lane's query
-  TsaRegs<D> R;
+  TileRegs<D> R;
 
-  for (int cb = k_lo; cb < k_hi; cb += kTsaIdx) {
-    const int nk = min(kTsaIdx, k_hi - cb);
-    const int nt = (nk + kTsaKeys - 1) / kTsaKeys;
+  for (int cb = k_lo; cb < k_hi; cb += kTileIdx) {
+    const int nk = min(kTileIdx, k_hi - cb);
+    const int nt = (nk + kTileKeys - 1) / kTileKeys;
     __syncthreads();                             // the previous chunk is done with LDS
 #pragma unroll 8
     for (int i = tid; i < nk; i += NT) sm.kidx[i] = clampT(I[cb + i]);
     __syncthreads();
-    tsa_load<D>(Kg, Vg, sm.kidx, nk, 0, tid, R);
-    tsa_store<D>(sm, 0, tid, R);
-    if (nt > 1) tsa_load<D>(Kg, Vg, sm.kidx, nk, 1, tid, R);
+    tile_load<D>(Kg, Vg, sm.kidx, nk, 0, tid, R);
+    tile_store<D>(sm, 0, tid, R);
+    if (nt > 1) tile_load<D>(Kg, Vg, sm.kidx, nk, 1, tid, R);
     // tiles in pairs, so that each step's LDS buffer is a compile-time constant
     auto step = [&](int t, auto bufc) {
       constexpr int buf = decltype(bufc)::value;
       __syncthreads();                           // tile t is in buf; the other buffer is free
-      if (t + 1 < nt) tsa_store<D>(sm, buf ^ 1, tid, R);
-      if (t + 2 < nt) tsa_load<D>(Kg, Vg, sm.kidx, nk, t + 2, tid, R);
+      if (t + 1 < nt) tile_store<D>(sm, buf ^ 1, tid, R);
+      if (t + 2 < nt) tile_load<D>(Kg, Vg, sm.kidx, nk, t + 2, tid, R);
       // S^T = K Q^T over the tile's four 16-row quarters (LDS rows st * 16 ..): element
       // r of s[st] is key cb + t * 64 + 32 (st >> 1) + 8 lq + 4 (st & 1) + r against
       // query qi
-      constexpr int NST = kTsaKeys / 16;
-      tsa_f32x4_t s[NST];
+      constexpr int NST = kTileKeys / 16;
+      tile_f32x4_t s[NST];
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
-        s[st] = tsa_f32x4_t{0.f, 0.f, 0.f, 0.f};
+        s[st] = tile_f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           const uint4 ka =
@@ -224,7 +115,7 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
           s[st] = mfma16(ka, qa[kc], s[st]);
         }
       }
-      const int kt0 = cb + t * kTsaKeys;   // the tile's first key; the wave's first query is q0 + 16 * wave
+      const int kt0 = cb + t * kTileKeys;   // the tile's first key; the wave's first query is q0 + 16 * wave
       float x[NST][4];
       // `masked` checks every key (tiles at the end of the range or on the causal
       // diagonal); the interior tiles skip the checks
@@ -242,7 +133,7 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
             }
           }
       };
-      if (kt0 + kTsaKeys <= k_hi && (!p.causal || kt0 + kTsaKeys - 1 <= q0 + wave * 16))
+      if (kt0 + kTileKeys <= k_hi && (!p.causal || kt0 + kTileKeys - 1 <= q0 + wave * 16))
         scores(std::false_type{});
       else
         scores(std::true_type{});
@@ -278,10 +169,10 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
 #pragma unroll
       for (int hh = 0; hh < NST / 2; ++hh) {
         uint4 pb;
-        pb.x = (uint32_t)tsa_bf16(pr[2 * hh][0]) | ((uint32_t)tsa_bf16(pr[2 * hh][1]) << 16);
-        pb.y = (uint32_t)tsa_bf16(pr[2 * hh][2]) | ((uint32_t)tsa_bf16(pr[2 * hh][3]) << 16);
-        pb.z = (uint32_t)tsa_bf16(pr[2 * hh + 1][0]) | ((uint32_t)tsa_bf16(pr[2 * hh + 1][1]) << 16);
-        pb.w = (uint32_t)tsa_bf16(pr[2 * hh + 1][2]) | ((uint32_t)tsa_bf16(pr[2 * hh + 1][3]) << 16);
+        pb.x = (uint32_t)tile_bf16(pr[2 * hh][0]) | ((uint32_t)tile_bf16(pr[2 * hh][1]) << 16);
+        pb.y = (uint32_t)tile_bf16(pr[2 * hh][2]) | ((uint32_t)tile_bf16(pr[2 * hh][3]) << 16);
+        pb.z = (uint32_t)tile_bf16(pr[2 * hh + 1][0]) | ((uint32_t)tile_bf16(pr[2 * hh + 1][1]) << 16);
+        pb.w = (uint32_t)tile_bf16(pr[2 * hh + 1][2]) | ((uint32_t)tile_bf16(pr[2 * hh + 1][3]) << 16);
 #pragma unroll
         for (int n = 0; n < NO; ++n) {
           const uint4 va = *reinterpret_cast<const uint4*>(&sm.vt[buf][Smem::vrow(n * 16 + lr) + 32 * hh + 8 * lq]);
@@ -300,10 +191,10 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
     const size_t unit = ((size_t)row * p.qtiles + qt) * p.nsplit + sp;
     const int ql = wave * 16 + lr;
     if (lq == 0) {
-      p.part_ml[(unit * kTsaQ + ql) * 2 + 0] = m;
-      p.part_ml[(unit * kTsaQ + ql) * 2 + 1] = L;
+      p.part_ml[(unit * kTileQ + ql) * 2 + 0] = m;
+      p.part_ml[(unit * kTileQ + ql) * 2 + 1] = L;
     }
-    float* po = p.part_o + (unit * kTsaQ + ql) * D + 4 * lq;
+    float* po = p.part_o + (unit * kTileQ + ql) * D + 4 * lq;
 #pragma unroll
     for (int n = 0; n < NO; ++n)
       *reinterpret_cast<float4*>(po + n * 16) = make_float4(o[n][0], o[n][1], o[n][2], o[n][3]);
@@ -316,8 +207,8 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
 #pragma unroll
     for (int n = 0; n < NO; ++n) {
       uint2 w;
-      w.x = (uint32_t)tsa_bf16(o[n][0] * il) | ((uint32_t)tsa_bf16(o[n][1] * il) << 16);
-      w.y = (uint32_t)tsa_bf16(o[n][2] * il) | ((uint32_t)tsa_bf16(o[n][3] * il) << 16);
+      w.x = (uint32_t)tile_bf16(o[n][0] * il) | ((uint32_t)tile_bf16(o[n][1] * il) << 16);
+      w.y = (uint32_t)tile_bf16(o[n][2] * il) | ((uint32_t)tile_bf16(o[n][3] * il) << 16);
       *reinterpret_cast<uint2*>(dst + n * 16) = w;
     }
   }
@@ -328,25 +219,25 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa(TsaParams p) {
 // A wave takes 4 queries at a time, a lane DL adjacent dimensions of each; every load
 // of the 4 queries is issued before the first use.
 template <int D>
-__global__ __launch_bounds__(kTsaWaves * 64) void k_tsa_merge(TsaParams p) {
+__global__ __launch_bounds__(kTileWaves * 64) void k_tsa_merge(TsaParams p) {
   constexpr int DL = D / 64;
   constexpr int QW = 4;                                        // queries per step of a wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x / p.qtiles, qt = blockIdx.x % p.qtiles;
   const int b = row / p.Hq, h = row % p.Hq;
-  const int kk = p.kk, q0 = qt * kTsaQ;
-  const int nkeys = p.causal ? min(q0 + kTsaQ, kk) : kk;
+  const int kk = p.kk, q0 = qt * kTileQ;
+  const int nkeys = p.causal ? min(q0 + kTileQ, kk) : kk;
   const int ns = (nkeys + p.split_keys - 1) / p.split_keys;   // splits that ran (1..8)
   const int32_t* I = p.idx + (size_t)row * kk;
   const size_t base = ((size_t)row * p.qtiles + qt) * p.nsplit;
   uint16_t* out = p.out + (size_t)h * p.B * p.T * D + (size_t)b * p.T * D;
-  for (int qs = wave * QW; qs < kTsaQ; qs += kTsaWaves * QW) {
+  for (int qs = wave * QW; qs < kTileQ; qs += kTileWaves * QW) {
     float ml[QW][8][2], po[QW][8][DL];
 #pragma unroll
     for (int j = 0; j < QW; ++j)
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const size_t u = (base + min(s, ns - 1)) * kTsaQ + qs + j;
+        const size_t u = (base + min(s, ns - 1)) * kTileQ + qs + j;
         ml[j][s][0] = p.part_ml[u * 2];
         ml[j][s][1] = p.part_ml[u * 2 + 1];
 #pragma unroll
@@ -375,7 +266,7 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa_merge(TsaParams p) {
       const int pos = min(max(I[qi], 0), p.T - 1);
       const float il = 1.f / L;
 #pragma unroll
-      for (int e = 0; e < DL; ++e) out[(size_t)pos * D + lane * DL + e] = tsa_bf16(acc[e] * il);
+      for (int e = 0; e < DL; ++e) out[(size_t)pos * D + lane * DL + e] = tile_bf16(acc[e] * il);
     }
   }
 }
@@ -383,7 +274,7 @@ __global__ __launch_bounds__(kTsaWaves * 64) void k_tsa_merge(TsaParams p) {
 }  // namespace
 
 hipError_t launch_tsa(const TsaParams& p, hipStream_t st) {
-  const dim3 grid((unsigned)((size_t)p.B * p.Hq * p.qtiles * p.nsplit)), block(kTsaWaves * 64);
+  const dim3 grid((unsigned)((size_t)p.B * p.Hq * p.qtiles * p.nsplit)), block(kTileWaves * 64);
   if (p.D == 128)
     hipLaunchKernelGGL(k_tsa<128>, grid, block, 0, st, p);
   else
@@ -398,7 +289,7 @@ hipError_t launch_tsa(const TsaParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-int tsa_queries_per_block() { return kTsaQ; }
+int tsa_queries_per_block() { return kTileQ; }
 
 // Key splits only when the (row, query block) workgroups alone would leave most of
 // the chip idle (fewer than 512 of them): splits of kTsaSplitKeys keys or more, at
@@ -407,10 +298,10 @@ int tsa_queries_per_block() { return kTsaQ; }
 // chip is full).
 void tsa_splits(int64_t rows, int kk, int D, int* nsplit, int* split_keys, size_t* part_bytes) {
   constexpr int kTsaSplitKeys = 256;
-  const int64_t qtiles = (kk + kTsaQ - 1) / kTsaQ;
-  int ks = max(kTsaSplitKeys, ((kk + 7) / 8 + kTsaKeys - 1) / kTsaKeys * kTsaKeys);
+  const int64_t qtiles = (kk + kTileQ - 1) / kTileQ;
+  int ks = max(kTsaSplitKeys, ((kk + 7) / 8 + kTileKeys - 1) / kTileKeys * kTileKeys);
   int ns = (kk + ks - 1) / ks;
-  size_t bytes = (size_t)rows * qtiles * ns * kTsaQ * (D + 2) * 4;
+  size_t bytes = (size_t)rows * qtiles * ns * kTileQ * (D + 2) * 4;
   if (ns <= 1 || rows * qtiles >= 512 || bytes > ((size_t)256 << 20)) {
     ns = 1;
     ks = kk;

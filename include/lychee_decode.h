@@ -235,6 +235,33 @@ ld_status ld_tsa_attention(const ld_shape* shape, const void* q, const void* k_c
                            void* out, uint32_t flags, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* One layer of the recurrence over a causal PREFILL of T prompt tokens per sequence:
+   the extension to the prefill stage that the LycheeDecode summary page names in its
+   future-work paragraph, with method steps 3 and 4 read for T query rows. Layouts
+   (head-major, one contiguous prompt per sequence): Q and O bf16 [Hq][B*T][d], K and V
+   bf16 [Hkv][B*T][d], where sequence b owns rows b*T .. b*T + T - 1 (ld_shape:
+   seq_len = T, total_tokens 0 or B*T, no kv_indptr, paging or 8-bit codes, else
+   LD_ERR_UNSUPPORTED). Prompt row t attends to tokens 0..t of its own sequence.
+     - Retrieval heads (bits of retrieval_mask): causal full attention; their S row
+       (b,h) of s_out becomes argsTopK of the column sums of their attention matrix A
+       (importance_j = sum over rows t >= j of A[t][j], the attention mass token j
+       receives; ranked in the top-k order above, ascending indices out).
+     - Sparse heads: row t attends to the tokens of S row (b,h) of s_in at positions
+       <= t (a row that sees none of them is zero); S^{l+1} = S^{l} (rows copied when
+       s_out differs from s_in). Their S rows must be ascending (this library writes
+       them so).
+   S is dense [B][Hq][k], 1 <= k <= T (the same layout as the decode layers').
+   importance_out (nullable): fp32 [B][Hq][T], written for retrieval heads only.
+   flags: LD_FLAG_SKIP_TOPK (attention only: no column sums, S and importance left as
+   they were). Workspace: ld_prefill_workspace_size(shape, k) bytes, zeroed once with
+   ld_workspace_init. */
+size_t ld_prefill_workspace_size(const ld_shape* shape, int32_t k);
+ld_status ld_prefill_hybrid_layer(const ld_shape* shape, uint64_t retrieval_mask,
+                                  const void* q, const void* k_cache, const void* v_cache,
+                                  int32_t k, const int32_t* s_in, int32_t* s_out,
+                                  float* importance_out, void* out, uint32_t flags,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* One full layer of the recurrence (method steps 3 and 4) for all Hq heads:
    retrieval heads (bits of retrieval_mask) attend to all rows and write their
    argsTopK rows into s_out; sparse heads attend to S row (b,h) of s_in and S^{l+1} =

@@ -241,3 +241,28 @@ def test_layer_plan_validates_like_the_layer(lib):
     assert pl(_shape(), mask=1 << 40) == INV
     assert pl(_shape(), s_in=None) == INV                   # sparse heads without S
     assert pl(_shape(head_dim=80)) == UNS
+
+
+def test_prefill_workspace_and_arguments(lib):
+    """The prefill layer takes one contiguous bf16 prompt per sequence; invalid shapes
+    and arguments are rejected on the host (no call here reaches a kernel)."""
+    INV, UNS, WSE = 1, 2, 3
+    s = _shape(seq_len=4096)
+    n = lib.ld_prefill_workspace_size(ctypes.byref(s), 1000)
+    assert n >= 2 * 32 * 4096 * 4                          # log-sum-exp and column sums
+    assert lib.ld_prefill_workspace_size(ctypes.byref(s), 0) == 0
+    assert lib.ld_prefill_workspace_size(ctypes.byref(s), 4097) == 0
+    fp8 = _shape(seq_len=4096, kv_dtype=1, k_scale=1.0, v_scale=1.0)
+    assert lib.ld_prefill_workspace_size(ctypes.byref(fp8), 10) == 0
+
+    def pf(shape, mask=(1 << 32) - 1, kk=100, s_in=None, s_out=FAKE, flags=0, ws=FAKE, wsb=1 << 40):
+        return lib.ld_prefill_hybrid_layer(ctypes.byref(shape), mask, FAKE, FAKE, FAKE, kk, s_in, s_out, None,
+                                           FAKE, flags, ws, wsb, None)
+    assert pf(s, mask=1) == INV                            # sparse heads without S
+    assert pf(s, s_out=None) == INV                        # retrieval heads select into nothing
+    assert pf(s, kk=0) == INV and pf(s, kk=4097) == INV
+    assert pf(s, flags=ld.FLAG_S_CHAINED) == INV           # only LD_FLAG_SKIP_TOPK is taken
+    assert pf(s, ws=None) == WSE and pf(s, wsb=16) == WSE
+    assert pf(fp8) == UNS                                  # 8-bit codes: decode only
+    assert pf(_shape(seq_len=4096, kv_indptr=FAKE)) == UNS   # ragged prompts
+    assert pf(_shape(seq_len=4096, head_dim=80)) == UNS
