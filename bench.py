@@ -309,6 +309,9 @@ def main():
     if args.workload in TSA_WORKLOADS:
         tsa_bench(args, torch, ld, dev)
         return
+    if args.workload in PREFILL_WORKLOADS:
+        prefill_bench(args, torch, ld, dev)
+        return
     result = decode_bench(args, torch, ld, DecodeStep, wl, dev, args.workload, not args.no_cpu_baseline)
     also = default_also(args) if args.also == "auto" else [x for x in args.also.split(",") if x and x != "none"]
     if also:
@@ -703,6 +706,147 @@ def tsa_bench(args, torch, ld, dev):
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = tsa_cpu_baseline(q, kc, vc, scores, k, causal, us_layer, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+# The hybrid-head layer over a causal prompt (the prefill extension of the recurrence):
+# Llama-3-8B head layout, one 32K prompt, k = 30 % of it; a full layer (every head
+# retrieves) followed by a layer with two seeded retrieval heads and a sparse-only one.
+PREFILL_WORKLOADS = {
+    "prefill_llama3_8b_32k": dict(B=1, Hq=32, Hkv=8, d=128, T=32768, layers=3, per_layer=2),
+}
+
+
+def prefill_flops(masks, S_rows, T, d):
+    """Matrix flops of one prefill layer per mask: causal q.k and p.v of retrieval rows
+    (4 d per visible pair), the q.k of their column sums (2 d per visible pair), and the
+    q.k and p.v of sparse rows over their visible set tokens (a token at position s is
+    visible to T - s rows). -> (attention flops, column-sum flops)"""
+    pairs = T * (T + 1) // 2
+    attn, col = 0, 0
+    for h, row in enumerate(S_rows):
+        if masks >> h & 1:
+            attn += 4 * d * pairs
+            col += 2 * d * pairs
+        else:
+            attn += 4 * d * int(np.sum(T - row.astype(np.int64)))
+    return attn, col
+
+
+def prefill_bench(args, torch, ld, dev):
+    """Time each prefill layer of the workload (attention, column sums and selection)
+    and the attention launch alone (LD_FLAG_SKIP_TOPK), report the attention kernel
+    against the matrix-core roofline, and time the oracle on the first tokens."""
+    import workloads as wl
+    c = PREFILL_WORKLOADS[args.workload]
+    B, Hq, Hkv, d, T, L = c["B"], c["Hq"], c["Hkv"], c["d"], c["T"], c["layers"]
+    k = int(0.3 * T)
+    masks = wl.seeded_masks(wl.stream_seed("prefill-masks", args.workload) % 1000, L, Hq, c["per_layer"])
+    masks[-1] = 0
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.stream_seed("prefill", args.workload))
+    layers = []
+    for _ in range(L):
+        layers.append(tuple(torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+                            for shape in ((Hq, B * T, d), (Hkv, B * T, d), (Hkv, B * T, d))))
+    S = torch.empty((B, Hq, k), dtype=torch.int32, device=dev)
+    out = torch.empty_like(layers[0][0])
+    shape = ld.tsa_shape(layers[0][0], layers[0][1], B)
+    ws = ld.PrefillWorkspace(shape, k, dev)
+    log(f"[bench] {args.workload}: B={B} Hq={Hq} Hkv={Hkv} d={d} T={T} k={k} masks={[hex(m) for m in masks]}")
+
+    def run_layer(l, flags=0):
+        q, kc, vc = layers[l]
+        ld.prefill_hybrid_layer(q, kc, vc, masks[l], k, S if l else None, batch=B, s_out=S, out=out,
+                                flags=flags, workspace=ws)
+
+    # S before every layer (the accounting pass) -> flops
+    flops = []
+    for l in range(L):
+        S_rows = S.cpu().numpy()[0] if l else np.zeros((Hq, k), dtype=np.int32)
+        flops.append(prefill_flops(masks[l], S_rows, T, d))
+        run_layer(l)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
+
+    def timed_steps(n, flags=0):
+        spans = []
+        for rep in range(n + args.warmup):
+            ev[0].record()
+            for l in range(L):
+                run_layer(l, flags)
+                ev[l + 1].record()
+            torch.cuda.synchronize()
+            if rep >= args.warmup:
+                spans.append([ev[l].elapsed_time(ev[l + 1]) * 1e3 for l in range(L)])
+        return np.median(np.array(spans), axis=0)        # us per layer
+
+    reps = max(3, args.steps // 4)
+    us_layer = timed_steps(reps)
+    us_attn = timed_steps(reps, ld.FLAG_SKIP_TOPK)        # the attention launch alone (the S
+    # buffer is left as the full steps wrote it, so the sparse layers keep their sets)
+    tf_attn = [flops[l][0] / (us_attn[l] * 1e-6) / 1e12 for l in range(L)]
+    for l in range(L):
+        log(f"[bench] layer {l} mask={masks[l]:#x}: {us_layer[l]:.0f} us (attention alone {us_attn[l]:.0f} us, "
+            f"{tf_attn[l]:.0f} TFLOP/s)")
+    total_flops = float(sum(a + cc for a, cc in flops))
+    us_total = float(np.sum(us_layer))
+    result = {
+        "metric": "hybrid-head prefill layer time (attention + column sums + selection)",
+        "value": round(us_total / L, 1),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_total / 1e3, 4),
+        "us_per_layer": [round(float(x), 1) for x in us_layer],
+        "us_attention_per_layer": [round(float(x), 1) for x in us_attn],
+        "tflops_attention_per_layer": [round(float(x), 1) for x in tf_attn],
+        "tflops_step": round(total_flops / (us_total * 1e-6) / 1e12, 1),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "prompt_len": T, "k": k, "layers": L, "retrieval_masks": [hex(m) for m in masks]},
+        "roofline": {"bound": "mfma", "achieved": round(tf_attn[0], 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf_attn[0] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": f"k_prefill_attn (d={d}, every head retrieving)",
+                     "avg_launch_us": round(float(us_attn[0]), 2), "flops_per_launch": int(flops[0][0]),
+                     "launches_timed": reps},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(layers[0], B, T, k, masks[0], us_layer[0], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def prefill_cpu_baseline(layer, B, T, k, mask, gpu_us, target_s):
+    """The oracle's prefill layer on the first Tp tokens of the prompt (Tp doubled from
+    256 while the run stays under about target_s / 4 seconds), scaled to T by (T/Tp)^2
+    (the layer's work is quadratic in the prompt length)."""
+    from oracle import lychee_oracle as orc
+    import workloads as wl
+    q, kc, vc = layer
+    Hq = q.shape[0]
+    ret = [bool(mask >> h & 1) for h in range(Hq)]
+    Tp, spent, cpu = 256, 0.0, 0.0
+    while True:
+        qs = orc.bf16_bits_to_f64(wl.bf16_bits(q[:, :Tp]))
+        ks = orc.bf16_bits_to_f64(wl.bf16_bits(kc[:, :Tp]))
+        vs = orc.bf16_bits_to_f64(wl.bf16_bits(vc[:, :Tp]))
+        t0, c0 = time.perf_counter(), time.process_time()
+        orc.prefill_hybrid_layer(qs, ks, vs, 1, ret, max(1, int(0.3 * Tp)))
+        spent, cpu = time.perf_counter() - t0, time.process_time() - c0
+        log(f"[bench] oracle prefill layer at {Tp} tokens: {spent:.1f}s")
+        if spent * 4 * 4 > target_s or Tp * 2 > T:
+            break
+        Tp *= 2
+    est_us = spent * (T / Tp) ** 2 * 1e6
+    return {"value": round(est_us, 1), "unit": "us", "cores": round(cpu / spent, 1), "kind": "oracle",
+            "cpu_model": _cpu_model(), "gpu_speedup": round(est_us / gpu_us, 1),
+            "sample": f"the oracle's layer over the first {Tp} of {T} prompt tokens ({Hq} heads, mask {mask:#x}), "
+                      f"{spent:.1f} s wall, scaled by (T/{Tp})^2"}
 
 
 def tsa_cpu_baseline(q, kc, vc, scores, k, causal, us_layer, target_s):

@@ -124,6 +124,11 @@ def _build() -> dict:
         name="ragged_b8", index=4, batch=8, layers=32, num_q_heads=32, num_kv_heads=8,
         head_dim=128, seq_lens=lens, k_per_seq=tuple(_floor30(n) for n in lens),
         retrieval_masks=_seeded_mask(2, 32, 32, 32), heavy_frac=0.01, ragged_csr=True)
+    # between the two headline lengths: the Llama-3-8B layout at 64K (launch-shape checks)
+    w["llama3_8b_64k"] = Workload(
+        name="llama3_8b_64k", index=6, batch=1, layers=32, num_q_heads=32,
+        num_kv_heads=8, head_dim=128, seq_lens=(65536,), k_per_seq=(_floor30(65536),),
+        retrieval_masks=_seeded_mask(2, 32, 32, 32), heavy_frac=0.01)
     w["hysparse_7layer"] = Workload(
         name="hysparse_7layer", index=5, batch=1, layers=7, num_q_heads=32,
         num_kv_heads=8, head_dim=128, seq_lens=(131072,), k_per_seq=(4096,),
