@@ -19,7 +19,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 
 struct SelArrays {
-  size_t tickets, hist1, hist2, depart, err;          // zero between calls
+  size_t tickets, hist1, hist2, err;                  // zero between calls
   size_t sel_info, span_cnt, span_off, cand;
   int C;
   int64_t ncap;
@@ -55,7 +55,6 @@ void sel_ctrl(SelArrays& a, int rows, Take take) {
   a.tickets = take((size_t)rows * 4);
   a.hist1 = take((size_t)rows * kRep * kHist1Bins * 4);
   a.hist2 = take((size_t)rows * kHist2Bins * 4);
-  a.depart = take((size_t)rows * 4);
 }
 template <typename Take>
 void sel_data(SelArrays& a, int rows, int n, Take take) {
@@ -93,7 +92,6 @@ void fill_sel(SelParams& sp, const SelArrays& a, void* ws) {
   sp.hist1 = at<uint32_t>(ws, a.hist1);
   sp.hist2 = at<uint32_t>(ws, a.hist2);
   sp.tickets = at<uint32_t>(ws, a.tickets);
-  sp.depart = at<uint32_t>(ws, a.depart);
   sp.err = at<uint32_t>(ws, a.err);
   sp.sel_info = at<uint32_t>(ws, a.sel_info);
   sp.span_cnt = at<uint32_t>(ws, a.span_cnt);
@@ -726,7 +724,7 @@ ld_status ld_prefill_hybrid_layer(const ld_shape* shape, uint64_t retrieval_mask
   pp.v = static_cast<const uint16_t*>(v_cache);
   pp.out = static_cast<uint16_t*>(out);
   pp.B = B; pp.Hq = Hq; pp.Hkv = shape->num_kv_heads; pp.D = D; pp.T = T;
-  pp.qtiles = (T + 63) / 64;
+  pp.qtiles = (T + prefill_rows_per_block() - 1) / prefill_rows_per_block();
   pp.retrieval = retrieval_mask;
   pp.s_in = s_in;
   pp.kk = k;

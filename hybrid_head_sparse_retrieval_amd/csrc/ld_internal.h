@@ -122,8 +122,7 @@ struct SelParams {
   uint32_t* hist1;        // [slots][kRep][kHist1Bins] (summed over replicas), zero between calls
   uint32_t* hist2;        // [slots][kHist2Bins], zero between calls
   uint32_t* tickets;      // [slots] arrivals, zero between calls
-  uint32_t* depart;       // [slots] departures from the row barrier, zero between calls
-  uint32_t* err;          // set when a row barrier gave up waiting (never expected)
+  uint32_t* err;          // the workspace's wait flag (set by the attention launch's bounded waits)
   uint32_t* sel_info;     // [slots][4]: b1, k1, T, i_tie
   uint32_t* span_cnt;     // [slots][C][2]: keys above bin b1, candidates (keys in bin b1)
   uint32_t* span_off;     // [slots][C]: output offset of each span
@@ -218,7 +217,7 @@ struct PrefillParams {
   const uint16_t* v;
   uint16_t* out;
   int B, Hq, Hkv, D, T;
-  int qtiles;             // ceil(T / 64)
+  int qtiles;             // ceil(T / prefill_rows_per_block()): row blocks, and key blocks of the sums
   uint64_t retrieval;     // bit h: query head h attends to every earlier token
   const int32_t* s_in;    // [B][Hq][kk] ascending token sets of the sparse heads
   int kk;
@@ -228,6 +227,7 @@ struct PrefillParams {
   int nret;               // retrieval heads (column-sum launch: rows b * nret + i)
   uint8_t heads[64];      // their ids, ascending
 };
+int prefill_rows_per_block();
 hipError_t launch_prefill_attention(const PrefillParams& p, hipStream_t st);
 hipError_t launch_prefill_colsum(const PrefillParams& p, hipStream_t st);
 

@@ -25,10 +25,17 @@ namespace ld {
 
 namespace {
 
+// 8 waves of 16 rows: a workgroup's 128 prompt rows (or, for the column sums, 128 keys)
+// share every K/V (or Q) tile it loads, which halves the re-reads against 64 rows; with
+// about 200 VGPRs per lane a compute unit holds one such workgroup, the same waves as
+// two of 4.
+constexpr int kPfWaves = 8;
+constexpr int kPfRows = 16 * kPfWaves;
+
 template <int D>
-__global__ __launch_bounds__(kTileWaves * 64) void k_prefill_attn(PrefillParams p) {
+__global__ __launch_bounds__(kPfWaves * 64) void k_prefill_attn(PrefillParams p) {
   using Smem = TileSmem<D>;
-  constexpr int NT = kTileWaves * 64;
+  constexpr int NT = kPfWaves * 64;
   constexpr int KS = Smem::KS;
   constexpr int KC = D / 32;                                  // k-steps over the head dimension
   constexpr int NO = D / 16;                                  // 16-dim output tiles
@@ -38,9 +45,10 @@ __global__ __launch_bounds__(kTileWaves * 64) void k_prefill_attn(PrefillParams 
   const int lr = lane & 15, lq = lane >> 4;
   // row (b, h) and query block; blocks go out in the order 0, 1, .., then from the last
   // one down, each over all rows, so that workgroups sharing a compute unit pair a
-  // short block with a long one
+  // short block with a long one. The rows rotate by one per block, so that a row's
+  // blocks do not all land on one XCD (consecutive workgroup ids take turns on them)
   const int rows = p.B * p.Hq;
-  const int jq = blockIdx.x / rows, row = blockIdx.x % rows;
+  const int jq = blockIdx.x / rows, row = (blockIdx.x % rows + jq) % rows;
   const int half = (p.qtiles + 1) / 2;
   const int qt = jq < half ? jq : p.qtiles - 1 - (jq - half);
   const int b = row / p.Hq, h = row % p.Hq, g = h / (p.Hq / p.Hkv);
@@ -51,9 +59,9 @@ __global__ __launch_bounds__(kTileWaves * 64) void k_prefill_attn(PrefillParams 
   const uint16_t* Qh = p.q + (size_t)h * plane + seq0 * D;
   const uint16_t* Kg = p.k + (size_t)g * plane + seq0 * D;
   const uint16_t* Vg = p.v + (size_t)g * plane + seq0 * D;
-  const int q0 = qt * kTileQ;
+  const int q0 = qt * kPfRows;
   const int qi = q0 + wave * 16 + lr;                         // this lane's query row
-  const int lim = min(q0 + kTileQ, T) - 1;                    // the block's last row
+  const int lim = min(q0 + kPfRows, T) - 1;                   // the block's last row
   uint4 qa[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc)
@@ -68,7 +76,7 @@ __global__ __launch_bounds__(kTileWaves * 64) void k_prefill_attn(PrefillParams 
   tile_f32x4_t o[NO];
 #pragma unroll
   for (int n = 0; n < NO; ++n) o[n] = tile_f32x4_t{0.f, 0.f, 0.f, 0.f};
-  TileRegs<D> R;
+  TileRegs<D, kPfWaves> R;
 
   // keys in chunks of kTileIdx positions staged in LDS: a retrieval row's keys are the
   // tokens 0 .. lim; a sparse row's, the entries of S up to lim (a prefix, S ascending)
@@ -89,14 +97,14 @@ __global__ __launch_bounds__(kTileWaves * 64) void k_prefill_attn(PrefillParams 
     const int nk = ret ? avail : cnt;                         // keys of the chunk the block may see
     if (nk == 0) break;
     const int nt = (nk + kTileKeys - 1) / kTileKeys;
-    tile_load<D>(Kg, Vg, sm.kidx, nk, 0, tid, R);
-    tile_store<D>(sm, 0, tid, R);
-    if (nt > 1) tile_load<D>(Kg, Vg, sm.kidx, nk, 1, tid, R);
+    tile_load<D, kPfWaves>(Kg, Vg, sm.kidx, nk, 0, tid, R);
+    tile_store<D, kPfWaves>(sm, 0, tid, R);
+    if (nt > 1) tile_load<D, kPfWaves>(Kg, Vg, sm.kidx, nk, 1, tid, R);
     auto step = [&](int t, auto bufc) {
       constexpr int buf = decltype(bufc)::value;
       __syncthreads();                           // tile t is in buf; the other buffer is free
-      if (t + 1 < nt) tile_store<D>(sm, buf ^ 1, tid, R);
-      if (t + 2 < nt) tile_load<D>(Kg, Vg, sm.kidx, nk, t + 2, tid, R);
+      if (t + 1 < nt) tile_store<D, kPfWaves>(sm, buf ^ 1, tid, R);
+      if (t + 2 < nt) tile_load<D, kPfWaves>(Kg, Vg, sm.kidx, nk, t + 2, tid, R);
       constexpr int NST = kTileKeys / 16;
       tile_f32x4_t s[NST];
 #pragma unroll
@@ -202,7 +210,7 @@ struct ColSmem {
 
 template <int D>
 struct ColRegs {
-  static constexpr int LPT = kTileKeys * (D / 8) / (kTileWaves * 64);
+  static constexpr int LPT = kTileKeys * (D / 8) / (kPfWaves * 64);
   uint4 r[LPT];
   float ls;
 };
@@ -212,7 +220,7 @@ __device__ __forceinline__ void col_load(const uint16_t* Qh, const float* lse, i
                                          ColRegs<D>& R) {
 #pragma unroll
   for (int i = 0; i < ColRegs<D>::LPT; ++i) {
-    const int u = tid + i * kTileWaves * 64;
+    const int u = tid + i * kPfWaves * 64;
     const int r = u / (D / 8), c = u % (D / 8);
     R.r[i] = *reinterpret_cast<const uint4*>(Qh + (size_t)min(t0 + r, T - 1) * D + c * 8);
   }
@@ -223,7 +231,7 @@ template <int D>
 __device__ __forceinline__ void col_store(ColSmem<D>& sm, int buf, int tid, const ColRegs<D>& R) {
 #pragma unroll
   for (int i = 0; i < ColRegs<D>::LPT; ++i) {
-    const int u = tid + i * kTileWaves * 64;
+    const int u = tid + i * kPfWaves * 64;
     const int r = u / (D / 8), c = u % (D / 8);
     *reinterpret_cast<uint4*>(&sm.qt[buf][tile_krow(r) * ColSmem<D>::KS + c * 8]) =
         make_uint4(R.r[i].x, R.r[i].y, R.r[i].z, R.r[i].w);
@@ -232,7 +240,7 @@ __device__ __forceinline__ void col_store(ColSmem<D>& sm, int buf, int tid, cons
 }
 
 template <int D>
-__global__ __launch_bounds__(kTileWaves * 64) void k_prefill_colsum(PrefillParams p) {
+__global__ __launch_bounds__(kPfWaves * 64) void k_prefill_colsum(PrefillParams p) {
   using Smem = ColSmem<D>;
   constexpr int KS = Smem::KS;
   constexpr int KC = D / 32;
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(kTileWaves * 64) void k_prefill_colsum(PrefillParam
   // retrieval row rr = b * nret + i and key block kb; the first key blocks (seen by the
   // most query rows) go out first
   const int rrows = p.B * p.nret;
-  const int kb = blockIdx.x / rrows, rr = blockIdx.x % rrows;
+  const int kb = blockIdx.x / rrows, rr = (blockIdx.x % rrows + kb) % rrows;   // rotated as above
   const int b = rr / p.nret, h = p.heads[rr % p.nret], g = h / (p.Hq / p.Hkv);
   const int row = b * p.Hq + h;
   const int T = p.T;
@@ -252,7 +260,7 @@ __global__ __launch_bounds__(kTileWaves * 64) void k_prefill_colsum(PrefillParam
   const uint16_t* Qh = p.q + (size_t)h * plane + seq0 * D;
   const uint16_t* Kg = p.k + (size_t)g * plane + seq0 * D;
   const float* lse = p.lse + (size_t)row * T;
-  const int j = kb * kTileKeys + wave * 16 + lr;              // this lane's key
+  const int j = kb * kPfRows + wave * 16 + lr;                // this lane's key
   uint4 ka[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc)
@@ -260,8 +268,8 @@ __global__ __launch_bounds__(kTileWaves * 64) void k_prefill_colsum(PrefillParam
                      : make_uint4(0, 0, 0, 0);
   const float sl = p.scale * kTileLog2e;
   float acc = 0.f;
-  const int t_first = kb;                                     // query tiles that see the block
-  const int nt = p.qtiles - t_first;
+  const int t_first = kb * (kPfRows / kTileKeys);             // 64-row query tiles that see the block
+  const int nt = (T + kTileKeys - 1) / kTileKeys - t_first;
   ColRegs<D> R;
   col_load<D>(Qh, lse, T, t_first * kTileKeys, tid, R);
   col_store<D>(sm, 0, tid, R);
@@ -284,8 +292,8 @@ __global__ __launch_bounds__(kTileWaves * 64) void k_prefill_colsum(PrefillParam
     }
     const int t0 = (t_first + t) * kTileKeys;
     // rows past T carry an infinite log-sum-exp (weight 0); rows before the key are
-    // masked on the diagonal tile only
-    const bool diag = t == 0;
+    // masked on the tiles that overlap the key block only
+    const bool diag = t < kPfRows / kTileKeys;
 #pragma unroll
     for (int st = 0; st < NST; ++st)
 #pragma unroll
@@ -305,8 +313,10 @@ __global__ __launch_bounds__(kTileWaves * 64) void k_prefill_colsum(PrefillParam
 
 }  // namespace
 
+int prefill_rows_per_block() { return kPfRows; }
+
 hipError_t launch_prefill_attention(const PrefillParams& p, hipStream_t st) {
-  const dim3 grid((unsigned)((size_t)p.B * p.Hq * p.qtiles)), block(kTileWaves * 64);
+  const dim3 grid((unsigned)((size_t)p.B * p.Hq * p.qtiles)), block(kPfWaves * 64);
   if (p.D == 128)
     hipLaunchKernelGGL(k_prefill_attn<128>, grid, block, 0, st, p);
   else
@@ -315,7 +325,7 @@ hipError_t launch_prefill_attention(const PrefillParams& p, hipStream_t st) {
 }
 
 hipError_t launch_prefill_colsum(const PrefillParams& p, hipStream_t st) {
-  const dim3 grid((unsigned)((size_t)p.B * p.nret * p.qtiles)), block(kTileWaves * 64);
+  const dim3 grid((unsigned)((size_t)p.B * p.nret * p.qtiles)), block(kPfWaves * 64);
   if (p.D == 128)
     hipLaunchKernelGGL(k_prefill_colsum<128>, grid, block, 0, st, p);
   else

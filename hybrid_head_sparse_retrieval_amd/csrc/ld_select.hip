@@ -573,8 +573,9 @@ __device__ __forceinline__ int span_offsets(int nsp, SpanSmem& sm, uint32_t* off
   return (int)sm.misc[3];
 }
 
-// Two-kernel selection (any grid size): k_sel_cand, whose last span of a row runs
-// phase 2 and stores T, i_tie and the span offsets, then k_sel_write.
+// Selection in two launches, which assumes nothing about how many of its workgroups the
+// device holds at once: k_sel_cand, whose last span of a row runs phase 2 and stores T,
+// i_tie and the span offsets, then k_sel_write.
 __global__ __launch_bounds__(kSpanThreads) void k_sel_cand(const SelParams p) {
   __shared__ SpanSmem sm;
   const int r = blockIdx.x / p.C, c = blockIdx.x % p.C;
@@ -616,65 +617,6 @@ __global__ __launch_bounds__(kSpanThreads) void k_sel_write(const SelParams p) {
   const int off = (int)p.span_off[(size_t)slot * p.C + c];
   uint32_t key[kSpanRounds][4];
   load_span(v.sc, v.n, c * kSelSpan, threadIdx.x, key);
-  span_write(p, v, c, T, i_tie, off, key, sm);
-}
-
-// One-kernel selection for grids whose workgroups are all resident at once: the
-// spans of a row meet at a barrier after phase 1 (a device-coherent arrival counter,
-// with a bounded wait), then every span runs phase 2 itself and writes its part of
-// the row from the keys still in registers. The last span to leave clears the
-// arrival and departure counters and the digit-2 histogram.
-__global__ __launch_bounds__(kSpanThreads) void k_sel_fused(const SelParams p) {
-  __shared__ SpanSmem sm;
-  const int r = blockIdx.x / p.C, c = blockIdx.x % p.C;
-  const RowView v = row_view(p, r);
-  const int n = v.n, kk = v.k;
-  if (n < 1 || kk < 1) return;
-  const int nsp = (n + kSelSpan - 1) / kSelSpan;
-  if (c >= nsp) return;
-  const int tid = threadIdx.x;
-  const int slot = v.slot;
-  const uint32_t b1 = p.sel_info[slot * 4 + 0];
-  const uint32_t k1 = p.sel_info[slot * 4 + 1];
-  uint64_t* cand = p.cand + (size_t)slot * p.ncap;
-  uint32_t* gh2 = p.hist2 + (size_t)slot * kHist2Bins;
-  uint32_t key[kSpanRounds][4];
-  load_span(v.sc, n, c * kSelSpan, tid, key);
-  span_candidates(p, slot, c, n, b1, key, cand, gh2, sm);
-
-  // ---- row barrier: every span's candidates, counts and histogram are stored
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(p.tickets + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old != (uint32_t)nsp - 1u) {
-      int spins = 0;
-      // read-modify-write polls are performed where the arrivals are counted
-      while (__hip_atomic_fetch_add(p.tickets + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)nsp) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > kMaxSpins) {               // never expected: report and go on
-          st_dev(p.err, 1u);
-          break;
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  uint32_t T, i_tie;
-  row_threshold(p, slot, nsp, b1, k1, gh2, false, cand, sm, T, i_tie);
-  const int off = span_offsets(nsp, sm, nullptr, c);
-
-  // ---- departure (this span has read everything shared)
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(p.depart + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.flag = (old == (uint32_t)nsp - 1u);
-  }
-  __syncthreads();
-  if (sm.flag) {
-    if (tid == 0) { p.tickets[slot] = 0u; p.depart[slot] = 0u; }
-    for (int i = tid; i < kHist2Bins; i += kSpanThreads) gh2[i] = 0u;
-  }
   span_write(p, v, c, T, i_tie, off, key, sm);
 }
 
@@ -786,26 +728,9 @@ hipError_t launch_block_expand(const BlockParams& p, int rows, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Workgroups of k_sel_fused that the current device holds at once.
-int64_t fused_capacity() {
-  static std::atomic<int64_t> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int64_t c = cache[dev].load(std::memory_order_relaxed);
-  if (c > 0) return c;
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_sel_fused, kSpanThreads, 0) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  c = (int64_t)per_cu * cus;
-  cache[dev].store(c, std::memory_order_relaxed);
-  return c;
-}
-
 int select_launches(const SelParams& p, bool with_hist) {
   if (with_hist && p.mode == 0 && p.n <= kSmallRow) return 1;
-  const int fused = (int64_t)p.nrows * p.C <= fused_capacity() ? 1 : 2;
-  return (with_hist ? 1 : 0) + fused;
+  return (with_hist ? 1 : 0) + 2;
 }
 
 hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist) {
@@ -819,12 +744,8 @@ hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist) {
     hipLaunchKernelGGL(k_sel_hist, dim3((unsigned)p.nrows * (unsigned)p.Ch), dim3(kThreads), 0, st, ph);
   }
   const dim3 grid((unsigned)p.nrows * (unsigned)p.C);
-  if ((int64_t)p.nrows * p.C <= fused_capacity()) {
-    hipLaunchKernelGGL(k_sel_fused, grid, dim3(kSpanThreads), 0, st, p);
-  } else {
-    hipLaunchKernelGGL(k_sel_cand, grid, dim3(kSpanThreads), 0, st, p);
-    hipLaunchKernelGGL(k_sel_write, grid, dim3(kSpanThreads), 0, st, p);
-  }
+  hipLaunchKernelGGL(k_sel_cand, grid, dim3(kSpanThreads), 0, st, p);
+  hipLaunchKernelGGL(k_sel_write, grid, dim3(kSpanThreads), 0, st, p);
   return hipGetLastError();
 }
 

@@ -47,30 +47,30 @@ __device__ __forceinline__ uint16_t tile_bf16(float x) { return __builtin_bit_ca
 // coalesced); V as pairs of rows (2p, 2p + 1) at one 16-byte column piece, so that
 // the transposed store writes whole words (two keys of one dimension). Rows past the
 // chunk's nk keys repeat its last key; they are masked.
-template <int D>
-struct TileRegs {
-  static constexpr int LPT = kTileKeys * (D / 8) / (kTileWaves * 64);        // K pieces per thread
+template <int D, int NW = kTileWaves>
+struct TileRegs {   // per thread of a workgroup of NW waves
+  static constexpr int LPT = kTileKeys * (D / 8) / (NW * 64);        // K pieces per thread
   static constexpr int VITEMS = (kTileKeys / 2) * (D / 8);                   // V row pairs x pieces
-  static constexpr int LPV = (VITEMS + kTileWaves * 64 - 1) / (kTileWaves * 64);
+  static constexpr int LPV = (VITEMS + NW * 64 - 1) / (NW * 64);
   uint4 k[LPT];
   uint4 v[LPV][2];
 };
 
-template <int D>
+template <int D, int NW = kTileWaves>
 __device__ __forceinline__ void tile_load(const uint16_t* Kg, const uint16_t* Vg, const int* kidx, int nk, int t,
-                                         int tid, TileRegs<D>& R) {
-  using RG = TileRegs<D>;
+                                         int tid, TileRegs<D, NW>& R) {
+  using RG = TileRegs<D, NW>;
   const int base = t * kTileKeys;
 #pragma unroll
   for (int i = 0; i < RG::LPT; ++i) {
-    const int u = tid + i * kTileWaves * 64;
+    const int u = tid + i * NW * 64;
     const int r = u / (D / 8), c = u % (D / 8);
     const size_t pos = (size_t)kidx[min(base + r, nk - 1)];
     R.k[i] = *reinterpret_cast<const uint4*>(Kg + pos * D + c * 8);
   }
 #pragma unroll
   for (int i = 0; i < RG::LPV; ++i) {
-    const int u = tid + i * kTileWaves * 64;
+    const int u = tid + i * NW * 64;
     if (u < RG::VITEMS) {
       const int rp = u % (kTileKeys / 2), c = u / (kTileKeys / 2);
       const size_t p0 = (size_t)kidx[min(base + 2 * rp, nk - 1)];
@@ -91,20 +91,20 @@ __device__ __forceinline__ int tile_krow(int r) {
 
 // The loaded pieces to LDS buffer `buf`: K rows permuted by tile_krow, V transposed (word j of a pair
 // holds dimension c * 8 + j of keys 2p and 2p + 1).
-template <int D>
-__device__ __forceinline__ void tile_store(TileSmem<D>& sm, int buf, int tid, const TileRegs<D>& R) {
-  using RG = TileRegs<D>;
+template <int D, int NW = kTileWaves>
+__device__ __forceinline__ void tile_store(TileSmem<D>& sm, int buf, int tid, const TileRegs<D, NW>& R) {
+  using RG = TileRegs<D, NW>;
   constexpr int KS = TileSmem<D>::KS, VS = TileSmem<D>::VS;
 #pragma unroll
   for (int i = 0; i < RG::LPT; ++i) {
-    const int u = tid + i * kTileWaves * 64;
+    const int u = tid + i * NW * 64;
     const int r = u / (D / 8), c = u % (D / 8);
     *reinterpret_cast<uint4*>(&sm.kt[buf][tile_krow(r) * KS + c * 8]) =
         make_uint4(R.k[i].x, R.k[i].y, R.k[i].z, R.k[i].w);
   }
 #pragma unroll
   for (int i = 0; i < RG::LPV; ++i) {
-    const int u = tid + i * kTileWaves * 64;
+    const int u = tid + i * NW * 64;
     if (u < RG::VITEMS) {
       const int rp = u % (kTileKeys / 2), c = u / (kTileKeys / 2);
       const uint32_t a[4] = {R.v[i][0].x, R.v[i][0].y, R.v[i][0].z, R.v[i][0].w};
