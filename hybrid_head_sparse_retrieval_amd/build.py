@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "liblychee_decode.so")
 UNITS = [("ld_api.hip", "ld_api.o", []), ("ld_select.hip", "ld_select.o", []),
          ("ld_window.hip", "ld_window.o", []), ("ld_tsa.hip", "ld_tsa.o", []),
          ("ld_prefill.hip", "ld_prefill.o", [])] + \
-        [("ld_attention.hip", f"ld_attention_g{g}.o", [f"-DLD_ATTN_G={g}"]) for g in (1, 2, 4, 8)]
+        [("ld_attention.hip", f"ld_attention_g{g}.o", [f"-DLD_ATTN_G={g}"]) for g in (1, 2, 4, 8)] + \
+        [("ld_attention.hip", f"ld_attention_blk_g{g}.o", [f"-DLD_ATTN_G={g}", "-DLD_ATTN_BLK=1"]) for g in (1, 2, 4, 8)]
 SOURCES = sorted({u[0] for u in UNITS})
 
 ARCH = "gfx950"

@@ -223,6 +223,15 @@ int64_t attention_capacity(int D, int G, int waves, bool fp8) {
 }
 
 hipError_t launch_attention(const AttnParams& p, int D, int G, dim3 grid, hipStream_t st) {
+  if (p.gather_blocks) {
+    switch (G) {
+      case 1: return launch_attention_blk_g<1>(p, D, grid, st);
+      case 2: return launch_attention_blk_g<2>(p, D, grid, st);
+      case 4: return launch_attention_blk_g<4>(p, D, grid, st);
+      case 8: return launch_attention_blk_g<8>(p, D, grid, st);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (G) {
     case 1: return launch_attention_g<1>(p, D, grid, st);
     case 2: return launch_attention_g<2>(p, D, grid, st);
@@ -403,7 +412,8 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   }
   ap.ngroups = ng;
   ap.ng_dense = ng_dense;
-  ap.waves = choose_waves(flags);
+  ap.gather_blocks = (flags & LD_FLAG_BLOCK_SELECT) ? 1 : 0;   // the sets are whole 64-token blocks
+  ap.waves = ap.gather_blocks ? 4 : choose_waves(flags);
   // Finisher mode (default): the last split of each KV group to arrive merges O, and
   // the retrieval rows are selected inside the launch by the splits that arrive just
   // before it. At most a quarter of the resident capacity may wait for its group's last
@@ -453,7 +463,10 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   ap.nsplit_d = (N + ap.ts_d - 1) / ap.ts_d;
   ap.nsplit_s = (N + ap.ts_s - 1) / ap.ts_s;
   ap.bitmaps = bitmaps; ap.W = L.W;
-  ap.logits = scores_out ? scores_out : (do_topk ? at<float>(ws, L.logits) : nullptr);
+  // token selection reads the logits from the workspace (or scores_out); block selection
+  // takes the launch's block maxima instead
+  ap.logits = scores_out ? scores_out : ((do_topk && !block) ? at<float>(ws, L.logits) : nullptr);
+  ap.blk_out = block ? at<float>(ws, L.blk_scores) : nullptr;
   ap.part_ml = at<float>(ws, L.part_ml);
   ap.part_acc = at<float>(ws, L.part_acc);
   ap.P = L.P;
@@ -489,7 +502,6 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   // radix select over the block scores, then the kept blocks' tokens), or by tokens
   if (block) {
     BlockParams bk{};
-    bk.logits = ap.logits; bk.seq_len = N;
     bk.scores = at<float>(ws, L.blk_scores);
     bk.kept = at<int32_t>(ws, L.blk_idx);
     bk.rows = B * nret; bk.nblk = N / kBlock; bk.kblk = k / kBlock;
@@ -497,7 +509,6 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
     bk.bitmaps = bitmaps; bk.W = L.W;
     bk.Hq = Hq; bk.nret = nret;
     std::memcpy(bk.heads, ret_heads, sizeof(ret_heads));
-    LD_LAUNCH(launch_block_max(bk, bk.rows, st), 1);
     SelParams sp{};
     sp.mode = 0;
     sp.nrows = bk.rows;

@@ -661,7 +661,10 @@ __device__ __forceinline__ void part_select(uint32_t* hist, uint32_t* cand_lds, 
 
 // F8: K and V hold E4M3 codes (one byte per element, dequantised exactly to bf16 /
 // fp32 in registers; their per-tensor scales are folded into p.scale and p.v_scale).
-template <int D, int G, int NW, bool F8>
+// BLK: token-block selection (the sets are whole 64-row blocks): stream mode also keeps
+// the retrieval rows' block maxima, gather mode spreads the blocks over the waves; a
+// separate instance, so that the token path carries none of it.
+template <int D, int G, int NW, bool F8, bool BLK = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams p) {
   constexpr int NT = 64 * NW;
   constexpr int KCH = D / 32;        // MFMA k-steps per row
@@ -680,6 +683,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   const int mr = lane & 15, mk = lane >> 4;   // MFMA roles: row/column, k-group
   const int rg = lane >> 3, li = lane & 7;    // P.V roles: row in step, dim slice
   const bool do_hist = p.do_topk != 0;
+  const bool do_blk = BLK && p.blk_out != nullptr;   // block maxima of the retrieval rows' logits
 
   int bid = blockIdx.x;
   const int dense_blocks = p.B * p.ng_dense * p.nsplit_d;
@@ -785,12 +789,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   // (one chunk, loaded before the membership words arrive, non-members masked), then
   // the members of the rest of its block (its own visit list), so the list needs no
   // workgroup-wide step and memory is busy from the start.
+  // With p.gather_blocks (sets made of whole 64-row blocks, clustered rather than spread),
+  // a wave owns the interleaved 64-row steps wave, wave + NW, .. of the split instead, so
+  // that the selected blocks spread over the waves; visit positions stay per wave.
   int nlist = nrows;
   int nl_w = 0;
   const int gR = ((ts + 64 * NW - 1) / (64 * NW)) * 64;   // gather: rows per wave
-  const int lbase = dense ? 0 : wave * gR;
+  const bool ilv = BLK && !dense;
+  const int lbase = dense ? 0 : wave * gR;                // the wave's visit positions start here
+  auto step_row = [&](int c) { return ilv ? (c * NW + wave) * 64 : lbase + c * 64; };   // first row of step c
   const int rend = dense ? nrows : min(nrows, lbase + gR);
-  const int head = dense ? 0 : min(CROWS, max(0, rend - lbase));
+  const int head = dense ? 0 : (ilv ? min(CROWS, max(0, nrows - wave * 64)) : min(CROWS, max(0, rend - lbase)));
   auto chunks_of = [&](int n) {
     const int ntiles = (n + kTile - 1) / kTile;
     const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
@@ -815,7 +824,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 
   uint4 kr[3][TPC][KCH], vr[3][RSC][NV];
 
-  auto row_of = [&](int pos) -> int { return (dense || pos < lbase + head) ? pos : (int)sm.list[pos]; };
+  auto row_of = [&](int pos) -> int {
+    if constexpr (BLK) {
+      if (dense) return pos;
+      if (pos < lbase + head) return ilv ? wave * 64 + (pos - lbase) : pos;   // the head rows
+      return (int)sm.list[pos];
+    } else {
+      return (dense || pos < lbase + head) ? pos : (int)sm.list[pos];
+    }
+  };
   auto load_chunk = [&](int c, uint4 (&kd)[TPC][KCH], uint4 (&vd)[RSC][NV]) {
 #pragma unroll
     for (int t = 0; t < TPC; ++t) {
@@ -856,8 +873,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   static_assert(2 * GCH <= 64, "one word per lane");
   uint32_t gbw[G];
   if (!dense) {
-    const int word = ((r0 + lbase) >> 5) + lane;
-    const bool ok = lane < 2 * GCH && lbase + 32 * lane < rend && word < p.W;
+    int word;
+    bool ok;
+    if constexpr (BLK) {
+      const int srow = step_row(lane >> 1) + 32 * (lane & 1);   // lanes 2c, 2c+1: the words of step c
+      word = (r0 + srow) >> 5;
+      ok = lane < 2 * GCH && srow < (ilv ? nrows : rend) && word < p.W;
+    } else {
+      word = ((r0 + lbase) >> 5) + lane;
+      ok = lane < 2 * GCH && lbase + 32 * lane < rend && word < p.W;
+    }
 #pragma unroll
     for (int j = 0; j < G; ++j)
       gbw[j] = ((spm >> j & 1) && ok) ? p.bitmaps[(size_t)(hq0 + j) * p.W + word] : 0u;
@@ -871,7 +896,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   }
 
   // ---- membership of each row of the tile, and the visit list
-  if (do_hist && ret) {
+  if ((do_hist || do_blk) && ret) {           // histogram bins, or block-maximum keys
     for (int j = 0; j < G; ++j)
       if (ret >> j & 1u)
         for (int i = tid; i < kHist1Bins / 4; i += NT) reinterpret_cast<uint4*>(sm.u.hist[j])[i] = make_uint4(0, 0, 0, 0);
@@ -915,25 +940,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     }
   }
   if (spm && !dense) {
-    // rows owned by this wave: [lbase, rend) of the split, 64 per ballot; the head rows
+    // rows owned by this wave: its 64-row steps (step_row), one per ballot; the head rows
     // keep their positions (their membership masks the softmax), the rest are listed
     constexpr int CH = GCH;
+    const int rlim = ilv ? nrows : rend;
     uint32_t mrow[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int r = lbase + c * 64 + lane;
-      mrow[c] = r < rend ? row_bits(gbw, c) : 0u;
+      const int r = step_row(c) + lane;
+      mrow[c] = r < rlim ? row_bits(gbw, c) : 0u;
     }
     if (lane < head) sm.hmp[lbase + lane] = (uint8_t)mrow[0];
     int cnt = head;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      if (lbase + c * 64 >= rend) break;
+      if (step_row(c) >= rlim) break;
       const bool listed = mrow[c] != 0u && (c > 0 || lane >= head);
       const uint64_t bal = __ballot(listed);
       const int pre = __popcll(bal & ((1ull << lane) - 1ull));
       if (listed) {
-        sm.list[lbase + cnt + pre] = (uint16_t)(lbase + c * 64 + lane);
+        sm.list[lbase + cnt + pre] = (uint16_t)(step_row(c) + lane);
         sm.hmp[lbase + cnt + pre] = (uint8_t)mrow[c];
       }
       cnt += __popcll(bal);
@@ -967,6 +993,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       const int pos0 = tb + 4 * mk;
       uint32_t hm4 = 0;
       if (spm) hm4 = *reinterpret_cast<const uint32_t*>(&sm.hmp[pos0]);
+      uint32_t bkey = 0u;                              // the lane's 4 rows share a 64-row block
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int pos = pos0 + r;
@@ -976,10 +1003,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
         if (ret_lane && pos < lim) {
           if (lg) st_dev(lg + pos, s);                   // stream mode: pos is the row
           if (do_hist) atomicAdd(&sm.u.hist[mr][score_key(s) >> 21], 1u);
+          if (do_blk) bkey = max(bkey, score_key(s));
         }
         tl[t][r] = mem ? s * kLog2e : -LD_INF;
         cm = fmaxf(cm, tl[t][r]);
       }
+      if (do_blk && ret_lane && pos0 < lim) atomicMax(&sm.u.hist[mr][pos0 >> 6], bkey);
     }
     cm = max_xor32(max_xor16(cm));
     const float mn = fmaxf(m_lane, cm);
@@ -1063,6 +1092,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
         if (c.z) atomicAdd(hg + 4 * i + 2, c.z);
         if (c.w) atomicAdd(hg + 4 * i + 3, c.w);
       }
+    }
+  }
+  // ---- block maxima of this split's rows (whole 64-row blocks: splits start at multiples
+  // of 64 rows), as fp32 (NaN only for a block of NaN logits), one store per block
+  if (do_blk && ret) {
+    __syncthreads();
+    const int nblk = p.seq_len / 64, b0 = r0 / 64, nbs = (nrows + 63) / 64;
+    const int rb = b * __popcll(p.retrieval);
+    for (int j = 0; j < G; ++j) {
+      if (!(ret >> j & 1u)) continue;
+      const int h = (hq0 + j) - b * p.Hq;
+      float* dst = p.blk_out + (size_t)(rb + __popcll(p.retrieval & ((1ull << h) - 1ull))) * nblk + b0;
+      for (int i = tid; i < nbs; i += NT) dst[i] = key_score(sm.u.hist[j][i]);
     }
   }
   __syncthreads();   // the LDS union is reused below
@@ -1257,14 +1299,36 @@ hipError_t launch_dgf(const AttnParams& p, dim3 grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+// token-block sets: the 4-wave block instance (the host sets 4 waves for them)
+template <int D, int G, bool F8>
+hipError_t launch_dgf_blk(const AttnParams& p, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_attention<D, G, 4, F8, true>), grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-// This file is compiled once per KV group size (LD_ATTN_G = 1, 2, 4 or 8), so that the
-// kernel instantiations compile in parallel; the dispatch over G is in ld_api.hip.
+// This file is compiled once per KV group size (LD_ATTN_G = 1, 2, 4 or 8) and kind of
+// sets (LD_ATTN_BLK 0: tokens, 1: whole token blocks), so that the kernel instances
+// compile in parallel, each kind in a code object of its own; the dispatch is in
+// ld_api.hip.
 #ifndef LD_ATTN_G
 #error "compile ld_attention.hip with -DLD_ATTN_G=<1|2|4|8>"
 #endif
+#ifndef LD_ATTN_BLK
+#define LD_ATTN_BLK 0
+#endif
 
+#if LD_ATTN_BLK
+template <int G>
+hipError_t launch_attention_blk_g(const AttnParams& p, int D, dim3 grid, hipStream_t st) {
+  if (D == 128) return p.kv_fp8 ? launch_dgf_blk<128, G, true>(p, grid, st) : launch_dgf_blk<128, G, false>(p, grid, st);
+  if (D == 64) return p.kv_fp8 ? launch_dgf_blk<64, G, true>(p, grid, st) : launch_dgf_blk<64, G, false>(p, grid, st);
+  return hipErrorInvalidValue;
+}
+
+template hipError_t launch_attention_blk_g<LD_ATTN_G>(const AttnParams&, int, dim3, hipStream_t);
+#else
 template <int G>
 int64_t attention_capacity_g(int D, int waves, bool fp8) {
   if (D == 128) return fp8 ? capacity_dgf<128, G, true>(waves) : capacity_dgf<128, G, false>(waves);
@@ -1280,5 +1344,6 @@ hipError_t launch_attention_g(const AttnParams& p, int D, dim3 grid, hipStream_t
 
 template int64_t attention_capacity_g<LD_ATTN_G>(int, int, bool);
 template hipError_t launch_attention_g<LD_ATTN_G>(const AttnParams&, int, dim3, hipStream_t);
+#endif
 
 }  // namespace ld

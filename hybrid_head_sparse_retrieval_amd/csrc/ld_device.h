@@ -58,6 +58,13 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The fp32 value of an order-preserving key (the inverse of score_key; key 0 is NaN,
+// and -0.0 comes back as +0.0, which the top-k order does not tell apart).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  if (k == 0u) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // S row of query-head slot `slot`: dense [slot * k_dense, +k_dense), or the CSR row

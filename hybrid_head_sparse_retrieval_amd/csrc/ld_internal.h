@@ -98,6 +98,12 @@ struct AttnParams {
                           // selector clears its flag once it has seen it)
   int32_t* s_out;         // S rows written for selecting heads
   uint32_t* err;          // set when a barrier gave up waiting (never expected)
+  // token-block sets (the last fields, so that the token path's argument layout is the
+  // one it was tuned with): the maxima of each retrieval row's logits over 64-row blocks,
+  // [B*nret][seq_len / 64] (row b * nret + the head's rank among the retrieval heads), or
+  // null; and the block instance (gather waves own interleaved 64-row steps)
+  float* blk_out;
+  int gather_blocks;
 };
 
 // argsTopK over rows. Row slots index the per-row workspace arrays.
@@ -147,8 +153,7 @@ struct CopyParams {
 // Token-block selection (HySparse): block maxima of retrieval rows' logits, and the
 // kept blocks' tokens written as S rows and membership bitmaps.
 struct BlockParams {
-  const float* logits; int seq_len;       // [B*Hq][seq_len] logits of the layer
-  float* scores;                          // [rows][nblk] block maxima
+  float* scores;                          // [rows][nblk] block maxima (written by the attention launch)
   const int32_t* kept;                    // [rows][kblk] kept blocks, ascending
   int rows, nblk, kblk;                   // retrieval rows, blocks per row, blocks kept per row
   int32_t* s_out; int k_dense;            // S rows [B][Hq][k_dense], k_dense = kblk * kBlock
@@ -165,13 +170,13 @@ int64_t attention_capacity(int D, int G, int waves, bool fp8);   // workgroups r
 // unit and the launch
 template <int G> int64_t attention_capacity_g(int D, int waves, bool fp8);
 template <int G> hipError_t launch_attention_g(const AttnParams& p, int D, dim3 grid, hipStream_t st);
+template <int G> hipError_t launch_attention_blk_g(const AttnParams& p, int D, dim3 grid, hipStream_t st);
 hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist);
 // kernels launch_select launches for p (1 to 3)
 int select_launches(const SelParams& p, bool with_hist);
 hipError_t launch_bitmap_build(const BitmapParams& p, int rows, hipStream_t st);
 hipError_t launch_copy_rows(const CopyParams& p, int rows, hipStream_t st);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t st);
-hipError_t launch_block_max(const BlockParams& p, int rows, hipStream_t st);
 // Sliding-window branch of a HySparse sparse layer: o[b*Hq+h] = softmax(q kw^T * scale) vw
 // over the W rows of sequence b in kw/vw [Hkv][B*W][D] (bf16), fp32 out.
 struct WindowParams {
