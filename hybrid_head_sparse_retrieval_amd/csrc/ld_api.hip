@@ -272,20 +272,37 @@ bool choose_splits(int N, int B, int ng_dense, int ng_sparse, double rho, int se
     *ts_d = *ts_s = 256 << (v - 1);
     return true;
   }
+  // Every split of the launch runs at once. A streaming split of d rows visits d rows, a
+  // gathering split of s rows about rho * s, and a streaming group's selection adds
+  // about sel_rows rows' time after its last split; the launch ends with the slower of
+  // the two. For each gather split size, the streaming groups get the smallest split
+  // (a multiple of 64, at least 192 rows) whose grid still fits next to the gathering
+  // groups', and the pair that ends first wins (ties: the smaller splits).
+  double best = 1e300;
+  int bd = 0, bs = 0;
   for (int s = 256; s <= kMaxSplitRows; s += 64) {
-    int d = (int)(rho * s) - sel_rows;
-    d = std::max(192, std::min(kMaxSplitRows, (d + 63) / 64 * 64));
-    if (ng_dense == 0) d = s;
-    if (ng_sparse == 0) { d = s; }
-    if (nsp(d) > kMaxSplits || nsp(s) > kMaxSplits) continue;
-    const int64_t wgs = (int64_t)B * (ng_dense * nsp(d) + ng_sparse * nsp(s));
-    if (wgs <= capacity) {
-      *ts_d = d;
-      *ts_s = s;
-      return true;
+    if (ng_sparse && nsp(s) > kMaxSplits) continue;
+    const int64_t used = ng_sparse ? (int64_t)B * ng_sparse * nsp(s) : 0;
+    if (used > capacity) continue;
+    int d = s;
+    if (ng_dense) {
+      const int64_t room = (capacity - used) / ((int64_t)B * ng_dense);   // splits per streaming group
+      if (room < 1) continue;
+      d = (int)std::max<int64_t>(192, ((N + room - 1) / room + 63) / 64 * 64);
+      if (d > kMaxSplitRows || nsp(d) > kMaxSplits) continue;
     }
+    const double cost = std::max(ng_dense ? (double)(d + sel_rows) : 0.0, ng_sparse ? rho * s : 0.0);
+    if (cost < best) {
+      best = cost;
+      bd = d;
+      bs = ng_sparse ? s : d;
+    }
+    if (!ng_sparse) break;                     // only streaming groups: s plays no part
   }
-  return false;
+  if (!bd) return false;
+  *ts_d = bd;
+  *ts_s = bs;
+  return true;
 }
 
 // Uniform split size when the grid cannot fit one round: the smallest power of two
