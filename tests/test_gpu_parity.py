@@ -413,3 +413,11 @@ def test_both_sides_of_the_in_launch_selection_rule():
         lo, hi = (mid, hi) if inl(mid) else (lo, mid)
     for n in (lo, hi):
         run_layers(1, 32, 8, 128, [n], [full, 1 << 7], 40 + n % 7)
+
+
+@pytest.mark.parametrize("waves", [1, 2])
+def test_both_wave_counts_match_oracle(waves):
+    """The launch runs 4 waves per workgroup unless the caller asks for 8
+    (LD_FLAG_WAVES(2)); both instances of the Llama head shape match the oracle."""
+    ld = _ld()
+    run_layers(1, 32, 8, 128, [4100], wl.seeded_masks(31, 3, 32, 2), 31, extra_flags=ld.flag_waves(waves))
