@@ -685,6 +685,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   const bool do_hist = p.do_topk != 0;
   const bool do_blk = BLK && p.blk_out != nullptr;   // block maxima of the retrieval rows' logits
 
+  {
+    // touch every 64-byte line of the kernel arguments in one round, so that the argument
+    // reads of the prologue hit the scalar cache instead of missing one line after another
+    typedef const volatile uint32_t __attribute__((address_space(4))) karg_u32;
+    karg_u32* ka = (karg_u32*)__builtin_amdgcn_kernarg_segment_ptr();
+    uint32_t t = 0;
+#pragma unroll
+    for (int i = 0; i < (int)sizeof(AttnParams); i += 64) t ^= ka[i / 4];
+    asm volatile("" ::"s"(t));
+  }
   int bid = blockIdx.x;
   const int dense_blocks = p.B * p.ng_dense * p.nsplit_d;
   int split, gi, b, ts;
