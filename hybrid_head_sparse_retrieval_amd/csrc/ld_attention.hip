@@ -1217,12 +1217,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     constexpr int COLS = G * (D / 4);
     int f = -1;                               // selector index
     if (late == 0) {
-      // every split is in: clear the selecting rows' counters, release the others
-      if (tid < G && (selm >> tid & 1u)) st_dev(p.sel_cnt + (size_t)(hq0 + tid) * 2, 0u);
-      if (tid == 0) st_dev(tk, 0u);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      // every split is in: release the others (the selectors once their rows' counters
+      // are clear), and clear the ticket for the next call (ordered after this launch)
+      if (nsel) {
+        if (tid < G && (selm >> tid & 1u)) st_dev(p.sel_cnt + (size_t)(hq0 + tid) * 2, 0u);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
       if (nmg - 1 + nsel) group_publish(rel, nmg - 1 + nsel, (uint64_t)1);
+      if (tid == 0) st_dev(tk, 0u);
     } else if (late < nmg + nsel) {
       group_wait(rel, late - 1, (uint64_t)1, p.err);
       if (tid == 0) st_dev(rel + (size_t)(late - 1) * kRelStride, (uint64_t)0);   // ready for the next call
