@@ -38,10 +38,13 @@
  *  - Workspace: caller-owned device memory of at least ld_workspace_size() bytes
  *    (ld_topk_workspace_size() for ld_topk_select), 256-byte aligned. It must be
  *    zeroed once with ld_workspace_init() before its first use; every completed call
- *    leaves it ready for the next one (its counters back at zero, per-KV-group call
- *    epochs advanced, the S bitmaps that LD_FLAG_S_CHAINED relies on kept). Calls that
- *    share a workspace must be ordered (same stream); concurrent calls need separate
- *    workspaces.
+ *    leaves it ready for the next one (its counters and flags back at zero, the S
+ *    bitmaps that LD_FLAG_S_CHAINED relies on kept). Calls that share a workspace must
+ *    be ordered (same stream); concurrent calls need separate workspaces. No launch
+ *    relies on all of its workgroups being resident at once: workgroups that wait for
+ *    others of the same launch wait only for ones that are running or still to start,
+ *    and are kept to a fraction of what the device holds, so other work on the device
+ *    (other streams, other processes) can slow a call but not stall it.
  *  - Errors: arguments are validated on the host before any launch; a failing check
  *    returns an error code and launches nothing. Launch failures return LD_ERR_HIP.
  *    Faults inside kernels surface at the caller's next synchronisation. Per-sequence
@@ -94,7 +97,9 @@ enum {
      of 64 consecutive tokens with the largest block maxima of its logits (ties to the
      lower block, NaN lowest) and S = their tokens in ascending order. Requires k and
      seq_len to be multiples of 64, uniform sequences (kv_indptr NULL) and dense S
-     (s_indptr NULL); otherwise the call returns LD_ERR_INVALID_ARGUMENT. */
+     (s_indptr NULL); otherwise the call returns LD_ERR_INVALID_ARGUMENT. In a layer
+     without retrieval heads it tells the launch that the sets are whole blocks, which
+     only changes how the work is split (any sets give the same result). */
   LD_FLAG_BLOCK_SELECT = 1u << 3
 };
 /* Optional launch-shape overrides (0 = automatic): rows per attention split =

@@ -72,3 +72,26 @@ def test_block_selection_rejects_unsupported_shapes():
     S = torch.zeros((1, 4, 700), dtype=torch.int32, device=dev)
     with pytest.raises(ld.LycheeDecodeError, match="invalid argument"):
         ld.hybrid_layer(qd, kd, vd, 0xF, 700, None, s_out=S, flags=ld.FLAG_BLOCK_SELECT, workspace=ws)
+
+
+def test_block_hint_on_token_sets_gives_the_same_layer():
+    """LD_FLAG_BLOCK_SELECT on a layer without retrieval heads only changes how the
+    gather work is split among waves: token sets (not whole blocks) give the oracle's
+    layer all the same, including ragged split tails."""
+    ld = _ld()
+    dev = "cuda"
+    B, Hq, Hkv, d, n, k = 1, 8, 2, 128, 5000, 1500
+    S = torch.zeros((B, Hq, k), dtype=torch.int32, device=dev)
+    q0, k0, v0 = wl.random_qkv(B, Hq, Hkv, d, n, 970)
+    ws = ld.Workspace(ld.make_shape(q0.to(dev), k0.to(dev)), k, dev)
+    ld.hybrid_layer(q0.to(dev), k0.to(dev), v0.to(dev), 0xFF, k, None, s_out=S, workspace=ws)
+    q1, k1, v1 = wl.random_qkv(B, Hq, Hkv, d, n, 971)
+    out = ld.hybrid_layer(q1.to(dev), k1.to(dev), v1.to(dev), 0x00, k, S, s_out=S, workspace=ws,
+                          flags=ld.FLAG_BLOCK_SELECT | ld.FLAG_S_CHAINED)
+    torch.cuda.synchronize()
+    Sh = S.cpu().numpy()
+    S_in = {(0, h): Sh[0, h].astype(np.int64) for h in range(Hq)}
+    O_ref, _, _ = orc.hybrid_layer_bf16(wl.bf16_bits(q1), wl.bf16_bits(k1), wl.bf16_bits(v1), [0, n],
+                                        [False] * Hq, [k], S_in)
+    gh.check_outputs(out, O_ref, [(0, h) for h in range(Hq)], "token sets with the block hint")
+    ws.check()
