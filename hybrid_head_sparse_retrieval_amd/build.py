@@ -16,12 +16,14 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblychee_decode.so")
-# (source, object, extra options): the attention kernels compile once per KV group size
+# (source, object, extra options): the attention kernels compile once per KV group size and
+# kind of instance (token sets, block sets, token sets over paged KV)
 UNITS = [("ld_api.hip", "ld_api.o", []), ("ld_select.hip", "ld_select.o", []),
          ("ld_window.hip", "ld_window.o", []), ("ld_tsa.hip", "ld_tsa.o", []),
          ("ld_prefill.hip", "ld_prefill.o", [])] + \
         [("ld_attention.hip", f"ld_attention_g{g}.o", [f"-DLD_ATTN_G={g}"]) for g in (1, 2, 4, 8)] + \
-        [("ld_attention.hip", f"ld_attention_blk_g{g}.o", [f"-DLD_ATTN_G={g}", "-DLD_ATTN_BLK=1"]) for g in (1, 2, 4, 8)]
+        [("ld_attention.hip", f"ld_attention_blk_g{g}.o", [f"-DLD_ATTN_G={g}", "-DLD_ATTN_BLK=1"]) for g in (1, 2, 4, 8)] + \
+        [("ld_attention.hip", f"ld_attention_pg_g{g}.o", [f"-DLD_ATTN_G={g}", "-DLD_ATTN_PG=1"]) for g in (1, 2, 4, 8)]
 SOURCES = sorted({u[0] for u in UNITS})
 
 ARCH = "gfx950"

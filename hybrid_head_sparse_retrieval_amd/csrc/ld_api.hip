@@ -197,28 +197,29 @@ int cu_count() {
 
 namespace ld {
 
-int64_t attention_capacity(int D, int G, int waves, bool fp8) {
-  // cached per device and (D, G, waves, KV format)
-  static std::atomic<int64_t> cache[64][2][4][2][2];
+int64_t attention_capacity(int D, int G, int waves, bool fp8, bool paged) {
+  // cached per device and (D, G, waves, KV format, paged)
+  static std::atomic<int64_t> cache[64][2][4][2][2][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   const int di = D == 128 ? 1 : 0;
   const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
   const int wi = waves == 8 ? 1 : 0;
   const int fi = fp8 ? 1 : 0;
-  int64_t c = cache[dev][di][gi][wi][fi].load(std::memory_order_relaxed);
+  const int pi = paged ? 1 : 0;
+  int64_t c = cache[dev][di][gi][wi][fi][pi].load(std::memory_order_relaxed);
   if (c > 0) return c;
   int64_t per_cu = 0;
   switch (G) {
-    case 1: per_cu = attention_capacity_g<1>(D, waves, fp8); break;
-    case 2: per_cu = attention_capacity_g<2>(D, waves, fp8); break;
-    case 4: per_cu = attention_capacity_g<4>(D, waves, fp8); break;
-    case 8: per_cu = attention_capacity_g<8>(D, waves, fp8); break;
+    case 1: per_cu = paged ? attention_capacity_pg_g<1>(D, waves, fp8) : attention_capacity_g<1>(D, waves, fp8); break;
+    case 2: per_cu = paged ? attention_capacity_pg_g<2>(D, waves, fp8) : attention_capacity_g<2>(D, waves, fp8); break;
+    case 4: per_cu = paged ? attention_capacity_pg_g<4>(D, waves, fp8) : attention_capacity_g<4>(D, waves, fp8); break;
+    case 8: per_cu = paged ? attention_capacity_pg_g<8>(D, waves, fp8) : attention_capacity_g<8>(D, waves, fp8); break;
   }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   c = per_cu * cus;
-  cache[dev][di][gi][wi][fi].store(c, std::memory_order_relaxed);
+  cache[dev][di][gi][wi][fi][pi].store(c, std::memory_order_relaxed);
   return c;
 }
 
@@ -229,6 +230,15 @@ hipError_t launch_attention(const AttnParams& p, int D, int G, dim3 grid, hipStr
       case 2: return launch_attention_blk_g<2>(p, D, grid, st);
       case 4: return launch_attention_blk_g<4>(p, D, grid, st);
       case 8: return launch_attention_blk_g<8>(p, D, grid, st);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (p.page_shift) {
+    switch (G) {
+      case 1: return launch_attention_pg_g<1>(p, D, grid, st);
+      case 2: return launch_attention_pg_g<2>(p, D, grid, st);
+      case 4: return launch_attention_pg_g<4>(p, D, grid, st);
+      case 8: return launch_attention_pg_g<8>(p, D, grid, st);
     }
     return hipErrorInvalidValue;
   }
@@ -437,7 +447,7 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   // arrival at once, so every wait ends. Separate mode (LD_FLAG_SEPARATE_SELECT, or
   // chosen here when the in-launch selectors would be too few for the rows): ticket
   // merge inside the launch and the selection in launches of their own.
-  const int64_t capacity = attention_capacity(D, G, ap.waves, ap.kv_fp8 != 0);
+  const int64_t capacity = attention_capacity(D, G, ap.waves, ap.kv_fp8 != 0, ap.page_shift != 0);
   bool fin = !(flags & LD_FLAG_SEPARATE_SELECT);
   bool in_select = fin && do_topk && !block;
   const int sel_groups = B * ng_dense;

@@ -264,6 +264,39 @@ __device__ __forceinline__ int select_k(const AttnParams& p, int slot, int nb) {
   return min(kk, nb);
 }
 
+// The value of v in this lane's partner of a combining step over aligned groups of 2 OFF
+// lanes: DPP moves inside rows of 16 lanes (after the steps below OFF, the lanes of a
+// group of OFF hold the same partial fold, so the half-row mirror serves as the step of
+// 4), and the row-pair / half-wave swaps across rows.
+template <int OFF>
+__device__ __forceinline__ float partner(float v) {
+  if constexpr (OFF == 1) return dpp_f<0xB1>(v);          // quad_perm [1,0,3,2]
+  else if constexpr (OFF == 2) return dpp_f<0x4E>(v);     // quad_perm [2,3,0,1]
+  else if constexpr (OFF == 4) return dpp_f<0x141>(v);    // row_half_mirror
+  else if constexpr (OFF == 8) return xor8_f(v);
+  else {
+    const int lane = (int)(threadIdx.x & 63u);
+    const auto w = OFF == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                             : __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & OFF) ? w[0] : w[1]);
+  }
+}
+// Folds the online-softmax state (max in log2 units, sum, unnormalised output) of the
+// partner lane into this lane's.
+template <int OFF>
+__device__ __forceinline__ void fold_partner(float& m, float& l, float4& o) {
+  const float m2 = partner<OFF>(m), l2 = partner<OFF>(l);
+  const float ox = partner<OFF>(o.x), oy = partner<OFF>(o.y);
+  const float oz = partner<OFF>(o.z), ow = partner<OFF>(o.w);
+  const float mn = fmaxf(m, m2);
+  const float mu = (mn == -LD_INF) ? 0.f : mn;
+  const float w1 = exp2_fast(m - mu), w2 = exp2_fast(m2 - mu);
+  l = l * w1 + l2 * w2;
+  o.x = o.x * w1 + ox * w2; o.y = o.y * w1 + oy * w2;
+  o.z = o.z * w1 + oz * w2; o.w = o.w * w1 + ow * w2;
+  m = mn;
+}
+
 // Output columns [c_lo, c_hi) (float4 columns, head-major) of the group's active heads
 // from its ns split partials (max in log2 units, sum, unnormalised output), by one
 // workgroup without a barrier: TP adjacent lanes share each column, each folds every
@@ -309,19 +342,13 @@ __device__ __forceinline__ void merge_final(const AttnParams& p, uint32_t act, i
       }
     }
   }
-  // combine the TP lanes of the column (all lanes take part in the shuffles)
-  for (int off = 1; off < TP; off <<= 1) {
-    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
-    const float ox = __shfl_xor(o.x, off), oy = __shfl_xor(o.y, off);
-    const float oz = __shfl_xor(o.z, off), ow = __shfl_xor(o.w, off);
-    const float mn = fmaxf(m, m2);
-    const float mu = (mn == -LD_INF) ? 0.f : mn;
-    const float w1 = exp2_fast(m - mu), w2 = exp2_fast(m2 - mu);
-    l = l * w1 + l2 * w2;
-    o.x = o.x * w1 + ox * w2; o.y = o.y * w1 + oy * w2;
-    o.z = o.z * w1 + oz * w2; o.w = o.w * w1 + ow * w2;
-    m = mn;
-  }
+  // combine the TP lanes of the column (all lanes take part)
+  if (TP > 1) fold_partner<1>(m, l, o);
+  if (TP > 2) fold_partner<2>(m, l, o);
+  if (TP > 4) fold_partner<4>(m, l, o);
+  if (TP > 8) fold_partner<8>(m, l, o);
+  if (TP > 16) fold_partner<16>(m, l, o);
+  if (TP > 32) fold_partner<32>(m, l, o);
   if (live && r == 0) store_o<D>(p, hq0 + j, d0, o, p.v_scale / l);
 }
 
@@ -664,7 +691,7 @@ __device__ __forceinline__ void part_select(uint32_t* hist, uint32_t* cand_lds, 
 // BLK: token-block selection (the sets are whole 64-row blocks): stream mode also keeps
 // the retrieval rows' block maxima, gather mode spreads the blocks over the waves; a
 // separate instance, so that the token path carries none of it.
-template <int D, int G, int NW, bool F8, bool BLK = false>
+template <int D, int G, int NW, bool F8, bool BLK = false, bool PG = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams p) {
   constexpr int NT = 64 * NW;
   constexpr int KCH = D / 32;        // MFMA k-steps per row
@@ -722,7 +749,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     g = (int)__builtin_ctzll(m);
   }
 
-  const bool paged = p.page_shift != 0;
+  // paged KV: an instance of its own for token sets, so that the unpaged one carries no
+  // page arithmetic (the block instance decides at run time)
+  const bool paged = BLK ? p.page_shift != 0 : PG;
   int64_t tok0;
   int nb;
   if (p.kv_indptr) {
@@ -877,6 +906,48 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     }
   };
 
+  // The first chunks (unpaged KV) go through buffer resources over the split's rows: a
+  // position past the valid ones reads zero from past the end of the resource, so the
+  // loads need no per-lane branch. (Around a branch the compiler merged a loaded register
+  // into the register holding the zero, and that copy waited for the load before the
+  // prologue could go on.)
+  const int sbytes = paged ? 0 : nrows * D * EB;
+  const __amdgpu_buffer_rsrc_t krs = rsrc_n(kbase, sbytes), vrs = rsrc_n(vbase, sbytes);
+  constexpr uint32_t kPast = 0x80000000u;     // past the end of every such resource
+  auto load_chunk_b = [&](int c, uint4 (&kd)[TPC][KCH], uint4 (&vd)[RSC][NV]) {
+#pragma unroll
+    for (int t = 0; t < TPC; ++t) {
+      const int tb = tbase(c, t);
+      const int pa = tb + mr;
+      const uint32_t ko = pa < lim ? (uint32_t)((row_of(pa) * D + mk * 8) * EB) : kPast;
+#pragma unroll
+      for (int kk = 0; kk < KCH; ++kk) {
+        if constexpr (F8) {
+          const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(krs, ko + kk * 32, 0, 0);
+          kd[t][kk] = make_uint4(x.x, x.y, 0, 0);
+        } else {
+          const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(krs, ko + kk * 64, 0, 0);
+          kd[t][kk] = make_uint4(x.x, x.y, x.z, x.w);
+        }
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int pv = tb + h2 * 8 + rg;
+        const uint32_t vo = pv < lim ? (uint32_t)((row_of(pv) * D + li * 8) * EB) : kPast;
+#pragma unroll
+        for (int c2 = 0; c2 < NV; ++c2) {
+          if constexpr (F8) {
+            const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(vrs, vo + c2 * 64, 0, 0);
+            vd[t * 2 + h2][c2] = make_uint4(x.x, x.y, 0, 0);
+          } else {
+            const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(vrs, vo + c2 * 128, 0, 0);
+            vd[t * 2 + h2][c2] = make_uint4(x.x, x.y, x.z, x.w);
+          }
+        }
+      }
+    }
+  };
+
   // gather mode: the membership words of the wave's block, issued first so that their
   // wait does not include the head rows' loads
   constexpr int GCH = kMaxSplitRows / (64 * NW);   // 64-row steps of a wave's block
@@ -897,12 +968,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     for (int j = 0; j < G; ++j)
       gbw[j] = ((spm >> j & 1) && ok) ? p.bitmaps[(size_t)(hq0 + j) * p.W + word] : 0u;
   }
-  if (dense) {
+  if (!paged) {
+    // no branch: a chunk past the wave's rows reads zeros
+    load_chunk_b(0, kr[0], vr[0]);            // gather mode: the head rows, no list needed
+    if (dense) load_chunk_b(1, kr[1], vr[1]);
+  } else if (dense) {
     const int nc0 = chunks_of(nrows);
     if (nc0 > 0) load_chunk(0, kr[0], vr[0]);
     if (nc0 > 1) load_chunk(1, kr[1], vr[1]);
   } else if (head > 0) {
-    load_chunk(0, kr[0], vr[0]);              // the head rows: no list needed
+    load_chunk(0, kr[0], vr[0]);
   }
 
   // ---- membership of each row of the tile, and the visit list
@@ -980,7 +1055,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   __syncthreads();
 
   int nchunks = dense ? chunks_of(nlist) : (nl_w + CROWS - 1) / CROWS;
-  if (!dense && nchunks > 1) load_chunk(1, kr[1], vr[1]);   // chunk 0 (the head) is on its way
+  if (!dense && nchunks > 1) {                // chunk 0 (the head) is on its way
+    if (paged) load_chunk(1, kr[1], vr[1]);
+    else load_chunk_b(1, kr[1], vr[1]);
+  }
 
   auto compute_chunk = [&](int c, const uint4 (&kd)[TPC][KCH], const uint4 (&vd)[RSC][NV]) {
     // q . K on the matrix cores
@@ -1292,23 +1370,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   }
 }
 
-template <int D, int G, bool F8>
+template <int D, int G, bool F8, bool PG>
 int64_t capacity_dgf(int waves) {
   int per_cu = 0;
   hipError_t e;
   if (waves == 8)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attention<D, G, 8, F8>, 512, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attention<D, G, 8, F8, false, PG>, 512, 0);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attention<D, G, 4, F8>, 256, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attention<D, G, 4, F8, false, PG>, 256, 0);
   return e == hipSuccess ? per_cu : 0;
 }
 
-template <int D, int G, bool F8>
+template <int D, int G, bool F8, bool PG>
 hipError_t launch_dgf(const AttnParams& p, dim3 grid, hipStream_t st) {
   if (p.waves == 8)
-    hipLaunchKernelGGL((k_attention<D, G, 8, F8>), grid, dim3(512), 0, st, p);
+    hipLaunchKernelGGL((k_attention<D, G, 8, F8, false, PG>), grid, dim3(512), 0, st, p);
   else
-    hipLaunchKernelGGL((k_attention<D, G, 4, F8>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_attention<D, G, 4, F8, false, PG>), grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1322,7 +1400,8 @@ hipError_t launch_dgf_blk(const AttnParams& p, dim3 grid, hipStream_t st) {
 }  // namespace
 
 // This file is compiled once per KV group size (LD_ATTN_G = 1, 2, 4 or 8) and kind of
-// sets (LD_ATTN_BLK 0: tokens, 1: whole token blocks), so that the kernel instances
+// instance (LD_ATTN_BLK 1: sets of whole token blocks; else LD_ATTN_PG 1: token sets
+// over paged KV; neither: token sets over contiguous KV), so that the kernel instances
 // compile in parallel, each kind in a code object of its own; the dispatch is in
 // ld_api.hip.
 #ifndef LD_ATTN_G
@@ -1330,6 +1409,9 @@ hipError_t launch_dgf_blk(const AttnParams& p, dim3 grid, hipStream_t st) {
 #endif
 #ifndef LD_ATTN_BLK
 #define LD_ATTN_BLK 0
+#endif
+#ifndef LD_ATTN_PG
+#define LD_ATTN_PG 0
 #endif
 
 #if LD_ATTN_BLK
@@ -1341,17 +1423,37 @@ hipError_t launch_attention_blk_g(const AttnParams& p, int D, dim3 grid, hipStre
 }
 
 template hipError_t launch_attention_blk_g<LD_ATTN_G>(const AttnParams&, int, dim3, hipStream_t);
+#elif LD_ATTN_PG
+template <int G>
+int64_t attention_capacity_pg_g(int D, int waves, bool fp8) {
+  if (D == 128) return fp8 ? capacity_dgf<128, G, true, true>(waves) : capacity_dgf<128, G, false, true>(waves);
+  return fp8 ? capacity_dgf<64, G, true, true>(waves) : capacity_dgf<64, G, false, true>(waves);
+}
+
+template <int G>
+hipError_t launch_attention_pg_g(const AttnParams& p, int D, dim3 grid, hipStream_t st) {
+  if (D == 128)
+    return p.kv_fp8 ? launch_dgf<128, G, true, true>(p, grid, st) : launch_dgf<128, G, false, true>(p, grid, st);
+  if (D == 64)
+    return p.kv_fp8 ? launch_dgf<64, G, true, true>(p, grid, st) : launch_dgf<64, G, false, true>(p, grid, st);
+  return hipErrorInvalidValue;
+}
+
+template int64_t attention_capacity_pg_g<LD_ATTN_G>(int, int, bool);
+template hipError_t launch_attention_pg_g<LD_ATTN_G>(const AttnParams&, int, dim3, hipStream_t);
 #else
 template <int G>
 int64_t attention_capacity_g(int D, int waves, bool fp8) {
-  if (D == 128) return fp8 ? capacity_dgf<128, G, true>(waves) : capacity_dgf<128, G, false>(waves);
-  return fp8 ? capacity_dgf<64, G, true>(waves) : capacity_dgf<64, G, false>(waves);
+  if (D == 128) return fp8 ? capacity_dgf<128, G, true, false>(waves) : capacity_dgf<128, G, false, false>(waves);
+  return fp8 ? capacity_dgf<64, G, true, false>(waves) : capacity_dgf<64, G, false, false>(waves);
 }
 
 template <int G>
 hipError_t launch_attention_g(const AttnParams& p, int D, dim3 grid, hipStream_t st) {
-  if (D == 128) return p.kv_fp8 ? launch_dgf<128, G, true>(p, grid, st) : launch_dgf<128, G, false>(p, grid, st);
-  if (D == 64) return p.kv_fp8 ? launch_dgf<64, G, true>(p, grid, st) : launch_dgf<64, G, false>(p, grid, st);
+  if (D == 128)
+    return p.kv_fp8 ? launch_dgf<128, G, true, false>(p, grid, st) : launch_dgf<128, G, false, false>(p, grid, st);
+  if (D == 64)
+    return p.kv_fp8 ? launch_dgf<64, G, true, false>(p, grid, st) : launch_dgf<64, G, false, false>(p, grid, st);
   return hipErrorInvalidValue;
 }
 

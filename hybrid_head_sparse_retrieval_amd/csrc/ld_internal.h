@@ -165,12 +165,14 @@ constexpr int kBlock = 64;                // tokens per block
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_attention(const AttnParams& p, int D, int G, dim3 grid, hipStream_t st);
-int64_t attention_capacity(int D, int G, int waves, bool fp8);   // workgroups resident at once
+int64_t attention_capacity(int D, int G, int waves, bool fp8, bool paged);   // workgroups resident at once
 // per KV group size G (ld_attention.hip, one compilation per G): occupancy per compute
 // unit and the launch
 template <int G> int64_t attention_capacity_g(int D, int waves, bool fp8);
 template <int G> hipError_t launch_attention_g(const AttnParams& p, int D, dim3 grid, hipStream_t st);
 template <int G> hipError_t launch_attention_blk_g(const AttnParams& p, int D, dim3 grid, hipStream_t st);
+template <int G> int64_t attention_capacity_pg_g(int D, int waves, bool fp8);
+template <int G> hipError_t launch_attention_pg_g(const AttnParams& p, int D, dim3 grid, hipStream_t st);
 hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist);
 // kernels launch_select launches for p (1 to 3)
 int select_launches(const SelParams& p, bool with_hist);
