@@ -452,14 +452,17 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   bool in_select = fin && do_topk && !block;
   const int sel_groups = B * ng_dense;
   // Merge helpers and selectors wait for their group's last split: up to 8 workgroups
-  // per group merge O (half the budget at most); of the rest, few rows share up to
+  // (4 in a launch that selects) per group merge O (half the budget at most); of the
+  // rest, few rows share up to
   // kMaxParts selectors each (enough for one pass of 16 keys per thread), many rows get
   // one selector each (sel_cap per group; 0: the last arrival selects every row).
   {
     const int64_t budget = capacity / 4;
     const int64_t rows = (int64_t)B * nret;
     const int64_t groups_total = std::max<int64_t>(1, (int64_t)B * ng);
-    ap.merge_w = (int)std::max<int64_t>(1, std::min<int64_t>(8, 1 + budget / 2 / groups_total));
+    // (4 mergers per group when the launch also selects: its retrieval layers took 102.4
+    // against 104.5 us at 128K rows, the merge itself no longer)
+    ap.merge_w = (int)std::max<int64_t>(1, std::min<int64_t>(in_select ? 4 : 8, 1 + budget / 2 / groups_total));
     const int64_t sel_budget = budget - (int64_t)(ap.merge_w - 1) * groups_total;
     const int64_t pass = 16LL * 64 * ap.waves;
     const int64_t want = std::max<int64_t>(2, (N + pass - 1) / pass);
