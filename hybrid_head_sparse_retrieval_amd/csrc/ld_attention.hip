@@ -496,6 +496,11 @@ __device__ __forceinline__ void part_select(uint32_t* hist, uint32_t* cand_lds, 
     above = t.x;
   }
   if (parts > 1 && tid == 0) st_dev(gpub + part, (uint64_t)(uint32_t)above | ((uint64_t)(uint32_t)ncand << 32));
+  // the digit-2 and digit-3 histograms start from zero (the append counts are done with
+  // the LDS); the gather below counts digit 2 as the candidates arrive
+  for (int i = tid; i < kHist2Bins + kHist3Bins; i += NT) hist[i] = 0u;
+  uint32_t* h2 = hist;
+  uint32_t* h3 = hist + kHist2Bins;
   __builtin_amdgcn_s_waitcnt(0);                // this part's candidates and counts are stored
   __syncthreads();
   // ---- the parts meet
@@ -551,7 +556,10 @@ __device__ __forceinline__ void part_select(uint32_t* hist, uint32_t* cand_lds, 
     if (parts > 1) {
 #pragma unroll
       for (int u = 0; u < SPEC; ++u)
-        if (gi + u * tpp < n_q) dstq[gi + u * tpp] = sv[u];
+        if (gi + u * tpp < n_q) {
+          dstq[gi + u * tpp] = sv[u];
+          atomicAdd(&h2[(sv[u] >> 10) & 0x7ffu], 1u);
+        }
     }
     for (int i0 = first; i0 < n_q; i0 += SPEC * tpp) {
 #pragma unroll
@@ -561,7 +569,10 @@ __device__ __forceinline__ void part_select(uint32_t* hist, uint32_t* cand_lds, 
       }
 #pragma unroll
       for (int u = 0; u < SPEC; ++u)
-        if (i0 + gi + u * tpp < n_q) dstq[i0 + gi + u * tpp] = sv[u];
+        if (i0 + gi + u * tpp < n_q) {
+          dstq[i0 + gi + u * tpp] = sv[u];
+          atomicAdd(&h2[(sv[u] >> 10) & 0x7ffu], 1u);
+        }
     }
   }
   // earlier parts' keys above bin b1
@@ -575,22 +586,30 @@ __device__ __forceinline__ void part_select(uint32_t* hist, uint32_t* cand_lds, 
     while (q + 1 < parts && poff[q + 1] <= i) ++q;
     return ld_dev(gcand + (size_t)q * R + (i - poff[q]));
   };
-  uint32_t* h2 = hist;
-  uint32_t* h3 = hist + kHist2Bins;
-  __syncthreads();
-  for (int i = tid; i < kHist2Bins + kHist3Bins; i += NT) hist[i] = 0u;
-  __syncthreads();
-  for (int i = tid; i < total; i += NT) atomicAdd(&h2[(cand_at(i) >> 10) & 0x7ffu], 1u);
-  __syncthreads();
+  // candidates [0, n) of the gathered list in batches: each thread reads CB of them
+  // before it uses any (entries past n read as ~0, which no 21-bit candidate equals)
+  constexpr int CB = 8;
+  auto for_cands = [&](int n, auto&& f) {
+    for (int i0 = tid; i0 < n; i0 += CB * NT) {
+      uint32_t c[CB];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) c[u] = i0 + u * NT < n ? cand_at(i0 + u * NT) : ~0u;
+#pragma unroll
+      for (int u = 0; u < CB; ++u)
+        if (c[u] != ~0u) f(c[u]);
+    }
+  };
+  if (!in_lds) {                                // (in LDS, the gather counted digit 2)
+    for_cands(total, [&](uint32_t c) { atomicAdd(&h2[(c >> 10) & 0x7ffu], 1u); });
+    __syncthreads();
+  }
   find_bin_from_top<kHist2Bins, NT>([&](int i) { return h2[i]; }, k1, wcnt, res);
   const uint32_t b2 = res[0], k2 = k1 - res[1];
   __syncthreads();
   if (tid == 0) { res[0] = 0; res[1] = 0; }
-  __syncthreads();
-  for (int i = tid; i < total; i += NT) {
-    const uint32_t c = cand_at(i);
+  for_cands(total, [&](uint32_t c) {
     if (((c >> 10) & 0x7ffu) == b2) atomicAdd(&h3[c & 0x3ffu], 1u);
-  }
+  });
   __syncthreads();
   find_bin_from_top<kHist3Bins, NT>([&](int i) { return h3[i]; }, k2, wcnt, res);
   const uint32_t t21 = (b2 << 10) | res[0];     // T's bits 20..0
@@ -598,11 +617,10 @@ __device__ __forceinline__ void part_select(uint32_t* hist, uint32_t* cand_lds, 
   const int et = (int)(k2 - res[1]);            // keys equal to T that are kept
   // ---- earlier parts' candidates above / equal to T; this part's keys equal to T
   int gt = 0, eqb = 0;
-  for (int i = tid; i < poff[part]; i += NT) {
-    const uint32_t c = cand_at(i);
+  for_cands(poff[part], [&](uint32_t c) {
     gt += c > t21 ? 1 : 0;
     eqb += c == t21 ? 1 : 0;
-  }
+  });
   int eqm = 0;
   {
     int ps = 0;

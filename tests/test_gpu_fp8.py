@@ -1,6 +1,9 @@
 """Quantised KV (8-bit E4M3 codes with per-tensor scales): with unit scales the layers
-give O and S bit for bit equal to the bf16 path on the decoded values (every E4M3
-value is exact in bf16); with other scales, paged or not, they match the oracle."""
+give S bit for bit equal to the bf16 path on the decoded values (every E4M3 value is
+exact in bf16, so the logits are the same), and O equal up to the order of its fp32
+sums (the E4M3 path takes two 16-row tiles per online-softmax step, the bf16 path one,
+so a running sum can round differently: O may differ in its last bf16 bit); with other
+scales, paged or not, they match the oracle."""
 import numpy as np
 import pytest
 
@@ -57,7 +60,9 @@ def test_fp8_unit_scales_equal_bf16_of_decoded(case):
         ob = ld.hybrid_layer(qd, kb.to(dev), vb.to(dev), mask, k, Sb if l else None, s_out=Sb, flags=flags,
                              workspace=wsb)
         torch.cuda.synchronize()
-        assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)), f"layer {l}: O differs"
+        # at most one bf16 unit in the last place (2^-7 relative) apart, element by element
+        oaf, obf = oa.float(), ob.float()
+        assert torch.all((oaf - obf).abs() <= 2.0 ** -7 * obf.abs() + 1e-7), f"layer {l}: O differs"
         assert torch.equal(Sa, Sb), f"layer {l}: S differs"
     wsa.check()
     wsb.check()
