@@ -622,8 +622,10 @@ def decode_bench(args, torch, ld, DecodeStep, wl, dev, name, cpu_leg):
 # Token Sparse Attention over a prefill (the page's budget range of 512-1024 kept tokens
 # per head, at its 128K context), Llama-3-8B head layout, causal, with the residual form
 # of the scatter (unselected rows keep what the caller wrote, so no zero fill).
+# The page's form has no mask (every kept token attends to every kept token); the causal
+# form (a kept token sees the kept tokens at or before it) is timed beside it.
 TSA_WORKLOADS = {
-    "tsa_llama3_8b_128k": dict(B=1, Hq=32, Hkv=8, d=128, T=131072, k=1024, causal=True),
+    "tsa_llama3_8b_128k": dict(B=1, Hq=32, Hkv=8, d=128, T=131072, k=1024, causal=False),
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, vendor figure
 
@@ -647,10 +649,10 @@ def tsa_bench(args, torch, ld, dev):
     ws = ld.TsaWorkspace(ld.tsa_shape(q, kc, B), k, dev)
     log(f"[bench] {args.workload}: B={B} Hq={Hq} Hkv={Hkv} d={d} T={T} k={k} causal={causal}")
 
-    def layer():
+    def layer(causal=causal):
         ld.tsa_attention(q, kc, vc, scores, k, idx_out=idx, out=out, causal=causal, zero_fill=False, workspace=ws)
 
-    def dense():
+    def dense(causal=causal):
         ld.tsa_attention(q, kc, vc, None, k, idx_out=idx, out=out, causal=causal, zero_fill=False, workspace=ws,
                          given_idx=True, batch=B)
 
@@ -668,17 +670,27 @@ def tsa_bench(args, torch, ld, dev):
 
     us_layer = timed(layer, args.steps)
     us_dense = timed(dense, args.steps)
-    # matrix work of the dense stage: 2 d flops for q.k and 2 d for p.v per allowed pair
-    pairs = B * Hq * (kk * (kk + 1) // 2 if causal else kk * kk)
-    flops = 4.0 * d * pairs
+
+    def dense_flops(c):
+        # matrix work of the dense stage: 2 d flops for q.k and 2 d for p.v per allowed pair
+        return 4.0 * d * B * Hq * (kk * (kk + 1) // 2 if c else kk * kk)
+
+    flops = dense_flops(causal)
     tflops = flops / (us_dense * 1e-6) / 1e12
+    # the other form, timed the same way
+    other = not causal
+    us_layer_o = timed(lambda: layer(other), args.steps)
+    us_dense_o = timed(lambda: dense(other), args.steps)
+    tflops_o = dense_flops(other) / (us_dense_o * 1e-6) / 1e12
     # bytes the layer must move: the scores, the kept rows of q, k, v (k, v once per KV
     # group's union of kept rows) and the scattered output rows
     idx_h = idx.cpu().numpy()
     G = Hq // Hkv
     kv_rows = sum(np.unique(idx_h[b, g * G:(g + 1) * G]).size for b in range(B) for g in range(Hkv))
     layer_bytes_ = scores.numel() * 4 + Hq * B * kk * d * 2 * 2 + kv_rows * d * 2 * 2 + idx_h.size * 4
-    log(f"[bench] layer {us_layer:.1f} us, dense stage {us_dense:.1f} us = {tflops:.1f} TFLOP/s")
+    log(f"[bench] layer {us_layer:.1f} us, dense stage {us_dense:.1f} us = {tflops:.1f} TFLOP/s; "
+        f"{'causal' if other else 'unmasked'} form: layer {us_layer_o:.1f} us, dense {us_dense_o:.1f} us = "
+        f"{tflops_o:.1f} TFLOP/s")
     result = {
         "metric": "token-sparse prefill attention layer time (select + dense + scatter)",
         "value": round(us_layer, 2),
@@ -702,6 +714,10 @@ def tsa_bench(args, torch, ld, dev):
                      "kernel": f"k_tsa (d={d})", "avg_launch_us": round(us_dense, 2),
                      "flops_per_launch": int(flops), "launches_timed": args.steps},
         "cpu_baseline": None,
+        ("causal_form" if other else "unmasked_form"): {
+            "us_layer": round(us_layer_o, 2), "us_dense_stage": round(us_dense_o, 2),
+            "tflops_dense": round(tflops_o, 1), "frac_dense": round(tflops_o / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops_per_launch": int(dense_flops(other))},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = tsa_cpu_baseline(q, kc, vc, scores, k, causal, us_layer, args.cpu_seconds)
