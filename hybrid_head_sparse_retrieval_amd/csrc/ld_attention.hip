@@ -265,9 +265,10 @@ __device__ __forceinline__ int select_k(const AttnParams& p, int slot, int nb) {
 }
 
 // The value of v in this lane's partner of a combining step over aligned groups of 2 OFF
-// lanes: DPP moves inside rows of 16 lanes (after the steps below OFF, the lanes of a
-// group of OFF hold the same partial fold, so the half-row mirror serves as the step of
-// 4), and the row-pair / half-wave swaps across rows.
+// lanes: DPP moves inside rows of 16 lanes, and the row-pair / half-wave swaps across
+// rows. After the steps below OFF, every lane of an aligned group of OFF lanes holds a
+// fold of all of that group's states, so any lane of the neighbouring group serves as
+// the partner: the half-row mirror gives the step of 4.
 template <int OFF>
 __device__ __forceinline__ float partner(float v) {
   if constexpr (OFF == 1) return dpp_f<0xB1>(v);          // quad_perm [1,0,3,2]
