@@ -237,25 +237,6 @@ __device__ __forceinline__ void merge_splits(AttnSmem<D, G, NW>& sm, const AttnP
   __syncthreads();
 }
 
-// Digit 1 of row `slot` (bin b1 and k1, the keys still to take from it) from the sum
-// of its histogram replicas, stored in sel_info for the selection launch.
-template <int D, int G, int NW>
-__device__ __forceinline__ void digit1_info(AttnSmem<D, G, NW>& sm, const AttnParams& p, int slot, int kk) {
-  constexpr int NT = 64 * NW;
-  const int tid = threadIdx.x;
-  uint32_t* hs = sm.u.sel.hist;
-  __syncthreads();    // the LDS union is free
-  if (kk >= 1) hist1_sum(hs, p.hist1, slot);
-  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
-  __syncthreads();
-  if (kk >= 1) find_bin_from_top<kHist1Bins, NT>([&](int i) { return hs[i]; }, (uint32_t)kk, sm.wcnt, sm.res);
-  __syncthreads();
-  if (tid == 0) {
-    p.sel_info[slot * 4 + 0] = sm.res[0];
-    p.sel_info[slot * 4 + 1] = (uint32_t)kk - sm.res[1];
-  }
-}
-
 // k of the row: the row's selection length, at most the sequence length nb.
 __device__ __forceinline__ int select_k(const AttnParams& p, int slot, int nb) {
   int64_t so;
@@ -446,11 +427,14 @@ __device__ __forceinline__ void part_select(uint32_t* hist, uint32_t* cand_lds, 
   };
   if (kk >= 1 && npass) load(0);               // in flight with the histogram sum
   // ---- digit 1 from the row's counts (the sum of the replicas)
-  hist1_sum(hist, p.hist1, slot);
+  hist1_sum<NT>(hist, p.hist1, slot);
   if (tid == 0) { res[0] = 0; res[1] = 0; }
   __syncthreads();
   if (parts == 1) hist1_clear(p.hist1, slot);   // the only reader
-  if (kk < 1) return;
+  if (kk < 1) {                                 // nothing to keep; no part uses the counts
+    if (parts > 1 && part == 0) hist1_clear(p.hist1, slot);
+    return;
+  }
   uint32_t b1, k1;
   {
     uint32_t h1[PB1];
@@ -870,7 +854,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 
   const bool head_lane = mr < G;
   const bool ret_lane = head_lane && ((ret >> mr) & 1u);
-  float* lg = (p.logits && ret_lane) ? p.logits + (size_t)(hq0 + mr) * p.seq_len + r0 : nullptr;
+  // logits of the retrieval rows (stream mode: a visit position is the row), four rows per
+  // lane and tile in one 16-byte store through a resource over the group's rows:
+  // device-coherent (sc1) when selectors of this launch read them back, write-back when
+  // the selection runs in launches of its own (the launch boundary publishes them)
+  const bool lg_on = p.logits != nullptr && ret_lane;
+  const __amdgpu_buffer_rsrc_t lrs = rsrc(p.logits ? p.logits + (size_t)hq0 * p.seq_len : nullptr);
+  const bool lg_vec = (p.seq_len & 3) == 0 && ((uintptr_t)p.logits & 15u) == 0;
+  const uint32_t lg_off = (uint32_t)(((size_t)mr * p.seq_len + r0) * 4);
+  const bool lg_coh = p.fin != 0;
   const float scale = p.scale;
 
   float m_lane = -LD_INF, l_lane = 0.f;     // running max / sum of head mr (lanes mr < G)
@@ -901,10 +893,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 #pragma unroll
       for (int kk = 0; kk < KCH; ++kk) {
         if constexpr (F8) {
-          const uint2 c = va ? *reinterpret_cast<const uint2*>(kp + kk * 32) : make_uint2(0, 0);
+          const uint2 c = va ? ld_stream8(kp + kk * 32) : make_uint2(0, 0);
           kd[t][kk] = make_uint4(c.x, c.y, 0, 0);
         } else {
-          kd[t][kk] = va ? *reinterpret_cast<const uint4*>(kp + kk * 64) : make_uint4(0, 0, 0, 0);
+          kd[t][kk] = va ? ld_stream16(kp + kk * 64) : make_uint4(0, 0, 0, 0);
         }
       }
 #pragma unroll
@@ -915,10 +907,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 #pragma unroll
         for (int c2 = 0; c2 < NV; ++c2) {
           if constexpr (F8) {
-            const uint2 c = vv ? *reinterpret_cast<const uint2*>(vp + c2 * 64) : make_uint2(0, 0);
+            const uint2 c = vv ? ld_stream8(vp + c2 * 64) : make_uint2(0, 0);
             vd[t * 2 + h2][c2] = make_uint4(c.x, c.y, 0, 0);
           } else {
-            vd[t * 2 + h2][c2] = vv ? *reinterpret_cast<const uint4*>(vp + c2 * 128) : make_uint4(0, 0, 0, 0);
+            vd[t * 2 + h2][c2] = vv ? ld_stream16(vp + c2 * 128) : make_uint4(0, 0, 0, 0);
           }
         }
       }
@@ -942,10 +934,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 #pragma unroll
       for (int kk = 0; kk < KCH; ++kk) {
         if constexpr (F8) {
-          const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(krs, ko + kk * 32, 0, 0);
+          const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(krs, ko + kk * 32, 0, kNt);
           kd[t][kk] = make_uint4(x.x, x.y, 0, 0);
         } else {
-          const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(krs, ko + kk * 64, 0, 0);
+          const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(krs, ko + kk * 64, 0, kNt);
           kd[t][kk] = make_uint4(x.x, x.y, x.z, x.w);
         }
       }
@@ -956,10 +948,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 #pragma unroll
         for (int c2 = 0; c2 < NV; ++c2) {
           if constexpr (F8) {
-            const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(vrs, vo + c2 * 64, 0, 0);
+            const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(vrs, vo + c2 * 64, 0, kNt);
             vd[t * 2 + h2][c2] = make_uint4(x.x, x.y, 0, 0);
           } else {
-            const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(vrs, vo + c2 * 128, 0, 0);
+            const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(vrs, vo + c2 * 128, 0, kNt);
             vd[t * 2 + h2][c2] = make_uint4(x.x, x.y, x.z, x.w);
           }
         }
@@ -1101,19 +1093,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       uint32_t hm4 = 0;
       if (spm) hm4 = *reinterpret_cast<const uint32_t*>(&sm.hmp[pos0]);
       uint32_t bkey = 0u;                              // the lane's 4 rows share a 64-row block
+      u32x4_t lv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int pos = pos0 + r;
         const uint32_t hm = spm ? ((hm4 >> (8 * r)) & 0xffu) : ret;
         const bool mem = head_lane && pos < lim && ((hm >> mr) & 1u);
         const float s = dacc[t][r] * scale;
+        lv[r] = __float_as_uint(s);
         if (ret_lane && pos < lim) {
-          if (lg) st_dev(lg + pos, s);                   // stream mode: pos is the row
           if (do_hist) atomicAdd(&sm.u.hist[mr][score_key(s) >> 21], 1u);
           if (do_blk) bkey = max(bkey, score_key(s));
         }
         tl[t][r] = mem ? s * kLog2e : -LD_INF;
         cm = fmaxf(cm, tl[t][r]);
+      }
+      if (lg_on && pos0 < lim) {
+        const uint32_t o = lg_off + (uint32_t)pos0 * 4u;
+        if (lg_vec && pos0 + 3 < lim) {
+          if (lg_coh) __builtin_amdgcn_raw_buffer_store_b128(lv, lrs, o, 0, kSc1);
+          else __builtin_amdgcn_raw_buffer_store_b128(lv, lrs, o, 0, 0);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (pos0 + r < lim) {
+              if (lg_coh) __builtin_amdgcn_raw_buffer_store_b32(lv[r], lrs, o + 4u * r, 0, kSc1);
+              else __builtin_amdgcn_raw_buffer_store_b32(lv[r], lrs, o + 4u * r, 0, 0);
+            }
+          }
+        }
       }
       if (do_blk && ret_lane && pos0 < lim) atomicMax(&sm.u.hist[mr][pos0 >> 6], bkey);
     }
@@ -1377,16 +1385,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     merge_splits<D, G, NW, true>(sm, p, act, hq0, p.l1_ml, p.l1_acc, p.P1, 0, nu, nullptr, nullptr, 0);
   }
 
-  // ---- first selection digit for each retrieval head (fused histogram complete)
-  if (do_hist) {
-    for (int j = 0; j < G; ++j) {
-      if (!(ret >> j & 1u)) continue;
-      const int slot = hq0 + j;
-      digit1_info<D, G, NW>(sm, p, slot, select_k(p, slot, nb));
-      hist1_clear(p.hist1, slot);
-      __syncthreads();
-    }
-  }
+  // (the selection launches that follow read the fused digit-1 histogram: each of their
+  // workgroups finds the first digit from it while its own scores load)
 }
 
 template <int D, int G, bool F8, bool PG>

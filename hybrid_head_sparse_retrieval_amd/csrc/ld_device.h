@@ -294,6 +294,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
 constexpr int kSc1 = 16;   // cache-policy bit of sc1 for buffer instructions
+constexpr int kNt = 2;     // cache-policy bit of nt (streaming: read once) for buffer instructions
+
+typedef unsigned int u32x2_v __attribute__((ext_vector_type(2)));
+// KV rows are read once per launch: loads with the nontemporal hint, which keeps them from
+// displacing the lines that are reused (partials, membership words, Q)
+__device__ __forceinline__ uint4 ld_stream16(const char* p) {
+  const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ uint2 ld_stream8(const char* p) {
+  const u32x2_v x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_v*>(p));
+  return make_uint2(x.x, x.y);
+}
 // The same over `bytes` bytes from `base`: loads past them return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_n(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
@@ -311,11 +324,13 @@ __device__ __forceinline__ void hist1_clear(uint32_t* h1, int slot) {
   uint4* r = reinterpret_cast<uint4*>(h1 + (size_t)slot * kRep * kHist1Bins);
   for (int i = threadIdx.x; i < kRep * kHist1Bins / 4; i += (int)blockDim.x) r[i] = make_uint4(0u, 0u, 0u, 0u);
 }
+// NT: the workgroup's thread count (it sizes the thread's register columns).
+template <int NT>
 __device__ __forceinline__ void hist1_sum(uint32_t* lds, const uint32_t* h1, int slot) {
   const __amdgpu_buffer_rsrc_t r = rsrc(h1 + (size_t)slot * kRep * kHist1Bins);
   // every load of the thread's columns is issued before the first sum
-  constexpr int kMaxCols = 4;                  // column groups per thread (blockDim.x >= 128)
-  const int nt = (int)blockDim.x;
+  constexpr int kMaxCols = (kHist1Bins / 4 + NT - 1) / NT;   // column groups per thread
+  constexpr int nt = NT;
   u32x4_t a[kMaxCols][kRep];
 #pragma unroll
   for (int c = 0; c < kMaxCols; ++c) {

@@ -6,9 +6,10 @@
 // (digit 1 = bits 31..21, digit 2 = bits 20..10, digit 3 = bits 9..0), over spans
 // of 16384 scores, one 1024-thread workgroup per span:
 //   1. digit-1 histogram of the row (fused into the attention kernel for retrieval
-//      heads, or k_sel_hist over 512-score chunks for standalone rows); the last
-//      workgroup of the row picks the bin b1 holding the k-th largest key;
-//   2. k_sel_cand: each span counts its keys above bin b1 and stores its keys of bin
+//      heads, or k_sel_hist over 512-score chunks for standalone rows);
+//   2. k_sel_cand: each span sums the row's digit-1 histogram while its scores load and
+//      picks the bin b1 holding the k-th largest key (the last span of the row clears
+//      the histogram); it counts its keys above bin b1 and stores its keys of bin
 //      b1 (the candidates) with their digit-2 histogram; the last span of the row
 //      finds digit 2, then from the candidates digit 3 (threshold key T), the highest
 //      kept index i_tie among the keys equal to T (ties go to lower indices) and the
@@ -94,9 +95,6 @@ __device__ __forceinline__ void hist1_whole(const float* __restrict__ s, uint32_
 
 __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
   __shared__ uint32_t hist[kHist1Bins];
-  __shared__ int tmp[4];
-  __shared__ uint32_t res[2];
-  __shared__ int flag;
   const int r = blockIdx.x / p.C, c = blockIdx.x % p.C;
   const RowView v = row_view(p, r);
   const int hc = p.hchunk;
@@ -124,18 +122,6 @@ __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
   uint32_t* gh = hist1_mine(p.hist1, v.slot);
   for (int i = tid; i < kHist1Bins; i += kThreads)
     if (hist[i]) atomicAdd(gh + i, hist[i]);
-  const uint32_t nch = (uint32_t)((v.n + hc - 1) / hc);
-  if (!arrive_last(p.tickets + v.slot, nch, &flag)) return;
-  if (tid == 0) { res[0] = 0; res[1] = 0; p.tickets[v.slot] = 0; }
-  __syncthreads();    // every thread is done with its own counts in hist
-  hist1_sum(hist, p.hist1, v.slot);
-  __syncthreads();
-  find_bin_from_top<kHist1Bins, kThreads>([&](int i) { return hist[i]; }, (uint32_t)v.k, tmp, res);
-  if (tid == 0) {
-    p.sel_info[v.slot * 4 + 0] = res[0];
-    p.sel_info[v.slot * 4 + 1] = (uint32_t)v.k - res[1];
-  }
-  hist1_clear(p.hist1, v.slot);
 }
 
 // ------------------------------------------------ short standalone rows
@@ -581,20 +567,30 @@ __global__ __launch_bounds__(kSpanThreads) void k_sel_cand(const SelParams p) {
   const int r = blockIdx.x / p.C, c = blockIdx.x % p.C;
   const RowView v = row_view(p, r);
   const int n = v.n, kk = v.k;
-  if (n < 1 || kk < 1) return;
+  if (n < 1) return;
+  if (kk < 1) {                                 // an empty row of a CSR S: nothing to keep,
+    if (c == 0) hist1_clear(p.hist1, v.slot);   // but its histogram may hold counts
+    return;
+  }
   const int nsp = (n + kSelSpan - 1) / kSelSpan;
   if (c >= nsp) return;
   const int tid = threadIdx.x;
   const int slot = v.slot;
-  const uint32_t b1 = p.sel_info[slot * 4 + 0];
-  const uint32_t k1 = p.sel_info[slot * 4 + 1];
   uint64_t* cand = p.cand + (size_t)slot * p.ncap;
   uint32_t* gh2 = p.hist2 + (size_t)slot * kHist2Bins;
   uint32_t key[kSpanRounds][4];
   load_span(v.sc, n, c * kSelSpan, tid, key);
-  span_candidates(p, slot, c, n, b1, key, cand, gh2, sm);
+  // digit 1 from the row's histogram (the sum of its replicas), while the scores load
+  hist1_sum<kSpanThreads>(sm.hist, p.hist1, slot);
+  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
+  __syncthreads();
+  find_bin_from_top<kHist1Bins, kSpanThreads>([&](int i) { return sm.hist[i]; }, (uint32_t)kk, sm.tmp, sm.res);
+  const uint32_t b1 = sm.res[0];
+  const uint32_t k1 = (uint32_t)kk - sm.res[1];
+  span_candidates(p, slot, c, n, b1, key, cand, gh2, sm);   // (find_bin ends with a barrier)
   if (!arrive_last(p.tickets + slot, (uint32_t)nsp, &sm.flag)) return;
   if (tid == 0) p.tickets[slot] = 0u;
+  hist1_clear(p.hist1, slot);                   // every span has read it
   uint32_t T, i_tie;
   row_threshold(p, slot, nsp, b1, k1, gh2, true, cand, sm, T, i_tie);
   (void)span_offsets(nsp, sm, p.span_off + (size_t)slot * p.C, -1);

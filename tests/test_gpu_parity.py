@@ -371,6 +371,40 @@ def test_csr_rows_are_clipped_to_the_s_buffer():
                     assert np.array_equal(g[a:e], want), (l, b, h)
 
 
+@pytest.mark.parametrize("flags", [0, 4])   # selection in the attention launch, or in launches of its own
+def test_empty_csr_row_leaves_no_counts_behind(flags):
+    """A retrieval row whose CSR S row is empty keeps nothing, yet the attention launch
+    counts its scores into the first-digit histogram; those counts must be gone before
+    the next call on the same workspace selects that row (LycheeDecode summary page,
+    method step 3: each call's argsTopK sees only its own scores)."""
+    ld = _ld()
+    dev = "cuda"
+    B, Hq, Hkv, d, N, k = 1, 4, 4, 64, 3000, 300
+    shape = None
+    ws = None
+    for call, rows in enumerate([[k, 0, k, k], [k, k, k, k]]):
+        ind_h = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+        s_indptr = torch.as_tensor(ind_h, device=dev)
+        S = torch.full((int(ind_h[-1]),), -1, dtype=torch.int32, device=dev)
+        qc, kc, vc = wl.random_qkv(B, Hq, Hkv, d, N, 1300 + call)
+        q, kk, vv = qc.to(dev), kc.to(dev), vc.to(dev)
+        if ws is None:
+            shape = ld.make_shape(q, kk, None, N)
+            ws = ld.Workspace(shape, k, dev)
+        scores = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device=dev)
+        out = torch.empty_like(q)
+        ld.hybrid_layer(q, kk, vv, 0xF, k, None, s_out=S, s_indptr=s_indptr, scores_out=scores, out=out,
+                        flags=flags, workspace=ws, seq_len=N)
+        torch.cuda.synchronize()
+        g = S.cpu().numpy()
+        sc = scores.cpu().numpy()
+        for h in range(Hq):
+            a, e = int(ind_h[h]), int(ind_h[h + 1])
+            if e > a:
+                assert np.array_equal(g[a:e], orc.select_topk_f32(sc[0, h], e - a)), (call, h)
+    ws.check()
+
+
 def _plan_for(ld, Hq, Hkv, d, N, mask, s_in=True, flags=0):
     dev = "cuda"
     q = torch.empty((1, Hq, d), dtype=torch.bfloat16, device=dev)
