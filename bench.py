@@ -104,14 +104,19 @@ def layer_bytes(w, l, S_in, d, kv_elem=2):
     return kv + qo, kv + qo + s_io
 
 
-ATTN_SOURCE = os.path.join(ROOT, "hybrid_head_sparse_retrieval_amd", "csrc", "ld_attention.hip")
+# the attention kernel's translation unit: its source and the headers it includes
+ATTN_SOURCES = [os.path.join(ROOT, "hybrid_head_sparse_retrieval_amd", "csrc", f)
+                for f in ("ld_attention.hip", "ld_device.h", "ld_internal.h")]
 COPY_BYTES = 1 << 30
 
 
-def source_hash(path=ATTN_SOURCE):
+def source_hash(paths=ATTN_SOURCES):
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_path(workload):

@@ -893,7 +893,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 #pragma unroll
       for (int kk = 0; kk < KCH; ++kk) {
         if constexpr (F8) {
-          const uint2 c = va ? ld_stream8(kp + kk * 32) : make_uint2(0, 0);
+          const uint2 c = va ? *reinterpret_cast<const uint2*>(kp + kk * 32) : make_uint2(0, 0);
           kd[t][kk] = make_uint4(c.x, c.y, 0, 0);
         } else {
           kd[t][kk] = va ? ld_stream16(kp + kk * 64) : make_uint4(0, 0, 0, 0);
@@ -907,7 +907,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 #pragma unroll
         for (int c2 = 0; c2 < NV; ++c2) {
           if constexpr (F8) {
-            const uint2 c = vv ? ld_stream8(vp + c2 * 64) : make_uint2(0, 0);
+            const uint2 c = vv ? *reinterpret_cast<const uint2*>(vp + c2 * 64) : make_uint2(0, 0);
             vd[t * 2 + h2][c2] = make_uint4(c.x, c.y, 0, 0);
           } else {
             vd[t * 2 + h2][c2] = vv ? ld_stream16(vp + c2 * 128) : make_uint4(0, 0, 0, 0);
@@ -934,7 +934,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 #pragma unroll
       for (int kk = 0; kk < KCH; ++kk) {
         if constexpr (F8) {
-          const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(krs, ko + kk * 32, 0, kNt);
+          const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(krs, ko + kk * 32, 0, 0);
           kd[t][kk] = make_uint4(x.x, x.y, 0, 0);
         } else {
           const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(krs, ko + kk * 64, 0, kNt);
@@ -948,7 +948,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 #pragma unroll
         for (int c2 = 0; c2 < NV; ++c2) {
           if constexpr (F8) {
-            const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(vrs, vo + c2 * 64, 0, kNt);
+            const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(vrs, vo + c2 * 64, 0, 0);
             vd[t * 2 + h2][c2] = make_uint4(x.x, x.y, 0, 0);
           } else {
             const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(vrs, vo + c2 * 128, 0, kNt);

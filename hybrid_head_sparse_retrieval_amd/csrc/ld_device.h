@@ -296,16 +296,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
 constexpr int kSc1 = 16;   // cache-policy bit of sc1 for buffer instructions
 constexpr int kNt = 2;     // cache-policy bit of nt (streaming: read once) for buffer instructions
 
-typedef unsigned int u32x2_v __attribute__((ext_vector_type(2)));
-// KV rows are read once per launch: loads with the nontemporal hint, which keeps them from
-// displacing the lines that are reused (partials, membership words, Q)
+// bf16 KV rows are read once per launch: loads with the nontemporal hint, which keeps them
+// from displacing the lines that are reused (partials, membership words, Q). (E4M3 rows
+// keep plain loads: there four loads of a wave share each 128-byte line of K, and with the
+// hint the later ones fetched it again, 32K steps 1.20 against 1.12 ms.)
 __device__ __forceinline__ uint4 ld_stream16(const char* p) {
   const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(x.x, x.y, x.z, x.w);
-}
-__device__ __forceinline__ uint2 ld_stream8(const char* p) {
-  const u32x2_v x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_v*>(p));
-  return make_uint2(x.x, x.y);
 }
 // The same over `bytes` bytes from `base`: loads past them return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_n(const void* base, int bytes) {
