@@ -71,6 +71,17 @@ def test_heavy_ties_at_threshold():
         _check(x, k)
 
 
+@pytest.mark.parametrize("n", [4097, 30001, 32768])
+def test_heavy_ties_within_two_spans(n):
+    # one or two spans: many keys equal to the k-th value, NaN among them; only the lowest
+    # indices among the ties are kept
+    rng = _rng(n)
+    x = rng.integers(0, 5, size=(3, n)).astype(np.float32)
+    x[1, ::7] = np.nan
+    for k in (1, n // 5, n // 2, n - 3):
+        _check(x, k)
+
+
 def test_near_ties_differ_in_last_bit():
     base = np.float32(0.7)
     n = 3000
@@ -104,10 +115,10 @@ def test_repeated_calls_reuse_workspace():
 
 
 def test_more_spans_than_resident_workgroups():
-    # 300 rows of two 16384-score spans: more workgroups than the device holds at once
+    # 300 rows of three 16384-score spans: more workgroups than the device holds at once
     # (the selection launches assume nothing about residency)
     rng = _rng(5)
-    x = rng.normal(size=(300, 17000)).astype(np.float32)
+    x = rng.normal(size=(300, 40000)).astype(np.float32)
     x[7, :] = 1.0                                   # a constant row: ties everywhere
     x[9, 100:200] = np.nan
     _check(x, 5100, with_vals=False)
@@ -121,6 +132,8 @@ def test_more_spans_than_resident_workgroups():
     (3, 131072, 39321),    # 2048-score chunks: one round of 2
     (50, 5000, 1500),      # 1024-score chunks: one float4 per thread, the ragged last chunk scalar
     (40, 16385, 5000),     # rows whose starts are not 16-byte aligned take the scalar loads
+    (12, 40961, 12000),    # the same over three spans
+    (6, 33000, 9000),      # a ragged last chunk over three spans
 ])
 def test_digit1_chunk_sizes(rows, n, k):
     _check(_rng(7 + rows).normal(size=(rows, n)).astype(np.float32), k, with_vals=False)
