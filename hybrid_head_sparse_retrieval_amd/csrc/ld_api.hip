@@ -273,7 +273,9 @@ int choose_waves(uint32_t flags) {
 // when the group selects inside the launch, the selection's fixed latency counted as
 // `sel_rows` rows of streaming. The smallest ts_s that fits gives the most parallelism.
 // Returns false when no choice fits (the caller then takes one uniform size).
-constexpr int kSelRows = 512;
+// (sel_rows = 256 rows measured best: 32K steps 1.184 / 1.179 / 1.190 / 1.191 / 1.237 ms and
+// 128K steps 3.210 / 3.206 / 3.211 / 3.284 / 3.328 ms for 128 / 256 / 384 / 512 / 768)
+constexpr int kSelRows = 256;
 // A streamed row of a group that serves a retrieval head costs about 1.12 visited rows of
 // a gathering group: it also writes the row's logits and counts them in the fused
 // histogram (measured per workgroup at 128K rows: 21.9 against 24.5 rows per us).
