@@ -642,7 +642,7 @@ ld_status ld_hysparse_layer(const ld_shape* shape, const void* q, const void* k_
   if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return LD_ERR_INVALID_ARGUMENT;
   if (!aligned16(k_window) || !aligned16(v_window)) return LD_ERR_INVALID_ARGUMENT;
-  if (flags & ~(uint32_t)LD_FLAG_S_CHAINED) return LD_ERR_INVALID_ARGUMENT;
+  if (flags & ~(uint32_t)(LD_FLAG_S_CHAINED | LD_FLAG_BLOCK_SELECT)) return LD_ERR_INVALID_ARGUMENT;
   if (k < 1 || k > shape->seq_len) return LD_ERR_INVALID_ARGUMENT;
   if (!workspace || workspace_bytes < H.total || ((uintptr_t)workspace & 15u)) return LD_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);

@@ -83,6 +83,7 @@ struct AttnSmem {
   int cnt4[NW][2];
   int ncnt[kRep];                    // candidate counts of the sub-lists
   int pages[kMaxSplitRows / 16 + 1]; // paged KV: page ids of the split's rows
+  uint16_t blk[kMaxSplitRows / 64];  // block sets: the split's share of its group's union of 64-row blocks
   float pl[NW][kChunkRows][G];       // per wave: probabilities of the chunk's rows (up to)
   union {
     uint32_t hist[G][kHist1Bins];
@@ -776,8 +777,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   }
   const int nsplit_b = (nb + ts - 1) / ts;
   if (nb <= 0 || split >= nsplit_b) return;
-  const int r0 = split * ts;
-  const int nrows = min(ts, nb - r0);
+  int r0 = split * ts;
+  int nrows = min(ts, nb - r0);
 
   // Head roles inside the group (bit j <-> query head g*G + j).
   uint32_t act = 0, ret = 0;
@@ -802,6 +803,69 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
       qb[kk] = make_uint4(0, 0, 0, 0);
   }
 
+  // ---- block sets (the caller's hint; unpaged KV, at most 512 blocks per wave): a
+  // gathering split takes an equal share of its group's union of selected 64-row blocks
+  // instead of a range of rows, so that the group's splits visit about the same number
+  // of rows however the blocks fall (a few blocks per split leave contiguous ranges very
+  // unequal). Thread t reads the membership words of blocks 8t .. 8t + 7 of the group's
+  // sparse heads, the workgroup ranks the union's blocks, and the split keeps ranks
+  // [U * split / nsplit_b, U * (split + 1) / nsplit_b) in sm.blk; local row r of the
+  // split is then row 64 * blk[r / 64] + r % 64 of the sequence. Every row of a kept block
+  // is visited, each head masked by its own membership.
+  bool bsh = false;
+  if constexpr (BLK) {
+    bsh = !dense && !paged && p.gather_blocks != 0 && nb <= 8 * 64 * NT;
+    if (bsh) {
+      const int nblk = (nb + 63) >> 6;
+      uint32_t wd[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) wd[i] = 0u;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (!(spm >> j & 1)) continue;
+        const __amdgpu_buffer_rsrc_t rb = rsrc_n(p.bitmaps + (size_t)(hq0 + j) * p.W, p.W * 4);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rb, (16 * tid + 4 * q4) * 4, 0, 0);
+          wd[4 * q4 + 0] |= x.x; wd[4 * q4 + 1] |= x.y; wd[4 * q4 + 2] |= x.z; wd[4 * q4 + 3] |= x.w;
+        }
+      }
+      uint32_t u = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) u |= (uint32_t)(8 * tid + i < nblk && (wd[2 * i] | wd[2 * i + 1]) != 0u) << i;
+      int wt;
+      const int pre = wave_excl_scan(__popc(u), wt);
+      if (lane == 0) sm.wcnt[wave] = wt;
+      __syncthreads();
+      int below = 0, U = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int c = sm.wcnt[w];
+        below += w < wave ? c : 0;
+        U += c;
+      }
+      const int lo = (int)((int64_t)U * split / nsplit_b), hi = (int)((int64_t)U * (split + 1) / nsplit_b);
+      int rank = below + pre;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (u >> i & 1u) {
+          if (rank >= lo && rank < hi) sm.blk[rank - lo] = (uint16_t)(8 * tid + i);
+          ++rank;
+        }
+      }
+      r0 = 0;
+      nrows = (hi - lo) * 64;                 // at most ts: a share holds at most ts / 64 blocks
+      __syncthreads();
+    }
+  }
+  // row of the sequence, from r0, of local row r of the split
+  auto lrow = [&](int r) -> int {
+    if constexpr (BLK) {
+      if (bsh) return ((int)sm.blk[(r >> 6) & (kMaxSplitRows / 64 - 1)] << 6) + (r & 63);
+    }
+    return r;
+  };
+
   // ---- per-wave streaming state (tiles wave, wave+4, ...; TPC tiles per chunk)
   constexpr int EB = F8 ? 1 : 2;              // bytes per K/V element
   const char* kbase = static_cast<const char*>(p.kc) + ((size_t)g * p.kv_head_stride + (size_t)(tok0 + r0) * D) * EB;
@@ -821,7 +885,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   }
   // element offset of row r of the split from kbase / vbase (paged: from the head's pool)
   auto row_off = [&](int r) -> ptrdiff_t {
-    if (!paged) return (ptrdiff_t)r * D;
+    if (!paged) return (ptrdiff_t)lrow(r) * D;
     const int i = r0 + r;
     return (((ptrdiff_t)sm.pages[(i >> pshift) - pg0] << pshift) + (i & pmask) - r0) * D;
   };
@@ -922,7 +986,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
   // loads need no per-lane branch. (Around a branch the compiler merged a loaded register
   // into the register holding the zero, and that copy waited for the load before the
   // prologue could go on.)
-  const int sbytes = paged ? 0 : nrows * D * EB;
+  const int sbytes = paged ? 0 : (bsh ? nb : nrows) * D * EB;
   const __amdgpu_buffer_rsrc_t krs = rsrc_n(kbase, sbytes), vrs = rsrc_n(vbase, sbytes);
   constexpr uint32_t kPast = 0x80000000u;     // past the end of every such resource
   auto load_chunk_b = [&](int c, uint4 (&kd)[TPC][KCH], uint4 (&vd)[RSC][NV]) {
@@ -930,7 +994,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     for (int t = 0; t < TPC; ++t) {
       const int tb = tbase(c, t);
       const int pa = tb + mr;
-      const uint32_t ko = pa < lim ? (uint32_t)((row_of(pa) * D + mk * 8) * EB) : kPast;
+      const uint32_t ko = pa < lim ? (uint32_t)((lrow(row_of(pa)) * D + mk * 8) * EB) : kPast;
 #pragma unroll
       for (int kk = 0; kk < KCH; ++kk) {
         if constexpr (F8) {
@@ -944,7 +1008,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int pv = tb + h2 * 8 + rg;
-        const uint32_t vo = pv < lim ? (uint32_t)((row_of(pv) * D + li * 8) * EB) : kPast;
+        const uint32_t vo = pv < lim ? (uint32_t)((lrow(row_of(pv)) * D + li * 8) * EB) : kPast;
 #pragma unroll
         for (int c2 = 0; c2 < NV; ++c2) {
           if constexpr (F8) {
@@ -969,8 +1033,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
     bool ok;
     if constexpr (BLK) {
       const int srow = step_row(lane >> 1) + 32 * (lane & 1);   // lanes 2c, 2c+1: the words of step c
-      word = (r0 + srow) >> 5;
-      ok = lane < 2 * GCH && srow < (ilv ? nrows : rend) && word < p.W;
+      const bool in = lane < 2 * GCH && srow < (ilv ? nrows : rend);
+      word = in ? (r0 + lrow(srow)) >> 5 : 0;
+      ok = in && word < p.W;
     } else {
       word = ((r0 + lbase) >> 5) + lane;
       ok = lane < 2 * GCH && lbase + 32 * lane < rend && word < p.W;
@@ -1044,7 +1109,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attention(const AttnParams 
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int r = step_row(c) + lane;
-      mrow[c] = r < rlim ? row_bits(gbw, c) : 0u;
+      // (a block share's last block may reach past the sequence: its rows there are no members)
+      mrow[c] = (r < rlim && (!bsh || lrow(r) < nb)) ? row_bits(gbw, c) : 0u;
     }
     if (lane < head) sm.hmp[lbase + lane] = (uint8_t)mrow[0];
     int cnt = head;

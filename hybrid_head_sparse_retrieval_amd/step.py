@@ -15,7 +15,7 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (FLAG_S_CHAINED, HySparseWorkspace, Workspace, hybrid_layer, hybrid_layer_plan,
+from . import (FLAG_BLOCK_SELECT, FLAG_S_CHAINED, HySparseWorkspace, Workspace, hybrid_layer, hybrid_layer_plan,
                hysparse_layer, make_shape)
 
 
@@ -81,7 +81,8 @@ class DecodeStep:
             if self.s_indptr is not None:
                 raise ValueError("window branches are set up for dense S")
             return hysparse_layer(q, kc, vc, self.k_arg, self.S, window[0], window[1], window[2],
-                                  out=self.outs[l], flags=FLAG_S_CHAINED, workspace=self._ws(q, kc),
+                                  out=self.outs[l], flags=FLAG_S_CHAINED | (self.split_flag & FLAG_BLOCK_SELECT),
+                                  workspace=self._ws(q, kc),
                                   kv_indptr=self.kv_indptr, seq_len=self.N, block_table=block_table,
                                   page_size=page_size)
         return hybrid_layer(q, kc, vc, self.masks[l], self.k_arg, self.S if l > 0 else None,

@@ -202,8 +202,10 @@ ld_status ld_sparse_decode(const ld_shape* shape, uint64_t head_mask,
    window_len in 1..4096. The workspace must hold ld_hysparse_workspace_size() bytes
    (zeroed once, as for the other entry points). It starts with a layer workspace of
    `shape`, so the same buffer serves ld_hybrid_layer for the full layer, and a sparse
-   layer passing LD_FLAG_S_CHAINED (the only flag taken) reuses the bitmaps that the full
-   layer's selection left there. Errors are found before the first launch. */
+   layer passing LD_FLAG_S_CHAINED reuses the bitmaps that the full layer's selection
+   left there. flags: LD_FLAG_S_CHAINED and LD_FLAG_BLOCK_SELECT (as on a layer without
+   retrieval heads: the sets are whole 64-token blocks, which only changes how the work
+   is split). Errors are found before the first launch. */
 size_t ld_hysparse_workspace_size(const ld_shape* shape, int32_t k_max, int32_t window_len);
 ld_status ld_hysparse_layer(const ld_shape* shape, const void* q, const void* k_cache,
                             const void* v_cache, int32_t k, const int32_t* s_in,

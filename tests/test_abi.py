@@ -173,7 +173,9 @@ def test_hysparse_workspace_and_arguments(lib):
     assert hys(s, kw=None) == INV and hys(s, gate=None) == INV and hys(s, s_in=None) == INV
     assert hys(s, vw=FAKE + 8) == INV                       # misaligned window cache
     assert hys(s, gate=FAKE + 2) == INV
-    assert hys(s, flags=8) == INV                           # block selection is the full layer's
+    assert hys(s, flags=4) == INV                           # selection modes are the full layer's
+    assert hys(s, flags=1) == INV
+    assert hys(s, flags=2 | 8 | 16) == INV                  # an unknown bit beside the accepted ones
     assert hys(s, ws=None) == WSE and hys(s, wsb=1 << 20) == WSE
     assert hys(_shape(head_dim=80)) == UNS
 

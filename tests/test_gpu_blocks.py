@@ -95,3 +95,42 @@ def test_block_hint_on_token_sets_gives_the_same_layer():
                                         [False] * Hq, [k], S_in)
     gh.check_outputs(out, O_ref, [(0, h) for h in range(Hq)], "token sets with the block hint")
     ws.check()
+
+
+def test_block_hint_on_a_ragged_batch():
+    """The block hint over a ragged batch: each sequence's splits share out that
+    sequence's union of 64-row blocks (lengths that end inside a block, sequences that
+    start past row 0), with token sets and with whole-block sets."""
+    ld = _ld()
+    dev = "cuda"
+    B, Hq, Hkv, d = 3, 8, 2, 128
+    lens = [4100, 777, 6400]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, N = int(offs[-1]), max(lens)
+    kv_indptr = torch.as_tensor(offs, device=dev)
+    rng = np.random.default_rng(980)
+    for blocks in (False, True):
+        rows = {}
+        for b in range(B):
+            for h in range(Hq):
+                n = lens[b]
+                if blocks:
+                    nblk = (n + 63) // 64
+                    kb = rng.choice(nblk, size=max(1, nblk // 5), replace=False)
+                    s = np.concatenate([np.arange(64 * j, min(64 * j + 64, n)) for j in sorted(kb)])
+                else:
+                    s = np.sort(rng.choice(n, size=max(1, n // 4), replace=False))
+                rows[(b, h)] = s.astype(np.int64)
+        ind_h = np.concatenate([[0], np.cumsum([rows[(b, h)].size for b in range(B) for h in range(Hq)])])
+        s_indptr = torch.as_tensor(ind_h.astype(np.int64), device=dev)
+        S = torch.as_tensor(np.concatenate([rows[(b, h)] for b in range(B) for h in range(Hq)]).astype(np.int32),
+                            device=dev)
+        q, kc, vc = wl.random_qkv(B, Hq, Hkv, d, T, 981 + int(blocks))
+        qd, kd, vd = q.to(dev), kc.to(dev), vc.to(dev)
+        out = ld.hybrid_layer(qd, kd, vd, 0x00, int(max(r.size for r in rows.values())), S, s_out=S,
+                              s_indptr=s_indptr, kv_indptr=kv_indptr, seq_len=N, flags=ld.FLAG_BLOCK_SELECT)
+        torch.cuda.synchronize()
+        O_ref, _, _ = orc.hybrid_layer_bf16(wl.bf16_bits(q), wl.bf16_bits(kc), wl.bf16_bits(vc), offs,
+                                            [False] * Hq, [int(max(r.size for r in rows.values()))] * B, rows)
+        gh.check_outputs(out, O_ref, [(b, h) for b in range(B) for h in range(Hq)],
+                         f"ragged batch, {'block' if blocks else 'token'} sets with the block hint")

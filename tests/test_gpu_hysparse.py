@@ -109,7 +109,7 @@ def test_hysparse_layer_rejects_bad_arguments():
     kw = torch.zeros((4, 16, 64), dtype=torch.bfloat16, device=dev)
     ws = ld.HySparseWorkspace(shape, 64, 16, dev)
     with pytest.raises(ld.LycheeDecodeError, match="invalid argument"):
-        ld.hysparse_layer(qd, kd, vd, 64, S, kw, kw, gate, flags=ld.FLAG_BLOCK_SELECT, workspace=ws)
+        ld.hysparse_layer(qd, kd, vd, 64, S, kw, kw, gate, flags=ld.FLAG_SEPARATE_SELECT, workspace=ws)
 
 
 def test_full_layer_then_hysparse_layers_share_one_workspace():
