@@ -134,3 +134,31 @@ def test_block_hint_on_a_ragged_batch():
                                             [False] * Hq, [int(max(r.size for r in rows.values()))] * B, rows)
         gh.check_outputs(out, O_ref, [(b, h) for b in range(B) for h in range(Hq)],
                          f"ragged batch, {'block' if blocks else 'token'} sets with the block hint")
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,n", [
+    (4, 4, 64, 3000),       # one query head per KV head
+    (16, 2, 128, 9000),     # eight query heads per KV head
+    (4, 2, 64, 140000),     # past the rows that block shares cover: the splits keep row ranges
+])
+def test_block_hint_shapes(Hq, Hkv, d, n):
+    """Whole-block sets with the block hint on a layer of sparse heads, for other group
+    sizes and for a sequence longer than the block shares handle."""
+    ld = _ld()
+    dev = "cuda"
+    rng = np.random.default_rng(990 + n)
+    nblk = (n + 63) // 64
+    rows = {}
+    for h in range(Hq):
+        kb = np.sort(rng.choice(nblk, size=max(1, nblk // 10), replace=False))
+        rows[(0, h)] = np.concatenate([np.arange(64 * j, min(64 * j + 64, n)) for j in kb]).astype(np.int64)
+    k = int(max(r.size for r in rows.values()))
+    ind_h = np.concatenate([[0], np.cumsum([rows[(0, h)].size for h in range(Hq)])]).astype(np.int64)
+    S = torch.as_tensor(np.concatenate([rows[(0, h)] for h in range(Hq)]).astype(np.int32), device=dev)
+    q, kc, vc = wl.random_qkv(1, Hq, Hkv, d, n, 991)
+    out = ld.hybrid_layer(q.to(dev), kc.to(dev), vc.to(dev), 0x00, k, S, s_out=S,
+                          s_indptr=torch.as_tensor(ind_h, device=dev), flags=ld.FLAG_BLOCK_SELECT)
+    torch.cuda.synchronize()
+    O_ref, _, _ = orc.hybrid_layer_bf16(wl.bf16_bits(q), wl.bf16_bits(kc), wl.bf16_bits(vc), [0, n],
+                                        [False] * Hq, [k], rows)
+    gh.check_outputs(out, O_ref, [(0, h) for h in range(Hq)], f"block sets, G = {Hq // Hkv}, n = {n}")
