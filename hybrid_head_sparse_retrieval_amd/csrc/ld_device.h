@@ -313,17 +313,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_n(const void* base, int b
 // workgroup) writes the sum of the kRep replicas of row `slot` to lds[kHist1Bins],
 // with 128-bit loads that are contiguous across the lanes. The caller synchronises
 // before reading lds.
-__device__ __forceinline__ uint32_t* hist1_mine(uint32_t* h1, int slot) {
-  return h1 + ((size_t)slot * kRep + rep_of_block()) * kHist1Bins;
+// reps: the replicas the row's writers use (at most kRep; the others stay zero).
+__device__ __forceinline__ uint32_t* hist1_mine(uint32_t* h1, int slot, int reps = kRep) {
+  return h1 + ((size_t)slot * kRep + (int)(blockIdx.x % (unsigned)reps)) * kHist1Bins;
 }
 // Clears the kRep replicas of row `slot` (every thread of the workgroup).
-__device__ __forceinline__ void hist1_clear(uint32_t* h1, int slot) {
+__device__ __forceinline__ void hist1_clear(uint32_t* h1, int slot, int reps = kRep) {
   uint4* r = reinterpret_cast<uint4*>(h1 + (size_t)slot * kRep * kHist1Bins);
-  for (int i = threadIdx.x; i < kRep * kHist1Bins / 4; i += (int)blockDim.x) r[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = threadIdx.x; i < reps * kHist1Bins / 4; i += (int)blockDim.x) r[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 // NT: the workgroup's thread count (it sizes the thread's register columns).
 template <int NT>
-__device__ __forceinline__ void hist1_sum(uint32_t* lds, const uint32_t* h1, int slot) {
+__device__ __forceinline__ void hist1_sum(uint32_t* lds, const uint32_t* h1, int slot, int reps = kRep) {
   const __amdgpu_buffer_rsrc_t r = rsrc(h1 + (size_t)slot * kRep * kHist1Bins);
   // every load of the thread's columns is issued before the first sum
   constexpr int kMaxCols = (kHist1Bins / 4 + NT - 1) / NT;   // column groups per thread
@@ -334,7 +335,9 @@ __device__ __forceinline__ void hist1_sum(uint32_t* lds, const uint32_t* h1, int
     const int i = threadIdx.x + c * nt;
 #pragma unroll
     for (int q = 0; q < kRep; ++q)
-      if (i < kHist1Bins / 4) a[c][q] = __builtin_amdgcn_raw_buffer_load_b128(r, (q * kHist1Bins + 4 * i) * 4, 0, kSc1);
+      a[c][q] = (i < kHist1Bins / 4 && q < reps)
+                    ? __builtin_amdgcn_raw_buffer_load_b128(r, (q * kHist1Bins + 4 * i) * 4, 0, kSc1)
+                    : u32x4_t{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int c = 0; c < kMaxCols; ++c) {

@@ -134,6 +134,7 @@ struct SelParams {
   uint32_t* span_off;     // [slots][C]: output offset of each span
   uint64_t* cand;         // [slots][ncap]: (index << 32 | key) of the candidates, per span
   int64_t ncap;           // C * kSelSpan
+  int hist_reps;          // set by launch_select: digit-1 histogram replicas the rows use
 };
 
 // Build membership bitmaps of sparse heads from S rows.

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void k_sel_hist(const SelParams p) {
     for (int i = lo + tid; i < hi; i += kThreads) atomicAdd(&hist[score_key(v.sc[i]) >> 21], 1u);
   }
   __syncthreads();
-  uint32_t* gh = hist1_mine(p.hist1, v.slot);
+  uint32_t* gh = hist1_mine(p.hist1, v.slot, p.hist_reps);
   for (int i = tid; i < kHist1Bins; i += kThreads)
     if (hist[i]) atomicAdd(gh + i, hist[i]);
 }
@@ -569,7 +569,7 @@ __global__ __launch_bounds__(kSpanThreads) void k_sel_cand(const SelParams p) {
   const int n = v.n, kk = v.k;
   if (n < 1) return;
   if (kk < 1) {                                 // an empty row of a CSR S: nothing to keep,
-    if (c == 0) hist1_clear(p.hist1, v.slot);   // but its histogram may hold counts
+    if (c == 0) hist1_clear(p.hist1, v.slot, p.hist_reps);   // but its histogram may hold counts
     return;
   }
   const int nsp = (n + kSelSpan - 1) / kSelSpan;
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(kSpanThreads) void k_sel_cand(const SelParams p) {
   uint32_t key[kSpanRounds][4];
   load_span(v.sc, n, c * kSelSpan, tid, key);
   // digit 1 from the row's histogram (the sum of its replicas), while the scores load
-  hist1_sum<kSpanThreads>(sm.hist, p.hist1, slot);
+  hist1_sum<kSpanThreads>(sm.hist, p.hist1, slot, p.hist_reps);
   if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
   __syncthreads();
   find_bin_from_top<kHist1Bins, kSpanThreads>([&](int i) { return sm.hist[i]; }, (uint32_t)kk, sm.tmp, sm.res);
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(kSpanThreads) void k_sel_cand(const SelParams p) {
   span_candidates(p, slot, c, n, b1, key, cand, gh2, sm);   // (find_bin ends with a barrier)
   if (!arrive_last(p.tickets + slot, (uint32_t)nsp, &sm.flag)) return;
   if (tid == 0) p.tickets[slot] = 0u;
-  hist1_clear(p.hist1, slot);                   // every span has read it
+  hist1_clear(p.hist1, slot, p.hist_reps);      // every span has read it
   uint32_t T, i_tie;
   row_threshold(p, slot, nsp, b1, k1, gh2, true, cand, sm, T, i_tie);
   (void)span_offsets(nsp, sm, p.span_off + (size_t)slot * p.C, -1);
@@ -696,6 +696,8 @@ hipError_t launch_block_expand(const BlockParams& p, int rows, hipStream_t st) {
   return hipGetLastError();
 }
 
+constexpr int kHistOneRepChunks = 16;   // histogram workgroups per row that share one replica
+
 int select_launches(const SelParams& p, bool with_hist) {
   if (with_hist && p.mode == 0 && p.n <= kSmallRow) return 1;
   return (with_hist ? 1 : 0) + 2;
@@ -706,14 +708,20 @@ hipError_t launch_select(const SelParams& p, hipStream_t st, bool with_hist) {
     hipLaunchKernelGGL(k_sel_small, dim3((unsigned)p.nrows), dim3(kSmallThreads), 0, st, p);
     return hipGetLastError();
   }
+  // The histogram launch spreads a row's counts over replicas only when many of its
+  // workgroups share the row (their atomics would meet on the same bins); with a few, one
+  // replica is enough, and the candidate launch then sums one instead of kRep. The
+  // attention launch's fused histogram always uses kRep.
+  SelParams q = p;
+  q.hist_reps = (with_hist && p.Ch <= kHistOneRepChunks) ? 1 : kRep;
   if (with_hist) {
-    SelParams ph = p;
+    SelParams ph = q;
     ph.C = p.Ch;
     hipLaunchKernelGGL(k_sel_hist, dim3((unsigned)p.nrows * (unsigned)p.Ch), dim3(kThreads), 0, st, ph);
   }
   const dim3 grid((unsigned)p.nrows * (unsigned)p.C);
-  hipLaunchKernelGGL(k_sel_cand, grid, dim3(kSpanThreads), 0, st, p);
-  hipLaunchKernelGGL(k_sel_write, grid, dim3(kSpanThreads), 0, st, p);
+  hipLaunchKernelGGL(k_sel_cand, grid, dim3(kSpanThreads), 0, st, q);
+  hipLaunchKernelGGL(k_sel_write, grid, dim3(kSpanThreads), 0, st, q);
   return hipGetLastError();
 }
 
