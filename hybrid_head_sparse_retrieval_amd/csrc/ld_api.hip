@@ -60,7 +60,7 @@ template <typename Take>
 void sel_data(SelArrays& a, int rows, int n, Take take) {
   a.C = (n + kSelSpan - 1) / kSelSpan;
   a.ncap = (int64_t)a.C * kSelSpan;
-  a.sel_info = take((size_t)rows * 16);
+  a.sel_info = take((size_t)rows * 8);
   a.span_cnt = take((size_t)rows * a.C * 8);
   a.span_off = take((size_t)rows * a.C * 4);
   a.cand = take((size_t)rows * a.ncap * 8);
@@ -513,7 +513,6 @@ ld_status run_layer(const ld_shape* shape, uint64_t active, uint64_t retrieval, 
   ap.P1 = L.P1;
   ap.do_topk = (do_topk && !block) ? 1 : 0;     // block selection needs the logits only
   ap.hist1 = at<uint32_t>(ws, L.sel.hist1);
-  ap.sel_info = at<uint32_t>(ws, L.sel.sel_info);
   ap.k_dense = k;
   ap.s_indptr = s_indptr;
   ap.s_cap = s_cap;

@@ -80,7 +80,6 @@ struct AttnParams {
   float* l1_ml;           // [B*Hq][P1][2]  first-level merged partials
   float* l1_acc;          // [B*Hq][P1][D]
   uint32_t* hist1;        // [B*Hq][kRep][kHist1Bins] (summed over replicas), zero between calls
-  uint32_t* sel_info;     // [B*Hq][4]
   int k_dense;
   // finisher mode: the last split of each (b, g) to arrive merges O; with do_topk, up to
   // sel_cap splits that arrive just before it wait for it and then select the group's
@@ -129,7 +128,7 @@ struct SelParams {
   uint32_t* hist2;        // [slots][kHist2Bins], zero between calls
   uint32_t* tickets;      // [slots] arrivals, zero between calls
   uint32_t* err;          // the workspace's wait flag (set by the attention launch's bounded waits)
-  uint32_t* sel_info;     // [slots][4]: b1, k1, T, i_tie
+  uint32_t* sel_info;     // [slots][2]: the threshold key T and i_tie, from the row's last span
   uint32_t* span_cnt;     // [slots][C][2]: keys above bin b1, candidates (keys in bin b1)
   uint32_t* span_off;     // [slots][C]: output offset of each span
   uint64_t* cand;         // [slots][ncap]: (index << 32 | key) of the candidates, per span

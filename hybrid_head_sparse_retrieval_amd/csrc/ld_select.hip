@@ -595,8 +595,8 @@ __global__ __launch_bounds__(kSpanThreads) void k_sel_cand(const SelParams p) {
   row_threshold(p, slot, nsp, b1, k1, gh2, true, cand, sm, T, i_tie);
   (void)span_offsets(nsp, sm, p.span_off + (size_t)slot * p.C, -1);
   if (tid == 0) {
-    p.sel_info[slot * 4 + 2] = T;
-    p.sel_info[slot * 4 + 3] = i_tie;
+    p.sel_info[slot * 2 + 0] = T;
+    p.sel_info[slot * 2 + 1] = i_tie;
   }
 }
 
@@ -608,8 +608,8 @@ __global__ __launch_bounds__(kSpanThreads) void k_sel_write(const SelParams p) {
   const int nsp = (v.n + kSelSpan - 1) / kSelSpan;
   if (c >= nsp) return;
   const int slot = v.slot;
-  const uint32_t T = p.sel_info[slot * 4 + 2];
-  const uint32_t i_tie = p.sel_info[slot * 4 + 3];
+  const uint32_t T = p.sel_info[slot * 2 + 0];
+  const uint32_t i_tie = p.sel_info[slot * 2 + 1];
   const int off = (int)p.span_off[(size_t)slot * p.C + c];
   uint32_t key[kSpanRounds][4];
   load_span(v.sc, v.n, c * kSelSpan, threadIdx.x, key);
